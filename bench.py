@@ -1,0 +1,177 @@
+"""Throughput of the emulated DGEMM (Ozaki scheme II on INT8 MFMA) on one MI355X.
+
+Workload: square DGEMM M = N = K = 8192, op = N/N, alpha = 1, beta = 0,
+entries (u - 1/2) exp(0.5 g), u ~ U(0,1), g ~ N(0,1), seeded; one "step" is
+one emulated DGEMM at each s in {8, 12, 16} (three calls, every phase of the
+method inside each).  Inputs are resident in HBM before timing starts.
+
+Printed: ONE JSON line with the metric (emulated TFLOP/s, 2MNK flops per
+call), the per-s breakdown (phase times from HIP events recorded on the
+stream the kernels run on, INT8 MFMA utilisation of the GEMM phase and HBM
+GB/s of the memory-bound phases), the roofline of the residue-GEMM kernel and
+the oracle's rate on the host cores (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--s 8,12,16]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(m, n, k, s, beta_nonzero=False):
+    """Minimum work of one call (each operand read once, INT8 intermediates)."""
+    return dict(
+        int8_ops=2.0 * m * n * k * s,
+        scan_bytes=8.0 * (m * k + k * n),
+        encode_bytes=(8.0 + s) * (m * k + k * n),
+        gemm_bytes=s * (m * k + k * n) + s * m * n,
+        recon_bytes=(s + 8.0) * m * n + (8.0 * m * n if beta_nonzero else 0.0),
+    )
+
+
+def cpu_baseline(A, B, m, n, k, s, side, seed=12345):
+    """The oracle (as it stands) on a seeded side x side sample of output
+    entries of the same workload, on all host cores."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, side, replace=False)]))[:side]
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, side, replace=False)]))[:side]
+    ii, jj = np.meshgrid(rows, cols, indexing="ij")
+    nt = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.gemm_entries(False, "N", "N", m, n, k, 1.0, A, m, B, k, 0.0, None, m, s,
+                        rows=ii.reshape(-1), cols=jj.reshape(-1), nthreads=nt)
+    dt = time.perf_counter() - t0
+    entries = ii.size
+    return dict(value=2.0 * k * entries / dt / 1e12, unit="TFLOP/s", cores=nt, kind="oracle",
+                sample=f"{rows.size}x{cols.size} sampled output entries of the {m}x{n}x{k} "
+                       f"s={s} workload (exact wide-integer products), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--s", type=str, default="8,12,16")
+    ap.add_argument("--n", type=int, default=8192)
+    ap.add_argument("--cpu-side", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the emulated GEMM of a single device "
+              f"(got --gpus {args.gpus}); multi-GPU runs are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+
+    s_list = [int(x) for x in args.s.split(",")]
+    m = n = k = args.n
+    log(f"[bench] generating {m}x{k} and {k}x{n} inputs (phi = 0.5, seeded)")
+    A = workloads.real_matrix(m, k, workloads.seed(2, 0), "phi", 0.5)
+    B = workloads.real_matrix(k, n, workloads.seed(2, 1), "phi", 0.5)
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.zeros(m * n, dtype=torch.float64, device="cuda")
+    stream = torch.cuda.current_stream()
+    handles = {s: oz2.Handle(stream) for s in s_list}
+    for h in handles.values():
+        h.set_timing(True)
+
+    def step(record):
+        for s in s_list:
+            handles[s].dgemm("N", "N", m, n, k, 1.0, dA, m, dB, k, 0.0, dC, m, s)
+        if record is not None:
+            for s in s_list:
+                record[s].append(handles[s].phase_times())
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    phases = {s: [] for s in s_list}
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(phases)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / args.steps * 1e3
+    flops_per_step = 2.0 * m * n * k * len(s_list)
+    value = flops_per_step / (dt / args.steps) / 1e12
+
+    per_s = {}
+    gemm_ops = gemm_ms = 0.0
+    for s in s_list:
+        ph = np.mean(np.array(phases[s]), axis=0)  # ms: scan, encode, gemm, reconstruct
+        w = algorithmic(m, n, k, s)
+        call_ms = float(np.sum(ph))
+        per_s[str(s)] = dict(
+            tflops=2.0 * m * n * k / (call_ms * 1e-3) / 1e12,
+            ms=dict(scan=round(float(ph[0]), 4), encode=round(float(ph[1]), 4),
+                    gemm=round(float(ph[2]), 4), reconstruct=round(float(ph[3]), 4)),
+            gemm_int8_tops=w["int8_ops"] / (ph[2] * 1e-3) / 1e12,
+            gemm_int8_util=w["int8_ops"] / (ph[2] * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            scan_gbs=w["scan_bytes"] / (ph[0] * 1e-3) / 1e9,
+            encode_gbs=w["encode_bytes"] / (ph[1] * 1e-3) / 1e9,
+            reconstruct_gbs=w["recon_bytes"] / (ph[3] * 1e-3) / 1e9,
+        )
+        gemm_ops += w["int8_ops"]
+        gemm_ms += float(ph[2])
+    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    roofline = dict(kernel="residue_gemm_kernel (INT8 MFMA, fused mod m)", bound="mfma",
+                    achieved=round(achieved, 2), peak=PEAK_INT8_TOPS, unit="TOP/s",
+                    frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=None,
+                    per_launch_ops="2*M*N*K*s (s = 8, 12, 16; one launch per call)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        s_cpu = s_list[-1]
+        log(f"[bench] oracle cpu baseline on a {args.cpu_side}^2 entry sample, s={s_cpu}")
+        cpu = cpu_baseline(A, B, m, n, k, s_cpu, args.cpu_side)
+
+    out = {
+        "metric": "emulated DGEMM TFLOP/s at N=8192, s=8/12/16 (+ INT8 MFMA util, HBM GB/s)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64 (emulated on int8 MFMA)",
+        "data": "synthetic",
+        "config": {"workload": f"dgemm_{m}_NN_phi0.5_s{'_'.join(map(str, s_list))}",
+                   "m": m, "n": n, "k": k, "s": s_list, "ops": "N/N", "alpha": 1.0, "beta": 0.0},
+        "per_s": per_s,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    for h in handles.values():
+        h.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,253 @@
+"""oz2 -- Ozaki scheme II DGEMM/ZGEMM emulation on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/oz2.h``: argument marshalling
+and host-side extent checks only.  Every step of the computation runs in the
+HIP kernels of ``liboz2.so``; torch is used for device memory and streams.
+If the library is missing, every entry point raises -- there is no fallback.
+
+Matrices follow BLAS conventions: column-major, op in {'N', 'T', 'C'},
+leading dimensions.  A torch tensor passed as a matrix is used through its
+data pointer as flat column-major storage, so a row-major torch tensor of
+shape (cols, ld) is a column-major (ld x cols) matrix.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = ["Handle", "Oz2Error", "lib", "plan_info", "moduli_for_bits", "EXPORTED_SYMBOLS",
+           "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboz2.so")
+
+# every function declared in include/oz2.h
+EXPORTED_SYMBOLS = (
+    "oz2_create", "oz2_destroy", "oz2_set_stream", "oz2_set_memory_limit",
+    "oz2_get_workspace_size", "oz2_set_timing", "oz2_get_phase_times", "oz2_moduli_for_bits",
+    "oz2_plan_info", "oz2_dgemm", "oz2_zgemm", "oz2_dgemm_strided_batched", "oz2_status_string",
+    "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt",
+)
+
+_lib = None
+
+
+class Oz2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        text = _raw().oz2_status_string(status).decode() if _lib is not None else str(status)
+        if status < 0:
+            text = f"argument {-status} is invalid"
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def _raw():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, C, D, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_char,
+                               ctypes.c_double, ctypes.c_size_t)
+        sig = {
+            "oz2_create": [P],
+            "oz2_destroy": [P],
+            "oz2_set_stream": [P, P],
+            "oz2_set_memory_limit": [P, SZ],
+            "oz2_get_workspace_size": [P, P],
+            "oz2_set_timing": [P, I],
+            "oz2_get_phase_times": [P, P],
+            "oz2_moduli_for_bits": [I64, I, I],
+            "oz2_plan_info": [I, I64, I, P, P, P, P],
+            "oz2_dgemm": [P, C, C, I64, I64, I64, D, P, I64, P, I64, D, P, I64, I],
+            "oz2_zgemm": [P, C, C, I64, I64, I64, P, P, I64, P, I64, P, P, I64, I],
+            "oz2_dgemm_strided_batched": [P, C, C, I64, I64, I64, D, P, I64, I64, P, I64, I64, D,
+                                          P, I64, I64, I64, I],
+            "oz2_set_debug": [P, I],
+            "oz2_debug_copy": [P, I, P, SZ, P, P],
+            "oz2_test_crt": [P, I64, I, P, P],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = I
+        L.oz2_status_string.argtypes = [I]
+        L.oz2_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it has not been built)."""
+    return _raw()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Oz2Error(fn, status)
+
+
+def plan_info(s: int, k: int, is_complex: bool = False) -> dict:
+    mods = (ctypes.c_int32 * 24)()
+    t, nl, l2 = ctypes.c_int(), ctypes.c_int(), ctypes.c_double()
+    _check("oz2_plan_info", _raw().oz2_plan_info(s, k, int(is_complex), mods, ctypes.byref(t),
+                                                  ctypes.byref(nl), ctypes.byref(l2)))
+    return dict(moduli=tuple(mods[:s]), t=t.value, NL=nl.value, log2M=l2.value)
+
+
+def moduli_for_bits(k: int, bits: int = 53, is_complex: bool = False) -> int:
+    return int(_raw().oz2_moduli_for_bits(k, bits, int(is_complex)))
+
+
+def _extent(rows: int, cols: int, ld: int) -> int:
+    return 0 if rows == 0 or cols == 0 else (cols - 1) * ld + rows
+
+
+def _dev_ptr(x, dtype_name: str, need: int, what: str):
+    """Device pointer of a CUDA torch tensor holding at least `need` elements."""
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    want = {"f64": torch.float64, "c128": torch.complex128, "u8": torch.uint8,
+            "u32": torch.int32}[dtype_name]
+    if x.dtype != want:
+        raise TypeError(f"{what} must have dtype {want}, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a device (cuda) tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if x.numel() < need:
+        raise ValueError(f"{what} holds {x.numel()} elements, the call needs {need}")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+class Handle:
+    """An oz2 handle bound to the current device; work goes to torch's
+    current stream at the time of each call unless a stream is given."""
+
+    def __init__(self, stream=None):
+        h = ctypes.c_void_p()
+        _check("oz2_create", _raw().oz2_create(ctypes.byref(h)))
+        self._h = h
+        self._stream = stream
+
+    def close(self) -> None:
+        if self._h is not None and self._h.value:
+            _raw().oz2_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ---------------------------------------------------------------- config
+    def _bind_stream(self) -> None:
+        import torch
+        st = self._stream if self._stream is not None else torch.cuda.current_stream()
+        _raw().oz2_set_stream(self._h, ctypes.c_void_p(st.cuda_stream))
+
+    def set_memory_limit(self, nbytes: int) -> None:
+        _check("oz2_set_memory_limit", _raw().oz2_set_memory_limit(self._h, nbytes))
+
+    def workspace_size(self) -> int:
+        v = ctypes.c_size_t()
+        _check("oz2_get_workspace_size", _raw().oz2_get_workspace_size(self._h, ctypes.byref(v)))
+        return v.value
+
+    def set_timing(self, enable: bool) -> None:
+        _check("oz2_set_timing", _raw().oz2_set_timing(self._h, int(enable)))
+
+    def phase_times(self) -> list:
+        arr = (ctypes.c_float * 4)()
+        _check("oz2_get_phase_times", _raw().oz2_get_phase_times(self._h, arr))
+        return list(arr)
+
+    def set_debug(self, enable: bool) -> None:
+        _check("oz2_set_debug", _raw().oz2_set_debug(self._h, int(enable)))
+
+    # ------------------------------------------------------------------ BLAS
+    @staticmethod
+    def _stored(op: str, rows: int, cols: int):
+        return (rows, cols) if op.upper() == "N" else (cols, rows)
+
+    def dgemm(self, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s):
+        ra, ca = self._stored(transa, m, k)
+        rb, cb = self._stored(transb, k, n)
+        need_ab = m > 0 and n > 0 and k > 0 and alpha != 0.0
+        pa = _dev_ptr(A, "f64", _extent(ra, ca, lda), "A") if need_ab else None
+        pb = _dev_ptr(B, "f64", _extent(rb, cb, ldb), "B") if need_ab else None
+        pc = _dev_ptr(C, "f64", _extent(m, n, ldc), "C") if m > 0 and n > 0 else None
+        self._bind_stream()
+        _check("oz2_dgemm", _raw().oz2_dgemm(self._h, transa.encode(), transb.encode(), m, n, k,
+                                             float(alpha), pa, lda, pb, ldb, float(beta), pc,
+                                             ldc, s))
+
+    def zgemm(self, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s):
+        ra, ca = self._stored(transa, m, k)
+        rb, cb = self._stored(transb, k, n)
+        alpha, beta = complex(alpha), complex(beta)
+        need_ab = m > 0 and n > 0 and k > 0 and alpha != 0
+        pa = _dev_ptr(A, "c128", _extent(ra, ca, lda), "A") if need_ab else None
+        pb = _dev_ptr(B, "c128", _extent(rb, cb, ldb), "B") if need_ab else None
+        pc = _dev_ptr(C, "c128", _extent(m, n, ldc), "C") if m > 0 and n > 0 else None
+        al = (ctypes.c_double * 2)(alpha.real, alpha.imag)
+        be = (ctypes.c_double * 2)(beta.real, beta.imag)
+        self._bind_stream()
+        _check("oz2_zgemm", _raw().oz2_zgemm(self._h, transa.encode(), transb.encode(), m, n, k,
+                                             al, pa, lda, pb, ldb, be, pc, ldc, s))
+
+    def dgemm_strided_batched(self, transa, transb, m, n, k, alpha, A, lda, strideA, B, ldb,
+                              strideB, beta, C, ldc, strideC, batch, s):
+        ra, ca = self._stored(transa, m, k)
+        rb, cb = self._stored(transb, k, n)
+        live = batch > 0 and m > 0 and n > 0
+        need_ab = live and k > 0 and alpha != 0.0
+        last = max(batch - 1, 0)
+        pa = _dev_ptr(A, "f64", last * strideA + _extent(ra, ca, lda), "A") if need_ab else None
+        pb = _dev_ptr(B, "f64", last * strideB + _extent(rb, cb, ldb), "B") if need_ab else None
+        pc = _dev_ptr(C, "f64", last * strideC + _extent(m, n, ldc), "C") if live else None
+        self._bind_stream()
+        _check("oz2_dgemm_strided_batched",
+               _raw().oz2_dgemm_strided_batched(self._h, transa.encode(), transb.encode(), m, n,
+                                                k, float(alpha), pa, lda, strideA, pb, ldb,
+                                                strideB, float(beta), pc, ldc, strideC, batch, s))
+
+    # ------------------------------------------------------------ test hooks
+    def debug_copy(self, which: int) -> np.ndarray:
+        """Intermediate buffer `which` of the last call, copied to the host
+        (see oz2_debug_copy in include/oz2.h for the layouts)."""
+        nbytes = ctypes.c_size_t()
+        dims = (ctypes.c_int64 * 5)()
+        _check("oz2_debug_copy", _raw().oz2_debug_copy(self._h, which, None, 0,
+                                                       ctypes.byref(nbytes), dims))
+        dtype = {0: np.uint64, 1: np.uint64, 2: np.int8, 3: np.int8, 4: np.uint8, 5: np.uint32}[which]
+        out = np.empty(nbytes.value // np.dtype(dtype).itemsize, dtype=dtype)
+        _check("oz2_debug_copy", _raw().oz2_debug_copy(self._h, which, out.ctypes.data_as(ctypes.c_void_p),
+                                                       out.nbytes, ctypes.byref(nbytes), dims))
+        d = [int(x) for x in dims]
+        if which in (2, 3):
+            return out.reshape(d[0], d[1], d[2], d[3])
+        if which == 4:
+            return out.reshape(d[4], d[0], d[1], d[2], d[3])
+        if which == 5:
+            return out.reshape(d[0], d[2], d[3], d[4])
+        return out
+
+    def test_crt(self, residues, s: int, words) -> None:
+        """CRT of residues (uint8 device tensor [s][count]) into N_L int32
+        words per entry (int32 device tensor [count][N_L])."""
+        count = residues.numel() // s
+        nl = plan_info(s, 1)["NL"]
+        pr = _dev_ptr(residues, "u8", s * count, "residues")
+        pw = _dev_ptr(words, "u32", count * nl, "words")
+        self._bind_stream()
+        _check("oz2_test_crt", _raw().oz2_test_crt(self._h, count, s, pr, pw))

@@ -1,0 +1,458 @@
+// oz2_api.cpp -- the C ABI declared in include/oz2.h: argument checking,
+// BLAS quick returns, the per-call plan (scaling width, padding, workspace
+// layout) and the launch sequence scan -> encode -> residue GEMM ->
+// reconstruct on the handle's stream.
+//
+// "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
+// Ozaki Scheme II on the Xe2 Architecture": Sec. 4 (the pipeline runs
+// entirely on the device; the host only computes O(s) tables), Sec. 6 (one
+// in-order queue, asynchronous submission; workspace reused across calls and
+// capped by a resident-memory hint), Sec. 9.1 (interface = dgemm/zgemm plus
+// the number of moduli; default precision policy).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+
+#include "oz2.h"
+#include "oz2_internal.h"
+
+using namespace oz2;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
+
+// a run of at most this many k-positions keeps |INT32 accumulator| <= 2^31 - 2^20
+// (Arc page Sec. 2.3 step 3: exact while k 128^2 < 2^31); a multiple of 64
+constexpr int64_t kMaxRunK = 131008;
+
+struct Layout {
+    int sets = 1, outs = 1, s = 0, NL = 0, t = 0, chunks = 1;
+    int64_t m = 0, n = 0, k = 0, mp = 0, np = 0, kp = 0;
+    size_t off_amaxA = 0, off_amaxB = 0, off_pa = 0, off_pb = 0, off_res = 0, off_chat = 0;
+    size_t bytes_pa = 0, bytes_pb = 0, bytes_res = 0, bytes_chat = 0, total = 0;
+    bool valid = false;
+};
+
+}  // namespace
+
+struct oz2_context {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    void* ws = nullptr;
+    size_t ws_size = 0;
+    size_t mem_limit = 0;
+    int timing = 0;
+    int debug = 0;
+    bool timed = false;
+    hipEvent_t ev[5] = {};
+    Layout last;
+};
+
+namespace {
+
+bool valid_op(char c) {
+    return c == 'N' || c == 'n' || c == 'T' || c == 't' || c == 'C' || c == 'c';
+}
+bool is_trans(char c) { return !(c == 'N' || c == 'n'); }
+bool is_conj(char c) { return c == 'C' || c == 'c'; }
+
+int ensure_workspace(oz2_context* h, size_t bytes) {
+    if (bytes <= h->ws_size) return OZ2_STATUS_SUCCESS;
+    size_t cap = h->mem_limit;
+    if (cap == 0) {
+        size_t free_b = 0, total_b = 0;
+        if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
+        cap = free_b + h->ws_size;
+    }
+    if (bytes > cap) return OZ2_STATUS_WORKSPACE_LIMIT;
+    if (h->ws) {
+        if (hipStreamSynchronize(h->stream) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
+        (void)hipFree(h->ws);
+        h->ws = nullptr;
+        h->ws_size = 0;
+    }
+    if (hipMalloc(&h->ws, bytes) != hipSuccess) {
+        h->ws = nullptr;
+        (void)hipGetLastError();
+        return OZ2_STATUS_ALLOC_FAILED;
+    }
+    h->ws_size = bytes;
+    return OZ2_STATUS_SUCCESS;
+}
+
+#define OZ2_LAUNCH(expr)                                  \
+    do {                                                  \
+        if ((expr) != hipSuccess) return OZ2_STATUS_HIP_ERROR; \
+    } while (0)
+
+void fill_mod_tables(const ModuliPlan& pl, EncodeParams* E, bool ext) {
+    for (int q = 0; q < pl.s; ++q) {
+        E->mod[q] = (uint32_t)pl.mod[q];
+        E->barrett[q] = pl.barrett[q];
+        E->h[q] = pl.h[q];
+        E->K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
+        for (int l = 0; l < kExtLimbs; ++l) E->c[q][l] = pl.c21[q][l];
+    }
+}
+
+template <class P>
+void fill_crt_tables(const ModuliPlan& pl, P* R) {
+    for (int q = 0; q < pl.s; ++q) {
+        R->finv[q] = pl.finv[q];
+        for (int l = 0; l < 2 * pl.NL; ++l) R->W16[q][l] = pl.W16[q][l];
+    }
+    for (int l = 0; l < 2 * pl.NL; ++l) R->M16[l] = pl.M16[l];
+}
+
+int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n,
+              int64_t k, const double alpha[2], const double* A, int64_t lda, const double* B,
+              int64_t ldb, const double beta[2], double* C, int64_t ldc, int s) {
+    if (!h) return -1;
+    if (!valid_op(transa)) return -2;
+    if (!valid_op(transb)) return -3;
+    if (m < 0) return -4;
+    if (n < 0) return -5;
+    if (k < 0) return -6;
+    const int64_t rows_a = is_trans(transa) ? k : m;
+    const int64_t rows_b = is_trans(transb) ? n : k;
+    if (lda < (rows_a > 1 ? rows_a : 1)) return -9;
+    if (ldb < (rows_b > 1 ? rows_b : 1)) return -11;
+    if (ldc < (m > 1 ? m : 1)) return -14;
+    if (s < kMinS || s > kMaxS) return -15;
+    if (m == 0 || n == 0) return OZ2_STATUS_SUCCESS;
+    if (!C) return -13;
+    const bool alpha_zero = alpha[0] == 0.0 && alpha[1] == 0.0;
+    const bool beta_zero = beta[0] == 0.0 && beta[1] == 0.0;
+    h->timed = false;
+    if (alpha_zero || k == 0) {
+        OZ2_LAUNCH(launch_scale_c(C, m, n, ldc, beta, cplx, h->stream));
+        return OZ2_STATUS_SUCCESS;
+    }
+    if (!A) return -8;
+    if (!B) return -10;
+
+    const ModuliPlan* pl = moduli_plan(s);
+    if (!pl) return OZ2_STATUS_INTERNAL;
+    const int t = scaling_width(*pl, k, cplx);
+    if (t < 1) return OZ2_STATUS_RANGE;
+    const bool ext = t > kMaxStdT;
+
+    Layout L;
+    L.sets = cplx ? 3 : 1;
+    L.outs = cplx ? 2 : 1;
+    L.s = s;
+    L.NL = pl->NL;
+    L.t = t;
+    L.m = m; L.n = n; L.k = k;
+    L.mp = round_up(m, kPadM);
+    L.np = round_up(n, kPadM);
+    L.kp = round_up(k, kPadK);
+    size_t off = 0;
+    L.off_amaxA = off; off = align_up(off + 8 * (size_t)L.mp);
+    L.off_amaxB = off; off = align_up(off + 8 * (size_t)L.np);
+    L.bytes_pa = (size_t)L.sets * s * L.mp * L.kp;
+    L.off_pa = off; off = align_up(off + L.bytes_pa);
+    L.bytes_pb = (size_t)L.sets * s * L.np * L.kp;
+    L.off_pb = off; off = align_up(off + L.bytes_pb);
+    L.chunks = (int)((L.kp + kMaxRunK - 1) / kMaxRunK);
+    L.bytes_res = (size_t)L.chunks * L.outs * s * L.n * L.mp;
+    L.off_res = off; off = align_up(off + L.bytes_res);
+    L.bytes_chat = h->debug ? (size_t)L.outs * L.n * L.mp * L.NL * 4 : 0;
+    L.off_chat = off; off = align_up(off + L.bytes_chat);
+    L.total = off;
+    int st = ensure_workspace(h, L.total);
+    if (st) return st;
+    char* ws = (char*)h->ws;
+    uint64_t* amaxA = (uint64_t*)(ws + L.off_amaxA);
+    uint64_t* amaxB = (uint64_t*)(ws + L.off_amaxB);
+    int8_t* pa = (int8_t*)(ws + L.off_pa);
+    int8_t* pb = (int8_t*)(ws + L.off_pb);
+    uint8_t* res = (uint8_t*)(ws + L.off_res);
+    uint32_t* chat = h->debug ? (uint32_t*)(ws + L.off_chat) : nullptr;
+    hipStream_t stm = h->stream;
+
+    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[0], stm));
+    // phase 1: row maxima of op(A), column maxima of op(B)
+    OZ2_LAUNCH(launch_fill_u64(amaxA, L.mp, 0, stm));
+    OZ2_LAUNCH(launch_fill_u64(amaxB, L.np, 0, stm));
+    {
+        ScanParams S{};
+        S.X = A; S.ld = lda; S.nvec = m; S.k = k; S.amax = amaxA;
+        const bool contig = is_trans(transa);  // row i of op(A) = column i of A
+        int64_t vb = (m + 255) / 256, chunks = 2048 / (vb > 0 ? vb : 1);
+        if (chunks < 1) chunks = 1;
+        S.pchunk = (k + chunks - 1) / chunks;
+        OZ2_LAUNCH(launch_scan(S, contig, cplx, stm));
+        ScanParams Sb{};
+        Sb.X = B; Sb.ld = ldb; Sb.nvec = n; Sb.k = k; Sb.amax = amaxB;
+        const bool contig_b = !is_trans(transb);  // column j of op(B) = column j of B
+        vb = (n + 255) / 256;
+        chunks = 2048 / (vb > 0 ? vb : 1);
+        if (chunks < 1) chunks = 1;
+        Sb.pchunk = (k + chunks - 1) / chunks;
+        OZ2_LAUNCH(launch_scan(Sb, contig_b, cplx, stm));
+    }
+    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
+    // phase 2: integerize and encode both operands
+    {
+        EncodeParams E{};
+        fill_mod_tables(*pl, &E, ext);
+        E.t = t; E.s = s;
+        E.X = A; E.ld = lda; E.nvec = m; E.k = k; E.vpad = L.mp; E.kpad = L.kp;
+        E.set_stride = (int64_t)s * L.mp * L.kp;
+        E.amax = amaxA; E.planes = pa; E.conj = cplx && is_conj(transa);
+        OZ2_LAUNCH(launch_encode(E, is_trans(transa), cplx, ext, stm));
+        E.X = B; E.ld = ldb; E.nvec = n; E.vpad = L.np;
+        E.set_stride = (int64_t)s * L.np * L.kp;
+        E.amax = amaxB; E.planes = pb; E.conj = cplx && is_conj(transb);
+        OZ2_LAUNCH(launch_encode(E, !is_trans(transb), cplx, ext, stm));
+    }
+    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
+    // phase 3: s exact INT8 products, reduced mod m_t on chip, one launch per
+    // k run of at most kMaxRunK positions
+    const int64_t chunk_stride = (int64_t)L.outs * s * L.n * L.mp;
+    {
+        GemmParams G{};
+        G.A = pa; G.B = pb;
+        G.mp = L.mp; G.np = L.np; G.kp = L.kp; G.n = n;
+        G.a_set_stride = (int64_t)s * L.mp * L.kp;
+        G.b_set_stride = (int64_t)s * L.np * L.kp;
+        G.c_set_stride = (int64_t)s * L.n * L.mp;
+        G.s = s;
+        for (int q = 0; q < s; ++q) {
+            G.mod[q] = (uint32_t)pl->mod[q];
+            G.barrett[q] = pl->barrett[q];
+            G.bias[q] = pl->gemm_bias[q];
+        }
+        for (int c = 0; c < L.chunks; ++c) {
+            G.C = res + c * chunk_stride;
+            G.k_begin = c * kMaxRunK;
+            const int64_t k_end = (c + 1) * kMaxRunK < L.kp ? (c + 1) * kMaxRunK : L.kp;
+            G.k_steps = (int)((k_end - G.k_begin) / kPadK);
+            OZ2_LAUNCH(launch_residue_gemm(G, cplx, stm));
+        }
+    }
+    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
+    // phase 4: CRT, rounding, scale back, alpha/beta
+    {
+        ReconParams R{};
+        fill_crt_tables(*pl, &R);
+        R.R = res; R.mp = L.mp; R.m = m; R.n = n;
+        R.r_set_stride = (int64_t)s * L.n * L.mp;
+        R.r_chunk_stride = chunk_stride;
+        R.chunks = L.chunks;
+        for (int q = 0; q < s; ++q) R.mod[q] = (uint32_t)pl->mod[q];
+        R.amaxA = amaxA; R.amaxB = amaxB;
+        R.C = C; R.ldc = ldc;
+        R.alpha[0] = alpha[0]; R.alpha[1] = alpha[1];
+        R.beta[0] = beta[0]; R.beta[1] = beta[1];
+        R.t = t; R.s = s; R.chat = chat;
+        OZ2_LAUNCH(launch_reconstruct(R, pl->NL, cplx, !beta_zero, stm));
+    }
+    if (h->timing) {
+        OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
+        h->timed = true;
+    }
+    L.valid = true;
+    h->last = L;
+    return OZ2_STATUS_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oz2_create(oz2_handle_t* out) {
+    if (!out) return -1;
+    *out = nullptr;
+    oz2_context* h = new (std::nothrow) oz2_context();
+    if (!h) return OZ2_STATUS_ALLOC_FAILED;
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return OZ2_STATUS_HIP_ERROR;
+    }
+    for (auto& e : h->ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            delete h;
+            return OZ2_STATUS_HIP_ERROR;
+        }
+    }
+    *out = h;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_destroy(oz2_handle_t h) {
+    if (!h) return -1;
+    (void)hipStreamSynchronize(h->stream);
+    if (h->ws) (void)hipFree(h->ws);
+    for (auto& e : h->ev)
+        if (e) (void)hipEventDestroy(e);
+    delete h;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_set_stream(oz2_handle_t h, void* stream) {
+    if (!h) return -1;
+    h->stream = (hipStream_t)stream;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_set_memory_limit(oz2_handle_t h, size_t bytes) {
+    if (!h) return -1;
+    h->mem_limit = bytes;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_get_workspace_size(oz2_handle_t h, size_t* bytes) {
+    if (!h) return -1;
+    if (!bytes) return -2;
+    *bytes = h->ws_size;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_set_timing(oz2_handle_t h, int enable) {
+    if (!h) return -1;
+    h->timing = enable ? 1 : 0;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_get_phase_times(oz2_handle_t h, float ms[4]) {
+    if (!h) return -1;
+    if (!ms) return -2;
+    if (!h->timed) {
+        for (int i = 0; i < 4; ++i) ms[i] = 0.0f;
+        return OZ2_STATUS_SUCCESS;
+    }
+    if (hipEventSynchronize(h->ev[4]) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
+    for (int i = 0; i < 4; ++i)
+        if (hipEventElapsedTime(&ms[i], h->ev[i], h->ev[i + 1]) != hipSuccess)
+            return OZ2_STATUS_HIP_ERROR;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_moduli_for_bits(int64_t k, int bits, int is_complex) {
+    for (int s = kMinS; s <= kMaxS; ++s) {
+        const ModuliPlan* pl = moduli_plan(s);
+        if (scaling_width(*pl, k, is_complex != 0) >= bits) return s;
+    }
+    return kMaxS;
+}
+
+int oz2_plan_info(int num_moduli, int64_t k, int is_complex, int32_t* moduli_out, int* t_out,
+                  int* nl_out, double* log2M_out) {
+    const ModuliPlan* pl = moduli_plan(num_moduli);
+    if (!pl) return -1;
+    if (moduli_out)
+        for (int q = 0; q < kMaxS; ++q) moduli_out[q] = q < pl->s ? pl->mod[q] : 0;
+    if (t_out) *t_out = scaling_width(*pl, k, is_complex != 0);
+    if (nl_out) *nl_out = pl->NL;
+    if (log2M_out) *log2M_out = pl->log2M;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_dgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
+              double alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
+              double beta, double* C, int64_t ldc, int num_moduli) {
+    const double al[2] = {alpha, 0.0}, be[2] = {beta, 0.0};
+    return gemm_impl(h, false, transa, transb, m, n, k, al, A, lda, B, ldb, be, C, ldc, num_moduli);
+}
+
+int oz2_zgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
+              const double* alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
+              const double* beta, double* C, int64_t ldc, int num_moduli) {
+    if (!alpha) return -7;
+    if (!beta) return -12;
+    return gemm_impl(h, true, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc,
+                     num_moduli);
+}
+
+int oz2_dgemm_strided_batched(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n,
+                              int64_t k, double alpha, const double* A, int64_t lda,
+                              int64_t strideA, const double* B, int64_t ldb, int64_t strideB,
+                              double beta, double* C, int64_t ldc, int64_t strideC,
+                              int64_t batch, int num_moduli) {
+    if (batch < 0) return -18;
+    if (strideA < 0) return -10;
+    if (strideB < 0) return -13;
+    if (strideC < 0) return -17;
+    const double al[2] = {alpha, 0.0}, be[2] = {beta, 0.0};
+    for (int64_t b = 0; b < batch; ++b) {
+        int st = gemm_impl(h, false, transa, transb, m, n, k, al, A ? A + b * strideA : nullptr,
+                           lda, B ? B + b * strideB : nullptr, ldb, be,
+                           C ? C + b * strideC : nullptr, ldc, num_moduli);
+        if (st) return st;
+    }
+    return OZ2_STATUS_SUCCESS;
+}
+
+const char* oz2_status_string(int status) {
+    switch (status) {
+        case OZ2_STATUS_SUCCESS: return "success";
+        case OZ2_STATUS_ALLOC_FAILED: return "device workspace allocation failed";
+        case OZ2_STATUS_HIP_ERROR: return "HIP runtime error";
+        case OZ2_STATUS_RANGE: return "no scaling width t >= 1 for this number of moduli and k";
+        case OZ2_STATUS_WORKSPACE_LIMIT: return "workspace would exceed the memory limit";
+        case OZ2_STATUS_NOT_SUPPORTED: return "not supported on this device";
+        case OZ2_STATUS_INTERNAL: return "internal error";
+        default: return status < 0 ? "invalid argument" : "unknown status";
+    }
+}
+
+int oz2_set_debug(oz2_handle_t h, int debug) {
+    if (!h) return -1;
+    h->debug = debug ? 1 : 0;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_debug_copy(oz2_handle_t h, int which, void* dst, size_t capacity, size_t* bytes,
+                   int64_t dims[5]) {
+    if (!h) return -1;
+    const Layout& L = h->last;
+    if (!L.valid) return OZ2_STATUS_INTERNAL;
+    size_t off = 0, nbytes = 0;
+    int64_t d[5] = {1, 1, 1, 1, 1};
+    switch (which) {
+        case 0: off = L.off_amaxA; nbytes = 8 * (size_t)L.mp; d[2] = L.mp; break;
+        case 1: off = L.off_amaxB; nbytes = 8 * (size_t)L.np; d[2] = L.np; break;
+        case 2: off = L.off_pa; nbytes = L.bytes_pa;
+            d[0] = L.sets; d[1] = L.s; d[2] = L.mp; d[3] = L.kp; break;
+        case 3: off = L.off_pb; nbytes = L.bytes_pb;
+            d[0] = L.sets; d[1] = L.s; d[2] = L.np; d[3] = L.kp; break;
+        case 4: off = L.off_res; nbytes = L.bytes_res;
+            d[0] = L.outs; d[1] = L.s; d[2] = L.n; d[3] = L.mp; d[4] = L.chunks; break;
+        case 5: off = L.off_chat; nbytes = L.bytes_chat;
+            d[0] = L.outs; d[2] = L.n; d[3] = L.mp; d[4] = L.NL; break;
+        default: return -2;
+    }
+    if (bytes) *bytes = nbytes;
+    if (dims)
+        for (int i = 0; i < 5; ++i) dims[i] = d[i];
+    if (!dst) return OZ2_STATUS_SUCCESS;
+    if (capacity < nbytes) return -4;
+    if (hipStreamSynchronize(h->stream) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
+    if (nbytes && hipMemcpy(dst, (char*)h->ws + off, nbytes, hipMemcpyDeviceToHost) != hipSuccess)
+        return OZ2_STATUS_HIP_ERROR;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_test_crt(oz2_handle_t h, int64_t count, int num_moduli, const uint8_t* residues,
+                 uint32_t* words) {
+    if (!h) return -1;
+    if (count < 0) return -2;
+    const ModuliPlan* pl = moduli_plan(num_moduli);
+    if (!pl) return -3;
+    if (count == 0) return OZ2_STATUS_SUCCESS;
+    if (!residues) return -4;
+    if (!words) return -5;
+    CrtTestParams P{};
+    fill_crt_tables(*pl, &P);
+    P.R = residues; P.count = count; P.words = words; P.s = num_moduli;
+    OZ2_LAUNCH(launch_crt_test(P, pl->NL, h->stream));
+    return OZ2_STATUS_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// oz2_internal.h -- kernel parameter blocks and launchers shared by the
+// C-ABI layer (oz2_api.cpp) and the device code (oz2_kernels.hip,
+// oz2_gemm.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "oz2_plan.h"
+
+namespace oz2 {
+
+// Residue planes of op(A) and op(B) are int8 [sets][s][rows_pad][k_pad],
+// every row (a row of op(A) or a column of op(B)) k-contiguous and padded
+// with zeros; sets = 1 (real) or 3 (complex: re, im, re+im).
+// Product residues are uint8 [outs][s][n][m_pad] holding values in [0, m_t)
+// (outs = 1 real, 2 complex: Re, Im), i.e. column-major like C.
+constexpr int kPadM = 256;   // row padding of the A planes / product planes
+constexpr int kPadK = 64;    // k padding of the planes (the GEMM k step)
+
+// Vector layout of an operand as seen by scan/encode: vector v (a row of
+// op(A) or a column of op(B)) has element p at X[v*ld + p] when contiguous,
+// at X[v + p*ld] otherwise (complex: in units of complex128).
+struct ScanParams {
+    const double* X;
+    int64_t ld;
+    int64_t nvec;
+    int64_t k;
+    int64_t pchunk;     // strided scan: p-range per block
+    uint64_t* amax;     // bit pattern of max |x| (sign cleared) per vector
+};
+
+struct EncodeParams {
+    const double* X;
+    int64_t ld;
+    int64_t nvec, k;         // logical sizes
+    int64_t vpad, kpad;      // plane row count and row length
+    int64_t set_stride;      // bytes between the sets of planes
+    const uint64_t* amax;
+    int8_t* planes;
+    int conj;                // negate imaginary parts (op = 'C')
+    int t, s;
+    uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS];
+    uint32_t c[kMaxS][kExtLimbs];
+};
+
+struct GemmParams {
+    const int8_t* A;   // planes of op(A): [sets][s][mp][kp]
+    const int8_t* B;   // planes of op(B): [sets][s][np][kp]
+    uint8_t* C;        // [outs][s][n][mp]
+    int64_t mp, np, kp, n;
+    int64_t a_set_stride, b_set_stride, c_set_stride;  // bytes
+    int s;
+    int tiles_m, tiles_n;
+    int64_t k_begin;   // first k position of this launch (multiple of 64)
+    int k_steps;       // 64-wide k steps of this launch: <= 2047 keeps INT32 exact
+    uint32_t mod[kMaxS], barrett[kMaxS], bias[kMaxS];
+};
+
+struct ReconParams {
+    const uint8_t* R;       // product residues [chunks][outs][s][n][mp]
+    int64_t mp, m, n;
+    int64_t r_set_stride;   // bytes between Re and Im residues
+    int64_t r_chunk_stride; // bytes between the residues of successive k runs
+    int chunks;             // k runs whose residues are summed mod m_t
+    const uint64_t* amaxA;
+    const uint64_t* amaxB;
+    double* C;
+    int64_t ldc;
+    double alpha[2], beta[2];
+    int t, s;
+    uint32_t* chat;         // optional debug copy of c_hat words [outs][n][mp][NL]
+    float finv[kMaxS];
+    uint32_t W16[kMaxS][kMaxLimb16];
+    uint32_t M16[kMaxLimb16];
+    uint32_t mod[kMaxS];
+};
+
+struct CrtTestParams {
+    const uint8_t* R;  // [s][count]
+    int64_t count;
+    uint32_t* words;   // [count][NL]
+    int s;
+    float finv[kMaxS];
+    uint32_t W16[kMaxS][kMaxLimb16];
+    uint32_t M16[kMaxLimb16];
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_fill_u64(uint64_t* p, int64_t n, uint64_t value, hipStream_t st);
+hipError_t launch_scan(const ScanParams& P, bool contiguous, bool cplx, hipStream_t st);
+hipError_t launch_encode(const EncodeParams& P, bool contiguous, bool cplx, bool ext,
+                         hipStream_t st);
+hipError_t launch_residue_gemm(const GemmParams& P, bool cplx, hipStream_t st);
+hipError_t launch_reconstruct(const ReconParams& P, int NL, bool cplx, bool beta_nonzero,
+                              hipStream_t st);
+hipError_t launch_scale_c(double* C, int64_t m, int64_t n, int64_t ldc, const double beta[2],
+                          bool cplx, hipStream_t st);
+hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st);
+
+}  // namespace oz2

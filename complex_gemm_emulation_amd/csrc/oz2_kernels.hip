@@ -1,0 +1,610 @@
+// oz2_kernels.hip -- memory-bound phases of Ozaki scheme II on gfx950:
+// row/column exponent scan, integer-only residue encoder, CRT reconstruction
+// with the alpha/beta epilogue.
+//
+// Method: "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc
+// GPUs: Ozaki Scheme II on the Xe2 Architecture":
+//   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scan + scale_of()
+//   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
+//   Sec. 4.2  residues from 21-bit limbs of a_hat + 2^62 with precomputed
+//             2^(21 l) mod m and K_m = (h_m - 2^62) mod m; no FP64 and no
+//             branches per modulus                 -> encode_kernel
+//   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
+//             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
+//             top 64 bits + sticky rounded once to double, times
+//             2^(-D_i-E_j)                         -> reconstruct_kernel
+//   Sec. 5    ZGEMM: residues of re, im and re+im; Re and Im reconstructed
+//   Sec. 8.1  non-finite row/column -> NaN row/column
+// Compiled with -ffp-contract=off: the alpha/beta epilogue is evaluated
+// exactly as written, every operation rounded separately.
+#include "oz2_internal.h"
+
+namespace oz2 {
+namespace {
+
+constexpr uint64_t kAbsMask = 0x7FFFFFFFFFFFFFFFull;
+constexpr uint64_t kInfBits = 0x7FF0000000000000ull;
+
+__device__ __forceinline__ uint64_t abs_bits(double x) {
+    return (uint64_t)__double_as_longlong(x) & kAbsMask;
+}
+
+// e(x) with 2^(e-1) <= x < 2^e for a positive finite double given by its bits
+__device__ __forceinline__ int frexp_exp_bits(uint64_t b) {
+    int eb = (int)(b >> 52);
+    return eb ? eb - 1022 : (64 - __clzll((long long)b)) - 1074;
+}
+
+// D = t - e(amax); 0 for an all-zero vector; `bad` for a non-finite one
+__device__ __forceinline__ int scale_of(uint64_t amax, int t, bool& bad) {
+    bad = amax >= kInfBits;
+    return (bad || amax == 0) ? 0 : t - frexp_exp_bits(amax);
+}
+
+// |rint(a 2^D)| for |a 2^D| < 2^61 (the standard width, t <= 61)
+__device__ __forceinline__ uint64_t rint_scaled_mag64(uint64_t bits, int D) {
+    const int eb = (int)((bits >> 52) & 0x7ff);
+    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
+    const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
+    const int sh = (eb ? eb - 1075 : -1074) + D;
+    if (sh >= 0) return sig << sh;
+    const int n = -sh;
+    if (n > 63) return 0;
+    const uint64_t q = sig >> n;
+    const uint64_t rem = sig & ((1ull << n) - 1);
+    const uint64_t half = 1ull << (n - 1);
+    return q + (uint64_t)((rem > half) | ((rem == half) & (uint32_t)(q & 1)));
+}
+
+// |rint(a 2^D)| for |a 2^D| < 2^100 (the extended width)
+__device__ __forceinline__ unsigned __int128 rint_scaled_mag128(uint64_t bits, int D) {
+    const int eb = (int)((bits >> 52) & 0x7ff);
+    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
+    const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
+    const int sh = (eb ? eb - 1075 : -1074) + D;
+    if (sh >= 0) return (unsigned __int128)sig << sh;
+    return (unsigned __int128)rint_scaled_mag64(bits, D);
+}
+
+// v mod m for v < 2^32 with q = floor(v R / 2^32), R = floor(2^32 / m):
+// q is floor(v/m) or one less, so r = v - q m lies in [0, 2m)
+__device__ __forceinline__ uint32_t mod_small(uint32_t v, uint32_t m, uint32_t R) {
+    const uint32_t q = __umulhi(v, R);
+    const uint32_t r = v - __umul24(q, m);  // q < 2^24: v/m < 5 * 2^21 + 1
+    const uint32_t r2 = r - m;
+    return r < r2 ? r : r2;
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
+}
+
+// ------------------------------------------------------------------ fill
+__global__ void fill_u64_kernel(uint64_t* p, int64_t n, uint64_t v) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// ------------------------------------------------------------------ scan
+// One wavefront per vector whose elements are contiguous.
+template <bool CPLX>
+__global__ __launch_bounds__(256) void scan_contig_kernel(ScanParams P) {
+    const int lane = threadIdx.x & 63;
+    const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (v >= P.nvec) return;
+    constexpr int W = CPLX ? 2 : 1;
+    const int64_t len = P.k * W;
+    const double* x = P.X + v * P.ld * W;
+    uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+    int64_t p = lane;
+    for (; p + 192 < len; p += 256) {
+        m0 = max(m0, abs_bits(x[p]));
+        m1 = max(m1, abs_bits(x[p + 64]));
+        m2 = max(m2, abs_bits(x[p + 128]));
+        m3 = max(m3, abs_bits(x[p + 192]));
+    }
+    for (; p < len; p += 64) m0 = max(m0, abs_bits(x[p]));
+    unsigned long long mx = max(max(m0, m1), max(m2, m3));
+    for (int off = 32; off >= 1; off >>= 1) {
+        unsigned long long o = __shfl_xor(mx, off);
+        mx = mx > o ? mx : o;
+    }
+    if (lane == 0) P.amax[v] = mx;
+}
+
+// One thread per vector whose elements are strided (a wavefront reads 64
+// consecutive vectors at one p, coalesced); the p range is split across
+// blocks and combined with an atomic max on the zero-filled output.
+template <bool CPLX>
+__global__ __launch_bounds__(256) void scan_strided_kernel(ScanParams P) {
+    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (v >= P.nvec) return;
+    const int64_t p0 = (int64_t)blockIdx.y * P.pchunk;
+    const int64_t p1 = min(P.k, p0 + P.pchunk);
+    uint64_t mx = 0;
+    for (int64_t p = p0; p < p1; ++p) {
+        if (CPLX) {
+            const double* z = P.X + 2 * (v + p * P.ld);
+            mx = max(mx, max(abs_bits(z[0]), abs_bits(z[1])));
+        } else {
+            mx = max(mx, abs_bits(P.X[v + p * P.ld]));
+        }
+    }
+    if (mx) atomicMax((unsigned long long*)&P.amax[v], (unsigned long long)mx);
+}
+
+// ---------------------------------------------------------------- encode
+// A block encodes a tile of TV vectors x 64 k-positions.  Every thread owns
+// groups of 4 consecutive k-positions of one vector, so that each modulus
+// costs one 32-bit store per group; a wavefront writes 4 rows x 64 bytes of
+// each plane.  Strided operands are transposed through LDS first.
+template <bool CPLX>
+struct EncodeTile {
+    static constexpr int TV = CPLX ? 32 : 64;   // vectors per tile
+    static constexpr int TP = 64;               // k positions per tile
+    static constexpr int GROUPS = TV * TP / 4;  // 4-element groups
+    static constexpr int PER_THREAD = GROUPS / 256;
+};
+
+// residue limbs of one element: 21-bit limbs of a_hat + 2^62 (standard)
+// or a_hat + 2^104 (extended); sign handled by the bias
+template <bool EXT>
+struct Limbs {
+    uint32_t u[EXT ? kExtLimbs : kStdLimbs];
+};
+
+template <bool EXT>
+__device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
+    Limbs<EXT> L;
+    const uint64_t bits = (uint64_t)__double_as_longlong(a);
+    const bool neg = (bits >> 63) != 0;
+    if (!EXT) {
+        uint64_t mag = zero ? 0 : rint_scaled_mag64(bits, D);
+        uint64_t x = neg ? (1ull << 62) - mag : (1ull << 62) + mag;
+        L.u[0] = (uint32_t)(x & 0x1FFFFF);
+        L.u[1] = (uint32_t)((x >> 21) & 0x1FFFFF);
+        L.u[2] = (uint32_t)(x >> 42);
+    } else {
+        unsigned __int128 mag = zero ? 0 : rint_scaled_mag128(bits, D);
+        const unsigned __int128 bias = (unsigned __int128)1 << 104;
+        unsigned __int128 x = neg ? bias - mag : bias + mag;
+        const uint64_t lo = (uint64_t)x, hi = (uint64_t)(x >> 64);
+        L.u[0] = (uint32_t)(lo & 0x1FFFFF);
+        L.u[1] = (uint32_t)((lo >> 21) & 0x1FFFFF);
+        L.u[2] = (uint32_t)((lo >> 42) & 0x1FFFFF);
+        L.u[3] = (uint32_t)(((lo >> 63) | (hi << 1)) & 0x1FFFFF);
+        L.u[4] = (uint32_t)((hi >> 20) & 0x1FFFFF);
+    }
+    return L;
+}
+
+// (a_hat + h) mod m in [0, m), before removing the offset h
+template <bool EXT>
+__device__ __forceinline__ uint32_t residue_off(const Limbs<EXT>& L, const EncodeParams& P, int t) {
+    uint32_t v = P.K[t];
+    v += __umul24(L.u[0], P.c[t][0]);
+    v += __umul24(L.u[1], P.c[t][1]);
+    v += __umul24(L.u[2], P.c[t][2]);
+    if (EXT) {
+        v += __umul24(L.u[3], P.c[t][3]);
+        v += __umul24(L.u[4], P.c[t][4]);
+    }
+    return mod_small(v, P.mod[t], P.barrett[t]);
+}
+
+template <bool CONTIG, bool CPLX, bool EXT>
+__global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
+    using T = EncodeTile<CPLX>;
+    const int tid = threadIdx.x;
+    const int64_t tiles_p = P.kpad / T::TP;
+    const int64_t tp = blockIdx.x % tiles_p;
+    const int64_t tv = blockIdx.x / tiles_p;
+    const int64_t v0 = tv * T::TV, p0 = tp * T::TP;
+    constexpr int W = CPLX ? 2 : 1;
+
+    // strided operands: transpose the tile through LDS (re and im planes)
+    __shared__ double tile[CONTIG ? 1 : W][CONTIG ? 1 : T::TV][CONTIG ? 1 : T::TP + 1];
+    if (!CONTIG) {
+        constexpr int ROWS_PER_PASS = 256 / T::TV;
+#pragma unroll
+        for (int j = 0; j < T::TP / ROWS_PER_PASS; ++j) {
+            const int v = tid % T::TV;
+            const int p = tid / T::TV + ROWS_PER_PASS * j;
+            const int64_t gv = v0 + v, gp = p0 + p;
+            double re = 0.0, im = 0.0;
+            if (gv < P.nvec && gp < P.k) {
+                const double* src = P.X + W * (gv + gp * P.ld);
+                re = src[0];
+                if (CPLX) im = src[1];
+            }
+            tile[0][v][p] = re;
+            if (CPLX) tile[W - 1][v][p] = im;
+        }
+        __syncthreads();
+    }
+
+    const int64_t plane = P.vpad * P.kpad;
+#pragma unroll
+    for (int g = 0; g < T::PER_THREAD; ++g) {
+        const int grp = tid + 256 * g;
+        const int v = grp / (T::TP / 4);
+        const int p4 = (grp % (T::TP / 4)) * 4;
+        const int64_t gv = v0 + v;
+        double xr[4], xi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (CONTIG) {
+                const int64_t gp = p0 + p4 + e;
+                xr[e] = 0.0;
+                xi[e] = 0.0;
+                if (gv < P.nvec && gp < P.k) {
+                    const double* src = P.X + W * (gv * P.ld + gp);
+                    xr[e] = src[0];
+                    if (CPLX) xi[e] = src[1];
+                }
+            } else {
+                xr[e] = tile[0][v][p4 + e];
+                xi[e] = CPLX ? tile[W - 1][v][p4 + e] : 0.0;
+            }
+            if (CPLX && P.conj) xi[e] = -xi[e];
+        }
+        bool bad;
+        const int D = scale_of(gv < P.nvec ? P.amax[gv] : 0ull, P.t, bad);
+        Limbs<EXT> lr[4], li[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            lr[e] = make_limbs<EXT>(xr[e], D, bad);
+            if (CPLX) li[e] = make_limbs<EXT>(xi[e], D, bad);
+        }
+        int8_t* dst = P.planes + gv * P.kpad + p0 + p4;
+        for (int t = 0; t < P.s; ++t) {
+            const uint32_t h = P.h[t];
+            uint32_t r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = residue_off<EXT>(lr[e], P, t);
+            *(uint32_t*)(dst + t * plane) = pack4(r[0] - h, r[1] - h, r[2] - h, r[3] - h);
+            if (CPLX) {
+                const uint32_t m = P.mod[t];
+                uint32_t ri[4], rs[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ri[e] = residue_off<EXT>(li[e], P, t);
+                    // (re + im + h) mod m from (re + h) mod m and (im + h) mod m
+                    uint32_t x = r[e] + ri[e] + (m - h);  // < 3m
+                    uint32_t x1 = x - m;
+                    x = x < x1 ? x : x1;
+                    x1 = x - m;
+                    rs[e] = x < x1 ? x : x1;
+                }
+                *(uint32_t*)(dst + P.set_stride + t * plane) =
+                    pack4(ri[0] - h, ri[1] - h, ri[2] - h, ri[3] - h);
+                *(uint32_t*)(dst + 2 * P.set_stride + t * plane) =
+                    pack4(rs[0] - h, rs[1] - h, rs[2] - h, rs[3] - h);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ reconstruct
+// bytewise (a + b) mod m of four residues in [0, m)
+__device__ __forceinline__ uint32_t add_mod_bytes(uint32_t a, uint32_t b, uint32_t m) {
+    uint32_t out = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t x = ((a >> (8 * e)) & 0xffu) + ((b >> (8 * e)) & 0xffu);
+        const uint32_t x1 = x - m;
+        out |= (x < x1 ? x : x1) << (8 * e);
+    }
+    return out;
+}
+
+// c_hat from the residues of one entry, accumulated over the moduli
+template <int NL>
+struct Crt {
+    static constexpr int L16 = 2 * NL;
+    float z;
+    int32_t L[L16];
+    __device__ __forceinline__ void init() {
+        z = 0.0f;
+#pragma unroll
+        for (int l = 0; l < L16; ++l) L[l] = 0;
+    }
+    // r in [0, m_t): every term r * W16 < 2^8 * 2^16, 24 terms < 2^29
+    __device__ __forceinline__ void add(uint32_t r, float finv, const uint32_t* W) {
+        z = __builtin_fmaf((float)r, finv, z);
+#pragma unroll
+        for (int l = 0; l < L16; ++l) L[l] += (int32_t)__umul24(r, W[l]);
+    }
+    // c_hat = Z - q M mod 2^(32 NL), two's complement words
+    __device__ __forceinline__ void finish(const uint32_t* M16, uint32_t w[NL]) {
+        const int32_t q = (int32_t)__builtin_rintf(z);  // |z - Z/M| < 2^-6, Z/M within 1/4 of q
+        int32_t carry = 0;
+        uint32_t d[L16];
+#pragma unroll
+        for (int l = 0; l < L16; ++l) {
+            const int32_t c = L[l] - q * (int32_t)M16[l] + carry;
+            d[l] = (uint32_t)c & 0xffffu;
+            carry = c >> 16;
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) w[i] = d[2 * i] | (d[2 * i + 1] << 16);
+    }
+};
+
+// RN(c * 2^-S) of a two's-complement integer c given by NL 32-bit words:
+// the top 64 bits below the leading one OR-ed with a sticky bit of the rest,
+// converted once with round-to-nearest-even, then scaled by a power of two
+// (a second rounding only when the result is subnormal).
+template <int NL>
+__device__ __forceinline__ double words_to_double(uint32_t w[NL], int S) {
+    const bool neg = (w[NL - 1] >> 31) != 0;
+    if (neg) {
+        uint32_t carry = 1;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint32_t x = ~w[i] + carry;
+            carry = carry & (x == 0 ? 1u : 0u);
+            w[i] = x;
+        }
+    }
+    int top = -1;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        if (w[i]) top = i;
+    if (top < 0) return 0.0;
+    uint32_t x3 = 0, x2 = 0, x1 = 0, x0 = 0, below = 0;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        if (i == top) x3 = w[i];
+        if (i == top - 1) x2 = w[i];
+        if (i == top - 2) x1 = w[i];
+        if (i == top - 3) x0 = w[i];
+        if (i < top - 3) below |= w[i];
+    }
+    const int lz = __clz((int)x3);
+    uint64_t hi = ((uint64_t)x3 << 32) | x2;
+    uint64_t lo = ((uint64_t)x1 << 32) | x0;
+    uint64_t win = hi, rest = lo;
+    if (lz) {
+        win = (hi << lz) | (lo >> (64 - lz));
+        rest = lo << lz;
+    }
+    win |= (uint64_t)((rest | below) != 0);
+    // u64 -> double with a single rounding: hi*2^32 is exact, the FMA rounds once
+    const double dh = (double)(uint32_t)(win >> 32);
+    const double dl = (double)(uint32_t)win;
+    const double d = __builtin_fma(dh, 4294967296.0, dl);
+    const int e2 = 32 * top + 31 - lz - 63 - S;
+    const double r = __builtin_ldexp(d, e2);
+    return neg ? -r : r;
+}
+
+template <int NL, bool CPLX, bool BETA>
+__global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
+    const int64_t groups_per_col = P.mp / 4;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t j = gid / groups_per_col;
+    const int64_t i0 = (gid % groups_per_col) * 4;
+    if (j >= P.n || i0 >= P.m) return;
+
+    Crt<NL> acc[CPLX ? 2 : 1][4];
+#pragma unroll
+    for (int o = 0; o < (CPLX ? 2 : 1); ++o)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[o][e].init();
+
+    const int64_t plane = P.n * P.mp;
+    const uint8_t* src = P.R + j * P.mp + i0;
+    for (int t = 0; t < P.s; ++t) {
+        const float fi = P.finv[t];
+        const uint32_t* W = P.W16[t];
+#pragma unroll
+        for (int o = 0; o < (CPLX ? 2 : 1); ++o) {
+            const uint8_t* at = src + o * P.r_set_stride + t * plane;
+            uint32_t rw = *(const uint32_t*)at;
+            // residues of the k runs (Arc page Sec. 4.3) are summed mod m_t
+            for (int c = 1; c < P.chunks; ++c)
+                rw = add_mod_bytes(rw, *(const uint32_t*)(at + c * P.r_chunk_stride), P.mod[t]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[o][e].add((rw >> (8 * e)) & 0xffu, fi, W);
+        }
+    }
+
+    bool badB;
+    const int E = scale_of(P.amaxB[j], P.t, badB);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t i = i0 + e;
+        if (i >= P.m) break;
+        bool badA;
+        const int D = scale_of(P.amaxA[i], P.t, badA);
+        double x[2];
+#pragma unroll
+        for (int o = 0; o < (CPLX ? 2 : 1); ++o) {
+            uint32_t w[NL];
+            acc[o][e].finish(P.M16, w);
+            if (P.chat) {
+                uint32_t* dst = P.chat + (((int64_t)o * P.n + j) * P.mp + i) * NL;
+#pragma unroll
+                for (int q = 0; q < NL; ++q) dst[q] = w[q];
+            }
+            x[o] = words_to_double<NL>(w, D + E);
+            if (badA || badB) x[o] = __builtin_nan("");
+        }
+        double* c = P.C + (CPLX ? 2 : 1) * (i + j * P.ldc);
+        if (!CPLX) {
+            const double t1 = P.alpha[0] * x[0];
+            if (BETA) {
+                const double t2 = P.beta[0] * c[0];
+                c[0] = t1 + t2;
+            } else {
+                c[0] = t1;
+            }
+        } else {
+            const double ar = P.alpha[0], ai = P.alpha[1];
+            const double t1 = ar * x[0], t2 = ai * x[1];
+            const double ure = t1 - t2;
+            const double t3 = ar * x[1], t4 = ai * x[0];
+            const double uim = t3 + t4;
+            if (BETA) {
+                const double br = P.beta[0], bi = P.beta[1];
+                const double cr = c[0], ci = c[1];
+                const double t5 = br * cr, t6 = bi * ci;
+                const double vre = t5 - t6;
+                const double t7 = br * ci, t8 = bi * cr;
+                const double vim = t7 + t8;
+                c[0] = ure + vre;
+                c[1] = uim + vim;
+            } else {
+                c[0] = ure;
+                c[1] = uim;
+            }
+        }
+    }
+}
+
+template <int NL>
+__global__ __launch_bounds__(256) void crt_test_kernel(CrtTestParams P) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= P.count) return;
+    Crt<NL> acc;
+    acc.init();
+    for (int t = 0; t < P.s; ++t) acc.add(P.R[t * P.count + q], P.finv[t], P.W16[t]);
+    uint32_t w[NL];
+    acc.finish(P.M16, w);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) P.words[q * NL + i] = w[i];
+}
+
+// C <- beta C (BLAS quick return for alpha = 0 or k = 0); C not read if beta = 0
+template <bool CPLX>
+__global__ __launch_bounds__(256) void scale_c_kernel(double* C, int64_t m, int64_t n, int64_t ldc,
+                                                      double br, double bi) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= m * n) return;
+    const int64_t i = gid % m, j = gid / m;
+    double* c = C + (CPLX ? 2 : 1) * (i + j * ldc);
+    const bool zero = (br == 0.0 && bi == 0.0);
+    if (!CPLX) {
+        c[0] = zero ? 0.0 : br * c[0];
+    } else if (zero) {
+        c[0] = 0.0;
+        c[1] = 0.0;
+    } else {
+        const double cr = c[0], ci = c[1];
+        const double t3 = br * cr, t4 = bi * ci;
+        const double t5 = br * ci, t6 = bi * cr;
+        c[0] = t3 - t4;
+        c[1] = t5 + t6;
+    }
+}
+
+int64_t blocks_for(int64_t n, int64_t per) { return (n + per - 1) / per; }
+
+}  // namespace
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_fill_u64(uint64_t* p, int64_t n, uint64_t value, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t nb = blocks_for(n, 256);
+    if (nb > 4096) nb = 4096;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3((unsigned)nb), dim3(256), 0, st, p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const ScanParams& P, bool contiguous, bool cplx, hipStream_t st) {
+    if (P.nvec <= 0 || P.k <= 0) return hipSuccess;
+    if (contiguous) {
+        dim3 grid((unsigned)blocks_for(P.nvec, 4));
+        if (cplx)
+            hipLaunchKernelGGL(scan_contig_kernel<true>, grid, dim3(256), 0, st, P);
+        else
+            hipLaunchKernelGGL(scan_contig_kernel<false>, grid, dim3(256), 0, st, P);
+    } else {
+        dim3 grid((unsigned)blocks_for(P.nvec, 256), (unsigned)blocks_for(P.k, P.pchunk));
+        if (cplx)
+            hipLaunchKernelGGL(scan_strided_kernel<true>, grid, dim3(256), 0, st, P);
+        else
+            hipLaunchKernelGGL(scan_strided_kernel<false>, grid, dim3(256), 0, st, P);
+    }
+    return hipGetLastError();
+}
+
+template <bool CONTIG, bool CPLX, bool EXT>
+static hipError_t encode_go(const EncodeParams& P, hipStream_t st) {
+    using T = EncodeTile<CPLX>;
+    const int64_t nb = (P.vpad / T::TV) * (P.kpad / T::TP);
+    hipLaunchKernelGGL((encode_kernel<CONTIG, CPLX, EXT>), dim3((unsigned)nb), dim3(256), 0, st, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeParams& P, bool contiguous, bool cplx, bool ext,
+                         hipStream_t st) {
+    if (P.vpad % 64 || P.kpad % 64) return hipErrorInvalidValue;
+    const int idx = (contiguous ? 4 : 0) | (cplx ? 2 : 0) | (ext ? 1 : 0);
+    switch (idx) {
+        case 0: return encode_go<false, false, false>(P, st);
+        case 1: return encode_go<false, false, true>(P, st);
+        case 2: return encode_go<false, true, false>(P, st);
+        case 3: return encode_go<false, true, true>(P, st);
+        case 4: return encode_go<true, false, false>(P, st);
+        case 5: return encode_go<true, false, true>(P, st);
+        case 6: return encode_go<true, true, false>(P, st);
+        default: return encode_go<true, true, true>(P, st);
+    }
+}
+
+template <int NL>
+static hipError_t recon_go(const ReconParams& P, bool cplx, bool beta, hipStream_t st) {
+    const int64_t nb = blocks_for((P.mp / 4) * P.n, 256);
+    dim3 g((unsigned)nb), b(256);
+    if (cplx) {
+        if (beta) hipLaunchKernelGGL((reconstruct_kernel<NL, true, true>), g, b, 0, st, P);
+        else hipLaunchKernelGGL((reconstruct_kernel<NL, true, false>), g, b, 0, st, P);
+    } else {
+        if (beta) hipLaunchKernelGGL((reconstruct_kernel<NL, false, true>), g, b, 0, st, P);
+        else hipLaunchKernelGGL((reconstruct_kernel<NL, false, false>), g, b, 0, st, P);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_reconstruct(const ReconParams& P, int NL, bool cplx, bool beta_nonzero,
+                              hipStream_t st) {
+    if (P.mp % 4) return hipErrorInvalidValue;
+    switch (NL) {
+        case 2: return recon_go<2>(P, cplx, beta_nonzero, st);
+        case 3: return recon_go<3>(P, cplx, beta_nonzero, st);
+        case 4: return recon_go<4>(P, cplx, beta_nonzero, st);
+        case 5: return recon_go<5>(P, cplx, beta_nonzero, st);
+        case 6: return recon_go<6>(P, cplx, beta_nonzero, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_scale_c(double* C, int64_t m, int64_t n, int64_t ldc, const double beta[2],
+                          bool cplx, hipStream_t st) {
+    if (m <= 0 || n <= 0) return hipSuccess;
+    dim3 g((unsigned)blocks_for(m * n, 256));
+    if (cplx)
+        hipLaunchKernelGGL(scale_c_kernel<true>, g, dim3(256), 0, st, C, m, n, ldc, beta[0], beta[1]);
+    else
+        hipLaunchKernelGGL(scale_c_kernel<false>, g, dim3(256), 0, st, C, m, n, ldc, beta[0], 0.0);
+    return hipGetLastError();
+}
+
+hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st) {
+    if (P.count <= 0) return hipSuccess;
+    dim3 g((unsigned)blocks_for(P.count, 256));
+    switch (NL) {
+        case 2: hipLaunchKernelGGL(crt_test_kernel<2>, g, dim3(256), 0, st, P); break;
+        case 3: hipLaunchKernelGGL(crt_test_kernel<3>, g, dim3(256), 0, st, P); break;
+        case 4: hipLaunchKernelGGL(crt_test_kernel<4>, g, dim3(256), 0, st, P); break;
+        case 5: hipLaunchKernelGGL(crt_test_kernel<5>, g, dim3(256), 0, st, P); break;
+        case 6: hipLaunchKernelGGL(crt_test_kernel<6>, g, dim3(256), 0, st, P); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace oz2

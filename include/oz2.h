@@ -1,0 +1,177 @@
+/*
+ * oz2.h -- C ABI of the oz2 library: FP64 real and complex matrix products
+ * (DGEMM / ZGEMM) emulated with Ozaki scheme II on the INT8 matrix cores of
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the BLAS one, C <- alpha op(A) op(B) + beta C, with
+ * column-major storage, op in {N, T, C} and leading dimensions ("Emulating
+ * DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs: Ozaki Scheme II
+ * on the Xe2 Architecture", Sec. 1 contributions and Sec. 2.1 notation).
+ * The interface mirrors dgemm/zgemm with one extra argument, the number of
+ * moduli s (same page, Sec. 9.1).  How a call is computed (same page, Sec. 2.3
+ * and Sec. 4): every row of op(A) and column of op(B) is scaled by a power of
+ * two and rounded to integers with at most t+1 bits (Sec. 4.1), the integers
+ * are reduced to signed INT8 residues modulo s pairwise-coprime moduli <= 256
+ * (Sec. 2.3 step 2, Sec. 4.2), s exact INT8 products with INT32 accumulation
+ * are formed (Sec. 2.3 step 3, Sec. 4.3), and the integer product is recovered
+ * by the Chinese remainder theorem, rounded once to double and scaled back
+ * (Sec. 4.4).  ZGEMM uses the exact integer 3M (Karatsuba) form, 3s INT8
+ * products (Sec. 5).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers to matrices are DEVICE pointers (hipMalloc / torch CUDA
+ *    tensors) owned by the caller; the library never frees them.  Complex
+ *    matrices are interleaved (re, im) pairs of doubles (complex128).
+ *  - Work is enqueued asynchronously, in order, on the handle's stream;
+ *    calls return without synchronizing.  Device-side faults surface at the
+ *    caller's next synchronization.
+ *  - Return value: 0 on success; -i when argument i (1-based, the handle is
+ *    argument 1) is invalid, LAPACK "info" style; a positive OZ2_STATUS_*
+ *    code for run-time failures (see oz2_status_string()).
+ *  - A handle is not thread-safe; use one handle per host thread.
+ *  - Quick returns follow reference BLAS: m = 0 or n = 0 does nothing;
+ *    alpha = 0 or k = 0 sets C <- beta C (C is not read when beta = 0) and
+ *    A and B are not read.  When beta = 0, C is never read, so NaN in C does
+ *    not propagate.
+ *  - An Inf or NaN anywhere in a row of op(A) (column of op(B)) makes the
+ *    whole row (column) of the result NaN (Arc page Sec. 8.1 and Sec. 9.3).
+ *  - Results are deterministic and independent of the launch configuration:
+ *    all accumulation is exact integer arithmetic (Arc page Sec. 9.1).
+ *    Normal results are the correctly rounded value of
+ *    2^(-D_i-E_j) * c_hat_ij; subnormal results may be rounded twice
+ *    (Arc page Sec. 4.4, Sec. 9.3).  alpha/beta are then applied as
+ *    t1 = alpha*x; t2 = beta*c; C = t1 + t2 (complex:
+ *    re = (ar*xr - ai*xi) + (br*cr - bi*ci), im = (ar*xi + ai*xr) + (br*ci + bi*cr)),
+ *    each operation rounded separately.
+ */
+#ifndef OZ2_H
+#define OZ2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct oz2_context* oz2_handle_t;
+
+enum {
+    OZ2_STATUS_SUCCESS = 0,
+    OZ2_STATUS_ALLOC_FAILED = 1,     /* device workspace allocation failed */
+    OZ2_STATUS_HIP_ERROR = 2,        /* a HIP runtime call or launch failed */
+    OZ2_STATUS_RANGE = 3,            /* no scaling width t >= 1 for this (s, k) */
+    OZ2_STATUS_WORKSPACE_LIMIT = 4,  /* workspace would exceed the memory limit */
+    OZ2_STATUS_NOT_SUPPORTED = 5,    /* e.g. no gfx950 device */
+    OZ2_STATUS_INTERNAL = 6
+};
+
+/* Create a handle bound to the current HIP device; its stream is the null
+ * stream until oz2_set_stream().  *h receives the handle. */
+int oz2_create(oz2_handle_t* h);
+
+/* Free the handle and its workspace (waits for the handle's stream first).
+ * The stream itself is not destroyed. */
+int oz2_destroy(oz2_handle_t h);
+
+/* All later work of this handle is enqueued on `stream` (a hipStream_t,
+ * NULL for the null stream). */
+int oz2_set_stream(oz2_handle_t h, void* stream);
+
+/* Cap on the workspace in bytes; 0 (the default) means the free device
+ * memory reported by hipMemGetInfo at allocation time.  A call whose
+ * workspace would exceed the cap returns OZ2_STATUS_WORKSPACE_LIMIT
+ * (the resident-memory hint of Arc page Sec. 6, memory-aware tiling). */
+int oz2_set_memory_limit(oz2_handle_t h, size_t bytes);
+
+/* Current workspace size in bytes (0 before the first call). */
+int oz2_get_workspace_size(oz2_handle_t h, size_t* bytes);
+
+/* Enable (1) or disable (0) per-phase hipEvent timing of later calls. */
+int oz2_set_timing(oz2_handle_t h, int enable);
+
+/* Phase times in milliseconds of the last timed call: ms[0] scan (row/column
+ * exponents), ms[1] encode (integerize + residues), ms[2] residue GEMM,
+ * ms[3] reconstruct (CRT + alpha/beta).  Synchronizes with the last call. */
+int oz2_get_phase_times(oz2_handle_t h, float ms[4]);
+
+/* Default precision policy (Arc page Sec. 9.1): the smallest s in [2, 24]
+ * whose scaling width t(s, k) reaches `bits`; 24 when none does. */
+int oz2_moduli_for_bits(int64_t k, int bits, int is_complex);
+
+/* Host-side plan of the method for (s, k): moduli in descending order
+ * (moduli_out[24], first s entries used), the scaling width t (<= 0 when
+ * none exists), N_L = number of 32-bit words of c_hat, and log2 M.  Any
+ * output pointer may be NULL.  Returns -1 for s outside [2, 24]. */
+int oz2_plan_info(int num_moduli, int64_t k, int is_complex, int32_t* moduli_out,
+                  int* t_out, int* nl_out, double* log2M_out);
+
+/* C <- alpha op(A) op(B) + beta C.  op(A) is m x k, op(B) is k x n, C is
+ * m x n; lda >= max(1, rows of A as stored), likewise ldb, ldc >= max(1, m).
+ * transa/transb in {'N','T','C'} (upper or lower case; 'C' = 'T' here).
+ * 2 <= num_moduli <= 24; k may exceed 131071 (the INT32 accumulation is
+ * split internally, Arc page Sec. 4.3).  Returns OZ2_STATUS_RANGE when no
+ * scaling width exists for (num_moduli, k). */
+int oz2_dgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
+              double alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
+              double beta, double* C, int64_t ldc, int num_moduli);
+
+/* Complex version (Arc page Sec. 5): A, B, C are interleaved complex128;
+ * alpha[2] and beta[2] are HOST arrays (re, im); 'C' conjugates.  Uses one
+ * exponent per row/column shared by the real and imaginary parts and the
+ * scaling width of a 2k-term product. */
+int oz2_zgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
+              const double* alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
+              const double* beta, double* C, int64_t ldc, int num_moduli);
+
+/* batch independent products C_b <- alpha op(A_b) op(B_b) + beta C_b with
+ * A_b = A + b*strideA (in doubles), likewise B and C.  A stride of 0 shares
+ * one operand across the batch (the shared operators of a tensor mode
+ * product: "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode
+ * Products", Sec. 2.1 Eq. (5) and Sec. 5.1).  Every product uses its own
+ * row/column exponents, as separate oz2_dgemm calls would. */
+int oz2_dgemm_strided_batched(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n,
+                              int64_t k, double alpha, const double* A, int64_t lda,
+                              int64_t strideA, const double* B, int64_t ldb, int64_t strideB,
+                              double beta, double* C, int64_t ldc, int64_t strideC,
+                              int64_t batch, int num_moduli);
+
+/* Human-readable text of a status code (static storage). */
+const char* oz2_status_string(int status);
+
+/* ---------------------------------------------------------------------
+ * Test hooks (the GPU analogues of the split and CRT unit tests of the Arc
+ * page, Sec. 8.1).  Not needed for normal use.
+ * ------------------------------------------------------------------- */
+
+/* debug = 1: later calls also keep c_hat (N_L 32-bit two's-complement words
+ * per entry, entry-major, column-major entry order) in the workspace. */
+int oz2_set_debug(oz2_handle_t h, int debug);
+
+/* Copy an intermediate buffer of the handle's LAST call to HOST memory
+ * `dst` (at most `capacity` bytes; synchronizes first).  `which`:
+ *   0 row maxima |op(A)| as IEEE bit patterns, uint64[m_pad]
+ *   1 column maxima |op(B)|, uint64[n_pad]
+ *   2 residue planes of op(A): int8[sets][s][m_pad][k_pad] (sets = 1 real,
+ *     3 complex: re, im, re+im), rows k-contiguous
+ *   3 residue planes of op(B): int8[sets][s][n_pad][k_pad]
+ *   4 product residues in [0, m_t): uint8[outs][s][n][m_pad] (outs = 1 real,
+ *     2 complex: Re, Im)
+ *   5 c_hat words (only when debug was enabled): uint32[outs][n][m_pad][N_L]
+ * dims[0..4] receive (sets or outs, s, rows, cols, runs or N_L) of the buffer.
+ * Returns the byte size in *bytes.  -2 for an unknown `which`. */
+int oz2_debug_copy(oz2_handle_t h, int which, void* dst, size_t capacity, size_t* bytes,
+                   int64_t dims[5]);
+
+/* CRT reconstruction only: from residues r[t][q] in [0, m_t) (DEVICE
+ * uint8[num_moduli][count]) compute c = the integer in (-M/2, M/2] that is
+ * congruent to r_t mod m_t for every t, valid when |c| <= M/4, as N_L
+ * two's-complement 32-bit words per entry (DEVICE uint32[count][N_L]). */
+int oz2_test_crt(oz2_handle_t h, int64_t count, int num_moduli, const uint8_t* residues,
+                 uint32_t* words);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OZ2_H */

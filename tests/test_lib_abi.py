@@ -1,0 +1,62 @@
+"""The C-ABI library loads, exports every symbol include/oz2.h declares, and
+its host planner agrees with the independently written oracle (no GPU)."""
+import os
+import re
+
+import pytest
+
+import complex_gemm_emulation_amd as oz2
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "oz2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oz2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_match_binding_list():
+    assert _declared_symbols() == sorted(oz2.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    import ctypes
+    lib = ctypes.CDLL(oz2.LIB_PATH)
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("s", range(2, 25))
+def test_planner_matches_oracle(s):
+    # two independent searches for the max-product moduli set, and two
+    # independent t(s, k) computations, must agree
+    for k in (1, 16, 256, 4096, 8192, 131071, 300000):
+        for cplx in (False, True):
+            info = oz2.plan_info(s, k, cplx)
+            assert info["moduli"] == oracle.max_product_moduli(s)
+            assert info["NL"] == oracle.n_limbs(s)
+            t = oracle.scaling_width(s, k, cplx)
+            assert info["t"] == t, (s, k, cplx)
+            assert abs(info["log2M"] - oracle.log2_M(s)) < 1e-9
+
+
+def test_moduli_for_bits_matches_oracle():
+    for k in (16, 256, 4096, 65536, 1 << 20):
+        for bits in (24, 40, 53, 70):
+            assert oz2.moduli_for_bits(k, bits) == oracle.moduli_for_bits(k, bits)
+
+
+def test_plan_info_rejects_bad_s():
+    with pytest.raises(oz2.Oz2Error):
+        oz2.plan_info(1, 10)
+    with pytest.raises(oz2.Oz2Error):
+        oz2.plan_info(25, 10)
+
+
+def test_status_strings():
+    lib = oz2.lib()
+    assert lib.oz2_status_string(0) == b"success"
+    assert b"scaling width" in lib.oz2_status_string(3)
+    assert lib.oz2_status_string(-3) == b"invalid argument"
