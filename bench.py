@@ -12,8 +12,12 @@ GB/s of the memory-bound phases), the roofline of the residue-GEMM kernel and
 the oracle's rate on the host cores (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--s 8,12,16]
+       python bench.py --copy-calibration ...   (also runs a plain device copy of
+       known size first, so that hardware byte counters taken over the same
+       process can be scaled to bytes)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +31,9 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+GEMM_SOURCE = os.path.join(ROOT, "complex_gemm_emulation_amd", "csrc", "oz2_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "residue_gemm_traffic.json")
+COPY_CAL_BYTES = 1 << 30     # bytes read (and written) by the calibration copy
 
 
 def log(msg):
@@ -42,6 +49,36 @@ def algorithmic(m, n, k, s, beta_nonzero=False):
         gemm_bytes=s * (m * k + k * n) + s * m * n,
         recon_bytes=(s + 8.0) * m * n + (8.0 * m * n if beta_nonzero else 0.0),
     )
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per residue-GEMM launch from the committed counter runs,
+    or None when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256_16") != source_digest(GEMM_SOURCE):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def copy_calibration(torch):
+    """A plain device copy of COPY_CAL_BYTES bytes, three times: the
+    reference against which FETCH_SIZE / WRITE_SIZE counters are scaled."""
+    n = COPY_CAL_BYTES // 8
+    src = torch.empty(n, dtype=torch.float64, device="cuda").uniform_(-1, 1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(A, B, m, n, k, s, side, seed=12345):
@@ -70,8 +107,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--s", type=str, default="8,12,16")
     ap.add_argument("--n", type=int, default=8192)
-    ap.add_argument("--cpu-side", type=int, default=128)
+    ap.add_argument("--cpu-side", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the emulated GEMM of a single device "
@@ -83,6 +121,9 @@ def main():
     import complex_gemm_emulation_amd as oz2
     import workloads
 
+    if args.copy_calibration:
+        log(f"[bench] calibration copy of {COPY_CAL_BYTES} bytes x 3")
+        copy_calibration(torch)
     s_list = [int(x) for x in args.s.split(",")]
     m = n = k = args.n
     log(f"[bench] generating {m}x{k} and {k}x{n} inputs (phi = 0.5, seeded)")
@@ -137,11 +178,15 @@ def main():
         )
         gemm_ops += w["int8_ops"]
         gemm_ms += float(ph[2])
+    # residue GEMM: one launch per call; the mean launch of a step does
+    # 2 M N K (sum of s) / len(s) INT8 ops, timed by HIP events on its stream
     achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    traffic = measured_traffic()
     roofline = dict(kernel="residue_gemm_kernel (INT8 MFMA, fused mod m)", bound="mfma",
                     achieved=round(achieved, 2), peak=PEAK_INT8_TOPS, unit="TOP/s",
-                    frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=None,
-                    per_launch_ops="2*M*N*K*s (s = 8, 12, 16; one launch per call)")
+                    frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=traffic,
+                    ops_per_launch=gemm_ops / len(s_list),
+                    launch_ms=round(gemm_ms / len(s_list), 4))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -160,7 +205,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64 (emulated on int8 MFMA)",
+        "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": f"dgemm_{m}_NN_phi0.5_s{'_'.join(map(str, s_list))}",
                    "m": m, "n": n, "k": k, "s": s_list, "ops": "N/N", "alpha": 1.0, "beta": 0.0},
