@@ -25,9 +25,10 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t x, int64_t q) { return (x + q - 1) / q * q; }
 
-// a run of at most this many k-positions keeps |INT32 accumulator| <= 2^31 - 2^20
-// (Arc page Sec. 2.3 step 3: exact while k 128^2 < 2^31); a multiple of 64
-constexpr int64_t kMaxRunK = 131008;
+// a run of at most this many k-positions keeps |INT32 accumulator| <= 2^31 - 2^22
+// (Arc page Sec. 2.3 step 3: exact while k 128^2 < 2^31); a multiple of kPadK
+constexpr int64_t kMaxRunK = 130816;
+static_assert(kMaxRunK % kPadK == 0, "runs must be whole pairs of GEMM k steps");
 
 struct Layout {
     int sets = 1, outs = 1, s = 0, NL = 0, t = 0, chunks = 1;
@@ -232,7 +233,7 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
             G.C = res + c * chunk_stride;
             G.k_begin = c * kMaxRunK;
             const int64_t k_end = (c + 1) * kMaxRunK < L.kp ? (c + 1) * kMaxRunK : L.kp;
-            G.k_steps = (int)((k_end - G.k_begin) / kPadK);
+            G.k_steps = (int)((k_end - G.k_begin) / kGemmStepK);
             OZ2_LAUNCH(launch_residue_gemm(G, cplx, stm));
         }
     }

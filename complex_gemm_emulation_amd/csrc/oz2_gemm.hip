@@ -5,32 +5,38 @@
 // "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
 // Ozaki Scheme II on the Xe2 Architecture", Sec. 2.3 step 3: each product
 // A^(t) B^(t) is exact with INT32 accumulation while k 128^2 < 2^31; Sec. 4.3:
-// longer k is split into runs of at most 131008 positions, one launch per
-// run, and the residues of the runs are summed mod m_t in the reconstruction
-// (bitwise the same residue as an unsplit product).  "EmuGEMM: Fused Tensor Core Kernels
-// for Precision Emulation", Sec. IV-A (Eq. 14-15): reducing the INT32
-// accumulator on chip and writing only one byte per entry removes the INT32
-// round trip; Sec. IV-B (Eq. 16-18): the three products of the complex 3M
-// form run as three k-loops over one accumulator and only Re and Im leave
-// the chip.  Here T1 mod m and then T1 + T2 mod m are parked in the output
-// planes between the k-loops (each lane rereads only what it wrote), so no
-// registers beyond one accumulator set are held across the loops.
+// longer k is split into runs (here of at most 130816 positions), one launch
+// per run, and the residues of the runs are summed mod m_t in the
+// reconstruction (bitwise the same residue as an unsplit product).
+// "EmuGEMM: Fused Tensor Core Kernels for Precision Emulation", Sec. IV-A
+// (Eq. 14-15): reducing the INT32 accumulator on chip and writing one byte per
+// entry removes the INT32 round trip; Sec. IV-B (Eq. 16-18): the three
+// products of the complex 3M form run as three k-loops of one block and only
+// Re and Im leave the chip.  Here T1 mod m and then T1 + T2 mod m are parked
+// in the output planes between the k-loops (each lane rereads only what it
+// wrote), so no registers beyond one accumulator set are held across loops.
 //
 // Data layout: both operands are k-contiguous planes (rows of op(A), columns
-// of op(B)), zero-padded in k to a multiple of 64 and in rows to a multiple
+// of op(B)), zero-padded in k to a multiple of 256 and in rows to a multiple
 // of 256, so the main loop has no bounds checks.  The output plane of
 // modulus t is uint8 [n][m_pad] (column-major like C) holding C^(t) mod m_t
 // in [0, m_t).
 //
-// Kernel shape: a 256-thread block (4 wavefronts, 2 x 2) computes a BM x BN
-// tile of one modulus; each wavefront owns (BM/2) x (BN/2) accumulators in
-// 32x32 MFMA tiles.  k advances in steps of 64 bytes staged through LDS with
-// double buffering; global loads of step k+1 are in flight while step k is
-// multiplied.  LDS rows are 64 bytes of four 16-byte chunks whose position
-// is XOR-swizzled by the row index so that the 16-byte MFMA operand reads of
-// 8 (or 16) consecutive rows hit distinct banks.  Blocks are remapped so
-// that each of the 8 XCDs (which receive blocks round-robin) works on a
-// contiguous range of tiles, grouped 8 tiles tall for L2 reuse.
+// Kernel shape (CDNA4): a BM x BN tile of one modulus per block, WM x WN
+// wavefronts, each owning (BM/WM) x (BN/WN) INT32 accumulators in 32 x 32
+// MFMA tiles.  k advances 128 bytes per step through two LDS stages filled by
+// direct global->LDS loads (global_load_lds_dwordx4: no VGPR staging, no
+// ds_write), so the loads of step k+1 (and, after the mid-step barrier, of
+// step k+2) overlap the MFMAs of step k.  Operand fragments are double
+// buffered in registers and the MFMAs are interleaved one-to-one with the
+// LDS fragment reads of the next 32-wide k sub-step (sched_group_barrier).
+// LDS rows are 128 bytes of eight 16-byte chunks whose position is XOR-ed
+// with (row/2) mod 8: the LDS serves a 16-byte-per-lane read 16 lanes per
+// clock over 64 banks, and 16 consecutive rows then hit distinct bank groups.
+// The 256 x 256 tile uses 8 wavefronts (two per SIMD) so that one wave's
+// MFMAs cover the other's waits.  Blocks are remapped so that each of the 8
+// XCDs (which receive blocks round-robin) works on a contiguous range of
+// tiles, grouped 8 tiles tall for L2 reuse.
 #include "oz2_internal.h"
 
 namespace oz2 {
@@ -38,21 +44,14 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* global_ptr_t;
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
-struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-    static constexpr int NT = WM * WN * 64;
-    static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int FM = WTM / 32, FN = WTN / 32;
-    static constexpr int KSUB = BK / 32;
-    static constexpr int CH = BK / 16;
-    static constexpr int A_LD = BM * CH / NT, B_LD = BN * CH / NT;
-    static constexpr int LDS_A = BM * BK, LDS_B = BN * BK;
-    static_assert(A_LD * NT == BM * CH && B_LD * NT == BN * CH, "tile/thread mismatch");
-};
+constexpr int kBK = 128;         // k bytes per step (four 32-wide MFMA sub-steps)
+constexpr int kChunks = kBK / 16;
 
-__device__ __forceinline__ int swz(int row, int ch) { return ((row >> 1) ^ (row >> 3)) & (ch - 1); }
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 // INT32 accumulator -> [0, m): bias makes it non-negative (a multiple of m,
 // chosen for |acc| <= 2^31 - 2^20 + 255), Barrett quotient floor(u R / 2^32)
@@ -65,13 +64,26 @@ __device__ __forceinline__ uint32_t acc_mod(int32_t acc, uint32_t m, uint32_t R,
     return r < r2 ? r : r2;
 }
 
-template <class T, bool CPLX>
-__global__ __launch_bounds__(T::NT, 1) void residue_gemm_kernel(GemmParams P) {
-    __shared__ __attribute__((aligned(16))) int8_t smem[2 * (T::LDS_A + T::LDS_B)];
+__device__ __forceinline__ uint32_t pack4(const uint32_t r[4]) {
+    return r[0] | (r[1] << 8) | (r[2] << 16) | (r[3] << 24);
+}
+
+template <int BM, int BN, int WM, int WN, bool CPLX>
+__global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParams P) {
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
+    constexpr int LOADS_A = BM * kChunks / 64 / NW;  // wave-wide 1 KiB loads per wave and stage
+    constexpr int LOADS_B = BN * kChunks / 64 / NW;
+    static_assert(LOADS_A * 64 * NW == BM * kChunks && LOADS_B * 64 * NW == BN * kChunks, "tile/wave mismatch");
+    __shared__ __attribute__((aligned(1024))) int8_t sA0[BM * kBK];
+    __shared__ __attribute__((aligned(1024))) int8_t sB0[BN * kBK];
+    __shared__ __attribute__((aligned(1024))) int8_t sA1[BM * kBK];
+    __shared__ __attribute__((aligned(1024))) int8_t sB1[BN * kBK];
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave % T::WM, wn = wave / T::WM;
+    const int wm = wave % WM, wn = wave / WM;
 
     // block -> (modulus, tile row, tile column)
     const int nb = gridDim.x;
@@ -90,100 +102,124 @@ __global__ __launch_bounds__(T::NT, 1) void residue_gemm_kernel(GemmParams P) {
 
     const uint32_t m = P.mod[t], R = P.barrett[t], bias = P.bias[t];
     const int64_t kp = P.kp;
-    const int nk = P.k_steps;  // this launch covers k in [k_begin, k_begin + 64 k_steps)
+    const int nk = P.k_steps;  // even; this launch covers k in [k_begin, k_begin + 128 nk)
 
-    v16i acc[T::FM][T::FN];
+    // per-lane source offsets of the direct loads: piece = 16 bytes landing at
+    // LDS byte 16 * piece, i.e. row piece / 8, stored chunk position piece % 8
+    uint32_t goffA[LOADS_A], goffB[LOADS_B];
+#pragma unroll
+    for (int q = 0; q < LOADS_A; ++q) {
+        const int piece = (wave * LOADS_A + q) * 64 + lane;
+        const int row = piece / kChunks, pos = piece % kChunks;
+        goffA[q] = (uint32_t)(row * kp + ((pos ^ ((row >> 1) & 7)) << 4));
+    }
+#pragma unroll
+    for (int q = 0; q < LOADS_B; ++q) {
+        const int piece = (wave * LOADS_B + q) * 64 + lane;
+        const int row = piece / kChunks, pos = piece % kChunks;
+        goffB[q] = (uint32_t)(row * kp + ((pos ^ ((row >> 1) & 7)) << 4));
+    }
+    const int fr = lane & 31;
+    const int aoff = (wm * WTM + fr) * kBK;
+    const int boff = (wn * WTN + fr) * kBK;
+    const int row_out0 = tm * BM + wm * WTM + 4 * (lane >> 5);
+    const int col_out0 = tn * BN + wn * WTN + fr;
 
-    const int row_out0 = tm * T::BM + wm * T::WTM + 4 * (lane >> 5);
-    const int col_out0 = tn * T::BN + wn * T::WTN + (lane & 31);
+    v16i acc[FM][FN];
+    v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
 
 #pragma unroll 1
     for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
-        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.mp * kp +
-                           (int64_t)tm * T::BM * kp + P.k_begin;
-        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.np * kp +
-                           (int64_t)tn * T::BN * kp + P.k_begin;
+        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.mp * kp + (int64_t)tm * BM * kp + P.k_begin;
+        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.np * kp + (int64_t)tn * BN * kp + P.k_begin;
+        auto issue = [&](int kt, int8_t* dA, int8_t* dB) {
+            const int8_t* Ak = Ag + (int64_t)kt * kBK;
+            const int8_t* Bk = Bg + (int64_t)kt * kBK;
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
+            for (int q = 0; q < LOADS_A; ++q)
+                __builtin_amdgcn_global_load_lds((global_ptr_t)(Ak + goffA[q]),
+                                                 (lds_ptr_t)(dA + (wave * LOADS_A + q) * 1024), 16, 0, 0);
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j)
+            for (int q = 0; q < LOADS_B; ++q)
+                __builtin_amdgcn_global_load_lds((global_ptr_t)(Bk + goffB[q]),
+                                                 (lds_ptr_t)(dB + (wave * LOADS_B + q) * 1024), 16, 0, 0);
+        };
+        // fragments of sub-step ks: lane l holds row (l mod 32), chunk 2 ks + l / 32
+        auto rd = [&](const int8_t* cA, const int8_t* cB, int ks, v4i (&a)[FM], v4i (&b)[FN]) {
+            const int c = ks * 2 + (lane >> 5);
+            const int sw = (c ^ ((fr >> 1) & 7)) << 4;
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = *(const v4i*)(cA + aoff + i * 32 * kBK + sw);
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = *(const v4i*)(cB + boff + j * 32 * kBK + sw);
+        };
+        auto mm = [&](v4i (&a)[FM], v4i (&b)[FN]) {
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        };
+        constexpr int NMF = FM * FN, NDS = FM + FN, NDMA = LOADS_A + LOADS_B;
+        auto sched = [&](bool with_dma) {
+#pragma unroll
+            for (int q = 0; q < NDS; ++q) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+                if (with_dma) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (NDMA + NDS - 1) / NDS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMF - NDS, 0);
+        };
+        // one k-step on stage c*; then the next stage n* is read and the DMA of
+        // step kdma refills the stage just consumed (w* == c*)
+        auto kstep = [&](const int8_t* cA, const int8_t* cB, const int8_t* nA, const int8_t* nB, int8_t* wA,
+                         int8_t* wB, int kdma) {
+            rd(cA, cB, 1, fa1, fb1);
+            mm(fa0, fb0);
+            sched(false);
+            rd(cA, cB, 2, fa0, fb0);
+            mm(fa1, fb1);
+            sched(false);
+            rd(cA, cB, 3, fa1, fb1);
+            mm(fa0, fb0);
+            sched(false);
+            // every read of this stage has returned and this wave's DMA of the
+            // next stage has landed; after the barrier both hold block-wide
+            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+            __syncthreads();
+            // past the last step these re-read valid data that is not used
+            rd(nA, nB, 0, fa0, fb0);
+            issue(kdma, wA, wB);
+            mm(fa1, fb1);
+            sched(true);
+        };
+
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-
-        v4i ra[T::A_LD], rb[T::B_LD];
-        auto gload = [&](int kt) {
-#pragma unroll
-            for (int q = 0; q < T::A_LD; ++q) {
-                const int idx = tid + q * T::NT;
-                const int row = idx / T::CH, c = idx % T::CH;
-                ra[q] = *(const v4i*)(Ag + (int64_t)row * kp + (int64_t)kt * T::BK + c * 16);
-            }
-#pragma unroll
-            for (int q = 0; q < T::B_LD; ++q) {
-                const int idx = tid + q * T::NT;
-                const int row = idx / T::CH, c = idx % T::CH;
-                rb[q] = *(const v4i*)(Bg + (int64_t)row * kp + (int64_t)kt * T::BK + c * 16);
-            }
-        };
-        auto sstore = [&](int buf) {
-            int8_t* As = smem + buf * (T::LDS_A + T::LDS_B);
-            int8_t* Bs = As + T::LDS_A;
-#pragma unroll
-            for (int q = 0; q < T::A_LD; ++q) {
-                const int idx = tid + q * T::NT;
-                const int row = idx / T::CH, c = idx % T::CH;
-                *(v4i*)(As + row * T::BK + ((c ^ swz(row, T::CH)) << 4)) = ra[q];
-            }
-#pragma unroll
-            for (int q = 0; q < T::B_LD; ++q) {
-                const int idx = tid + q * T::NT;
-                const int row = idx / T::CH, c = idx % T::CH;
-                *(v4i*)(Bs + row * T::BK + ((c ^ swz(row, T::CH)) << 4)) = rb[q];
-            }
-        };
-        auto compute = [&](int buf) {
-            const int8_t* As = smem + buf * (T::LDS_A + T::LDS_B);
-            const int8_t* Bs = As + T::LDS_A;
-#pragma unroll
-            for (int ks = 0; ks < T::KSUB; ++ks) {
-                const int c = ks * 2 + (lane >> 5);
-                v4i a[T::FM], b[T::FN];
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i) {
-                    const int row = wm * T::WTM + i * 32 + (lane & 31);
-                    a[i] = *(const v4i*)(As + row * T::BK + ((c ^ swz(row, T::CH)) << 4));
-                }
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j) {
-                    const int row = wn * T::WTN + j * 32 + (lane & 31);
-                    b[j] = *(const v4i*)(Bs + row * T::BK + ((c ^ swz(row, T::CH)) << 4));
-                }
-#pragma unroll
-                for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < T::FN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-            }
-        };
-
-        gload(0);
-        sstore(0);
+        issue(0, sA0, sB0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
+        issue(1, sA1, sB1);
+        rd(sA0, sB0, 0, fa0, fb0);
 #pragma unroll 1
-        for (int kt = 0; kt < nk; ++kt) {
-            const bool more = kt + 1 < nk;
-            if (more) gload(kt + 1);
-            compute(kt & 1);
-            if (more) sstore((kt + 1) & 1);
-            __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            kstep(sA0, sB0, sA1, sB1, sA0, sB0, min(kt + 2, nk - 1));
+            kstep(sA1, sB1, sA0, sB0, sA1, sB1, min(kt + 3, nk - 1));
         }
+        // no LDS DMA may be in flight when the stages are reused or released
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
 
         // epilogue: lane holds rows 8g + 4(lane/32) + {0..3} of column lane%32
         // of every 32x32 tile, i.e. four consecutive bytes of the output plane
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
+        for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
+            for (int j = 0; j < FN; ++j) {
                 const int64_t col = col_out0 + j * 32;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
@@ -192,14 +228,13 @@ __global__ __launch_bounds__(T::NT, 1) void residue_gemm_kernel(GemmParams P) {
                     for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][4 * g + e], m, R, bias);
                     const int64_t row = row_out0 + i * 32 + 8 * g;
                     uint8_t* re_dst = P.C + (int64_t)t * P.n * P.mp + col * P.mp + row;
-                    uint8_t* im_dst = re_dst + P.c_set_stride;
                     if (col >= P.n) continue;
                     if (!CPLX || pass == 0) {
-                        // real: the result; complex pass 0: T1 mod m parked in
-                        // the Re plane (each lane rereads only its own words)
-                        *(uint32_t*)re_dst = r[0] | (r[1] << 8) | (r[2] << 16) | (r[3] << 24);
+                        // real: the result; complex pass 0: T1 mod m parked in the Re plane
+                        *(uint32_t*)re_dst = pack4(r);
                     } else if (pass == 1) {
                         // Re = T1 - T2; T1 + T2 parked in the Im plane
+                        uint8_t* im_dst = re_dst + P.c_set_stride;
                         const uint32_t t1w = *(const uint32_t*)re_dst;
                         uint32_t re[4], sm[4];
 #pragma unroll
@@ -212,10 +247,11 @@ __global__ __launch_bounds__(T::NT, 1) void residue_gemm_kernel(GemmParams P) {
                             const uint32_t y1 = y - m;
                             sm[e] = y < y1 ? y : y1;
                         }
-                        *(uint32_t*)re_dst = re[0] | (re[1] << 8) | (re[2] << 16) | (re[3] << 24);
-                        *(uint32_t*)im_dst = sm[0] | (sm[1] << 8) | (sm[2] << 16) | (sm[3] << 24);
+                        *(uint32_t*)re_dst = pack4(re);
+                        *(uint32_t*)im_dst = pack4(sm);
                     } else {
                         // Im = T3 - (T1 + T2)
+                        uint8_t* im_dst = re_dst + P.c_set_stride;
                         const uint32_t sw = *(const uint32_t*)im_dst;
                         uint32_t im[4];
 #pragma unroll
@@ -224,7 +260,7 @@ __global__ __launch_bounds__(T::NT, 1) void residue_gemm_kernel(GemmParams P) {
                             const uint32_t x1 = x - m;
                             im[e] = x < x1 ? x : x1;
                         }
-                        *(uint32_t*)im_dst = im[0] | (im[1] << 8) | (im[2] << 16) | (im[3] << 24);
+                        *(uint32_t*)im_dst = pack4(im);
                     }
                 }
             }
@@ -232,29 +268,28 @@ __global__ __launch_bounds__(T::NT, 1) void residue_gemm_kernel(GemmParams P) {
     }
 }
 
-using BigTile = Tile<256, 256, 64, 2, 2>;
-using SmallTile = Tile<128, 128, 64, 2, 2>;
-
-template <class T>
+template <int BM, int BN, int WM, int WN>
 hipError_t gemm_go(GemmParams P, bool cplx, hipStream_t st) {
-    P.tiles_m = (int)(P.mp / T::BM);
-    P.tiles_n = (int)(P.np / T::BN);
+    P.tiles_m = (int)(P.mp / BM);
+    P.tiles_n = (int)(P.np / BN);
     const int64_t nb = (int64_t)P.tiles_m * P.tiles_n * P.s;
+    const dim3 block(64 * WM * WN);
     if (cplx)
-        hipLaunchKernelGGL((residue_gemm_kernel<T, true>), dim3((unsigned)nb), dim3(T::NT), 0, st, P);
+        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, true>), dim3((unsigned)nb), block, 0, st, P);
     else
-        hipLaunchKernelGGL((residue_gemm_kernel<T, false>), dim3((unsigned)nb), dim3(T::NT), 0, st, P);
+        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, false>), dim3((unsigned)nb), block, 0, st, P);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_residue_gemm(const GemmParams& P, bool cplx, hipStream_t st) {
-    if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK) return hipErrorInvalidValue;
-    // large outputs: 256 x 256 tiles; otherwise 128 x 128 for more blocks
+    if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK || P.k_begin % kBK) return hipErrorInvalidValue;
+    if (P.k_steps <= 0 || P.k_steps % 2 || P.k_begin + (int64_t)P.k_steps * kBK > P.kp) return hipErrorInvalidValue;
+    // large outputs: 256 x 256 tiles on 8 wavefronts; otherwise 128 x 128 on 4
     const int64_t big_blocks = (P.mp / 256) * (P.np / 256) * P.s;
-    if (big_blocks >= 1024) return gemm_go<BigTile>(P, cplx, st);
-    return gemm_go<SmallTile>(P, cplx, st);
+    if (big_blocks >= 512) return gemm_go<256, 256, 2, 4>(P, cplx, st);
+    return gemm_go<128, 128, 2, 2>(P, cplx, st);
 }
 
 }  // namespace oz2

@@ -17,7 +17,8 @@ namespace oz2 {
 // Product residues are uint8 [outs][s][n][m_pad] holding values in [0, m_t)
 // (outs = 1 real, 2 complex: Re, Im), i.e. column-major like C.
 constexpr int kPadM = 256;   // row padding of the A planes / product planes
-constexpr int kPadK = 64;    // k padding of the planes (the GEMM k step)
+constexpr int kPadK = 256;   // k padding of the planes (two 128-byte GEMM k steps)
+constexpr int kGemmStepK = 128;  // k bytes per GEMM k step
 
 // Vector layout of an operand as seen by scan/encode: vector v (a row of
 // op(A) or a column of op(B)) has element p at X[v*ld + p] when contiguous,
@@ -53,8 +54,8 @@ struct GemmParams {
     int64_t a_set_stride, b_set_stride, c_set_stride;  // bytes
     int s;
     int tiles_m, tiles_n;
-    int64_t k_begin;   // first k position of this launch (multiple of 64)
-    int k_steps;       // 64-wide k steps of this launch: <= 2047 keeps INT32 exact
+    int64_t k_begin;   // first k position of this launch (multiple of 128)
+    int k_steps;       // 128-wide k steps of this launch (even): <= 1022 keeps INT32 exact
     uint32_t mod[kMaxS], barrett[kMaxS], bias[kMaxS];
 };
 

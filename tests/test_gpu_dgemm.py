@@ -143,12 +143,12 @@ def test_k_split_runs(handle):
     # k beyond one exact INT32 run (Arc page Sec. 4.3): split runs must give
     # the same c_hat as the oracle's unsplit exact product
     m, n = 9, 7
-    for k in (131008, 131072, 140001):
+    for k in (130816, 131071, 131072, 140001):
         A = workloads.real_matrix(m, k, workloads.seed(77, 0) + k, "phi", 1.0)
         B = workloads.real_matrix(k, n, workloads.seed(77, 1) + k, "phi", 1.0)
         _run_full(handle, "N", "N", m, n, k, 1.0, 0.0, 16, A, m, B, k, None, m, label=f"ksplit{k}")
         runs = handle.debug_copy(4).shape[0]
-        assert runs == (1 if k <= 131008 else 2)
+        assert runs == (1 if k <= 130816 else 2)
 
 
 def test_crt_boundary_one_minus_ulp(handle):
