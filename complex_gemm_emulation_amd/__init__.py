@@ -221,6 +221,28 @@ class Handle:
                                                 k, float(alpha), pa, lda, strideA, pb, ldb,
                                                 strideB, float(beta), pc, ldc, strideC, batch, s))
 
+    def tensor_mode_chain(self, X, A, B, C, n, batch, s, Y=None, work=None):
+        """Y = X x1 A x2 B x3 C for `batch` independent n x n x n tensors
+        (column-major X[i + n j + n^2 k + n^3 b]) and shared n x n operators,
+        each mode one emulated product with its own per-fiber and
+        per-operator-row scales ("You Only Convert Twice", Sec. 2.1 Eq. (5)
+        and Sec. 5.1): mode 1 is A X_(1); modes 2 and 3 are strided batches
+        of slice x operator^T.  Returns Y (allocated if not given)."""
+        import torch
+        n2, n3 = n * n, n * n * n
+        total = n3 * batch
+        if Y is None:
+            Y = torch.empty(total, dtype=torch.float64, device=X.device)
+        if work is None:
+            work = torch.empty(total, dtype=torch.float64, device=X.device)
+        self.dgemm("N", "N", n, n2 * batch, n, 1.0, A, n, X, n, 0.0, work, n, s)
+        self.dgemm_strided_batched("N", "T", n, n, n, 1.0, work, n, n2, B, n, 0, 0.0, Y, n, n2,
+                                   n * batch, s)
+        self.dgemm_strided_batched("N", "T", n2, n, n, 1.0, Y, n2, n3, C, n, 0, 0.0, work, n2, n3,
+                                   batch, s)
+        Y.copy_(work)
+        return Y
+
     # ------------------------------------------------------------ test hooks
     def debug_copy(self, which: int) -> np.ndarray:
         """Intermediate buffer `which` of the last call, copied to the host

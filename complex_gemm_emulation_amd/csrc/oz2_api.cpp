@@ -109,6 +109,50 @@ void fill_crt_tables(const ModuliPlan& pl, P* R) {
     for (int l = 0; l < 2 * pl.NL; ++l) R->M16[l] = pl.M16[l];
 }
 
+// the fused short-k path applies when k fits one wavefront's registers and
+// one of the output dimensions is small, so that the operand tile re-encoded
+// per output tile is the small one
+bool small_path(const oz2_context* h, int64_t m, int64_t n, int64_t k) {
+    return !h->debug && k >= 1 && k <= kSmallMaxK && (m <= 64 || n <= 64);
+}
+
+int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char transb, int64_t m,
+               int64_t n, int64_t k, double alpha, const double* A, int64_t lda, int64_t strideA,
+               const double* B, int64_t ldb, int64_t strideB, double beta, double* C, int64_t ldc,
+               int64_t strideC, int64_t batch, int s) {
+    if (pl.NL <= 4 && t > kMaxStdT) return OZ2_STATUS_INTERNAL;
+    SmallParams P{};
+    P.A = A; P.lda = lda; P.strideA = strideA;
+    P.B = B; P.ldb = ldb; P.strideB = strideB;
+    P.C = C; P.ldc = ldc; P.strideC = strideC;
+    P.m = m; P.n = n; P.k = k; P.batch = batch;
+    P.transa = is_trans(transa) ? 1 : 0;
+    P.transb = is_trans(transb) ? 1 : 0;
+    P.alpha = alpha; P.beta = beta;
+    P.t = t; P.s = s;
+    const bool ext = pl.NL >= 5;
+    for (int q = 0; q < s; ++q) {
+        P.mod[q] = (uint32_t)pl.mod[q];
+        P.barrett[q] = pl.barrett[q];
+        P.h[q] = pl.h[q];
+        P.K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
+        P.bias[q] = pl.gemm_bias[q];
+        for (int l = 0; l < kExtLimbs; ++l) P.c[q][l] = pl.c21[q][l];
+    }
+    fill_crt_tables(pl, &P);
+    hipStream_t stm = h->stream;
+    h->last.valid = false;
+    if (h->timing)
+        for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+    OZ2_LAUNCH(launch_small_gemm(P, pl.NL, beta != 0.0, stm));
+    if (h->timing) {
+        OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
+        OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
+        h->timed = true;
+    }
+    return OZ2_STATUS_SUCCESS;
+}
+
 int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n,
               int64_t k, const double alpha[2], const double* A, int64_t lda, const double* B,
               int64_t ldb, const double beta[2], double* C, int64_t ldc, int s) {
@@ -141,6 +185,9 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
     const int t = scaling_width(*pl, k, cplx);
     if (t < 1) return OZ2_STATUS_RANGE;
     const bool ext = t > kMaxStdT;
+    if (!cplx && small_path(h, m, n, k))
+        return small_impl(h, *pl, t, transa, transb, m, n, k, alpha[0], A, lda, 0, B, ldb, 0, beta[0], C,
+                          ldc, 0, 1, s);
 
     Layout L;
     L.sets = cplx ? 3 : 1;
@@ -376,10 +423,36 @@ int oz2_dgemm_strided_batched(oz2_handle_t h, char transa, char transb, int64_t 
                               int64_t strideA, const double* B, int64_t ldb, int64_t strideB,
                               double beta, double* C, int64_t ldc, int64_t strideC,
                               int64_t batch, int num_moduli) {
-    if (batch < 0) return -18;
+    if (!h) return -1;
+    if (!valid_op(transa)) return -2;
+    if (!valid_op(transb)) return -3;
+    if (m < 0) return -4;
+    if (n < 0) return -5;
+    if (k < 0) return -6;
+    const int64_t rows_a = is_trans(transa) ? k : m;
+    const int64_t rows_b = is_trans(transb) ? n : k;
+    if (lda < (rows_a > 1 ? rows_a : 1)) return -9;
     if (strideA < 0) return -10;
+    if (ldb < (rows_b > 1 ? rows_b : 1)) return -12;
     if (strideB < 0) return -13;
+    if (ldc < (m > 1 ? m : 1)) return -16;
     if (strideC < 0) return -17;
+    if (batch < 0) return -18;
+    if (num_moduli < kMinS || num_moduli > kMaxS) return -19;
+    if (m == 0 || n == 0 || batch == 0) return OZ2_STATUS_SUCCESS;
+    if (!C) return -15;
+    if (alpha != 0.0 && k > 0 && small_path(h, m, n, k)) {
+        if (!A) return -8;
+        if (!B) return -11;
+        const ModuliPlan* pl = moduli_plan(num_moduli);
+        if (!pl) return OZ2_STATUS_INTERNAL;
+        const int t = scaling_width(*pl, k, false);
+        if (t < 1) return OZ2_STATUS_RANGE;
+        h->timed = false;
+        return small_impl(h, *pl, t, transa, transb, m, n, k, alpha, A, lda, strideA, B, ldb, strideB,
+                          beta, C, ldc, strideC, batch, num_moduli);
+    }
+    // otherwise one call of the four-phase path per product
     const double al[2] = {alpha, 0.0}, be[2] = {beta, 0.0};
     for (int64_t b = 0; b < batch; ++b) {
         int st = gemm_impl(h, false, transa, transb, m, n, k, al, A ? A + b * strideA : nullptr,

@@ -1,0 +1,215 @@
+// oz2_device.h -- device arithmetic shared by the kernels of oz2: IEEE-bit
+// scaling, integer-only residue generation, CRT reconstruction in 16-bit
+// limbs and the correctly rounded conversion back to double.
+//
+// "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
+// Ozaki Scheme II on the Xe2 Architecture":
+//   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scale_of()
+//   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
+//   Sec. 4.2  residues from 21-bit limbs of a_hat + 2^62 with precomputed
+//             2^(21 l) mod m and K_m = (h_m - 2^62) mod m -> make_limbs(),
+//             residue_of_limbs()
+//   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
+//             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
+//             top 64 bits + sticky rounded once to double -> Crt,
+//             words_to_double()
+// Device-only; included by the .hip translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "oz2_plan.h"
+
+namespace oz2 {
+namespace dev {
+
+constexpr uint64_t kAbsMask = 0x7FFFFFFFFFFFFFFFull;
+constexpr uint64_t kInfBits = 0x7FF0000000000000ull;
+
+__device__ __forceinline__ uint64_t abs_bits(double x) {
+    return (uint64_t)__double_as_longlong(x) & kAbsMask;
+}
+
+// e(x) with 2^(e-1) <= x < 2^e for a positive finite double given by its bits
+__device__ __forceinline__ int frexp_exp_bits(uint64_t b) {
+    int eb = (int)(b >> 52);
+    return eb ? eb - 1022 : (64 - __clzll((long long)b)) - 1074;
+}
+
+// D = t - e(amax); 0 for an all-zero vector; `bad` for a non-finite one
+__device__ __forceinline__ int scale_of(uint64_t amax, int t, bool& bad) {
+    bad = amax >= kInfBits;
+    return (bad || amax == 0) ? 0 : t - frexp_exp_bits(amax);
+}
+
+// |rint(a 2^D)| for |a 2^D| < 2^61 (the standard width, t <= 61)
+__device__ __forceinline__ uint64_t rint_scaled_mag64(uint64_t bits, int D) {
+    const int eb = (int)((bits >> 52) & 0x7ff);
+    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
+    const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
+    const int sh = (eb ? eb - 1075 : -1074) + D;
+    if (sh >= 0) return sig << sh;
+    const int n = -sh;
+    if (n > 63) return 0;
+    const uint64_t q = sig >> n;
+    const uint64_t rem = sig & ((1ull << n) - 1);
+    const uint64_t half = 1ull << (n - 1);
+    return q + (uint64_t)((rem > half) | ((rem == half) & (uint32_t)(q & 1)));
+}
+
+// |rint(a 2^D)| for |a 2^D| < 2^100 (the extended width)
+__device__ __forceinline__ unsigned __int128 rint_scaled_mag128(uint64_t bits, int D) {
+    const int eb = (int)((bits >> 52) & 0x7ff);
+    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
+    const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
+    const int sh = (eb ? eb - 1075 : -1074) + D;
+    if (sh >= 0) return (unsigned __int128)sig << sh;
+    return (unsigned __int128)rint_scaled_mag64(bits, D);
+}
+
+// v mod m for v < 2^32 with q = floor(v R / 2^32), R = floor(2^32 / m):
+// q is floor(v/m) or one less, so r = v - q m lies in [0, 2m)
+__device__ __forceinline__ uint32_t mod_small(uint32_t v, uint32_t m, uint32_t R) {
+    const uint32_t q = __umulhi(v, R);
+    const uint32_t r = v - __umul24(q, m);  // q < 2^24: v/m < 5 * 2^21 + 1
+    const uint32_t r2 = r - m;
+    return r < r2 ? r : r2;
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
+}
+
+// residue limbs of one element: 21-bit limbs of a_hat + 2^62 (standard)
+// or a_hat + 2^104 (extended); sign handled by the bias
+template <bool EXT>
+struct Limbs {
+    uint32_t u[EXT ? kExtLimbs : kStdLimbs];
+};
+
+template <bool EXT>
+__device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
+    Limbs<EXT> L;
+    const uint64_t bits = (uint64_t)__double_as_longlong(a);
+    const bool neg = (bits >> 63) != 0;
+    if (!EXT) {
+        uint64_t mag = zero ? 0 : rint_scaled_mag64(bits, D);
+        uint64_t x = neg ? (1ull << 62) - mag : (1ull << 62) + mag;
+        L.u[0] = (uint32_t)(x & 0x1FFFFF);
+        L.u[1] = (uint32_t)((x >> 21) & 0x1FFFFF);
+        L.u[2] = (uint32_t)(x >> 42);
+    } else {
+        unsigned __int128 mag = zero ? 0 : rint_scaled_mag128(bits, D);
+        const unsigned __int128 bias = (unsigned __int128)1 << 104;
+        unsigned __int128 x = neg ? bias - mag : bias + mag;
+        const uint64_t lo = (uint64_t)x, hi = (uint64_t)(x >> 64);
+        L.u[0] = (uint32_t)(lo & 0x1FFFFF);
+        L.u[1] = (uint32_t)((lo >> 21) & 0x1FFFFF);
+        L.u[2] = (uint32_t)((lo >> 42) & 0x1FFFFF);
+        L.u[3] = (uint32_t)(((lo >> 63) | (hi << 1)) & 0x1FFFFF);
+        L.u[4] = (uint32_t)((hi >> 20) & 0x1FFFFF);
+    }
+    return L;
+}
+
+// (a_hat + h) mod m in [0, m), before removing the offset h, from the limbs;
+// Kc is K_m (standard or extended width), c the 2^(21 l) mod m constants
+template <bool EXT>
+__device__ __forceinline__ uint32_t residue_of_limbs(const Limbs<EXT>& L, uint32_t Kc, const uint32_t* c,
+                                                     uint32_t m, uint32_t R) {
+    uint32_t v = Kc;
+    v += __umul24(L.u[0], c[0]);
+    v += __umul24(L.u[1], c[1]);
+    v += __umul24(L.u[2], c[2]);
+    if (EXT) {
+        v += __umul24(L.u[3], c[3]);
+        v += __umul24(L.u[4], c[4]);
+    }
+    return mod_small(v, m, R);
+}
+
+// c_hat from the residues of one entry, accumulated over the moduli
+template <int NL>
+struct Crt {
+    static constexpr int L16 = 2 * NL;
+    float z;
+    int32_t L[L16];
+    __device__ __forceinline__ void init() {
+        z = 0.0f;
+#pragma unroll
+        for (int l = 0; l < L16; ++l) L[l] = 0;
+    }
+    // r in [0, m_t): every term r * W16 < 2^8 * 2^16, 24 terms < 2^29
+    __device__ __forceinline__ void add(uint32_t r, float finv, const uint32_t* W) {
+        z = __builtin_fmaf((float)r, finv, z);
+#pragma unroll
+        for (int l = 0; l < L16; ++l) L[l] += (int32_t)__umul24(r, W[l]);
+    }
+    // c_hat = Z - q M mod 2^(32 NL), two's complement words
+    __device__ __forceinline__ void finish(const uint32_t* M16, uint32_t w[NL]) {
+        const int32_t q = (int32_t)__builtin_rintf(z);  // |z - Z/M| < 2^-6, Z/M within 1/4 of q
+        int32_t carry = 0;
+        uint32_t d[L16];
+#pragma unroll
+        for (int l = 0; l < L16; ++l) {
+            const int32_t c = L[l] - q * (int32_t)M16[l] + carry;
+            d[l] = (uint32_t)c & 0xffffu;
+            carry = c >> 16;
+        }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) w[i] = d[2 * i] | (d[2 * i + 1] << 16);
+    }
+};
+
+// RN(c * 2^-S) of a two's-complement integer c given by NL 32-bit words:
+// the top 64 bits below the leading one OR-ed with a sticky bit of the rest,
+// converted once with round-to-nearest-even, then scaled by a power of two
+// (a second rounding only when the result is subnormal).
+template <int NL>
+__device__ __forceinline__ double words_to_double(uint32_t w[NL], int S) {
+    const bool neg = (w[NL - 1] >> 31) != 0;
+    if (neg) {
+        uint32_t carry = 1;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const uint32_t x = ~w[i] + carry;
+            carry = carry & (x == 0 ? 1u : 0u);
+            w[i] = x;
+        }
+    }
+    int top = -1;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+        if (w[i]) top = i;
+    if (top < 0) return 0.0;
+    uint32_t x3 = 0, x2 = 0, x1 = 0, x0 = 0, below = 0;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        if (i == top) x3 = w[i];
+        if (i == top - 1) x2 = w[i];
+        if (i == top - 2) x1 = w[i];
+        if (i == top - 3) x0 = w[i];
+        if (i < top - 3) below |= w[i];
+    }
+    const int lz = __clz((int)x3);
+    uint64_t hi = ((uint64_t)x3 << 32) | x2;
+    uint64_t lo = ((uint64_t)x1 << 32) | x0;
+    uint64_t win = hi, rest = lo;
+    if (lz) {
+        win = (hi << lz) | (lo >> (64 - lz));
+        rest = lo << lz;
+    }
+    win |= (uint64_t)((rest | below) != 0);
+    // u64 -> double with a single rounding: hi*2^32 is exact, the FMA rounds once
+    const double dh = (double)(uint32_t)(win >> 32);
+    const double dl = (double)(uint32_t)win;
+    const double d = __builtin_fma(dh, 4294967296.0, dl);
+    const int e2 = 32 * top + 31 - lz - 63 - S;
+    const double r = __builtin_ldexp(d, e2);
+    return neg ? -r : r;
+}
+
+}  // namespace dev
+}  // namespace oz2

@@ -78,6 +78,30 @@ struct ReconParams {
     uint32_t mod[kMaxS];
 };
 
+// Fused path for a short inner dimension (oz2_small.hip): every step of the
+// method for a 16 x 16 output tile in one wavefront, batched with strides.
+constexpr int64_t kSmallMaxK = 32;
+struct SmallParams {
+    const double* A;
+    int64_t lda, strideA;      // strides in doubles; 0 shares the operand
+    const double* B;
+    int64_t ldb, strideB;
+    double* C;
+    int64_t ldc, strideC;
+    int64_t m, n, k, batch;
+    int transa, transb;        // 1 = transposed ('T' or 'C')
+    int tiles_m, tiles_n;      // filled by the launcher
+    int64_t tiles_total;
+    int tiles_per_wave;
+    double alpha, beta;
+    int t, s;
+    uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS], bias[kMaxS];
+    uint32_t c[kMaxS][kExtLimbs];
+    float finv[kMaxS];
+    uint32_t W16[kMaxS][kMaxLimb16];
+    uint32_t M16[kMaxLimb16];
+};
+
 struct CrtTestParams {
     const uint8_t* R;  // [s][count]
     int64_t count;
@@ -99,5 +123,6 @@ hipError_t launch_reconstruct(const ReconParams& P, int NL, bool cplx, bool beta
 hipError_t launch_scale_c(double* C, int64_t m, int64_t n, int64_t ldc, const double beta[2],
                           bool cplx, hipStream_t st);
 hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st);
+hipError_t launch_small_gemm(SmallParams P, int NL, bool beta_nonzero, hipStream_t st);
 
 }  // namespace oz2

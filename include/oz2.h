@@ -92,7 +92,9 @@ int oz2_set_timing(oz2_handle_t h, int enable);
 
 /* Phase times in milliseconds of the last timed call: ms[0] scan (row/column
  * exponents), ms[1] encode (integerize + residues), ms[2] residue GEMM,
- * ms[3] reconstruct (CRT + alpha/beta).  Synchronizes with the last call. */
+ * ms[3] reconstruct (CRT + alpha/beta).  A call that took the fused short-k
+ * path (see oz2_dgemm) reports its single kernel in ms[2] and 0 elsewhere.
+ * Synchronizes with the last call. */
 int oz2_get_phase_times(oz2_handle_t h, float ms[4]);
 
 /* Default precision policy (Arc page Sec. 9.1): the smallest s in [2, 24]
@@ -111,7 +113,11 @@ int oz2_plan_info(int num_moduli, int64_t k, int is_complex, int32_t* moduli_out
  * transa/transb in {'N','T','C'} (upper or lower case; 'C' = 'T' here).
  * 2 <= num_moduli <= 24; k may exceed 131071 (the INT32 accumulation is
  * split internally, Arc page Sec. 4.3).  Returns OZ2_STATUS_RANGE when no
- * scaling width exists for (num_moduli, k). */
+ * scaling width exists for (num_moduli, k).
+ * Products with 1 <= k <= 32 and m <= 64 or n <= 64 take a fused path (one
+ * kernel, every step of the method per 16 x 16 output tile in registers)
+ * that gives bit-identical results to the four-phase path and needs no
+ * workspace. */
 int oz2_dgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
               double alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
               double beta, double* C, int64_t ldc, int num_moduli);
@@ -129,7 +135,12 @@ int oz2_zgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, in
  * one operand across the batch (the shared operators of a tensor mode
  * product: "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode
  * Products", Sec. 2.1 Eq. (5) and Sec. 5.1).  Every product uses its own
- * row/column exponents, as separate oz2_dgemm calls would. */
+ * row/column exponents, as separate oz2_dgemm calls would (bit-identical
+ * results).  With 1 <= k <= 32 and m <= 64 or n <= 64 the whole batch is one
+ * launch of the fused path; otherwise the products run one after another on
+ * the four-phase path.  Argument numbers of the -i codes: h 1, transa 2,
+ * transb 3, m 4, n 5, k 6, alpha 7, A 8, lda 9, strideA 10, B 11, ldb 12,
+ * strideB 13, beta 14, C 15, ldc 16, strideC 17, batch 18, num_moduli 19. */
 int oz2_dgemm_strided_batched(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n,
                               int64_t k, double alpha, const double* A, int64_t lda,
                               int64_t strideA, const double* B, int64_t ldb, int64_t strideB,
@@ -144,8 +155,10 @@ const char* oz2_status_string(int status);
  * page, Sec. 8.1).  Not needed for normal use.
  * ------------------------------------------------------------------- */
 
-/* debug = 1: later calls also keep c_hat (N_L 32-bit two's-complement words
- * per entry, entry-major, column-major entry order) in the workspace. */
+/* debug = 1: later calls take the four-phase path (never the fused short-k
+ * one) and also keep c_hat (N_L 32-bit two's-complement words per entry,
+ * entry-major, column-major entry order) in the workspace, so that every
+ * intermediate buffer can be copied out with oz2_debug_copy. */
 int oz2_set_debug(oz2_handle_t h, int debug);
 
 /* Copy an intermediate buffer of the handle's LAST call to HOST memory
