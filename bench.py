@@ -1,17 +1,27 @@
-"""Throughput of the emulated DGEMM (Ozaki scheme II on INT8 MFMA) on one MI355X.
+"""Throughput of Ozaki scheme II DGEMM/ZGEMM emulation on INT8 MFMA, one MI355X.
 
-Workload: square DGEMM M = N = K = 8192, op = N/N, alpha = 1, beta = 0,
-entries (u - 1/2) exp(0.5 g), u ~ U(0,1), g ~ N(0,1), seeded; one "step" is
-one emulated DGEMM at each s in {8, 12, 16} (three calls, every phase of the
-method inside each).  Inputs are resident in HBM before timing starts.
+Default workload (the headline): square DGEMM M = N = K = 8192, op = N/N,
+alpha = 1, beta = 0, entries (u - 1/2) exp(0.5 g), u ~ U(0,1), g ~ N(0,1),
+seeded; one "step" is one emulated DGEMM at each s in {8, 12, 16} (three
+calls, every phase of the method inside each).  Inputs are resident in HBM
+before timing starts.
 
-Printed: ONE JSON line with the metric (emulated TFLOP/s, 2MNK flops per
-call), the per-s breakdown (phase times from HIP events recorded on the
-stream the kernels run on, INT8 MFMA utilisation of the GEMM phase and HBM
-GB/s of the memory-bound phases), the roofline of the residue-GEMM kernel and
-the oracle's rate on the host cores (cpu_baseline).
+Other workloads (--workload), each printing the same kind of JSON line:
+  wide4096   DGEMM 4096^3, op T/N, alpha 1.5, beta -0.5, random C, entries
+             with exp(4 g) spread, s in {20, 24} (extended-width residues)
+  zgemm4096  ZGEMM 4096^3 via the integer 3M form, op(A) = C (conjugate
+             transpose), op(B) = N, alpha (0.7, -0.3), beta (0.2, 0.1),
+             random C, s = 16; 8 MNK flops per call
+  chain      Y = X x1 A x2 B x3 C for 32768 tensors of 16^3 with shared
+             16 x 16 operators, one emulated product per mode (s = 16);
+             metric GDoF/s = tensor entries per second of whole chains
 
-Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--s 8,12,16]
+Printed: ONE JSON line with the metric, per-call phase times (HIP events
+recorded on the stream the kernels run on), the roofline of the dominant
+kernel and the oracle's rate on a bounded sample on the host cores
+(cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload dgemm8192]
        python bench.py --copy-calibration ...   (also runs a plain device copy of
        known size first, so that hardware byte counters taken over the same
        process can be scaled to bytes)
@@ -34,20 +44,25 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 GEMM_SOURCE = os.path.join(ROOT, "complex_gemm_emulation_amd", "csrc", "oz2_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "residue_gemm_traffic.json")
 COPY_CAL_BYTES = 1 << 30     # bytes read (and written) by the calibration copy
+METRIC = "emulated DGEMM TFLOP/s at N=8192, s=8/12/16 (+ INT8 MFMA util, HBM GB/s)"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(m, n, k, s, beta_nonzero=False):
-    """Minimum work of one call (each operand read once, INT8 intermediates)."""
+def algorithmic(m, n, k, s, cplx=False, beta_nonzero=False):
+    """Minimum work of one call (each operand read once, INT8 intermediates).
+    Complex: 3 residue sets per operand (re, im, re+im), 3s products, 2 outputs."""
+    w = 2 if cplx else 1           # doubles per element
+    sets = 3 if cplx else 1
+    outs = 2 if cplx else 1
     return dict(
-        int8_ops=2.0 * m * n * k * s,
-        scan_bytes=8.0 * (m * k + k * n),
-        encode_bytes=(8.0 + s) * (m * k + k * n),
-        gemm_bytes=s * (m * k + k * n) + s * m * n,
-        recon_bytes=(s + 8.0) * m * n + (8.0 * m * n if beta_nonzero else 0.0),
+        int8_ops=2.0 * m * n * k * s * sets,
+        scan_bytes=8.0 * w * (m * k + k * n),
+        encode_bytes=(8.0 * w + sets * s) * (m * k + k * n),
+        gemm_bytes=sets * s * (m * k + k * n) + outs * s * m * n,
+        recon_bytes=(outs * s + 8.0 * w) * m * n + (8.0 * w * m * n if beta_nonzero else 0.0),
     )
 
 
@@ -56,15 +71,16 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per residue-GEMM launch from the committed counter runs,
-    or None when the kernel source changed since they were taken."""
+def measured_traffic(workload):
+    """HBM bytes per residue-GEMM launch from the committed counter runs of
+    this workload, or None when the kernel source changed since they were
+    taken (or none were taken for this workload)."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_digest(GEMM_SOURCE):
+    if rec.get("source_sha256_16") != source_digest(GEMM_SOURCE) or rec.get("bench_workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -81,65 +97,87 @@ def copy_calibration(torch):
     del src, dst
 
 
-def cpu_baseline(A, B, m, n, k, s, side, seed=12345):
+def sample_entries(m, n, side, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, min(side, m), replace=False)]))[:side]
+    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(side, n), replace=False)]))[:side]
+    ii, jj = np.meshgrid(rows, cols, indexing="ij")
+    return ii.reshape(-1), jj.reshape(-1), rows.size, cols.size
+
+
+def cpu_baseline_gemm(spec, ops_a, A, B, C, s, side, label):
     """The oracle (as it stands) on a seeded side x side sample of output
     entries of the same workload, on all host cores."""
     import oracle
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, side, replace=False)]))[:side]
-    cols = np.unique(np.concatenate([[0, n - 1], rng.choice(n, side, replace=False)]))[:side]
-    ii, jj = np.meshgrid(rows, cols, indexing="ij")
+    m, n, k = spec["m"], spec["n"], spec["k"]
+    ii, jj, nr, nc = sample_entries(m, n, side, 12345)
     nt = oracle.max_threads()
+    lda, ldb = ops_a
     t0 = time.perf_counter()
-    oracle.gemm_entries(False, "N", "N", m, n, k, 1.0, A, m, B, k, 0.0, None, m, s,
-                        rows=ii.reshape(-1), cols=jj.reshape(-1), nthreads=nt)
+    oracle.gemm_entries(spec["cplx"], spec["transa"], spec["transb"], m, n, k, spec["alpha"], A, lda,
+                        B, ldb, spec["beta"], C, m, s, rows=ii, cols=jj, nthreads=nt)
     dt = time.perf_counter() - t0
-    entries = ii.size
-    return dict(value=2.0 * k * entries / dt / 1e12, unit="TFLOP/s", cores=nt, kind="oracle",
-                sample=f"{rows.size}x{cols.size} sampled output entries of the {m}x{n}x{k} "
-                       f"s={s} workload (exact wide-integer products), {dt:.1f} s")
+    flops_per_entry = (8.0 if spec["cplx"] else 2.0) * k
+    return dict(value=flops_per_entry * ii.size / dt / 1e12, unit="TFLOP/s", cores=nt, kind="oracle",
+                sample=f"{nr}x{nc} sampled output entries of the {label} s={s} workload "
+                       f"(exact wide-integer products), {dt:.1f} s")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--s", type=str, default="8,12,16")
-    ap.add_argument("--n", type=int, default=8192)
-    ap.add_argument("--cpu-side", type=int, default=1024)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: the emulated GEMM of a single device "
-              f"(got --gpus {args.gpus}); multi-GPU runs are not part of this build",
-              file=sys.stderr)
-        sys.exit(2)
+GEMM_SPECS = {
+    "dgemm8192": dict(cplx=False, m=8192, n=8192, k=8192, s=[8, 12, 16], transa="N", transb="N",
+                      alpha=1.0, beta=0.0, phi=0.5, seedw=2, cpu_side=1024),
+    "wide4096": dict(cplx=False, m=4096, n=4096, k=4096, s=[20, 24], transa="T", transb="N",
+                     alpha=1.5, beta=-0.5, phi=4.0, seedw=3, cpu_side=640),
+    "zgemm4096": dict(cplx=True, m=4096, n=4096, k=4096, s=[16], transa="C", transb="N",
+                      alpha=complex(0.7, -0.3), beta=complex(0.2, 0.1), phi=0.5, seedw=4,
+                      cpu_side=512),
+}
 
+
+def run_gemm(args, name):
     import torch
     import complex_gemm_emulation_amd as oz2
     import workloads
 
-    if args.copy_calibration:
-        log(f"[bench] calibration copy of {COPY_CAL_BYTES} bytes x 3")
-        copy_calibration(torch)
-    s_list = [int(x) for x in args.s.split(",")]
-    m = n = k = args.n
-    log(f"[bench] generating {m}x{k} and {k}x{n} inputs (phi = 0.5, seeded)")
-    A = workloads.real_matrix(m, k, workloads.seed(2, 0), "phi", 0.5)
-    B = workloads.real_matrix(k, n, workloads.seed(2, 1), "phi", 0.5)
+    spec = dict(GEMM_SPECS[name])
+    if args.s:
+        spec["s"] = [int(x) for x in args.s.split(",")]
+    if args.n and name == "dgemm8192":
+        spec["m"] = spec["n"] = spec["k"] = args.n
+    m, n, k, cplx = spec["m"], spec["n"], spec["k"], spec["cplx"]
+    ta, tb = spec["transa"], spec["transb"]
+    w = workloads.seed
+    ra, ca = workloads.stored_shape(ta, m, k)
+    rb, cb = workloads.stored_shape(tb, k, n)
+    log(f"[bench] {name}: generating inputs (seeded)")
+    if cplx:
+        A = workloads.complex_matrix(ra, ca, w(spec["seedw"], 0), w(spec["seedw"], 3), "phi", spec["phi"])
+        B = workloads.complex_matrix(rb, cb, w(spec["seedw"], 1), w(spec["seedw"], 4), "phi", spec["phi"])
+        C = workloads.complex_matrix(m, n, w(spec["seedw"], 2), w(spec["seedw"], 5), "uniform")
+    else:
+        A = workloads.real_matrix(ra, ca, w(spec["seedw"], 0), "phi", spec["phi"])
+        B = workloads.real_matrix(rb, cb, w(spec["seedw"], 1), "phi", spec["phi"])
+        C = workloads.real_matrix(m, n, w(spec["seedw"], 2), "uniform") if spec["beta"] != 0 else None
     dA = torch.from_numpy(A).cuda()
     dB = torch.from_numpy(B).cuda()
-    dC = torch.zeros(m * n, dtype=torch.float64, device="cuda")
+    # beta != 0: C starts as the seeded random matrix; later calls update it in
+    # place (|beta| < 1 keeps it bounded), the same work every call
+    if C is not None:
+        dC = torch.from_numpy(C.copy()).cuda()
+    else:
+        dC = torch.zeros(m * n, dtype=torch.complex128 if cplx else torch.float64, device="cuda")
     stream = torch.cuda.current_stream()
+    s_list = spec["s"]
     handles = {s: oz2.Handle(stream) for s in s_list}
     for h in handles.values():
         h.set_timing(True)
 
     def step(record):
         for s in s_list:
-            handles[s].dgemm("N", "N", m, n, k, 1.0, dA, m, dB, k, 0.0, dC, m, s)
+            if cplx:
+                handles[s].zgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
+            else:
+                handles[s].dgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
         if record is not None:
             for s in s_list:
                 record[s].append(handles[s].phase_times())
@@ -157,65 +195,183 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt / args.steps * 1e3
-    flops_per_step = 2.0 * m * n * k * len(s_list)
-    value = flops_per_step / (dt / args.steps) / 1e12
+    fl = (8.0 if cplx else 2.0) * m * n * k
+    value = fl * len(s_list) / (dt / args.steps) / 1e12
 
     per_s = {}
     gemm_ops = gemm_ms = 0.0
+    beta_nz = spec["beta"] != 0
     for s in s_list:
         ph = np.mean(np.array(phases[s]), axis=0)  # ms: scan, encode, gemm, reconstruct
-        w = algorithmic(m, n, k, s)
+        wk = algorithmic(m, n, k, s, cplx, beta_nz)
         call_ms = float(np.sum(ph))
         per_s[str(s)] = dict(
-            tflops=2.0 * m * n * k / (call_ms * 1e-3) / 1e12,
+            tflops=fl / (call_ms * 1e-3) / 1e12,
             ms=dict(scan=round(float(ph[0]), 4), encode=round(float(ph[1]), 4),
                     gemm=round(float(ph[2]), 4), reconstruct=round(float(ph[3]), 4)),
-            gemm_int8_tops=w["int8_ops"] / (ph[2] * 1e-3) / 1e12,
-            gemm_int8_util=w["int8_ops"] / (ph[2] * 1e-3) / 1e12 / PEAK_INT8_TOPS,
-            scan_gbs=w["scan_bytes"] / (ph[0] * 1e-3) / 1e9,
-            encode_gbs=w["encode_bytes"] / (ph[1] * 1e-3) / 1e9,
-            reconstruct_gbs=w["recon_bytes"] / (ph[3] * 1e-3) / 1e9,
+            gemm_int8_tops=wk["int8_ops"] / (ph[2] * 1e-3) / 1e12,
+            gemm_int8_util=wk["int8_ops"] / (ph[2] * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+            scan_gbs=wk["scan_bytes"] / (ph[0] * 1e-3) / 1e9,
+            encode_gbs=wk["encode_bytes"] / (ph[1] * 1e-3) / 1e9,
+            reconstruct_gbs=wk["recon_bytes"] / (ph[3] * 1e-3) / 1e9,
         )
-        gemm_ops += w["int8_ops"]
+        gemm_ops += wk["int8_ops"]
         gemm_ms += float(ph[2])
-    # residue GEMM: one launch per call; the mean launch of a step does
-    # 2 M N K (sum of s) / len(s) INT8 ops, timed by HIP events on its stream
+    # residue GEMM: one launch per call; the mean launch of a step does the
+    # mean of the calls' INT8 ops, timed by HIP events on its stream
     achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
-    traffic = measured_traffic()
     roofline = dict(kernel="residue_gemm_kernel (INT8 MFMA, fused mod m)", bound="mfma",
                     achieved=round(achieved, 2), peak=PEAK_INT8_TOPS, unit="TOP/s",
-                    frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=traffic,
+                    frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=measured_traffic(name),
                     ops_per_launch=gemm_ops / len(s_list),
                     launch_ms=round(gemm_ms / len(s_list), 4))
 
     cpu = None
     if not args.no_cpu_baseline:
         s_cpu = s_list[-1]
-        log(f"[bench] oracle cpu baseline on a {args.cpu_side}^2 entry sample, s={s_cpu}")
-        cpu = cpu_baseline(A, B, m, n, k, s_cpu, args.cpu_side)
+        side = args.cpu_side or spec["cpu_side"]
+        log(f"[bench] oracle cpu baseline on a {side}^2 entry sample, s={s_cpu}")
+        cpu = cpu_baseline_gemm(spec, (ra, rb), A, B, C, s_cpu, side, f"{m}x{n}x{k}")
 
-    out = {
-        "metric": "emulated DGEMM TFLOP/s at N=8192, s=8/12/16 (+ INT8 MFMA util, HBM GB/s)",
+    for h in handles.values():
+        h.close()
+    kind = "zgemm" if cplx else "dgemm"
+    return {
+        "metric": METRIC if name == "dgemm8192" else
+                  f"emulated {'ZGEMM' if cplx else 'DGEMM'} TFLOP/s ({'8' if cplx else '2'}MNK/t)",
         "value": round(value, 3),
         "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "i8",
-        "data": "synthetic",
-        "config": {"workload": f"dgemm_{m}_NN_phi0.5_s{'_'.join(map(str, s_list))}",
-                   "m": m, "n": n, "k": k, "s": s_list, "ops": "N/N", "alpha": 1.0, "beta": 0.0},
+        "config": {"workload": f"{kind}_{m}_{ta}{tb}_phi{spec['phi']}_s{'_'.join(map(str, s_list))}",
+                   "m": m, "n": n, "k": k, "s": s_list, "ops": f"{ta}/{tb}",
+                   "alpha": str(spec["alpha"]), "beta": str(spec["beta"])},
         "per_s": per_s,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out))
-    for h in handles.values():
-        h.close()
+
+
+def oracle_chain(X, Aop, Bop, Cop, n, nt, s):
+    """The three emulated modes of nt tensors with the oracle, as the library
+    decomposes them (mode 1 over all nt tensors at once)."""
+    import oracle
+    n2, n3 = n * n, n ** 3
+    z1 = oracle.gemm_entries(False, "N", "N", n, n2 * nt, n, 1.0, Aop, n, X[:n3 * nt], n, 0.0, None,
+                             n, s, nthreads=oracle.max_threads())["out"]
+    z2 = np.zeros(n3 * nt)
+    for q in range(n * nt):
+        z2[q * n2:(q + 1) * n2] = oracle.gemm_entries(False, "N", "T", n, n, n, 1.0, z1[q * n2:],
+                                                      n, Bop, n, 0.0, None, n, s, nthreads=1)["out"]
+    y = np.zeros(n3 * nt)
+    for b in range(nt):
+        y[b * n3:(b + 1) * n3] = oracle.gemm_entries(False, "N", "T", n2, n, n, 1.0, z2[b * n3:], n2,
+                                                     Cop, n, 0.0, None, n2, s, nthreads=1)["out"]
+    return y
+
+
+def run_chain(args):
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+
+    w = workloads.WORKLOADS[5]
+    n, batch, s = w["n"], w["batch"], w["s"][0]
+    n3 = n ** 3
+    log(f"[bench] chain: generating {batch} tensors of {n}^3 (seeded)")
+    X = workloads.tensor_batch(n, batch, workloads.seed(5, 0))
+    ops = [workloads.real_matrix(n, n, workloads.seed(5, q)) for q in (1, 2, 3)]
+    dX = torch.from_numpy(X).cuda()
+    dops = [torch.from_numpy(o).cuda() for o in ops]
+    dY = torch.empty_like(dX)
+    work = torch.empty_like(dX)
+    h = oz2.Handle(torch.cuda.current_stream())
+    h.set_timing(True)
+    launch_ms = []
+
+    def step(record):
+        h.tensor_mode_chain(dX, dops[0], dops[1], dops[2], n, batch, s, Y=dY, work=work)
+        if record is not None:
+            launch_ms.append(h.phase_times()[2])  # the last mode's fused launch
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(launch_ms)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / args.steps * 1e3
+    dofs = float(n3 * batch)
+    value = dofs / (dt / args.steps) / 1e9
+    # the fused kernel reads each input entry and writes each output entry once
+    lm = float(np.mean(launch_ms))
+    bytes_per_launch = 16.0 * n3 * batch
+    achieved = bytes_per_launch / (lm * 1e-3) / 1e9
+    roofline = dict(kernel="small_gemm_kernel (fused short-k Ozaki II, mode 3)", bound="hbm",
+                    achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                    bytes_per_launch=bytes_per_launch, launch_ms=round(lm, 4))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = args.chain_cpu_tensors
+        log(f"[bench] oracle cpu baseline on {nt} tensors")
+        t0 = time.perf_counter()
+        oracle_chain(X, ops[0], ops[1], ops[2], n, nt, s)
+        cdt = time.perf_counter() - t0
+        cpu = dict(value=n3 * nt / cdt / 1e9, unit="GDoF/s", cores=oracle.max_threads(), kind="oracle",
+                   sample=f"first {nt} of the {batch} tensors, all three modes, {cdt:.1f} s")
+    h.close()
+    return {
+        "metric": "tensor-mode chain GDoF/s (Y = X x1 A x2 B x3 C, per-mode Ozaki II)",
+        "value": round(value, 3),
+        "unit": "GDoF/s",
+        "ms_per_step": round(ms_per_step, 3),
+        "dtype": "i8",
+        "config": {"workload": f"tensor_chain_n{n}_b{batch}_s{s}", "n": n, "batch": batch, "s": s,
+                   "modes": 3, "emulated_tflops": round(3 * 2.0 * n * dofs / (dt / args.steps) / 1e12, 3)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="dgemm8192",
+                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain"])
+    ap.add_argument("--s", type=str, default="")
+    ap.add_argument("--n", type=int, default=0)
+    ap.add_argument("--cpu-side", type=int, default=0)
+    ap.add_argument("--chain-cpu-tensors", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the emulated GEMM of a single device "
+              f"(got --gpus {args.gpus}); runs on several GPUs are not part of this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        log(f"[bench] calibration copy of {COPY_CAL_BYTES} bytes x 3")
+        copy_calibration(torch)
+    out = run_chain(args) if args.workload == "chain" else run_gemm(args, args.workload)
+    line = {"metric": out["metric"], "value": out["value"], "unit": out["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
+            "data": "synthetic", "config": out["config"]}
+    for key in ("per_s", "roofline", "cpu_baseline"):
+        if key in out:
+            line[key] = out[key]
+    print(json.dumps(line))
 
 
 if __name__ == "__main__":

@@ -235,12 +235,12 @@ class Handle:
             Y = torch.empty(total, dtype=torch.float64, device=X.device)
         if work is None:
             work = torch.empty(total, dtype=torch.float64, device=X.device)
-        self.dgemm("N", "N", n, n2 * batch, n, 1.0, A, n, X, n, 0.0, work, n, s)
-        self.dgemm_strided_batched("N", "T", n, n, n, 1.0, work, n, n2, B, n, 0, 0.0, Y, n, n2,
+        # X -> Y (mode 1) -> work (mode 2) -> Y (mode 3)
+        self.dgemm("N", "N", n, n2 * batch, n, 1.0, A, n, X, n, 0.0, Y, n, s)
+        self.dgemm_strided_batched("N", "T", n, n, n, 1.0, Y, n, n2, B, n, 0, 0.0, work, n, n2,
                                    n * batch, s)
-        self.dgemm_strided_batched("N", "T", n2, n, n, 1.0, Y, n2, n3, C, n, 0, 0.0, work, n2, n3,
+        self.dgemm_strided_batched("N", "T", n2, n, n, 1.0, work, n2, n3, C, n, 0, 0.0, Y, n2, n3,
                                    batch, s)
-        Y.copy_(work)
         return Y
 
     # ------------------------------------------------------------ test hooks
