@@ -130,72 +130,98 @@ __device__ __forceinline__ uint32_t residue_of_limbs(const Limbs<EXT>& L, uint32
     return mod_small(v, m, R);
 }
 
-// c_hat from the residues of one entry, accumulated over the moduli
+// c_hat from the residues of one entry, accumulated over the moduli two at a
+// time: z with two FP32 FMAs in ascending t, the 16-bit limbs of
+// r_t W_t + r_(t+1) W_(t+1) with one v_dot2_u32_u16 per limb (r and the two
+// limbs of W packed as 16-bit pairs).  Every term r W16 < 2^8 2^16, so the
+// limb sums of 24 moduli stay below 2^29.
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
 template <int NL>
 struct Crt {
     static constexpr int L16 = 2 * NL;
     float z;
-    int32_t L[L16];
+    uint32_t L[L16];
     __device__ __forceinline__ void init() {
         z = 0.0f;
 #pragma unroll
-        for (int l = 0; l < L16; ++l) L[l] = 0;
+        for (int l = 0; l < L16; ++l) L[l] = 0u;
     }
-    // r in [0, m_t): every term r * W16 < 2^8 * 2^16, 24 terms < 2^29
-    __device__ __forceinline__ void add(uint32_t r, float finv, const uint32_t* W) {
-        z = __builtin_fmaf((float)r, finv, z);
+    // moduli t, t+1: residues packed as ra | rb << 16 (rb = 0 past the last
+    // modulus, where fb = 0 and the high halves of W2 are 0 too); fra, frb the
+    // residues as floats; W2[l] = W16[t][l] | W16[t+1][l] << 16
+    __device__ __forceinline__ void add2(uint32_t packed, float fra, float frb, float fa, float fb,
+                                         const uint32_t* W2) {
+        z = __builtin_fmaf(fra, fa, z);
+        z = __builtin_fmaf(frb, fb, z);
+        const v2u16 r = __builtin_bit_cast(v2u16, packed);
 #pragma unroll
-        for (int l = 0; l < L16; ++l) L[l] += (int32_t)__umul24(r, W[l]);
+        for (int l = 0; l < L16; ++l)
+            L[l] = __builtin_amdgcn_udot2(r, __builtin_bit_cast(v2u16, W2[l]), L[l], false);
     }
-    // c_hat = Z - q M mod 2^(32 NL), two's complement words
+    __device__ __forceinline__ void add2(uint32_t ra, uint32_t rb, float fa, float fb, const uint32_t* W2) {
+        add2(ra | (rb << 16), (float)ra, (float)rb, fa, fb, W2);
+    }
+    // c_hat = Z - q M mod 2^(32 NL), two's complement words.  |q| <= 24 * 256
+    // and M16 < 2^16, so q M16 fits the 24-bit multiplier; one carry pass.
     __device__ __forceinline__ void finish(const uint32_t* M16, uint32_t w[NL]) {
         const int32_t q = (int32_t)__builtin_rintf(z);  // |z - Z/M| < 2^-6, Z/M within 1/4 of q
         int32_t carry = 0;
-        uint32_t d[L16];
+        uint32_t lo16 = 0;
 #pragma unroll
         for (int l = 0; l < L16; ++l) {
-            const int32_t c = L[l] - q * (int32_t)M16[l] + carry;
-            d[l] = (uint32_t)c & 0xffffu;
+            const int32_t c = (int32_t)L[l] + __mul24(-q, (int32_t)M16[l]) + carry;
+            if (l & 1)
+                w[l >> 1] = lo16 | ((uint32_t)c << 16);
+            else
+                lo16 = (uint32_t)c & 0xffffu;
             carry = c >> 16;
         }
-#pragma unroll
-        for (int i = 0; i < NL; ++i) w[i] = d[2 * i] | (d[2 * i + 1] << 16);
     }
 };
 
 // RN(c * 2^-S) of a two's-complement integer c given by NL 32-bit words:
 // the top 64 bits below the leading one OR-ed with a sticky bit of the rest,
 // converted once with round-to-nearest-even, then scaled by a power of two
-// (a second rounding only when the result is subnormal).
+// (a second rounding only when the result is subnormal).  Branch-free: the
+// magnitude by xor and carry, the leading word moved to the top in steps of
+// 4, 2 and 1 words.
 template <int NL>
 __device__ __forceinline__ double words_to_double(uint32_t w[NL], int S) {
-    const bool neg = (w[NL - 1] >> 31) != 0;
-    if (neg) {
-        uint32_t carry = 1;
-#pragma unroll
-        for (int i = 0; i < NL; ++i) {
-            const uint32_t x = ~w[i] + carry;
-            carry = carry & (x == 0 ? 1u : 0u);
-            w[i] = x;
-        }
-    }
-    int top = -1;
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-        if (w[i]) top = i;
-    if (top < 0) return 0.0;
-    uint32_t x3 = 0, x2 = 0, x1 = 0, x0 = 0, below = 0;
+    const uint32_t sgn = (uint32_t)((int32_t)w[NL - 1] >> 31);
+    uint32_t c = sgn & 1u;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-        if (i == top) x3 = w[i];
-        if (i == top - 1) x2 = w[i];
-        if (i == top - 2) x1 = w[i];
-        if (i == top - 3) x0 = w[i];
-        if (i < top - 3) below |= w[i];
+        const uint32_t y = (w[i] ^ sgn) + c;
+        c = y < c ? 1u : 0u;
+        w[i] = y;
     }
+    int shift = 0;
+    if (NL > 4) {
+        const bool z4 = (w[NL - 1] | w[NL - 2] | w[NL - 3] | w[NL - 4]) == 0;
+#pragma unroll
+        for (int i = NL - 1; i >= 0; --i) w[i] = z4 ? (i >= 4 ? w[i - 4] : 0u) : w[i];
+        shift += z4 ? 4 : 0;
+    }
+    if (NL > 2) {
+        const bool z2 = (w[NL - 1] | w[NL - 2]) == 0;
+#pragma unroll
+        for (int i = NL - 1; i >= 0; --i) w[i] = z2 ? (i >= 2 ? w[i - 2] : 0u) : w[i];
+        shift += z2 ? 2 : 0;
+    }
+    {
+        const bool z1 = w[NL - 1] == 0;
+#pragma unroll
+        for (int i = NL - 1; i >= 0; --i) w[i] = z1 ? (i >= 1 ? w[i - 1] : 0u) : w[i];
+        shift += z1 ? 1 : 0;
+    }
+    const uint32_t x3 = w[NL - 1];
     const int lz = __clz((int)x3);
-    uint64_t hi = ((uint64_t)x3 << 32) | x2;
-    uint64_t lo = ((uint64_t)x1 << 32) | x0;
+    const uint64_t hi = ((uint64_t)x3 << 32) | w[NL - 2];
+    const uint64_t lo = NL >= 4 ? (((uint64_t)w[NL - 3] << 32) | w[NL - 4]) : (NL == 3 ? ((uint64_t)w[0] << 32) : 0ull);
+    uint32_t below = 0;
+#pragma unroll
+    for (int i = 0; i + 4 < NL; ++i) below |= w[i];
     uint64_t win = hi, rest = lo;
     if (lz) {
         win = (hi << lz) | (lo >> (64 - lz));
@@ -206,9 +232,9 @@ __device__ __forceinline__ double words_to_double(uint32_t w[NL], int S) {
     const double dh = (double)(uint32_t)(win >> 32);
     const double dl = (double)(uint32_t)win;
     const double d = __builtin_fma(dh, 4294967296.0, dl);
-    const int e2 = 32 * top + 31 - lz - 63 - S;
-    const double r = __builtin_ldexp(d, e2);
-    return neg ? -r : r;
+    const int e2 = 32 * (NL - 1 - shift) + 31 - lz - 63 - S;
+    const double r = x3 ? __builtin_ldexp(d, e2) : 0.0;  // integer zero gives +0
+    return sgn ? -r : r;
 }
 
 }  // namespace dev

@@ -73,7 +73,7 @@ struct ReconParams {
     int t, s;
     uint32_t* chat;         // optional debug copy of c_hat words [outs][n][mp][NL]
     float finv[kMaxS];
-    uint32_t W16[kMaxS][kMaxLimb16];
+    uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];
     uint32_t mod[kMaxS];
 };
@@ -98,7 +98,7 @@ struct SmallParams {
     uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS], bias[kMaxS];
     uint32_t c[kMaxS][kExtLimbs];
     float finv[kMaxS];
-    uint32_t W16[kMaxS][kMaxLimb16];
+    uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];
 };
 
@@ -108,7 +108,7 @@ struct CrtTestParams {
     uint32_t* words;   // [count][NL]
     int s;
     float finv[kMaxS];
-    uint32_t W16[kMaxS][kMaxLimb16];
+    uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];
 };
 

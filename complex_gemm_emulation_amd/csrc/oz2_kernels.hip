@@ -221,18 +221,41 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
 
     const int64_t plane = P.n * P.mp;
     const uint8_t* src = P.R + j * P.mp + i0;
-    for (int t = 0; t < P.s; ++t) {
-        const float fi = P.finv[t];
-        const uint32_t* W = P.W16[t];
+    // the residue words of 4 entries for every modulus (k runs summed mod m_t,
+    // Arc page Sec. 4.3), all loads issued before any arithmetic; s <= 4 NL
+    constexpr int SMAX = 4 * NL;
 #pragma unroll
-        for (int o = 0; o < (CPLX ? 2 : 1); ++o) {
-            const uint8_t* at = src + o * P.r_set_stride + t * plane;
-            uint32_t rw = *(const uint32_t*)at;
-            // residues of the k runs (Arc page Sec. 4.3) are summed mod m_t
-            for (int c = 1; c < P.chunks; ++c)
-                rw = add_mod_bytes(rw, *(const uint32_t*)(at + c * P.r_chunk_stride), P.mod[t]);
+    for (int o = 0; o < (CPLX ? 2 : 1); ++o) {
+        uint32_t rw[SMAX];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[o][e].add((rw >> (8 * e)) & 0xffu, fi, W);
+        for (int t = 0; t < SMAX; ++t) {
+            rw[t] = 0u;
+            if (t < P.s) rw[t] = *(const uint32_t*)(src + o * P.r_set_stride + t * plane);
+        }
+        for (int c = 1; c < P.chunks; ++c) {
+#pragma unroll
+            for (int t = 0; t < SMAX; ++t)
+                if (t < P.s)
+                    rw[t] = add_mod_bytes(rw[t], *(const uint32_t*)(src + o * P.r_set_stride + t * plane +
+                                                                     c * P.r_chunk_stride),
+                                          P.mod[t]);
+        }
+#pragma unroll
+        for (int t = 0; t < SMAX; t += 2) {
+            if (t < P.s) {
+                const float fa = P.finv[t], fb = P.finv[t + 1];
+                const uint32_t* W2 = P.W2[t >> 1];
+                const uint32_t wa = rw[t], wb = rw[t + 1];
+                // entry e: byte e of wa in bits 0-7, byte e of wb in bits 16-23
+                acc[o][0].add2(__builtin_amdgcn_perm(wb, wa, 0x0c040c00u), (float)(wa & 0xffu),
+                               (float)(wb & 0xffu), fa, fb, W2);
+                acc[o][1].add2(__builtin_amdgcn_perm(wb, wa, 0x0c050c01u), (float)((wa >> 8) & 0xffu),
+                               (float)((wb >> 8) & 0xffu), fa, fb, W2);
+                acc[o][2].add2(__builtin_amdgcn_perm(wb, wa, 0x0c060c02u), (float)((wa >> 16) & 0xffu),
+                               (float)((wb >> 16) & 0xffu), fa, fb, W2);
+                acc[o][3].add2(__builtin_amdgcn_perm(wb, wa, 0x0c070c03u), (float)(wa >> 24), (float)(wb >> 24),
+                               fa, fb, W2);
+            }
         }
     }
 
@@ -295,7 +318,9 @@ __global__ __launch_bounds__(256) void crt_test_kernel(CrtTestParams P) {
     if (q >= P.count) return;
     Crt<NL> acc;
     acc.init();
-    for (int t = 0; t < P.s; ++t) acc.add(P.R[t * P.count + q], P.finv[t], P.W16[t]);
+    for (int t = 0; t < P.s; t += 2)
+        acc.add2(P.R[t * P.count + q], t + 1 < P.s ? P.R[(t + 1) * P.count + q] : 0u, P.finv[t], P.finv[t + 1],
+                 P.W2[t >> 1]);
     uint32_t w[NL];
     acc.finish(P.M16, w);
 #pragma unroll

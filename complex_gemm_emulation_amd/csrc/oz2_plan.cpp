@@ -209,6 +209,11 @@ void build_plan(int s, ModuliPlan* p) {
         const uint64_t lo = (1ull << 31) - (1ull << 20) + 255;
         p->gemm_bias[t] = (uint32_t)(((lo + m - 1) / m) * m);
     }
+    // limb pairs for the two-moduli-per-instruction CRT accumulation; past the
+    // last modulus the high halves stay 0
+    for (int u = 0; u < (s + 1) / 2; ++u)
+        for (int l = 0; l < 2 * p->NL; ++l)
+            p->W2[u][l] = p->W16[2 * u][l] | (2 * u + 1 < s ? p->W16[2 * u + 1][l] << 16 : 0u);
 }
 
 std::once_flag g_once[kMaxS + 1];

@@ -46,6 +46,7 @@ struct ModuliPlan {
     float finv[kMaxS] = {};       // fl32(y_t / m_t), y_t = (M/m_t)^-1 mod m_t
     uint32_t W16[kMaxS][kMaxLimb16] = {};  // 16-bit limbs of W_t = (M/m_t) y_t
     uint32_t M16[kMaxLimb16] = {};         // 16-bit limbs of M
+    uint32_t W2[kMaxS / 2][kMaxLimb16] = {};  // W16 of moduli 2u and 2u+1 packed in 16-bit halves
     // residue generation (Sec. 4.2)
     uint32_t h[kMaxS] = {};       // floor((m-1)/2)
     uint32_t c21[kMaxS][kExtLimbs] = {};   // 2^(21 l) mod m

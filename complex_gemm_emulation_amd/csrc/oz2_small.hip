@@ -126,12 +126,19 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
         for (int e = 0; e < 4; ++e) acc[e].init();
         const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-        for (int t = 0; t < SMAX; ++t) {
+        for (int t = 0; t < SMAX; t += 2) {
             if (t < P.s) {
-                const v4i c = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t], fb[t], zero, 0, 0, 0);
-                const uint32_t m = P.mod[t], R = P.barrett[t], bias = P.bias[t];
+                const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t], fb[t], zero, 0, 0, 0);
+                const bool two = t + 1 < P.s;
+                const v4i cb = two ? __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1], fb[t + 1], zero, 0, 0, 0) : zero;
+                const uint32_t m0 = P.mod[t], R0 = P.barrett[t], b0 = P.bias[t];
+                const uint32_t m1 = P.mod[t + 1], R1 = P.barrett[t + 1], b1 = P.bias[t + 1];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e].add(acc_mod(c[e], m, R, bias), P.finv[t], P.W16[t]);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t ra = acc_mod(ca[e], m0, R0, b0);
+                    const uint32_t rb = two ? acc_mod(cb[e], m1, R1, b1) : 0u;
+                    acc[e].add2(ra, rb, P.finv[t], P.finv[t + 1], P.W2[t >> 1]);
+                }
             }
         }
 
