@@ -96,7 +96,7 @@ void fill_mod_tables(const ModuliPlan& pl, EncodeParams* E, bool ext) {
         E->barrett[q] = pl.barrett[q];
         E->h[q] = pl.h[q];
         E->K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
-        for (int l = 0; l < kExtLimbs; ++l) E->c[q][l] = pl.c21[q][l];
+        for (int l = 0; l < kExtWords; ++l) E->c[q][l] = pl.c2[q][l];
     }
 }
 
@@ -136,7 +136,7 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
         P.h[q] = pl.h[q];
         P.K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
         P.bias[q] = pl.gemm_bias[q];
-        for (int l = 0; l < kExtLimbs; ++l) P.c[q][l] = pl.c21[q][l];
+        for (int l = 0; l < kExtWords; ++l) P.c[q][l] = pl.c2[q][l];
     }
     fill_crt_tables(pl, &P);
     hipStream_t stm = h->stream;

@@ -6,8 +6,10 @@
 // Ozaki Scheme II on the Xe2 Architecture":
 //   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scale_of()
 //   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
-//   Sec. 4.2  residues from 21-bit limbs of a_hat + 2^62 with precomputed
-//             2^(21 l) mod m and K_m = (h_m - 2^62) mod m -> make_limbs(),
+//   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
+//             2^(limb position) mod m and K_m = (h_m - 2^62) mod m; the page
+//             uses 21-bit limbs, here 16-bit limbs read in pairs by
+//             v_dot2_u32_u16 (the same congruence) -> make_limbs(),
 //             residue_of_limbs()
 //   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
 //             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
@@ -82,11 +84,12 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
     return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
 }
 
-// residue limbs of one element: 21-bit limbs of a_hat + 2^62 (standard)
-// or a_hat + 2^104 (extended); sign handled by the bias
+// residue limbs of one element: the 32-bit words of a_hat + 2^62 (standard
+// width) or a_hat + 2^104 (extended width), each read as a pair of 16-bit
+// limbs; the sign is absorbed by the bias
 template <bool EXT>
 struct Limbs {
-    uint32_t u[EXT ? kExtLimbs : kStdLimbs];
+    uint32_t w[EXT ? kExtWords : kStdWords];
 };
 
 template <bool EXT>
@@ -95,38 +98,35 @@ __device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
     const uint64_t bits = (uint64_t)__double_as_longlong(a);
     const bool neg = (bits >> 63) != 0;
     if (!EXT) {
-        uint64_t mag = zero ? 0 : rint_scaled_mag64(bits, D);
-        uint64_t x = neg ? (1ull << 62) - mag : (1ull << 62) + mag;
-        L.u[0] = (uint32_t)(x & 0x1FFFFF);
-        L.u[1] = (uint32_t)((x >> 21) & 0x1FFFFF);
-        L.u[2] = (uint32_t)(x >> 42);
+        const uint64_t mag = zero ? 0 : rint_scaled_mag64(bits, D);
+        const uint64_t x = neg ? (1ull << 62) - mag : (1ull << 62) + mag;
+        L.w[0] = (uint32_t)x;
+        L.w[1] = (uint32_t)(x >> 32);
     } else {
-        unsigned __int128 mag = zero ? 0 : rint_scaled_mag128(bits, D);
+        const unsigned __int128 mag = zero ? 0 : rint_scaled_mag128(bits, D);
         const unsigned __int128 bias = (unsigned __int128)1 << 104;
-        unsigned __int128 x = neg ? bias - mag : bias + mag;
+        const unsigned __int128 x = neg ? bias - mag : bias + mag;
         const uint64_t lo = (uint64_t)x, hi = (uint64_t)(x >> 64);
-        L.u[0] = (uint32_t)(lo & 0x1FFFFF);
-        L.u[1] = (uint32_t)((lo >> 21) & 0x1FFFFF);
-        L.u[2] = (uint32_t)((lo >> 42) & 0x1FFFFF);
-        L.u[3] = (uint32_t)(((lo >> 63) | (hi << 1)) & 0x1FFFFF);
-        L.u[4] = (uint32_t)((hi >> 20) & 0x1FFFFF);
+        L.w[0] = (uint32_t)lo;
+        L.w[1] = (uint32_t)(lo >> 32);
+        L.w[2] = (uint32_t)hi;
+        L.w[3] = (uint32_t)(hi >> 32);
     }
     return L;
 }
 
-// (a_hat + h) mod m in [0, m), before removing the offset h, from the limbs;
-// Kc is K_m (standard or extended width), c the 2^(21 l) mod m constants
+// (a_hat + h) mod m in [0, m), before removing the offset h: v = K_m +
+// sum_l u_l (2^(16 l) mod m) over the 16-bit limbs u_l, two limbs per
+// v_dot2_u32_u16 against c2[p] = (2^(32p) mod m) | (2^(32p+16) mod m) << 16.
+// v < 2^27, so the Barrett quotient of mod_small fits the 24-bit multiplier.
 template <bool EXT>
-__device__ __forceinline__ uint32_t residue_of_limbs(const Limbs<EXT>& L, uint32_t Kc, const uint32_t* c,
+__device__ __forceinline__ uint32_t residue_of_limbs(const Limbs<EXT>& L, uint32_t Kc, const uint32_t* c2,
                                                      uint32_t m, uint32_t R) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
     uint32_t v = Kc;
-    v += __umul24(L.u[0], c[0]);
-    v += __umul24(L.u[1], c[1]);
-    v += __umul24(L.u[2], c[2]);
-    if (EXT) {
-        v += __umul24(L.u[3], c[3]);
-        v += __umul24(L.u[4], c[4]);
-    }
+#pragma unroll
+    for (int p = 0; p < (EXT ? kExtWords : kStdWords); ++p)
+        v = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, L.w[p]), __builtin_bit_cast(u16x2, c2[p]), v, false);
     return mod_small(v, m, R);
 }
 

@@ -43,7 +43,7 @@ struct EncodeParams {
     int conj;                // negate imaginary parts (op = 'C')
     int t, s;
     uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS];
-    uint32_t c[kMaxS][kExtLimbs];
+    uint32_t c[kMaxS][kExtWords];     // 16-bit limb-pair constants (see oz2_device.h)
 };
 
 struct GemmParams {
@@ -96,7 +96,7 @@ struct SmallParams {
     double alpha, beta;
     int t, s;
     uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS], bias[kMaxS];
-    uint32_t c[kMaxS][kExtLimbs];
+    uint32_t c[kMaxS][kExtWords];     // 16-bit limb-pair constants (see oz2_device.h)
     float finv[kMaxS];
     uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];

@@ -6,8 +6,8 @@
 // GPUs: Ozaki Scheme II on the Xe2 Architecture":
 //   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scan + scale_of()
 //   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
-//   Sec. 4.2  residues from 21-bit limbs of a_hat + 2^62 with precomputed
-//             2^(21 l) mod m and K_m = (h_m - 2^62) mod m; no FP64 and no
+//   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
+//             2^(limb position) mod m and K_m = (h_m - 2^62) mod m; no FP64 and no
 //             branches per modulus                 -> encode_kernel
 //   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
 //             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
@@ -164,7 +164,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
             if (CPLX) li[e] = make_limbs<EXT>(xi[e], D, bad);
         }
         int8_t* dst = P.planes + gv * P.kpad + p0 + p4;
-        for (int t = 0; t < P.s; ++t) {
+        // four moduli per trip: their constants are fetched together
+        for (int t0 = 0; t0 < P.s; t0 += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int t = t0 + u;
+            if (t >= P.s) break;
             const uint32_t h = P.h[t];
             uint32_t r[4];
 #pragma unroll
@@ -188,6 +193,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
                 *(uint32_t*)(dst + 2 * P.set_stride + t * plane) =
                     pack4(rs[0] - h, rs[1] - h, rs[2] - h, rs[3] - h);
             }
+          }
         }
     }
 }

@@ -7,8 +7,9 @@
 //    Table 2); among equal products the lexicographically largest descending
 //    sequence is taken.
 //  * Sec. 4.1: t is the largest integer with k 2^(2t) <= M/4 (2k for ZGEMM).
-//  * Sec. 4.2: residues from 21-bit limbs of a_hat + 2^62 with the constants
-//    2^(21 l) mod m and K_m = (h_m - 2^62) mod m, h_m = floor((m-1)/2).
+//  * Sec. 4.2: residues from limbs of a_hat + 2^62 with the constants
+//    2^(limb position) mod m and K_m = (h_m - 2^62) mod m, h_m = floor((m-1)/2);
+//    the limbs here are 16 bits wide (the page's are 21), packed in pairs.
 //  * Sec. 4.4: z = sum r_t fl32(y_t/m_t); c_hat = sum r_t W_t - q M in 16-bit
 //    limbs; N_L 32-bit words.
 #include "oz2_plan.h"
@@ -201,7 +202,7 @@ void build_plan(int s, ModuliPlan* p) {
         p->finv[t] = fy / fm;
         uint32_t h = (m - 1) / 2;
         p->h[t] = h;
-        for (int l = 0; l < kExtLimbs; ++l) p->c21[t][l] = pow2_mod(21 * l, m);
+        for (int q = 0; q < kExtWords; ++q) p->c2[t][q] = pow2_mod(32 * q, m) | (pow2_mod(32 * q + 16, m) << 16);
         p->Kstd[t] = (h + m - pow2_mod(62, m)) % m;
         p->Kext[t] = (h + m - pow2_mod(104, m)) % m;
         p->barrett[t] = (uint32_t)((1ull << 32) / m);

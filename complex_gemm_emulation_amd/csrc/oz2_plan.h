@@ -15,8 +15,8 @@ constexpr int kMinS = 2;
 constexpr int kMaxS = 24;
 constexpr int kMaxNL = 6;            // 32-bit words of c_hat for s <= 24 (log2 M < 192)
 constexpr int kMaxLimb16 = 2 * kMaxNL;
-constexpr int kStdLimbs = 3;         // 21-bit limbs of a_hat + 2^62 (t <= 61)
-constexpr int kExtLimbs = 5;         // 21-bit limbs of a_hat + 2^104 (t <= 100)
+constexpr int kStdWords = 2;         // 32-bit words (16-bit limb pairs) of a_hat + 2^62 (t <= 61)
+constexpr int kExtWords = 4;         // 32-bit words of a_hat + 2^104 (t <= 100)
 constexpr int kMaxStdT = 61;
 
 // Small unsigned big integer (little-endian 32-bit words), enough for M < 2^192
@@ -49,7 +49,7 @@ struct ModuliPlan {
     uint32_t W2[kMaxS / 2][kMaxLimb16] = {};  // W16 of moduli 2u and 2u+1 packed in 16-bit halves
     // residue generation (Sec. 4.2)
     uint32_t h[kMaxS] = {};       // floor((m-1)/2)
-    uint32_t c21[kMaxS][kExtLimbs] = {};   // 2^(21 l) mod m
+    uint32_t c2[kMaxS][kExtWords] = {};    // (2^(32p) mod m) | (2^(32p+16) mod m) << 16
     uint32_t Kstd[kMaxS] = {};    // (h - 2^62) mod m
     uint32_t Kext[kMaxS] = {};    // (h - 2^104) mod m
     uint32_t barrett[kMaxS] = {}; // floor(2^32 / m)
