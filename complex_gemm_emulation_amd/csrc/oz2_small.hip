@@ -45,10 +45,24 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
     }
 }
 
+// per-modulus constants, staged in LDS once per block: read at uniform
+// addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes
+struct ModConst {
+    uint32_t mod, barrett, bias, h, K;
+    uint32_t c2[kExtWords];
+    float finv;
+};
+struct SmallConsts {
+    ModConst q[kMaxS + 1];            // one zeroed entry past the last modulus
+    uint32_t W2[kMaxS / 2][kMaxLimb16];
+    uint32_t M16[kMaxLimb16];
+};
+
 // exponent of the vector held by lanes l, l^16, l^32, l^48 and the residue
 // bytes of this lane's 8 values for every modulus (byte e = k 8 kq + e)
 template <int SMAX, bool EXT>
-__device__ __forceinline__ void encode8(const double x[8], const SmallParams& P, long frag[SMAX], int& D, bool& bad) {
+__device__ __forceinline__ void encode8(const double x[8], const SmallParams& P, const SmallConsts& Q,
+                                        long frag[SMAX], int& D, bool& bad) {
     uint64_t mx = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) mx = max(mx, abs_bits(x[e]));
@@ -63,11 +77,12 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
 #pragma unroll
     for (int t = 0; t < SMAX; ++t) {
         if (t < P.s) {
-            const uint32_t h = P.h[t];
+            const ModConst& C = Q.q[t];
+            const uint32_t h = C.h;
             uint32_t w[2] = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t r = residue_of_limbs<EXT>(L[e], P.K[t], P.c[t], P.mod[t], P.barrett[t]) - h;
+                const uint32_t r = residue_of_limbs<EXT>(L[e], C.K, C.c2, C.mod, C.barrett) - h;
                 w[e >> 2] |= (r & 0xffu) << (8 * (e & 3));
             }
             frag[t] = (long)((uint64_t)w[0] | ((uint64_t)w[1] << 32));
@@ -94,12 +109,43 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
     const int vi = lane & 15, kq = lane >> 4;
     const int64_t per_batch = (int64_t)P.tiles_m * P.tiles_n;
 
+    __shared__ SmallConsts Q;
+    {
+        // stage the constant tables (a few hundred words) in LDS
+        uint32_t* dst = (uint32_t*)&Q;
+        constexpr int nq = (int)(sizeof(ModConst) / 4);
+        for (int i = threadIdx.x; i < (int)(sizeof(SmallConsts) / 4); i += blockDim.x) {
+            uint32_t v = 0u;
+            if (i < (kMaxS + 1) * nq) {
+                const int t = i / nq, f = i % nq;
+                if (t < P.s) {
+                    if (f == 0) v = P.mod[t];
+                    else if (f == 1) v = P.barrett[t];
+                    else if (f == 2) v = P.bias[t];
+                    else if (f == 3) v = P.h[t];
+                    else if (f == 4) v = P.K[t];
+                    else if (f < 5 + kExtWords) v = P.c[t][f - 5];
+                    else v = __float_as_uint(P.finv[t]);
+                }
+            } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16) {
+                const int j = i - (kMaxS + 1) * nq;
+                v = P.W2[j / kMaxLimb16][j % kMaxLimb16];
+            } else {
+                v = P.M16[i - (kMaxS + 1) * nq - (kMaxS / 2) * kMaxLimb16];
+            }
+            dst[i] = v;
+        }
+        __syncthreads();
+    }
+
     long fa[SMAX], fb[SMAX];
     int DA = 0, EB = 0;
     bool badA = false, badB = false;
     int64_t keyA = -1, keyB = -1;
 
     for (int64_t tile = first; tile < last; ++tile) {
+        // keeps the LDS constant reads inside the loop (no hoisting into registers)
+        asm volatile("" ::: "memory");
         const int64_t b = tile / per_batch;
         const int64_t rem = tile - b * per_batch;
         const int64_t tm = rem / P.tiles_n, tn = rem - tm * P.tiles_n;
@@ -109,7 +155,7 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
         if (ka != keyA) {
             double x[8];
             load8(P.A + b * P.strideA, P.lda, P.transa != 0, i0 + vi, P.m, P.k, kq, x);
-            encode8<SMAX, EXT>(x, P, fa, DA, badA);
+            encode8<SMAX, EXT>(x, P, Q, fa, DA, badA);
             keyA = ka;
         }
         // columns j0.. of op(B_b): contiguous for op = N
@@ -117,7 +163,7 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
         if (kb != keyB) {
             double x[8];
             load8(P.B + b * P.strideB, P.ldb, P.transb == 0, j0 + vi, P.n, P.k, kq, x);
-            encode8<SMAX, EXT>(x, P, fb, EB, badB);
+            encode8<SMAX, EXT>(x, P, Q, fb, EB, badB);
             keyB = kb;
         }
 
@@ -131,13 +177,13 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                 const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t], fb[t], zero, 0, 0, 0);
                 const bool two = t + 1 < P.s;
                 const v4i cb = two ? __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1], fb[t + 1], zero, 0, 0, 0) : zero;
-                const uint32_t m0 = P.mod[t], R0 = P.barrett[t], b0 = P.bias[t];
-                const uint32_t m1 = P.mod[t + 1], R1 = P.barrett[t + 1], b1 = P.bias[t + 1];
+                const ModConst& C0 = Q.q[t];
+                const ModConst& C1 = Q.q[t + 1];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t ra = acc_mod(ca[e], m0, R0, b0);
-                    const uint32_t rb = two ? acc_mod(cb[e], m1, R1, b1) : 0u;
-                    acc[e].add2(ra, rb, P.finv[t], P.finv[t + 1], P.W2[t >> 1]);
+                    const uint32_t ra = acc_mod(ca[e], C0.mod, C0.barrett, C0.bias);
+                    const uint32_t rb = two ? acc_mod(cb[e], C1.mod, C1.barrett, C1.bias) : 0u;
+                    acc[e].add2(ra, rb, C0.finv, C1.finv, Q.W2[t >> 1]);
                 }
             }
         }
@@ -151,7 +197,7 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
             const int Dr = __shfl(DA, r);
             const bool badr = __shfl((int)badA, r) != 0;
             uint32_t w[NL];
-            acc[e].finish(P.M16, w);
+            acc[e].finish(Q.M16, w);
             double x = words_to_double<NL>(w, Dr + EB);
             if (badr || badB) x = __builtin_nan("");
             const int64_t row = i0 + r;
