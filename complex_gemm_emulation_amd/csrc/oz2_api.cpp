@@ -152,42 +152,10 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
     return OZ2_STATUS_SUCCESS;
 }
 
-int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n,
-              int64_t k, const double alpha[2], const double* A, int64_t lda, const double* B,
-              int64_t ldb, const double beta[2], double* C, int64_t ldc, int s) {
-    if (!h) return -1;
-    if (!valid_op(transa)) return -2;
-    if (!valid_op(transb)) return -3;
-    if (m < 0) return -4;
-    if (n < 0) return -5;
-    if (k < 0) return -6;
-    const int64_t rows_a = is_trans(transa) ? k : m;
-    const int64_t rows_b = is_trans(transb) ? n : k;
-    if (lda < (rows_a > 1 ? rows_a : 1)) return -9;
-    if (ldb < (rows_b > 1 ? rows_b : 1)) return -11;
-    if (ldc < (m > 1 ? m : 1)) return -14;
-    if (s < kMinS || s > kMaxS) return -15;
-    if (m == 0 || n == 0) return OZ2_STATUS_SUCCESS;
-    if (!C) return -13;
-    const bool alpha_zero = alpha[0] == 0.0 && alpha[1] == 0.0;
-    const bool beta_zero = beta[0] == 0.0 && beta[1] == 0.0;
-    h->timed = false;
-    if (alpha_zero || k == 0) {
-        OZ2_LAUNCH(launch_scale_c(C, m, n, ldc, beta, cplx, h->stream));
-        return OZ2_STATUS_SUCCESS;
-    }
-    if (!A) return -8;
-    if (!B) return -10;
-
-    const ModuliPlan* pl = moduli_plan(s);
-    if (!pl) return OZ2_STATUS_INTERNAL;
-    const int t = scaling_width(*pl, k, cplx);
-    if (t < 1) return OZ2_STATUS_RANGE;
-    const bool ext = t > kMaxStdT;
-    if (!cplx && small_path(h, m, n, k))
-        return small_impl(h, *pl, t, transa, transb, m, n, k, alpha[0], A, lda, 0, B, ldb, 0, beta[0], C,
-                          ldc, 0, 1, s);
-
+// workspace layout of the four-phase path for one m x n x k product
+Layout plan_layout(const oz2_context* h, bool cplx, int s, const ModuliPlan& plan, int t, int64_t m, int64_t n,
+                   int64_t k) {
+    const ModuliPlan* pl = &plan;
     Layout L;
     L.sets = cplx ? 3 : 1;
     L.outs = cplx ? 2 : 1;
@@ -211,6 +179,39 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
     L.bytes_chat = h->debug ? (size_t)L.outs * L.n * L.mp * L.NL * 4 : 0;
     L.off_chat = off; off = align_up(off + L.bytes_chat);
     L.total = off;
+    return L;
+}
+
+// whether a workspace of `bytes` is allowed: under the memory limit when one
+// is set, else within the free device memory (plus the current workspace);
+// *cap receives the bound
+bool fits(oz2_context* h, size_t bytes, size_t* cap) {
+    if (h->mem_limit) {
+        *cap = h->mem_limit;
+        return bytes <= h->mem_limit;
+    }
+    if (bytes <= h->ws_size) {
+        *cap = h->ws_size;
+        return true;
+    }
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) {
+        (void)hipGetLastError();
+        *cap = h->ws_size;
+        return false;
+    }
+    *cap = free_b + h->ws_size;
+    return bytes <= *cap;
+}
+
+// the four phases for one block (the whole product when untiled); record:
+// phase events of this call
+int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n, int64_t k,
+         const double alpha[2], const double* A, int64_t lda, const double* B, int64_t ldb,
+         const double beta[2], double* C, int64_t ldc, int s, const ModuliPlan* pl, int t, bool ext,
+         bool record) {
+    const bool beta_zero = beta[0] == 0.0 && beta[1] == 0.0;
+    Layout L = plan_layout(h, cplx, s, *pl, t, m, n, k);
     int st = ensure_workspace(h, L.total);
     if (st) return st;
     char* ws = (char*)h->ws;
@@ -222,7 +223,7 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
     uint32_t* chat = h->debug ? (uint32_t*)(ws + L.off_chat) : nullptr;
     hipStream_t stm = h->stream;
 
-    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[0], stm));
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[0], stm));
     // phase 1: row maxima of op(A), column maxima of op(B)
     OZ2_LAUNCH(launch_fill_u64(amaxA, L.mp, 0, stm));
     OZ2_LAUNCH(launch_fill_u64(amaxB, L.np, 0, stm));
@@ -243,7 +244,7 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
         Sb.pchunk = (k + chunks - 1) / chunks;
         OZ2_LAUNCH(launch_scan(Sb, contig_b, cplx, stm));
     }
-    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
     // phase 2: integerize and encode both operands
     {
         EncodeParams E{};
@@ -258,7 +259,7 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
         E.amax = amaxB; E.planes = pb; E.conj = cplx && is_conj(transb);
         OZ2_LAUNCH(launch_encode(E, !is_trans(transb), cplx, ext, stm));
     }
-    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
     // phase 3: s exact INT8 products, reduced mod m_t on chip, one launch per
     // k run of at most kMaxRunK positions
     const int64_t chunk_stride = (int64_t)L.outs * s * L.n * L.mp;
@@ -283,7 +284,7 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
             OZ2_LAUNCH(launch_residue_gemm(G, cplx, stm));
         }
     }
-    if (h->timing) OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
     // phase 4: CRT, rounding, scale back, alpha/beta
     {
         ReconParams R{};
@@ -300,13 +301,88 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
         R.t = t; R.s = s; R.chat = chat;
         OZ2_LAUNCH(launch_reconstruct(R, pl->NL, cplx, !beta_zero, stm));
     }
-    if (h->timing) {
+    if (record) {
         OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
         h->timed = true;
     }
     L.valid = true;
     h->last = L;
     return OZ2_STATUS_SUCCESS;
+}
+
+int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n,
+              int64_t k, const double alpha[2], const double* A, int64_t lda, const double* B,
+              int64_t ldb, const double beta[2], double* C, int64_t ldc, int s) {
+    if (!h) return -1;
+    if (!valid_op(transa)) return -2;
+    if (!valid_op(transb)) return -3;
+    if (m < 0) return -4;
+    if (n < 0) return -5;
+    if (k < 0) return -6;
+    const int64_t rows_a = is_trans(transa) ? k : m;
+    const int64_t rows_b = is_trans(transb) ? n : k;
+    if (lda < (rows_a > 1 ? rows_a : 1)) return -9;
+    if (ldb < (rows_b > 1 ? rows_b : 1)) return -11;
+    if (ldc < (m > 1 ? m : 1)) return -14;
+    if (s < kMinS || s > kMaxS) return -15;
+    if (m == 0 || n == 0) return OZ2_STATUS_SUCCESS;
+    if (!C) return -13;
+    const bool alpha_zero = alpha[0] == 0.0 && alpha[1] == 0.0;
+    h->timed = false;
+    if (alpha_zero || k == 0) {
+        OZ2_LAUNCH(launch_scale_c(C, m, n, ldc, beta, cplx, h->stream));
+        return OZ2_STATUS_SUCCESS;
+    }
+    if (!A) return -8;
+    if (!B) return -10;
+
+    const ModuliPlan* pl = moduli_plan(s);
+    if (!pl) return OZ2_STATUS_INTERNAL;
+    const int t = scaling_width(*pl, k, cplx);
+    if (t < 1) return OZ2_STATUS_RANGE;
+    const bool ext = t > kMaxStdT;
+    if (!cplx && small_path(h, m, n, k))
+        return small_impl(h, *pl, t, transa, transb, m, n, k, alpha[0], A, lda, 0, B, ldb, 0, beta[0], C,
+                          ldc, 0, 1, s);
+
+    // memory-aware tiling (Arc page Sec. 6, memory-aware tiling): blocks of C
+    // with all of k each, so every block's row and column exponents are the
+    // full ones and the result is bitwise that of the untiled product
+    const Layout full = plan_layout(h, cplx, s, *pl, t, m, n, k);
+    size_t cap = 0;
+    if (!fits(h, full.total, &cap)) {
+        int64_t T = kPadM;
+        while (T < (m > n ? m : n)) T *= 2;
+        for (; T >= kPadM; T /= 2) {
+            const int64_t mt = m < T ? m : T, nt = n < T ? n : T;
+            if (plan_layout(h, cplx, s, *pl, t, mt, nt, k).total <= cap) break;
+        }
+        if (T < kPadM) return OZ2_STATUS_WORKSPACE_LIMIT;
+        const int64_t mt = m < T ? m : T, nt = n < T ? n : T;
+        const int64_t w = cplx ? 2 : 1;  // doubles per element
+        hipStream_t stm = h->stream;
+        const bool rec = h->timing != 0;
+        if (rec)
+            for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+        for (int64_t j0 = 0; j0 < n; j0 += nt) {
+            for (int64_t i0 = 0; i0 < m; i0 += mt) {
+                const int64_t mb = m - i0 < mt ? m - i0 : mt, nb = n - j0 < nt ? n - j0 : nt;
+                const double* Ab = A + w * (is_trans(transa) ? i0 * lda : i0);
+                const double* Bb = B + w * (is_trans(transb) ? j0 : j0 * ldb);
+                double* Cb = C + w * (i0 + j0 * ldc);
+                const int st = core(h, cplx, transa, transb, mb, nb, k, alpha, Ab, lda, Bb, ldb, beta, Cb, ldc, s,
+                                    pl, t, ext, false);
+                if (st) return st;
+            }
+        }
+        if (rec) {
+            for (int e = 3; e < 5; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+            h->timed = true;
+        }
+        return OZ2_STATUS_SUCCESS;
+    }
+    return core(h, cplx, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, pl, t, ext,
+                h->timing != 0);
 }
 
 }  // namespace

@@ -79,9 +79,14 @@ int oz2_destroy(oz2_handle_t h);
 int oz2_set_stream(oz2_handle_t h, void* stream);
 
 /* Cap on the workspace in bytes; 0 (the default) means the free device
- * memory reported by hipMemGetInfo at allocation time.  A call whose
- * workspace would exceed the cap returns OZ2_STATUS_WORKSPACE_LIMIT
- * (the resident-memory hint of Arc page Sec. 6, memory-aware tiling). */
+ * memory reported by hipMemGetInfo at the call.  A product whose workspace
+ * would exceed the cap is computed in blocks of C (square, a power-of-two
+ * multiple of 256 on a side, each with all of k) one after another: every
+ * block has the full row and column exponents, so the result is bitwise
+ * that of the untiled call (the resident-memory hint and memory-aware tiling
+ * of Arc page Sec. 6).  OZ2_STATUS_WORKSPACE_LIMIT is returned only when
+ * not even a 256 x 256 block fits.  A tiled call reports its whole duration
+ * in ms[2] of oz2_get_phase_times, and oz2_debug_copy sees its last block. */
 int oz2_set_memory_limit(oz2_handle_t h, size_t bytes);
 
 /* Current workspace size in bytes (0 before the first call). */
