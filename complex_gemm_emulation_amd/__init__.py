@@ -257,7 +257,9 @@ class Handle:
                                                        out.nbytes, ctypes.byref(nbytes), dims))
         d = [int(x) for x in dims]
         if which in (2, 3):
-            return out.reshape(d[0], d[1], d[2], d[3])
+            # k-panels [sets][s][k_pad/64][rows_pad][64] -> [sets][s][rows_pad][k_pad]
+            panels = out.reshape(d[0], d[1], d[2], d[3], d[4])
+            return np.ascontiguousarray(panels.transpose(0, 1, 3, 2, 4)).reshape(d[0], d[1], d[3], d[2] * d[4])
         if which == 4:
             return out.reshape(d[4], d[0], d[1], d[2], d[3])
         if which == 5:

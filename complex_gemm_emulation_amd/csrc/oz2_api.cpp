@@ -568,9 +568,9 @@ int oz2_debug_copy(oz2_handle_t h, int which, void* dst, size_t capacity, size_t
         case 0: off = L.off_amaxA; nbytes = 8 * (size_t)L.mp; d[2] = L.mp; break;
         case 1: off = L.off_amaxB; nbytes = 8 * (size_t)L.np; d[2] = L.np; break;
         case 2: off = L.off_pa; nbytes = L.bytes_pa;
-            d[0] = L.sets; d[1] = L.s; d[2] = L.mp; d[3] = L.kp; break;
+            d[0] = L.sets; d[1] = L.s; d[2] = L.kp / kPanelK; d[3] = L.mp; d[4] = kPanelK; break;
         case 3: off = L.off_pb; nbytes = L.bytes_pb;
-            d[0] = L.sets; d[1] = L.s; d[2] = L.np; d[3] = L.kp; break;
+            d[0] = L.sets; d[1] = L.s; d[2] = L.kp / kPanelK; d[3] = L.np; d[4] = kPanelK; break;
         case 4: off = L.off_res; nbytes = L.bytes_res;
             d[0] = L.outs; d[1] = L.s; d[2] = L.n; d[3] = L.mp; d[4] = L.chunks; break;
         case 5: off = L.off_chat; nbytes = L.bytes_chat;

@@ -16,27 +16,31 @@
 // in the output planes between the k-loops (each lane rereads only what it
 // wrote), so no registers beyond one accumulator set are held across loops.
 //
-// Data layout: both operands are k-contiguous planes (rows of op(A), columns
-// of op(B)), zero-padded in k to a multiple of 256 and in rows to a multiple
-// of 256, so the main loop has no bounds checks.  The output plane of
-// modulus t is uint8 [n][m_pad] (column-major like C) holding C^(t) mod m_t
-// in [0, m_t).
+// Data layout: both operands are planes of 64-position k-panels (rows of
+// op(A), columns of op(B), 64 contiguous bytes per row within a panel),
+// zero-padded in k to a multiple of 256 and in rows to a multiple of 256, so
+// the main loop has no bounds checks and one k step of a tile is one
+// contiguous run of memory.  The output plane of modulus t is uint8
+// [n][m_pad] (column-major like C) holding C^(t) mod m_t in [0, m_t).
 //
 // Kernel shape (CDNA4): a BM x BN tile of one modulus per block, WM x WN
 // wavefronts, each owning (BM/WM) x (BN/WN) INT32 accumulators in 32 x 32
-// MFMA tiles.  k advances 128 bytes per step through two LDS stages filled by
-// direct global->LDS loads (global_load_lds_dwordx4: no VGPR staging, no
-// ds_write), so the loads of step k+1 (and, after the mid-step barrier, of
-// step k+2) overlap the MFMAs of step k.  Operand fragments are double
-// buffered in registers and the MFMAs are interleaved one-to-one with the
-// LDS fragment reads of the next 32-wide k sub-step (sched_group_barrier).
-// LDS rows are 128 bytes of eight 16-byte chunks whose position is XOR-ed
-// with (row/2) mod 8: the LDS serves a 16-byte-per-lane read 16 lanes per
-// clock over 64 banks, and 16 consecutive rows then hit distinct bank groups.
-// The 256 x 256 tile uses 8 wavefronts (two per SIMD) so that one wave's
-// MFMAs cover the other's waits.  Blocks are remapped so that each of the 8
-// XCDs (which receive blocks round-robin) works on a contiguous range of
-// tiles, grouped 8 tiles tall for L2 reuse.
+// MFMA tiles.  k advances one 64-byte panel per step through four LDS stages
+// filled by direct global->LDS loads (global_load_lds_dwordx4: no VGPR
+// staging, no ds_write) issued three steps ahead, so a load has three steps
+// of MFMAs to arrive.  The loads are issued from inline assembly: the
+// compiler cannot tell the stages of an LDS-DMA pipeline apart and would
+// otherwise wait for every load in flight before each LDS read; here the
+// kernel's own vmcnt wait before each step's barrier orders them.  Operand
+// fragments are double buffered in registers and the MFMAs are interleaved
+// one-to-one with the LDS fragment reads of the next 32-wide k sub-step
+// (sched_group_barrier).  LDS rows are 64 bytes of four 16-byte chunks whose
+// position is XOR-ed with (row/4) mod 4: the LDS serves a 16-byte-per-lane
+// read 16 lanes per clock over 64 banks, and 16 consecutive rows then hit
+// distinct bank groups.  The 256 x 256 tile uses 8 wavefronts (two per SIMD)
+// so that one wave's MFMAs cover the other's waits.  Blocks are remapped so
+// that each of the 8 XCDs (which receive blocks round-robin) works on a
+// contiguous range of tiles, grouped 8 tiles tall for L2 reuse.
 #include "oz2_internal.h"
 
 namespace oz2 {
@@ -47,11 +51,14 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* global_ptr_t;
 
-constexpr int kBK = 128;         // k bytes per step (four 32-wide MFMA sub-steps)
+constexpr int kBK = kGemmStepK;  // k bytes per step (two 32-wide MFMA sub-steps)
 constexpr int kChunks = kBK / 16;
+constexpr int kStages = 4;
+static_assert(kBK == kPanelK, "one k step is one panel");
+static_assert(kPadK % (kBK * kStages) == 0, "padded k holds whole stage rounds");
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // INT32 accumulator -> [0, m): bias makes it non-negative (a multiple of m,
 // chosen for |acc| <= 2^31 - 2^20 + 255), Barrett quotient floor(u R / 2^32)
@@ -68,6 +75,24 @@ __device__ __forceinline__ uint32_t pack4(const uint32_t r[4]) {
     return r[0] | (r[1] << 8) | (r[2] << 16) | (r[3] << 24);
 }
 
+// one wave-wide 1 KiB direct load: 16 bytes per lane from base + voff into
+// LDS at lds + 16 lane (M0 holds lds; one wait state before the load).  M0
+// is reserved to the compiler, which warns about the clobber; these kernels
+// use M0 nowhere else (a CPU test checks the generated code for that).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_1k(const int8_t* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(base)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate: vmcnt(n) (bits 3:0 and 15:14), expcnt off, lgkmcnt(0)
+// or off
+constexpr int waitcnt_vm(int n, bool lgkm0) {
+    return (n & 15) | ((n >> 4) << 14) | 0x0070 | (lgkm0 ? 0 : 0x0F00);
+}
+
 template <int BM, int BN, int WM, int WN, bool CPLX>
 __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParams P) {
     constexpr int NW = WM * WN;
@@ -75,14 +100,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     constexpr int LOADS_A = BM * kChunks / 64 / NW;  // wave-wide 1 KiB loads per wave and stage
     constexpr int LOADS_B = BN * kChunks / 64 / NW;
     static_assert(LOADS_A * 64 * NW == BM * kChunks && LOADS_B * 64 * NW == BN * kChunks, "tile/wave mismatch");
-    __shared__ __attribute__((aligned(1024))) int8_t sA0[BM * kBK];
-    __shared__ __attribute__((aligned(1024))) int8_t sB0[BN * kBK];
-    __shared__ __attribute__((aligned(1024))) int8_t sA1[BM * kBK];
-    __shared__ __attribute__((aligned(1024))) int8_t sB1[BN * kBK];
+    constexpr int STAGE = (BM + BN) * kBK;  // A rows then B rows
+    // one object per stage
+    __shared__ __attribute__((aligned(1024))) int8_t sS0[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS1[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS2[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS3[STAGE];
+    static_assert(kStages == 4, "four stage objects");
+    auto stage = [&](int st) -> int8_t* { return st == 0 ? sS0 : st == 1 ? sS1 : st == 2 ? sS2 : sS3; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int wm = wave % WM, wn = wave / WM;
 
     // block -> (modulus, tile row, tile column)
@@ -102,56 +132,57 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
 
     const uint32_t m = P.mod[t], R = P.barrett[t], bias = P.bias[t];
     const int64_t kp = P.kp;
-    const int nk = P.k_steps;  // even; this launch covers k in [k_begin, k_begin + 128 nk)
+    const int nk = P.k_steps;  // multiple of 4; this launch covers k in [k_begin, k_begin + 64 nk)
 
     // per-lane source offsets of the direct loads: piece = 16 bytes landing at
-    // LDS byte 16 * piece, i.e. row piece / 8, stored chunk position piece % 8
+    // LDS byte 16 * piece, i.e. row piece / 4, stored chunk position piece % 4
     uint32_t goffA[LOADS_A], goffB[LOADS_B];
 #pragma unroll
     for (int q = 0; q < LOADS_A; ++q) {
         const int piece = (wave * LOADS_A + q) * 64 + lane;
         const int row = piece / kChunks, pos = piece % kChunks;
-        goffA[q] = (uint32_t)(row * kp + ((pos ^ ((row >> 1) & 7)) << 4));
+        goffA[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
     }
 #pragma unroll
     for (int q = 0; q < LOADS_B; ++q) {
         const int piece = (wave * LOADS_B + q) * 64 + lane;
         const int row = piece / kChunks, pos = piece % kChunks;
-        goffB[q] = (uint32_t)(row * kp + ((pos ^ ((row >> 1) & 7)) << 4));
+        goffB[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
     }
     const int fr = lane & 31;
     const int aoff = (wm * WTM + fr) * kBK;
-    const int boff = (wn * WTN + fr) * kBK;
+    const int boff = BM * kBK + (wn * WTN + fr) * kBK;
     const int row_out0 = tm * BM + wm * WTM + 4 * (lane >> 5);
     const int col_out0 = tn * BN + wn * WTN + fr;
+    const int64_t panelA = P.mp * kBK, panelB = P.np * kBK;  // bytes per k step
 
     v16i acc[FM][FN];
-    v4i fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+    v4i fa[2][FM], fb[2][FN];
 
 #pragma unroll 1
     for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
-        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.mp * kp + (int64_t)tm * BM * kp + P.k_begin;
-        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.np * kp + (int64_t)tn * BN * kp + P.k_begin;
-        auto issue = [&](int kt, int8_t* dA, int8_t* dB) {
-            const int8_t* Ak = Ag + (int64_t)kt * kBK;
-            const int8_t* Bk = Bg + (int64_t)kt * kBK;
+        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.mp * kp + (P.k_begin / kBK) * panelA +
+                           (int64_t)tm * BM * kBK;
+        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.np * kp + (P.k_begin / kBK) * panelB +
+                           (int64_t)tn * BN * kBK;
+        auto issue = [&](int kt, int st) {
+            const int8_t* Ak = Ag + (int64_t)kt * panelA;
+            const int8_t* Bk = Bg + (int64_t)kt * panelB;
+            const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)stage(st);
 #pragma unroll
-            for (int q = 0; q < LOADS_A; ++q)
-                __builtin_amdgcn_global_load_lds((global_ptr_t)(Ak + goffA[q]),
-                                                 (lds_ptr_t)(dA + (wave * LOADS_A + q) * 1024), 16, 0, 0);
+            for (int q = 0; q < LOADS_A; ++q) dma_1k(Ak, goffA[q], lds + (wave_u * LOADS_A + q) * 1024);
 #pragma unroll
-            for (int q = 0; q < LOADS_B; ++q)
-                __builtin_amdgcn_global_load_lds((global_ptr_t)(Bk + goffB[q]),
-                                                 (lds_ptr_t)(dB + (wave * LOADS_B + q) * 1024), 16, 0, 0);
+            for (int q = 0; q < LOADS_B; ++q) dma_1k(Bk, goffB[q], lds + BM * kBK + (wave_u * LOADS_B + q) * 1024);
         };
         // fragments of sub-step ks: lane l holds row (l mod 32), chunk 2 ks + l / 32
-        auto rd = [&](const int8_t* cA, const int8_t* cB, int ks, v4i (&a)[FM], v4i (&b)[FN]) {
+        auto rd = [&](int st, int ks, v4i (&a)[FM], v4i (&b)[FN]) {
+            const int8_t* S = stage(st);
             const int c = ks * 2 + (lane >> 5);
-            const int sw = (c ^ ((fr >> 1) & 7)) << 4;
+            const int sw = (c ^ ((fr >> 2) & 3)) << 4;
 #pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = *(const v4i*)(cA + aoff + i * 32 * kBK + sw);
+            for (int i = 0; i < FM; ++i) a[i] = *(const v4i*)(S + aoff + i * 32 * kBK + sw);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = *(const v4i*)(cB + boff + j * 32 * kBK + sw);
+            for (int j = 0; j < FN; ++j) b[j] = *(const v4i*)(S + boff + j * 32 * kBK + sw);
         };
         auto mm = [&](v4i (&a)[FM], v4i (&b)[FN]) {
 #pragma unroll
@@ -160,38 +191,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
         };
-        constexpr int NMF = FM * FN, NDS = FM + FN, NDMA = LOADS_A + LOADS_B;
-        auto sched = [&](bool with_dma) {
+        constexpr int NMF = FM * FN, NDS = FM + FN;
+        auto sched = [&]() {
 #pragma unroll
             for (int q = 0; q < NDS; ++q) {
                 __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-                if (with_dma) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, (NDMA + NDS - 1) / NDS, 0);
             }
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMF - NDS, 0);
         };
-        // one k-step on stage c*; then the next stage n* is read and the DMA of
-        // step kdma refills the stage just consumed (w* == c*)
-        auto kstep = [&](const int8_t* cA, const int8_t* cB, const int8_t* nA, const int8_t* nB, int8_t* wA,
-                         int8_t* wB, int kdma) {
-            rd(cA, cB, 1, fa1, fb1);
-            mm(fa0, fb0);
-            sched(false);
-            rd(cA, cB, 2, fa0, fb0);
-            mm(fa1, fb1);
-            sched(false);
-            rd(cA, cB, 3, fa1, fb1);
-            mm(fa0, fb0);
-            sched(false);
-            // every read of this stage has returned and this wave's DMA of the
-            // next stage has landed; after the barrier both hold block-wide
-            __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        // this wave's loads of the next step have landed when at most the
+        // loads of the two steps after it are in flight
+        constexpr int kLoadsPerStep = LOADS_A + LOADS_B;
+        constexpr int kWaitStep = waitcnt_vm((kStages - 2) * kLoadsPerStep, true);
+        constexpr int kWaitFirst = waitcnt_vm((kStages - 1) * kLoadsPerStep, false);
+        static_assert((kStages - 1) * kLoadsPerStep < 64, "vmcnt range");
+        // one k step on stage st; after the barrier the next stage's first
+        // fragments are read and the loads of step kdma refill stage st
+        auto kstep = [&](int st, int kdma) {
+            rd(st, 1, fa[1], fb[1]);
+            mm(fa[0], fb[0]);
+            sched();
+            // every read of this stage has returned and the next stage has
+            // landed for this wave; after the barrier both hold block-wide
+            __builtin_amdgcn_s_waitcnt(kWaitStep);
             __syncthreads();
-            // past the last step these re-read valid data that is not used
-            rd(nA, nB, 0, fa0, fb0);
-            issue(kdma, wA, wB);
-            mm(fa1, fb1);
-            sched(true);
+            // past the last step these read data that is not used
+            rd((st + 1) % kStages, 0, fa[0], fb[0]);
+            issue(kdma, st);
+            mm(fa[1], fb[1]);
+            sched();
         };
 
 #pragma unroll
@@ -200,18 +229,20 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-        issue(0, sA0, sB0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+        for (int j = 0; j < kStages; ++j) issue(j, j);
+        __builtin_amdgcn_s_waitcnt(kWaitFirst);
         __syncthreads();
-        issue(1, sA1, sB1);
-        rd(sA0, sB0, 0, fa0, fb0);
+        rd(0, 0, fa[0], fb[0]);
 #pragma unroll 1
-        for (int kt = 0; kt < nk; kt += 2) {
-            kstep(sA0, sB0, sA1, sB1, sA0, sB0, min(kt + 2, nk - 1));
-            kstep(sA1, sB1, sA0, sB0, sA1, sB1, min(kt + 3, nk - 1));
+        for (int kt = 0; kt < nk; kt += kStages) {
+            // steps past the end reload the last step (same count of loads
+            // per step keeps the vmcnt arithmetic exact)
+#pragma unroll
+            for (int j = 0; j < kStages; ++j) kstep(j, min(kt + j + kStages, nk - 1));
         }
         // no LDS DMA may be in flight when the stages are reused or released
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, false));
         __syncthreads();
 
         // epilogue: lane holds rows 8g + 4(lane/32) + {0..3} of column lane%32
@@ -284,8 +315,9 @@ hipError_t gemm_go(GemmParams P, bool cplx, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_residue_gemm(const GemmParams& P, bool cplx, hipStream_t st) {
-    if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK || P.k_begin % kBK) return hipErrorInvalidValue;
-    if (P.k_steps <= 0 || P.k_steps % 2 || P.k_begin + (int64_t)P.k_steps * kBK > P.kp) return hipErrorInvalidValue;
+    if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK || P.k_begin % (kBK * kStages)) return hipErrorInvalidValue;
+    if (P.k_steps <= 0 || P.k_steps % kStages || P.k_begin + (int64_t)P.k_steps * kBK > P.kp)
+        return hipErrorInvalidValue;
     // large outputs: 256 x 256 tiles on 8 wavefronts; otherwise 128 x 128 on 4
     const int64_t big_blocks = (P.mp / 256) * (P.np / 256) * P.s;
     if (big_blocks >= 512) return gemm_go<256, 256, 2, 4>(P, cplx, st);

@@ -11,14 +11,17 @@
 
 namespace oz2 {
 
-// Residue planes of op(A) and op(B) are int8 [sets][s][rows_pad][k_pad],
-// every row (a row of op(A) or a column of op(B)) k-contiguous and padded
-// with zeros; sets = 1 (real) or 3 (complex: re, im, re+im).
+// Residue planes of op(A) and op(B) are int8 [sets][s][k_pad/64][rows_pad][64]:
+// k-panels of 64 positions, each panel holding every row (a row of op(A) or a
+// column of op(B)) as 64 contiguous bytes, zero-padded in rows and k; sets = 1
+// (real) or 3 (complex: re, im, re+im).  One GEMM k step of a 256-row tile is
+// then 16 KiB of contiguous memory.
 // Product residues are uint8 [outs][s][n][m_pad] holding values in [0, m_t)
 // (outs = 1 real, 2 complex: Re, Im), i.e. column-major like C.
 constexpr int kPadM = 256;   // row padding of the A planes / product planes
-constexpr int kPadK = 256;   // k padding of the planes (two 128-byte GEMM k steps)
-constexpr int kGemmStepK = 128;  // k bytes per GEMM k step
+constexpr int kPadK = 256;   // k padding of the planes (four GEMM k steps)
+constexpr int kPanelK = 64;  // k positions per panel of the residue planes
+constexpr int kGemmStepK = 64;   // k bytes per GEMM k step (one panel)
 
 // Vector layout of an operand as seen by scan/encode: vector v (a row of
 // op(A) or a column of op(B)) has element p at X[v*ld + p] when contiguous,
@@ -54,8 +57,8 @@ struct GemmParams {
     int64_t a_set_stride, b_set_stride, c_set_stride;  // bytes
     int s;
     int tiles_m, tiles_n;
-    int64_t k_begin;   // first k position of this launch (multiple of 128)
-    int k_steps;       // 128-wide k steps of this launch (even): <= 1022 keeps INT32 exact
+    int64_t k_begin;   // first k position of this launch (multiple of 256)
+    int k_steps;       // 64-wide k steps of this launch (multiple of 4): <= 2044 keeps INT32 exact
     uint32_t mod[kMaxS], barrett[kMaxS], bias[kMaxS];
 };
 

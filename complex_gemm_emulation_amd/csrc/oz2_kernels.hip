@@ -84,11 +84,11 @@ __global__ __launch_bounds__(256) void scan_strided_kernel(ScanParams P) {
 // A block encodes a tile of TV vectors x 64 k-positions.  Every thread owns
 // groups of 4 consecutive k-positions of one vector, so that each modulus
 // costs one 32-bit store per group; a wavefront writes 4 rows x 64 bytes of
-// each plane.  Strided operands are transposed through LDS first.
+// each plane, 256 contiguous bytes of one k-panel.  Strided operands are transposed through LDS first.
 template <bool CPLX>
 struct EncodeTile {
     static constexpr int TV = CPLX ? 32 : 64;   // vectors per tile
-    static constexpr int TP = 64;               // k positions per tile
+    static constexpr int TP = kPanelK;          // k positions per tile: one panel
     static constexpr int GROUPS = TV * TP / 4;  // 4-element groups
     static constexpr int PER_THREAD = GROUPS / 256;
 };
@@ -163,7 +163,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
             lr[e] = make_limbs<EXT>(xr[e], D, bad);
             if (CPLX) li[e] = make_limbs<EXT>(xi[e], D, bad);
         }
-        int8_t* dst = P.planes + gv * P.kpad + p0 + p4;
+        // k-panel layout: panel p0 / 64, row gv, byte p4
+        int8_t* dst = P.planes + (p0 / kPanelK) * P.vpad * kPanelK + gv * kPanelK + p4;
         // four moduli per trip: their constants are fetched together
         for (int t0 = 0; t0 < P.s; t0 += 4) {
 #pragma unroll

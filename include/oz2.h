@@ -170,13 +170,16 @@ int oz2_set_debug(oz2_handle_t h, int debug);
  * `dst` (at most `capacity` bytes; synchronizes first).  `which`:
  *   0 row maxima |op(A)| as IEEE bit patterns, uint64[m_pad]
  *   1 column maxima |op(B)|, uint64[n_pad]
- *   2 residue planes of op(A): int8[sets][s][m_pad][k_pad] (sets = 1 real,
- *     3 complex: re, im, re+im), rows k-contiguous
- *   3 residue planes of op(B): int8[sets][s][n_pad][k_pad]
+ *   2 residue planes of op(A) in k-panels: int8[sets][s][k_pad/64][m_pad][64]
+ *     (sets = 1 real, 3 complex: re, im, re+im): panel p holds k positions
+ *     64p .. 64p+63 of every row as 64 contiguous bytes
+ *   3 residue planes of op(B): int8[sets][s][k_pad/64][n_pad][64]
  *   4 product residues in [0, m_t): uint8[outs][s][n][m_pad] (outs = 1 real,
  *     2 complex: Re, Im)
  *   5 c_hat words (only when debug was enabled): uint32[outs][n][m_pad][N_L]
- * dims[0..4] receive (sets or outs, s, rows, cols, runs or N_L) of the buffer.
+ * dims[0..4] receive the buffer's extents: (sets, s, k_pad/64, rows_pad, 64)
+ * for 2 and 3; (outs, s, n, m_pad, runs) for 4; (outs, 1, n, m_pad, N_L)
+ * for 5; (1, 1, rows_pad, 1, 1) for 0 and 1.
  * Returns the byte size in *bytes.  -2 for an unknown `which`. */
 int oz2_debug_copy(oz2_handle_t h, int which, void* dst, size_t capacity, size_t* bytes,
                    int64_t dims[5]);

@@ -1,0 +1,67 @@
+"""Generated-code checks of the residue GEMM kernel (no GPU: hipcc
+cross-compiles gfx950 assembly here).
+
+The kernel issues its global->LDS loads from inline assembly that writes M0,
+a register the compiler reserves.  That is sound only while the compiler
+itself uses M0 nowhere in these kernels; and the point of issuing the loads
+that way is that the wait before each k step's barrier leaves the loads of
+the two following steps in flight (vmcnt(2 steps), not vmcnt(0)).  Both are
+properties of the compiler's output, checked here on every kernel instance.
+"""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "complex_gemm_emulation_amd", "csrc", "oz2_gemm.hip")
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "oz2_gemm.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernels(asm):
+    bodies = {}
+    for m in re.finditer(r"^(_Z\w*residue_gemm_kernel\w*):", asm, re.M):
+        end = asm.index(".Lfunc_end", m.end())
+        lines = [l.split(";")[0].strip() for l in asm[m.end():end].split("\n")]
+        bodies[m.group(1)] = [l for l in lines if l and not l.startswith(".")]
+    return bodies
+
+
+def test_m0_written_only_by_the_load_sequence(gemm_asm):
+    kernels = _kernels(gemm_asm)
+    assert len(kernels) == 4  # {256, 128} tiles x {real, complex}
+    for name, lines in kernels.items():
+        for i, l in enumerate(lines):
+            if re.search(r"\bm0\b", l):
+                # only the inline sequence: s_mov_b32 m0, sX ; s_nop 0 ; global_load_lds_dwordx4
+                assert l.startswith("s_mov_b32 m0,"), (name, l)
+                assert lines[i + 1] == "s_nop 0", (name, lines[i + 1])
+                assert lines[i + 2].startswith("global_load_lds_dwordx4"), (name, lines[i + 2])
+        loads = [l for l in lines if l.startswith("global_load_lds")]
+        writes = [l for l in lines if l.startswith("s_mov_b32 m0,")]
+        assert loads and len(loads) == len(writes), name
+
+
+def test_main_loop_keeps_two_steps_of_loads_in_flight(gemm_asm):
+    for name, lines in _kernels(gemm_asm).items():
+        # the wait before every barrier: vmcnt(12) after the prologue's four
+        # steps of loads, vmcnt(8) in each of the four unrolled k steps of the
+        # main loop (two steps of four loads per wave stay in flight), and one
+        # full drain before the epilogue
+        before_barrier = [lines[i - 1] for i, l in enumerate(lines) if l == "s_barrier"]
+        counts = [int(m.group(1)) for w in before_barrier for m in [re.search(r"vmcnt\((\d+)\)", w)] if m]
+        assert counts.count(8) == 4, (name, counts)
+        assert counts.count(12) == 1 and counts.count(0) == 1, (name, counts)
