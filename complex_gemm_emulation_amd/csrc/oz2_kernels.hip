@@ -85,12 +85,15 @@ __global__ __launch_bounds__(256) void scan_strided_kernel(ScanParams P) {
 // groups of 4 consecutive k-positions of one vector, so that each modulus
 // costs one 32-bit store per group; a wavefront writes 4 rows x 64 bytes of
 // each plane, 256 contiguous bytes of one k-panel.  Strided operands are transposed through LDS first.
-template <bool CPLX>
+template <bool CONTIG, bool CPLX>
 struct EncodeTile {
-    static constexpr int TV = CPLX ? 32 : 64;   // vectors per tile
+    // strided tiles are half as tall: their LDS transpose buffer (TV x 65
+    // doubles per part) then allows eight wavefronts per SIMD
+    static constexpr int TV = CONTIG ? (CPLX ? 32 : 64) : (CPLX ? 16 : 32);  // vectors per tile
     static constexpr int TP = kPanelK;          // k positions per tile: one panel
     static constexpr int GROUPS = TV * TP / 4;  // 4-element groups
     static constexpr int PER_THREAD = GROUPS / 256;
+    static_assert(PER_THREAD >= 1 && PER_THREAD * 256 == GROUPS, "tile/thread mismatch");
 };
 
 // (a_hat + h) mod m in [0, m), before removing the offset h
@@ -101,7 +104,7 @@ __device__ __forceinline__ uint32_t residue_off(const Limbs<EXT>& L, const Encod
 
 template <bool CONTIG, bool CPLX, bool EXT>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
-    using T = EncodeTile<CPLX>;
+    using T = EncodeTile<CONTIG, CPLX>;
     const int tid = threadIdx.x;
     const int64_t tiles_p = P.kpad / T::TP;
     const int64_t tp = blockIdx.x % tiles_p;
@@ -390,7 +393,7 @@ hipError_t launch_scan(const ScanParams& P, bool contiguous, bool cplx, hipStrea
 
 template <bool CONTIG, bool CPLX, bool EXT>
 static hipError_t encode_go(const EncodeParams& P, hipStream_t st) {
-    using T = EncodeTile<CPLX>;
+    using T = EncodeTile<CONTIG, CPLX>;
     const int64_t nb = (P.vpad / T::TV) * (P.kpad / T::TP);
     hipLaunchKernelGGL((encode_kernel<CONTIG, CPLX, EXT>), dim3((unsigned)nb), dim3(256), 0, st, P);
     return hipGetLastError();
