@@ -12,9 +12,9 @@
 // (Eq. 14-15): reducing the INT32 accumulator on chip and writing one byte per
 // entry removes the INT32 round trip; Sec. IV-B (Eq. 16-18): the three
 // products of the complex 3M form run as three k-loops of one block and only
-// Re and Im leave the chip.  Here T1 mod m and then T1 + T2 mod m are parked
-// in the output planes between the k-loops (each lane rereads only what it
-// wrote), so no registers beyond one accumulator set are held across loops.
+// Re and Im leave the chip.  Between the k-loops T1 mod m and then
+// (T1 + T2) mod m stay in registers as packed bytes (a quarter of an
+// accumulator set), so the epilogues of the three loops read no memory.
 //
 // Data layout: both operands are planes of 64-position k-panels (rows of
 // op(A), columns of op(B), 64 contiguous bytes per row within a panel),
@@ -158,6 +158,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
 
     v16i acc[FM][FN];
     v4i fa[2][FM], fb[2][FN];
+    // complex: T1 mod m, then (T1 + T2) mod m, four bytes per word, kept in
+    // registers across the k-loops of the three products
+    uint32_t park[CPLX ? FM : 1][CPLX ? FN : 1][4];
 
 #pragma unroll 1
     for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
@@ -259,14 +262,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
                     for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][4 * g + e], m, R, bias);
                     const int64_t row = row_out0 + i * 32 + 8 * g;
                     uint8_t* re_dst = P.C + (int64_t)t * P.n * P.mp + col * P.mp + row;
-                    if (col >= P.n) continue;
-                    if (!CPLX || pass == 0) {
-                        // real: the result; complex pass 0: T1 mod m parked in the Re plane
-                        *(uint32_t*)re_dst = pack4(r);
+                    if (!CPLX) {
+                        if (col < P.n) *(uint32_t*)re_dst = pack4(r);
+                    } else if (pass == 0) {
+                        park[i][j][g] = pack4(r);  // T1 mod m
                     } else if (pass == 1) {
-                        // Re = T1 - T2; T1 + T2 parked in the Im plane
-                        uint8_t* im_dst = re_dst + P.c_set_stride;
-                        const uint32_t t1w = *(const uint32_t*)re_dst;
+                        // Re = T1 - T2 leaves; T1 + T2 stays parked
+                        const uint32_t t1w = park[i][j][g];
                         uint32_t re[4], sm[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -278,12 +280,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
                             const uint32_t y1 = y - m;
                             sm[e] = y < y1 ? y : y1;
                         }
-                        *(uint32_t*)re_dst = pack4(re);
-                        *(uint32_t*)im_dst = pack4(sm);
+                        park[i][j][g] = pack4(sm);
+                        if (col < P.n) *(uint32_t*)re_dst = pack4(re);
                     } else {
                         // Im = T3 - (T1 + T2)
-                        uint8_t* im_dst = re_dst + P.c_set_stride;
-                        const uint32_t sw = *(const uint32_t*)im_dst;
+                        const uint32_t sw = park[i][j][g];
                         uint32_t im[4];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
                             const uint32_t x1 = x - m;
                             im[e] = x < x1 ? x : x1;
                         }
-                        *(uint32_t*)im_dst = pack4(im);
+                        if (col < P.n) *(uint32_t*)(re_dst + P.c_set_stride) = pack4(im);
                     }
                 }
             }
