@@ -15,6 +15,9 @@ Other workloads (--workload), each printing the same kind of JSON line:
   chain      Y = X x1 A x2 B x3 C for 32768 tensors of 16^3 with shared
              16 x 16 operators, one emulated product per mode (s = 16);
              metric GDoF/s = tensor entries per second of whole chains
+  nonsquare  the eight m x k x n shapes of the Arc page's Table 10 (k from
+             256 to 65536, m or n from 1024 to 65536), N/N, U(-1,1) entries,
+             s = 8 and 16; one step = the 16 calls, all inputs resident
 
 Printed: ONE JSON line with the metric, per-call phase times (HIP events
 recorded on the stream the kernels run on), the roofline of the dominant
@@ -252,6 +255,96 @@ def run_gemm(args, name):
     }
 
 
+def run_nonsquare(args):
+    """The non-square shapes at s = 8 and 16: value = all calls' 2mnk flops
+    over their total time; per shape and s the phase times."""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+
+    W = workloads.NONSQUARE
+    s_list = list(W["s"])
+    shapes = [tuple(x) for x in W["shapes"]]
+    dev = []
+    for q, (m, k, n) in enumerate(shapes):
+        log(f"[bench] nonsquare: generating {m}x{k}x{n} (seeded)")
+        A = workloads.real_matrix(m, k, workloads.nonsquare_seed(q, 0), W["dist"])
+        B = workloads.real_matrix(k, n, workloads.nonsquare_seed(q, 1), W["dist"])
+        dev.append((torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(),
+                    torch.zeros(m * n, dtype=torch.float64, device="cuda")))
+        del A, B
+    stream = torch.cuda.current_stream()
+    handles = {s: oz2.Handle(stream) for s in s_list}
+    for h in handles.values():
+        h.set_timing(True)
+    phases = {(q, s): [] for q in range(len(shapes)) for s in s_list}
+
+    def step(record):
+        for q, (m, k, n) in enumerate(shapes):
+            dA, dB, dC = dev[q]
+            for s in s_list:
+                handles[s].dgemm("N", "N", m, n, k, 1.0, dA, m, dB, k, 0.0, dC, m, s)
+                if record:
+                    phases[(q, s)].append(handles[s].phase_times())
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    flops = sum(2.0 * m * n * k for (m, k, n) in shapes) * len(s_list)
+    value = flops / (dt / args.steps) / 1e12
+    per_shape = {}
+    gemm_ops = gemm_ms = 0.0
+    for q, (m, k, n) in enumerate(shapes):
+        rec = {}
+        for s in s_list:
+            ph = np.mean(np.array(phases[(q, s)]), axis=0)
+            wk = algorithmic(m, n, k, s)
+            rec[str(s)] = dict(tflops=round(2.0 * m * n * k / (float(np.sum(ph)) * 1e-3) / 1e12, 2),
+                               ms=dict(scan=round(float(ph[0]), 4), encode=round(float(ph[1]), 4),
+                                       gemm=round(float(ph[2]), 4), reconstruct=round(float(ph[3]), 4)),
+                               gemm_int8_tops=round(wk["int8_ops"] / (ph[2] * 1e-3) / 1e12, 1))
+            gemm_ops += wk["int8_ops"]
+            gemm_ms += float(ph[2])
+        per_shape[f"{m}x{k}x{n}"] = rec
+    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    calls = len(shapes) * len(s_list)
+    roofline = dict(kernel="residue_gemm_kernel (INT8 MFMA, fused mod m)", bound="mfma",
+                    achieved=round(achieved, 2), peak=PEAK_INT8_TOPS, unit="TOP/s",
+                    frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=None,
+                    ops_per_launch=gemm_ops / calls, launch_ms=round(gemm_ms / calls, 4))
+    cpu = None
+    if not args.no_cpu_baseline:
+        q = 1  # 8192 x 1024 x 8192
+        m, k, n = shapes[q]
+        A = workloads.real_matrix(m, k, workloads.nonsquare_seed(q, 0), W["dist"])
+        B = workloads.real_matrix(k, n, workloads.nonsquare_seed(q, 1), W["dist"])
+        spec = dict(m=m, n=n, k=k, cplx=False, transa="N", transb="N", alpha=1.0, beta=0.0)
+        side = args.cpu_side or 1024
+        log(f"[bench] oracle cpu baseline on a {side}^2 entry sample of {m}x{k}x{n}, s=16")
+        cpu = cpu_baseline_gemm(spec, (m, k), A, B, None, 16, side, f"{m}x{k}x{n}")
+    for h in handles.values():
+        h.close()
+    return {
+        "metric": "emulated DGEMM TFLOP/s over the Table 10 non-square shapes (2mnk/t)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(dt / args.steps * 1e3, 3),
+        "dtype": "i8",
+        "config": {"workload": "dgemm_nonsquare_table10_s8_16", "shapes_mkn": [list(x) for x in shapes],
+                   "s": s_list, "ops": "N/N", "dist": W["dist"]},
+        "per_shape": per_shape,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
 def oracle_chain(X, Aop, Bop, Cop, n, nt, s):
     """The three emulated modes of nt tensors with the oracle, as the library
     decomposes them (mode 1 over all nt tensors at once)."""
@@ -345,7 +438,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
-                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain"])
+                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "nonsquare"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)
@@ -354,21 +447,25 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the emulated GEMM of a single device "
-              f"(got --gpus {args.gpus}); runs on several GPUs are not part of this build",
-              file=sys.stderr)
+        print(f"bench.py measures the emulated GEMM on one GPU (got --gpus {args.gpus}); "
+              f"multi-GPU runs are not supported", file=sys.stderr)
         sys.exit(2)
 
     import torch
     if args.copy_calibration:
         log(f"[bench] calibration copy of {COPY_CAL_BYTES} bytes x 3")
         copy_calibration(torch)
-    out = run_chain(args) if args.workload == "chain" else run_gemm(args, args.workload)
+    if args.workload == "chain":
+        out = run_chain(args)
+    elif args.workload == "nonsquare":
+        out = run_nonsquare(args)
+    else:
+        out = run_gemm(args, args.workload)
     line = {"metric": out["metric"], "value": out["value"], "unit": out["unit"], "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
             "data": "synthetic", "config": out["config"]}
-    for key in ("per_s", "roofline", "cpu_baseline"):
+    for key in ("per_s", "per_shape", "roofline", "cpu_baseline"):
         if key in out:
             line[key] = out[key]
     print(json.dumps(line))

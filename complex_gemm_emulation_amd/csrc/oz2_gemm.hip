@@ -25,10 +25,11 @@
 //
 // Kernel shape (CDNA4): a BM x BN tile of one modulus per block, WM x WN
 // wavefronts, each owning (BM/WM) x (BN/WN) INT32 accumulators in 32 x 32
-// MFMA tiles.  k advances one 64-byte panel per step through four LDS stages
+// MFMA tiles.  k advances one 64-byte panel per step through NST LDS stages
 // filled by direct global->LDS loads (global_load_lds_dwordx4: no VGPR
-// staging, no ds_write) issued three steps ahead, so a load has three steps
-// of MFMAs to arrive.  The loads are issued from inline assembly: the
+// staging, no ds_write) issued NST - 1 steps ahead: four stages for the
+// 256 x 256 tile, so a load has three steps of MFMAs to arrive; two for the
+// 128 x 128 tile, which instead runs four blocks per CU.  The loads are issued from inline assembly: the
 // compiler cannot tell the stages of an LDS-DMA pipeline apart and would
 // otherwise wait for every load in flight before each LDS read; here the
 // kernel's own vmcnt wait before each step's barrier orders them.  Operand
@@ -53,9 +54,9 @@ typedef __attribute__((address_space(1))) void* global_ptr_t;
 
 constexpr int kBK = kGemmStepK;  // k bytes per step (two 32-wide MFMA sub-steps)
 constexpr int kChunks = kBK / 16;
-constexpr int kStages = 4;
+constexpr int kMaxStages = 4;  // LDS stages of the 256 x 256 tile; 128 x 128 tiles use 2
 static_assert(kBK == kPanelK, "one k step is one panel");
-static_assert(kPadK % (kBK * kStages) == 0, "padded k holds whole stage rounds");
+static_assert(kPadK % (kBK * kMaxStages) == 0, "padded k holds whole stage rounds");
 
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
@@ -93,8 +94,10 @@ constexpr int waitcnt_vm(int n, bool lgkm0) {
     return (n & 15) | ((n >> 4) << 14) | 0x0070 | (lgkm0 ? 0 : 0x0F00);
 }
 
-template <int BM, int BN, int WM, int WN, bool CPLX>
+template <int BM, int BN, int WM, int WN, int NST, bool CPLX>
 __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParams P) {
+    constexpr int kStages = NST;
+    static_assert(NST == 2 || NST == 4, "two or four stages");
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
     constexpr int LOADS_A = BM * kChunks / 64 / NW;  // wave-wide 1 KiB loads per wave and stage
@@ -104,9 +107,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     // one object per stage
     __shared__ __attribute__((aligned(1024))) int8_t sS0[STAGE];
     __shared__ __attribute__((aligned(1024))) int8_t sS1[STAGE];
-    __shared__ __attribute__((aligned(1024))) int8_t sS2[STAGE];
-    __shared__ __attribute__((aligned(1024))) int8_t sS3[STAGE];
-    static_assert(kStages == 4, "four stage objects");
+    __shared__ __attribute__((aligned(1024))) int8_t sS2[NST > 2 ? STAGE : 1];
+    __shared__ __attribute__((aligned(1024))) int8_t sS3[NST > 2 ? STAGE : 1];
     auto stage = [&](int st) -> int8_t* { return st == 0 ? sS0 : st == 1 ? sS1 : st == 2 ? sS2 : sS3; };
 
     const int tid = threadIdx.x;
@@ -300,29 +302,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST>
 hipError_t gemm_go(GemmParams P, bool cplx, hipStream_t st) {
     P.tiles_m = (int)(P.mp / BM);
     P.tiles_n = (int)(P.np / BN);
     const int64_t nb = (int64_t)P.tiles_m * P.tiles_n * P.s;
     const dim3 block(64 * WM * WN);
     if (cplx)
-        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, true>), dim3((unsigned)nb), block, 0, st, P);
+        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, true>), dim3((unsigned)nb), block, 0, st, P);
     else
-        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, false>), dim3((unsigned)nb), block, 0, st, P);
+        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, false>), dim3((unsigned)nb), block, 0, st, P);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_residue_gemm(const GemmParams& P, bool cplx, hipStream_t st) {
-    if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK || P.k_begin % (kBK * kStages)) return hipErrorInvalidValue;
-    if (P.k_steps <= 0 || P.k_steps % kStages || P.k_begin + (int64_t)P.k_steps * kBK > P.kp)
+    if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK || P.k_begin % (kBK * kMaxStages))
         return hipErrorInvalidValue;
-    // large outputs: 256 x 256 tiles on 8 wavefronts; otherwise 128 x 128 on 4
+    if (P.k_steps <= 0 || P.k_steps % kMaxStages || P.k_begin + (int64_t)P.k_steps * kBK > P.kp)
+        return hipErrorInvalidValue;
+    // 256 x 256 tiles on 8 wavefronts with four stages unless the grid is
+    // small or the k-loop very short.  Otherwise 128 x 128 tiles on 4
+    // wavefronts with two stages (32 KiB): four blocks per CU, whose epilogues
+    // overlap the others' MFMAs.  Measured at 8192 x k x 8192, s = 8: 9%
+    // faster at k = 256, even at k = 1024, and 22% slower at
+    // 16384 x 2048 x 16384 (twice the L2->LDS bytes per MAC).
     const int64_t big_blocks = (P.mp / 256) * (P.np / 256) * P.s;
-    if (big_blocks >= 512) return gemm_go<256, 256, 2, 4>(P, cplx, st);
-    return gemm_go<128, 128, 2, 2>(P, cplx, st);
+    if (big_blocks >= 512 && (int64_t)P.k_steps * kBK > 512) return gemm_go<256, 256, 2, 4, 4>(P, cplx, st);
+    return gemm_go<128, 128, 2, 2, 2>(P, cplx, st);
 }
 
 }  // namespace oz2

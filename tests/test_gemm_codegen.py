@@ -42,7 +42,7 @@ def _kernels(asm):
 
 def test_m0_written_only_by_the_load_sequence(gemm_asm):
     kernels = _kernels(gemm_asm)
-    assert len(kernels) == 4  # {256, 128} tiles x {real, complex}
+    assert len(kernels) == 4  # {256 x 256 four stages, 128 x 128 two stages} x {real, complex}
     for name, lines in kernels.items():
         for i, l in enumerate(lines):
             if re.search(r"\bm0\b", l):
@@ -55,13 +55,29 @@ def test_m0_written_only_by_the_load_sequence(gemm_asm):
         assert loads and len(loads) == len(writes), name
 
 
-def test_main_loop_keeps_two_steps_of_loads_in_flight(gemm_asm):
-    for name, lines in _kernels(gemm_asm).items():
-        # the wait before every barrier: vmcnt(12) after the prologue's four
-        # steps of loads, vmcnt(8) in each of the four unrolled k steps of the
-        # main loop (two steps of four loads per wave stay in flight), and one
+def _template_args(name):
+    # residue_gemm_kernel<BM, BN, WM, WN, NST, CPLX>
+    ints = [int(x) for x in re.findall(r"Li(\d+)E", name)]
+    bm, bn, wm, wn, nst = ints[:5]
+    return bm, bn, wm, wn, nst
+
+
+def test_main_loop_keeps_loads_in_flight(gemm_asm):
+    kernels = _kernels(gemm_asm)
+    assert {_template_args(n)[4] for n in kernels} == {2, 4}
+    for name, lines in kernels.items():
+        bm, bn, wm, wn, nst = _template_args(name)
+        loads = (bm + bn) * 4 // (64 * wm * wn)  # 1 KiB loads per wave and step
+        # the wait before every barrier: the prologue's NST steps of loads
+        # less the first step, then in each of the NST unrolled k steps of the
+        # main loop the loads of NST - 2 later steps still in flight, then one
         # full drain before the epilogue
         before_barrier = [lines[i - 1] for i, l in enumerate(lines) if l == "s_barrier"]
         counts = [int(m.group(1)) for w in before_barrier for m in [re.search(r"vmcnt\((\d+)\)", w)] if m]
-        assert counts.count(8) == 4, (name, counts)
-        assert counts.count(12) == 1 and counts.count(0) == 1, (name, counts)
+        loop = (nst - 2) * loads
+        first = (nst - 1) * loads
+        assert counts.count(first) == 1, (name, counts)
+        if loop:
+            assert counts.count(loop) == nst and counts.count(0) == 1, (name, counts)
+        else:
+            assert counts.count(0) == nst + 1, (name, counts)

@@ -42,6 +42,19 @@ WORKLOADS = {
             dist="uniform"),
 }
 
+# Non-square shapes (m, k, n) at s = 8 and 16, N/N, U(-1, 1) inputs: the
+# shape list of the Arc page's Table 10 (Sec. 7.1).  The emulation's run time
+# does not depend on the values, so the cheapest distribution to draw is used.
+NONSQUARE = dict(id=6, s=(8, 16), dist="uniform",
+                 shapes=((8192, 256, 8192), (8192, 1024, 8192), (8192, 32768, 8192),
+                         (8192, 65536, 8192), (65536, 4096, 1024), (1024, 4096, 65536),
+                         (4000, 8000, 4000), (16384, 2048, 16384)))
+
+
+def nonsquare_seed(shape_index: int, operand: int) -> int:
+    """seed of operand (0 = A, 1 = B) of the shape_index-th non-square shape"""
+    return seed(NONSQUARE["id"], 10 * int(shape_index) + int(operand))
+
 
 def seed(workload: int, operand: int) -> int:
     return SEED_BASE + 100 * int(workload) + int(operand)
