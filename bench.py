@@ -15,6 +15,9 @@ Other workloads (--workload), each printing the same kind of JSON line:
   chain      Y = X x1 A x2 B x3 C for 32768 tensors of 16^3 with shared
              16 x 16 operators, one emulated product per mode (s = 16);
              metric GDoF/s = tensor entries per second of whole chains
+  reuse8192  the headline product with op(A) prepared once and reused; each
+             call re-encodes B (oz2_operand_update) and runs
+             oz2_gemm_prepared (phase times: GEMM and reconstruct only)
   nonsquare  the eight m x k x n shapes of the Arc page's Table 10 (k from
              256 to 65536, m or n from 1024 to 65536), N/N, U(-1,1) entries,
              s = 8 and 16; one step = the 16 calls, all inputs resident
@@ -134,6 +137,11 @@ GEMM_SPECS = {
     "zgemm4096": dict(cplx=True, m=4096, n=4096, k=4096, s=[16], transa="C", transb="N",
                       alpha=complex(0.7, -0.3), beta=complex(0.2, 0.1), phi=0.5, seedw=4,
                       cpu_side=512),
+    # the headline product with op(A) prepared once (oz2_operand_create) and
+    # reused by every call: each call re-encodes B into a prepared op(B)
+    # (oz2_operand_update) and runs oz2_gemm_prepared
+    "reuse8192": dict(cplx=False, m=8192, n=8192, k=8192, s=[8, 12, 16], transa="N", transb="N",
+                      alpha=1.0, beta=0.0, phi=0.5, seedw=2, cpu_side=1024, prepared_a=True),
 }
 
 
@@ -175,9 +183,20 @@ def run_gemm(args, name):
     for h in handles.values():
         h.set_timing(True)
 
+    prepared = {}
+    if spec.get("prepared_a"):
+        for s in s_list:
+            prepared[s] = (handles[s].prepare("A", ta, m, k, dA, ra, s, cplx),
+                           handles[s].prepare("B", tb, n, k, dB, rb, s, cplx))
+        torch.cuda.synchronize()
+
     def step(record):
         for s in s_list:
-            if cplx:
+            if prepared:
+                pa, pb = prepared[s]
+                handles[s].update(pb, dB, rb)
+                handles[s].gemm_prepared(pa, pb, spec["alpha"], spec["beta"], dC, m)
+            elif cplx:
                 handles[s].zgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
             else:
                 handles[s].dgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
@@ -236,17 +255,22 @@ def run_gemm(args, name):
         log(f"[bench] oracle cpu baseline on a {side}^2 entry sample, s={s_cpu}")
         cpu = cpu_baseline_gemm(spec, (ra, rb), A, B, C, s_cpu, side, f"{m}x{n}x{k}")
 
+    for pa, pb in prepared.values():
+        pa.close()
+        pb.close()
     for h in handles.values():
         h.close()
     kind = "zgemm" if cplx else "dgemm"
     return {
         "metric": METRIC if name == "dgemm8192" else
-                  f"emulated {'ZGEMM' if cplx else 'DGEMM'} TFLOP/s ({'8' if cplx else '2'}MNK/t)",
+                  f"emulated {'ZGEMM' if cplx else 'DGEMM'} TFLOP/s ({'8' if cplx else '2'}MNK/t)"
+                  + (", op(A) prepared once and reused" if prepared else ""),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "ms_per_step": round(ms_per_step, 3),
         "dtype": "i8",
-        "config": {"workload": f"{kind}_{m}_{ta}{tb}_phi{spec['phi']}_s{'_'.join(map(str, s_list))}",
+        "config": {"workload": f"{kind}_{m}_{ta}{tb}_phi{spec['phi']}_s{'_'.join(map(str, s_list))}"
+                               + ("_prepared_a" if prepared else ""),
                    "m": m, "n": n, "k": k, "s": s_list, "ops": f"{ta}/{tb}",
                    "alpha": str(spec["alpha"]), "beta": str(spec["beta"])},
         "per_s": per_s,
@@ -438,7 +462,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
-                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "nonsquare"])
+                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "nonsquare", "reuse8192"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)

@@ -17,8 +17,8 @@ import os
 
 import numpy as np
 
-__all__ = ["Handle", "Oz2Error", "lib", "plan_info", "moduli_for_bits", "EXPORTED_SYMBOLS",
-           "LIB_PATH"]
+__all__ = ["Handle", "Operand", "Oz2Error", "lib", "plan_info", "moduli_for_bits",
+           "EXPORTED_SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboz2.so")
 
@@ -27,7 +27,8 @@ EXPORTED_SYMBOLS = (
     "oz2_create", "oz2_destroy", "oz2_set_stream", "oz2_set_memory_limit",
     "oz2_get_workspace_size", "oz2_set_timing", "oz2_get_phase_times", "oz2_moduli_for_bits",
     "oz2_plan_info", "oz2_dgemm", "oz2_zgemm", "oz2_dgemm_strided_batched", "oz2_status_string",
-    "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt",
+    "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt", "oz2_operand_create",
+    "oz2_operand_update", "oz2_operand_destroy", "oz2_gemm_prepared",
 )
 
 _lib = None
@@ -67,6 +68,10 @@ def _raw():
             "oz2_set_debug": [P, I],
             "oz2_debug_copy": [P, I, P, SZ, P, P],
             "oz2_test_crt": [P, I64, I, P, P],
+            "oz2_operand_create": [P, C, I, C, I64, I64, P, I64, I, P],
+            "oz2_operand_update": [P, P, P, I64],
+            "oz2_operand_destroy": [P],
+            "oz2_gemm_prepared": [P, P, P, P, P, P, I64],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -120,6 +125,32 @@ def _dev_ptr(x, dtype_name: str, need: int, what: str):
     if x.numel() < need:
         raise ValueError(f"{what} holds {x.numel()} elements, the call needs {need}")
     return ctypes.c_void_p(x.data_ptr())
+
+
+class Operand:
+    """A prepared operand (oz2_operand_create): the exponents and residue
+    planes of op(A) (side 'A') or op(B) (side 'B') kept on the device."""
+
+    def __init__(self, ptr, side, cplx, trans, rows, k, s):
+        self._p = ptr
+        self.side, self.cplx, self.trans, self.rows, self.k, self.s = side, cplx, trans, rows, k, s
+
+    def close(self) -> None:
+        if self._p is not None and self._p.value:
+            _raw().oz2_operand_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
 
 
 class Handle:
@@ -220,6 +251,43 @@ class Handle:
                _raw().oz2_dgemm_strided_batched(self._h, transa.encode(), transb.encode(), m, n,
                                                 k, float(alpha), pa, lda, strideA, pb, ldb,
                                                 strideB, float(beta), pc, ldc, strideC, batch, s))
+
+    # ------------------------------------------------------ prepared operands
+    def prepare(self, side, trans, rows, k, X, ld, s, cplx=False) -> Operand:
+        """Scan and encode op(X) once (oz2_operand_create): side 'A' gives
+        op(A) with rows = m, side 'B' gives op(B) with rows = n."""
+        side, trans = side.upper(), trans.upper()
+        if side == "A":
+            r, c = self._stored(trans, rows, k)
+        else:
+            r, c = self._stored(trans, k, rows)
+        px = _dev_ptr(X, "c128" if cplx else "f64", _extent(r, c, ld), "X")
+        out = ctypes.c_void_p()
+        self._bind_stream()
+        _check("oz2_operand_create",
+               _raw().oz2_operand_create(self._h, side.encode(), int(cplx), trans.encode(), rows, k,
+                                         px, ld, s, ctypes.byref(out)))
+        return Operand(out, side, cplx, trans, rows, k, s)
+
+    def update(self, op: Operand, X, ld) -> None:
+        """Re-encode new data of the same shape into `op` (oz2_operand_update)."""
+        if op.side == "A":
+            r, c = self._stored(op.trans, op.rows, op.k)
+        else:
+            r, c = self._stored(op.trans, op.k, op.rows)
+        px = _dev_ptr(X, "c128" if op.cplx else "f64", _extent(r, c, ld), "X")
+        self._bind_stream()
+        _check("oz2_operand_update", _raw().oz2_operand_update(self._h, op._p, px, ld))
+
+    def gemm_prepared(self, pa: Operand, pb: Operand, alpha, beta, C, ldc) -> None:
+        """C <- alpha op(A) op(B) + beta C from two prepared operands."""
+        m, n = pa.rows, pb.rows
+        alpha, beta = complex(alpha), complex(beta)
+        pc = _dev_ptr(C, "c128" if pa.cplx else "f64", _extent(m, n, ldc), "C")
+        al = (ctypes.c_double * 2)(alpha.real, alpha.imag)
+        be = (ctypes.c_double * 2)(beta.real, beta.imag)
+        self._bind_stream()
+        _check("oz2_gemm_prepared", _raw().oz2_gemm_prepared(self._h, pa._p, pb._p, al, be, pc, ldc))
 
     def tensor_mode_chain(self, X, A, B, C, n, batch, s, Y=None, work=None):
         """Y = X x1 A x2 B x3 C for `batch` independent n x n x n tensors

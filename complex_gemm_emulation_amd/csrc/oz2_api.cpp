@@ -36,6 +36,7 @@ struct Layout {
     size_t off_amaxA = 0, off_amaxB = 0, off_pa = 0, off_pb = 0, off_res = 0, off_chat = 0;
     size_t bytes_pa = 0, bytes_pb = 0, bytes_res = 0, bytes_chat = 0, total = 0;
     bool valid = false;
+    bool prepared = false;  // operands came from oz2_operand objects (not in the workspace)
 };
 
 }  // namespace
@@ -51,6 +52,18 @@ struct oz2_context {
     bool timed = false;
     hipEvent_t ev[5] = {};
     Layout last;
+};
+
+// a scanned and encoded operand kept on the device between products
+struct oz2_operand {
+    int device = 0;
+    bool cplx = false, is_a = true, ext = false;
+    char trans = 'N';
+    int64_t rows = 0, k = 0, rows_pad = 0, kp = 0;
+    int s = 0, t = 0, sets = 1;
+    void* mem = nullptr;
+    uint64_t* amax = nullptr;  // [rows_pad] bit patterns of the row (column) maxima
+    int8_t* planes = nullptr;  // [sets][s][kp/64][rows_pad][64]
 };
 
 namespace {
@@ -154,7 +167,7 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
 
 // workspace layout of the four-phase path for one m x n x k product
 Layout plan_layout(const oz2_context* h, bool cplx, int s, const ModuliPlan& plan, int t, int64_t m, int64_t n,
-                   int64_t k) {
+                   int64_t k, bool with_operands = true) {
     const ModuliPlan* pl = &plan;
     Layout L;
     L.sets = cplx ? 3 : 1;
@@ -167,12 +180,16 @@ Layout plan_layout(const oz2_context* h, bool cplx, int s, const ModuliPlan& pla
     L.np = round_up(n, kPadM);
     L.kp = round_up(k, kPadK);
     size_t off = 0;
-    L.off_amaxA = off; off = align_up(off + 8 * (size_t)L.mp);
-    L.off_amaxB = off; off = align_up(off + 8 * (size_t)L.np);
-    L.bytes_pa = (size_t)L.sets * s * L.mp * L.kp;
-    L.off_pa = off; off = align_up(off + L.bytes_pa);
-    L.bytes_pb = (size_t)L.sets * s * L.np * L.kp;
-    L.off_pb = off; off = align_up(off + L.bytes_pb);
+    if (with_operands) {
+        L.off_amaxA = off; off = align_up(off + 8 * (size_t)L.mp);
+        L.off_amaxB = off; off = align_up(off + 8 * (size_t)L.np);
+        L.bytes_pa = (size_t)L.sets * s * L.mp * L.kp;
+        L.off_pa = off; off = align_up(off + L.bytes_pa);
+        L.bytes_pb = (size_t)L.sets * s * L.np * L.kp;
+        L.off_pb = off; off = align_up(off + L.bytes_pb);
+    } else {
+        L.prepared = true;
+    }
     L.chunks = (int)((L.kp + kMaxRunK - 1) / kMaxRunK);
     L.bytes_res = (size_t)L.chunks * L.outs * s * L.n * L.mp;
     L.off_res = off; off = align_up(off + L.bytes_res);
@@ -204,69 +221,58 @@ bool fits(oz2_context* h, size_t bytes, size_t* cap) {
     return bytes <= *cap;
 }
 
-// the four phases for one block (the whole product when untiled); record:
-// phase events of this call
-int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n, int64_t k,
-         const double alpha[2], const double* A, int64_t lda, const double* B, int64_t ldb,
-         const double beta[2], double* C, int64_t ldc, int s, const ModuliPlan* pl, int t, bool ext,
-         bool record) {
+// phase 1 for one operand: the row maxima of op(A) (is_a) or the column
+// maxima of op(B).  Row i of op(A) is column i of A when transposed; column
+// j of op(B) is column j of B when not.
+bool operand_contiguous(bool is_a, char trans) { return is_a ? is_trans(trans) : !is_trans(trans); }
+
+int scan_operand(oz2_context* h, bool cplx, bool is_a, char trans, int64_t rows, int64_t k, const double* X,
+                 int64_t ld, uint64_t* amax, int64_t rows_pad) {
+    hipStream_t stm = h->stream;
+    OZ2_LAUNCH(launch_fill_u64(amax, rows_pad, 0, stm));
+    ScanParams S{};
+    S.X = X; S.ld = ld; S.nvec = rows; S.k = k; S.amax = amax;
+    const int64_t vb = (rows + 255) / 256;
+    int64_t chunks = 2048 / (vb > 0 ? vb : 1);
+    if (chunks < 1) chunks = 1;
+    S.pchunk = (k + chunks - 1) / chunks;
+    OZ2_LAUNCH(launch_scan(S, operand_contiguous(is_a, trans), cplx, stm));
+    return OZ2_STATUS_SUCCESS;
+}
+
+// phase 2 for one operand: integerize with the scan's exponents and write the
+// residue planes [sets][s][kp/64][rows_pad][64]
+int encode_operand(oz2_context* h, bool cplx, bool is_a, char trans, int64_t rows, int64_t k, const double* X,
+                   int64_t ld, int s, const ModuliPlan* pl, int t, bool ext, const uint64_t* amax,
+                   int8_t* planes, int64_t rows_pad, int64_t kp) {
+    EncodeParams E{};
+    fill_mod_tables(*pl, &E, ext);
+    E.t = t; E.s = s;
+    E.X = X; E.ld = ld; E.nvec = rows; E.k = k; E.vpad = rows_pad; E.kpad = kp;
+    E.set_stride = (int64_t)s * rows_pad * kp;
+    E.amax = amax; E.planes = planes; E.conj = cplx && is_conj(trans);
+    OZ2_LAUNCH(launch_encode(E, operand_contiguous(is_a, trans), cplx, ext, h->stream));
+    return OZ2_STATUS_SUCCESS;
+}
+
+// phases 3 and 4: s exact INT8 products reduced mod m_t on chip (one launch
+// per k run of at most kMaxRunK positions), then CRT, rounding, scale back
+// and alpha/beta.  L gives the padded sizes and the workspace offsets of the
+// product residues (and c_hat).
+int product(oz2_context* h, bool cplx, const Layout& L, const int8_t* pa, const uint64_t* amaxA, const int8_t* pb,
+            const uint64_t* amaxB, const double alpha[2], const double beta[2], double* C, int64_t ldc,
+            const ModuliPlan* pl, bool record) {
     const bool beta_zero = beta[0] == 0.0 && beta[1] == 0.0;
-    Layout L = plan_layout(h, cplx, s, *pl, t, m, n, k);
-    int st = ensure_workspace(h, L.total);
-    if (st) return st;
+    const int s = L.s;
     char* ws = (char*)h->ws;
-    uint64_t* amaxA = (uint64_t*)(ws + L.off_amaxA);
-    uint64_t* amaxB = (uint64_t*)(ws + L.off_amaxB);
-    int8_t* pa = (int8_t*)(ws + L.off_pa);
-    int8_t* pb = (int8_t*)(ws + L.off_pb);
     uint8_t* res = (uint8_t*)(ws + L.off_res);
     uint32_t* chat = h->debug ? (uint32_t*)(ws + L.off_chat) : nullptr;
     hipStream_t stm = h->stream;
-
-    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[0], stm));
-    // phase 1: row maxima of op(A), column maxima of op(B)
-    OZ2_LAUNCH(launch_fill_u64(amaxA, L.mp, 0, stm));
-    OZ2_LAUNCH(launch_fill_u64(amaxB, L.np, 0, stm));
-    {
-        ScanParams S{};
-        S.X = A; S.ld = lda; S.nvec = m; S.k = k; S.amax = amaxA;
-        const bool contig = is_trans(transa);  // row i of op(A) = column i of A
-        int64_t vb = (m + 255) / 256, chunks = 2048 / (vb > 0 ? vb : 1);
-        if (chunks < 1) chunks = 1;
-        S.pchunk = (k + chunks - 1) / chunks;
-        OZ2_LAUNCH(launch_scan(S, contig, cplx, stm));
-        ScanParams Sb{};
-        Sb.X = B; Sb.ld = ldb; Sb.nvec = n; Sb.k = k; Sb.amax = amaxB;
-        const bool contig_b = !is_trans(transb);  // column j of op(B) = column j of B
-        vb = (n + 255) / 256;
-        chunks = 2048 / (vb > 0 ? vb : 1);
-        if (chunks < 1) chunks = 1;
-        Sb.pchunk = (k + chunks - 1) / chunks;
-        OZ2_LAUNCH(launch_scan(Sb, contig_b, cplx, stm));
-    }
-    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
-    // phase 2: integerize and encode both operands
-    {
-        EncodeParams E{};
-        fill_mod_tables(*pl, &E, ext);
-        E.t = t; E.s = s;
-        E.X = A; E.ld = lda; E.nvec = m; E.k = k; E.vpad = L.mp; E.kpad = L.kp;
-        E.set_stride = (int64_t)s * L.mp * L.kp;
-        E.amax = amaxA; E.planes = pa; E.conj = cplx && is_conj(transa);
-        OZ2_LAUNCH(launch_encode(E, is_trans(transa), cplx, ext, stm));
-        E.X = B; E.ld = ldb; E.nvec = n; E.vpad = L.np;
-        E.set_stride = (int64_t)s * L.np * L.kp;
-        E.amax = amaxB; E.planes = pb; E.conj = cplx && is_conj(transb);
-        OZ2_LAUNCH(launch_encode(E, !is_trans(transb), cplx, ext, stm));
-    }
-    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
-    // phase 3: s exact INT8 products, reduced mod m_t on chip, one launch per
-    // k run of at most kMaxRunK positions
     const int64_t chunk_stride = (int64_t)L.outs * s * L.n * L.mp;
     {
         GemmParams G{};
         G.A = pa; G.B = pb;
-        G.mp = L.mp; G.np = L.np; G.kp = L.kp; G.n = n;
+        G.mp = L.mp; G.np = L.np; G.kp = L.kp; G.n = L.n;
         G.a_set_stride = (int64_t)s * L.mp * L.kp;
         G.b_set_stride = (int64_t)s * L.np * L.kp;
         G.c_set_stride = (int64_t)s * L.n * L.mp;
@@ -285,11 +291,10 @@ int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t
         }
     }
     if (record) OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
-    // phase 4: CRT, rounding, scale back, alpha/beta
     {
         ReconParams R{};
         fill_crt_tables(*pl, &R);
-        R.R = res; R.mp = L.mp; R.m = m; R.n = n;
+        R.R = res; R.mp = L.mp; R.m = L.m; R.n = L.n;
         R.r_set_stride = (int64_t)s * L.n * L.mp;
         R.r_chunk_stride = chunk_stride;
         R.chunks = L.chunks;
@@ -298,13 +303,41 @@ int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t
         R.C = C; R.ldc = ldc;
         R.alpha[0] = alpha[0]; R.alpha[1] = alpha[1];
         R.beta[0] = beta[0]; R.beta[1] = beta[1];
-        R.t = t; R.s = s; R.chat = chat;
+        R.t = L.t; R.s = s; R.chat = chat;
         OZ2_LAUNCH(launch_reconstruct(R, pl->NL, cplx, !beta_zero, stm));
     }
     if (record) {
         OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
         h->timed = true;
     }
+    return OZ2_STATUS_SUCCESS;
+}
+
+// the four phases for one block (the whole product when untiled); record:
+// phase events of this call
+int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n, int64_t k,
+         const double alpha[2], const double* A, int64_t lda, const double* B, int64_t ldb,
+         const double beta[2], double* C, int64_t ldc, int s, const ModuliPlan* pl, int t, bool ext,
+         bool record) {
+    Layout L = plan_layout(h, cplx, s, *pl, t, m, n, k);
+    int st = ensure_workspace(h, L.total);
+    if (st) return st;
+    char* ws = (char*)h->ws;
+    uint64_t* amaxA = (uint64_t*)(ws + L.off_amaxA);
+    uint64_t* amaxB = (uint64_t*)(ws + L.off_amaxB);
+    int8_t* pa = (int8_t*)(ws + L.off_pa);
+    int8_t* pb = (int8_t*)(ws + L.off_pb);
+    hipStream_t stm = h->stream;
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[0], stm));
+    if ((st = scan_operand(h, cplx, true, transa, m, k, A, lda, amaxA, L.mp))) return st;
+    if ((st = scan_operand(h, cplx, false, transb, n, k, B, ldb, amaxB, L.np))) return st;
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
+    if ((st = encode_operand(h, cplx, true, transa, m, k, A, lda, s, pl, t, ext, amaxA, pa, L.mp, L.kp))) return st;
+    if ((st = encode_operand(h, cplx, false, transb, n, k, B, ldb, s, pl, t, ext, amaxB, pb, L.np, L.kp)))
+        return st;
+    if (record) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
+    st = product(h, cplx, L, pa, amaxA, pb, amaxB, alpha, beta, C, ldc, pl, record);
+    if (st) return st;
     L.valid = true;
     h->last = L;
     return OZ2_STATUS_SUCCESS;
@@ -551,6 +584,117 @@ const char* oz2_status_string(int status) {
     }
 }
 
+int oz2_operand_create(oz2_handle_t h, char side, int is_complex, char trans, int64_t rows, int64_t k,
+                       const double* X, int64_t ld, int num_moduli, oz2_operand_t* out) {
+    if (!h) return -1;
+    const bool is_a = side == 'A' || side == 'a';
+    if (!is_a && !(side == 'B' || side == 'b')) return -2;
+    if (!valid_op(trans)) return -4;
+    if (rows < 1) return -5;
+    if (k < 1) return -6;
+    if (!X) return -7;
+    // stored rows: A is m x k (N) or k x m (T/C); B is k x n (N) or n x k (T/C)
+    const int64_t stored = is_a ? (is_trans(trans) ? k : rows) : (is_trans(trans) ? rows : k);
+    if (ld < stored) return -8;
+    if (num_moduli < kMinS || num_moduli > kMaxS) return -9;
+    if (!out) return -10;
+    *out = nullptr;
+    const bool cplx = is_complex != 0;
+    const ModuliPlan* pl = moduli_plan(num_moduli);
+    if (!pl) return OZ2_STATUS_INTERNAL;
+    const int t = scaling_width(*pl, k, cplx);
+    if (t < 1) return OZ2_STATUS_RANGE;
+    oz2_operand* op = new (std::nothrow) oz2_operand();
+    if (!op) return OZ2_STATUS_ALLOC_FAILED;
+    op->device = h->device;
+    op->cplx = cplx; op->is_a = is_a; op->trans = trans;
+    op->rows = rows; op->k = k;
+    op->rows_pad = round_up(rows, kPadM);
+    op->kp = round_up(k, kPadK);
+    op->s = num_moduli; op->t = t; op->ext = t > kMaxStdT;
+    op->sets = cplx ? 3 : 1;
+    const size_t off_planes = align_up(8 * (size_t)op->rows_pad);
+    const size_t bytes = off_planes + (size_t)op->sets * op->s * op->rows_pad * op->kp;
+    if (hipMalloc(&op->mem, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        delete op;
+        return OZ2_STATUS_ALLOC_FAILED;
+    }
+    op->amax = (uint64_t*)op->mem;
+    op->planes = (int8_t*)op->mem + off_planes;
+    int st = scan_operand(h, cplx, is_a, trans, rows, k, X, ld, op->amax, op->rows_pad);
+    if (!st) st = encode_operand(h, cplx, is_a, trans, rows, k, X, ld, op->s, pl, t, op->ext, op->amax, op->planes,
+                                 op->rows_pad, op->kp);
+    if (st) {
+        (void)hipStreamSynchronize(h->stream);
+        (void)hipFree(op->mem);
+        delete op;
+        return st;
+    }
+    *out = op;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_operand_update(oz2_handle_t h, oz2_operand_t op, const double* X, int64_t ld) {
+    if (!h) return -1;
+    if (!op) return -2;
+    if (!X) return -3;
+    const int64_t stored = op->is_a ? (is_trans(op->trans) ? op->k : op->rows) : (is_trans(op->trans) ? op->rows : op->k);
+    if (ld < stored) return -4;
+    const ModuliPlan* pl = moduli_plan(op->s);
+    if (!pl) return OZ2_STATUS_INTERNAL;
+    int st = scan_operand(h, op->cplx, op->is_a, op->trans, op->rows, op->k, X, ld, op->amax, op->rows_pad);
+    if (st) return st;
+    return encode_operand(h, op->cplx, op->is_a, op->trans, op->rows, op->k, X, ld, op->s, pl, op->t, op->ext,
+                          op->amax, op->planes, op->rows_pad, op->kp);
+}
+
+int oz2_operand_destroy(oz2_operand_t op) {
+    if (!op) return -1;
+    if (op->mem && hipFree(op->mem) != hipSuccess) {
+        (void)hipGetLastError();
+        delete op;
+        return OZ2_STATUS_HIP_ERROR;
+    }
+    delete op;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const double* alpha,
+                      const double* beta, double* C, int64_t ldc) {
+    if (!h) return -1;
+    if (!pa || !pa->is_a) return -2;
+    if (!pb || pb->is_a || pb->cplx != pa->cplx || pb->s != pa->s || pb->k != pa->k) return -3;
+    if (!alpha) return -4;
+    if (!beta) return -5;
+    if (!C) return -6;
+    const int64_t m = pa->rows, n = pb->rows, k = pa->k;
+    if (ldc < m) return -7;
+    const bool cplx = pa->cplx;
+    const double al[2] = {alpha[0], cplx ? alpha[1] : 0.0};
+    const double be[2] = {beta[0], cplx ? beta[1] : 0.0};
+    h->timed = false;
+    if (al[0] == 0.0 && al[1] == 0.0) {
+        OZ2_LAUNCH(launch_scale_c(C, m, n, ldc, be, cplx, h->stream));
+        return OZ2_STATUS_SUCCESS;
+    }
+    const ModuliPlan* pl = moduli_plan(pa->s);
+    if (!pl) return OZ2_STATUS_INTERNAL;
+    Layout L = plan_layout(h, cplx, pa->s, *pl, pa->t, m, n, k, false);
+    size_t cap = 0;
+    if (!fits(h, L.total, &cap)) return OZ2_STATUS_WORKSPACE_LIMIT;
+    int st = ensure_workspace(h, L.total);
+    if (st) return st;
+    const bool rec = h->timing != 0;
+    if (rec)
+        for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], h->stream));
+    st = product(h, cplx, L, pa->planes, pa->amax, pb->planes, pb->amax, al, be, C, ldc, pl, rec);
+    if (st) return st;
+    L.valid = true;
+    h->last = L;
+    return OZ2_STATUS_SUCCESS;
+}
+
 int oz2_set_debug(oz2_handle_t h, int debug) {
     if (!h) return -1;
     h->debug = debug ? 1 : 0;
@@ -564,6 +708,7 @@ int oz2_debug_copy(oz2_handle_t h, int which, void* dst, size_t capacity, size_t
     if (!L.valid) return OZ2_STATUS_INTERNAL;
     size_t off = 0, nbytes = 0;
     int64_t d[5] = {1, 1, 1, 1, 1};
+    if (L.prepared && which >= 0 && which <= 3) return OZ2_STATUS_NOT_SUPPORTED;
     switch (which) {
         case 0: off = L.off_amaxA; nbytes = 8 * (size_t)L.mp; d[2] = L.mp; break;
         case 1: off = L.off_amaxB; nbytes = 8 * (size_t)L.np; d[2] = L.np; break;

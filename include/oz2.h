@@ -152,6 +152,59 @@ int oz2_dgemm_strided_batched(oz2_handle_t h, char transa, char transb, int64_t 
                               double beta, double* C, int64_t ldc, int64_t strideC,
                               int64_t batch, int num_moduli);
 
+/* ---------------------------------------------------------------------
+ * Prepared operands: the row exponents and residue planes of op(A), or the
+ * column exponents and residue planes of op(B), computed once and kept on
+ * the device, so that products which reuse an operand skip its scan and
+ * encode phases.  The Arc page names reuse of the residues of A across
+ * calls as future work (Sec. 10); the chain page caches the operators'
+ * residues the same way ("You Only Convert Twice", Sec. 5, Algorithm 6 and
+ * Fig. 4).  A prepared operand depends on (side, complex, op, rows, k, s):
+ * every product that uses it has the same k and num_moduli, and therefore
+ * the same scaling width t, so results are bitwise those of oz2_dgemm /
+ * oz2_zgemm on the same data.
+ * ------------------------------------------------------------------- */
+typedef struct oz2_operand* oz2_operand_t;
+
+/* Allocate DEVICE memory for a prepared operand (owned by the returned
+ * object; rows_pad * k_pad * s * sets bytes plus 8 * rows_pad, with
+ * rows_pad = rows rounded up to 256, k_pad = k rounded up to 256, sets = 1
+ * real or 3 complex) and enqueue its scan and encode on h's stream.
+ * side 'A': X is A, op(A) = op(X) is rows x k (rows = m), X stored m x k
+ * (trans 'N') or k x m (trans 'T' or 'C'); side 'B': X is B, op(B) is
+ * k x rows (rows = n), X stored k x n ('N') or n x k ('T' / 'C').  X is a
+ * DEVICE pointer (complex128 when is_complex), read only by the enqueued
+ * work: it may be changed or freed once h's stream has passed this call.
+ * Argument numbers of the -i codes: h 1, side 2, trans 4, rows 5, k 6,
+ * X 7, ld 8, num_moduli 9, out 10.  OZ2_STATUS_RANGE when no scaling width
+ * exists for (num_moduli, k); OZ2_STATUS_ALLOC_FAILED when the device
+ * memory cannot be allocated.  *out is NULL on any failure. */
+int oz2_operand_create(oz2_handle_t h, char side, int is_complex, char trans, int64_t rows, int64_t k,
+                       const double* X, int64_t ld, int num_moduli, oz2_operand_t* out);
+
+/* Re-encode new data of the same shape into `op` (scan and encode enqueued
+ * on h's stream): -1 h, -2 op, -3 X, -4 ld.  Work already enqueued that
+ * reads `op` uses the old data (stream order). */
+int oz2_operand_update(oz2_handle_t h, oz2_operand_t op, const double* X, int64_t ld);
+
+/* Free a prepared operand's device memory (hipFree waits for the device, so
+ * enqueued work that reads it completes first). */
+int oz2_operand_destroy(oz2_operand_t op);
+
+/* C <- alpha op(A) op(B) + beta C from a prepared op(A) (side 'A') and a
+ * prepared op(B) (side 'B') with the same is_complex, k and num_moduli: the
+ * residue GEMM and reconstruct phases only.  m = rows of pa, n = rows of pb.
+ * alpha[2], beta[2]: HOST arrays (re, im); the imaginary parts are ignored
+ * for real operands.  C is a DEVICE pointer, ldc >= m.  The workspace holds
+ * only the product residues; when it exceeds the memory limit the call
+ * returns OZ2_STATUS_WORKSPACE_LIMIT (no tiling on this path).  Phase times:
+ * ms[0] = ms[1] = 0.  Argument numbers of the -i codes: h 1, pa 2, pb 3
+ * (also when it does not match pa), alpha 4, beta 5, C 6, ldc 7.
+ * oz2_debug_copy of buffers 0-3 after such a call returns
+ * OZ2_STATUS_NOT_SUPPORTED (they live in the operand objects). */
+int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const double* alpha,
+                      const double* beta, double* C, int64_t ldc);
+
 /* Human-readable text of a status code (static storage). */
 const char* oz2_status_string(int status);
 

@@ -60,3 +60,12 @@ def test_status_strings():
     assert lib.oz2_status_string(0) == b"success"
     assert b"scaling width" in lib.oz2_status_string(3)
     assert lib.oz2_status_string(-3) == b"invalid argument"
+
+
+def test_prepared_operand_entry_points_reject_null_handles():
+    # no GPU needed: argument checks run before any HIP call
+    lib = oz2.lib()
+    assert lib.oz2_operand_create(None, b"A", 0, b"N", 1, 1, None, 1, 8, None) == -1
+    assert lib.oz2_operand_update(None, None, None, 1) == -1
+    assert lib.oz2_operand_destroy(None) == -1
+    assert lib.oz2_gemm_prepared(None, None, None, None, None, None, 1) == -1
