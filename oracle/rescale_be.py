@@ -1,0 +1,322 @@
+"""CPU oracle for OzII-RescaleBE (persistent Ozaki scheme II tensor mode-product
+chains) -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The product never imports, links or
+executes anything under ``oracle/``, and this module shares no code, tables or
+constant generators with it.
+
+Source page (cited by title and section; nothing here is copied from it):
+"You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products"
+
+* Sec. 2.3, Eq. (11)-(12): centred residues [v]_p.
+* Sec. 2.3.1, Eq. (14)-(15), and Algorithm 1 (RnsDrop): rescaling by a
+  modulus q on the residues, v' = (v - [v]_q) / q, scale alpha' = alpha q.
+* Sec. 2.3.2, Eq. (16)-(17), Sec. 4.4, Eq. (24)-(26), and Algorithm 4
+  (MrcDigits, BaseExtend): centred mixed-radix digits by successive modular
+  elimination, weights omega_{i,p} = [prod_{j<i} q_j]_p.
+* Sec. 4.3, Eq. (21)-(23), and Algorithms 2-3 (DropPlan, Planner): operator
+  row-sum bounds rho_i, the greedy drop schedule, the search for b.
+* Sec. 5.1, Eq. (27), and Algorithm 5 (Encode, ToRns, ReconstructFP64).
+* Sec. 5.2, Eq. (28), and Algorithm 7 (OzII-RescaleBE): encode the tensor
+  once with one exponent, a residue product per modulus and mode, g_i drops
+  and one base extension after each non-final mode, one reconstruction with
+  the scale alpha * Gamma.
+
+Readings where the page leaves a step open (listed in the design doc as well):
+
+1. Working basis: the page takes the first s entries of an external library's
+   modulus table, of which it prints only the first three (256, 255, 253).
+   Here the basis is the max-product set of s pairwise-coprime moduli <= 256
+   that the DGEMM emulation uses (``oracle.max_product_moduli``), in
+   descending order, so 256 -- the only even modulus -- comes first, as
+   Algorithm 4 and ReconstructFP64 require.
+2. fl64(q_j V + d_j) in ReconstructFP64 is one rounding of the exact value
+   (a fused multiply-add), as fl64(expression) denotes.
+3. The scalar scale alpha is a double: alpha <- fl64(alpha q) at each drop,
+   in drop order.  Gamma (Eq. 28) is a power of two per entry, so
+   sigma = alpha Gamma is exact and the result is fl64(sigma V).
+4. One exponent per tensor of a batch (the encoding group of the persistent
+   method is "the complete tensor").
+5. The chain is the three-direction pass Y = X x1 A x2 B x3 C of the page's
+   Eq. (1): every mode is contracted once, so no pending operator scales are
+   folded into later operators.
+6. Non-finite input entries are outside the algorithm ("assume finite
+   operands"); a tensor with any non-finite entry maps to an all-NaN output.
+
+Tensors are flat column-major arrays X[i + n j + n^2 k]; operators are flat
+column-major n x n arrays A[i + n j] = A_ij.
+"""
+from __future__ import annotations
+
+import math
+from typing import Sequence
+
+import numpy as np
+
+from .oz2_oracle import max_product_moduli, moduli_product
+
+MAX_BITS = 53  # Algorithm 3 starts the search at the FP64 significand
+
+
+# ----------------------------------------------------------------------------
+# Residues (Sec. 2.3, Eq. 11-12)
+# ----------------------------------------------------------------------------
+def centered(v: int, p: int) -> int:
+    """[v]_p: the remainder r = v - p floor(v/p), moved to r - p when r >= ceil(p/2)."""
+    r = v % p
+    return r if r < (p + 1) // 2 else r - p
+
+
+def centered_array(v: np.ndarray, p: int) -> np.ndarray:
+    """Eq. (11) entrywise on an int64 array (|v| < 2^62)."""
+    r = np.mod(v, p)
+    return np.where(r < (p + 1) // 2, r, r - p)
+
+
+def to_rns(vbar: np.ndarray, basis: Sequence[int]) -> dict:
+    """ToRns (Algorithm 5): one centred residue plane per modulus."""
+    return {p: centered_array(vbar, p) for p in basis}
+
+
+# ----------------------------------------------------------------------------
+# Rescaling (Sec. 2.3.1, Eq. 14-15, Algorithm 1)
+# ----------------------------------------------------------------------------
+def rns_drop(R: dict, L: Sequence[int], q: int):
+    """RnsDrop: residues of v' = (v - [v]_q)/q on L without q, by Eq. (15)
+    [v']_p = [([v]_p - r_q)(q^{-1} mod p)]_p.  Returns (R', L')."""
+    S = R[q]
+    out = {}
+    for p in L:
+        if p == q:
+            continue
+        out[p] = centered_array((R[p] - S) * pow(q, -1, p), p)
+    return out, [p for p in L if p != q]
+
+
+# ----------------------------------------------------------------------------
+# Base extension (Sec. 2.3.2, Sec. 4.4 Eq. 24-26, Algorithm 4)
+# ----------------------------------------------------------------------------
+def mrc_digits(R: dict, order: Sequence[int]) -> list:
+    """MrcDigits: d_i = U_i, then U_j <- [(U_j - d_i)(q_i^{-1} mod q_j)]_{q_j}
+    for the later moduli j, in the given order (even modulus first)."""
+    U = {p: np.array(R[p], dtype=np.int64, copy=True) for p in order}
+    digits = []
+    for i, qi in enumerate(order):
+        di = U[qi]
+        digits.append(di)
+        for qj in order[i + 1:]:
+            U[qj] = centered_array((U[qj] - di) * pow(qi, -1, qj), qj)
+    return digits
+
+
+def mixed_radix_weights(order: Sequence[int]) -> list:
+    """W_i = prod_{j<i} q_j (Eq. 24), as exact integers."""
+    W, w = [], 1
+    for q in order:
+        W.append(w)
+        w *= q
+    return W
+
+
+def base_extend(R: dict, order: Sequence[int], targets: Sequence[int]) -> dict:
+    """BaseExtend: the residues of the same integer on the target moduli,
+    t <- [t + d_i omega_{i,p}]_p with omega_{i,p} = [W_i]_p (Eq. 26); the
+    digits are computed once and shared by every target."""
+    digits = mrc_digits(R, order)
+    W = mixed_radix_weights(order)
+    out = dict(R)
+    for p in targets:
+        t = np.zeros_like(digits[0])
+        for di, Wi in zip(digits, W):
+            t = centered_array(t + di * centered(Wi, p), p)
+        out[p] = t
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Encoding and reconstruction (Sec. 5.1 Eq. 27, Algorithm 5)
+# ----------------------------------------------------------------------------
+def encode_group(values: np.ndarray, b: int):
+    """Encode for one group: E with 2^(E-1) <= max|G| < 2^E, e = b - E,
+    Gbar = round(2^e G) with ties to even.  An all-zero group gives (0, 0)."""
+    v = np.asarray(values, dtype=np.float64)
+    mx = float(np.max(np.abs(v))) if v.size else 0.0
+    if mx == 0.0:
+        return np.zeros(v.shape, dtype=np.int64), 0
+    E = math.frexp(mx)[1]
+    e = b - E
+    return np.rint(np.ldexp(v, e)).astype(np.int64), e
+
+
+def encode_rows(M: np.ndarray, b: int):
+    """Encode with every row of M as one group (operator rows, Eq. 27):
+    returns (Mbar, f) with f the row exponents."""
+    rows = [encode_group(M[a, :], b) for a in range(M.shape[0])]
+    return np.stack([r[0] for r in rows]), np.array([r[1] for r in rows], dtype=np.int64)
+
+
+def horner_fp64(digits: Sequence[np.ndarray], order: Sequence[int]) -> np.ndarray:
+    """V = fl64(d_m); V <- fl64(q_j V + d_j) for j = m-1 .. 1, each step one
+    rounding of the exact value (reading 2)."""
+    m = len(order)
+    flat = [np.asarray(d).reshape(-1) for d in digits]
+    out = np.empty(flat[0].size)
+    for x in range(flat[0].size):
+        V = float(int(flat[m - 1][x]))
+        for j in range(m - 2, -1, -1):
+            V = float(order[j] * int(V) + int(flat[j][x]))
+        out[x] = V
+    return out.reshape(np.asarray(digits[0]).shape)
+
+
+def reconstruct_fp64(R: dict, order: Sequence[int], sigma) -> np.ndarray:
+    """ReconstructFP64: centred MRC digits on the ordered basis, FP64 Horner,
+    then fl64(sigma * V) entrywise."""
+    V = horner_fp64(mrc_digits(R, order), order)
+    return np.asarray(sigma, dtype=np.float64) * V
+
+
+# ----------------------------------------------------------------------------
+# Planning (Sec. 4.3 Eq. 21-23, Algorithms 2-3)
+# ----------------------------------------------------------------------------
+def row_sum_bound(Mbar: np.ndarray) -> int:
+    """rho = max_j sum_k |Mbar_jk| (Eq. 21), exact."""
+    return max(sum(abs(int(x)) for x in row) for row in Mbar)
+
+
+def drop_plan(b: int, rhos: Sequence[int], basis: Sequence[int], tau: int = 1):
+    """DropPlan: drop counts (g_1 .. g_d) or None (the page's failure)."""
+    B = 1 << b
+    L = list(basis)
+    PL = moduli_product(L)
+    d = len(rhos)
+    g = []
+    for i in range(d):
+        B = B * rhos[i]
+        if 2 * B >= PL:
+            return None
+        gi = 0
+        if i < d - 1:
+            while len(L) > 1 and B // min(L) >= (1 << b):
+                q = min(L)
+                Bq = B // q + 1
+                if 2 * Bq >= PL // q:
+                    return None
+                L.remove(q)
+                PL //= q
+                B = Bq
+                gi += 1
+            if tau == 1:
+                L = list(basis)
+                PL = moduli_product(L)
+        g.append(gi)
+    return g
+
+
+def planner(ops: Sequence[np.ndarray], basis: Sequence[int]):
+    """Planner: the largest b <= 53 whose drop plan (with restoration) passes,
+    with rho_i(b) from the operators encoded at b.  Returns (b, g) or None."""
+    for b in range(MAX_BITS, 0, -1):
+        rhos = [row_sum_bound(encode_rows(M, b)[0]) for M in ops]
+        g = drop_plan(b, rhos, basis, 1)
+        if g is not None:
+            return b, g
+    return None
+
+
+# ----------------------------------------------------------------------------
+# The chain (Sec. 5.2, Eq. 28, Algorithm 7)
+# ----------------------------------------------------------------------------
+def tensor_from_flat(x: np.ndarray, n: int) -> np.ndarray:
+    """T[i, j, k] = x[i + n j + n^2 k]"""
+    return np.asarray(x).reshape(n, n, n).transpose(2, 1, 0)
+
+
+def tensor_to_flat(T: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(T.transpose(2, 1, 0)).reshape(-1)
+
+
+def matrix_from_flat(a: np.ndarray, n: int) -> np.ndarray:
+    """M[i, j] = a[i + n j]"""
+    return np.asarray(a, dtype=np.float64).reshape(n, n).T
+
+
+def mode_product(T: np.ndarray, M: np.ndarray, mode: int) -> np.ndarray:
+    """T x_{mode+1} M: the operator's second index contracts the mode (exact int64)."""
+    if mode == 0:
+        return np.einsum("ak,kjl->ajl", M, T)
+    if mode == 1:
+        return np.einsum("ak,ikl->ial", M, T)
+    return np.einsum("ak,ijk->ija", M, T)
+
+
+def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int):
+    """Plan and prepare the operators (Algorithm 7 lines 2-9): returns a dict
+    with basis, b, g, the integer operators and their row exponents, the
+    operator residues per modulus, and the dropped moduli per mode."""
+    basis = list(max_product_moduli(s))           # descending: 256 first
+    ops = [matrix_from_flat(a, n) for a in ops_flat]
+    plan = planner(ops, basis)
+    if plan is None:
+        return None
+    b, g = plan
+    enc = [encode_rows(M, b) for M in ops]
+    drops = []
+    for gi in g:
+        L = list(basis)
+        dq = []
+        for _ in range(gi):
+            q = min(L)
+            dq.append(q)
+            L.remove(q)
+        drops.append(dq)
+    return dict(basis=basis, b=b, g=g, Abar=[e[0] for e in enc], f=[e[1] for e in enc],
+                Ares=[{p: centered_array(e[0], p) for p in basis} for e in enc], drops=drops, n=n, s=s)
+
+
+def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np.ndarray:
+    """Algorithm 7 for one tensor; returns the flat column-major result.
+    `keep`, if given, receives the residues after every stage (for tests)."""
+    n, basis, b = plan["n"], plan["basis"], plan["b"]
+    x = np.asarray(x_flat, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        return np.full(n ** 3, np.nan)
+    T = tensor_from_flat(x, n)
+    Xbar, e = encode_group(T, b)
+    alpha = math.ldexp(1.0, -e)
+    R = to_rns(Xbar, basis)
+    if keep is not None:
+        keep["encoded"] = (Xbar, e)
+        keep["stages"] = []
+    for i in range(3):
+        R = {p: centered_array(mode_product(R[p], plan["Ares"][i][p], i), p) for p in basis}
+        if keep is not None:
+            keep["stages"].append(("product", i, dict(R)))
+        if plan["g"][i] > 0:
+            L = list(basis)
+            for q in plan["drops"][i]:
+                R, L = rns_drop(R, L, q)
+                alpha = alpha * q
+            R = base_extend(R, L, [p for p in basis if p not in L])
+            if keep is not None:
+                keep["stages"].append(("extended", i, dict(R)))
+    f1, f2, f3 = plan["f"]
+    gamma_exp = -(f1[:, None, None] + f2[None, :, None] + f3[None, None, :])
+    sigma = np.ldexp(alpha, gamma_exp)
+    if keep is not None:
+        keep["alpha"] = alpha
+    return tensor_to_flat(reconstruct_fp64(R, basis, sigma))
+
+
+def rescale_be_chain(X: np.ndarray, ops_flat: Sequence[np.ndarray], n: int, s: int, batch: int):
+    """Y = X x1 A x2 B x3 C for `batch` tensors by OzII-RescaleBE; returns
+    (Y flat, plan) or (None, None) when the planner finds no b."""
+    plan = prepare_chain(ops_flat, n, s)
+    if plan is None:
+        return None, None
+    n3 = n ** 3
+    Y = np.empty(n3 * batch)
+    for t in range(batch):
+        Y[t * n3:(t + 1) * n3] = chain_tensor(X[t * n3:(t + 1) * n3], plan)
+    return Y, plan
