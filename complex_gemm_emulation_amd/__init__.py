@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-__all__ = ["Handle", "Operand", "Oz2Error", "lib", "plan_info", "moduli_for_bits",
+__all__ = ["Handle", "Operand", "ChainPlan", "Oz2Error", "lib", "plan_info", "moduli_for_bits",
            "EXPORTED_SYMBOLS", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboz2.so")
@@ -28,7 +28,8 @@ EXPORTED_SYMBOLS = (
     "oz2_get_workspace_size", "oz2_set_timing", "oz2_get_phase_times", "oz2_moduli_for_bits",
     "oz2_plan_info", "oz2_dgemm", "oz2_zgemm", "oz2_dgemm_strided_batched", "oz2_status_string",
     "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt", "oz2_operand_create",
-    "oz2_operand_update", "oz2_operand_destroy", "oz2_gemm_prepared",
+    "oz2_operand_update", "oz2_operand_destroy", "oz2_gemm_prepared", "oz2_chain_plan_create",
+    "oz2_chain_plan_info", "oz2_chain_rescale_be", "oz2_chain_plan_destroy",
 )
 
 _lib = None
@@ -72,6 +73,10 @@ def _raw():
             "oz2_operand_update": [P, P, P, I64],
             "oz2_operand_destroy": [P],
             "oz2_gemm_prepared": [P, P, P, P, P, P, I64],
+            "oz2_chain_plan_create": [P, I64, P, P, P, I, P],
+            "oz2_chain_plan_info": [P, P, P],
+            "oz2_chain_rescale_be": [P, P, P, P, I64],
+            "oz2_chain_plan_destroy": [P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -138,6 +143,37 @@ class Operand:
     def close(self) -> None:
         if self._p is not None and self._p.value:
             _raw().oz2_operand_destroy(self._p)
+            self._p = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+class ChainPlan:
+    """A planned persistent tensor-mode chain (oz2_chain_plan_create):
+    significand bits b, drop counts g and the operators' residues on the
+    device, reusable for any number of tensor batches."""
+
+    def __init__(self, ptr, n, s):
+        self._p = ptr
+        self.n, self.s = n, s
+        b = ctypes.c_int()
+        g = (ctypes.c_int * 3)()
+        _check("oz2_chain_plan_info", _raw().oz2_chain_plan_info(ptr, ctypes.byref(b), g))
+        self.b, self.g = b.value, tuple(g)
+
+    def close(self) -> None:
+        if self._p is not None and self._p.value:
+            _raw().oz2_chain_plan_destroy(self._p)
             self._p = None
 
     def __del__(self):
@@ -288,6 +324,28 @@ class Handle:
         be = (ctypes.c_double * 2)(beta.real, beta.imag)
         self._bind_stream()
         _check("oz2_gemm_prepared", _raw().oz2_gemm_prepared(self._h, pa._p, pb._p, al, be, pc, ldc))
+
+    # ------------------------------------------------- persistent chains
+    def chain_plan(self, A1, A2, A3, n, s) -> ChainPlan:
+        """Plan Y = X x1 A1 x2 A2 x3 A3 by OzII-RescaleBE
+        (oz2_chain_plan_create); A1..A3 are host n x n column-major arrays."""
+        mats = [np.ascontiguousarray(np.asarray(M, dtype=np.float64).reshape(-1)) for M in (A1, A2, A3)]
+        for M in mats:
+            if M.size < n * n:
+                raise ValueError(f"operator holds {M.size} entries, n x n needs {n * n}")
+        out = ctypes.c_void_p()
+        ptrs = [M.ctypes.data_as(ctypes.c_void_p) for M in mats]
+        _check("oz2_chain_plan_create",
+               _raw().oz2_chain_plan_create(self._h, n, ptrs[0], ptrs[1], ptrs[2], s, ctypes.byref(out)))
+        return ChainPlan(out, n, s)
+
+    def chain_rescale_be(self, plan: ChainPlan, X, Y, batch) -> None:
+        """Run a planned chain on `batch` tensors (oz2_chain_rescale_be)."""
+        need = batch * plan.n ** 3
+        px = _dev_ptr(X, "f64", need, "X") if batch > 0 else None
+        py = _dev_ptr(Y, "f64", need, "Y") if batch > 0 else None
+        self._bind_stream()
+        _check("oz2_chain_rescale_be", _raw().oz2_chain_rescale_be(self._h, plan._p, px, py, batch))
 
     def tensor_mode_chain(self, X, A, B, C, n, batch, s, Y=None, work=None):
         """Y = X x1 A x2 B x3 C for `batch` independent n x n x n tensors

@@ -66,6 +66,13 @@ struct oz2_operand {
     int8_t* planes = nullptr;  // [sets][s][kp/64][rows_pad][64]
 };
 
+// a planned persistent tensor-mode chain: the kernel's tables and the
+// operator residues on the device
+struct oz2_chain_plan {
+    ChainParams params;        // b, g, Qd and device pointers; X, Y, batch per call
+    void* mem = nullptr;       // device: ChainTables, then the operator residues
+};
+
 namespace {
 
 bool valid_op(char c) {
@@ -693,6 +700,95 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
     L.valid = true;
     h->last = L;
     return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_chain_plan_create(oz2_handle_t h, int64_t n, const double* A1, const double* A2, const double* A3,
+                          int num_moduli, oz2_chain_plan_t* out) {
+    if (!h) return -1;
+    if (n < 1 || n > kChainN) return -2;
+    if (!A1) return -3;
+    if (!A2) return -4;
+    if (!A3) return -5;
+    if (num_moduli < kMinS || num_moduli > kChainMaxS) return -6;
+    if (!out) return -7;
+    *out = nullptr;
+    oz2_chain_plan* plan = new (std::nothrow) oz2_chain_plan();
+    if (!plan) return OZ2_STATUS_ALLOC_FAILED;
+    constexpr size_t kOpsBytes = 3 * kChainMaxS * kChainN * kChainN;
+    const size_t off_ops = align_up(sizeof(ChainTables));
+    struct Host {
+        ChainTables tab;
+        int8_t ops[kOpsBytes];
+    };
+    Host* host = new (std::nothrow) Host();
+    if (!host) {
+        delete plan;
+        return OZ2_STATUS_ALLOC_FAILED;
+    }
+    const double* ops[3] = {A1, A2, A3};
+    int st = chain_plan(num_moduli, (int)n, ops, &plan->params, &host->tab, host->ops);
+    if (!st && hipMalloc(&plan->mem, off_ops + kOpsBytes) != hipSuccess) {
+        (void)hipGetLastError();
+        plan->mem = nullptr;
+        st = OZ2_STATUS_ALLOC_FAILED;
+    }
+    if (!st && (hipMemcpy(plan->mem, &host->tab, sizeof(ChainTables), hipMemcpyHostToDevice) != hipSuccess ||
+                hipMemcpy((char*)plan->mem + off_ops, host->ops, kOpsBytes, hipMemcpyHostToDevice) != hipSuccess))
+        st = OZ2_STATUS_HIP_ERROR;
+    delete host;
+    if (st) {
+        if (plan->mem) (void)hipFree(plan->mem);
+        delete plan;
+        return st;
+    }
+    plan->params.tab = (const float*)plan->mem;
+    plan->params.ops = (const int8_t*)((char*)plan->mem + off_ops);
+    *out = plan;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_chain_plan_info(oz2_chain_plan_t plan, int* b, int* g) {
+    if (!plan) return -1;
+    if (b) *b = plan->params.b;
+    if (g)
+        for (int i = 0; i < 3; ++i) g[i] = plan->params.g[i];
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X, double* Y, int64_t batch) {
+    if (!h) return -1;
+    if (!plan) return -2;
+    if (batch < 0 || batch > INT32_MAX) return -5;
+    h->timed = false;
+    if (batch == 0) return OZ2_STATUS_SUCCESS;
+    if (!X) return -3;
+    if (!Y) return -4;
+    ChainParams P = plan->params;
+    P.X = X;
+    P.Y = Y;
+    P.batch = batch;
+    hipStream_t stm = h->stream;
+    h->last.valid = false;
+    if (h->timing)
+        for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+    OZ2_LAUNCH(launch_chain(P, stm));
+    if (h->timing) {
+        OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
+        OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
+        h->timed = true;
+    }
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_chain_plan_destroy(oz2_chain_plan_t plan) {
+    if (!plan) return -1;
+    int st = OZ2_STATUS_SUCCESS;
+    if (plan->mem && hipFree(plan->mem) != hipSuccess) {
+        (void)hipGetLastError();
+        st = OZ2_STATUS_HIP_ERROR;
+    }
+    delete plan;
+    return st;
 }
 
 int oz2_set_debug(oz2_handle_t h, int debug) {

@@ -1,0 +1,189 @@
+// oz2_chain_plan.cpp -- host planning of the persistent tensor-mode chain
+// (OzII-RescaleBE).
+//
+// "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products":
+//  - Sec. 5.1 Eq. (27) and Algorithm 5: every operator row is one encoding
+//    group, f = b - E with 2^(E-1) <= max|row| < 2^E, rounded to nearest
+//    (ties to even);
+//  - Sec. 4.3 Eq. (21): rho_i = maximal absolute row sum of the integer
+//    operator;
+//  - Algorithm 2 (DropPlan) with restoration, Algorithm 3 (Planner): the
+//    largest b <= 53 whose greedy schedule passes every range check, with
+//    exact wide-integer bounds;
+//  - Sec. 2.3 Eq. (11): centred residues, [v]_p in [-floor(p/2), ceil(p/2) - 1];
+//  - Sec. 4.4 Eq. (24)-(26): mixed-radix weights omega_{i,p} = [prod_{l<i} m_l]_p.
+// The basis is the max-product modulus set of the DGEMM emulation for s,
+// descending, so 256 (its only even modulus) comes first.
+#include <cmath>
+#include <cstring>
+
+#include "oz2.h"
+#include "oz2_internal.h"
+
+namespace oz2 {
+namespace {
+
+int centered(int64_t v, int p) {
+    int64_t r = v % p;
+    if (r < 0) r += p;
+    return (int)(r < (p + 1) / 2 ? r : r - p);
+}
+
+int64_t inverse_mod(int64_t a, int64_t p) {
+    // extended Euclid; a and p coprime
+    int64_t t = 0, nt = 1, r = p, nr = ((a % p) + p) % p;
+    while (nr) {
+        const int64_t q = r / nr;
+        int64_t x = t - q * nt; t = nt; nt = x;
+        x = r - q * nr; r = nr; nr = x;
+    }
+    return t < 0 ? t + p : t;
+}
+
+UBig add(const UBig& a, const UBig& b) {
+    UBig c;
+    uint64_t carry = 0;
+    for (int i = 0; i < UBig::kWords; ++i) {
+        const uint64_t s = (uint64_t)a.w[i] + b.w[i] + carry;
+        c.w[i] = (uint32_t)s;
+        carry = s >> 32;
+    }
+    return c;
+}
+
+UBig mul_u64(const UBig& a, uint64_t m) {
+    UBig lo = a, hi = a;
+    lo.mul_small((uint32_t)m);
+    hi.mul_small((uint32_t)(m >> 32));
+    return add(lo, hi.shl(32));
+}
+
+UBig pow2(int e) { return UBig::from_u64(1).shl(e); }
+
+// Encode one operator at b (rows = groups): integer entries and row exponents
+bool encode_rows(const double* A, int n, int b, int64_t* Abar, int* f) {
+    for (int a = 0; a < n; ++a) {
+        double mx = 0.0;
+        for (int k = 0; k < n; ++k) {
+            const double x = A[a + (int64_t)n * k];
+            if (!std::isfinite(x)) return false;
+            mx = std::fmax(mx, std::fabs(x));
+        }
+        if (mx == 0.0) {
+            f[a] = 0;
+            for (int k = 0; k < n; ++k) Abar[a * n + k] = 0;
+            continue;
+        }
+        int E = 0;
+        (void)std::frexp(mx, &E);
+        f[a] = b - E;
+        for (int k = 0; k < n; ++k)
+            Abar[a * n + k] = (int64_t)std::nearbyint(std::ldexp(A[a + (int64_t)n * k], f[a]));
+    }
+    return true;
+}
+
+uint64_t row_sum_bound(const int64_t* Abar, int n) {
+    uint64_t rho = 0;
+    for (int a = 0; a < n; ++a) {
+        uint64_t r = 0;
+        for (int k = 0; k < n; ++k) r += (uint64_t)std::llabs(Abar[a * n + k]);
+        rho = r > rho ? r : rho;
+    }
+    return rho;
+}
+
+// DropPlan with restoration (tau = 1); false on a failed range check
+bool drop_plan(int b, const uint64_t rho[3], const int* basis, int s, int g[3]) {
+    UBig PL = UBig::from_u64(1);
+    for (int i = 0; i < s; ++i) PL.mul_small((uint32_t)basis[i]);
+    const UBig P = PL;
+    const UBig two_b = pow2(b);
+    UBig B = two_b;
+    int nL = s;
+    for (int i = 0; i < 3; ++i) {
+        B = mul_u64(B, rho[i]);
+        if (B.shl(1).cmp(PL) >= 0) return false;
+        g[i] = 0;
+        if (i < 2) {
+            while (nL > 1) {
+                const uint32_t q = (uint32_t)basis[nL - 1];  // smallest available modulus
+                const UBig Bq0 = B.div_small(q);
+                if (Bq0.cmp(two_b) < 0) break;
+                const UBig Bq = add(Bq0, UBig::from_u64(1));
+                const UBig PLq = PL.div_small(q);
+                if (Bq.shl(1).cmp(PLq) >= 0) return false;
+                PL = PLq;
+                B = Bq;
+                --nL;
+                ++g[i];
+            }
+            PL = P;
+            nL = s;
+        }
+    }
+    return true;
+}
+
+}  // namespace
+
+int chain_plan(int s, int n, const double* const ops[3], ChainParams* P, ChainTables* T, int8_t* ops_residues) {
+    const ModuliPlan* pl = moduli_plan(s);
+    if (!pl || s > kChainMaxS || n < 1 || n > kChainN) return OZ2_STATUS_INTERNAL;
+    if (pl->mod[0] != 256) return OZ2_STATUS_INTERNAL;
+    for (int i = 1; i < s; ++i)
+        if (pl->mod[i] % 2 == 0) return OZ2_STATUS_INTERNAL;
+    int64_t Abar[3][kChainN * kChainN];
+    int f[3][kChainN];
+    int b = 53, g[3] = {0, 0, 0};
+    for (; b >= 1; --b) {
+        uint64_t rho[3];
+        for (int i = 0; i < 3; ++i) {
+            if (!encode_rows(ops[i], n, b, Abar[i], f[i])) return -(3 + i);
+            rho[i] = row_sum_bound(Abar[i], n);
+        }
+        if (drop_plan(b, rho, pl->mod, s, g)) break;
+    }
+    if (b < 1) return OZ2_STATUS_RANGE;
+    P->n = n;
+    P->s = s;
+    P->b = b;
+    for (int i = 0; i < 3; ++i) P->g[i] = g[i];
+    // alpha multiplier: the dropped moduli (the g smallest, smallest first)
+    // in drop order, each product rounded to double
+    double Qd = 1.0;
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < g[i]; ++j) Qd = Qd * (double)pl->mod[s - 1 - j];
+    P->Qd = Qd;
+    std::memset(ops_residues, 0, 3 * kChainMaxS * kChainN * kChainN);
+    for (int i = 0; i < 3; ++i) {
+        for (int a = 0; a < kChainN; ++a) T->fexp[i][a] = a < n ? f[i][a] : 0;
+        for (int q = 0; q < s; ++q)
+            for (int a = 0; a < n; ++a)
+                for (int k = 0; k < n; ++k)
+                    ops_residues[((i * kChainMaxS + q) * kChainN + a) * kChainN + k] =
+                        (int8_t)centered(Abar[i][a * n + k], pl->mod[q]);
+    }
+    // kernel tables in slot order: the s moduli right-aligned in kChainMaxS
+    // slots (descending), the unused leading slots with the modulus 1
+    const int first = kChainMaxS - s;
+    int slot[kChainMaxS];
+    for (int u = 0; u < kChainMaxS; ++u) slot[u] = u < first ? 1 : pl->mod[u - first];
+    for (int u = 0; u < kChainMaxS; ++u) {
+        T->mod[u] = (float)slot[u];
+        T->rmod[u] = 1.0f / (float)slot[u];
+    }
+    for (int i = 0; i < kChainMaxS; ++i)
+        for (int j = 0; j < kChainMaxS; ++j)
+            T->inv[i][j] = i != j ? (float)inverse_mod(slot[i], slot[j]) : 0.0f;
+    for (int j = 0; j < kChainMaxS; ++j) {
+        int64_t w = 1;  // prod_{l<i} slot[l] reduced mod slot[j]
+        for (int i = 0; i < kChainMaxS; ++i) {
+            T->omega[i][j] = (float)centered(w, slot[j]);
+            w = (w * slot[i]) % slot[j];
+        }
+    }
+    return OZ2_STATUS_SUCCESS;
+}
+
+}  // namespace oz2

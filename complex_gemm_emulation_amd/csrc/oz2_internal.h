@@ -105,6 +105,39 @@ struct SmallParams {
     uint32_t M16[kMaxLimb16];
 };
 
+// Persistent tensor-mode chain, OzII-RescaleBE ("You Only Convert Twice:
+// Ozaki Scheme II for Chained Tensor Mode Products", Sec. 5.2 and
+// Algorithm 7): Y = X x1 A1 x2 A2 x3 A3 for a batch of n x n x n tensors,
+// one block per tensor, residues in LDS for the whole chain (oz2_chain.hip).
+constexpr int kChainN = 16;      // tensor side of the kernel's tiles (n <= 16 is zero padded)
+constexpr int kChainMaxS = 16;   // moduli: two LDS buffers of 16 residue planes (128 KiB)
+struct ChainParams {
+    const double* X;             // [batch][n^3] column-major tensors
+    double* Y;
+    int64_t batch;
+    int n, s, b;
+    int g[3];                    // moduli dropped after mode i (g[2] = 0)
+    double Qd;                   // fl64 product of the dropped moduli, in drop order
+    const int8_t* ops;           // device [3][kChainMaxS][16][16] centred residues of the integer operators
+    const float* tab;            // device ChainTables (below)
+};
+
+// Constant tables of the chain kernel, in slot order (the s moduli
+// right-aligned in kChainMaxS slots, descending; unused slots hold 1)
+struct ChainTables {
+    float inv[kChainMaxS][kChainMaxS];    // m_i^{-1} mod m_j (i != j), in [0, m_j)
+    float omega[kChainMaxS][kChainMaxS];  // [prod_{l<i} m_l]_{m_j}, centred
+    float mod[kChainMaxS];                // m_u
+    float rmod[kChainMaxS];               // fl32(1 / m_u)
+    int fexp[3][kChainN];                 // operator row exponents f_{i,a} (0 for padding rows)
+};
+
+// Host planning of the chain (Algorithms 2, 3 and 5 of the chain page):
+// the significand bits b, the drop counts g, and the integer operators'
+// row exponents and centred residues.  ops: three HOST n x n column-major
+// operators.  Returns 0, or OZ2_STATUS_RANGE when no b in [1, 53] passes.
+int chain_plan(int s, int n, const double* const ops[3], ChainParams* P, ChainTables* T, int8_t* ops_residues);
+
 struct CrtTestParams {
     const uint8_t* R;  // [s][count]
     int64_t count;
@@ -127,5 +160,6 @@ hipError_t launch_scale_c(double* C, int64_t m, int64_t n, int64_t ldc, const do
                           bool cplx, hipStream_t st);
 hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st);
 hipError_t launch_small_gemm(SmallParams P, int NL, bool beta_nonzero, hipStream_t st);
+hipError_t launch_chain(const ChainParams& P, hipStream_t st);
 
 }  // namespace oz2

@@ -1,0 +1,148 @@
+"""GPU parity of the persistent tensor-mode chain (oz2_chain_plan_create /
+oz2_chain_rescale_be, OzII-RescaleBE of "You Only Convert Twice: Ozaki
+Scheme II for Chained Tensor Mode Products", Algorithm 7) against the CPU
+oracle (oracle/rescale_be.py), through the C ABI.
+
+Bar: the plan (b, g) equals the oracle planner's, and every output entry is
+bit-identical to the oracle's: every step is exact integer arithmetic except
+the FP64 Horner evaluation and the final scaling, which both sides perform in
+the same order with the same roundings.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+rb = oracle.rescale_be
+
+
+@pytest.fixture(scope="module")
+def handle():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import complex_gemm_emulation_amd as oz2
+    h = oz2.Handle()
+    yield h
+    h.close()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _ops(n, seed, dist="uniform", phi=0.5):
+    return [workloads.real_matrix(n, n, seed + q, dist, phi) for q in range(3)]
+
+
+def _check_bitwise(got, want, label):
+    g = np.ascontiguousarray(got).view(np.int64)
+    w = np.ascontiguousarray(want).view(np.int64)
+    nan = np.isnan(got) & np.isnan(want)
+    bad = np.nonzero((g != w) & ~nan)[0]
+    assert bad.size == 0, (f"{label}: {bad.size} entries differ, first {bad[:4]}: "
+                           f"got {got[bad[:4]]} want {want[bad[:4]]}")
+
+
+CASES = [
+    # n, s, batch, tensor distribution
+    (16, 16, 3, "uniform"),
+    (16, 12, 2, "phi"),
+    (8, 16, 4, "uniform"),
+    (5, 10, 3, "uniform"),   # ragged: padded to 16 inside the kernel
+    (12, 8, 2, "phi"),
+    (1, 6, 5, "uniform"),
+]
+
+
+@pytest.mark.parametrize("n,s,batch,dist", CASES, ids=[f"n{c[0]}s{c[1]}b{c[2]}{c[3]}" for c in CASES])
+def test_chain_matches_oracle_bitwise(handle, n, s, batch, dist):
+    import torch
+    _say(f"[chain] n={n} s={s} batch={batch} {dist}")
+    ops = _ops(n, 8000 + 10 * n + s)
+    if dist == "uniform":
+        X = workloads.tensor_batch(n, batch, 8100 + n + s)
+    else:
+        X = workloads.real_matrix(n ** 3, batch, 8200 + n + s, "phi", 2.0)
+    want, plan = rb.rescale_be_chain(X, ops, n, s, batch)
+    assert plan is not None
+    with handle.chain_plan(ops[0], ops[1], ops[2], n, s) as cp:
+        assert (cp.b, list(cp.g)) == (plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
+        dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
+        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
+        torch.cuda.synchronize()
+    _check_bitwise(from_dev(dY), want, f"n={n} s={s}")
+
+
+def test_chain_edge_tensors(handle):
+    """zero tensor, a non-finite entry, a subnormal-scale tensor, a huge-range
+    tensor and an ordinary one in one batch"""
+    import torch
+    n, s = 16, 16
+    ops = _ops(n, 8300, "phi", 1.0)
+    n3 = n ** 3
+    X = workloads.tensor_batch(n, 5, 8301)
+    X[:n3] = 0.0
+    X[n3 + 77] = np.nan
+    X[2 * n3:3 * n3] *= 2.0 ** -1060          # subnormal entries
+    X[3 * n3:4 * n3] = workloads.real_matrix(n3, 1, 8302, "phi", 6.0)
+    want, plan = rb.rescale_be_chain(X, ops, n, s, 5)
+    with handle.chain_plan(ops[0], ops[1], ops[2], n, s) as cp:
+        dY = torch.empty(n3 * 5, dtype=torch.float64, device="cuda")
+        handle.chain_rescale_be(cp, to_dev(X), dY, 5)
+        torch.cuda.synchronize()
+    got = from_dev(dY)
+    assert np.all(got[:n3] == 0.0)
+    assert np.all(np.isnan(got[n3:2 * n3]))
+    _check_bitwise(got, want, "edge tensors")
+
+
+def test_chain_full_workload_sampled(handle):
+    """The 32768-tensor batch of 16^3 tensors at s = 16 in the launch bench.py
+    times; the first, last and six seeded tensors against the oracle."""
+    import torch
+    w = workloads.WORKLOADS[5]
+    n, batch, s = w["n"], w["batch"], w["s"][0]
+    n3 = n ** 3
+    X = workloads.tensor_batch(n, batch, workloads.seed(5, 0))
+    ops = [workloads.real_matrix(n, n, workloads.seed(5, q)) for q in (1, 2, 3)]
+    plan = rb.prepare_chain(ops, n, s)
+    with handle.chain_plan(ops[0], ops[1], ops[2], n, s) as cp:
+        dY = torch.empty(n3 * batch, dtype=torch.float64, device="cuda")
+        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
+        torch.cuda.synchronize()
+    rng = np.random.default_rng(8400)
+    picks = sorted({0, batch - 1, *rng.choice(batch, 6, replace=False).tolist()})
+    Y = from_dev(dY)
+    for t in picks:
+        _say(f"[chain full] tensor {t}")
+        want = rb.chain_tensor(X[t * n3:(t + 1) * n3], plan)
+        _check_bitwise(Y[t * n3:(t + 1) * n3], want, f"tensor {t}")
+
+
+def test_chain_argument_errors(handle):
+    import ctypes
+    import complex_gemm_emulation_amd as oz2
+    lib = oz2.lib()
+    A = np.eye(4)
+    p = A.ctypes.data_as(ctypes.c_void_p)
+    out = ctypes.c_void_p()
+    assert lib.oz2_chain_plan_create(handle._h, 0, p, p, p, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 17, p, p, p, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 4, None, p, p, 8, ctypes.byref(out)) == -3
+    assert lib.oz2_chain_plan_create(handle._h, 4, p, p, p, 17, ctypes.byref(out)) == -6
+    bad = np.eye(4)
+    bad[1, 2] = np.inf
+    assert lib.oz2_chain_plan_create(handle._h, 4, p, bad.ctypes.data_as(ctypes.c_void_p), p, 8,
+                                     ctypes.byref(out)) == -4
+    assert not out.value
+    with handle.chain_plan(A, A, A, 4, 8) as cp:
+        assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, 0) == 0   # empty batch
+        assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, 1) == -3
+        assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, -1) == -5
