@@ -18,6 +18,9 @@ Other workloads (--workload), each printing the same kind of JSON line:
   reuse8192  the headline product with op(A) prepared once and reused; each
              call re-encodes B (oz2_operand_update) and runs
              oz2_gemm_prepared (phase times: GEMM and reconstruct only)
+  chain_rbe  the same chain by OzII-RescaleBE ("You Only Convert Twice",
+             Algorithm 7): one kernel per chain, residues persist across the
+             modes (rescaling + base extension), reconstruction once
   nonsquare  the eight m x k x n shapes of the Arc page's Table 10 (k from
              256 to 65536, m or n from 1024 to 65536), N/N, U(-1,1) entries,
              s = 8 and 16; one step = the 16 calls, all inputs resident
@@ -47,6 +50,10 @@ if ROOT not in sys.path:
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense INT8 MFMA, TOP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+# MI355X vector ALU in 32-bit lane operations per second: the published
+# fp32 vector rate, 157.3 TFLOP/s, counts an FMA as two flops, so one
+# operation of any kind per lane is 78.6 T/s (256 CUs x 128 lanes x 2.4 GHz)
+PEAK_VALU_TOPS = 157.3 / 2
 GEMM_SOURCE = os.path.join(ROOT, "complex_gemm_emulation_amd", "csrc", "oz2_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "residue_gemm_traffic.json")
 COPY_CAL_BYTES = 1 << 30     # bytes read (and written) by the calibration copy
@@ -369,6 +376,97 @@ def run_nonsquare(args):
     }
 
 
+def rbe_valu_ops_per_entry(s, g):
+    """Vector-ALU operations per tensor entry that the modular steps of an
+    OzII-RescaleBE chain take, counting one per 32-bit lane operation and two
+    per fp64 one: a centred reduction [x]_m is 3 (fma, floor, fma), a
+    mixed-radix or drop step [(x - y) c]_m is 5.  Per mode, the s products of
+    an entry are reduced; after modes 1 and 2, with k = s - g kept moduli,
+    RnsDrop takes sum_j (s - 1 - j) steps, the digits k (k - 1) / 2 steps and
+    BaseExtend g sums of k products plus a reduction; ReconstructFP64 takes
+    s (s - 1) / 2 digit steps, s - 1 fp64 Horner FMAs and one scaling.  The
+    encode and the integer MFMA products are not counted."""
+    ops = 3 * 3 * s
+    for gi in list(g)[:2]:
+        k = s - gi
+        ops += 5 * sum(s - 1 - j for j in range(gi)) + 5 * k * (k - 1) // 2 + gi * (k + 3)
+    ops += 5 * s * (s - 1) // 2 + 2 * (s - 1) + 2
+    return ops
+
+
+def run_chain_rbe(args):
+    """The 32768 x 16^3 chain by OzII-RescaleBE: one kernel per chain, the
+    tensor in residue form from encode to reconstruction."""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+
+    w = workloads.WORKLOADS[5]
+    n, batch, s = w["n"], w["batch"], w["s"][0]
+    n3 = n ** 3
+    log(f"[bench] chain_rbe: generating {batch} tensors of {n}^3 (seeded)")
+    X = workloads.tensor_batch(n, batch, workloads.seed(5, 0))
+    ops = [workloads.real_matrix(n, n, workloads.seed(5, q)) for q in (1, 2, 3)]
+    dX = torch.from_numpy(X).cuda()
+    dY = torch.empty_like(dX)
+    h = oz2.Handle(torch.cuda.current_stream())
+    h.set_timing(True)
+    plan = h.chain_plan(ops[0], ops[1], ops[2], n, s)
+    launch_ms = []
+
+    def step(record):
+        h.chain_rescale_be(plan, dX, dY, batch)
+        if record is not None:
+            launch_ms.append(h.phase_times()[2])
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(launch_ms)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    value = n3 * batch / (dt / args.steps) / 1e9
+    lm = float(np.mean(launch_ms))
+    ops_per_launch = float(rbe_valu_ops_per_entry(s, plan.g)) * n3 * batch
+    achieved = ops_per_launch / (lm * 1e-3) / 1e12
+    bytes_per_launch = 16.0 * n3 * batch  # each input entry read and each output entry written once
+    roofline = dict(kernel="chain_kernel (OzII-RescaleBE, whole chain)", bound="alu",
+                    achieved=round(achieved, 2), peak=round(PEAK_VALU_TOPS, 2), unit="TOP/s",
+                    frac=round(achieved / PEAK_VALU_TOPS, 4), traffic=None,
+                    ops_per_launch=ops_per_launch, launch_ms=round(lm, 4),
+                    hbm_GBs=round(bytes_per_launch / (lm * 1e-3) / 1e9, 1))
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nt = args.chain_rbe_cpu_tensors
+        log(f"[bench] oracle cpu baseline on {nt} tensors")
+        t0 = time.perf_counter()
+        rplan = oracle.rescale_be.prepare_chain(ops, n, s)
+        for t in range(nt):
+            oracle.rescale_be.chain_tensor(X[t * n3:(t + 1) * n3], rplan)
+        cdt = time.perf_counter() - t0
+        cpu = dict(value=n3 * nt / cdt / 1e9, unit="GDoF/s", cores=1, kind="oracle",
+                   sample=f"first {nt} of the {batch} tensors, whole chain, {cdt:.1f} s")
+    info = dict(b=plan.b, g=list(plan.g))
+    plan.close()
+    h.close()
+    return {
+        "metric": "tensor-mode chain GDoF/s (Y = X x1 A x2 B x3 C, OzII-RescaleBE persistent residues)",
+        "value": round(value, 3),
+        "unit": "GDoF/s",
+        "ms_per_step": round(dt / args.steps * 1e3, 3),
+        "dtype": "i8",
+        "config": {"workload": f"tensor_chain_rescale_be_n{n}_b{batch}_s{s}", "n": n, "batch": batch, "s": s,
+                   "plan": info},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+
+
 def oracle_chain(X, Aop, Bop, Cop, n, nt, s):
     """The three emulated modes of nt tensors with the oracle, as the library
     decomposes them (mode 1 over all nt tensors at once)."""
@@ -462,11 +560,13 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
-                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "nonsquare", "reuse8192"])
+                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "nonsquare",
+                             "reuse8192"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)
     ap.add_argument("--chain-cpu-tensors", type=int, default=256)
+    ap.add_argument("--chain-rbe-cpu-tensors", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -481,6 +581,8 @@ def main():
         copy_calibration(torch)
     if args.workload == "chain":
         out = run_chain(args)
+    elif args.workload == "chain_rbe":
+        out = run_chain_rbe(args)
     elif args.workload == "nonsquare":
         out = run_nonsquare(args)
     else:

@@ -13,9 +13,12 @@
 //  - Sec. 2.3 Eq. (11): centred residues, [v]_m in [-floor(m/2), ceil(m/2) - 1].
 //
 // Design (CDNA4): one block of 8 wavefronts per tensor.  The tensor's residue
-// planes (up to 16 moduli x 16^3 bytes) stay in LDS for the whole chain, in
-// two buffers that alternate between modes, so HBM sees each input entry
-// read once and each output entry written once.  A mode product is, per
+// planes (up to 16 moduli x 16^3 bytes) stay in LDS for the whole chain, so
+// HBM sees each input entry read once and each output entry written once.
+// A mode is done in place in one 64 KB buffer: every wavefront first reduces
+// and packs its products into registers, then a barrier, then the rescaled
+// planes overwrite the old ones; at about 78 KB of LDS a block, two tensors
+// share a compute unit (4 wavefronts per SIMD).  A mode product is, per
 // modulus, Y^T = R^T Abar^T on v_mfma_i32_16x16x32_i8: the 256 rows of R^T
 // (the fibres along the contracted index) form 16 tiles of 16 rows, two per
 // wavefront; k = 16 fills half of the MFMA's 32.  Each lane then holds four
@@ -57,15 +60,121 @@ __device__ __forceinline__ float dmod_odd(double v, double m, double rm) {
     return (float)r;
 }
 
-// the signed byte of entry `ent` in a word of four packed residues, as a float
-__device__ __forceinline__ float unpack(uint32_t w, int ent) {
-    return (float)(int)(int8_t)(w >> (8 * ent));
+// the signed byte `e` of a word of four packed residues, as a float
+__device__ __forceinline__ float unpack(uint32_t w, int e) {
+    return (float)(int)(int8_t)(w >> (8 * e));
 }
 
+// four centred residues (exact integers held as floats) as one word
+__device__ __forceinline__ uint32_t pack4(float r0, float r1, float r2, float r3) {
+    return ((uint32_t)(int)r0 & 0xffu) | (((uint32_t)(int)r1 & 0xffu) << 8) |
+           (((uint32_t)(int)r2 & 0xffu) << 16) | (((uint32_t)(int)r3 & 0xffu) << 24);
+}
 
-__global__ __launch_bounds__(512, 1) void chain_kernel(ChainParams P) {
-    __shared__ __attribute__((aligned(16))) int8_t buf0[kSlots * kPlane];
-    __shared__ __attribute__((aligned(16))) int8_t buf1[kSlots * kPlane];
+// After a non-final mode, for the four entries of a lane: RnsDrop g times
+// (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), store
+// the kept slots, MrcDigits on them and BaseExtend to the dropped slots
+// (Algorithm 4, Eq. 26), storing those too.  Every slot loop is unrolled;
+// with G >= 0 the drop count is a compile-time constant and the guards
+// fold away, with G < 0 it is g_rt and the guards are uniform branches.
+// Unused leading slots (modulus 1) hold zeros after every step; they are
+// stored like the others, and their zero operators make them inert.
+// at: this lane's word of slot 0 in the plane buffer.
+template <int G>
+__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, int8_t* at) {
+    const int g = G >= 0 ? G : g_rt;
+    const int keep = kSlots - 1 - g;  // last slot of the reduced basis
+#pragma unroll
+    for (int qs = kSlots - 1; qs > 0; --qs)
+        if (qs > keep) {
+#pragma unroll
+            for (int p = 0; p < qs; ++p) {
+                const float iv = T->inv[qs][p], m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
+            }
+        }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u)
+        if (u <= keep) *(uint32_t*)(at + u * kPlane) = pack4(r[0][u], r[1][u], r[2][u], r[3][u]);
+    // mixed-radix digits of the kept residues, in place
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+#pragma unroll
+        for (int j = i + 1; j < kSlots; ++j)
+            if (j <= keep) {
+                const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e][j] = cmod((r[e][j] - r[e][i]) * iv, m, rm);
+            }
+#pragma unroll
+    for (int p = 1; p < kSlots; ++p)
+        if (p > keep) {
+            float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < kSlots - 1; ++i)
+                if (i <= keep) {
+                    const float w = T->omega[i][p];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
+                }
+            const float m = T->mod[p], rm = T->rmod[p];
+            *(uint32_t*)(at + p * kPlane) = pack4(cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm),
+                                                  cmod(ts[3], m, rm));
+        }
+}
+
+// residue products of one 16-fibre tile for every slot, reduced modulo the
+// slot's modulus and packed: pk[u] holds the four entries of this lane
+__device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*opm)[kChainN * kChainN],
+                                              const ChainTables* T, int t, int a, int kq,
+                                              uint32_t (&pk)[kSlots]) {
+#pragma unroll
+    for (int u0 = 0; u0 < kSlots; u0 += 4) {
+        v4i acc[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            // lanes with kq >= 2 hold k >= 16: zero operands (the loads stay
+            // in bounds and unconditional); unused slots have zero operators
+            const int u = u0 + v;
+            const long a8 = *(const long*)(buf + u * kPlane + (16 * t + a) * kChainN + 8 * (kq & 1));
+            const long b8 = *(const long*)(&opm[u][a * kChainN + 8 * (kq & 1)]);
+            acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a8 : 0l, kq < 2 ? b8 : 0l, v4i{0, 0, 0, 0}, 0, 0,
+                                                           0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int u = u0 + v;
+            const float m = T->mod[u], rm = T->rmod[u];
+            pk[u] = pack4(cmod((float)acc[v][0], m, rm), cmod((float)acc[v][1], m, rm),
+                          cmod((float)acc[v][2], m, rm), cmod((float)acc[v][3], m, rm));
+        }
+    }
+}
+
+// unpack the four entries of every slot of one tile and rescale them
+template <int G0, int G1>
+__device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint32_t (&pk)[kSlots],
+                                             const ChainTables* T, int8_t* at) {
+    float r[4][kSlots];
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q][u] = unpack(pk[u], q);
+    if (G0 >= 0 && G0 == G1)
+        rescale_extend<G0>(0, r, T, at);
+    else if (mode == 0)
+        rescale_extend<G0>(g[0], r, T, at);
+    else
+        rescale_extend<G1>(g[1], r, T, at);
+}
+
+// G0, G1: the drop counts after modes 1 and 2 when fixed at compile time,
+// -1 to read them from P.g
+template <int G0, int G1>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 4)))
+void chain_kernel(ChainParams P) {
+    __shared__ __attribute__((aligned(16))) int8_t buf[kSlots * kPlane];
     __shared__ __attribute__((aligned(16))) int8_t ops[3][kSlots][kChainN * kChainN];
     __shared__ ChainTables KT;
     __shared__ unsigned long long smax;
@@ -78,9 +187,8 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(ChainParams P) {
     const int first = kSlots - P.s;  // first active slot
     const double* X = P.X + (int64_t)blockIdx.x * n3;
     double* Y = P.Y + (int64_t)blockIdx.x * n3;
-    // stage the constant tables and the operator residues (slot order) in LDS
-    // (read per use: as kernel-argument or scalar loads the compiler would
-    // hoist all of them out of the loops and spill registers)
+    // constant tables and operator residues (slot order) staged in LDS and
+    // read per use (hoisted into registers they would not fit)
     static_assert(sizeof(ChainTables) % 4 == 0, "words");
     for (int x = tid; x < (int)(sizeof(ChainTables) / 4); x += 512)
         ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
@@ -139,129 +247,71 @@ __global__ __launch_bounds__(512, 1) void chain_kernel(ChainParams P) {
             for (int j = 0; j < 8; ++j)
                 w[j >> 2] |= ((uint32_t)(int)dmod_odd(xb[j], m, rm) & 0xffu) << (8 * (j & 3));
         }
-        *(uint2*)(buf0 + u * kPlane + idx0) = make_uint2(w[0], w[1]);
+        *(uint2*)(buf + u * kPlane + idx0) = make_uint2(w[0], w[1]);
     }
     __syncthreads();
 
-    // ----------------------------------------------------------- mode loop
+    // ------------------------------------------------- modes 1 and 2, in place
     const int a = lane & 15;   // MFMA row of A / column of B and of the output
     const int kq = lane >> 4;  // k group of the operands (0, 1 hold k < 16), output row group
-    const int8_t* src = buf0;
-    int8_t* dst = buf1;
 #pragma unroll 1
-    for (int mode = 0; mode < 3; ++mode) {
-        const int g = P.g[mode];
-        const int keep = kSlots - 1 - g;  // last slot of the reduced basis
+    for (int mode = 0; mode < 2; ++mode) {
+        asm volatile("" ::: "memory");  // keep the table reads inside the loop
+        uint32_t pk0[kSlots], pk1[kSlots];
+        tile_products(buf, ops[mode], T, wave, a, kq, pk0);
+        tile_products(buf, ops[mode], T, wave + 8, a, kq, pk1);
+        __syncthreads();  // every plane read before any is overwritten
+        // next layout: fibre (t + 16 a), index 4 kq .. 4 kq + 3
+        rescale_tile<G0, G1>(mode, P.g, pk0, T, buf + (wave + 16 * a) * kChainN + 4 * kq);
+        asm volatile("" ::: "memory");  // one tile at a time
+        rescale_tile<G0, G1>(mode, P.g, pk1, T, buf + (wave + 8 + 16 * a) * kChainN + 4 * kq);
+        __syncthreads();
+    }
+
+    // ---------------------------------------- mode 3 and ReconstructFP64
+    // (Algorithm 5): entries (a1, a2, a3) = (4 kq + q, t, a); sigma = alpha Gamma
+    const double alpha = ldexp(P.Qd, -e);
 #pragma unroll 1
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = wave + 8 * tt;  // tile: fibres 16 t .. 16 t + 15
-            // residue products, reduced and packed: pk[u] = four entries' bytes
-            uint32_t pk[kSlots];
-            {
-                v4i acc[kSlots];
+    for (int tt = 0; tt < 2; ++tt) {
+        asm volatile("" ::: "memory");
+        const int t = wave + 8 * tt;
+        uint32_t pk[kSlots];
+        tile_products(buf, ops[2], T, t, a, kq, pk);
+        float d[4][kSlots];
 #pragma unroll
-                for (int u = 0; u < kSlots; ++u) {
-                    acc[u] = v4i{0, 0, 0, 0};
-                    if (u < first) continue;
-                    long af = 0, bf = 0;
-                    if (kq < 2) {
-                        af = *(const long*)(src + u * kPlane + (16 * t + a) * kChainN + 8 * kq);
-                        bf = *(const long*)(&ops[mode][u][a * kChainN + 8 * kq]);
-                    }
-                    acc[u] = __builtin_amdgcn_mfma_i32_16x16x32_i8(af, bf, acc[u], 0, 0, 0);
-                }
+        for (int u = 0; u < kSlots; ++u)
 #pragma unroll
-                for (int u = 0; u < kSlots; ++u) {
-                    const float m = T->mod[u], rm = T->rmod[u];
-                    uint32_t w = 0u;
+            for (int q = 0; q < 4; ++q) d[q][u] = unpack(pk[u], q);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        w |= ((uint32_t)(int)cmod((float)acc[u][q], m, rm) & 0xffu) << (8 * q);
-                    pk[u] = w;
-                }
+        for (int i = 0; i < kSlots - 1; ++i)
+#pragma unroll
+            for (int j = i + 1; j < kSlots; ++j) {
+                const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) d[q][j] = cmod((d[q][j] - d[q][i]) * iv, m, rm);
             }
-            if (mode < 2) {
-                uint32_t out[kSlots];
+        double V[4];
 #pragma unroll
-                for (int u = 0; u < kSlots; ++u) out[u] = 0u;
-#pragma unroll 1
-                for (int ent = 0; ent < 4; ++ent) {
-                    asm volatile("" ::: "memory");  // keep the constant reads inside the loop
-                    float r[kSlots];
+        for (int q = 0; q < 4; ++q) V[q] = (double)d[q][kSlots - 1];
 #pragma unroll
-                    for (int u = 0; u < kSlots; ++u) r[u] = unpack(pk[u], ent);
-                    if (g > 0) {
-                        // RnsDrop (Algorithm 1): slot 15 - j is the smallest
-                        // modulus left; the outer loops run with uniform
-                        // indices, the slot loops unrolled
-#pragma unroll 1
-                        for (int qs = kSlots - 1; qs > keep; --qs) {
-                            const float S = r[qs];
+        for (int j = kSlots - 2; j >= 0; --j) {
+            const double m = (double)T->mod[j];
 #pragma unroll
-                            for (int p = 0; p < kSlots - 1; ++p)
-                                if (p < qs) r[p] = cmod((r[p] - S) * T->inv[qs][p], T->mod[p], T->rmod[p]);
-                        }
-                        // MrcDigits (Algorithm 4) on slots 0 .. keep, in a copy
-                        float d[kSlots];
+            for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)d[q][j]);
+        }
+        // the values are complete here (the compiler would otherwise sink
+        // each entry's whole digit computation into its guarded store)
 #pragma unroll
-                        for (int u = 0; u < kSlots; ++u) d[u] = r[u];
-#pragma unroll 1
-                        for (int i = 0; i < keep; ++i) {
-                            const float di = d[i];
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(V[q]));
+        if (t < n && a < n) {
+            const int f23 = T->fexp[1][t] + T->fexp[2][a];
+            double* y = Y + (int64_t)n * (t + (int64_t)n * a);
 #pragma unroll
-                            for (int j = 1; j < kSlots; ++j)
-                                if (j > i && j <= keep) d[j] = cmod((d[j] - di) * T->inv[i][j], T->mod[j], T->rmod[j]);
-                        }
-                        // BaseExtend: the dropped slots from the shared digits
-#pragma unroll 1
-                        for (int p = keep + 1; p < kSlots; ++p) {
-                            float tsum = 0.0f;
-#pragma unroll
-                            for (int i = 0; i < kSlots - 1; ++i)
-                                if (i <= keep) tsum = fmaf(d[i], T->omega[i][p], tsum);
-                            r[p] = cmod(tsum, T->mod[p], T->rmod[p]);
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < kSlots; ++u)
-                        out[u] = (out[u] >> 8) | (((uint32_t)(int)r[u] & 0xffu) << 24);
-                }
-                // next layout: fibre (t + 16 a), index 4 kq .. 4 kq + 3
-#pragma unroll
-                for (int u = 0; u < kSlots; ++u)
-                    if (u >= first) *(uint32_t*)(dst + u * kPlane + (t + 16 * a) * kChainN + 4 * kq) = out[u];
-            } else {
-                // ReconstructFP64 (Algorithm 5): entries (a1, a2, a3) =
-                // (4 kq + ent, t, a); sigma = alpha Gamma
-                const double alpha = ldexp(P.Qd, -e);
-#pragma unroll 1
-                for (int ent = 0; ent < 4; ++ent) {
-                    asm volatile("" ::: "memory");
-                    float d[kSlots];
-#pragma unroll
-                    for (int u = 0; u < kSlots; ++u) d[u] = unpack(pk[u], ent);
-#pragma unroll 1
-                    for (int i = 0; i < kSlots - 1; ++i) {
-                        const float di = d[i];
-#pragma unroll
-                        for (int j = 1; j < kSlots; ++j)
-                            if (j > i) d[j] = cmod((d[j] - di) * T->inv[i][j], T->mod[j], T->rmod[j]);
-                    }
-                    double V = (double)d[kSlots - 1];
-#pragma unroll
-                    for (int j = kSlots - 2; j >= 0; --j) V = fma((double)T->mod[j], V, (double)d[j]);
-                    const int a1 = 4 * kq + ent, a2 = t, a3 = a;
-                    if (a1 < n && a2 < n && a3 < n) {
-                        const double sigma = ldexp(alpha, -(T->fexp[0][a1] + T->fexp[1][a2] + T->fexp[2][a3]));
-                        Y[a1 + (int64_t)n * (a2 + (int64_t)n * a3)] = sigma * V;
-                    }
-                }
+            for (int q = 0; q < 4; ++q) {
+                const int a1 = 4 * kq + q;
+                if (a1 < n) y[a1] = ldexp(alpha, -(T->fexp[0][a1] + f23)) * V[q];
             }
         }
-        __syncthreads();
-        const int8_t* nsrc = dst;
-        dst = (int8_t*)src;
-        src = nsrc;
     }
 }
 
@@ -271,7 +321,19 @@ hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
     if (P.n < 1 || P.n > kChainN || P.s < kMinS || P.s > kChainMaxS || P.batch < 1 || P.batch > INT32_MAX)
         return hipErrorInvalidValue;
     if (P.g[2] != 0 || P.g[0] < 0 || P.g[1] < 0 || P.g[0] >= P.s || P.g[1] >= P.s) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(chain_kernel, dim3((unsigned)P.batch), dim3(512), 0, st, P);
+    const dim3 grid((unsigned)P.batch), block(512);
+    // compile-time drop counts for the plans of 16^3 tensors with 16, 14,
+    // 12, 10 and 8 moduli; any other plan takes the guarded instance
+    if (P.g[0] == 7 && P.g[1] == 7)
+        hipLaunchKernelGGL((chain_kernel<7, 7>), grid, block, 0, st, P);
+    else if (P.g[0] == 6 && P.g[1] == 6)
+        hipLaunchKernelGGL((chain_kernel<6, 6>), grid, block, 0, st, P);
+    else if (P.g[0] == 4 && P.g[1] == 5)
+        hipLaunchKernelGGL((chain_kernel<4, 5>), grid, block, 0, st, P);
+    else if (P.g[0] == 4 && P.g[1] == 4)
+        hipLaunchKernelGGL((chain_kernel<4, 4>), grid, block, 0, st, P);
+    else
+        hipLaunchKernelGGL((chain_kernel<-1, -1>), grid, block, 0, st, P);
     return hipGetLastError();
 }
 
