@@ -113,10 +113,11 @@ int ensure_workspace(oz2_context* h, size_t bytes) {
 void fill_mod_tables(const ModuliPlan& pl, EncodeParams* E, bool ext) {
     for (int q = 0; q < pl.s; ++q) {
         E->mod[q] = (uint32_t)pl.mod[q];
-        E->barrett[q] = pl.barrett[q];
         E->h[q] = pl.h[q];
         E->K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
-        for (int l = 0; l < kExtWords; ++l) E->c[q][l] = pl.c2[q][l];
+        E->frcp[q] = pl.frcp[q];
+        E->foff[q] = pl.foff[q];
+        for (int l = 0; l < kExtWords; ++l) E->c[q][l] = pl.c4[q][l];
     }
 }
 
@@ -153,10 +154,11 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
     for (int q = 0; q < s; ++q) {
         P.mod[q] = (uint32_t)pl.mod[q];
         P.barrett[q] = pl.barrett[q];
-        P.h[q] = pl.h[q];
         P.K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
         P.bias[q] = pl.gemm_bias[q];
-        for (int l = 0; l < kExtWords; ++l) P.c[q][l] = pl.c2[q][l];
+        P.frcp[q] = pl.frcp[q];
+        P.foff[q] = pl.foff[q];
+        for (int l = 0; l < kExtWords; ++l) P.c[q][l] = pl.c4[q][l];
     }
     fill_crt_tables(pl, &P);
     hipStream_t stm = h->stream;

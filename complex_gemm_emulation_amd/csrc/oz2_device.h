@@ -7,10 +7,10 @@
 //   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scale_of()
 //   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
 //   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
-//             2^(limb position) mod m and K_m = (h_m - 2^62) mod m; the page
-//             uses 21-bit limbs, here 16-bit limbs read in pairs by
-//             v_dot2_u32_u16 (the same congruence) -> make_limbs(),
-//             residue_of_limbs()
+//             2^(limb position) mod m and a constant K_m; the page uses
+//             21-bit limbs, here byte limbs read four at a time by
+//             v_dot4_u32_u8 (the same congruence) -> make_limbs(),
+//             centred_residue()
 //   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
 //             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
 //             top 64 bits + sticky rounded once to double -> Crt,
@@ -85,8 +85,8 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
 }
 
 // residue limbs of one element: the 32-bit words of a_hat + 2^62 (standard
-// width) or a_hat + 2^104 (extended width), each read as a pair of 16-bit
-// limbs; the sign is absorbed by the bias
+// width) or a_hat + 2^104 (extended width), each read as four byte limbs;
+// the sign is absorbed by the bias
 template <bool EXT>
 struct Limbs {
     uint32_t w[EXT ? kExtWords : kStdWords];
@@ -115,19 +115,22 @@ __device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
     return L;
 }
 
-// (a_hat + h) mod m in [0, m), before removing the offset h: v = K_m +
-// sum_l u_l (2^(16 l) mod m) over the 16-bit limbs u_l, two limbs per
-// v_dot2_u32_u16 against c2[p] = (2^(32p) mod m) | (2^(32p+16) mod m) << 16.
-// v < 2^27, so the Barrett quotient of mod_small fits the 24-bit multiplier.
+// centred residue of a_hat in [-h, m - 1 - h] (h = floor((m - 1) / 2)):
+// v = K_m + sum_j b_j (2^(8j) mod m) over the bytes b_j of a_hat + 2^62 (or
+// 2^104), four bytes per v_dot4_u32_u8 against c4[p] (byte j of c4[p] is
+// 2^(32p + 8j) mod m), with K_m = (-2^62) mod m (or (-2^104) mod m), so
+// v = a_hat (mod m) and v < 16 255^2 + 256 < 2^20.  Then
+// r = v - m floor((v + h + 1/2) / m) in FP32: (v + h + 1/2) / m lies at least
+// 1 / (2m) from an integer, and fma(v, fl32(1/m), fl32((h + 1/2) / m)) is
+// within 2^-3 / m + 2^-24 of it, so the floor and r are exact.
 template <bool EXT>
-__device__ __forceinline__ uint32_t residue_of_limbs(const Limbs<EXT>& L, uint32_t Kc, const uint32_t* c2,
-                                                     uint32_t m, uint32_t R) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    uint32_t v = Kc;
+__device__ __forceinline__ int centred_residue(const Limbs<EXT>& L, uint32_t K, const uint32_t* c4, float m,
+                                               float rcp, float off) {
+    uint32_t v = K;
 #pragma unroll
-    for (int p = 0; p < (EXT ? kExtWords : kStdWords); ++p)
-        v = __builtin_amdgcn_udot2(__builtin_bit_cast(u16x2, L.w[p]), __builtin_bit_cast(u16x2, c2[p]), v, false);
-    return mod_small(v, m, R);
+    for (int p = 0; p < (EXT ? kExtWords : kStdWords); ++p) v = __builtin_amdgcn_udot4(L.w[p], c4[p], v, false);
+    const float vf = (float)v;
+    return (int)fmaf(-m, floorf(fmaf(vf, rcp, off)), vf);
 }
 
 // c_hat from the residues of one entry, accumulated over the moduli two at a

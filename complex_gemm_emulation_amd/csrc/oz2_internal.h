@@ -45,8 +45,9 @@ struct EncodeParams {
     int8_t* planes;
     int conj;                // negate imaginary parts (op = 'C')
     int t, s;
-    uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS];
-    uint32_t c[kMaxS][kExtWords];     // 16-bit limb-pair constants (see oz2_device.h)
+    uint32_t mod[kMaxS], h[kMaxS], K[kMaxS];
+    uint32_t c[kMaxS][kExtWords];     // byte-limb constants (see oz2_device.h)
+    float frcp[kMaxS], foff[kMaxS];   // fl32(1 / m), fl32((h + 1/2) / m)
 };
 
 struct GemmParams {
@@ -98,8 +99,9 @@ struct SmallParams {
     int tiles_per_wave;
     double alpha, beta;
     int t, s;
-    uint32_t mod[kMaxS], barrett[kMaxS], h[kMaxS], K[kMaxS], bias[kMaxS];
-    uint32_t c[kMaxS][kExtWords];     // 16-bit limb-pair constants (see oz2_device.h)
+    uint32_t mod[kMaxS], barrett[kMaxS], K[kMaxS], bias[kMaxS];
+    uint32_t c[kMaxS][kExtWords];     // byte-limb constants (see oz2_device.h)
+    float frcp[kMaxS], foff[kMaxS];   // fl32(1 / m), fl32((h + 1/2) / m)
     float finv[kMaxS];
     uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];

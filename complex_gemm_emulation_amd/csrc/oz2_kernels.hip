@@ -98,8 +98,8 @@ struct EncodeTile {
 
 // (a_hat + h) mod m in [0, m), before removing the offset h
 template <bool EXT>
-__device__ __forceinline__ uint32_t residue_off(const Limbs<EXT>& L, const EncodeParams& P, int t) {
-    return residue_of_limbs<EXT>(L, P.K[t], P.c[t], P.mod[t], P.barrett[t]);
+__device__ __forceinline__ int residue_of(const Limbs<EXT>& L, const EncodeParams& P, int t) {
+    return centred_residue<EXT>(L, P.K[t], P.c[t], (float)P.mod[t], P.frcp[t], P.foff[t]);
 }
 
 template <bool CONTIG, bool CPLX, bool EXT>
@@ -174,28 +174,23 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
           for (int u = 0; u < 4; ++u) {
             const int t = t0 + u;
             if (t >= P.s) break;
-            const uint32_t h = P.h[t];
-            uint32_t r[4];
+            int r[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = residue_off<EXT>(lr[e], P, t);
-            *(uint32_t*)(dst + t * plane) = pack4(r[0] - h, r[1] - h, r[2] - h, r[3] - h);
+            for (int e = 0; e < 4; ++e) r[e] = residue_of<EXT>(lr[e], P, t);
+            *(uint32_t*)(dst + t * plane) = pack4(r[0], r[1], r[2], r[3]);
             if (CPLX) {
-                const uint32_t m = P.mod[t];
-                uint32_t ri[4], rs[4];
+                const int m = (int)P.mod[t], lo = -(int)P.h[t], hi = m - 1 - (int)P.h[t];
+                int ri[4], rs[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    ri[e] = residue_off<EXT>(li[e], P, t);
-                    // (re + im + h) mod m from (re + h) mod m and (im + h) mod m
-                    uint32_t x = r[e] + ri[e] + (m - h);  // < 3m
-                    uint32_t x1 = x - m;
-                    x = x < x1 ? x : x1;
-                    x1 = x - m;
-                    rs[e] = x < x1 ? x : x1;
+                    ri[e] = residue_of<EXT>(li[e], P, t);
+                    // centred residue of re + im from those of re and im
+                    int x = r[e] + ri[e];
+                    x = x > hi ? x - m : x;
+                    rs[e] = x < lo ? x + m : x;
                 }
-                *(uint32_t*)(dst + P.set_stride + t * plane) =
-                    pack4(ri[0] - h, ri[1] - h, ri[2] - h, ri[3] - h);
-                *(uint32_t*)(dst + 2 * P.set_stride + t * plane) =
-                    pack4(rs[0] - h, rs[1] - h, rs[2] - h, rs[3] - h);
+                *(uint32_t*)(dst + P.set_stride + t * plane) = pack4(ri[0], ri[1], ri[2], ri[3]);
+                *(uint32_t*)(dst + 2 * P.set_stride + t * plane) = pack4(rs[0], rs[1], rs[2], rs[3]);
             }
           }
         }

@@ -202,9 +202,16 @@ void build_plan(int s, ModuliPlan* p) {
         p->finv[t] = fy / fm;
         uint32_t h = (m - 1) / 2;
         p->h[t] = h;
-        for (int q = 0; q < kExtWords; ++q) p->c2[t][q] = pow2_mod(32 * q, m) | (pow2_mod(32 * q + 16, m) << 16);
-        p->Kstd[t] = (h + m - pow2_mod(62, m)) % m;
-        p->Kext[t] = (h + m - pow2_mod(104, m)) % m;
+        for (int q = 0; q < kExtWords; ++q) {
+            uint32_t w = 0;
+            for (int j = 0; j < 4; ++j) w |= pow2_mod(32 * q + 8 * j, m) << (8 * j);
+            p->c4[t][q] = w;
+        }
+        p->Kstd[t] = (m - pow2_mod(62, m)) % m;
+        p->Kext[t] = (m - pow2_mod(104, m)) % m;
+        volatile float fone = 1.0f, fh = (float)h + 0.5f;
+        p->frcp[t] = fone / fm;
+        p->foff[t] = fh / fm;
         p->barrett[t] = (uint32_t)((1ull << 32) / m);
         // accumulators lie in [-(2^31 - 2^20 + 255), 2^31 - 2^20 + 255]
         const uint64_t lo = (1ull << 31) - (1ull << 20) + 255;

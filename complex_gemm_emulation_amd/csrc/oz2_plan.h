@@ -15,7 +15,7 @@ constexpr int kMinS = 2;
 constexpr int kMaxS = 24;
 constexpr int kMaxNL = 6;            // 32-bit words of c_hat for s <= 24 (log2 M < 192)
 constexpr int kMaxLimb16 = 2 * kMaxNL;
-constexpr int kStdWords = 2;         // 32-bit words (16-bit limb pairs) of a_hat + 2^62 (t <= 61)
+constexpr int kStdWords = 2;         // 32-bit words (four byte limbs each) of a_hat + 2^62 (t <= 61)
 constexpr int kExtWords = 4;         // 32-bit words of a_hat + 2^104 (t <= 100)
 constexpr int kMaxStdT = 61;
 
@@ -49,9 +49,11 @@ struct ModuliPlan {
     uint32_t W2[kMaxS / 2][kMaxLimb16] = {};  // W16 of moduli 2u and 2u+1 packed in 16-bit halves
     // residue generation (Sec. 4.2)
     uint32_t h[kMaxS] = {};       // floor((m-1)/2)
-    uint32_t c2[kMaxS][kExtWords] = {};    // (2^(32p) mod m) | (2^(32p+16) mod m) << 16
-    uint32_t Kstd[kMaxS] = {};    // (h - 2^62) mod m
-    uint32_t Kext[kMaxS] = {};    // (h - 2^104) mod m
+    uint32_t c4[kMaxS][kExtWords] = {};    // byte j of word p: 2^(32p + 8j) mod m
+    uint32_t Kstd[kMaxS] = {};    // (-2^62) mod m
+    uint32_t Kext[kMaxS] = {};    // (-2^104) mod m
+    float frcp[kMaxS] = {};       // fl32(1 / m)
+    float foff[kMaxS] = {};       // fl32((h + 1/2) / m)
     uint32_t barrett[kMaxS] = {}; // floor(2^32 / m)
     uint32_t gemm_bias[kMaxS] = {};  // multiple of m making any INT32 accumulator non-negative
 };

@@ -48,10 +48,11 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
 // per-modulus constants, staged in LDS once per block: read at uniform
 // addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes
 struct ModConst {
-    uint32_t mod, barrett, bias, h, K;
-    uint32_t c2[kExtWords];
-    float finv;
+    uint32_t mod, barrett, bias, K;
+    uint32_t c4[kExtWords];
+    float frcp, foff, finv;
 };
+static_assert(offsetof(ModConst, finv) == 4 * (6 + kExtWords), "staging order of ModConst");
 struct SmallConsts {
     ModConst q[kMaxS + 1];            // one zeroed entry past the last modulus
     uint32_t W2[kMaxS / 2][kMaxLimb16];
@@ -78,11 +79,11 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
     for (int t = 0; t < SMAX; ++t) {
         if (t < P.s) {
             const ModConst& C = Q.q[t];
-            const uint32_t h = C.h;
+            const float m = (float)C.mod;
             uint32_t w[2] = {0u, 0u};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const uint32_t r = residue_of_limbs<EXT>(L[e], C.K, C.c2, C.mod, C.barrett) - h;
+                const uint32_t r = (uint32_t)centred_residue<EXT>(L[e], C.K, C.c4, m, C.frcp, C.foff);
                 w[e >> 2] |= (r & 0xffu) << (8 * (e & 3));
             }
             frag[t] = (long)((uint64_t)w[0] | ((uint64_t)w[1] << 32));
@@ -122,9 +123,10 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                     if (f == 0) v = P.mod[t];
                     else if (f == 1) v = P.barrett[t];
                     else if (f == 2) v = P.bias[t];
-                    else if (f == 3) v = P.h[t];
-                    else if (f == 4) v = P.K[t];
-                    else if (f < 5 + kExtWords) v = P.c[t][f - 5];
+                    else if (f == 3) v = P.K[t];
+                    else if (f < 4 + kExtWords) v = P.c[t][f - 4];
+                    else if (f == 4 + kExtWords) v = __float_as_uint(P.frcp[t]);
+                    else if (f == 5 + kExtWords) v = __float_as_uint(P.foff[t]);
                     else v = __float_as_uint(P.finv[t]);
                 }
             } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16) {
