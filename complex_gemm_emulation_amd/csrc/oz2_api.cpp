@@ -153,9 +153,8 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
     const bool ext = pl.NL >= 5;
     for (int q = 0; q < s; ++q) {
         P.mod[q] = (uint32_t)pl.mod[q];
-        P.barrett[q] = pl.barrett[q];
         P.K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
-        P.bias[q] = pl.gemm_bias[q];
+        P.rcp[q] = pl.drcp[q];
         P.frcp[q] = pl.frcp[q];
         P.foff[q] = pl.foff[q];
         for (int l = 0; l < kExtWords; ++l) P.c[q][l] = pl.c4[q][l];
@@ -288,8 +287,7 @@ int product(oz2_context* h, bool cplx, const Layout& L, const int8_t* pa, const 
         G.s = s;
         for (int q = 0; q < s; ++q) {
             G.mod[q] = (uint32_t)pl->mod[q];
-            G.barrett[q] = pl->barrett[q];
-            G.bias[q] = pl->gemm_bias[q];
+            G.rcp[q] = pl->drcp[q];
         }
         for (int c = 0; c < L.chunks; ++c) {
             G.C = res + c * chunk_stride;

@@ -71,15 +71,6 @@ __device__ __forceinline__ unsigned __int128 rint_scaled_mag128(uint64_t bits, i
     return (unsigned __int128)rint_scaled_mag64(bits, D);
 }
 
-// v mod m for v < 2^32 with q = floor(v R / 2^32), R = floor(2^32 / m):
-// q is floor(v/m) or one less, so r = v - q m lies in [0, 2m)
-__device__ __forceinline__ uint32_t mod_small(uint32_t v, uint32_t m, uint32_t R) {
-    const uint32_t q = __umulhi(v, R);
-    const uint32_t r = v - __umul24(q, m);  // q < 2^24: v/m < 5 * 2^21 + 1
-    const uint32_t r2 = r - m;
-    return r < r2 ? r : r2;
-}
-
 __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
     return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
 }

@@ -61,15 +61,14 @@ static_assert(kPadK % (kBK * kMaxStages) == 0, "padded k holds whole stage round
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
-// INT32 accumulator -> [0, m): bias makes it non-negative (a multiple of m,
-// chosen for |acc| <= 2^31 - 2^20 + 255), Barrett quotient floor(u R / 2^32)
-// with R = floor(2^32/m) is floor(u/m) or one less.
-__device__ __forceinline__ uint32_t acc_mod(int32_t acc, uint32_t m, uint32_t R, uint32_t bias) {
-    const uint32_t u = (uint32_t)acc + bias;
-    const uint32_t q = __umulhi(u, R);
-    const uint32_t r = u - q * m;
-    const uint32_t r2 = r - m;
-    return r < r2 ? r : r2;
+// INT32 accumulator -> [0, m): r = acc - m floor((acc + 1/2) / m) in FP64.
+// (acc + 1/2) / m lies at least 1 / (2m) from an integer, and
+// fma(acc, fl64(1/m), fl64(1/(2m))) is within 2^-20 / m of it for
+// |acc| < 2^31, so the floor and r are exact (five full-rate FP64 and
+// conversion instructions instead of two quarter-rate 32-bit multiplies).
+__device__ __forceinline__ uint32_t acc_mod(int32_t acc, double m, double rcp, double half_rcp) {
+    const double a = (double)acc;
+    return (uint32_t)(int)fma(-m, floor(fma(a, rcp, half_rcp)), a);
 }
 
 __device__ __forceinline__ uint32_t pack4(const uint32_t r[4]) {
@@ -132,7 +131,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     const int tm = first_m + in % gsz;
     const int tn = in / gsz;
 
-    const uint32_t m = P.mod[t], R = P.barrett[t], bias = P.bias[t];
+    const uint32_t m = P.mod[t];
+    const double dm = (double)m, rcp = P.rcp[t], half_rcp = 0.5 * rcp;
     const int64_t kp = P.kp;
     const int nk = P.k_steps;  // multiple of 4; this launch covers k in [k_begin, k_begin + 64 nk)
 
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
                 for (int g = 0; g < 4; ++g) {
                     uint32_t r[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][4 * g + e], m, R, bias);
+                    for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][4 * g + e], dm, rcp, half_rcp);
                     const int64_t row = row_out0 + i * 32 + 8 * g;
                     uint8_t* re_dst = P.C + (int64_t)t * P.n * P.mp + col * P.mp + row;
                     if (!CPLX) {

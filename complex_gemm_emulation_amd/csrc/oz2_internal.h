@@ -60,7 +60,8 @@ struct GemmParams {
     int tiles_m, tiles_n;
     int64_t k_begin;   // first k position of this launch (multiple of 256)
     int k_steps;       // 64-wide k steps of this launch (multiple of 4): <= 2044 keeps INT32 exact
-    uint32_t mod[kMaxS], barrett[kMaxS], bias[kMaxS];
+    uint32_t mod[kMaxS];
+    double rcp[kMaxS];   // fl64(1 / m)
 };
 
 struct ReconParams {
@@ -99,7 +100,8 @@ struct SmallParams {
     int tiles_per_wave;
     double alpha, beta;
     int t, s;
-    uint32_t mod[kMaxS], barrett[kMaxS], K[kMaxS], bias[kMaxS];
+    uint32_t mod[kMaxS], K[kMaxS];
+    double rcp[kMaxS];                // fl64(1 / m)
     uint32_t c[kMaxS][kExtWords];     // byte-limb constants (see oz2_device.h)
     float frcp[kMaxS], foff[kMaxS];   // fl32(1 / m), fl32((h + 1/2) / m)
     float finv[kMaxS];

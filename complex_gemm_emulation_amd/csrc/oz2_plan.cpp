@@ -212,10 +212,8 @@ void build_plan(int s, ModuliPlan* p) {
         volatile float fone = 1.0f, fh = (float)h + 0.5f;
         p->frcp[t] = fone / fm;
         p->foff[t] = fh / fm;
-        p->barrett[t] = (uint32_t)((1ull << 32) / m);
-        // accumulators lie in [-(2^31 - 2^20 + 255), 2^31 - 2^20 + 255]
-        const uint64_t lo = (1ull << 31) - (1ull << 20) + 255;
-        p->gemm_bias[t] = (uint32_t)(((lo + m - 1) / m) * m);
+        volatile double done = 1.0, dm = (double)m;
+        p->drcp[t] = done / dm;
     }
     // limb pairs for the two-moduli-per-instruction CRT accumulation; past the
     // last modulus the high halves stay 0

@@ -54,8 +54,7 @@ struct ModuliPlan {
     uint32_t Kext[kMaxS] = {};    // (-2^104) mod m
     float frcp[kMaxS] = {};       // fl32(1 / m)
     float foff[kMaxS] = {};       // fl32((h + 1/2) / m)
-    uint32_t barrett[kMaxS] = {}; // floor(2^32 / m)
-    uint32_t gemm_bias[kMaxS] = {};  // multiple of m making any INT32 accumulator non-negative
+    double drcp[kMaxS] = {};      // fl64(1 / m), for the reduction of INT32 accumulators
 };
 
 // Max-product set of s pairwise-coprime integers <= 256 and its constants;

@@ -48,7 +48,7 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
 // per-modulus constants, staged in LDS once per block: read at uniform
 // addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes
 struct ModConst {
-    uint32_t mod, barrett, bias, K;
+    uint32_t mod, rcp_lo, rcp_hi, K;  // rcp: the two words of fl64(1 / m)
     uint32_t c4[kExtWords];
     float frcp, foff, finv;
 };
@@ -91,12 +91,12 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
     }
 }
 
-__device__ __forceinline__ uint32_t acc_mod(int32_t acc, uint32_t m, uint32_t R, uint32_t bias) {
-    const uint32_t u = (uint32_t)acc + bias;
-    const uint32_t q = __umulhi(u, R);
-    const uint32_t r = u - q * m;
-    const uint32_t r2 = r - m;
-    return r < r2 ? r : r2;
+// INT32 accumulator -> [0, m), exact in FP64 as in the residue GEMM:
+// r = acc - m floor((acc + 1/2) / m), |acc| < 2^31
+__device__ __forceinline__ uint32_t acc_mod(int32_t acc, const ModConst& C) {
+    const double a = (double)acc, m = (double)C.mod;
+    const double rcp = __hiloint2double((int)C.rcp_hi, (int)C.rcp_lo);
+    return (uint32_t)(int)fma(-m, floor(fma(a, rcp, 0.5 * rcp)), a);
 }
 
 template <int NL, bool BETA>
@@ -121,8 +121,8 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                 const int t = i / nq, f = i % nq;
                 if (t < P.s) {
                     if (f == 0) v = P.mod[t];
-                    else if (f == 1) v = P.barrett[t];
-                    else if (f == 2) v = P.bias[t];
+                    else if (f == 1) v = (uint32_t)__double2loint(P.rcp[t]);
+                    else if (f == 2) v = (uint32_t)__double2hiint(P.rcp[t]);
                     else if (f == 3) v = P.K[t];
                     else if (f < 4 + kExtWords) v = P.c[t][f - 4];
                     else if (f == 4 + kExtWords) v = __float_as_uint(P.frcp[t]);
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                 const ModConst& C1 = Q.q[t + 1];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t ra = acc_mod(ca[e], C0.mod, C0.barrett, C0.bias);
-                    const uint32_t rb = two ? acc_mod(cb[e], C1.mod, C1.barrett, C1.bias) : 0u;
+                    const uint32_t ra = acc_mod(ca[e], C0);
+                    const uint32_t rb = two ? acc_mod(cb[e], C1) : 0u;
                     acc[e].add2(ra, rb, C0.finv, C1.finv, Q.W2[t >> 1]);
                 }
             }
