@@ -152,6 +152,78 @@ GEMM_SPECS = {
 }
 
 
+def _dyadic(x):
+    """integer mantissas and exponents: x = q 2^e exactly (finite doubles)"""
+    mant, ex = np.frexp(np.asarray(x, dtype=np.float64))
+    return (mant * 2.0 ** 53).astype(np.int64), ex.astype(np.int64) - 53
+
+
+def _int_to_double(v, e):
+    """v 2^e rounded once to double (CPython's integer true division rounds
+    correctly)"""
+    return float(v << e) if e >= 0 else v / (1 << -e)
+
+
+def exact_dot(a, b):
+    """sum_p a_p b_p of two double vectors, exact in integers, rounded once"""
+    qa, ea = _dyadic(a)
+    qb, eb = _dyadic(b)
+    e = ea + eb
+    e0 = int(e.min())
+    tot = 0
+    for x, y, z in zip(qa.tolist(), qb.tolist(), (e - e0).tolist()):
+        tot += (x * y) << z
+    return _int_to_double(tot, e0)
+
+
+def normwise_error(got, ref):
+    got, ref = np.asarray(got), np.asarray(ref)
+    return float(np.sqrt(np.sum((got - ref) ** 2) / np.sum(ref ** 2)))
+
+
+def gemm_accuracy(dC, A, B, m, n, k, ta, tb, count=32, seed=4242):
+    """Normwise relative error of C = op(A) op(B) (beta = 0) on `count`
+    seeded entries (first and last included) against the exact product"""
+    rng = np.random.default_rng(seed)
+    ii = np.concatenate([[0, m - 1], rng.choice(m, count - 2)])
+    jj = np.concatenate([[0, n - 1], rng.choice(n, count - 2)])
+    C = dC.cpu().numpy()
+    Am = A.reshape(k, m).T if ta == "N" else A.reshape(m, k)   # Am[i] = row i of op(A)
+    Bm = B.reshape(n, k) if tb == "N" else B.reshape(k, n).T   # Bm[j] = column j of op(B)
+    got = np.array([C[i + j * m] for i, j in zip(ii, jj)])
+    ref = np.array([exact_dot(Am[i], Bm[j]) for i, j in zip(ii, jj)])
+    return normwise_error(got, ref), f"{count} seeded entries vs the exact product"
+
+
+def chain_accuracy(Y, X, ops, n, count):
+    """Normwise relative error of the first `count` chains
+    Y = X x1 A1 x2 A2 x3 A3 against the exact chain, in integers"""
+    n3 = n ** 3
+    mats = []
+    for a in ops:
+        q, e = _dyadic(a)
+        e0 = int(e.min())
+        M = np.array([int(v) << int(z) for v, z in zip(q.tolist(), (e - e0).tolist())], dtype=object)
+        mats.append((M.reshape(n, n).T, e0))   # M[i, j] = a[i + n j]
+    errs_num = errs_den = 0.0
+    for t in range(count):
+        x = X[t * n3:(t + 1) * n3]
+        q, e = _dyadic(x)
+        nz = x != 0
+        e0 = int(e[nz].min()) if nz.any() else 0
+        T = np.array([int(v) << int(z - e0) if f else 0 for v, z, f in zip(q.tolist(), e.tolist(), nz.tolist())],
+                     dtype=object).reshape(n, n, n).transpose(2, 1, 0)   # T[k1, k2, k3]
+        T = np.tensordot(mats[0][0], T, axes=([1], [0]))                        # [a1, k2, k3]
+        T = np.tensordot(mats[1][0], T, axes=([1], [1])).transpose(1, 0, 2)    # [a1, a2, k3]
+        T = np.tensordot(mats[2][0], T, axes=([1], [2])).transpose(1, 2, 0)    # [a1, a2, a3]
+        esum = e0 + mats[0][1] + mats[1][1] + mats[2][1]
+        ref = np.array([_int_to_double(int(v), esum) for v in T.transpose(2, 1, 0).reshape(-1)])
+        got = Y[t * n3:(t + 1) * n3]
+        errs_num += float(np.sum((got - ref) ** 2))
+        errs_den += float(np.sum(ref ** 2))
+    return float(np.sqrt(errs_num / errs_den)), f"first {count} tensors vs the exact chain"
+
+
 def run_gemm(args, name):
     import torch
     import complex_gemm_emulation_amd as oz2
@@ -262,6 +334,12 @@ def run_gemm(args, name):
         log(f"[bench] oracle cpu baseline on a {side}^2 entry sample, s={s_cpu}")
         cpu = cpu_baseline_gemm(spec, (ra, rb), A, B, C, s_cpu, side, f"{m}x{n}x{k}")
 
+    accuracy = None
+    if not cplx and spec["beta"] == 0:
+        log(f"[bench] accuracy of the s={s_list[-1]} result on sampled entries")
+        err, how = gemm_accuracy(dC, A, B, m, n, k, ta, tb)
+        accuracy = {"normwise_rel_err": err, "s": s_list[-1], "sample": how}
+
     for pa, pb in prepared.values():
         pa.close()
         pb.close()
@@ -281,6 +359,7 @@ def run_gemm(args, name):
                    "m": m, "n": n, "k": k, "s": s_list, "ops": f"{ta}/{tb}",
                    "alpha": str(spec["alpha"]), "beta": str(spec["beta"])},
         "per_s": per_s,
+        "accuracy": accuracy,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -451,6 +530,9 @@ def run_chain_rbe(args):
         cdt = time.perf_counter() - t0
         cpu = dict(value=n3 * nt / cdt / 1e9, unit="GDoF/s", cores=1, kind="oracle",
                    sample=f"first {nt} of the {batch} tensors, whole chain, {cdt:.1f} s")
+    log("[bench] accuracy against the exact chain")
+    err, how = chain_accuracy(dY.cpu().numpy(), X, ops, n, args.chain_acc_tensors)
+    accuracy = {"normwise_rel_err": err, "sample": how}
     info = dict(b=plan.b, g=list(plan.g))
     plan.close()
     h.close()
@@ -462,6 +544,7 @@ def run_chain_rbe(args):
         "dtype": "i8",
         "config": {"workload": f"tensor_chain_rescale_be_n{n}_b{batch}_s{s}", "n": n, "batch": batch, "s": s,
                    "plan": info},
+        "accuracy": accuracy,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -540,6 +623,9 @@ def run_chain(args):
         cdt = time.perf_counter() - t0
         cpu = dict(value=n3 * nt / cdt / 1e9, unit="GDoF/s", cores=oracle.max_threads(), kind="oracle",
                    sample=f"first {nt} of the {batch} tensors, all three modes, {cdt:.1f} s")
+    log("[bench] accuracy against the exact chain")
+    err, how = chain_accuracy(dY.cpu().numpy(), X, ops, n, args.chain_acc_tensors)
+    accuracy = {"normwise_rel_err": err, "sample": how}
     h.close()
     return {
         "metric": "tensor-mode chain GDoF/s (Y = X x1 A x2 B x3 C, per-mode Ozaki II)",
@@ -549,6 +635,7 @@ def run_chain(args):
         "dtype": "i8",
         "config": {"workload": f"tensor_chain_n{n}_b{batch}_s{s}", "n": n, "batch": batch, "s": s,
                    "modes": 3, "emulated_tflops": round(3 * 2.0 * n * dofs / (dt / args.steps) / 1e12, 3)},
+        "accuracy": accuracy,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -567,6 +654,7 @@ def main():
     ap.add_argument("--cpu-side", type=int, default=0)
     ap.add_argument("--chain-cpu-tensors", type=int, default=256)
     ap.add_argument("--chain-rbe-cpu-tensors", type=int, default=384)
+    ap.add_argument("--chain-acc-tensors", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -591,7 +679,7 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
             "data": "synthetic", "config": out["config"]}
-    for key in ("per_s", "per_shape", "roofline", "cpu_baseline"):
+    for key in ("per_s", "per_shape", "accuracy", "roofline", "cpu_baseline"):
         if key in out:
             line[key] = out[key]
     print(json.dumps(line))
