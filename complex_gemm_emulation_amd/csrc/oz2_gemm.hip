@@ -93,6 +93,45 @@ constexpr int waitcnt_vm(int n, bool lgkm0) {
     return (n & 15) | ((n >> 4) << 14) | 0x0070 | (lgkm0 ? 0 : 0x0F00);
 }
 
+// Block order.  Blocks start roughly in index order and are dealt
+// round-robin to the 8 XCDs (bid mod 8).  When the tiles of one modulus
+// split evenly over the XCDs, blocks run modulus after modulus: while one
+// modulus' planes are in use, the whole chip works on them, so they stay in
+// the 256 MB last-level cache.  Each XCD owns a band of tile rows (or of
+// tile columns) of that modulus and walks it in groups of at most 8 tiles,
+// so that its 32 resident blocks share few A and B bands in its L2.
+// Otherwise each XCD takes a contiguous range of blocks, grouped 8 tiles
+// tall.
+__device__ __forceinline__ void block_tile(int bid, int nb, int tiles_m, int tiles_n, int& t, int& tm, int& tn) {
+    constexpr int GROUP = 8;
+    const int tiles = tiles_m * tiles_n;
+    if (tiles % 8 == 0 && (tiles_m % 8 == 0 || tiles_n % 8 == 0)) {
+        t = bid / tiles;
+        const int r = bid % tiles;
+        const int x = r & 7, q = r >> 3;
+        const bool rows = tiles_m % 8 == 0;
+        const int bm = rows ? tiles_m / 8 : tiles_m;  // this XCD's band
+        const int bn = rows ? tiles_n : tiles_n / 8;
+        const int g = min(bm, GROUP);                  // group height within the band
+        const int per_group = g * bn;
+        const int first = (q / per_group) * g;
+        const int gsz = min(bm - first, g);
+        const int in = q % per_group;
+        tm = (rows ? x * bm : 0) + first + in % gsz;
+        tn = (rows ? 0 : x * bn) + in / gsz;
+        return;
+    }
+    const int lid = (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
+    t = lid / tiles;
+    const int rem = lid % tiles;
+    const int per_group = GROUP * tiles_n;
+    const int first_m = (rem / per_group) * GROUP;
+    const int gsz = min(tiles_m - first_m, GROUP);
+    const int in = rem % per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+}
+
 template <int BM, int BN, int WM, int WN, int NST, bool CPLX>
 __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParams P) {
     constexpr int kStages = NST;
@@ -117,19 +156,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     const int wm = wave % WM, wn = wave / WM;
 
     // block -> (modulus, tile row, tile column)
-    const int nb = gridDim.x;
-    const int bid = blockIdx.x;
-    const int lid = (nb & 7) == 0 ? (bid & 7) * (nb >> 3) + (bid >> 3) : bid;
-    const int tiles = P.tiles_m * P.tiles_n;
-    const int t = lid / tiles;
-    const int rem = lid % tiles;
-    constexpr int GROUP = 8;
-    const int per_group = GROUP * P.tiles_n;
-    const int first_m = (rem / per_group) * GROUP;
-    const int gsz = min(P.tiles_m - first_m, GROUP);
-    const int in = rem % per_group;
-    const int tm = first_m + in % gsz;
-    const int tn = in / gsz;
+    int t, tm, tn;
+    block_tile(blockIdx.x, gridDim.x, P.tiles_m, P.tiles_n, t, tm, tn);
 
     const uint32_t m = P.mod[t];
     const double dm = (double)m, rcp = P.rcp[t], half_rcp = 0.5 * rcp;
