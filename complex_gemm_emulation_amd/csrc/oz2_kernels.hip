@@ -210,12 +210,15 @@ __device__ __forceinline__ uint32_t add_mod_bytes(uint32_t a, uint32_t b, uint32
     return out;
 }
 
+// A wavefront reconstructs 256 consecutive rows of one column (mp is a
+// multiple of 256), 4 entries per lane; the column index is wave-uniform.
 template <int NL, bool CPLX, bool BETA>
 __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
-    const int64_t groups_per_col = P.mp / 4;
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t j = gid / groups_per_col;
-    const int64_t i0 = (gid % groups_per_col) * 4;
+    const uint32_t waves_per_col = (uint32_t)(P.mp / 256);
+    const uint32_t wid = blockIdx.x * 4u + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t jw = wid / waves_per_col;
+    const int64_t j = jw;
+    const int64_t i0 = (int64_t)(wid - jw * waves_per_col) * 256 + (threadIdx.x & 63) * 4;
     if (j >= P.n || i0 >= P.m) return;
 
     Crt<NL> acc[CPLX ? 2 : 1][4];
@@ -412,7 +415,7 @@ hipError_t launch_encode(const EncodeParams& P, bool contiguous, bool cplx, bool
 
 template <int NL>
 static hipError_t recon_go(const ReconParams& P, bool cplx, bool beta, hipStream_t st) {
-    const int64_t nb = blocks_for((P.mp / 4) * P.n, 256);
+    const int64_t nb = blocks_for((P.mp / 256) * P.n, 4);  // one wavefront per 256 rows of a column
     dim3 g((unsigned)nb), b(256);
     if (cplx) {
         if (beta) hipLaunchKernelGGL((reconstruct_kernel<NL, true, true>), g, b, 0, st, P);
@@ -426,7 +429,8 @@ static hipError_t recon_go(const ReconParams& P, bool cplx, bool beta, hipStream
 
 hipError_t launch_reconstruct(const ReconParams& P, int NL, bool cplx, bool beta_nonzero,
                               hipStream_t st) {
-    if (P.mp % 4) return hipErrorInvalidValue;
+    // wave indices are 32-bit
+    if (P.mp % 256 || (P.mp / 256) * P.n > (int64_t)UINT32_MAX - 4) return hipErrorInvalidValue;
     switch (NL) {
         case 2: return recon_go<2>(P, cplx, beta_nonzero, st);
         case 3: return recon_go<3>(P, cplx, beta_nonzero, st);
