@@ -123,7 +123,7 @@ void fill_mod_tables(const ModuliPlan& pl, EncodeParams* E, bool ext) {
 
 template <class P>
 void fill_crt_tables(const ModuliPlan& pl, P* R) {
-    for (int q = 0; q < pl.s; ++q) R->finv[q] = pl.finv[q];  // 0 past the last modulus
+    for (int u = 0; u < (pl.s + 1) / 2; ++u) R->Y2[u] = pl.Y2[u];  // high half 0 past the last modulus
     for (int u = 0; u < (pl.s + 1) / 2; ++u)
         for (int l = 0; l < 2 * pl.NL; ++l) R->W2[u][l] = pl.W2[u][l];
     for (int l = 0; l < 2 * pl.NL; ++l) R->M16[l] = pl.M16[l];

@@ -125,41 +125,42 @@ __device__ __forceinline__ int centred_residue(const Limbs<EXT>& L, uint32_t K, 
 }
 
 // c_hat from the residues of one entry, accumulated over the moduli two at a
-// time: z with two FP32 FMAs in ascending t, the 16-bit limbs of
-// r_t W_t + r_(t+1) W_(t+1) with one v_dot2_u32_u16 per limb (r and the two
-// limbs of W packed as 16-bit pairs).  Every term r W16 < 2^8 2^16, so the
-// limb sums of 24 moduli stay below 2^29.
+// time with one v_dot2_u32_u16 per limb: the 16-bit limbs of
+// r_t W_t + r_(t+1) W_(t+1) (r and the two limbs of W packed as 16-bit
+// pairs; every term r W16 < 2^8 2^16, so the limb sums of 24 moduli stay
+// below 2^29), and the quotient estimate z = sum r_t y_t / m_t in 16.16
+// fixed point, sum r_t Y_t with Y_t = round(2^16 y_t / m_t) < 2^16.
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 template <int NL>
 struct Crt {
     static constexpr int L16 = 2 * NL;
-    float z;
+    uint32_t zq;
     uint32_t L[L16];
     __device__ __forceinline__ void init() {
-        z = 0.0f;
+        zq = 0u;
 #pragma unroll
         for (int l = 0; l < L16; ++l) L[l] = 0u;
     }
     // moduli t, t+1: residues packed as ra | rb << 16 (rb = 0 past the last
-    // modulus, where fb = 0 and the high halves of W2 are 0 too); fra, frb the
-    // residues as floats; W2[l] = W16[t][l] | W16[t+1][l] << 16
-    __device__ __forceinline__ void add2(uint32_t packed, float fra, float frb, float fa, float fb,
-                                         const uint32_t* W2) {
-        z = __builtin_fmaf(fra, fa, z);
-        z = __builtin_fmaf(frb, fb, z);
+    // modulus, where the high halves of Y2 and W2 are 0 too);
+    // Y2 = Y_t | Y_(t+1) << 16, W2[l] = W16[t][l] | W16[t+1][l] << 16
+    __device__ __forceinline__ void add2(uint32_t packed, uint32_t Y2, const uint32_t* W2) {
         const v2u16 r = __builtin_bit_cast(v2u16, packed);
+        zq = __builtin_amdgcn_udot2(r, __builtin_bit_cast(v2u16, Y2), zq, false);
 #pragma unroll
         for (int l = 0; l < L16; ++l)
             L[l] = __builtin_amdgcn_udot2(r, __builtin_bit_cast(v2u16, W2[l]), L[l], false);
     }
-    __device__ __forceinline__ void add2(uint32_t ra, uint32_t rb, float fa, float fb, const uint32_t* W2) {
-        add2(ra | (rb << 16), (float)ra, (float)rb, fa, fb, W2);
+    __device__ __forceinline__ void add2(uint32_t ra, uint32_t rb, uint32_t Y2, const uint32_t* W2) {
+        add2(ra | (rb << 16), Y2, W2);
     }
     // c_hat = Z - q M mod 2^(32 NL), two's complement words.  |q| <= 24 * 256
     // and M16 < 2^16, so q M16 fits the 24-bit multiplier; one carry pass.
     __device__ __forceinline__ void finish(const uint32_t* M16, uint32_t w[NL]) {
-        const int32_t q = (int32_t)__builtin_rintf(z);  // |z - Z/M| < 2^-6, Z/M within 1/4 of q
+        // |zq 2^-16 - Z/M| <= sum r_t |Y_t 2^-16 - y_t/m_t| <= 24 255 2^-17 < 0.05
+        // and Z/M lies within 1/4 of q (|c_hat| <= M/4): rounding zq gives q
+        const int32_t q = (int32_t)((zq + 0x8000u) >> 16);
         int32_t carry = 0;
         uint32_t lo16 = 0;
 #pragma unroll

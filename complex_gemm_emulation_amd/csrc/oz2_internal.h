@@ -77,7 +77,7 @@ struct ReconParams {
     double alpha[2], beta[2];
     int t, s;
     uint32_t* chat;         // optional debug copy of c_hat words [outs][n][mp][NL]
-    float finv[kMaxS];
+    uint32_t Y2[kMaxS / 2]; // round(2^16 y_t / m_t) of moduli 2u and 2u+1 in 16-bit halves
     uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];
     uint32_t mod[kMaxS];
@@ -104,7 +104,7 @@ struct SmallParams {
     double rcp[kMaxS];                // fl64(1 / m)
     uint32_t c[kMaxS][kExtWords];     // byte-limb constants (see oz2_device.h)
     float frcp[kMaxS], foff[kMaxS];   // fl32(1 / m), fl32((h + 1/2) / m)
-    float finv[kMaxS];
+    uint32_t Y2[kMaxS / 2];           // round(2^16 y_t / m_t), pairs as in ReconParams
     uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];
 };
@@ -147,7 +147,7 @@ struct CrtTestParams {
     int64_t count;
     uint32_t* words;   // [count][NL]
     int s;
-    float finv[kMaxS];
+    uint32_t Y2[kMaxS / 2];
     uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16
     uint32_t M16[kMaxLimb16];
 };

@@ -251,18 +251,14 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
 #pragma unroll
         for (int t = 0; t < SMAX; t += 2) {
             if (t < P.s) {
-                const float fa = P.finv[t], fb = P.finv[t + 1];
+                const uint32_t Y2 = P.Y2[t >> 1];
                 const uint32_t* W2 = P.W2[t >> 1];
                 const uint32_t wa = rw[t], wb = rw[t + 1];
                 // entry e: byte e of wa in bits 0-7, byte e of wb in bits 16-23
-                acc[o][0].add2(__builtin_amdgcn_perm(wb, wa, 0x0c040c00u), (float)(wa & 0xffu),
-                               (float)(wb & 0xffu), fa, fb, W2);
-                acc[o][1].add2(__builtin_amdgcn_perm(wb, wa, 0x0c050c01u), (float)((wa >> 8) & 0xffu),
-                               (float)((wb >> 8) & 0xffu), fa, fb, W2);
-                acc[o][2].add2(__builtin_amdgcn_perm(wb, wa, 0x0c060c02u), (float)((wa >> 16) & 0xffu),
-                               (float)((wb >> 16) & 0xffu), fa, fb, W2);
-                acc[o][3].add2(__builtin_amdgcn_perm(wb, wa, 0x0c070c03u), (float)(wa >> 24), (float)(wb >> 24),
-                               fa, fb, W2);
+                acc[o][0].add2(__builtin_amdgcn_perm(wb, wa, 0x0c040c00u), Y2, W2);
+                acc[o][1].add2(__builtin_amdgcn_perm(wb, wa, 0x0c050c01u), Y2, W2);
+                acc[o][2].add2(__builtin_amdgcn_perm(wb, wa, 0x0c060c02u), Y2, W2);
+                acc[o][3].add2(__builtin_amdgcn_perm(wb, wa, 0x0c070c03u), Y2, W2);
             }
         }
     }
@@ -327,7 +323,7 @@ __global__ __launch_bounds__(256) void crt_test_kernel(CrtTestParams P) {
     Crt<NL> acc;
     acc.init();
     for (int t = 0; t < P.s; t += 2)
-        acc.add2(P.R[t * P.count + q], t + 1 < P.s ? P.R[(t + 1) * P.count + q] : 0u, P.finv[t], P.finv[t + 1],
+        acc.add2(P.R[t * P.count + q], t + 1 < P.s ? P.R[(t + 1) * P.count + q] : 0u, P.Y2[t >> 1],
                  P.W2[t >> 1]);
     uint32_t w[NL];
     acc.finish(P.M16, w);

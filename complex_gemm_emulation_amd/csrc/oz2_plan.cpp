@@ -196,10 +196,8 @@ void build_plan(int s, ModuliPlan* p) {
         UBig W = Mt;
         W.mul_small(y);
         for (int l = 0; l < 2 * p->NL; ++l) p->W16[t][l] = W.limb16(l);
-        // IEEE single division of two exactly representable integers is
-        // correctly rounded: fl32(y / m)
-        volatile float fy = (float)y, fm = (float)m;
-        p->finv[t] = fy / fm;
+        p->yfix[t] = (uint32_t)((((uint64_t)y << 17) + m) / (2ull * m));  // round(2^16 y / m)
+        volatile float fm = (float)m;
         uint32_t h = (m - 1) / 2;
         p->h[t] = h;
         for (int q = 0; q < kExtWords; ++q) {
@@ -217,6 +215,7 @@ void build_plan(int s, ModuliPlan* p) {
     }
     // limb pairs for the two-moduli-per-instruction CRT accumulation; past the
     // last modulus the high halves stay 0
+    for (int u = 0; u < (s + 1) / 2; ++u) p->Y2[u] = p->yfix[2 * u] | (2 * u + 1 < s ? p->yfix[2 * u + 1] << 16 : 0u);
     for (int u = 0; u < (s + 1) / 2; ++u)
         for (int l = 0; l < 2 * p->NL; ++l)
             p->W2[u][l] = p->W16[2 * u][l] | (2 * u + 1 < s ? p->W16[2 * u + 1][l] << 16 : 0u);

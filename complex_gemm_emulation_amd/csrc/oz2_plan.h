@@ -43,7 +43,8 @@ struct ModuliPlan {
     double log2M = 0.0;
     int NL = 0;                   // 32-bit words of c_hat: max(2, floor(log2 M / 32) + 1)
     // reconstruction (Sec. 4.4)
-    float finv[kMaxS] = {};       // fl32(y_t / m_t), y_t = (M/m_t)^-1 mod m_t
+    uint32_t yfix[kMaxS] = {};    // round(2^16 y_t / m_t), y_t = (M/m_t)^-1 mod m_t
+    uint32_t Y2[kMaxS / 2] = {};  // yfix of moduli 2u and 2u+1 in 16-bit halves
     uint32_t W16[kMaxS][kMaxLimb16] = {};  // 16-bit limbs of W_t = (M/m_t) y_t
     uint32_t M16[kMaxLimb16] = {};         // 16-bit limbs of M
     uint32_t W2[kMaxS / 2][kMaxLimb16] = {};  // W16 of moduli 2u and 2u+1 packed in 16-bit halves

@@ -50,14 +50,16 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
 struct ModConst {
     uint32_t mod, rcp_lo, rcp_hi, K;  // rcp: the two words of fl64(1 / m)
     uint32_t c4[kExtWords];
-    float frcp, foff, finv;
+    float frcp, foff;
 };
-static_assert(offsetof(ModConst, finv) == 4 * (6 + kExtWords), "staging order of ModConst");
+static_assert(offsetof(ModConst, foff) == 4 * (5 + kExtWords), "staging order of ModConst");
 struct SmallConsts {
     ModConst q[kMaxS + 1];            // one zeroed entry past the last modulus
     uint32_t W2[kMaxS / 2][kMaxLimb16];
     uint32_t M16[kMaxLimb16];
+    uint32_t Y2[kMaxS / 2];
 };
+static_assert(offsetof(SmallConsts, Y2) == offsetof(SmallConsts, M16) + 4 * kMaxLimb16, "staging order");
 
 // exponent of the vector held by lanes l, l^16, l^32, l^48 and the residue
 // bytes of this lane's 8 values for every modulus (byte e = k 8 kq + e)
@@ -126,14 +128,15 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                     else if (f == 3) v = P.K[t];
                     else if (f < 4 + kExtWords) v = P.c[t][f - 4];
                     else if (f == 4 + kExtWords) v = __float_as_uint(P.frcp[t]);
-                    else if (f == 5 + kExtWords) v = __float_as_uint(P.foff[t]);
-                    else v = __float_as_uint(P.finv[t]);
+                    else v = __float_as_uint(P.foff[t]);
                 }
             } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16) {
                 const int j = i - (kMaxS + 1) * nq;
                 v = P.W2[j / kMaxLimb16][j % kMaxLimb16];
-            } else {
+            } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16 + kMaxLimb16) {
                 v = P.M16[i - (kMaxS + 1) * nq - (kMaxS / 2) * kMaxLimb16];
+            } else {
+                v = P.Y2[i - (kMaxS + 1) * nq - (kMaxS / 2 + 1) * kMaxLimb16];
             }
             dst[i] = v;
         }
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t ra = acc_mod(ca[e], C0);
                     const uint32_t rb = two ? acc_mod(cb[e], C1) : 0u;
-                    acc[e].add2(ra, rb, C0.finv, C1.finv, Q.W2[t >> 1]);
+                    acc[e].add2(ra, rb, Q.Y2[t >> 1], Q.W2[t >> 1]);
                 }
             }
         }
