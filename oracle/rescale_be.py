@@ -38,9 +38,11 @@ Readings where the page leaves a step open (listed in the design doc as well):
    sigma = alpha Gamma is exact and the result is fl64(sigma V).
 4. One exponent per tensor of a batch (the encoding group of the persistent
    method is "the complete tensor").
-5. The chain is the three-direction pass Y = X x1 A x2 B x3 C of the page's
-   Eq. (1): every mode is contracted once, so no pending operator scales are
-   folded into later operators.
+5. A chain of depth d applies d operators, the i-th along direction
+   ((i - 1) mod 3) + 1: depth 3 is the three-direction pass of the page's
+   Eq. (1), longer chains revisit the directions in turn (Sec. 6).  A row
+   scale still pending on a direction is folded into the columns of the next
+   operator on it before that operator is encoded (Sec. 5.2).
 6. Non-finite input entries are outside the algorithm ("assume finite
    operands"); a tensor with any non-finite entry maps to an all-NaN output.
 
@@ -214,11 +216,39 @@ def drop_plan(b: int, rhos: Sequence[int], basis: Sequence[int], tau: int = 1):
     return g
 
 
+def chain_mode(i: int) -> int:
+    """Direction (0-based) of the i-th mode product: the chain visits the
+    three directions in turn, 1, 2, 3, 1, 2, ... (Sec. 6: a pass over all
+    three directions has depth 3, longer chains revisit them)."""
+    return i % 3
+
+
+def effective_operators(ops: Sequence[np.ndarray], b: int):
+    """The integer operators the chain actually applies (Sec. 5.2, the
+    paragraph after Eq. 28): a pending row scale 2^-f on a direction is
+    folded into the columns of the next operator on that direction before it
+    is encoded, and that operator's row exponents replace it.  Returns
+    (Abar list, f list, the exponents left pending on each direction); the
+    scales are powers of two, so the folding is exact."""
+    n = ops[0].shape[0]
+    pending = [np.zeros(n, dtype=np.int64) for _ in range(3)]
+    Abar, f = [], []
+    for i, M in enumerate(ops):
+        m = chain_mode(i)
+        Meff = np.ldexp(np.asarray(M, dtype=np.float64), -pending[m][None, :])
+        Ai, fi = encode_rows(Meff, b)
+        Abar.append(Ai)
+        f.append(fi)
+        pending[m] = fi
+    return Abar, f, pending
+
+
 def planner(ops: Sequence[np.ndarray], basis: Sequence[int]):
     """Planner: the largest b <= 53 whose drop plan (with restoration) passes,
-    with rho_i(b) from the operators encoded at b.  Returns (b, g) or None."""
+    with rho_i(b) from the effective operators encoded at b.  Returns
+    (b, g) or None."""
     for b in range(MAX_BITS, 0, -1):
-        rhos = [row_sum_bound(encode_rows(M, b)[0]) for M in ops]
+        rhos = [row_sum_bound(A) for A in effective_operators(ops, b)[0]]
         g = drop_plan(b, rhos, basis, 1)
         if g is not None:
             return b, g
@@ -243,7 +273,7 @@ def matrix_from_flat(a: np.ndarray, n: int) -> np.ndarray:
 
 
 def mode_product(T: np.ndarray, M: np.ndarray, mode: int) -> np.ndarray:
-    """T x_{mode+1} M: the operator's second index contracts the mode (exact int64)."""
+    """T x_{mode+1} M: the operator's second index contracts the mode."""
     if mode == 0:
         return np.einsum("ak,kjl->ajl", M, T)
     if mode == 1:
@@ -252,16 +282,18 @@ def mode_product(T: np.ndarray, M: np.ndarray, mode: int) -> np.ndarray:
 
 
 def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int):
-    """Plan and prepare the operators (Algorithm 7 lines 2-9): returns a dict
-    with basis, b, g, the integer operators and their row exponents, the
-    operator residues per modulus, and the dropped moduli per mode."""
+    """Plan and prepare the operators of a chain of depth d = len(ops_flat)
+    (Algorithm 7 lines 2-9): returns a dict with basis, b, g, the effective
+    integer operators and their row exponents, the exponents left pending on
+    each direction, the operator residues per modulus, and the dropped moduli
+    per mode."""
     basis = list(max_product_moduli(s))           # descending: 256 first
     ops = [matrix_from_flat(a, n) for a in ops_flat]
     plan = planner(ops, basis)
     if plan is None:
         return None
     b, g = plan
-    enc = [encode_rows(M, b) for M in ops]
+    Abar, f, pending = effective_operators(ops, b)
     drops = []
     for gi in g:
         L = list(basis)
@@ -271,8 +303,8 @@ def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int):
             dq.append(q)
             L.remove(q)
         drops.append(dq)
-    return dict(basis=basis, b=b, g=g, Abar=[e[0] for e in enc], f=[e[1] for e in enc],
-                Ares=[{p: centered_array(e[0], p) for p in basis} for e in enc], drops=drops, n=n, s=s)
+    return dict(basis=basis, b=b, g=g, Abar=Abar, f=f, F=pending,
+                Ares=[{p: centered_array(A, p) for p in basis} for A in Abar], drops=drops, n=n, s=s)
 
 
 def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np.ndarray:
@@ -289,8 +321,8 @@ def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np
     if keep is not None:
         keep["encoded"] = (Xbar, e)
         keep["stages"] = []
-    for i in range(3):
-        R = {p: centered_array(mode_product(R[p], plan["Ares"][i][p], i), p) for p in basis}
+    for i in range(len(plan["g"])):
+        R = {p: centered_array(mode_product(R[p], plan["Ares"][i][p], chain_mode(i)), p) for p in basis}
         if keep is not None:
             keep["stages"].append(("product", i, dict(R)))
         if plan["g"][i] > 0:
@@ -301,8 +333,8 @@ def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np
             R = base_extend(R, L, [p for p in basis if p not in L])
             if keep is not None:
                 keep["stages"].append(("extended", i, dict(R)))
-    f1, f2, f3 = plan["f"]
-    gamma_exp = -(f1[:, None, None] + f2[None, :, None] + f3[None, None, :])
+    F1, F2, F3 = plan["F"]   # Gamma (Eq. 28) from the scales left on each direction
+    gamma_exp = -(F1[:, None, None] + F2[None, :, None] + F3[None, None, :])
     sigma = np.ldexp(alpha, gamma_exp)
     if keep is not None:
         keep["alpha"] = alpha
@@ -310,7 +342,8 @@ def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np
 
 
 def rescale_be_chain(X: np.ndarray, ops_flat: Sequence[np.ndarray], n: int, s: int, batch: int):
-    """Y = X x1 A x2 B x3 C for `batch` tensors by OzII-RescaleBE; returns
+    """Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... (one operator per mode product, the
+    directions in turn) for `batch` tensors by OzII-RescaleBE; returns
     (Y flat, plan) or (None, None) when the planner finds no b."""
     plan = prepare_chain(ops_flat, n, s)
     if plan is None:
