@@ -197,7 +197,8 @@ def gemm_accuracy(dC, A, B, m, n, k, ta, tb, count=32, seed=4242):
 
 def chain_accuracy(Y, X, ops, n, count):
     """Normwise relative error of the first `count` chains
-    Y = X x1 A1 x2 A2 x3 A3 against the exact chain, in integers"""
+    Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... (operator i along direction i mod 3)
+    against the exact chain, in integers"""
     n3 = n ** 3
     mats = []
     for a in ops:
@@ -213,10 +214,11 @@ def chain_accuracy(Y, X, ops, n, count):
         e0 = int(e[nz].min()) if nz.any() else 0
         T = np.array([int(v) << int(z - e0) if f else 0 for v, z, f in zip(q.tolist(), e.tolist(), nz.tolist())],
                      dtype=object).reshape(n, n, n).transpose(2, 1, 0)   # T[k1, k2, k3]
-        T = np.tensordot(mats[0][0], T, axes=([1], [0]))                        # [a1, k2, k3]
-        T = np.tensordot(mats[1][0], T, axes=([1], [1])).transpose(1, 0, 2)    # [a1, a2, k3]
-        T = np.tensordot(mats[2][0], T, axes=([1], [2])).transpose(1, 2, 0)    # [a1, a2, a3]
-        esum = e0 + mats[0][1] + mats[1][1] + mats[2][1]
+        esum = e0
+        for i, (M, em) in enumerate(mats):
+            m = i % 3
+            T = np.moveaxis(np.tensordot(M, T, axes=([1], [m])), 0, m)
+            esum += em
         ref = np.array([_int_to_double(int(v), esum) for v in T.transpose(2, 1, 0).reshape(-1)])
         got = Y[t * n3:(t + 1) * n3]
         errs_num += float(np.sum((got - ref) ** 2))
@@ -457,16 +459,18 @@ def run_nonsquare(args):
 
 def rbe_valu_ops_per_entry(s, g):
     """Vector-ALU operations per tensor entry that the modular steps of an
-    OzII-RescaleBE chain take, counting one per 32-bit lane operation and two
-    per fp64 one: a centred reduction [x]_m is 3 (fma, floor, fma), a
-    mixed-radix or drop step [(x - y) c]_m is 5.  Per mode, the s products of
-    an entry are reduced; after modes 1 and 2, with k = s - g kept moduli,
-    RnsDrop takes sum_j (s - 1 - j) steps, the digits k (k - 1) / 2 steps and
-    BaseExtend g sums of k products plus a reduction; ReconstructFP64 takes
-    s (s - 1) / 2 digit steps, s - 1 fp64 Horner FMAs and one scaling.  The
-    encode and the integer MFMA products are not counted."""
-    ops = 3 * 3 * s
-    for gi in list(g)[:2]:
+    OzII-RescaleBE chain of depth d = len(g) take, counting one per 32-bit
+    lane operation and two per fp64 one: a centred reduction [x]_m is 3
+    (fma, floor, fma), a mixed-radix or drop step [(x - y) c]_m is 5.  Per
+    product, the s products of an entry are reduced; after every product but
+    the last, with k = s - g kept moduli, RnsDrop takes sum_j (s - 1 - j)
+    steps, the digits k (k - 1) / 2 steps and BaseExtend g sums of k
+    products plus a reduction; ReconstructFP64 takes s (s - 1) / 2 digit
+    steps, s - 1 fp64 Horner FMAs and one scaling.  The encode and the
+    integer MFMA products are not counted."""
+    g = list(g)
+    ops = 3 * s * len(g)
+    for gi in g[:-1]:
         k = s - gi
         ops += 5 * sum(s - 1 - j for j in range(gi)) + 5 * k * (k - 1) // 2 + gi * (k + 3)
     ops += 5 * s * (s - 1) // 2 + 2 * (s - 1) + 2
@@ -485,12 +489,13 @@ def run_chain_rbe(args):
     n3 = n ** 3
     log(f"[bench] chain_rbe: generating {batch} tensors of {n}^3 (seeded)")
     X = workloads.tensor_batch(n, batch, workloads.seed(5, 0))
-    ops = [workloads.real_matrix(n, n, workloads.seed(5, q)) for q in (1, 2, 3)]
+    depth = args.chain_depth
+    ops = [workloads.real_matrix(n, n, workloads.seed(5, q)) for q in range(1, depth + 1)]
     dX = torch.from_numpy(X).cuda()
     dY = torch.empty_like(dX)
     h = oz2.Handle(torch.cuda.current_stream())
     h.set_timing(True)
-    plan = h.chain_plan(ops[0], ops[1], ops[2], n, s)
+    plan = h.chain_plan(ops, n, s)
     launch_ms = []
 
     def step(record):
@@ -537,12 +542,16 @@ def run_chain_rbe(args):
     plan.close()
     h.close()
     return {
-        "metric": "tensor-mode chain GDoF/s (Y = X x1 A x2 B x3 C, OzII-RescaleBE persistent residues)",
+        "metric": ("tensor-mode chain GDoF/s (Y = X x1 A x2 B x3 C, OzII-RescaleBE persistent residues)"
+                   if depth == 3 else
+                   f"tensor-mode chain GDoF/s (depth {depth}: operator i along direction i mod 3, "
+                   "OzII-RescaleBE persistent residues)"),
         "value": round(value, 3),
         "unit": "GDoF/s",
         "ms_per_step": round(dt / args.steps * 1e3, 3),
         "dtype": "i8",
-        "config": {"workload": f"tensor_chain_rescale_be_n{n}_b{batch}_s{s}", "n": n, "batch": batch, "s": s,
+        "config": {"workload": f"tensor_chain_rescale_be_n{n}_b{batch}_s{s}" + (f"_d{depth}" if depth != 3 else ""),
+                   "n": n, "batch": batch, "s": s, "depth": depth,
                    "plan": info},
         "accuracy": accuracy,
         "roofline": roofline,
@@ -655,6 +664,7 @@ def main():
     ap.add_argument("--chain-cpu-tensors", type=int, default=256)
     ap.add_argument("--chain-rbe-cpu-tensors", type=int, default=384)
     ap.add_argument("--chain-acc-tensors", type=int, default=8)
+    ap.add_argument("--chain-depth", type=int, default=3, help="chain_rbe: operators (3 = one pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()

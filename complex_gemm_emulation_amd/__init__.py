@@ -73,8 +73,8 @@ def _raw():
             "oz2_operand_update": [P, P, P, I64],
             "oz2_operand_destroy": [P],
             "oz2_gemm_prepared": [P, P, P, P, P, P, I64],
-            "oz2_chain_plan_create": [P, I64, P, P, P, I, P],
-            "oz2_chain_plan_info": [P, P, P],
+            "oz2_chain_plan_create": [P, I64, I, P, I, P],
+            "oz2_chain_plan_info": [P, P, P, P],
             "oz2_chain_rescale_be": [P, P, P, P, I64],
             "oz2_chain_plan_destroy": [P],
         }
@@ -163,13 +163,16 @@ class ChainPlan:
     significand bits b, drop counts g and the operators' residues on the
     device, reusable for any number of tensor batches."""
 
+    MAX_DEPTH = 8
+
     def __init__(self, ptr, n, s):
         self._p = ptr
         self.n, self.s = n, s
+        d = ctypes.c_int()
         b = ctypes.c_int()
-        g = (ctypes.c_int * 3)()
-        _check("oz2_chain_plan_info", _raw().oz2_chain_plan_info(ptr, ctypes.byref(b), g))
-        self.b, self.g = b.value, tuple(g)
+        g = (ctypes.c_int * self.MAX_DEPTH)()
+        _check("oz2_chain_plan_info", _raw().oz2_chain_plan_info(ptr, ctypes.byref(d), ctypes.byref(b), g))
+        self.depth, self.b, self.g = d.value, b.value, tuple(g[:d.value])
 
     def close(self) -> None:
         if self._p is not None and self._p.value:
@@ -326,17 +329,18 @@ class Handle:
         _check("oz2_gemm_prepared", _raw().oz2_gemm_prepared(self._h, pa._p, pb._p, al, be, pc, ldc))
 
     # ------------------------------------------------- persistent chains
-    def chain_plan(self, A1, A2, A3, n, s) -> ChainPlan:
-        """Plan Y = X x1 A1 x2 A2 x3 A3 by OzII-RescaleBE
-        (oz2_chain_plan_create); A1..A3 are host n x n column-major arrays."""
-        mats = [np.ascontiguousarray(np.asarray(M, dtype=np.float64).reshape(-1)) for M in (A1, A2, A3)]
+    def chain_plan(self, ops, n, s) -> ChainPlan:
+        """Plan Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... by OzII-RescaleBE
+        (oz2_chain_plan_create): ops is a sequence of depth host n x n
+        column-major arrays, operator i contracting direction i mod 3."""
+        mats = [np.ascontiguousarray(np.asarray(M, dtype=np.float64).reshape(-1)) for M in ops]
         for M in mats:
             if M.size < n * n:
                 raise ValueError(f"operator holds {M.size} entries, n x n needs {n * n}")
         out = ctypes.c_void_p()
-        ptrs = [M.ctypes.data_as(ctypes.c_void_p) for M in mats]
+        ptrs = (ctypes.c_void_p * max(1, len(mats)))(*[M.ctypes.data_as(ctypes.c_void_p) for M in mats])
         _check("oz2_chain_plan_create",
-               _raw().oz2_chain_plan_create(self._h, n, ptrs[0], ptrs[1], ptrs[2], s, ctypes.byref(out)))
+               _raw().oz2_chain_plan_create(self._h, n, len(mats), ptrs, s, ctypes.byref(out)))
         return ChainPlan(out, n, s)
 
     def chain_rescale_be(self, plan: ChainPlan, X, Y, batch) -> None:

@@ -702,38 +702,39 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
     return OZ2_STATUS_SUCCESS;
 }
 
-int oz2_chain_plan_create(oz2_handle_t h, int64_t n, const double* A1, const double* A2, const double* A3,
-                          int num_moduli, oz2_chain_plan_t* out) {
+int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, int num_moduli,
+                          oz2_chain_plan_t* out) {
     if (!h) return -1;
     if (n < 1 || n > kChainN) return -2;
-    if (!A1) return -3;
-    if (!A2) return -4;
-    if (!A3) return -5;
-    if (num_moduli < kMinS || num_moduli > kChainMaxS) return -6;
-    if (!out) return -7;
+    if (depth < 1 || depth > kChainMaxD) return -3;
+    if (!ops) return -4;
+    for (int i = 0; i < depth; ++i)
+        if (!ops[i]) return -4;
+    if (num_moduli < kMinS || num_moduli > kChainMaxS) return -5;
+    if (!out) return -6;
     *out = nullptr;
     oz2_chain_plan* plan = new (std::nothrow) oz2_chain_plan();
     if (!plan) return OZ2_STATUS_ALLOC_FAILED;
-    constexpr size_t kOpsBytes = 3 * kChainMaxS * kChainN * kChainN;
+    const size_t ops_bytes = (size_t)depth * kChainMaxS * kChainN * kChainN;
     const size_t off_ops = align_up(sizeof(ChainTables));
     struct Host {
         ChainTables tab;
-        int8_t ops[kOpsBytes];
+        int8_t ops[kChainMaxD * kChainMaxS * kChainN * kChainN];
     };
     Host* host = new (std::nothrow) Host();
     if (!host) {
         delete plan;
         return OZ2_STATUS_ALLOC_FAILED;
     }
-    const double* ops[3] = {A1, A2, A3};
-    int st = chain_plan(num_moduli, (int)n, ops, &plan->params, &host->tab, host->ops);
-    if (!st && hipMalloc(&plan->mem, off_ops + kOpsBytes) != hipSuccess) {
+    int st = chain_plan(num_moduli, (int)n, depth, ops, &plan->params, &host->tab, host->ops);
+    if (st < 0) st = -4;  // a non-finite operator entry
+    if (!st && hipMalloc(&plan->mem, off_ops + ops_bytes) != hipSuccess) {
         (void)hipGetLastError();
         plan->mem = nullptr;
         st = OZ2_STATUS_ALLOC_FAILED;
     }
     if (!st && (hipMemcpy(plan->mem, &host->tab, sizeof(ChainTables), hipMemcpyHostToDevice) != hipSuccess ||
-                hipMemcpy((char*)plan->mem + off_ops, host->ops, kOpsBytes, hipMemcpyHostToDevice) != hipSuccess))
+                hipMemcpy((char*)plan->mem + off_ops, host->ops, ops_bytes, hipMemcpyHostToDevice) != hipSuccess))
         st = OZ2_STATUS_HIP_ERROR;
     delete host;
     if (st) {
@@ -747,11 +748,12 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, const double* A1, const dou
     return OZ2_STATUS_SUCCESS;
 }
 
-int oz2_chain_plan_info(oz2_chain_plan_t plan, int* b, int* g) {
+int oz2_chain_plan_info(oz2_chain_plan_t plan, int* depth, int* b, int* g) {
     if (!plan) return -1;
+    if (depth) *depth = plan->params.d;
     if (b) *b = plan->params.b;
     if (g)
-        for (int i = 0; i < 3; ++i) g[i] = plan->params.g[i];
+        for (int i = 0; i < plan->params.d; ++i) g[i] = plan->params.g[i];
     return OZ2_STATUS_SUCCESS;
 }
 

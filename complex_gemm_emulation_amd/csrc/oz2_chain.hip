@@ -163,19 +163,22 @@ __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint3
         for (int q = 0; q < 4; ++q) r[q][u] = unpack(pk[u], q);
     if (G0 >= 0 && G0 == G1)
         rescale_extend<G0>(0, r, T, at);
-    else if (mode == 0)
-        rescale_extend<G0>(g[0], r, T, at);
+    else if (G0 >= 0 && mode == 0)
+        rescale_extend<G0>(0, r, T, at);
+    else if (G0 >= 0)
+        rescale_extend<G1>(0, r, T, at);
     else
-        rescale_extend<G1>(g[1], r, T, at);
+        rescale_extend<-1>(g[mode], r, T, at);
 }
 
-// G0, G1: the drop counts after modes 1 and 2 when fixed at compile time,
-// -1 to read them from P.g
-template <int G0, int G1>
+// G0, G1: the drop counts after products 1 and 2 when fixed at compile time
+// (G0 = G1: after every product but the last), -1 to read them from P.g;
+// D: the depth when fixed at compile time, 0 to read it from P.d
+template <int G0, int G1, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 4)))
 void chain_kernel(ChainParams P) {
     __shared__ __attribute__((aligned(16))) int8_t buf[kSlots * kPlane];
-    __shared__ __attribute__((aligned(16))) int8_t ops[3][kSlots][kChainN * kChainN];
+    __shared__ __attribute__((aligned(16))) int8_t ops[3][kSlots][kChainN * kChainN];  // operator i in i mod 3
     __shared__ ChainTables KT;
     __shared__ unsigned long long smax;
 
@@ -193,12 +196,16 @@ void chain_kernel(ChainParams P) {
     for (int x = tid; x < (int)(sizeof(ChainTables) / 4); x += 512)
         ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
     const ChainTables* T = &KT;
-    for (int x = tid; x < 3 * kSlots * kChainN * kChainN / 8; x += 512) {
-        const int mode = x / (kSlots * 32), u = (x / 32) % kSlots, w = x % 32;
+    // operator i's residues (slot order) into LDS buffer i mod 3: 512 words of 8 bytes
+    auto stage_ops = [&](int i) {
+        static_assert(kSlots * kChainN * kChainN / 8 == 512, "one word per thread");
+        const int u = tid >> 5, w = tid & 31;
         long v = 0;
-        if (u >= first) v = *(const long*)(P.ops + ((mode * kSlots + (u - first)) * kChainN * kChainN) + 8 * w);
-        *(long*)(&ops[mode][u][8 * w]) = v;
-    }
+        if (u >= first) v = *(const long*)(P.ops + ((i * kSlots + (u - first)) * kChainN * kChainN) + 8 * w);
+        *(long*)(&ops[i % 3][u][8 * w]) = v;
+    };
+    const int d = D > 0 ? D : P.d;
+    for (int i = 0; i < 3 && i < d; ++i) stage_ops(i);
     if (tid == 0) smax = 0;
     __syncthreads();
 
@@ -251,65 +258,81 @@ void chain_kernel(ChainParams P) {
     }
     __syncthreads();
 
-    // ------------------------------------------------- modes 1 and 2, in place
+    // --------------------------------- every product but the last, in place
     const int a = lane & 15;   // MFMA row of A / column of B and of the output
     const int kq = lane >> 4;  // k group of the operands (0, 1 hold k < 16), output row group
 #pragma unroll 1
-    for (int mode = 0; mode < 2; ++mode) {
+    for (int mode = 0; mode + 1 < d; ++mode) {
         asm volatile("" ::: "memory");  // keep the table reads inside the loop
         uint32_t pk0[kSlots], pk1[kSlots];
-        tile_products(buf, ops[mode], T, wave, a, kq, pk0);
-        tile_products(buf, ops[mode], T, wave + 8, a, kq, pk1);
+        tile_products(buf, ops[mode % 3], T, wave, a, kq, pk0);
+        tile_products(buf, ops[mode % 3], T, wave + 8, a, kq, pk1);
         __syncthreads();  // every plane read before any is overwritten
         // next layout: fibre (t + 16 a), index 4 kq .. 4 kq + 3
         rescale_tile<G0, G1>(mode, P.g, pk0, T, buf + (wave + 16 * a) * kChainN + 4 * kq);
         asm volatile("" ::: "memory");  // one tile at a time
         rescale_tile<G0, G1>(mode, P.g, pk1, T, buf + (wave + 8 + 16 * a) * kChainN + 4 * kq);
+        asm volatile("" ::: "memory");
+        // operator mode + 3 into the buffer this product read (before the
+        // barrier above); it is next read three products later
+        if (mode + 3 < d) stage_ops(mode + 3);
         __syncthreads();
     }
 
-    // ---------------------------------------- mode 3 and ReconstructFP64
-    // (Algorithm 5): entries (a1, a2, a3) = (4 kq + q, t, a); sigma = alpha Gamma
+    // -------------------------------------- last product and ReconstructFP64
+    // (Algorithm 5), sigma = alpha Gamma.  Every product moves the contracted
+    // index out of layout position 0 and appends its output index, so after
+    // d products position p holds direction (p + d) mod 3; the lane's entries
+    // sit at positions (4 kq + q, t, a).
     const double alpha = ldexp(P.Qd, -e);
+    const int r3 = d % 3;
+    const int dir0 = r3, dir1 = (1 + r3) % 3, dir2 = (2 + r3) % 3;
+    const int64_t n2 = (int64_t)n * n;
+    const int64_t st0 = dir0 == 0 ? 1 : dir0 == 1 ? n : n2;
+    const int64_t st1 = dir1 == 0 ? 1 : dir1 == 1 ? n : n2;
+    const int64_t st2 = dir2 == 0 ? 1 : dir2 == 1 ? n : n2;
+    const int* F0 = T->fexp[dir0];
+    const int* F1 = T->fexp[dir1];
+    const int* F2 = T->fexp[dir2];
 #pragma unroll 1
     for (int tt = 0; tt < 2; ++tt) {
         asm volatile("" ::: "memory");
         const int t = wave + 8 * tt;
         uint32_t pk[kSlots];
-        tile_products(buf, ops[2], T, t, a, kq, pk);
-        float d[4][kSlots];
+        tile_products(buf, ops[(d - 1) % 3], T, t, a, kq, pk);
+        float dg[4][kSlots];
 #pragma unroll
         for (int u = 0; u < kSlots; ++u)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) d[q][u] = unpack(pk[u], q);
+            for (int q = 0; q < 4; ++q) dg[q][u] = unpack(pk[u], q);
 #pragma unroll
         for (int i = 0; i < kSlots - 1; ++i)
 #pragma unroll
             for (int j = i + 1; j < kSlots; ++j) {
                 const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) d[q][j] = cmod((d[q][j] - d[q][i]) * iv, m, rm);
+                for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
             }
         double V[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) V[q] = (double)d[q][kSlots - 1];
+        for (int q = 0; q < 4; ++q) V[q] = (double)dg[q][kSlots - 1];
 #pragma unroll
         for (int j = kSlots - 2; j >= 0; --j) {
             const double m = (double)T->mod[j];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)d[q][j]);
+            for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)dg[q][j]);
         }
         // the values are complete here (the compiler would otherwise sink
         // each entry's whole digit computation into its guarded store)
 #pragma unroll
         for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(V[q]));
         if (t < n && a < n) {
-            const int f23 = T->fexp[1][t] + T->fexp[2][a];
-            double* y = Y + (int64_t)n * (t + (int64_t)n * a);
+            const int f12 = F1[t] + F2[a];
+            double* y = Y + t * st1 + a * st2;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int a1 = 4 * kq + q;
-                if (a1 < n) y[a1] = ldexp(alpha, -(T->fexp[0][a1] + f23)) * V[q];
+                const int p0 = 4 * kq + q;
+                if (p0 < n) y[p0 * st0] = ldexp(alpha, -(F0[p0] + f12)) * V[q];
             }
         }
     }
@@ -320,20 +343,33 @@ void chain_kernel(ChainParams P) {
 hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
     if (P.n < 1 || P.n > kChainN || P.s < kMinS || P.s > kChainMaxS || P.batch < 1 || P.batch > INT32_MAX)
         return hipErrorInvalidValue;
-    if (P.g[2] != 0 || P.g[0] < 0 || P.g[1] < 0 || P.g[0] >= P.s || P.g[1] >= P.s) return hipErrorInvalidValue;
+    if (P.d < 1 || P.d > kChainMaxD || P.g[P.d - 1] != 0) return hipErrorInvalidValue;
+    for (int i = 0; i + 1 < P.d; ++i)
+        if (P.g[i] < 0 || P.g[i] >= P.s) return hipErrorInvalidValue;
+    // compile-time drop counts for the usual plans of 16^3 tensors (7 after
+    // every product with 16 or 14 moduli, 6 with 12, 4 with 8; 4 then 5 for
+    // a depth-3 chain with 10) and a compile-time depth for one pass over the
+    // three directions; any other plan takes a guarded or run-time instance
+    bool same = P.d >= 2;
+    for (int i = 1; i + 1 < P.d; ++i) same = same && P.g[i] == P.g[0];
+    const int g0 = same ? P.g[0] : -1;
     const dim3 grid((unsigned)P.batch), block(512);
-    // compile-time drop counts for the plans of 16^3 tensors with 16, 14,
-    // 12, 10 and 8 moduli; any other plan takes the guarded instance
-    if (P.g[0] == 7 && P.g[1] == 7)
-        hipLaunchKernelGGL((chain_kernel<7, 7>), grid, block, 0, st, P);
-    else if (P.g[0] == 6 && P.g[1] == 6)
-        hipLaunchKernelGGL((chain_kernel<6, 6>), grid, block, 0, st, P);
-    else if (P.g[0] == 4 && P.g[1] == 5)
-        hipLaunchKernelGGL((chain_kernel<4, 5>), grid, block, 0, st, P);
-    else if (P.g[0] == 4 && P.g[1] == 4)
-        hipLaunchKernelGGL((chain_kernel<4, 4>), grid, block, 0, st, P);
-    else
-        hipLaunchKernelGGL((chain_kernel<-1, -1>), grid, block, 0, st, P);
+    if (P.d == 3) {
+        if (g0 == 7)
+            hipLaunchKernelGGL((chain_kernel<7, 7, 3>), grid, block, 0, st, P);
+        else if (g0 == 6)
+            hipLaunchKernelGGL((chain_kernel<6, 6, 3>), grid, block, 0, st, P);
+        else if (g0 == 4)
+            hipLaunchKernelGGL((chain_kernel<4, 4, 3>), grid, block, 0, st, P);
+        else if (P.g[0] == 4 && P.g[1] == 5)
+            hipLaunchKernelGGL((chain_kernel<4, 5, 3>), grid, block, 0, st, P);
+        else
+            hipLaunchKernelGGL((chain_kernel<-1, -1, 3>), grid, block, 0, st, P);
+    } else if (g0 == 7) {
+        hipLaunchKernelGGL((chain_kernel<7, 7, 0>), grid, block, 0, st, P);
+    } else {
+        hipLaunchKernelGGL((chain_kernel<-1, -1, 0>), grid, block, 0, st, P);
+    }
     return hipGetLastError();
 }
 

@@ -5,6 +5,10 @@
 //  - Sec. 5.1 Eq. (27) and Algorithm 5: every operator row is one encoding
 //    group, f = b - E with 2^(E-1) <= max|row| < 2^E, rounded to nearest
 //    (ties to even);
+//  - Sec. 5.2 (after Eq. 28): in a chain longer than one pass, the row
+//    scales 2^-f still pending on a direction multiply the columns of the
+//    next operator on that direction before it is encoded; its own row
+//    exponents then replace them (operator i acts on direction i mod 3);
 //  - Sec. 4.3 Eq. (21): rho_i = maximal absolute row sum of the integer
 //    operator;
 //  - Algorithm 2 (DropPlan) with restoration, Algorithm 3 (Planner): the
@@ -60,12 +64,14 @@ UBig mul_u64(const UBig& a, uint64_t m) {
 
 UBig pow2(int e) { return UBig::from_u64(1).shl(e); }
 
-// Encode one operator at b (rows = groups): integer entries and row exponents
-bool encode_rows(const double* A, int n, int b, int64_t* Abar, int* f) {
+// Encode one operator at b (rows = groups) after folding the pending column
+// scales 2^-pend[k] into it (exact: powers of two): integer entries and row
+// exponents
+bool encode_rows(const double* A, const int* pend, int n, int b, int64_t* Abar, int* f) {
     for (int a = 0; a < n; ++a) {
         double mx = 0.0;
         for (int k = 0; k < n; ++k) {
-            const double x = A[a + (int64_t)n * k];
+            const double x = std::ldexp(A[a + (int64_t)n * k], -pend[k]);
             if (!std::isfinite(x)) return false;
             mx = std::fmax(mx, std::fabs(x));
         }
@@ -78,7 +84,7 @@ bool encode_rows(const double* A, int n, int b, int64_t* Abar, int* f) {
         (void)std::frexp(mx, &E);
         f[a] = b - E;
         for (int k = 0; k < n; ++k)
-            Abar[a * n + k] = (int64_t)std::nearbyint(std::ldexp(A[a + (int64_t)n * k], f[a]));
+            Abar[a * n + k] = (int64_t)std::nearbyint(std::ldexp(std::ldexp(A[a + (int64_t)n * k], -pend[k]), f[a]));
     }
     return true;
 }
@@ -93,19 +99,20 @@ uint64_t row_sum_bound(const int64_t* Abar, int n) {
     return rho;
 }
 
-// DropPlan with restoration (tau = 1); false on a failed range check
-bool drop_plan(int b, const uint64_t rho[3], const int* basis, int s, int g[3]) {
+// DropPlan with restoration (tau = 1) over d products; false on a failed
+// range check
+bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* g) {
     UBig PL = UBig::from_u64(1);
     for (int i = 0; i < s; ++i) PL.mul_small((uint32_t)basis[i]);
     const UBig P = PL;
     const UBig two_b = pow2(b);
     UBig B = two_b;
     int nL = s;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < d; ++i) {
         B = mul_u64(B, rho[i]);
         if (B.shl(1).cmp(PL) >= 0) return false;
         g[i] = 0;
-        if (i < 2) {
+        if (i < d - 1) {
             while (nL > 1) {
                 const uint32_t q = (uint32_t)basis[nL - 1];  // smallest available modulus
                 const UBig Bq0 = B.div_small(q);
@@ -127,43 +134,53 @@ bool drop_plan(int b, const uint64_t rho[3], const int* basis, int s, int g[3]) 
 
 }  // namespace
 
-int chain_plan(int s, int n, const double* const ops[3], ChainParams* P, ChainTables* T, int8_t* ops_residues) {
+int chain_plan(int s, int n, int d, const double* const* ops, ChainParams* P, ChainTables* T,
+               int8_t* ops_residues) {
     const ModuliPlan* pl = moduli_plan(s);
-    if (!pl || s > kChainMaxS || n < 1 || n > kChainN) return OZ2_STATUS_INTERNAL;
+    if (!pl || s > kChainMaxS || n < 1 || n > kChainN || d < 1 || d > kChainMaxD) return OZ2_STATUS_INTERNAL;
     if (pl->mod[0] != 256) return OZ2_STATUS_INTERNAL;
     for (int i = 1; i < s; ++i)
         if (pl->mod[i] % 2 == 0) return OZ2_STATUS_INTERNAL;
-    int64_t Abar[3][kChainN * kChainN];
-    int f[3][kChainN];
-    int b = 53, g[3] = {0, 0, 0};
+    for (int i = 0; i < d; ++i)
+        for (int x = 0; x < n * n; ++x)
+            if (!std::isfinite(ops[i][x])) return -(i + 1);
+    int64_t Abar[kChainMaxD][kChainN * kChainN];
+    int f[kChainMaxD][kChainN];
+    int pend[3][kChainN];
+    int b = 53, g[kChainMaxD] = {};
     for (; b >= 1; --b) {
-        uint64_t rho[3];
-        for (int i = 0; i < 3; ++i) {
-            if (!encode_rows(ops[i], n, b, Abar[i], f[i])) return -(3 + i);
+        uint64_t rho[kChainMaxD];
+        std::memset(pend, 0, sizeof(pend));
+        bool ok = true;
+        for (int i = 0; i < d && ok; ++i) {
+            // the effective operator: pending scales of its direction folded in
+            ok = encode_rows(ops[i], pend[i % 3], n, b, Abar[i], f[i]);
             rho[i] = row_sum_bound(Abar[i], n);
+            std::memcpy(pend[i % 3], f[i], sizeof(int) * n);
         }
-        if (drop_plan(b, rho, pl->mod, s, g)) break;
+        if (ok && drop_plan(b, d, rho, pl->mod, s, g)) break;
     }
     if (b < 1) return OZ2_STATUS_RANGE;
     P->n = n;
     P->s = s;
     P->b = b;
-    for (int i = 0; i < 3; ++i) P->g[i] = g[i];
+    P->d = d;
+    for (int i = 0; i < kChainMaxD; ++i) P->g[i] = i < d ? g[i] : 0;
     // alpha multiplier: the dropped moduli (the g smallest, smallest first)
     // in drop order, each product rounded to double
     double Qd = 1.0;
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < d; ++i)
         for (int j = 0; j < g[i]; ++j) Qd = Qd * (double)pl->mod[s - 1 - j];
     P->Qd = Qd;
-    std::memset(ops_residues, 0, 3 * kChainMaxS * kChainN * kChainN);
-    for (int i = 0; i < 3; ++i) {
-        for (int a = 0; a < kChainN; ++a) T->fexp[i][a] = a < n ? f[i][a] : 0;
+    std::memset(ops_residues, 0, (size_t)d * kChainMaxS * kChainN * kChainN);
+    for (int m = 0; m < 3; ++m)
+        for (int a = 0; a < kChainN; ++a) T->fexp[m][a] = a < n ? pend[m][a] : 0;
+    for (int i = 0; i < d; ++i)
         for (int q = 0; q < s; ++q)
             for (int a = 0; a < n; ++a)
                 for (int k = 0; k < n; ++k)
                     ops_residues[((i * kChainMaxS + q) * kChainN + a) * kChainN + k] =
                         (int8_t)centered(Abar[i][a * n + k], pl->mod[q]);
-    }
     // kernel tables in slot order: the s moduli right-aligned in kChainMaxS
     // slots (descending), the unused leading slots with the modulus 1
     const int first = kChainMaxS - s;

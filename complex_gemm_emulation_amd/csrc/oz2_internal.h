@@ -111,18 +111,20 @@ struct SmallParams {
 
 // Persistent tensor-mode chain, OzII-RescaleBE ("You Only Convert Twice:
 // Ozaki Scheme II for Chained Tensor Mode Products", Sec. 5.2 and
-// Algorithm 7): Y = X x1 A1 x2 A2 x3 A3 for a batch of n x n x n tensors,
-// one block per tensor, residues in LDS for the whole chain (oz2_chain.hip).
+// Algorithm 7): Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... for a batch of
+// n x n x n tensors, d operators applied along the directions in turn, one
+// block per tensor, residues in LDS for the whole chain (oz2_chain.hip).
 constexpr int kChainN = 16;      // tensor side of the kernel's tiles (n <= 16 is zero padded)
-constexpr int kChainMaxS = 16;   // moduli: two LDS buffers of 16 residue planes (128 KiB)
+constexpr int kChainMaxS = 16;   // moduli: one LDS buffer of 16 residue planes (64 KiB)
+constexpr int kChainMaxD = 8;    // chain depth: operators
 struct ChainParams {
     const double* X;             // [batch][n^3] column-major tensors
     double* Y;
     int64_t batch;
-    int n, s, b;
-    int g[3];                    // moduli dropped after mode i (g[2] = 0)
+    int n, s, b, d;
+    int g[kChainMaxD];           // moduli dropped after product i (g[d - 1] = 0)
     double Qd;                   // fl64 product of the dropped moduli, in drop order
-    const int8_t* ops;           // device [3][kChainMaxS][16][16] centred residues of the integer operators
+    const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators
     const float* tab;            // device ChainTables (below)
 };
 
@@ -133,14 +135,17 @@ struct ChainTables {
     float omega[kChainMaxS][kChainMaxS];  // [prod_{l<i} m_l]_{m_j}, centred
     float mod[kChainMaxS];                // m_u
     float rmod[kChainMaxS];               // fl32(1 / m_u)
-    int fexp[3][kChainN];                 // operator row exponents f_{i,a} (0 for padding rows)
+    int fexp[3][kChainN];                 // row exponents left pending on each direction (0 for padding)
 };
 
-// Host planning of the chain (Algorithms 2, 3 and 5 of the chain page):
-// the significand bits b, the drop counts g, and the integer operators'
-// row exponents and centred residues.  ops: three HOST n x n column-major
-// operators.  Returns 0, or OZ2_STATUS_RANGE when no b in [1, 53] passes.
-int chain_plan(int s, int n, const double* const ops[3], ChainParams* P, ChainTables* T, int8_t* ops_residues);
+// Host planning of the chain (Algorithms 2, 3 and 5 of the chain page, with
+// the pending row scales of a direction folded into the next operator on
+// it, Sec. 5.2): the significand bits b, the drop counts g, and the
+// effective integer operators' residues.  ops: d HOST n x n column-major
+// operators.  Returns 0, -(i + 1) for a non-finite entry in operator i, or
+// OZ2_STATUS_RANGE when no b in [1, 53] passes.
+int chain_plan(int s, int n, int d, const double* const* ops, ChainParams* P, ChainTables* T,
+               int8_t* ops_residues);
 
 struct CrtTestParams {
     const uint8_t* R;  // [s][count]

@@ -208,34 +208,45 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
 /* ---------------------------------------------------------------------
  * Persistent tensor-mode chains (OzII-RescaleBE, "You Only Convert Twice:
  * Ozaki Scheme II for Chained Tensor Mode Products", Sec. 5.2, Algorithm 7):
- * Y = X x1 A1 x2 A2 x3 A3 (Y_abc = sum A1_ai A2_bj A3_ck X_ijk) for a batch
- * of n x n x n tensors (column-major X[i + n j + n^2 k], tensor t at
- * X + t n^3) with shared n x n operators.  The tensor is encoded once with
- * one power-of-two exponent (b significand bits), stays in residue form
- * through all three mode products -- after modes 1 and 2 the g_i smallest
+ * Y = X x1 A1 x2 A2 x3 A3 x1 A4 x2 A5 ... for a batch of n x n x n tensors
+ * (column-major X[i + n j + n^2 k], tensor t at X + t n^3) with shared
+ * n x n operators.  A chain of depth d applies d operators; operator i
+ * (1-based) contracts direction ((i - 1) mod 3) + 1, so depth 3 is
+ * Y_abc = sum A1_ai A2_bj A3_ck X_ijk and longer chains revisit the
+ * directions in turn (Sec. 6).  The tensor is encoded once with one
+ * power-of-two exponent (b significand bits), stays in residue form through
+ * all d mode products -- after every product but the last the g_i smallest
  * moduli are dropped by rounded division (Sec. 2.3.1 Eq. 15, Algorithm 1)
  * and restored by mixed-radix base extension (Sec. 4.4 Eq. 26,
- * Algorithm 4) -- and is reconstructed once (Algorithm 5).  The residue
- * basis is the max-product modulus set for num_moduli, descending.
- * Limits of this implementation: 1 <= n <= 16, 2 <= num_moduli <= 16.
+ * Algorithm 4) -- and is reconstructed once (Algorithm 5).  Row scales still
+ * pending on a direction are folded into the columns of the next operator
+ * on it before that operator is encoded (Sec. 5.2, after Eq. 28).  The
+ * residue basis is the max-product modulus set for num_moduli, descending.
+ * Limits of this implementation: 1 <= n <= OZ2_CHAIN_MAX_N,
+ * 1 <= depth <= OZ2_CHAIN_MAX_DEPTH, 2 <= num_moduli <= OZ2_CHAIN_MAX_MODULI.
  * Results are deterministic; parity with the CPU oracle is bitwise.
  * ------------------------------------------------------------------- */
+#define OZ2_CHAIN_MAX_N 16
+#define OZ2_CHAIN_MAX_DEPTH 8
+#define OZ2_CHAIN_MAX_MODULI 16
 typedef struct oz2_chain_plan* oz2_chain_plan_t;
 
 /* Plan a chain (Algorithms 2, 3; host work): the largest b <= 53 whose
- * greedy drop schedule passes every range check for these operators, the
- * drop counts g, and the operators' row exponents and residues, which are
- * copied to DEVICE memory owned by the plan (12 KiB).  A1, A2, A3: HOST
- * n x n column-major operators of modes 1, 2 and 3 (finite; a non-finite
- * entry gives -3, -4 or -5).  Argument numbers: h 1, n 2, A1 3, A2 4, A3 5,
- * num_moduli 6, out 7.  OZ2_STATUS_RANGE when no b in [1, 53] passes.
- * The plan can be reused for any number of tensors and calls. */
-int oz2_chain_plan_create(oz2_handle_t h, int64_t n, const double* A1, const double* A2,
-                          const double* A3, int num_moduli, oz2_chain_plan_t* out);
+ * greedy drop schedule passes every range check for the effective
+ * operators, the drop counts g, and the effective operators' residues and
+ * the row exponents left pending on each direction, which are copied to
+ * DEVICE memory owned by the plan (2.3 KiB + depth * 4 KiB).  ops: HOST
+ * array of depth pointers to HOST n x n column-major operators (finite).
+ * Argument numbers: h 1, n 2, depth 3, ops 4 (also a NULL entry or a
+ * non-finite operator entry), num_moduli 5, out 6.  OZ2_STATUS_RANGE when
+ * no b in [1, 53] passes.  The plan can be reused for any number of tensors
+ * and calls. */
+int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, int num_moduli,
+                          oz2_chain_plan_t* out);
 
-/* The planned significand bits b and drop counts g[3] (either pointer may
- * be NULL). */
-int oz2_chain_plan_info(oz2_chain_plan_t plan, int* b, int* g);
+/* The plan's depth, significand bits b and drop counts g[0 .. depth - 1]
+ * (g[depth - 1] = 0); any pointer may be NULL, g must hold depth ints. */
+int oz2_chain_plan_info(oz2_chain_plan_t plan, int* depth, int* b, int* g);
 
 /* Run the planned chain on `batch` tensors: X and Y are DEVICE arrays of
  * batch * n^3 doubles that must not overlap.  One kernel on h's stream

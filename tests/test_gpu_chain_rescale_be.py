@@ -1,7 +1,7 @@
 """GPU parity of the persistent tensor-mode chain (oz2_chain_plan_create /
 oz2_chain_rescale_be, OzII-RescaleBE of "You Only Convert Twice: Ozaki
-Scheme II for Chained Tensor Mode Products", Algorithm 7) against the CPU
-oracle (oracle/rescale_be.py), through the C ABI.
+Scheme II for Chained Tensor Mode Products", Algorithm 7, chains of depth
+1 to 8) against the CPU oracle (oracle/rescale_be.py), through the C ABI.
 
 Bar: the plan (b, g) equals the oracle planner's, and every output entry is
 bit-identical to the oracle's: every step is exact integer arithmetic except
@@ -37,8 +37,8 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _ops(n, seed, dist="uniform", phi=0.5):
-    return [workloads.real_matrix(n, n, seed + q, dist, phi) for q in range(3)]
+def _ops(n, seed, dist="uniform", phi=0.5, d=3):
+    return [workloads.real_matrix(n, n, seed + q, dist, phi) for q in range(d)]
 
 
 def _check_bitwise(got, want, label):
@@ -72,8 +72,8 @@ def test_chain_matches_oracle_bitwise(handle, n, s, batch, dist):
         X = workloads.real_matrix(n ** 3, batch, 8200 + n + s, "phi", 2.0)
     want, plan = rb.rescale_be_chain(X, ops, n, s, batch)
     assert plan is not None
-    with handle.chain_plan(ops[0], ops[1], ops[2], n, s) as cp:
-        assert (cp.b, list(cp.g)) == (plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
+    with handle.chain_plan(ops, n, s) as cp:
+        assert (cp.depth, cp.b, list(cp.g)) == (3, plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
         dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
         handle.chain_rescale_be(cp, to_dev(X), dY, batch)
         torch.cuda.synchronize()
@@ -93,7 +93,7 @@ def test_chain_edge_tensors(handle):
     X[2 * n3:3 * n3] *= 2.0 ** -1060          # subnormal entries
     X[3 * n3:4 * n3] = workloads.real_matrix(n3, 1, 8302, "phi", 6.0)
     want, plan = rb.rescale_be_chain(X, ops, n, s, 5)
-    with handle.chain_plan(ops[0], ops[1], ops[2], n, s) as cp:
+    with handle.chain_plan(ops, n, s) as cp:
         dY = torch.empty(n3 * 5, dtype=torch.float64, device="cuda")
         handle.chain_rescale_be(cp, to_dev(X), dY, 5)
         torch.cuda.synchronize()
@@ -113,7 +113,7 @@ def test_chain_full_workload_sampled(handle):
     X = workloads.tensor_batch(n, batch, workloads.seed(5, 0))
     ops = [workloads.real_matrix(n, n, workloads.seed(5, q)) for q in (1, 2, 3)]
     plan = rb.prepare_chain(ops, n, s)
-    with handle.chain_plan(ops[0], ops[1], ops[2], n, s) as cp:
+    with handle.chain_plan(ops, n, s) as cp:
         dY = torch.empty(n3 * batch, dtype=torch.float64, device="cuda")
         handle.chain_rescale_be(cp, to_dev(X), dY, batch)
         torch.cuda.synchronize()
@@ -126,23 +126,60 @@ def test_chain_full_workload_sampled(handle):
         _check_bitwise(Y[t * n3:(t + 1) * n3], want, f"tensor {t}")
 
 
+DEPTH_CASES = [
+    # n, s, depth, batch
+    (16, 16, 1, 2),
+    (16, 16, 2, 2),
+    (16, 16, 4, 2),   # every g = 7: the compile-time instance
+    (16, 14, 5, 2),
+    (8, 16, 8, 3),    # the page's deepest chain; the last drop count differs
+    (5, 12, 6, 2),
+    (16, 16, 7, 1),
+]
+
+
+@pytest.mark.parametrize("n,s,d,batch", DEPTH_CASES, ids=[f"n{c[0]}s{c[1]}d{c[2]}" for c in DEPTH_CASES])
+def test_chain_depth_matches_oracle_bitwise(handle, n, s, d, batch):
+    """Longer chains revisit the directions (operator i along direction
+    i mod 3), with the pending row scales folded into the next operator on a
+    direction; every layout rotation d mod 3 is covered."""
+    import torch
+    _say(f"[chain depth] n={n} s={s} d={d} batch={batch}")
+    ops = _ops(n, 8500 + 10 * n + d, d=d)
+    X = workloads.tensor_batch(n, batch, 8600 + n + d)
+    want, plan = rb.rescale_be_chain(X, ops, n, s, batch)
+    assert plan is not None
+    with handle.chain_plan(ops, n, s) as cp:
+        assert (cp.depth, cp.b, list(cp.g)) == (d, plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
+        dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
+        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
+        torch.cuda.synchronize()
+    _check_bitwise(from_dev(dY), want, f"n={n} s={s} d={d}")
+
+
 def test_chain_argument_errors(handle):
     import ctypes
     import complex_gemm_emulation_amd as oz2
     lib = oz2.lib()
     A = np.eye(4)
     p = A.ctypes.data_as(ctypes.c_void_p)
+    three = (ctypes.c_void_p * 3)(p, p, p)
     out = ctypes.c_void_p()
-    assert lib.oz2_chain_plan_create(handle._h, 0, p, p, p, 8, ctypes.byref(out)) == -2
-    assert lib.oz2_chain_plan_create(handle._h, 17, p, p, p, 8, ctypes.byref(out)) == -2
-    assert lib.oz2_chain_plan_create(handle._h, 4, None, p, p, 8, ctypes.byref(out)) == -3
-    assert lib.oz2_chain_plan_create(handle._h, 4, p, p, p, 17, ctypes.byref(out)) == -6
+    assert lib.oz2_chain_plan_create(handle._h, 0, 3, three, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 17, 3, three, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 4, 0, three, 8, ctypes.byref(out)) == -3
+    assert lib.oz2_chain_plan_create(handle._h, 4, 9, three, 8, ctypes.byref(out)) == -3
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, None, 8, ctypes.byref(out)) == -4
+    holey = (ctypes.c_void_p * 3)(p, None, p)
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, holey, 8, ctypes.byref(out)) == -4
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, 17, ctypes.byref(out)) == -5
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, 8, None) == -6
     bad = np.eye(4)
     bad[1, 2] = np.inf
-    assert lib.oz2_chain_plan_create(handle._h, 4, p, bad.ctypes.data_as(ctypes.c_void_p), p, 8,
-                                     ctypes.byref(out)) == -4
+    badp = (ctypes.c_void_p * 3)(p, bad.ctypes.data_as(ctypes.c_void_p), p)
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, badp, 8, ctypes.byref(out)) == -4
     assert not out.value
-    with handle.chain_plan(A, A, A, 4, 8) as cp:
+    with handle.chain_plan([A, A, A], 4, 8) as cp:
         assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, 0) == 0   # empty batch
         assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, 1) == -3
         assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, -1) == -5
