@@ -1,12 +1,15 @@
 // oz2_chain.hip -- persistent Ozaki scheme II for chained tensor mode
-// products (OzII-RescaleBE): Y = X x1 A1 x2 A2 x3 A3 for a batch of
-// n x n x n tensors, every step of the chain in one kernel.
+// products (OzII-RescaleBE): Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... (depth d <= 8,
+// operator i along direction i mod 3) for a batch of n x n x n tensors,
+// every step of the chain in one kernel.
 //
 // "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products":
 //  - Sec. 5.2 and Algorithm 7: the tensor is encoded once with one exponent,
 //    multiplied mode after mode on its residue planes, rescaled by g_i
 //    moduli (Algorithm 1, Eq. 15) and base-extended (Algorithm 4, Eq. 26)
-//    after each non-final mode, and reconstructed once;
+//    after each non-final mode, and reconstructed once; the pending row
+//    scales of a direction are folded into the next operator on it on the
+//    host, before encoding;
 //  - Algorithm 5: Encode (rounding to nearest, ties to even), ToRns and
 //    ReconstructFP64 (centred mixed-radix digits, FP64 Horner, scaling by
 //    alpha * Gamma, Eq. 28);
@@ -27,6 +30,9 @@
 // registers.  The output is stored so that the next mode's contraction
 // index is the contiguous one: the four entries of a lane are four
 // consecutive bytes of the next layout (one 32-bit LDS write per modulus).
+// Each product thus rotates the layout by one direction, which is what a
+// chain visiting the directions in turn needs; the final store undoes the
+// rotation.  The operators' residues cycle through three LDS slots.
 //
 // Moduli sit right-aligned in 16 slots, descending, so that the smallest
 // (the ones dropped) are always slots 15, 14, ... at compile time; unused
