@@ -38,11 +38,12 @@ Readings where the page leaves a step open (listed in the design doc as well):
    sigma = alpha Gamma is exact and the result is fl64(sigma V).
 4. One exponent per tensor of a batch (the encoding group of the persistent
    method is "the complete tensor").
-5. A chain of depth d applies d operators, the i-th along direction
-   ((i - 1) mod 3) + 1: depth 3 is the three-direction pass of the page's
-   Eq. (1), longer chains revisit the directions in turn (Sec. 6).  A row
-   scale still pending on a direction is folded into the columns of the next
-   operator on it before that operator is encoded (Sec. 5.2).
+5. A chain of depth d applies d operators, by default the i-th along
+   direction ((i - 1) mod 3) + 1: depth 3 is the three-direction pass of the
+   page's Eq. (1), longer chains revisit the directions in turn (Sec. 6);
+   Algorithm 7 also takes any sequence of modes, and so does this oracle.
+   A row scale still pending on a direction is folded into the columns of
+   the next operator on it before that operator is encoded (Sec. 5.2).
 6. Non-finite input entries are outside the algorithm ("assume finite
    operands"); a tensor with any non-finite entry maps to an all-NaN output.
 
@@ -223,18 +224,25 @@ def chain_mode(i: int) -> int:
     return i % 3
 
 
-def effective_operators(ops: Sequence[np.ndarray], b: int):
+def default_modes(d: int) -> list:
+    """The directions in turn: 0, 1, 2, 0, 1, ..."""
+    return [chain_mode(i) for i in range(d)]
+
+
+def effective_operators(ops: Sequence[np.ndarray], b: int, modes: Sequence[int] | None = None):
     """The integer operators the chain actually applies (Sec. 5.2, the
     paragraph after Eq. 28): a pending row scale 2^-f on a direction is
     folded into the columns of the next operator on that direction before it
     is encoded, and that operator's row exponents replace it.  Returns
     (Abar list, f list, the exponents left pending on each direction); the
-    scales are powers of two, so the folding is exact."""
+    scales are powers of two, so the folding is exact.  modes[i] is the
+    direction (0-based) operator i contracts, the directions in turn if None."""
     n = ops[0].shape[0]
+    modes = default_modes(len(ops)) if modes is None else list(modes)
     pending = [np.zeros(n, dtype=np.int64) for _ in range(3)]
     Abar, f = [], []
     for i, M in enumerate(ops):
-        m = chain_mode(i)
+        m = modes[i]
         Meff = np.ldexp(np.asarray(M, dtype=np.float64), -pending[m][None, :])
         Ai, fi = encode_rows(Meff, b)
         Abar.append(Ai)
@@ -243,12 +251,12 @@ def effective_operators(ops: Sequence[np.ndarray], b: int):
     return Abar, f, pending
 
 
-def planner(ops: Sequence[np.ndarray], basis: Sequence[int]):
+def planner(ops: Sequence[np.ndarray], basis: Sequence[int], modes: Sequence[int] | None = None):
     """Planner: the largest b <= 53 whose drop plan (with restoration) passes,
     with rho_i(b) from the effective operators encoded at b.  Returns
     (b, g) or None."""
     for b in range(MAX_BITS, 0, -1):
-        rhos = [row_sum_bound(A) for A in effective_operators(ops, b)[0]]
+        rhos = [row_sum_bound(A) for A in effective_operators(ops, b, modes)[0]]
         g = drop_plan(b, rhos, basis, 1)
         if g is not None:
             return b, g
@@ -281,19 +289,23 @@ def mode_product(T: np.ndarray, M: np.ndarray, mode: int) -> np.ndarray:
     return np.einsum("ak,ijk->ija", M, T)
 
 
-def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int):
+def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int, modes: Sequence[int] | None = None):
     """Plan and prepare the operators of a chain of depth d = len(ops_flat)
     (Algorithm 7 lines 2-9): returns a dict with basis, b, g, the effective
     integer operators and their row exponents, the exponents left pending on
     each direction, the operator residues per modulus, and the dropped moduli
-    per mode."""
+    per mode.  modes[i]: the direction (0-based) of operator i, the
+    directions in turn if None (Algorithm 7 takes any sequence)."""
     basis = list(max_product_moduli(s))           # descending: 256 first
     ops = [matrix_from_flat(a, n) for a in ops_flat]
-    plan = planner(ops, basis)
+    modes = default_modes(len(ops)) if modes is None else [int(m) for m in modes]
+    if len(modes) != len(ops) or any(m not in (0, 1, 2) for m in modes):
+        raise ValueError("one direction in {0, 1, 2} per operator")
+    plan = planner(ops, basis, modes)
     if plan is None:
         return None
     b, g = plan
-    Abar, f, pending = effective_operators(ops, b)
+    Abar, f, pending = effective_operators(ops, b, modes)
     drops = []
     for gi in g:
         L = list(basis)
@@ -303,7 +315,7 @@ def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int):
             dq.append(q)
             L.remove(q)
         drops.append(dq)
-    return dict(basis=basis, b=b, g=g, Abar=Abar, f=f, F=pending,
+    return dict(basis=basis, b=b, g=g, modes=modes, Abar=Abar, f=f, F=pending,
                 Ares=[{p: centered_array(A, p) for p in basis} for A in Abar], drops=drops, n=n, s=s)
 
 
@@ -322,7 +334,7 @@ def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np
         keep["encoded"] = (Xbar, e)
         keep["stages"] = []
     for i in range(len(plan["g"])):
-        R = {p: centered_array(mode_product(R[p], plan["Ares"][i][p], chain_mode(i)), p) for p in basis}
+        R = {p: centered_array(mode_product(R[p], plan["Ares"][i][p], plan["modes"][i]), p) for p in basis}
         if keep is not None:
             keep["stages"].append(("product", i, dict(R)))
         if plan["g"][i] > 0:
@@ -341,11 +353,13 @@ def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np
     return tensor_to_flat(reconstruct_fp64(R, basis, sigma))
 
 
-def rescale_be_chain(X: np.ndarray, ops_flat: Sequence[np.ndarray], n: int, s: int, batch: int):
-    """Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... (one operator per mode product, the
-    directions in turn) for `batch` tensors by OzII-RescaleBE; returns
-    (Y flat, plan) or (None, None) when the planner finds no b."""
-    plan = prepare_chain(ops_flat, n, s)
+def rescale_be_chain(X: np.ndarray, ops_flat: Sequence[np.ndarray], n: int, s: int, batch: int,
+                     modes: Sequence[int] | None = None):
+    """Y = X x_{m1} A1 x_{m2} A2 ... (one operator per mode product, the
+    directions in turn unless `modes` gives them) for `batch` tensors by
+    OzII-RescaleBE; returns (Y flat, plan) or (None, None) when the planner
+    finds no b."""
+    plan = prepare_chain(ops_flat, n, s, modes)
     if plan is None:
         return None, None
     n3 = n ** 3

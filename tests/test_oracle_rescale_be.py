@@ -177,7 +177,7 @@ def _exact_integer_chain(plan, Xbar):
     stages = []
     v = np.array(Xbar, dtype=object)
     for i in range(len(plan["g"])):
-        v = rb.mode_product(v, np.array(plan["Abar"][i], dtype=object), rb.chain_mode(i))
+        v = rb.mode_product(v, np.array(plan["Abar"][i], dtype=object), plan["modes"][i])
         stages.append(("product", v))
         if plan["g"][i] > 0:
             for q in plan["drops"][i]:
@@ -204,12 +204,13 @@ def test_residue_chain_equals_integer_chain(n, s, d):
             assert np.array_equal(R[p], want), (kind, i, p)
 
 
-def _exact_chain(X, ops, n):
-    """the chain in rational arithmetic; operator i along direction i mod 3"""
+def _exact_chain(X, ops, n, modes=None):
+    """the chain in rational arithmetic; operator i along direction modes[i]
+    (i mod 3 by default)"""
     T = np.vectorize(Fraction)(rb.tensor_from_flat(X, n))
     for i, a in enumerate(ops):
         M = np.vectorize(Fraction)(rb.matrix_from_flat(a, n))
-        m = i % 3
+        m = i % 3 if modes is None else modes[i]
         T = np.moveaxis(np.tensordot(M, T, axes=([1], [m])), 0, m)
     return np.vectorize(float)(rb.tensor_to_flat(T))
 
@@ -258,3 +259,24 @@ def test_zero_and_nonfinite_tensors():
     Y, plan = rb.rescale_be_chain(X, ops, n, 16, 2)
     assert np.all(Y[:n ** 3] == 0.0)
     assert np.all(np.isnan(Y[n ** 3:]))
+
+
+@pytest.mark.parametrize("modes", [[1, 0, 2], [0, 0, 1], [2, 2, 2, 0], [1, 2, 1, 0, 0]])
+def test_any_mode_sequence(modes):
+    """Algorithm 7 takes any sequence of modes: the residue chain equals the
+    big-integer chain and the result is as accurate as the cyclic one"""
+    n, s = 8, 16
+    d = len(modes)
+    X = workloads.tensor_batch(n, 1, 950 + d)
+    ops = [workloads.real_matrix(n, n, 960 + q) for q in range(d)]
+    plan = rb.prepare_chain(ops, n, s, modes)
+    keep = {}
+    Y = rb.chain_tensor(X, plan, keep)
+    ints = _exact_integer_chain(plan, keep["encoded"][0])
+    for (kind, v), (_, i, R) in zip(ints, keep["stages"]):
+        for p in plan["basis"]:
+            want = np.vectorize(lambda x: rb.centered(int(x), p))(v)
+            assert np.array_equal(R[p], want), (kind, i, p)
+    ex = _exact_chain(X, ops, n, modes)
+    err = np.linalg.norm(Y - ex) / np.linalg.norm(ex)
+    assert err < 2.6e-15, err
