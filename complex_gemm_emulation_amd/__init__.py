@@ -73,7 +73,7 @@ def _raw():
             "oz2_operand_update": [P, P, P, I64],
             "oz2_operand_destroy": [P],
             "oz2_gemm_prepared": [P, P, P, P, P, P, I64],
-            "oz2_chain_plan_create": [P, I64, I, P, I, P],
+            "oz2_chain_plan_create": [P, I64, I, P, P, I, P],
             "oz2_chain_plan_info": [P, P, P, P],
             "oz2_chain_rescale_be": [P, P, P, P, I64],
             "oz2_chain_plan_destroy": [P],
@@ -329,18 +329,24 @@ class Handle:
         _check("oz2_gemm_prepared", _raw().oz2_gemm_prepared(self._h, pa._p, pb._p, al, be, pc, ldc))
 
     # ------------------------------------------------- persistent chains
-    def chain_plan(self, ops, n, s) -> ChainPlan:
-        """Plan Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... by OzII-RescaleBE
+    def chain_plan(self, ops, n, s, modes=None) -> ChainPlan:
+        """Plan Y = X x_{m1} A1 x_{m2} A2 ... by OzII-RescaleBE
         (oz2_chain_plan_create): ops is a sequence of depth host n x n
-        column-major arrays, operator i contracting direction i mod 3."""
+        column-major arrays; modes the directions in {1, 2, 3}, by default
+        1, 2, 3, 1, ..."""
         mats = [np.ascontiguousarray(np.asarray(M, dtype=np.float64).reshape(-1)) for M in ops]
         for M in mats:
             if M.size < n * n:
                 raise ValueError(f"operator holds {M.size} entries, n x n needs {n * n}")
         out = ctypes.c_void_p()
         ptrs = (ctypes.c_void_p * max(1, len(mats)))(*[M.ctypes.data_as(ctypes.c_void_p) for M in mats])
+        pm = None
+        if modes is not None:
+            if len(modes) != len(mats):
+                raise ValueError("one mode per operator")
+            pm = (ctypes.c_int * len(mats))(*[int(m) for m in modes])
         _check("oz2_chain_plan_create",
-               _raw().oz2_chain_plan_create(self._h, n, len(mats), ptrs, s, ctypes.byref(out)))
+               _raw().oz2_chain_plan_create(self._h, n, len(mats), ptrs, pm, s, ctypes.byref(out)))
         return ChainPlan(out, n, s)
 
     def chain_rescale_be(self, plan: ChainPlan, X, Y, batch) -> None:

@@ -702,16 +702,21 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
     return OZ2_STATUS_SUCCESS;
 }
 
-int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, int num_moduli,
-                          oz2_chain_plan_t* out) {
+int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, const int* modes,
+                          int num_moduli, oz2_chain_plan_t* out) {
     if (!h) return -1;
     if (n < 1 || n > kChainN) return -2;
     if (depth < 1 || depth > kChainMaxD) return -3;
     if (!ops) return -4;
     for (int i = 0; i < depth; ++i)
         if (!ops[i]) return -4;
-    if (num_moduli < kMinS || num_moduli > kChainMaxS) return -5;
-    if (!out) return -6;
+    int dirs[kChainMaxD];
+    for (int i = 0; i < depth; ++i) {
+        dirs[i] = modes ? modes[i] - 1 : i % 3;  // 1-based directions in the interface
+        if (dirs[i] < 0 || dirs[i] > 2) return -5;
+    }
+    if (num_moduli < kMinS || num_moduli > kChainMaxS) return -6;
+    if (!out) return -7;
     *out = nullptr;
     oz2_chain_plan* plan = new (std::nothrow) oz2_chain_plan();
     if (!plan) return OZ2_STATUS_ALLOC_FAILED;
@@ -726,7 +731,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         delete plan;
         return OZ2_STATUS_ALLOC_FAILED;
     }
-    int st = chain_plan(num_moduli, (int)n, depth, ops, &plan->params, &host->tab, host->ops);
+    int st = chain_plan(num_moduli, (int)n, depth, ops, dirs, &plan->params, &host->tab, host->ops);
     if (st < 0) st = -4;  // a non-finite operator entry
     if (!st && hipMalloc(&plan->mem, off_ops + ops_bytes) != hipSuccess) {
         (void)hipGetLastError();

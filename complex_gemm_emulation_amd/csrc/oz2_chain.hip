@@ -86,8 +86,23 @@ __device__ __forceinline__ uint32_t pack4(float r0, float r1, float r2, float r3
 // Unused leading slots (modulus 1) hold zeros after every step; they are
 // stored like the others, and their zero operators make them inert.
 // at: this lane's word of slot 0 in the plane buffer.
-template <int G>
-__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, int8_t* at) {
+// the four entries of a lane into one plane: contiguous (step 0, one 32-bit
+// store) or step bytes apart (byte stores; only with ANY layouts)
+template <bool ANY>
+__device__ __forceinline__ void store4(int8_t* p, int step, float r0, float r1, float r2, float r3) {
+    if (!ANY || step == 0) {
+        *(uint32_t*)p = pack4(r0, r1, r2, r3);
+    } else {
+        p[0] = (int8_t)(int)r0;
+        p[step] = (int8_t)(int)r1;
+        p[2 * step] = (int8_t)(int)r2;
+        p[3 * step] = (int8_t)(int)r3;
+    }
+}
+
+template <int G, bool ANY>
+__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, int8_t* at,
+                                               int step) {
     const int g = G >= 0 ? G : g_rt;
     const int keep = kSlots - 1 - g;  // last slot of the reduced basis
 #pragma unroll
@@ -102,7 +117,7 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
         }
 #pragma unroll
     for (int u = 0; u < kSlots; ++u)
-        if (u <= keep) *(uint32_t*)(at + u * kPlane) = pack4(r[0][u], r[1][u], r[2][u], r[3][u]);
+        if (u <= keep) store4<ANY>(at + u * kPlane, step, r[0][u], r[1][u], r[2][u], r[3][u]);
     // mixed-radix digits of the kept residues, in place
 #pragma unroll
     for (int i = 0; i < kSlots - 1; ++i)
@@ -125,8 +140,8 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
                     for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
                 }
             const float m = T->mod[p], rm = T->rmod[p];
-            *(uint32_t*)(at + p * kPlane) = pack4(cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm),
-                                                  cmod(ts[3], m, rm));
+            store4<ANY>(at + p * kPlane, step, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm),
+                        cmod(ts[3], m, rm));
         }
 }
 
@@ -159,27 +174,28 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
 }
 
 // unpack the four entries of every slot of one tile and rescale them
-template <int G0, int G1>
+template <int G0, int G1, bool ANY>
 __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint32_t (&pk)[kSlots],
-                                             const ChainTables* T, int8_t* at) {
+                                             const ChainTables* T, int8_t* at, int step) {
     float r[4][kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u)
 #pragma unroll
         for (int q = 0; q < 4; ++q) r[q][u] = unpack(pk[u], q);
     if (G0 >= 0 && G0 == G1)
-        rescale_extend<G0>(0, r, T, at);
+        rescale_extend<G0, ANY>(0, r, T, at, step);
     else if (G0 >= 0 && mode == 0)
-        rescale_extend<G0>(0, r, T, at);
+        rescale_extend<G0, ANY>(0, r, T, at, step);
     else if (G0 >= 0)
-        rescale_extend<G1>(0, r, T, at);
+        rescale_extend<G1, ANY>(0, r, T, at, step);
     else
-        rescale_extend<-1>(g[mode], r, T, at);
+        rescale_extend<-1, ANY>(g[mode], r, T, at, step);
 }
 
 // G0, G1: the drop counts after products 1 and 2 when fixed at compile time
 // (G0 = G1: after every product but the last), -1 to read them from P.g;
-// D: the depth when fixed at compile time, 0 to read it from P.d
+// D: the depth when fixed at compile time with the modes 1, 2, 3 (every
+// residue store contiguous), 0 to read the depth, modes and layouts from P
 template <int G0, int G1, int D>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 4)))
 void chain_kernel(ChainParams P) {
@@ -211,6 +227,7 @@ void chain_kernel(ChainParams P) {
         *(long*)(&ops[i % 3][u][8 * w]) = v;
     };
     const int d = D > 0 ? D : P.d;
+    const int m0 = D > 0 ? 0 : P.m0;
     for (int i = 0; i < 3 && i < d; ++i) stage_ops(i);
     if (tid == 0) smax = 0;
     __syncthreads();
@@ -260,7 +277,17 @@ void chain_kernel(ChainParams P) {
             for (int j = 0; j < 8; ++j)
                 w[j >> 2] |= ((uint32_t)(int)dmod_odd(xb[j], m, rm) & 0xffu) << (8 * (j & 3));
         }
-        *(uint2*)(buf + u * kPlane + idx0) = make_uint2(w[0], w[1]);
+        if (D > 0 || m0 == 0) {
+            *(uint2*)(buf + u * kPlane + idx0) = make_uint2(w[0], w[1]);
+        } else {
+            // first product along direction m0 + 1: position 0 holds k_m0
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kk[3] = {k1_0 + j, k2, k3};
+                buf[u * kPlane + kk[m0] + 16 * kk[(m0 + 1) % 3] + 256 * kk[(m0 + 2) % 3]] =
+                    (int8_t)(w[j >> 2] >> (8 * (j & 3)));
+            }
+        }
     }
     __syncthreads();
 
@@ -274,10 +301,19 @@ void chain_kernel(ChainParams P) {
         tile_products(buf, ops[mode % 3], T, wave, a, kq, pk0);
         tile_products(buf, ops[mode % 3], T, wave + 8, a, kq, pk1);
         __syncthreads();  // every plane read before any is overwritten
-        // next layout: fibre (t + 16 a), index 4 kq .. 4 kq + 3
-        rescale_tile<G0, G1>(mode, P.g, pk0, T, buf + (wave + 16 * a) * kChainN + 4 * kq);
+        // the lane's entries e = 4 kq + q, fibre t, output a, stored as
+        // (e, t, a): kind 0, entries contiguous; (t, e, a): kind 1, or
+        // (a, e, t): kind 2, entries 16 bytes apart -- position 0 is the
+        // next product's direction
+        const int kind = D > 0 ? 0 : P.kind[mode];
+        const int step = kind == 0 ? 0 : 16;
+        auto at = [&](int t) -> int8_t* {
+            return buf + (kind == 0 ? (t + 16 * a) * kChainN + 4 * kq
+                                    : kind == 1 ? t + 64 * kq + 256 * a : a + 64 * kq + 256 * t);
+        };
+        rescale_tile<G0, G1, D == 0>(mode, P.g, pk0, T, at(wave), step);
         asm volatile("" ::: "memory");  // one tile at a time
-        rescale_tile<G0, G1>(mode, P.g, pk1, T, buf + (wave + 8 + 16 * a) * kChainN + 4 * kq);
+        rescale_tile<G0, G1, D == 0>(mode, P.g, pk1, T, at(wave + 8), step);
         asm volatile("" ::: "memory");
         // operator mode + 3 into the buffer this product read (before the
         // barrier above); it is next read three products later
@@ -286,13 +322,11 @@ void chain_kernel(ChainParams P) {
     }
 
     // -------------------------------------- last product and ReconstructFP64
-    // (Algorithm 5), sigma = alpha Gamma.  Every product moves the contracted
-    // index out of layout position 0 and appends its output index, so after
-    // d products position p holds direction (p + d) mod 3; the lane's entries
-    // sit at positions (4 kq + q, t, a).
+    // (Algorithm 5), sigma = alpha Gamma.  The lane's entries 4 kq + q, its
+    // fibre t and its output a run along the directions P.fin (with the
+    // modes 1, 2, 3 the last product leaves them in that order).
     const double alpha = ldexp(P.Qd, -e);
-    const int r3 = d % 3;
-    const int dir0 = r3, dir1 = (1 + r3) % 3, dir2 = (2 + r3) % 3;
+    const int dir0 = D > 0 ? 0 : P.fin[0], dir1 = D > 0 ? 1 : P.fin[1], dir2 = D > 0 ? 2 : P.fin[2];
     const int64_t n2 = (int64_t)n * n;
     const int64_t st0 = dir0 == 0 ? 1 : dir0 == 1 ? n : n2;
     const int64_t st1 = dir1 == 0 ? 1 : dir1 == 1 ? n : n2;
@@ -351,7 +385,10 @@ hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
         return hipErrorInvalidValue;
     if (P.d < 1 || P.d > kChainMaxD || P.g[P.d - 1] != 0) return hipErrorInvalidValue;
     for (int i = 0; i + 1 < P.d; ++i)
-        if (P.g[i] < 0 || P.g[i] >= P.s) return hipErrorInvalidValue;
+        if (P.g[i] < 0 || P.g[i] >= P.s || P.kind[i] < 0 || P.kind[i] > 2) return hipErrorInvalidValue;
+    if (P.m0 < 0 || P.m0 > 2) return hipErrorInvalidValue;
+    for (int j = 0; j < 3; ++j)
+        if (P.fin[j] < 0 || P.fin[j] > 2) return hipErrorInvalidValue;
     // compile-time drop counts for the usual plans of 16^3 tensors (7 after
     // every product with 16 or 14 moduli, 6 with 12, 4 with 8; 4 then 5 for
     // a depth-3 chain with 10) and a compile-time depth for one pass over the
@@ -360,7 +397,7 @@ hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
     for (int i = 1; i + 1 < P.d; ++i) same = same && P.g[i] == P.g[0];
     const int g0 = same ? P.g[0] : -1;
     const dim3 grid((unsigned)P.batch), block(512);
-    if (P.d == 3) {
+    if (P.d == 3 && P.cyclic) {
         if (g0 == 7)
             hipLaunchKernelGGL((chain_kernel<7, 7, 3>), grid, block, 0, st, P);
         else if (g0 == 6)

@@ -134,8 +134,8 @@ bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* 
 
 }  // namespace
 
-int chain_plan(int s, int n, int d, const double* const* ops, ChainParams* P, ChainTables* T,
-               int8_t* ops_residues) {
+int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, ChainParams* P,
+               ChainTables* T, int8_t* ops_residues) {
     const ModuliPlan* pl = moduli_plan(s);
     if (!pl || s > kChainMaxS || n < 1 || n > kChainN || d < 1 || d > kChainMaxD) return OZ2_STATUS_INTERNAL;
     if (pl->mod[0] != 256) return OZ2_STATUS_INTERNAL;
@@ -154,9 +154,9 @@ int chain_plan(int s, int n, int d, const double* const* ops, ChainParams* P, Ch
         bool ok = true;
         for (int i = 0; i < d && ok; ++i) {
             // the effective operator: pending scales of its direction folded in
-            ok = encode_rows(ops[i], pend[i % 3], n, b, Abar[i], f[i]);
+            ok = encode_rows(ops[i], pend[modes[i]], n, b, Abar[i], f[i]);
             rho[i] = row_sum_bound(Abar[i], n);
-            std::memcpy(pend[i % 3], f[i], sizeof(int) * n);
+            std::memcpy(pend[modes[i]], f[i], sizeof(int) * n);
         }
         if (ok && drop_plan(b, d, rho, pl->mod, s, g)) break;
     }
@@ -166,6 +166,34 @@ int chain_plan(int s, int n, int d, const double* const* ops, ChainParams* P, Ch
     P->b = b;
     P->d = d;
     for (int i = 0; i < kChainMaxD; ++i) P->g[i] = i < d ? g[i] : 0;
+    // residue layout: a product contracts position 0 and leaves its lane's
+    // entries (the old position 1), fibres (old position 2) and outputs (its
+    // own direction); the next direction to contract goes to position 0
+    int pos[3] = {modes[0], (modes[0] + 1) % 3, (modes[0] + 2) % 3};
+    P->m0 = modes[0];
+    P->cyclic = 1;
+    for (int i = 0; i < d; ++i) P->cyclic &= modes[i] == i % 3;
+    for (int i = 0; i < kChainMaxD; ++i) P->kind[i] = 0;
+    for (int i = 0; i < d; ++i) {
+        const int de = pos[1], dt = pos[2], da = modes[i];
+        if (i == d - 1) {
+            P->fin[0] = de;
+            P->fin[1] = dt;
+            P->fin[2] = da;
+            break;
+        }
+        const int next = modes[i + 1];
+        if (next == de) {
+            P->kind[i] = 0;  // layout (e, t, a)
+            pos[0] = de, pos[1] = dt, pos[2] = da;
+        } else if (next == dt) {
+            P->kind[i] = 1;  // layout (t, e, a)
+            pos[0] = dt, pos[1] = de, pos[2] = da;
+        } else {
+            P->kind[i] = 2;  // layout (a, e, t)
+            pos[0] = da, pos[1] = de, pos[2] = dt;
+        }
+    }
     // alpha multiplier: the dropped moduli (the g smallest, smallest first)
     // in drop order, each product rounded to double
     double Qd = 1.0;

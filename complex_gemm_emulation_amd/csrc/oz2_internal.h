@@ -111,9 +111,9 @@ struct SmallParams {
 
 // Persistent tensor-mode chain, OzII-RescaleBE ("You Only Convert Twice:
 // Ozaki Scheme II for Chained Tensor Mode Products", Sec. 5.2 and
-// Algorithm 7): Y = X x1 A1 x2 A2 x3 A3 x1 A4 ... for a batch of
-// n x n x n tensors, d operators applied along the directions in turn, one
-// block per tensor, residues in LDS for the whole chain (oz2_chain.hip).
+// Algorithm 7): Y = X x_{m1} A1 x_{m2} A2 ... for a batch of n x n x n
+// tensors, d operators, by default along the directions in turn, one block
+// per tensor, residues in LDS for the whole chain (oz2_chain.hip).
 constexpr int kChainN = 16;      // tensor side of the kernel's tiles (n <= 16 is zero padded)
 constexpr int kChainMaxS = 16;   // moduli: one LDS buffer of 16 residue planes (64 KiB)
 constexpr int kChainMaxD = 8;    // chain depth: operators
@@ -123,6 +123,15 @@ struct ChainParams {
     int64_t batch;
     int n, s, b, d;
     int g[kChainMaxD];           // moduli dropped after product i (g[d - 1] = 0)
+    // residue layout: position 0 of a plane row is the contracted direction.
+    // m0: direction at position 0 before the first product (positions hold
+    // m0, m0 + 1, m0 + 2 mod 3); kind[i]: how product i's output is stored
+    // (0: the lane's four entries contiguous, 1 and 2: 16 bytes apart, see
+    // oz2_chain.hip); fin: directions of the last product's entry, fibre
+    // and output indices; cyclic: the modes are 0, 1, 2, 0, ...
+    int m0, cyclic;
+    int kind[kChainMaxD];
+    int fin[3];
     double Qd;                   // fl64 product of the dropped moduli, in drop order
     const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators
     const float* tab;            // device ChainTables (below)
@@ -140,12 +149,13 @@ struct ChainTables {
 
 // Host planning of the chain (Algorithms 2, 3 and 5 of the chain page, with
 // the pending row scales of a direction folded into the next operator on
-// it, Sec. 5.2): the significand bits b, the drop counts g, and the
-// effective integer operators' residues.  ops: d HOST n x n column-major
-// operators.  Returns 0, -(i + 1) for a non-finite entry in operator i, or
+// it, Sec. 5.2): the significand bits b, the drop counts g, the effective
+// integer operators' residues and the residue layout of every product.
+// ops: d HOST n x n column-major operators; modes: d directions in
+// {0, 1, 2}.  Returns 0, -(i + 1) for a non-finite entry in operator i, or
 // OZ2_STATUS_RANGE when no b in [1, 53] passes.
-int chain_plan(int s, int n, int d, const double* const* ops, ChainParams* P, ChainTables* T,
-               int8_t* ops_residues);
+int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, ChainParams* P,
+               ChainTables* T, int8_t* ops_residues);
 
 struct CrtTestParams {
     const uint8_t* R;  // [s][count]

@@ -208,12 +208,13 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
 /* ---------------------------------------------------------------------
  * Persistent tensor-mode chains (OzII-RescaleBE, "You Only Convert Twice:
  * Ozaki Scheme II for Chained Tensor Mode Products", Sec. 5.2, Algorithm 7):
- * Y = X x1 A1 x2 A2 x3 A3 x1 A4 x2 A5 ... for a batch of n x n x n tensors
+ * Y = X x_{m1} A1 x_{m2} A2 ... x_{md} Ad for a batch of n x n x n tensors
  * (column-major X[i + n j + n^2 k], tensor t at X + t n^3) with shared
- * n x n operators.  A chain of depth d applies d operators; operator i
- * (1-based) contracts direction ((i - 1) mod 3) + 1, so depth 3 is
- * Y_abc = sum A1_ai A2_bj A3_ck X_ijk and longer chains revisit the
- * directions in turn (Sec. 6).  The tensor is encoded once with one
+ * n x n operators; x_m contracts direction m in {1, 2, 3} with the
+ * operator's second index.  By default m_i = ((i - 1) mod 3) + 1, so depth 3
+ * is Y_abc = sum A1_ai A2_bj A3_ck X_ijk and longer chains revisit the
+ * directions in turn (Sec. 6); Algorithm 7 takes any sequence, and so does
+ * this interface (other sequences take slower byte-wise residue stores).  The tensor is encoded once with one
  * power-of-two exponent (b significand bits), stays in residue form through
  * all d mode products -- after every product but the last the g_i smallest
  * moduli are dropped by rounded division (Sec. 2.3.1 Eq. 15, Algorithm 1)
@@ -237,12 +238,13 @@ typedef struct oz2_chain_plan* oz2_chain_plan_t;
  * the row exponents left pending on each direction, which are copied to
  * DEVICE memory owned by the plan (2.3 KiB + depth * 4 KiB).  ops: HOST
  * array of depth pointers to HOST n x n column-major operators (finite).
- * Argument numbers: h 1, n 2, depth 3, ops 4 (also a NULL entry or a
- * non-finite operator entry), num_moduli 5, out 6.  OZ2_STATUS_RANGE when
- * no b in [1, 53] passes.  The plan can be reused for any number of tensors
- * and calls. */
-int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, int num_moduli,
-                          oz2_chain_plan_t* out);
+ * modes: HOST array of depth directions in {1, 2, 3}, or NULL for the
+ * directions in turn.  Argument numbers: h 1, n 2, depth 3, ops 4 (also a
+ * NULL entry or a non-finite operator entry), modes 5, num_moduli 6, out 7.
+ * OZ2_STATUS_RANGE when no b in [1, 53] passes.  The plan can be reused for
+ * any number of tensors and calls. */
+int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, const int* modes,
+                          int num_moduli, oz2_chain_plan_t* out);
 
 /* The plan's depth, significand bits b and drop counts g[0 .. depth - 1]
  * (g[depth - 1] = 0); any pointer may be NULL, g must hold depth ints. */

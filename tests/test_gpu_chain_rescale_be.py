@@ -157,6 +157,37 @@ def test_chain_depth_matches_oracle_bitwise(handle, n, s, d, batch):
     _check_bitwise(from_dev(dY), want, f"n={n} s={s} d={d}")
 
 
+MODE_CASES = [
+    # n, s, modes (1-based), batch
+    (16, 16, [2, 3, 1], 2),        # first product along direction 2: byte-wise encode stores
+    (16, 16, [1, 1, 2], 2),        # one direction twice in a row (store kind 2)
+    (16, 16, [1, 3, 2], 2),        # the fibre direction next (store kind 1)
+    (8, 16, [3, 3, 3, 1, 2], 2),
+    (12, 14, [2, 1, 2, 3, 3, 1], 1),
+    (5, 12, [3, 1, 1, 2], 2),      # drop counts 5, 6, 6: the guarded instance
+    (16, 12, [3, 2, 1], 2),        # depth 3 in another order: the run-time instance
+]
+
+
+@pytest.mark.parametrize("n,s,modes,batch", MODE_CASES, ids=["m" + "".join(map(str, c[2])) + f"n{c[0]}" for c in MODE_CASES])
+def test_chain_mode_sequences_match_oracle_bitwise(handle, n, s, modes, batch):
+    """Algorithm 7 with any sequence of modes: every residue layout kind and
+    first direction, through the run-time instance of the kernel"""
+    import torch
+    d = len(modes)
+    _say(f"[chain modes] n={n} s={s} modes={modes} batch={batch}")
+    ops = _ops(n, 8700 + 10 * n + d, d=d)
+    X = workloads.tensor_batch(n, batch, 8800 + n + d)
+    want, plan = rb.rescale_be_chain(X, ops, n, s, batch, [m - 1 for m in modes])
+    assert plan is not None
+    with handle.chain_plan(ops, n, s, modes) as cp:
+        assert (cp.depth, cp.b, list(cp.g)) == (d, plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
+        dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
+        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
+        torch.cuda.synchronize()
+    _check_bitwise(from_dev(dY), want, f"modes={modes}")
+
+
 def test_chain_argument_errors(handle):
     import ctypes
     import complex_gemm_emulation_amd as oz2
@@ -165,19 +196,21 @@ def test_chain_argument_errors(handle):
     p = A.ctypes.data_as(ctypes.c_void_p)
     three = (ctypes.c_void_p * 3)(p, p, p)
     out = ctypes.c_void_p()
-    assert lib.oz2_chain_plan_create(handle._h, 0, 3, three, 8, ctypes.byref(out)) == -2
-    assert lib.oz2_chain_plan_create(handle._h, 17, 3, three, 8, ctypes.byref(out)) == -2
-    assert lib.oz2_chain_plan_create(handle._h, 4, 0, three, 8, ctypes.byref(out)) == -3
-    assert lib.oz2_chain_plan_create(handle._h, 4, 9, three, 8, ctypes.byref(out)) == -3
-    assert lib.oz2_chain_plan_create(handle._h, 4, 3, None, 8, ctypes.byref(out)) == -4
+    assert lib.oz2_chain_plan_create(handle._h, 0, 3, three, None, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 17, 3, three, None, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 4, 0, three, None, 8, ctypes.byref(out)) == -3
+    assert lib.oz2_chain_plan_create(handle._h, 4, 9, three, None, 8, ctypes.byref(out)) == -3
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, None, None, 8, ctypes.byref(out)) == -4
     holey = (ctypes.c_void_p * 3)(p, None, p)
-    assert lib.oz2_chain_plan_create(handle._h, 4, 3, holey, 8, ctypes.byref(out)) == -4
-    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, 17, ctypes.byref(out)) == -5
-    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, 8, None) == -6
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, holey, None, 8, ctypes.byref(out)) == -4
+    badm = (ctypes.c_int * 3)(1, 4, 2)
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, badm, 8, ctypes.byref(out)) == -5
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, None, 17, ctypes.byref(out)) == -6
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, three, None, 8, None) == -7
     bad = np.eye(4)
     bad[1, 2] = np.inf
     badp = (ctypes.c_void_p * 3)(p, bad.ctypes.data_as(ctypes.c_void_p), p)
-    assert lib.oz2_chain_plan_create(handle._h, 4, 3, badp, 8, ctypes.byref(out)) == -4
+    assert lib.oz2_chain_plan_create(handle._h, 4, 3, badp, None, 8, ctypes.byref(out)) == -4
     assert not out.value
     with handle.chain_plan([A, A, A], 4, 8) as cp:
         assert lib.oz2_chain_rescale_be(handle._h, cp._p, None, None, 0) == 0   # empty batch
