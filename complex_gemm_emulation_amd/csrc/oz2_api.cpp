@@ -117,6 +117,7 @@ void fill_mod_tables(const ModuliPlan& pl, EncodeParams* E, bool ext) {
         E->K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
         E->frcp[q] = pl.frcp[q];
         E->foff[q] = pl.foff[q];
+        E->foffb[q] = pl.foffb[q];
         for (int l = 0; l < kExtWords; ++l) E->c[q][l] = pl.c4[q][l];
     }
 }
@@ -157,6 +158,7 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
         P.rcp[q] = pl.drcp[q];
         P.frcp[q] = pl.frcp[q];
         P.foff[q] = pl.foff[q];
+        P.foffb[q] = pl.foffb[q];
         for (int l = 0; l < kExtWords; ++l) P.c[q][l] = pl.c4[q][l];
     }
     fill_crt_tables(pl, &P);

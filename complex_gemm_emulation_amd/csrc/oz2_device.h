@@ -124,6 +124,29 @@ __device__ __forceinline__ int centred_residue(const Limbs<EXT>& L, uint32_t K, 
     return (int)fmaf(-m, floorf(fmaf(vf, rcp, off)), vf);
 }
 
+// the centred residues of four elements (one modulus) as the four bytes of a
+// word, byte e from L[e].  In offset binary: with K128 = K_m + 128 the dot
+// products give v' = v + 128, and f = v' - m floor((v' + hb + 1/2 - 128) / m)
+// = r + 128 lies in [0, 255] (hb = h, or 128 for m = 256, whose window
+// [-128, 127] has the same bytes as [-127, 128]).  The floor argument is the
+// one of centred_residue, so f is exact; v_cvt_pk_u8_f32 puts it in byte e,
+// and XOR 0x80 per byte turns r + 128 into the two's complement byte of r.
+template <bool EXT>
+__device__ __forceinline__ uint32_t residue_word(const Limbs<EXT>* L, uint32_t K128, const uint32_t* c4, float m,
+                                                 float rcp, float offb) {
+    uint32_t w = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t v = K128;
+#pragma unroll
+        for (int p = 0; p < (EXT ? kExtWords : kStdWords); ++p) v = __builtin_amdgcn_udot4(L[e].w[p], c4[p], v, false);
+        const float vf = (float)v;
+        const float f = fmaf(-m, floorf(fmaf(vf, rcp, offb)), vf);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(f, e, w);
+    }
+    return w ^ 0x80808080u;
+}
+
 // c_hat from the residues of one entry, accumulated over the moduli two at a
 // time with one v_dot2_u32_u16 per limb: the 16-bit limbs of
 // r_t W_t + r_(t+1) W_(t+1) (r and the two limbs of W packed as 16-bit

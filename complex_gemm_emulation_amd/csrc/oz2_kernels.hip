@@ -174,11 +174,14 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
           for (int u = 0; u < 4; ++u) {
             const int t = t0 + u;
             if (t >= P.s) break;
-            int r[4];
+            if (!CPLX) {
+                *(uint32_t*)(dst + t * plane) =
+                    residue_word<EXT>(lr, P.K[t] + 128u, P.c[t], (float)P.mod[t], P.frcp[t], P.foffb[t]);
+            } else {
+                int r[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) r[e] = residue_of<EXT>(lr[e], P, t);
-            *(uint32_t*)(dst + t * plane) = pack4(r[0], r[1], r[2], r[3]);
-            if (CPLX) {
+                for (int e = 0; e < 4; ++e) r[e] = residue_of<EXT>(lr[e], P, t);
+                *(uint32_t*)(dst + t * plane) = pack4(r[0], r[1], r[2], r[3]);
                 const int m = (int)P.mod[t], lo = -(int)P.h[t], hi = m - 1 - (int)P.h[t];
                 int ri[4], rs[4];
 #pragma unroll

@@ -210,6 +210,10 @@ void build_plan(int s, ModuliPlan* p) {
         volatile float fone = 1.0f, fh = (float)h + 0.5f;
         p->frcp[t] = fone / fm;
         p->foff[t] = fh / fm;
+        // offset-binary bytes (residue + 128 in [0, 255]): m = 256 takes the
+        // window [-128, 127], whose bytes are those of [-127, 128]
+        volatile float fhb = (float)(m == 256 ? 128u : h) + 0.5f - 128.0f;
+        p->foffb[t] = fhb / fm;
         volatile double done = 1.0, dm = (double)m;
         p->drcp[t] = done / dm;
     }

@@ -24,6 +24,12 @@
 // contiguous run of tiles; a tile operand equal to the previous tile's
 // (a shared operator, stride 0) is not loaded or encoded again.  Reads A, B
 // (and C when beta != 0) once from HBM and writes C once.
+//
+// For k <= 16 (the tensor chain's modes) half of the instruction's k would be
+// zero padding, and so would half of every lane's encode work.  There a
+// wavefront takes two tiles at a time instead: lanes 0-31 hold the first
+// tile's k = 0..15, lanes 32-63 the second's, and each tile's products use
+// op(A) with the other half's lanes zeroed (PAIR below).
 #include "oz2_device.h"
 #include "oz2_internal.h"
 
@@ -48,11 +54,11 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
 // per-modulus constants, staged in LDS once per block: read at uniform
 // addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes
 struct ModConst {
-    uint32_t mod, rcp_lo, rcp_hi, K;  // rcp: the two words of fl64(1 / m)
+    uint32_t mod, rcp_lo, rcp_hi, K128;  // rcp: the two words of fl64(1 / m); K128 = K_m + 128
     uint32_t c4[kExtWords];
-    float frcp, foff;
+    float frcp, foffb;                   // residue_word's constants
 };
-static_assert(offsetof(ModConst, foff) == 4 * (5 + kExtWords), "staging order of ModConst");
+static_assert(offsetof(ModConst, foffb) == 4 * (5 + kExtWords), "staging order of ModConst");
 struct SmallConsts {
     ModConst q[kMaxS + 1];            // one zeroed entry past the last modulus
     uint32_t W2[kMaxS / 2][kMaxLimb16];
@@ -61,9 +67,10 @@ struct SmallConsts {
 };
 static_assert(offsetof(SmallConsts, Y2) == offsetof(SmallConsts, M16) + 4 * kMaxLimb16, "staging order");
 
-// exponent of the vector held by lanes l, l^16, l^32, l^48 and the residue
-// bytes of this lane's 8 values for every modulus (byte e = k 8 kq + e)
-template <int SMAX, bool EXT>
+// exponent of the vector held by lanes l, l^16, l^32, l^48 (PAIR: l, l^16,
+// the lanes of one tile) and the residue bytes of this lane's 8 values for
+// every modulus (byte e = k 8 kq + e)
+template <int SMAX, bool EXT, bool PAIR>
 __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P, const SmallConsts& Q,
                                         long frag[SMAX], int& D, bool& bad) {
     uint64_t mx = 0;
@@ -71,8 +78,10 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
     for (int e = 0; e < 8; ++e) mx = max(mx, abs_bits(x[e]));
     unsigned long long o = __shfl_xor((unsigned long long)mx, 16);
     mx = mx > o ? mx : o;
-    o = __shfl_xor((unsigned long long)mx, 32);
-    mx = mx > o ? mx : o;
+    if (!PAIR) {
+        o = __shfl_xor((unsigned long long)mx, 32);
+        mx = mx > o ? mx : o;
+    }
     D = scale_of(mx, P.t, bad);
     Limbs<EXT> L[8];
 #pragma unroll
@@ -82,13 +91,9 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
         if (t < P.s) {
             const ModConst& C = Q.q[t];
             const float m = (float)C.mod;
-            uint32_t w[2] = {0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t r = (uint32_t)centred_residue<EXT>(L[e], C.K, C.c4, m, C.frcp, C.foff);
-                w[e >> 2] |= (r & 0xffu) << (8 * (e & 3));
-            }
-            frag[t] = (long)((uint64_t)w[0] | ((uint64_t)w[1] << 32));
+            const uint32_t w0 = residue_word<EXT>(L, C.K128, C.c4, m, C.frcp, C.foffb);
+            const uint32_t w1 = residue_word<EXT>(L + 4, C.K128, C.c4, m, C.frcp, C.foffb);
+            frag[t] = (long)((uint64_t)w0 | ((uint64_t)w1 << 32));
         }
     }
 }
@@ -101,15 +106,23 @@ __device__ __forceinline__ uint32_t acc_mod(int32_t acc, const ModConst& C) {
     return (uint32_t)(int)fma(-m, floor(fma(a, rcp, 0.5 * rcp)), a);
 }
 
-template <int NL, bool BETA>
-__global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
+// PAIR (k <= 16): the instruction's k of 32 holds two tiles.  Lanes 0-31
+// carry tile n at k = 0..15 and lanes 32-63 carry tile n + 1 there, so every
+// lane encodes useful values; the product of tile n + h takes the lanes of
+// half h of op(A) and zeros in the other half, which removes the other
+// tile's terms from the sum.
+template <int NL, bool BETA, bool PAIR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1 : 2))) void small_gemm_kernel(SmallParams P) {
     constexpr int SMAX = 4 * NL;     // N_L words hold products of up to 4 N_L moduli <= 256
     constexpr bool EXT = NL >= 5;    // t > 61 is only reachable with more than 16 moduli
+    constexpr int STEP = PAIR ? 2 : 1;
     const int lane = threadIdx.x & 63;
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t first = wave * P.tiles_per_wave;
     const int64_t last = min(first + (int64_t)P.tiles_per_wave, P.tiles_total);
-    const int vi = lane & 15, kq = lane >> 4;
+    const int vi = lane & 15;
+    const int kq = PAIR ? (lane >> 4) & 1 : lane >> 4;  // k = 8 kq .. 8 kq + 7 of the lane's tile
+    const int half = PAIR ? lane >> 5 : 0;              // which tile of the pair the lane carries
     const int64_t per_batch = (int64_t)P.tiles_m * P.tiles_n;
 
     __shared__ SmallConsts Q;
@@ -125,10 +138,10 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
                     if (f == 0) v = P.mod[t];
                     else if (f == 1) v = (uint32_t)__double2loint(P.rcp[t]);
                     else if (f == 2) v = (uint32_t)__double2hiint(P.rcp[t]);
-                    else if (f == 3) v = P.K[t];
+                    else if (f == 3) v = P.K[t] + 128u;
                     else if (f < 4 + kExtWords) v = P.c[t][f - 4];
                     else if (f == 4 + kExtWords) v = __float_as_uint(P.frcp[t]);
-                    else v = __float_as_uint(P.foff[t]);
+                    else v = __float_as_uint(P.foffb[t]);
                 }
             } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16) {
                 const int j = i - (kMaxS + 1) * nq;
@@ -146,89 +159,127 @@ __global__ __launch_bounds__(256) void small_gemm_kernel(SmallParams P) {
     long fa[SMAX], fb[SMAX];
     int DA = 0, EB = 0;
     bool badA = false, badB = false;
-    int64_t keyA = -1, keyB = -1;
+    // operand tiles held in fa / fb, for the first and the second tile of a pair
+    int64_t keyA0 = -1, keyA1 = -1, keyB0 = -1, keyB1 = -1;
 
-    for (int64_t tile = first; tile < last; ++tile) {
+    // batch entry and tile coordinates of a tile index (wave-uniform: scalar)
+    auto coords = [&](int64_t tile, int64_t& b, int64_t& tm, int64_t& tn) {
+        b = tile / per_batch;
+        const int64_t rem = tile - b * per_batch;
+        tm = rem / P.tiles_n;
+        tn = rem - tm * P.tiles_n;
+    };
+
+    for (int64_t tile = first; tile < last; tile += STEP) {
         // keeps the LDS constant reads inside the loop (no hoisting into registers)
         asm volatile("" ::: "memory");
-        const int64_t b = tile / per_batch;
-        const int64_t rem = tile - b * per_batch;
-        const int64_t tm = rem / P.tiles_n, tn = rem - tm * P.tiles_n;
-        const int64_t i0 = tm * 16, j0 = tn * 16;
-        // rows i0.. of op(A_b): contiguous in memory for op = T
-        const int64_t ka = (P.strideA ? b : 0) * P.tiles_m + tm;
-        if (ka != keyA) {
-            double x[8];
-            load8(P.A + b * P.strideA, P.lda, P.transa != 0, i0 + vi, P.m, P.k, kq, x);
-            encode8<SMAX, EXT>(x, P, Q, fa, DA, badA);
-            keyA = ka;
+        // a lone last tile fills both halves with itself
+        const int64_t tile1 = (PAIR && tile + 1 < last) ? tile + 1 : tile;
+        int64_t b0, tm0, tn0, b1, tm1, tn1;
+        coords(tile, b0, tm0, tn0);
+        if (PAIR) {
+            coords(tile1, b1, tm1, tn1);
+        } else {
+            b1 = b0;
+            tm1 = tm0;
+            tn1 = tn0;
         }
-        // columns j0.. of op(B_b): contiguous for op = N
-        const int64_t kb = (P.strideB ? b : 0) * P.tiles_n + tn;
-        if (kb != keyB) {
+        // the tile whose values this lane loads
+        const int64_t b = half ? b1 : b0, tm = half ? tm1 : tm0, tn = half ? tn1 : tn0;
+        // operand tiles as cache keys: rows tm.. of op(A_b), columns tn.. of
+        // op(B_b) (a zero stride shares the operand across the batch)
+        const int64_t ka0 = (P.strideA ? b0 : 0) * P.tiles_m + tm0, ka1 = (P.strideA ? b1 : 0) * P.tiles_m + tm1;
+        if (ka0 != keyA0 || ka1 != keyA1) {
+            // rows tm.. of op(A_b): contiguous in memory for op = T
             double x[8];
-            load8(P.B + b * P.strideB, P.ldb, P.transb == 0, j0 + vi, P.n, P.k, kq, x);
-            encode8<SMAX, EXT>(x, P, Q, fb, EB, badB);
-            keyB = kb;
+            load8(P.A + b * P.strideA, P.lda, P.transa != 0, tm * 16 + vi, P.m, P.k, kq, x);
+            encode8<SMAX, EXT, PAIR>(x, P, Q, fa, DA, badA);
+            keyA0 = ka0;
+            keyA1 = ka1;
+        }
+        const int64_t kb0 = (P.strideB ? b0 : 0) * P.tiles_n + tn0, kb1 = (P.strideB ? b1 : 0) * P.tiles_n + tn1;
+        if (kb0 != keyB0 || kb1 != keyB1) {
+            // columns tn.. of op(B_b): contiguous for op = N
+            double x[8];
+            load8(P.B + b * P.strideB, P.ldb, P.transb == 0, tn * 16 + vi, P.n, P.k, kq, x);
+            encode8<SMAX, EXT, PAIR>(x, P, Q, fb, EB, badB);
+            keyB0 = kb0;
+            keyB1 = kb1;
         }
 
-        Crt<NL> acc[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e].init();
-        const v4i zero = {0, 0, 0, 0};
+        for (int h = 0; h < STEP; ++h) {
+            if (h == 1 && tile1 == tile) break;
+            const long amask = (!PAIR || half == h) ? -1L : 0L;
+            Crt<NL> acc[4];
 #pragma unroll
-        for (int t = 0; t < SMAX; t += 2) {
-            if (t < P.s) {
-                const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t], fb[t], zero, 0, 0, 0);
-                const bool two = t + 1 < P.s;
-                const v4i cb = two ? __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1], fb[t + 1], zero, 0, 0, 0) : zero;
-                const ModConst& C0 = Q.q[t];
-                const ModConst& C1 = Q.q[t + 1];
+            for (int e = 0; e < 4; ++e) acc[e].init();
+            const v4i zero = {0, 0, 0, 0};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t ra = acc_mod(ca[e], C0);
-                    const uint32_t rb = two ? acc_mod(cb[e], C1) : 0u;
-                    acc[e].add2(ra, rb, Q.Y2[t >> 1], Q.W2[t >> 1]);
+            for (int t = 0; t < SMAX; t += 2) {
+                if (t < P.s) {
+                    const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t] & amask, fb[t], zero, 0, 0, 0);
+                    const bool two = t + 1 < P.s;
+                    const v4i cb = two ? __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero,
+                                                                               0, 0, 0)
+                                       : zero;
+                    const ModConst& C0 = Q.q[t];
+                    const ModConst& C1 = Q.q[t + 1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t ra = acc_mod(ca[e], C0);
+                        const uint32_t rb = two ? acc_mod(cb[e], C1) : 0u;
+                        acc[e].add2(ra, rb, Q.Y2[t >> 1], Q.W2[t >> 1]);
+                    }
                 }
             }
-        }
 
-        // entry (row 4 kq + e, column vi) of the tile
-        const int64_t col = j0 + vi;
-        double* Cb = P.C + b * P.strideC;
+            // entry (row 4 (lane / 16) + e, column vi) of tile + h; the
+            // exponents of its rows and column sit in the lanes of half h
+            const int64_t ob = h ? b1 : b0, otm = h ? tm1 : tm0, otn = h ? tn1 : tn0;
+            const int64_t col = otn * 16 + vi;
+            const int Ec = PAIR ? __shfl(EB, 32 * h + vi) : EB;
+            const bool badc = PAIR ? __shfl((int)badB, 32 * h + vi) != 0 : badB;
+            double* Cb = P.C + ob * P.strideC;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = 4 * kq + e;
-            const int Dr = __shfl(DA, r);
-            const bool badr = __shfl((int)badA, r) != 0;
-            uint32_t w[NL];
-            acc[e].finish(Q.M16, w);
-            double x = words_to_double<NL>(w, Dr + EB);
-            if (badr || badB) x = __builtin_nan("");
-            const int64_t row = i0 + r;
-            if (row < P.m && col < P.n) {
-                double* c = Cb + row + col * P.ldc;
-                const double t1 = P.alpha * x;
-                if (BETA) {
-                    const double t2 = P.beta * c[0];
-                    c[0] = t1 + t2;
-                } else {
-                    c[0] = t1;
+            for (int e = 0; e < 4; ++e) {
+                const int r = 4 * (lane >> 4) + e;
+                const int Dr = __shfl(DA, 32 * h + r);
+                const bool badr = __shfl((int)badA, 32 * h + r) != 0;
+                uint32_t w[NL];
+                acc[e].finish(Q.M16, w);
+                double x = words_to_double<NL>(w, Dr + Ec);
+                if (badr || badc) x = __builtin_nan("");
+                const int64_t row = otm * 16 + r;
+                if (row < P.m && col < P.n) {
+                    double* c = Cb + row + col * P.ldc;
+                    const double t1 = P.alpha * x;
+                    if (BETA) {
+                        const double t2 = P.beta * c[0];
+                        c[0] = t1 + t2;
+                    } else {
+                        c[0] = t1;
+                    }
                 }
             }
         }
     }
 }
 
-template <int NL>
+template <int NL, bool PAIR>
 hipError_t small_go(const SmallParams& P, bool beta, hipStream_t st) {
     const int64_t waves = (P.tiles_total + P.tiles_per_wave - 1) / P.tiles_per_wave;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
     if (beta)
-        hipLaunchKernelGGL((small_gemm_kernel<NL, true>), grid, block, 0, st, P);
+        hipLaunchKernelGGL((small_gemm_kernel<NL, true, PAIR>), grid, block, 0, st, P);
     else
-        hipLaunchKernelGGL((small_gemm_kernel<NL, false>), grid, block, 0, st, P);
+        hipLaunchKernelGGL((small_gemm_kernel<NL, false, PAIR>), grid, block, 0, st, P);
     return hipGetLastError();
+}
+
+template <int NL>
+hipError_t small_go(const SmallParams& P, bool beta, hipStream_t st) {
+    return P.k <= 16 ? small_go<NL, true>(P, beta, st) : small_go<NL, false>(P, beta, st);
 }
 
 }  // namespace
@@ -243,6 +294,9 @@ hipError_t launch_small_gemm(SmallParams P, int NL, bool beta_nonzero, hipStream
     const int64_t target_waves = 8192;
     P.tiles_per_wave = (int)((P.tiles_total + target_waves - 1) / target_waves);
     if (P.tiles_per_wave < 1) P.tiles_per_wave = 1;
+    // k <= 16 takes tiles in pairs: an even run leaves no half-empty pair
+    // except at the very end
+    if (P.k <= 16) P.tiles_per_wave += P.tiles_per_wave & 1;
     switch (NL) {
         case 2: return small_go<2>(P, beta_nonzero, st);
         case 3: return small_go<3>(P, beta_nonzero, st);
