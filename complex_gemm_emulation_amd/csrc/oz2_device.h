@@ -46,19 +46,24 @@ __device__ __forceinline__ int scale_of(uint64_t amax, int t, bool& bad) {
     return (bad || amax == 0) ? 0 : t - frexp_exp_bits(amax);
 }
 
+// |rint(sig 2^sh)| for sh < 0, ties to even, branch-free: a right shift by
+// n = -sh, clamped to [1, 63] (sig < 2^53, so n >= 63 leaves q = 0 and a
+// remainder below half, which is the right result for every n >= 54)
+__device__ __forceinline__ uint64_t rint_shift_right(uint64_t sig, int sh) {
+    const int n = min(max(-sh, 1), 63);
+    const uint64_t q = sig >> n;
+    const uint64_t rem = sig & ((1ull << n) - 1);
+    const uint64_t half = 1ull << (n - 1);
+    return q + (uint64_t)((rem > half) | ((rem == half) & (uint32_t)(q & 1)));
+}
+
 // |rint(a 2^D)| for |a 2^D| < 2^61 (the standard width, t <= 61)
 __device__ __forceinline__ uint64_t rint_scaled_mag64(uint64_t bits, int D) {
     const int eb = (int)((bits >> 52) & 0x7ff);
     const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
     const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
     const int sh = (eb ? eb - 1075 : -1074) + D;
-    if (sh >= 0) return sig << sh;
-    const int n = -sh;
-    if (n > 63) return 0;
-    const uint64_t q = sig >> n;
-    const uint64_t rem = sig & ((1ull << n) - 1);
-    const uint64_t half = 1ull << (n - 1);
-    return q + (uint64_t)((rem > half) | ((rem == half) & (uint32_t)(q & 1)));
+    return sh >= 0 ? sig << (sh & 63) : rint_shift_right(sig, sh);
 }
 
 // |rint(a 2^D)| for |a 2^D| < 2^100 (the extended width)
@@ -67,8 +72,7 @@ __device__ __forceinline__ unsigned __int128 rint_scaled_mag128(uint64_t bits, i
     const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
     const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
     const int sh = (eb ? eb - 1075 : -1074) + D;
-    if (sh >= 0) return (unsigned __int128)sig << sh;
-    return (unsigned __int128)rint_scaled_mag64(bits, D);
+    return sh >= 0 ? (unsigned __int128)sig << (sh & 127) : (unsigned __int128)rint_shift_right(sig, sh);
 }
 
 __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {

@@ -52,20 +52,21 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
 }
 
 // per-modulus constants, staged in LDS once per block: read at uniform
-// addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes
+// addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes.
+// Past the last modulus every field is zero.
 struct ModConst {
-    uint32_t mod, rcp_lo, rcp_hi, K128;  // rcp: the two words of fl64(1 / m); K128 = K_m + 128
+    float fm, frcp, fhalf, foffb;   // m, fl32(1 / m), fl32(1 / m) / 2, residue_word's offset
+    uint32_t K128;                  // K_m + 128 (residue_word)
     uint32_t c4[kExtWords];
-    float frcp, foffb;                   // residue_word's constants
 };
-static_assert(offsetof(ModConst, foffb) == 4 * (5 + kExtWords), "staging order of ModConst");
+constexpr int kTableWords = (kMaxS / 2) * kMaxLimb16 + kMaxLimb16 + kMaxS / 2;
 struct SmallConsts {
-    ModConst q[kMaxS + 1];            // one zeroed entry past the last modulus
+    ModConst q[kMaxS + 1];
     uint32_t W2[kMaxS / 2][kMaxLimb16];
     uint32_t M16[kMaxLimb16];
     uint32_t Y2[kMaxS / 2];
 };
-static_assert(offsetof(SmallConsts, Y2) == offsetof(SmallConsts, M16) + 4 * kMaxLimb16, "staging order");
+static_assert(sizeof(SmallConsts) == sizeof(ModConst) * (kMaxS + 1) + 4 * kTableWords, "table layout");
 
 // exponent of the vector held by lanes l, l^16, l^32, l^48 (PAIR: l, l^16,
 // the lanes of one tile) and the residue bytes of this lane's 8 values for
@@ -90,20 +91,22 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
     for (int t = 0; t < SMAX; ++t) {
         if (t < P.s) {
             const ModConst& C = Q.q[t];
-            const float m = (float)C.mod;
-            const uint32_t w0 = residue_word<EXT>(L, C.K128, C.c4, m, C.frcp, C.foffb);
-            const uint32_t w1 = residue_word<EXT>(L + 4, C.K128, C.c4, m, C.frcp, C.foffb);
+            const uint32_t w0 = residue_word<EXT>(L, C.K128, C.c4, C.fm, C.frcp, C.foffb);
+            const uint32_t w1 = residue_word<EXT>(L + 4, C.K128, C.c4, C.fm, C.frcp, C.foffb);
             frag[t] = (long)((uint64_t)w0 | ((uint64_t)w1 << 32));
         }
     }
 }
 
-// INT32 accumulator -> [0, m), exact in FP64 as in the residue GEMM:
-// r = acc - m floor((acc + 1/2) / m), |acc| < 2^31
+// INT32 accumulator -> [0, m): r = acc - m floor((acc + 1/2) / m) in FP32.
+// With k <= 32 and residues of magnitude <= 128, |acc| <= 2^19, so acc is
+// exact in FP32; (acc + 1/2) / m lies at least 1 / (2m) from an integer, and
+// fma(acc, fl32(1/m), fl32(1/m) / 2) is within 2^-5 / m + 2^-11 of it for
+// m >= 64 (every modulus here is >= 157), so the floor and r are exact.
+// Past the last modulus (all constants 0) it returns acc, which is 0 there.
 __device__ __forceinline__ uint32_t acc_mod(int32_t acc, const ModConst& C) {
-    const double a = (double)acc, m = (double)C.mod;
-    const double rcp = __hiloint2double((int)C.rcp_hi, (int)C.rcp_lo);
-    return (uint32_t)(int)fma(-m, floor(fma(a, rcp, 0.5 * rcp)), a);
+    const float a = (float)acc;
+    return (uint32_t)fmaf(-C.fm, floorf(fmaf(a, C.frcp, C.fhalf)), a);
 }
 
 // PAIR (k <= 16): the instruction's k of 32 holds two tiles.  Lanes 0-31
@@ -128,46 +131,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
     __shared__ SmallConsts Q;
     {
         // stage the constant tables (a few hundred words) in LDS
-        uint32_t* dst = (uint32_t*)&Q;
-        constexpr int nq = (int)(sizeof(ModConst) / 4);
-        for (int i = threadIdx.x; i < (int)(sizeof(SmallConsts) / 4); i += blockDim.x) {
-            uint32_t v = 0u;
-            if (i < (kMaxS + 1) * nq) {
-                const int t = i / nq, f = i % nq;
-                if (t < P.s) {
-                    if (f == 0) v = P.mod[t];
-                    else if (f == 1) v = (uint32_t)__double2loint(P.rcp[t]);
-                    else if (f == 2) v = (uint32_t)__double2hiint(P.rcp[t]);
-                    else if (f == 3) v = P.K[t] + 128u;
-                    else if (f < 4 + kExtWords) v = P.c[t][f - 4];
-                    else if (f == 4 + kExtWords) v = __float_as_uint(P.frcp[t]);
-                    else v = __float_as_uint(P.foffb[t]);
-                }
-            } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16) {
-                const int j = i - (kMaxS + 1) * nq;
-                v = P.W2[j / kMaxLimb16][j % kMaxLimb16];
-            } else if (i < (kMaxS + 1) * nq + (kMaxS / 2) * kMaxLimb16 + kMaxLimb16) {
-                v = P.M16[i - (kMaxS + 1) * nq - (kMaxS / 2) * kMaxLimb16];
-            } else {
-                v = P.Y2[i - (kMaxS + 1) * nq - (kMaxS / 2 + 1) * kMaxLimb16];
+        const int i = threadIdx.x;
+        if (i <= kMaxS) {
+            ModConst c{};
+            if (i < P.s) {
+                c.fm = (float)P.mod[i];
+                c.frcp = P.frcp[i];
+                c.fhalf = 0.5f * P.frcp[i];
+                c.foffb = P.foffb[i];
+                c.K128 = P.K[i] + 128u;
+#pragma unroll
+                for (int l = 0; l < kExtWords; ++l) c.c4[l] = P.c[i][l];
             }
-            dst[i] = v;
+            Q.q[i] = c;
+        }
+        for (int j = i; j < kTableWords; j += blockDim.x) {
+            uint32_t v;
+            if (j < (kMaxS / 2) * kMaxLimb16) v = P.W2[j / kMaxLimb16][j % kMaxLimb16];
+            else if (j < (kMaxS / 2 + 1) * kMaxLimb16) v = P.M16[j - (kMaxS / 2) * kMaxLimb16];
+            else v = P.Y2[j - (kMaxS / 2 + 1) * kMaxLimb16];
+            (&Q.W2[0][0])[j] = v;
         }
         __syncthreads();
     }
 
+    // fragments past the last modulus stay zero, so that the moduli can be
+    // taken in pairs without a guard
     long fa[SMAX], fb[SMAX];
+#pragma unroll
+    for (int t = 0; t < SMAX; ++t) fa[t] = fb[t] = 0;
     int DA = 0, EB = 0;
     bool badA = false, badB = false;
     // operand tiles held in fa / fb, for the first and the second tile of a pair
     int64_t keyA0 = -1, keyA1 = -1, keyB0 = -1, keyB1 = -1;
 
-    // batch entry and tile coordinates of a tile index (wave-uniform: scalar)
-    auto coords = [&](int64_t tile, int64_t& b, int64_t& tm, int64_t& tn) {
-        b = tile / per_batch;
-        const int64_t rem = tile - b * per_batch;
-        tm = rem / P.tiles_n;
-        tn = rem - tm * P.tiles_n;
+    // batch entry and tile coordinates (wave-uniform: scalar registers), one
+    // division at the start of the run, then stepped tile by tile
+    int64_t cb = first / per_batch, ctm = 0, ctn = 0;
+    {
+        const int64_t rem = first - cb * per_batch;
+        ctm = rem / P.tiles_n;
+        ctn = rem - ctm * P.tiles_n;
+    }
+    auto step = [&](int64_t& b, int64_t& tm, int64_t& tn) {
+        if (++tn == P.tiles_n) {
+            tn = 0;
+            if (++tm == P.tiles_m) {
+                tm = 0;
+                ++b;
+            }
+        }
     };
 
     for (int64_t tile = first; tile < last; tile += STEP) {
@@ -175,15 +188,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
         asm volatile("" ::: "memory");
         // a lone last tile fills both halves with itself
         const int64_t tile1 = (PAIR && tile + 1 < last) ? tile + 1 : tile;
-        int64_t b0, tm0, tn0, b1, tm1, tn1;
-        coords(tile, b0, tm0, tn0);
-        if (PAIR) {
-            coords(tile1, b1, tm1, tn1);
-        } else {
-            b1 = b0;
-            tm1 = tm0;
-            tn1 = tn0;
-        }
+        const int64_t b0 = cb, tm0 = ctm, tn0 = ctn;
+        int64_t b1 = b0, tm1 = tm0, tn1 = tn0;
+        if (tile1 != tile) step(b1, tm1, tn1);
+        cb = b1;
+        ctm = tm1;
+        ctn = tn1;
+        step(cb, ctm, ctn);
         // the tile whose values this lane loads
         const int64_t b = half ? b1 : b0, tm = half ? tm1 : tm0, tn = half ? tn1 : tn0;
         // operand tiles as cache keys: rows tm.. of op(A_b), columns tn.. of
@@ -218,19 +229,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
 #pragma unroll
             for (int t = 0; t < SMAX; t += 2) {
                 if (t < P.s) {
+                    // past the last modulus: zero fragments, constants and limbs
                     const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t] & amask, fb[t], zero, 0, 0, 0);
-                    const bool two = t + 1 < P.s;
-                    const v4i cb = two ? __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero,
-                                                                               0, 0, 0)
-                                       : zero;
+                    const v4i cb = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero, 0, 0, 0);
                     const ModConst& C0 = Q.q[t];
                     const ModConst& C1 = Q.q[t + 1];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t ra = acc_mod(ca[e], C0);
-                        const uint32_t rb = two ? acc_mod(cb[e], C1) : 0u;
-                        acc[e].add2(ra, rb, Q.Y2[t >> 1], Q.W2[t >> 1]);
-                    }
+                    for (int e = 0; e < 4; ++e)
+                        acc[e].add2(acc_mod(ca[e], C0), acc_mod(cb[e], C1), Q.Y2[t >> 1], Q.W2[t >> 1]);
                 }
             }
 
