@@ -213,6 +213,8 @@ __device__ __forceinline__ uint32_t add_mod_bytes(uint32_t a, uint32_t b, uint32
     return out;
 }
 
+typedef double v2d __attribute__((ext_vector_type(2)));
+
 // A wavefront reconstructs 256 consecutive rows of one column (mp is a
 // multiple of 256), 4 entries per lane; the column index is wave-uniform.
 template <int NL, bool CPLX, bool BETA>
@@ -268,39 +270,51 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
 
     bool badB;
     const int E = scale_of(P.amaxB[j], P.t, badB);
+    // the four entries' results (rows past m are computed from padding and
+    // not stored: amaxA has mp entries)
+    double x[4][2];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t i = i0 + e;
-        if (i >= P.m) break;
         bool badA;
         const int D = scale_of(P.amaxA[i], P.t, badA);
-        double x[2];
 #pragma unroll
         for (int o = 0; o < (CPLX ? 2 : 1); ++o) {
             uint32_t w[NL];
             acc[o][e].finish(P.M16, w);
-            if (P.chat) {
+            if (P.chat && i < P.m) {
                 uint32_t* dst = P.chat + (((int64_t)o * P.n + j) * P.mp + i) * NL;
 #pragma unroll
                 for (int q = 0; q < NL; ++q) dst[q] = w[q];
             }
-            x[o] = words_to_double<NL>(w, D + E);
-            if (badA || badB) x[o] = __builtin_nan("");
+            x[e][o] = words_to_double<NL>(w, D + E);
+            if (badA || badB) x[e][o] = __builtin_nan("");
         }
-        double* c = P.C + (CPLX ? 2 : 1) * (i + j * P.ldc);
+    }
+    // alpha / beta epilogue, every operation rounded separately
+    double out[4][2];
+    double* c0 = P.C + (CPLX ? 2 : 1) * (i0 + j * P.ldc);
+    const bool full = i0 + 3 < P.m;
+    // the lane's four entries are 32 (complex: 64) contiguous bytes: 16-byte
+    // stores when they are 16-byte aligned (wave-uniform: depends on j)
+    const bool vec = full && (((uintptr_t)c0 & 15u) == 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (!vec && i0 + e >= P.m) break;
+        const double* c = c0 + (CPLX ? 2 : 1) * e;
         if (!CPLX) {
-            const double t1 = P.alpha[0] * x[0];
+            const double t1 = P.alpha[0] * x[e][0];
             if (BETA) {
                 const double t2 = P.beta[0] * c[0];
-                c[0] = t1 + t2;
+                out[e][0] = t1 + t2;
             } else {
-                c[0] = t1;
+                out[e][0] = t1;
             }
         } else {
             const double ar = P.alpha[0], ai = P.alpha[1];
-            const double t1 = ar * x[0], t2 = ai * x[1];
+            const double t1 = ar * x[e][0], t2 = ai * x[e][1];
             const double ure = t1 - t2;
-            const double t3 = ar * x[1], t4 = ai * x[0];
+            const double t3 = ar * x[e][1], t4 = ai * x[e][0];
             const double uim = t3 + t4;
             if (BETA) {
                 const double br = P.beta[0], bi = P.beta[1];
@@ -309,12 +323,30 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
                 const double vre = t5 - t6;
                 const double t7 = br * ci, t8 = bi * cr;
                 const double vim = t7 + t8;
-                c[0] = ure + vre;
-                c[1] = uim + vim;
+                out[e][0] = ure + vre;
+                out[e][1] = uim + vim;
             } else {
-                c[0] = ure;
-                c[1] = uim;
+                out[e][0] = ure;
+                out[e][1] = uim;
             }
+        }
+    }
+    if (vec) {
+        v2d* d = (v2d*)c0;
+        if (!CPLX) {
+            d[0] = v2d{out[0][0], out[1][0]};
+            d[1] = v2d{out[2][0], out[3][0]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] = v2d{out[e][0], out[e][1]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (i0 + e >= P.m) break;
+            double* c = c0 + (CPLX ? 2 : 1) * e;
+            c[0] = out[e][0];
+            if (CPLX) c[1] = out[e][1];
         }
     }
 }
