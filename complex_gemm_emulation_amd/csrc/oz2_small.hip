@@ -38,6 +38,7 @@ namespace {
 
 using namespace dev;
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef double v2d __attribute__((ext_vector_type(2)));
 
 // the 8 values of lane l: vector v, k = 8 kq .. 8 kq + 7 (zero outside)
 __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, int64_t v, int64_t nvec,
@@ -246,7 +247,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
             const int64_t col = otn * 16 + vi;
             const int Ec = PAIR ? __shfl(EB, 32 * h + vi) : EB;
             const bool badc = PAIR ? __shfl((int)badB, 32 * h + vi) != 0 : badB;
-            double* Cb = P.C + ob * P.strideC;
+            // the lane's four rows are contiguous in C: two 16-byte stores
+            // when they are all in range and 16-byte aligned
+            const int64_t row0 = otm * 16 + 4 * (lane >> 4);
+            double* c0 = P.C + ob * P.strideC + row0 + col * P.ldc;
+            const bool vec = row0 + 3 < P.m && col < P.n && (((uintptr_t)c0 & 15u) == 0);
+            double out[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * (lane >> 4) + e;
@@ -256,17 +262,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
                 acc[e].finish(Q.M16, w);
                 double x = words_to_double<NL>(w, Dr + Ec);
                 if (badr || badc) x = __builtin_nan("");
-                const int64_t row = otm * 16 + r;
-                if (row < P.m && col < P.n) {
-                    double* c = Cb + row + col * P.ldc;
-                    const double t1 = P.alpha * x;
-                    if (BETA) {
-                        const double t2 = P.beta * c[0];
-                        c[0] = t1 + t2;
-                    } else {
-                        c[0] = t1;
-                    }
+                const bool in = row0 + e < P.m && col < P.n;
+                const double t1 = P.alpha * x;
+                if (BETA) {
+                    const double t2 = P.beta * (in ? c0[e] : 0.0);
+                    out[e] = t1 + t2;
+                } else {
+                    out[e] = t1;
                 }
+            }
+            if (vec) {
+                ((v2d*)c0)[0] = v2d{out[0], out[1]};
+                ((v2d*)c0)[1] = v2d{out[2], out[3]};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (row0 + e < P.m && col < P.n) c0[e] = out[e];
             }
         }
     }

@@ -200,3 +200,32 @@ def test_crt_hook_random_exact_integers(handle, s):
     w = from_dev(words).view(np.uint32).reshape(count, nl)
     for q, v in enumerate(vals):
         assert words_to_int(w[q]) == v, (s, q, v)
+
+
+@pytest.mark.parametrize("m,n,k,ldc", [(300, 77, 130, 300), (300, 77, 130, 301), (16, 200, 16, 18)],
+                         ids=["four-phase-ldc-even", "four-phase-ldc-odd", "fused-k16"])
+def test_c_base_only_8_byte_aligned(handle, m, n, k, ldc):
+    # C starting one double into its allocation: the 16-byte store path of
+    # the reconstruct and fused kernels must fall back to 8-byte stores
+    import torch
+    rng = np.random.default_rng(m * 7 + ldc)
+    A = workloads.real_matrix(m, k, int(rng.integers(1 << 30)), "phi", 1.0)
+    B = workloads.real_matrix(k, n, int(rng.integers(1 << 30)), "phi", 1.0)
+    C = workloads.real_matrix(ldc, n, int(rng.integers(1 << 30)), "uniform")
+    buf = np.concatenate([[7.0], C, [9.0]])
+    dbuf = to_dev(buf)
+    dC = dbuf[1:1 + ldc * n]
+    assert dC.data_ptr() % 16 == 8
+    _say(f"[dgemm] C base +8 bytes m={m} n={n} k={k} ldc={ldc}")
+    handle.set_debug(False)  # this module runs in debug mode, which bypasses the fused path
+    try:
+        handle.dgemm("N", "N", m, n, k, -0.5, to_dev(A), m, to_dev(B), k, 1.25, dC, ldc, 12)
+        torch.cuda.synchronize()
+    finally:
+        handle.set_debug(True)
+    got = from_dev(dbuf)
+    assert got[0] == 7.0 and got[-1] == 9.0
+    full = got[1:-1].reshape(n, ldc)
+    want = oracle.gemm_entries(False, "N", "N", m, n, k, -0.5, A, m, B, k, 1.25, C, ldc, 12)["out"]
+    check_float_parity(full[:, :m].T, want.reshape(n, m).T, f"C+8 {m}x{n}x{k} ldc={ldc}")
+    assert np.array_equal(full[:, m:], C.reshape(n, ldc)[:, m:])
