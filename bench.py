@@ -56,6 +56,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_VALU_TOPS = 157.3 / 2
 GEMM_SOURCE = os.path.join(ROOT, "complex_gemm_emulation_amd", "csrc", "oz2_gemm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "residue_gemm_traffic.json")
+SMALL_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "small_gemm_traffic.json")
 COPY_CAL_BYTES = 1 << 30     # bytes read (and written) by the calibration copy
 METRIC = "emulated DGEMM TFLOP/s at N=8192, s=8/12/16 (+ INT8 MFMA util, HBM GB/s)"
 
@@ -84,16 +85,26 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per residue-GEMM launch from the committed counter runs of
-    this workload, or None when the kernel source changed since they were
-    taken (or none were taken for this workload)."""
+def measured_traffic(workload, traffic_file=TRAFFIC_FILE):
+    """HBM bytes per launch of the bench's dominant kernel from the committed
+    counter runs of this workload, or None when the kernel's sources changed
+    since they were taken (or none were taken for this workload).  A record
+    names its sources (several files hashed in order) or, for the residue
+    GEMM, hashes oz2_gemm.hip."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256_16") != source_digest(GEMM_SOURCE) or rec.get("bench_workload") != workload:
+    if "sources" in rec:
+        h = hashlib.sha256()
+        for rel in rec["sources"]:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        digest = h.hexdigest()[:16]
+    else:
+        digest = source_digest(GEMM_SOURCE)
+    if rec.get("source_sha256_16") != digest or rec.get("bench_workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -620,7 +631,7 @@ def run_chain(args):
     achieved = bytes_per_launch / (lm * 1e-3) / 1e9
     roofline = dict(kernel="small_gemm_kernel (fused short-k Ozaki II, mode 3)", bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=None,
+                    frac=round(achieved / PEAK_HBM_GBS, 4), traffic=measured_traffic("chain", SMALL_TRAFFIC_FILE),
                     bytes_per_launch=bytes_per_launch, launch_ms=round(lm, 4))
     cpu = None
     if not args.no_cpu_baseline:
