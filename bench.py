@@ -187,6 +187,66 @@ def exact_dot(a, b):
     return _int_to_double(tot, e0)
 
 
+def exact_dot_fraction(a, b):
+    """sum_p a_p b_p of two double vectors as an exact Fraction"""
+    from fractions import Fraction
+    qa, ea = _dyadic(a)
+    qb, eb = _dyadic(b)
+    e = ea + eb
+    e0 = int(e.min())
+    tot = 0
+    for x, y, z in zip(qa.tolist(), qb.tolist(), (e - e0).tolist()):
+        tot += (x * y) << z
+    return Fraction(tot) * (Fraction(2) ** e0)
+
+
+def general_accuracy(h, spec, A, B, C, s, count=32, seed=4242):
+    """Normwise relative error of one call C <- alpha op(A) op(B) + beta C on
+    a fresh copy of C (the timed steps overwrite C) at `count` seeded entries
+    (first and last included), against alpha op(A) op(B) + beta C formed
+    exactly in rationals and rounded once; complex entries count both parts."""
+    import torch
+    from fractions import Fraction
+    m, n, k, cplx = spec["m"], spec["n"], spec["k"], spec["cplx"]
+    ta, tb = spec["transa"], spec["transb"]
+    ra = m if ta == "N" else k
+    rb = k if tb == "N" else n
+    dC = torch.from_numpy(C.copy()).cuda()
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    if cplx:
+        h.zgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
+    else:
+        h.dgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
+    torch.cuda.synchronize()
+    got_all = dC.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    ii = np.concatenate([[0, m - 1], rng.choice(m, count - 2)])
+    jj = np.concatenate([[0, n - 1], rng.choice(n, count - 2)])
+    Am = A.reshape(k, m).T if ta == "N" else A.reshape(m, k)   # Am[i] = row i of op(A) before conj
+    Bm = B.reshape(n, k) if tb == "N" else B.reshape(k, n).T   # Bm[j] = column j of op(B) before conj
+    al, be = complex(spec["alpha"]), complex(spec["beta"])
+    Far, Fai, Fbr, Fbi = (Fraction(x) for x in (al.real, al.imag, be.real, be.imag))
+    got, ref = [], []
+    for i, j in zip(ii, jj):
+        a, b = Am[i], Bm[j]
+        c = C[i + j * m]
+        if cplx:
+            if ta == "C":
+                a = np.conj(a)
+            if tb == "C":
+                b = np.conj(b)
+            pr = exact_dot_fraction(a.real, b.real) - exact_dot_fraction(a.imag, b.imag)
+            pi = exact_dot_fraction(a.real, b.imag) + exact_dot_fraction(a.imag, b.real)
+            cr, ci = Fraction(c.real), Fraction(c.imag)
+            ref += [float(Far * pr - Fai * pi + Fbr * cr - Fbi * ci), float(Far * pi + Fai * pr + Fbr * ci + Fbi * cr)]
+            g = got_all[i + j * m]
+            got += [g.real, g.imag]
+        else:
+            ref.append(float(Far * exact_dot_fraction(a, b) + Fbr * Fraction(float(c))))
+            got.append(got_all[i + j * m])
+    return normwise_error(got, ref), f"{count} seeded entries of one call on a fresh C vs alpha op(A) op(B) + beta C formed exactly"
+
+
 def normwise_error(got, ref):
     got, ref = np.asarray(got), np.asarray(ref)
     return float(np.sqrt(np.sum((got - ref) ** 2) / np.sum(ref ** 2)))
@@ -352,6 +412,13 @@ def run_gemm(args, name):
         log(f"[bench] accuracy of the s={s_list[-1]} result on sampled entries")
         err, how = gemm_accuracy(dC, A, B, m, n, k, ta, tb)
         accuracy = {"normwise_rel_err": err, "s": s_list[-1], "sample": how}
+    elif not prepared:
+        accuracy = {}
+        for s in s_list:
+            log(f"[bench] accuracy of one s={s} call on sampled entries")
+            err, how = general_accuracy(handles[s], spec, A, B, C, s)
+            accuracy[str(s)] = err
+        accuracy["sample"] = how
 
     for pa, pb in prepared.values():
         pa.close()
