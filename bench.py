@@ -420,6 +420,10 @@ def run_gemm(args, name):
             accuracy[str(s)] = err
         accuracy["sample"] = how
 
+    native = None
+    if not args.no_native:
+        native = native_fp64_rate(torch, dA, dB, m, n, k, ta, tb, cplx)
+
     for pa, pb in prepared.values():
         pa.close()
         pb.close()
@@ -441,8 +445,38 @@ def run_gemm(args, name):
         "per_s": per_s,
         "accuracy": accuracy,
         "roofline": roofline,
+        "native_fp64": native,
         "cpu_baseline": cpu,
     }
+
+
+def native_fp64_rate(torch, dA, dB, m, n, k, ta, tb, cplx, reps=5):
+    """Context, not a target: the same product in native FP64 (complex128)
+    with torch.matmul on the same GPU, which the pages use as the
+    denominator of their speed-ups.  Median of `reps` timed calls."""
+    def op(X, rows, cols, t):
+        Xm = X.reshape(cols, rows).T          # column-major rows x cols
+        if t == "N":
+            return Xm
+        return Xm.T.conj() if t == "C" else Xm.T
+    A = op(dA, m if ta == "N" else k, k if ta == "N" else m, ta).contiguous()
+    B = op(dB, k if tb == "N" else n, n if tb == "N" else k, tb).contiguous()
+    for _ in range(2):
+        C = A @ B
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        C = A @ B
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del C, A, B
+    ms = float(np.median(times))
+    fl = (8.0 if cplx else 2.0) * m * n * k
+    return {"tflops": round(fl / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 3),
+            "how": f"torch.matmul in {'complex128' if cplx else 'float64'}, median of {reps}"}
 
 
 def run_nonsquare(args):
@@ -744,6 +778,7 @@ def main():
     ap.add_argument("--chain-acc-tensors", type=int, default=8)
     ap.add_argument("--chain-depth", type=int, default=3, help="chain_rbe: operators (3 = one pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-native", action="store_true", help="skip timing the native FP64 product (context)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -767,7 +802,7 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
             "data": "synthetic", "config": out["config"]}
-    for key in ("per_s", "per_shape", "accuracy", "roofline", "cpu_baseline"):
+    for key in ("per_s", "per_shape", "accuracy", "roofline", "native_fp64", "cpu_baseline"):
         if key in out:
             line[key] = out[key]
     print(json.dumps(line))
