@@ -93,10 +93,19 @@ __device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
     const uint64_t bits = (uint64_t)__double_as_longlong(a);
     const bool neg = (bits >> 63) != 0;
     if (!EXT) {
-        const uint64_t mag = zero ? 0 : rint_scaled_mag64(bits, D);
-        const uint64_t x = neg ? (1ull << 62) - mag : (1ull << 62) + mag;
-        L.w[0] = (uint32_t)x;
-        L.w[1] = (uint32_t)(x >> 32);
+        // In FP64, exactly and branch-free: a 2^D is exact (a value that
+        // underflows is below 1/2 and rints to 0 either way), rint rounds
+        // ties to even, and the integer x (|x| <= 2^61) splits exactly into
+        // hi 2^32 + lo with 0 <= lo < 2^32; a_hat + 2^62 is then
+        // (hi + 2^30) 2^32 + lo.  Full-rate FP64 on this GPU makes this
+        // cheaper than shifting the significand.
+        const double x = __builtin_rint(__builtin_ldexp(zero ? 0.0 : a, D));
+        const double hi = __builtin_floor(x * 0x1p-32);
+        const double lo = __builtin_fma(hi, -0x1p32, x);
+        L.w[0] = (uint32_t)lo;
+        L.w[1] = (uint32_t)((int32_t)hi + (1 << 30));
+        (void)bits;
+        (void)neg;
     } else {
         const unsigned __int128 mag = zero ? 0 : rint_scaled_mag128(bits, D);
         const unsigned __int128 bias = (unsigned __int128)1 << 104;
