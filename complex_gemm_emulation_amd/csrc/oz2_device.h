@@ -5,12 +5,12 @@
 // "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
 // Ozaki Scheme II on the Xe2 Architecture":
 //   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scale_of()
-//   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
+//   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> make_limbs()
 //   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
 //             2^(limb position) mod m and a constant K_m; the page uses
 //             21-bit limbs, here byte limbs read four at a time by
-//             v_dot4_u32_u8 (the same congruence) -> make_limbs(),
-//             centred_residue()
+//             v_dot4_u32_u8 (the same congruence) -> centred_residue(),
+//             residue_word()
 //   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
 //             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
 //             top 64 bits + sticky rounded once to double -> Crt,
@@ -46,35 +46,6 @@ __device__ __forceinline__ int scale_of(uint64_t amax, int t, bool& bad) {
     return (bad || amax == 0) ? 0 : t - frexp_exp_bits(amax);
 }
 
-// |rint(sig 2^sh)| for sh < 0, ties to even, branch-free: a right shift by
-// n = -sh, clamped to [1, 63] (sig < 2^53, so n >= 63 leaves q = 0 and a
-// remainder below half, which is the right result for every n >= 54)
-__device__ __forceinline__ uint64_t rint_shift_right(uint64_t sig, int sh) {
-    const int n = min(max(-sh, 1), 63);
-    const uint64_t q = sig >> n;
-    const uint64_t rem = sig & ((1ull << n) - 1);
-    const uint64_t half = 1ull << (n - 1);
-    return q + (uint64_t)((rem > half) | ((rem == half) & (uint32_t)(q & 1)));
-}
-
-// |rint(a 2^D)| for |a 2^D| < 2^61 (the standard width, t <= 61)
-__device__ __forceinline__ uint64_t rint_scaled_mag64(uint64_t bits, int D) {
-    const int eb = (int)((bits >> 52) & 0x7ff);
-    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
-    const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
-    const int sh = (eb ? eb - 1075 : -1074) + D;
-    return sh >= 0 ? sig << (sh & 63) : rint_shift_right(sig, sh);
-}
-
-// |rint(a 2^D)| for |a 2^D| < 2^100 (the extended width)
-__device__ __forceinline__ unsigned __int128 rint_scaled_mag128(uint64_t bits, int D) {
-    const int eb = (int)((bits >> 52) & 0x7ff);
-    const uint64_t mant = bits & 0xFFFFFFFFFFFFFull;
-    const uint64_t sig = eb ? (mant | (1ull << 52)) : mant;
-    const int sh = (eb ? eb - 1075 : -1074) + D;
-    return sh >= 0 ? (unsigned __int128)sig << (sh & 127) : (unsigned __int128)rint_shift_right(sig, sh);
-}
-
 __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
     return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
 }
@@ -87,35 +58,25 @@ struct Limbs {
     uint32_t w[EXT ? kExtWords : kStdWords];
 };
 
+// In FP64, exactly and branch-free: a 2^D is exact (a value that underflows
+// is below 1/2 and rints to 0 either way) and rint rounds ties to even.  The
+// integer x (|x| <= 2^61, or 2^100 at the extended width) then splits
+// exactly into 32-bit words by floor(x 2^-32) and x - hi 2^32 (one fma, whose
+// exact result 0 <= lo < 2^32 is representable); the bias 2^62 (2^104) adds
+// 2^30 (2^8) to the signed top word.  Full-rate FP64 on this GPU makes this
+// cheaper than shifting and rounding the significand in integers.
 template <bool EXT>
 __device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
     Limbs<EXT> L;
-    const uint64_t bits = (uint64_t)__double_as_longlong(a);
-    const bool neg = (bits >> 63) != 0;
-    if (!EXT) {
-        // In FP64, exactly and branch-free: a 2^D is exact (a value that
-        // underflows is below 1/2 and rints to 0 either way), rint rounds
-        // ties to even, and the integer x (|x| <= 2^61) splits exactly into
-        // hi 2^32 + lo with 0 <= lo < 2^32; a_hat + 2^62 is then
-        // (hi + 2^30) 2^32 + lo.  Full-rate FP64 on this GPU makes this
-        // cheaper than shifting the significand.
-        const double x = __builtin_rint(__builtin_ldexp(zero ? 0.0 : a, D));
+    double x = __builtin_rint(__builtin_ldexp(zero ? 0.0 : a, D));
+    constexpr int W = EXT ? kExtWords : kStdWords;
+#pragma unroll
+    for (int i = 0; i + 1 < W; ++i) {
         const double hi = __builtin_floor(x * 0x1p-32);
-        const double lo = __builtin_fma(hi, -0x1p32, x);
-        L.w[0] = (uint32_t)lo;
-        L.w[1] = (uint32_t)((int32_t)hi + (1 << 30));
-        (void)bits;
-        (void)neg;
-    } else {
-        const unsigned __int128 mag = zero ? 0 : rint_scaled_mag128(bits, D);
-        const unsigned __int128 bias = (unsigned __int128)1 << 104;
-        const unsigned __int128 x = neg ? bias - mag : bias + mag;
-        const uint64_t lo = (uint64_t)x, hi = (uint64_t)(x >> 64);
-        L.w[0] = (uint32_t)lo;
-        L.w[1] = (uint32_t)(lo >> 32);
-        L.w[2] = (uint32_t)hi;
-        L.w[3] = (uint32_t)(hi >> 32);
+        L.w[i] = (uint32_t)__builtin_fma(hi, -0x1p32, x);
+        x = hi;
     }
+    L.w[W - 1] = (uint32_t)((int32_t)x + (EXT ? (1 << 8) : (1 << 30)));
     return L;
 }
 

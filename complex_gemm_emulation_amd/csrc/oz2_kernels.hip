@@ -5,10 +5,12 @@
 // Method: "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc
 // GPUs: Ozaki Scheme II on the Xe2 Architecture":
 //   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scan + scale_of()
-//   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> rint_scaled_*()
+//   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> make_limbs()
 //   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
-//             2^(limb position) mod m and K_m = (h_m - 2^62) mod m; no FP64 and no
-//             branches per modulus                 -> encode_kernel
+//             2^(limb position) mod m and K_m = (h_m - 2^62) mod m; no FP64
+//             and no branches in the loop over the moduli (a_hat itself is
+//             formed once per element by exact full-rate FP64 operations)
+//                                                  -> encode_kernel
 //   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
 //             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
 //             top 64 bits + sticky rounded once to double, times
