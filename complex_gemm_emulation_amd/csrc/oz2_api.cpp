@@ -113,10 +113,8 @@ int ensure_workspace(oz2_context* h, size_t bytes) {
 void fill_mod_tables(const ModuliPlan& pl, EncodeParams* E, bool ext) {
     for (int q = 0; q < pl.s; ++q) {
         E->mod[q] = (uint32_t)pl.mod[q];
-        E->h[q] = pl.h[q];
         E->K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
         E->frcp[q] = pl.frcp[q];
-        E->foff[q] = pl.foff[q];
         E->foffb[q] = pl.foffb[q];
         for (int l = 0; l < kExtWords; ++l) E->c[q][l] = pl.c4[q][l];
     }
@@ -157,7 +155,6 @@ int small_impl(oz2_context* h, const ModuliPlan& pl, int t, char transa, char tr
         P.K[q] = ext ? pl.Kext[q] : pl.Kstd[q];
         P.rcp[q] = pl.drcp[q];
         P.frcp[q] = pl.frcp[q];
-        P.foff[q] = pl.foff[q];
         P.foffb[q] = pl.foffb[q];
         for (int l = 0; l < kExtWords; ++l) P.c[q][l] = pl.c4[q][l];
     }

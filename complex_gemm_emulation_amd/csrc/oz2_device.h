@@ -46,10 +46,6 @@ __device__ __forceinline__ int scale_of(uint64_t amax, int t, bool& bad) {
     return (bad || amax == 0) ? 0 : t - frexp_exp_bits(amax);
 }
 
-__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
-    return (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b2 & 0xffu) << 16) | (b3 << 24);
-}
-
 // residue limbs of one element: the 32-bit words of a_hat + 2^62 (standard
 // width) or a_hat + 2^104 (extended width), each read as four byte limbs;
 // the sign is absorbed by the bias
@@ -80,45 +76,61 @@ __device__ __forceinline__ Limbs<EXT> make_limbs(double a, int D, bool zero) {
     return L;
 }
 
-// centred residue of a_hat in [-h, m - 1 - h] (h = floor((m - 1) / 2)):
-// v = K_m + sum_j b_j (2^(8j) mod m) over the bytes b_j of a_hat + 2^62 (or
-// 2^104), four bytes per v_dot4_u32_u8 against c4[p] (byte j of c4[p] is
-// 2^(32p + 8j) mod m), with K_m = (-2^62) mod m (or (-2^104) mod m), so
-// v = a_hat (mod m) and v < 16 255^2 + 256 < 2^20.  Then
-// r = v - m floor((v + h + 1/2) / m) in FP32: (v + h + 1/2) / m lies at least
-// 1 / (2m) from an integer, and fma(v, fl32(1/m), fl32((h + 1/2) / m)) is
-// within 2^-3 / m + 2^-24 of it, so the floor and r are exact.
+// v' = K128 + sum_j b_j (2^(8j) mod m) over the bytes b_j of a_hat + 2^62
+// (or 2^104), four bytes per v_dot4_u32_u8 against c4[p] (byte j of c4[p] is
+// 2^(32p + 8j) mod m).  With K128 = K_m + 128 and K_m = (-2^62) mod m (or
+// (-2^104) mod m), v' = a_hat + 128 (mod m), and v' < 16 255^2 + 2^9 < 2^20.
 template <bool EXT>
-__device__ __forceinline__ int centred_residue(const Limbs<EXT>& L, uint32_t K, const uint32_t* c4, float m,
-                                               float rcp, float off) {
-    uint32_t v = K;
+__device__ __forceinline__ uint32_t dot_limbs(const Limbs<EXT>& L, uint32_t K128, const uint32_t* c4) {
+    uint32_t v = K128;
 #pragma unroll
     for (int p = 0; p < (EXT ? kExtWords : kStdWords); ++p) v = __builtin_amdgcn_udot4(L.w[p], c4[p], v, false);
+    return v;
+}
+
+// offset-binary residue: f = v' - m floor((v' + hb + 1/2 - 128) / m) = r + 128
+// in [0, 255], where r is the centred residue of v' - 128 (hb = h, or 128 for
+// m = 256, whose window [-128, 127] has the same bytes as [-127, 128]).  The
+// floor argument is the one of centred_residue, and for v' < 2^21 and
+// m <= 256 the FP32 evaluation is within 2^-3 / m + 2^-11 < 1 / (2m) of it,
+// so f is exact.
+__device__ __forceinline__ float offset_residue(uint32_t v, float m, float rcp, float offb) {
     const float vf = (float)v;
-    return (int)fmaf(-m, floorf(fmaf(vf, rcp, off)), vf);
+    return fmaf(-m, floorf(fmaf(vf, rcp, offb)), vf);
 }
 
 // the centred residues of four elements (one modulus) as the four bytes of a
-// word, byte e from L[e].  In offset binary: with K128 = K_m + 128 the dot
-// products give v' = v + 128, and f = v' - m floor((v' + hb + 1/2 - 128) / m)
-// = r + 128 lies in [0, 255] (hb = h, or 128 for m = 256, whose window
-// [-128, 127] has the same bytes as [-127, 128]).  The floor argument is the
-// one of centred_residue, so f is exact; v_cvt_pk_u8_f32 puts it in byte e,
-// and XOR 0x80 per byte turns r + 128 into the two's complement byte of r.
+// word, byte e from L[e]: v_cvt_pk_u8_f32 puts each offset-binary residue
+// r + 128 in its byte, and XOR 0x80 per byte turns it into the two's
+// complement byte of r.
 template <bool EXT>
 __device__ __forceinline__ uint32_t residue_word(const Limbs<EXT>* L, uint32_t K128, const uint32_t* c4, float m,
                                                  float rcp, float offb) {
     uint32_t w = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        uint32_t v = K128;
-#pragma unroll
-        for (int p = 0; p < (EXT ? kExtWords : kStdWords); ++p) v = __builtin_amdgcn_udot4(L[e].w[p], c4[p], v, false);
-        const float vf = (float)v;
-        const float f = fmaf(-m, floorf(fmaf(vf, rcp, offb)), vf);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(f, e, w);
-    }
+    for (int e = 0; e < 4; ++e)
+        w = __builtin_amdgcn_cvt_pk_u8_f32(offset_residue(dot_limbs<EXT>(L[e], K128, c4), m, rcp, offb), e, w);
     return w ^ 0x80808080u;
+}
+
+// the same for a complex element's real and imaginary parts and their sum
+// (3M operands): the sum's v' is v'_re + v'_im - 128 < 2^21, which needs no
+// further dot products
+template <bool EXT>
+__device__ __forceinline__ void residue_words3(const Limbs<EXT>* Lr, const Limbs<EXT>* Li, uint32_t K128,
+                                               const uint32_t* c4, float m, float rcp, float offb, uint32_t& wr,
+                                               uint32_t& wi, uint32_t& ws) {
+    wr = wi = ws = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t vr = dot_limbs<EXT>(Lr[e], K128, c4), vi = dot_limbs<EXT>(Li[e], K128, c4);
+        wr = __builtin_amdgcn_cvt_pk_u8_f32(offset_residue(vr, m, rcp, offb), e, wr);
+        wi = __builtin_amdgcn_cvt_pk_u8_f32(offset_residue(vi, m, rcp, offb), e, wi);
+        ws = __builtin_amdgcn_cvt_pk_u8_f32(offset_residue(vr + vi - 128u, m, rcp, offb), e, ws);
+    }
+    wr ^= 0x80808080u;
+    wi ^= 0x80808080u;
+    ws ^= 0x80808080u;
 }
 
 // c_hat from the residues of one entry, accumulated over the moduli two at a

@@ -45,9 +45,9 @@ struct EncodeParams {
     int8_t* planes;
     int conj;                // negate imaginary parts (op = 'C')
     int t, s;
-    uint32_t mod[kMaxS], h[kMaxS], K[kMaxS];
+    uint32_t mod[kMaxS], K[kMaxS];
     uint32_t c[kMaxS][kExtWords];     // byte-limb constants (see oz2_device.h)
-    float frcp[kMaxS], foff[kMaxS];   // fl32(1 / m), fl32((h + 1/2) / m)
+    float frcp[kMaxS];                // fl32(1 / m)
     float foffb[kMaxS];               // fl32((hb + 1/2 - 128) / m) (oz2_plan.h)
 };
 
@@ -104,7 +104,7 @@ struct SmallParams {
     uint32_t mod[kMaxS], K[kMaxS];
     double rcp[kMaxS];                // fl64(1 / m)
     uint32_t c[kMaxS][kExtWords];     // byte-limb constants (see oz2_device.h)
-    float frcp[kMaxS], foff[kMaxS];   // fl32(1 / m), fl32((h + 1/2) / m)
+    float frcp[kMaxS];                // fl32(1 / m)
     float foffb[kMaxS];               // fl32((hb + 1/2 - 128) / m) (oz2_plan.h)
     uint32_t Y2[kMaxS / 2];           // round(2^16 y_t / m_t), pairs as in ReconParams
     uint32_t W2[kMaxS / 2][kMaxLimb16];  // 16-bit limbs of W_(2u) | W_(2u+1) << 16

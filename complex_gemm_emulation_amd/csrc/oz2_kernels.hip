@@ -98,12 +98,6 @@ struct EncodeTile {
     static_assert(PER_THREAD >= 1 && PER_THREAD * 256 == GROUPS, "tile/thread mismatch");
 };
 
-// (a_hat + h) mod m in [0, m), before removing the offset h
-template <bool EXT>
-__device__ __forceinline__ int residue_of(const Limbs<EXT>& L, const EncodeParams& P, int t) {
-    return centred_residue<EXT>(L, P.K[t], P.c[t], (float)P.mod[t], P.frcp[t], P.foff[t]);
-}
-
 template <bool CONTIG, bool CPLX, bool EXT>
 __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
     using T = EncodeTile<CONTIG, CPLX>;
@@ -180,22 +174,12 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
                 *(uint32_t*)(dst + t * plane) =
                     residue_word<EXT>(lr, P.K[t] + 128u, P.c[t], (float)P.mod[t], P.frcp[t], P.foffb[t]);
             } else {
-                int r[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e] = residue_of<EXT>(lr[e], P, t);
-                *(uint32_t*)(dst + t * plane) = pack4(r[0], r[1], r[2], r[3]);
-                const int m = (int)P.mod[t], lo = -(int)P.h[t], hi = m - 1 - (int)P.h[t];
-                int ri[4], rs[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ri[e] = residue_of<EXT>(li[e], P, t);
-                    // centred residue of re + im from those of re and im
-                    int x = r[e] + ri[e];
-                    x = x > hi ? x - m : x;
-                    rs[e] = x < lo ? x + m : x;
-                }
-                *(uint32_t*)(dst + P.set_stride + t * plane) = pack4(ri[0], ri[1], ri[2], ri[3]);
-                *(uint32_t*)(dst + 2 * P.set_stride + t * plane) = pack4(rs[0], rs[1], rs[2], rs[3]);
+                uint32_t wr, wi, ws;
+                residue_words3<EXT>(lr, li, P.K[t] + 128u, P.c[t], (float)P.mod[t], P.frcp[t], P.foffb[t], wr, wi,
+                                    ws);
+                *(uint32_t*)(dst + t * plane) = wr;
+                *(uint32_t*)(dst + P.set_stride + t * plane) = wi;
+                *(uint32_t*)(dst + 2 * P.set_stride + t * plane) = ws;
             }
           }
         }

@@ -207,9 +207,8 @@ void build_plan(int s, ModuliPlan* p) {
         }
         p->Kstd[t] = (m - pow2_mod(62, m)) % m;
         p->Kext[t] = (m - pow2_mod(104, m)) % m;
-        volatile float fone = 1.0f, fh = (float)h + 0.5f;
+        volatile float fone = 1.0f;
         p->frcp[t] = fone / fm;
-        p->foff[t] = fh / fm;
         // offset-binary bytes (residue + 128 in [0, 255]): m = 256 takes the
         // window [-128, 127], whose bytes are those of [-127, 128]
         volatile float fhb = (float)(m == 256 ? 128u : h) + 0.5f - 128.0f;

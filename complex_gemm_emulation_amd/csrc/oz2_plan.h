@@ -54,7 +54,6 @@ struct ModuliPlan {
     uint32_t Kstd[kMaxS] = {};    // (-2^62) mod m
     uint32_t Kext[kMaxS] = {};    // (-2^104) mod m
     float frcp[kMaxS] = {};       // fl32(1 / m)
-    float foff[kMaxS] = {};       // fl32((h + 1/2) / m)
     float foffb[kMaxS] = {};      // fl32((hb + 1/2 - 128) / m), hb = h (128 for m = 256)
     double drcp[kMaxS] = {};      // fl64(1 / m), for the reduction of INT32 accumulators
 };
