@@ -187,9 +187,10 @@ struct Crt {
 // RN(c * 2^-S) of a two's-complement integer c given by NL 32-bit words:
 // the top 64 bits below the leading one OR-ed with a sticky bit of the rest,
 // converted once with round-to-nearest-even, then scaled by a power of two
-// (a second rounding only when the result is subnormal).  Branch-free: the
-// magnitude by xor and carry, the leading word moved to the top in steps of
-// 4, 2 and 1 words.
+// (a second rounding only when the result is subnormal).  The magnitude by
+// xor and carry; the leading word moved to the top in steps of 4, 2 and 1
+// words, which a wave-uniform branch skips when every lane's top word is
+// already nonzero.
 template <int NL>
 __device__ __forceinline__ double words_to_double(uint32_t w[NL], int S) {
     const uint32_t sgn = (uint32_t)((int32_t)w[NL - 1] >> 31);
@@ -201,23 +202,27 @@ __device__ __forceinline__ double words_to_double(uint32_t w[NL], int S) {
         w[i] = y;
     }
     int shift = 0;
-    if (NL > 4) {
-        const bool z4 = (w[NL - 1] | w[NL - 2] | w[NL - 3] | w[NL - 4]) == 0;
+    // word shifts only when some lane's top word is zero (|c_hat| far below
+    // M: rare for real data), decided by a wave vote so the branch is uniform
+    if (!__all(w[NL - 1] != 0)) {
+        if (NL > 4) {
+            const bool z4 = (w[NL - 1] | w[NL - 2] | w[NL - 3] | w[NL - 4]) == 0;
 #pragma unroll
-        for (int i = NL - 1; i >= 0; --i) w[i] = z4 ? (i >= 4 ? w[i - 4] : 0u) : w[i];
-        shift += z4 ? 4 : 0;
-    }
-    if (NL > 2) {
-        const bool z2 = (w[NL - 1] | w[NL - 2]) == 0;
+            for (int i = NL - 1; i >= 0; --i) w[i] = z4 ? (i >= 4 ? w[i - 4] : 0u) : w[i];
+            shift += z4 ? 4 : 0;
+        }
+        if (NL > 2) {
+            const bool z2 = (w[NL - 1] | w[NL - 2]) == 0;
 #pragma unroll
-        for (int i = NL - 1; i >= 0; --i) w[i] = z2 ? (i >= 2 ? w[i - 2] : 0u) : w[i];
-        shift += z2 ? 2 : 0;
-    }
-    {
-        const bool z1 = w[NL - 1] == 0;
+            for (int i = NL - 1; i >= 0; --i) w[i] = z2 ? (i >= 2 ? w[i - 2] : 0u) : w[i];
+            shift += z2 ? 2 : 0;
+        }
+        {
+            const bool z1 = w[NL - 1] == 0;
 #pragma unroll
-        for (int i = NL - 1; i >= 0; --i) w[i] = z1 ? (i >= 1 ? w[i - 1] : 0u) : w[i];
-        shift += z1 ? 1 : 0;
+            for (int i = NL - 1; i >= 0; --i) w[i] = z1 ? (i >= 1 ? w[i - 1] : 0u) : w[i];
+            shift += z1 ? 1 : 0;
+        }
     }
     const uint32_t x3 = w[NL - 1];
     const int lz = __clz((int)x3);
