@@ -189,3 +189,21 @@ def test_tensor_chain_full_size_sampled(handle):
     for b in sorted({0, batch - 1, *rng.choice(batch, 6, replace=False).tolist()}):
         want = _oracle_chain(X[b * n3:(b + 1) * n3], Aop, Bop, Cop, n, s)
         check_float_parity(got[b * n3:(b + 1) * n3], want, f"chain tensor {b}")
+
+
+def test_fused_pairs_and_lone_last_tile_at_scale(handle):
+    # k = 16 takes tiles in pairs.  16387 tiles make runs of 4 tiles per
+    # wavefront, and the last run holds 3: two full pairs elsewhere, one pair
+    # and one lone tile at the end.  Every output is compared with the oracle.
+    import torch
+    m, k, n, s = 16, 16, 16 * 16387, 16
+    rng = np.random.default_rng(16387)
+    A = workloads.real_matrix(m, k, int(rng.integers(1 << 30)), "phi", 1.0)
+    B = workloads.real_matrix(k, n, int(rng.integers(1 << 30)), "phi", 1.0)
+    print(f"[small pairs at scale] m={m} n={n} k={k} s={s}", flush=True)
+    dC = torch.zeros(m * n, dtype=torch.float64, device="cuda")
+    handle.dgemm("N", "N", m, n, k, 1.0, to_dev(A), m, to_dev(B), k, 0.0, dC, m, s)
+    torch.cuda.synchronize()
+    got = from_dev(dC)
+    want = oracle.gemm_entries(False, "N", "N", m, n, k, 1.0, A, m, B, k, 0.0, None, m, s)["out"]
+    check_float_parity(got, want, "pairs at scale")
