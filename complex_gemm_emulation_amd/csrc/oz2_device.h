@@ -1,6 +1,7 @@
-// oz2_device.h -- device arithmetic shared by the kernels of oz2: IEEE-bit
-// scaling, integer-only residue generation, CRT reconstruction in 16-bit
-// limbs and the correctly rounded conversion back to double.
+// oz2_device.h -- device arithmetic shared by the kernels of oz2: exact
+// scaling and integerization, residues from byte-limb dot products, CRT
+// reconstruction in 16-bit limbs and the correctly rounded conversion back
+// to double.
 //
 // "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
 // Ozaki Scheme II on the Xe2 Architecture":

@@ -1,6 +1,6 @@
 // oz2_kernels.hip -- memory-bound phases of Ozaki scheme II on gfx950:
-// row/column exponent scan, integer-only residue encoder, CRT reconstruction
-// with the alpha/beta epilogue.
+// row/column exponent scan, exact residue encoder, CRT reconstruction with
+// the alpha/beta epilogue.
 //
 // Method: "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc
 // GPUs: Ozaki Scheme II on the Xe2 Architecture":

@@ -5,7 +5,7 @@
 // Method ("Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc
 // GPUs: Ozaki Scheme II on the Xe2 Architecture", Sec. 2.3 and Sec. 4): row
 // and column exponents over the whole of k (Sec. 4.1), integerization and
-// integer-only residues (Sec. 2.3, Sec. 4.2), s exact INT8 products (Sec. 4.3),
+// exact residues from integer limbs (Sec. 2.3, Sec. 4.2), s exact INT8 products (Sec. 4.3),
 // CRT with an FP32 quotient in 16-bit limbs and one correctly rounded
 // conversion (Sec. 4.4).  The workload it serves is the chained tensor mode
 // product ("You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode
