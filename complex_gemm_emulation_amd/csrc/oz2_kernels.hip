@@ -284,14 +284,40 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
     // the lane's four entries are 32 (complex: 64) contiguous bytes: 16-byte
     // stores when they are 16-byte aligned (wave-uniform: depends on j)
     const bool vec = full && (((uintptr_t)c0 & 15u) == 0);
+    // beta != 0: the lane's entries of C, read with the same 16-byte loads
+    // when aligned (entry e, part o at cin[e][o])
+    double cin[4][2] = {};
+    if (BETA) {
+        if (vec) {
+            const v2d* src = (const v2d*)c0;
+#pragma unroll
+            for (int q = 0; q < (CPLX ? 4 : 2); ++q) {
+                const v2d v = src[q];
+                if (CPLX) {
+                    cin[q][0] = v.x;
+                    cin[q][1] = v.y;
+                } else {
+                    cin[2 * q][0] = v.x;
+                    cin[2 * q + 1][0] = v.y;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (i0 + e >= P.m) break;
+                const double* c = c0 + (CPLX ? 2 : 1) * e;
+                cin[e][0] = c[0];
+                if (CPLX) cin[e][1] = c[1];
+            }
+        }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         if (!vec && i0 + e >= P.m) break;
-        const double* c = c0 + (CPLX ? 2 : 1) * e;
         if (!CPLX) {
             const double t1 = P.alpha[0] * x[e][0];
             if (BETA) {
-                const double t2 = P.beta[0] * c[0];
+                const double t2 = P.beta[0] * cin[e][0];
                 out[e][0] = t1 + t2;
             } else {
                 out[e][0] = t1;
@@ -304,7 +330,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(ReconParams P) {
             const double uim = t3 + t4;
             if (BETA) {
                 const double br = P.beta[0], bi = P.beta[1];
-                const double cr = c[0], ci = c[1];
+                const double cr = cin[e][0], ci = cin[e][1];
                 const double t5 = br * cr, t6 = bi * ci;
                 const double vre = t5 - t6;
                 const double t7 = br * ci, t8 = bi * cr;
