@@ -55,6 +55,14 @@ __device__ __forceinline__ float cmod(float x, float m, float rm) {
     return fmaf(-m, floorf(fmaf(x, rm, 0.5f)), x);
 }
 
+// the same reduction of x - 128, offset by 128: [x - 128]_m + 128 in
+// [0, 255] for m <= 256 (oh = fl32(1/2 - 128 fl32(1/m)); the floor argument
+// is within 2^-5 / m + 2^-12 of (x - 128) / m + 1/2, and exact for m = 256
+// and m = 1), the offset-binary byte that v_cvt_pk_u8_f32 packs
+__device__ __forceinline__ float cmod128(float x, float m, float rm, float oh) {
+    return fmaf(-m, floorf(fmaf(x, rm, oh)), x);
+}
+
 // centred residue of an integer-valued double |v| <= 2^53 modulo an odd m
 // (the quotient estimate can be one off; two corrections bring r into range)
 __device__ __forceinline__ float dmod_odd(double v, double m, double rm) {
@@ -66,9 +74,10 @@ __device__ __forceinline__ float dmod_odd(double v, double m, double rm) {
     return (float)r;
 }
 
-// the signed byte `e` of a word of four packed residues, as a float
-__device__ __forceinline__ float unpack(uint32_t w, int e) {
-    return (float)(int)(int8_t)(w >> (8 * e));
+// byte `e` of a word of four offset-binary residues, as a float: the
+// residue plus 128 (v_cvt_f32_ubyte)
+__device__ __forceinline__ float unpack128(uint32_t w, int e) {
+    return (float)((w >> (8 * e)) & 0xffu);
 }
 
 // four centred residues (exact integers held as floats) as one word
@@ -160,15 +169,18 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
             const int u = u0 + v;
             const long a8 = *(const long*)(buf + u * kPlane + (16 * t + a) * kChainN + 8 * (kq & 1));
             const long b8 = *(const long*)(&opm[u][a * kChainN + 8 * (kq & 1)]);
-            acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a8 : 0l, kq < 2 ? b8 : 0l, v4i{0, 0, 0, 0}, 0, 0,
-                                                           0);
+            // C = 128: the accumulators come out offset by 128
+            acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(kq < 2 ? a8 : 0l, kq < 2 ? b8 : 0l, v4i{128, 128, 128, 128},
+                                                           0, 0, 0);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int u = u0 + v;
-            const float m = T->mod[u], rm = T->rmod[u];
-            pk[u] = pack4(cmod((float)acc[v][0], m, rm), cmod((float)acc[v][1], m, rm),
-                          cmod((float)acc[v][2], m, rm), cmod((float)acc[v][3], m, rm));
+            const float m = T->mod[u], rm = T->rmod[u], oh = T->ohalf[u];
+            uint32_t w = 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w = __builtin_amdgcn_cvt_pk_u8_f32(cmod128((float)acc[v][q], m, rm, oh), q, w);
+            pk[u] = w;
         }
     }
 }
@@ -177,11 +189,19 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
 template <int G0, int G1, bool ANY>
 __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint32_t (&pk)[kSlots],
                                              const ChainTables* T, int8_t* at, int step) {
+    // offset by 128; the first drop's differences remove the offset from
+    // every kept slot, and without drops it is subtracted here
     float r[4][kSlots];
 #pragma unroll
     for (int u = 0; u < kSlots; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q][u] = unpack(pk[u], q);
+        for (int q = 0; q < 4; ++q) r[q][u] = unpack128(pk[u], q);
+    if (G0 < 0 && g[mode] == 0) {
+#pragma unroll
+        for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
+    }
     if (G0 >= 0 && G0 == G1)
         rescale_extend<G0, ANY>(0, r, T, at, step);
     else if (G0 >= 0 && mode == 0)
@@ -340,11 +360,13 @@ void chain_kernel(ChainParams P) {
         const int t = wave + 8 * tt;
         uint32_t pk[kSlots];
         tile_products(buf, ops[(d - 1) % 3], T, t, a, kq, pk);
+        // offset by 128: the first digit step's differences remove it from
+        // slots 1..; slot 0, the first digit itself, loses it after the steps
         float dg[4][kSlots];
 #pragma unroll
         for (int u = 0; u < kSlots; ++u)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][u] = unpack(pk[u], q);
+            for (int q = 0; q < 4; ++q) dg[q][u] = unpack128(pk[u], q);
 #pragma unroll
         for (int i = 0; i < kSlots - 1; ++i)
 #pragma unroll
@@ -353,6 +375,8 @@ void chain_kernel(ChainParams P) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
             }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
         double V[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) V[q] = (double)dg[q][kSlots - 1];

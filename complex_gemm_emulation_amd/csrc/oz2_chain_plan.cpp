@@ -217,6 +217,7 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
     for (int u = 0; u < kChainMaxS; ++u) {
         T->mod[u] = (float)slot[u];
         T->rmod[u] = 1.0f / (float)slot[u];
+        T->ohalf[u] = 0.5f - 128.0f * T->rmod[u];
     }
     for (int i = 0; i < kChainMaxS; ++i)
         for (int j = 0; j < kChainMaxS; ++j)

@@ -146,6 +146,7 @@ struct ChainTables {
     float omega[kChainMaxS][kChainMaxS];  // [prod_{l<i} m_l]_{m_j}, centred
     float mod[kChainMaxS];                // m_u
     float rmod[kChainMaxS];               // fl32(1 / m_u)
+    float ohalf[kChainMaxS];              // fl32(1/2 - 128 rmod[u]): reduction of an accumulator offset by 128
     int fexp[3][kChainN];                 // row exponents left pending on each direction (0 for padding)
 };
 
