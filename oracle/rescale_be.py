@@ -23,7 +23,7 @@ Source page (cited by title and section; nothing here is copied from it):
   and one base extension after each non-final mode, one reconstruction with
   the scale alpha * Gamma.
 
-Readings where the page leaves a step open (listed in the design doc as well):
+Readings where the page leaves a step open:
 
 1. Working basis: the page takes the first s entries of an external library's
    modulus table, of which it prints only the first three (256, 255, 253).
