@@ -10,8 +10,8 @@
 //   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
 //             2^(limb position) mod m and a constant K_m; the page uses
 //             21-bit limbs, here byte limbs read four at a time by
-//             v_dot4_u32_u8 (the same congruence) -> centred_residue(),
-//             residue_word()
+//             v_dot4_u32_u8 (the same congruence) -> residue_word();
+//             modulo 256 the low byte of a_hat     -> low_byte_word()
 //   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
 //             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
 //             top 64 bits + sticky rounded once to double -> Crt,
@@ -112,6 +112,14 @@ __device__ __forceinline__ uint32_t residue_word(const Limbs<EXT>* L, uint32_t K
     for (int e = 0; e < 4; ++e)
         w = __builtin_amdgcn_cvt_pk_u8_f32(offset_residue(dot_limbs<EXT>(L[e], K128, c4), m, rcp, offb), e, w);
     return w ^ 0x80808080u;
+}
+
+// residues modulo 256 in the window [-128, 127] of four elements: the low
+// byte of a_hat in two's complement, which is byte 0 of the first word (the
+// bias changes only the top word)
+template <bool EXT>
+__device__ __forceinline__ uint32_t low_byte_word(const Limbs<EXT>* L) {
+    return (L[0].w[0] & 0xffu) | ((L[1].w[0] & 0xffu) << 8) | ((L[2].w[0] & 0xffu) << 16) | (L[3].w[0] << 24);
 }
 
 // the same for a complex element's real and imaginary parts and their sum

@@ -164,8 +164,11 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
         }
         // k-panel layout: panel p0 / 64, row gv, byte p4
         int8_t* dst = P.planes + (p0 / kPanelK) * P.vpad * kPanelK + gv * kPanelK + p4;
-        // four moduli per trip: their constants are fetched together
-        for (int t0 = 0; t0 < P.s; t0 += 4) {
+        // the first modulus is 256 (the plan guarantees it): its plane is
+        // the low byte of a_hat; then four moduli per trip, whose constants
+        // are fetched together
+        if (!CPLX) *(uint32_t*)dst = low_byte_word<EXT>(lr);
+        for (int t0 = CPLX ? 0 : 1; t0 < P.s; t0 += 4) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int t = t0 + u;

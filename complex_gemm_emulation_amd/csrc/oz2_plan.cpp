@@ -232,6 +232,9 @@ ModuliPlan g_plans[kMaxS + 1];
 const ModuliPlan* moduli_plan(int s) {
     if (s < kMinS || s > kMaxS) return nullptr;
     std::call_once(g_once[s], [s] { build_plan(s, &g_plans[s]); });
+    // every max-product set starts with 256 (2^8 is coprime to every odd
+    // modulus); the encoders take that plane as the low byte of a_hat
+    if (g_plans[s].mod[0] != 256) return nullptr;
     return &g_plans[s];
 }
 

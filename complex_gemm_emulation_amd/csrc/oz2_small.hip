@@ -92,8 +92,10 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
     for (int t = 0; t < SMAX; ++t) {
         if (t < P.s) {
             const ModConst& C = Q.q[t];
-            const uint32_t w0 = residue_word<EXT>(L, C.K128, C.c4, C.fm, C.frcp, C.foffb);
-            const uint32_t w1 = residue_word<EXT>(L + 4, C.K128, C.c4, C.fm, C.frcp, C.foffb);
+            // the first modulus is 256: the low byte of a_hat
+            const uint32_t w0 = t == 0 ? low_byte_word<EXT>(L) : residue_word<EXT>(L, C.K128, C.c4, C.fm, C.frcp, C.foffb);
+            const uint32_t w1 =
+                t == 0 ? low_byte_word<EXT>(L + 4) : residue_word<EXT>(L + 4, C.K128, C.c4, C.fm, C.frcp, C.foffb);
             frag[t] = (long)((uint64_t)w0 | ((uint64_t)w1 << 32));
         }
     }

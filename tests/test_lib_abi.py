@@ -36,6 +36,8 @@ def test_planner_matches_oracle(s):
         for cplx in (False, True):
             info = oz2.plan_info(s, k, cplx)
             assert info["moduli"] == oracle.max_product_moduli(s)
+            # the encoders pack the first plane as the low byte of a_hat
+            assert info["moduli"][0] == 256
             assert info["NL"] == oracle.n_limbs(s)
             t = oracle.scaling_width(s, k, cplx)
             assert info["t"] == t, (s, k, cplx)
