@@ -237,9 +237,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
                     const v4i cb = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero, 0, 0, 0);
                     const ModConst& C0 = Q.q[t];
                     const ModConst& C1 = Q.q[t + 1];
+                    // modulus 256 (always the first): the low byte of the sum
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc[e].add2(acc_mod(ca[e], C0), acc_mod(cb[e], C1), Q.Y2[t >> 1], Q.W2[t >> 1]);
+                        acc[e].add2(t == 0 ? ((uint32_t)ca[e] & 0xffu) : acc_mod(ca[e], C0), acc_mod(cb[e], C1),
+                                    Q.Y2[t >> 1], Q.W2[t >> 1]);
                 }
             }
 
