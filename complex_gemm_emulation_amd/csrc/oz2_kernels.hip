@@ -167,8 +167,17 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeParams P) {
         // the first modulus is 256 (the plan guarantees it): its plane is
         // the low byte of a_hat; then four moduli per trip, whose constants
         // are fetched together
-        if (!CPLX) *(uint32_t*)dst = low_byte_word<EXT>(lr);
-        for (int t0 = CPLX ? 0 : 1; t0 < P.s; t0 += 4) {
+        if (!CPLX) {
+            *(uint32_t*)dst = low_byte_word<EXT>(lr);
+        } else {
+            // re, im, and re + im: the last as a bytewise sum mod 256 (the low
+            // seven bits of each byte add without reaching the next byte)
+            const uint32_t wr = low_byte_word<EXT>(lr), wi = low_byte_word<EXT>(li);
+            *(uint32_t*)dst = wr;
+            *(uint32_t*)(dst + P.set_stride) = wi;
+            *(uint32_t*)(dst + 2 * P.set_stride) = ((wr & 0x7f7f7f7fu) + (wi & 0x7f7f7f7fu)) ^ ((wr ^ wi) & 0x80808080u);
+        }
+        for (int t0 = 1; t0 < P.s; t0 += 4) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const int t = t0 + u;
