@@ -107,9 +107,11 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
 // fma(acc, fl32(1/m), fl32(1/m) / 2) is within 2^-5 / m + 2^-11 of it for
 // m >= 64 (every modulus here is >= 157), so the floor and r are exact.
 // Past the last modulus (all constants 0) it returns acc, which is 0 there.
-__device__ __forceinline__ uint32_t acc_mod(int32_t acc, const ModConst& C) {
+// The result is an integer-valued float; v_cvt_pk_u8_f32 converts it
+// straight into its byte of the packed word of a modulus pair.
+__device__ __forceinline__ float acc_mod(int32_t acc, const ModConst& C) {
     const float a = (float)acc;
-    return (uint32_t)fmaf(-C.fm, floorf(fmaf(a, C.frcp, C.fhalf)), a);
+    return fmaf(-C.fm, floorf(fmaf(a, C.frcp, C.fhalf)), a);
 }
 
 // PAIR (k <= 16): the instruction's k of 32 holds two tiles.  Lanes 0-31
@@ -237,11 +239,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
                     const v4i cb = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero, 0, 0, 0);
                     const ModConst& C0 = Q.q[t];
                     const ModConst& C1 = Q.q[t + 1];
-                    // modulus 256 (always the first): the low byte of the sum
+                    // residues of moduli t, t + 1 as the 16-bit halves of one
+                    // word; modulus 256 (always the first) is the low byte of the sum
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        acc[e].add2(t == 0 ? ((uint32_t)ca[e] & 0xffu) : acc_mod(ca[e], C0), acc_mod(cb[e], C1),
-                                    Q.Y2[t >> 1], Q.W2[t >> 1]);
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = t == 0 ? ((uint32_t)ca[e] & 0xffu)
+                                                   : __builtin_amdgcn_cvt_pk_u8_f32(acc_mod(ca[e], C0), 0, 0u);
+                        acc[e].add2(__builtin_amdgcn_cvt_pk_u8_f32(acc_mod(cb[e], C1), 2, lo), Q.Y2[t >> 1],
+                                    Q.W2[t >> 1]);
+                    }
                 }
             }
 
