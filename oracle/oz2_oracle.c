@@ -17,7 +17,9 @@
  * The BLAS operation is C <- alpha op(A) op(B) + beta C with column-major
  * storage (Sec. 2.1, Sec. 1).  The alpha/beta evaluation order is not given
  * by the pages; the one used is: t1 = alpha*x; t2 = beta*c; out = t1 + t2,
- * every operation rounded separately (compile with -ffp-contract=off).
+ * every operation rounded separately (compile with -ffp-contract=off).  The
+ * tests pin it order-free, against the rounding bound of the exact rational
+ * alpha*x + beta*c.
  */
 #include <math.h>
 #include <stdint.h>

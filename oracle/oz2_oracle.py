@@ -32,8 +32,12 @@ What the oracle computes (its own reading of the pages, step by step):
 Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against printed values of the pages (``tests/golden/``), closed forms, exact
 rational arithmetic (``fractions.Fraction``) and brute force; see each test.
-The alpha/beta evaluation order is *parity unpinned* by the pages (they give
-none); it is pinned only by the product and the oracle using the same order.
+The pages give no evaluation order for alpha/beta.  The epilogue is pinned
+without one: every output must lie within the rounding bound of separately
+rounded products and sums around the exact rational alpha*x + beta*c
+(``test_alpha_beta_epilogue_vs_exact_rationals``), which any sign, swap or
+conjugation mistake breaks.  Bitwise parity with the product additionally
+rests on both sides using the same order.
 """
 from __future__ import annotations
 

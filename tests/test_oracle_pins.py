@@ -286,9 +286,11 @@ def _stored(X, op, rows, cols):
     return Mx.T.conj() if op == "C" else Mx.T
 
 
-def _frac_pipeline(cplx, transa, transb, m, n, k, alpha, A, B, beta, C, s):
-    """The method re-derived with Fractions: scale, round half-even, exact
-    product, one correctly rounded division, then alpha/beta in IEEE double."""
+def _frac_products(cplx, transa, transb, m, n, k, A, B, s):
+    """x = op(A) op(B) by the method re-derived with Fractions: scale, round
+    half-even, exact product, one correctly rounded division by 2^(D+E).
+    No alpha/beta here: the epilogue is pinned on its own against exact
+    rationals (test_alpha_beta_epilogue_*)."""
     t = oracle.scaling_width(s, k, cplx)
     opA = _stored(A, transa, m, k)
     opB = _stored(B, transb, k, n)
@@ -317,9 +319,6 @@ def _frac_pipeline(cplx, transa, transb, m, n, k, alpha, A, B, beta, C, s):
     rows = [scale(opA[i, :]) for i in range(m)]
     cols = [scale(opB[:, j]) for j in range(n)]
     out = np.zeros((m, n), dtype=np.complex128 if cplx else np.float64)
-    ar, ai = parts(alpha)
-    br, bi = parts(beta)
-    Cm = C.reshape(n, m).T if C is not None else None
     for i in range(m):
         for j in range(n):
             (ra, D), (cb, E) = rows[i], cols[j]
@@ -329,19 +328,7 @@ def _frac_pipeline(cplx, transa, transb, m, n, k, alpha, A, B, beta, C, s):
                 cre = sum(a[0] * b[0] - a[1] * b[1] for a, b in zip(ra, cb))
                 cim = sum(a[0] * b[1] + a[1] * b[0] for a, b in zip(ra, cb))
                 xr, xi = to_double(cre, D + E), to_double(cim, D + E)
-            if not cplx:
-                v = ar * xr
-                if br != 0.0:
-                    v = v + br * float(Cm[i, j])
-                out[i, j] = v
-            else:
-                ure = ar * xr - ai * xi
-                uim = ar * xi + ai * xr
-                if br != 0.0 or bi != 0.0:
-                    cr, ci = parts(Cm[i, j])
-                    ure = ure + (br * cr - bi * ci)
-                    uim = uim + (br * ci + bi * cr)
-                out[i, j] = complex(ure, uim)
+            out[i, j] = complex(xr, xi) if cplx else xr
     return out
 
 
@@ -368,14 +355,144 @@ def test_bruteforce_tiny_vs_fraction(oracle_lib, seed):
     A = _wide_matrix(rng, *sa, cplx)
     B = _wide_matrix(rng, *sb, cplx)
     C = _wide_matrix(rng, m, n, cplx)
+    one, zero = (complex(1, 0), complex(0, 0)) if cplx else (1.0, 0.0)
+    # x = op(A) op(B): bit for bit against the Fraction derivation
+    r = oracle.gemm_entries(cplx, transa, transb, m, n, k, one, A, sa[0], B, sb[0], zero, None, m, s)
+    got = np.ascontiguousarray(r["out"].reshape(n, m).T)
+    want = np.ascontiguousarray(_frac_products(cplx, transa, transb, m, n, k, A, B, s))
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64)), (got, want)
+    # the alpha/beta call on the same operands: within the rounding bound of
+    # the exact alpha*x + beta*c (finite entries only)
     alpha = complex(rng.normal(), rng.normal()) if cplx else float(rng.normal())
     beta = complex(rng.normal(), rng.normal()) if cplx else (0.0 if seed % 2 else float(rng.normal()))
-    r = oracle.gemm_entries(cplx, transa, transb, m, n, k, alpha, A, sa[0], B, sb[0], beta, C, m, s)
-    got = r["out"].reshape(n, m).T
-    want = _frac_pipeline(cplx, transa, transb, m, n, k, alpha, A, B, beta, C, s)
-    gb = np.ascontiguousarray(got).view(np.uint64)
-    wb = np.ascontiguousarray(want).view(np.uint64)
-    assert np.array_equal(gb, wb), (got, want)
+    r2 = oracle.gemm_entries(cplx, transa, transb, m, n, k, alpha, A, sa[0], B, sb[0], beta, C, m, s)
+    xs, cs, outs = r["out"], C.reshape(-1), r2["out"]
+    fin = np.isfinite(xs) if not cplx else np.isfinite(xs.real) & np.isfinite(xs.imag)
+    nan_rows = ~fin
+    assert np.all(np.isnan(outs[nan_rows] if not cplx else outs[nan_rows].real))
+    _assert_epilogue_bound(cplx, alpha, beta, xs[fin], cs[fin], outs[fin])
+
+
+# ---------------------------------------------------------------------------
+# the alpha/beta epilogue (Arc page Sec. 1 and Sec. 2.1: the BLAS operation
+# C <- alpha op(A) op(B) + beta C).  The pages fix no evaluation order, so the
+# pin is order-free: every product and sum rounded once obeys a per-operation
+# bound against the exact rational alpha*x + beta*c.
+# ---------------------------------------------------------------------------
+_U = Fraction(1, 2 ** 53)
+_TINY = Fraction(1, 2 ** 1074)  # absolute error one rounding may add below 2^-1022
+
+
+def _epilogue_violations(cplx, alpha, beta, xs, cs, outs):
+    """Indices whose output breaks the bound.  Real: products p = (alpha x,
+    beta c); |out - sum p| <= u sum|p| + u |out| (+ subnormal slack).  Complex,
+    per component: four products, three sums; 2u sum|p| + u |out| bounds every
+    order of separately rounded operations."""
+    bad = []
+    ar, ai = (Fraction(float(np.real(alpha))), Fraction(float(np.imag(alpha)))) if cplx else (Fraction(float(alpha)), 0)
+    br, bi = (Fraction(float(np.real(beta))), Fraction(float(np.imag(beta)))) if cplx else (Fraction(float(beta)), 0)
+    beta_zero = br == 0 and bi == 0
+    for q in range(len(outs)):
+        if not cplx:
+            x, o = Fraction(float(xs[q])), float(outs[q])
+            prods = [ar * x] + ([] if beta_zero else [br * Fraction(float(cs[q]))])
+            comps = [(sum(prods), prods, o)]
+            fac, nround = 1, 2
+        else:
+            xr, xi = Fraction(float(xs[q].real)), Fraction(float(xs[q].imag))
+            pre = [ar * xr, -(ai * xi)]
+            pim = [ar * xi, ai * xr]
+            if not beta_zero:
+                cr, ci = Fraction(float(cs[q].real)), Fraction(float(cs[q].imag))
+                pre += [br * cr, -(bi * ci)]
+                pim += [br * ci, bi * cr]
+            comps = [(sum(pre), pre, float(outs[q].real)), (sum(pim), pim, float(outs[q].imag))]
+            fac, nround = 2, 7
+        for exact, prods, o in comps:
+            if not math.isfinite(o):
+                bad.append(q)
+                break
+            bound = fac * _U * sum(abs(p) for p in prods) + _U * abs(Fraction(o)) + nround * _TINY
+            if abs(Fraction(o) - exact) > bound * (1 + 8 * _U):
+                bad.append(q)
+                break
+    return bad
+
+
+def _assert_epilogue_bound(cplx, alpha, beta, xs, cs, outs):
+    bad = _epilogue_violations(cplx, alpha, beta, xs, cs, outs)
+    assert not bad, [(q, xs[q], cs[q], outs[q]) for q in bad[:5]]
+
+
+def _epilogue_operands(rng, cplx, m, n, k, spread):
+    """Operands whose products x = op(A) op(B) span magnitudes 2^+-spread row
+    by row, a zero row (x = +0 exactly) and C with signed zeros."""
+    def mat(r, c):
+        v = rng.uniform(-1, 1, r * c)
+        return v + 1j * rng.uniform(-1, 1, r * c) if cplx else v
+    A, B, C = mat(m, k), mat(k, n), mat(m, n)
+    rowscale = 2.0 ** rng.integers(-spread, spread + 1, size=m)
+    A = (A.reshape(k, m) * rowscale).reshape(-1)
+    A.reshape(k, m)[:, 0] = 0.0
+    colscale = 2.0 ** rng.integers(-spread, spread + 1, size=n)
+    C = (C.reshape(n, m) * colscale[:, None] * rowscale[None, :]).reshape(-1)
+    C[1] = -0.0
+    C[2] = 0.0
+    return A, B, C
+
+
+@pytest.mark.parametrize("cplx", [False, True])
+@pytest.mark.parametrize("spread", [0, 40, 400])
+def test_alpha_beta_epilogue_vs_exact_rationals(oracle_lib, cplx, spread):
+    rng = np.random.default_rng(880 + spread + int(cplx))
+    m, n, k = 7, 6, 9
+    A, B, C = _epilogue_operands(rng, cplx, m, n, k, spread)
+    one, zero = (complex(1, 0), complex(0, 0)) if cplx else (1.0, 0.0)
+    xs = oracle.gemm_entries(cplx, "N", "N", m, n, k, one, A, m, B, k, zero, None, m, 16)["out"]
+    assert xs.reshape(n, m)[:, 0].tolist() == [zero] * n  # zero row: integer zero -> +0
+    draws = [(rng.normal(), rng.normal()) for _ in range(4)]
+    draws += [(2.0 ** 300 * rng.normal(), 2.0 ** -300 * rng.normal()), (-0.0, 3.0), (0.75, -0.0)]
+    for (a1, a2), (b1, b2) in itertools.product(draws, repeat=2):
+        alpha = complex(a1, a2) if cplx else a1
+        for beta in ([complex(b1, b2), complex(0, 0)] if cplx else [b1, 0.0]):
+            if alpha == 0:
+                continue  # alpha = 0 is a quick return, pinned in test_quick_returns
+            Cin = C.copy()
+            if beta == 0:
+                Cin[:] = math.nan  # beta = 0: C is never read
+            outs = oracle.gemm_entries(cplx, "N", "N", m, n, k, alpha, A, m, B, k, beta, Cin, m, 16)["out"]
+            _assert_epilogue_bound(cplx, alpha, beta, xs, C, outs)
+            if not cplx and beta == 0:
+                # one operation: correctly rounded, and the zero's sign follows IEEE's product rule
+                for x, o in zip(xs, outs):
+                    assert o == oracle.fraction_to_double(Fraction(alpha) * Fraction(float(x)))
+                    if x == 0:
+                        assert np.signbit(o) == (np.signbit(alpha) != np.signbit(x))
+
+
+def test_alpha_beta_bound_rejects_planted_mistakes():
+    # The bound above must tell a correct epilogue from the plausible wrong
+    # ones: a sign flip, alpha and beta swapped, x and c swapped, a conjugate.
+    rng = np.random.default_rng(881)
+    for cplx in (False, True):
+        nq = 40
+        xs = rng.uniform(-1, 1, nq) + (1j * rng.uniform(-1, 1, nq) if cplx else 0)
+        cs = rng.uniform(-1, 1, nq) + (1j * rng.uniform(-1, 1, nq) if cplx else 0)
+        alpha = complex(0.7, -0.3) if cplx else 1.5
+        beta = complex(0.2, 0.1) if cplx else -0.5
+        right = [complex(Fraction(alpha.real) * Fraction(x.real) - Fraction(alpha.imag) * Fraction(x.imag)
+                         + Fraction(beta.real) * Fraction(c.real) - Fraction(beta.imag) * Fraction(c.imag),
+                         Fraction(alpha.real) * Fraction(x.imag) + Fraction(alpha.imag) * Fraction(x.real)
+                         + Fraction(beta.real) * Fraction(c.imag) + Fraction(beta.imag) * Fraction(c.real))
+                 if cplx else float(Fraction(alpha) * Fraction(x) + Fraction(beta) * Fraction(c))
+                 for x, c in zip(xs, cs)]
+        assert not _epilogue_violations(cplx, alpha, beta, xs, cs, np.array(right))
+        wrong = [alpha * xs - beta * cs, beta * xs + alpha * cs, alpha * cs + beta * xs]
+        if cplx:
+            wrong += [np.conj(alpha) * xs + beta * cs, alpha * xs + np.conj(beta) * cs,
+                      alpha * np.conj(xs) + beta * cs]
+        for w in wrong:
+            assert len(_epilogue_violations(cplx, alpha, beta, xs, cs, np.asarray(w))) > nq // 2
 
 
 def test_subnormal_and_overflow_outputs_vs_fraction(oracle_lib):
@@ -384,14 +501,14 @@ def test_subnormal_and_overflow_outputs_vs_fraction(oracle_lib):
     m, n, k = 4, 4, 5
     A = rng.uniform(-1, 1, m * k) * 2.0 ** -560
     B = rng.uniform(-1, 1, k * n) * 2.0 ** -500
-    want = _frac_pipeline(False, "N", "N", m, n, k, 1.0, A, B, 0.0, None, 16)
+    want = _frac_products(False, "N", "N", m, n, k, A, B, 16)
     r = oracle.gemm_entries(False, "N", "N", m, n, k, 1.0, A, m, B, k, 0.0, None, m, 16)
     got = np.ascontiguousarray(r["out"].reshape(n, m).T)
     assert np.all(np.abs(got) < 2.0 ** -1022)
     assert np.array_equal(got.view(np.uint64), np.ascontiguousarray(want).view(np.uint64))
     A2 = rng.uniform(-1, 1, m * k) * 2.0 ** 520
     B2 = rng.uniform(-1, 1, k * n) * 2.0 ** 510
-    want2 = _frac_pipeline(False, "N", "N", m, n, k, 1.0, A2, B2, 0.0, None, 16)
+    want2 = _frac_products(False, "N", "N", m, n, k, A2, B2, 16)
     r2 = oracle.gemm_entries(False, "N", "N", m, n, k, 1.0, A2, m, B2, k, 0.0, None, m, 16)
     got2 = r2["out"].reshape(n, m).T
     assert np.all(np.isinf(got2))
