@@ -51,6 +51,7 @@ struct oz2_context {
     int debug = 0;
     bool timed = false;
     hipEvent_t ev[5] = {};
+    hipEvent_t order_ev = nullptr;  // orders a stream switch after the old stream's work
     Layout last;
 };
 
@@ -443,6 +444,10 @@ int oz2_create(oz2_handle_t* out) {
             return OZ2_STATUS_HIP_ERROR;
         }
     }
+    if (hipEventCreateWithFlags(&h->order_ev, hipEventDisableTiming) != hipSuccess) {
+        delete h;
+        return OZ2_STATUS_HIP_ERROR;
+    }
     *out = h;
     return OZ2_STATUS_SUCCESS;
 }
@@ -453,13 +458,22 @@ int oz2_destroy(oz2_handle_t h) {
     if (h->ws) (void)hipFree(h->ws);
     for (auto& e : h->ev)
         if (e) (void)hipEventDestroy(e);
+    if (h->order_ev) (void)hipEventDestroy(h->order_ev);
     delete h;
     return OZ2_STATUS_SUCCESS;
 }
 
 int oz2_set_stream(oz2_handle_t h, void* stream) {
     if (!h) return -1;
-    h->stream = (hipStream_t)stream;
+    hipStream_t next = (hipStream_t)stream;
+    if (next == h->stream) return OZ2_STATUS_SUCCESS;
+    // Every call on a handle uses the same workspace, so the new stream waits
+    // for all work already queued on the old one.  Work on any earlier stream
+    // is then ordered before the current stream's, and synchronising the
+    // current stream (destroy, workspace growth) covers it too.
+    if (hipEventRecord(h->order_ev, h->stream) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
+    if (hipStreamWaitEvent(next, h->order_ev, 0) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
+    h->stream = next;
     return OZ2_STATUS_SUCCESS;
 }
 
@@ -499,6 +513,7 @@ int oz2_get_phase_times(oz2_handle_t h, float ms[4]) {
 int oz2_moduli_for_bits(int64_t k, int bits, int is_complex) {
     for (int s = kMinS; s <= kMaxS; ++s) {
         const ModuliPlan* pl = moduli_plan(s);
+        if (!pl) continue;
         if (scaling_width(*pl, k, is_complex != 0) >= bits) return s;
     }
     return kMaxS;

@@ -12,10 +12,13 @@
 //             21-bit limbs, here byte limbs read four at a time by
 //             v_dot4_u32_u8 (the same congruence) -> residue_word();
 //             modulo 256 the low byte of a_hat     -> low_byte_word()
-//   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
-//             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
-//             top 64 bits + sticky rounded once to double -> Crt,
-//             words_to_double()
+//   Sec. 4.4  the quotient q = rint(sum r_t y_t/m_t): the page sums FP32
+//             products; here the sum is taken in 16.16 fixed point,
+//             sum r_t round(2^16 y_t/m_t) by v_dot2_u32_u16, within 0.05 of
+//             Z/M, well inside the page's 1/4 margin, so q is the same;
+//             c_hat = sum r_t W_t - q M in 16-bit limbs (two moduli per
+//             v_dot2), one carry pass, top 64 bits + sticky rounded once
+//             to double -> Crt, words_to_double()
 // Device-only; included by the .hip translation units.
 #pragma once
 

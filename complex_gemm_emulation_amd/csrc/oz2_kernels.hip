@@ -6,14 +6,17 @@
 // GPUs: Ozaki Scheme II on the Xe2 Architecture":
 //   Sec. 4.1  D_i = t - e(max_p |a_ip|)            -> scan + scale_of()
 //   Sec. 2.3  a_hat = rint(a 2^D), ties to even     -> make_limbs()
-//   Sec. 4.2  residues from limbs of a_hat + 2^62 with precomputed
-//             2^(limb position) mod m and K_m = (h_m - 2^62) mod m; no FP64
-//             and no branches in the loop over the moduli (a_hat itself is
-//             formed once per element by exact full-rate FP64 operations)
+//   Sec. 4.2  residues from the byte limbs of a_hat + 2^62 (the page uses
+//             21-bit limbs) with precomputed 2^(8 l) mod m and
+//             K_m = (h_m - 2^62) mod m, four limbs per v_dot4_u32_u8; no
+//             FP64 and no branches in the loop over the moduli (a_hat itself
+//             is formed once per element by exact full-rate FP64 operations)
 //                                                  -> encode_kernel
-//   Sec. 4.4  z = sum r_t fl32(y_t/m_t) (FP32 FMAs), q = rint(z),
-//             c_hat = sum r_t W_t - q M in 16-bit limbs, one carry pass,
-//             top 64 bits + sticky rounded once to double, times
+//   Sec. 4.4  q = rint(sum r_t y_t/m_t), estimated in 16.16 fixed point
+//             (sum r_t round(2^16 y_t/m_t) by v_dot2, within 0.05 of Z/M;
+//             the page sums FP32 products, either is exact under its 1/4
+//             margin), c_hat = sum r_t W_t - q M in 16-bit limbs, one carry
+//             pass, top 64 bits + sticky rounded once to double, times
 //             2^(-D_i-E_j)                         -> reconstruct_kernel
 //   Sec. 5    ZGEMM: residues of re, im and re+im; Re and Im reconstructed
 //   Sec. 8.1  non-finite row/column -> NaN row/column

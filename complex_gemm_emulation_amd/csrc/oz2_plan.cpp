@@ -9,9 +9,10 @@
 //  * Sec. 4.1: t is the largest integer with k 2^(2t) <= M/4 (2k for ZGEMM).
 //  * Sec. 4.2: residues from limbs of a_hat + 2^62 with the constants
 //    2^(limb position) mod m and K_m = (h_m - 2^62) mod m, h_m = floor((m-1)/2);
-//    the limbs here are 16 bits wide (the page's are 21), packed in pairs.
-//  * Sec. 4.4: z = sum r_t fl32(y_t/m_t); c_hat = sum r_t W_t - q M in 16-bit
-//    limbs; N_L 32-bit words.
+//    the limbs here are bytes (the page's are 21 bits), four per 32-bit word.
+//  * Sec. 4.4: q = rint(sum r_t y_t/m_t) from the fixed-point constants
+//    Y_t = round(2^16 y_t/m_t) (the page uses fl32(y_t/m_t)); c_hat =
+//    sum r_t W_t - q M in 16-bit limbs; N_L 32-bit words.
 #include "oz2_plan.h"
 
 #include <cmath>

@@ -4,7 +4,8 @@
 // Method: "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc
 // GPUs: Ozaki Scheme II on the Xe2 Architecture" -- Sec. 2.3 (moduli, CRT
 // weights), Sec. 4.1 (scaling width t, Table 2), Sec. 4.2 (residue
-// constants of the limb method), Sec. 4.4 (FP32 quotient constants, 16-bit limbs, N_L).
+// constants of the byte-limb method), Sec. 4.4 (the quotient's fixed-point
+// constants round(2^16 y_t/m_t), 16-bit limbs of W_t and M, N_L).
 #pragma once
 
 #include <cstdint>

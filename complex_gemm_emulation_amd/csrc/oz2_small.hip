@@ -5,9 +5,10 @@
 // Method ("Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc
 // GPUs: Ozaki Scheme II on the Xe2 Architecture", Sec. 2.3 and Sec. 4): row
 // and column exponents over the whole of k (Sec. 4.1), integerization and
-// exact residues from integer limbs (Sec. 2.3, Sec. 4.2), s exact INT8 products (Sec. 4.3),
-// CRT with an FP32 quotient in 16-bit limbs and one correctly rounded
-// conversion (Sec. 4.4).  The workload it serves is the chained tensor mode
+// exact residues from byte limbs (Sec. 2.3, Sec. 4.2), s exact INT8 products
+// (Sec. 4.3), CRT in 16-bit limbs with the quotient estimated in 16.16 fixed
+// point (the page sums FP32 products; both give the same q under its 1/4
+// margin) and one correctly rounded conversion (Sec. 4.4).  The workload it serves is the chained tensor mode
 // product ("You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode
 // Products", Sec. 2.1 Eq. (5) and Sec. 5.1, OzII-Composed): every mode is a
 // batch of small products with one shared operator, whose row (column)

@@ -75,7 +75,11 @@ int oz2_create(oz2_handle_t* h);
 int oz2_destroy(oz2_handle_t h);
 
 /* All later work of this handle is enqueued on `stream` (a hipStream_t,
- * NULL for the null stream). */
+ * NULL for the null stream).  The handle's calls share one workspace, so on a
+ * change of stream the new stream is made to wait (an event, no host wait)
+ * for everything already queued on the old one: calls issued on different
+ * streams through one handle run in issue order.  Returns OZ2_STATUS_HIP_ERROR
+ * if the event cannot be recorded or waited on. */
 int oz2_set_stream(oz2_handle_t h, void* stream);
 
 /* Cap on the workspace in bytes; 0 (the default) means the free device

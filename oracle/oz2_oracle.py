@@ -299,14 +299,16 @@ def max_threads() -> int:
 
 def gemm_entries(is_complex: bool, transa: str, transb: str, m: int, n: int, k: int,
                  alpha, A, lda: int, B, ldb: int, beta, C, ldc: int, s: int,
-                 rows=None, cols=None, nthreads: int = 0) -> dict:
+                 rows=None, cols=None, nthreads: int = 0, chat_ints: bool = True) -> dict:
     """Oracle output of C <- alpha op(A) op(B) + beta C at the entries (rows[q], cols[q]).
 
     Matrices are column-major flat arrays (complex ones as complex128).  With
     rows/cols omitted every entry is computed (column-major order).  Returns
     dict(out=float64 or complex128 array, chat=list of exact integers (or
     (re, im) pairs), D, E, flags) where flags bit0/bit1 mark a non-finite
-    row of op(A) / column of op(B) (P1 Sec. 8.1).
+    row of op(A) / column of op(B) (P1 Sec. 8.1).  chat_ints=False skips the
+    list of Python integers (chat is then None; chat_words still holds c_hat
+    as 256-bit two's complement words), for calls over millions of entries.
     """
     lib = _Lib.get()
     if rows is None:
@@ -333,12 +335,13 @@ def gemm_entries(is_complex: bool, transa: str, transb: str, m: int, n: int, k: 
     if rc != 0:
         raise RuntimeError(f"orc_gemm_entries failed with {rc}")
     ch = chat.reshape(ns, ncomp, 4)
-    if is_complex:
+    outv = out.view(np.complex128) if is_complex else out
+    if not chat_ints:
+        chat_list = None
+    elif is_complex:
         chat_list = [(i256_to_int(ch[q, 0]), i256_to_int(ch[q, 1])) for q in range(ns)]
-        outv = out.view(np.complex128)
     else:
         chat_list = [i256_to_int(ch[q, 0]) for q in range(ns)]
-        outv = out
     return dict(out=outv, chat=chat_list, chat_words=ch, D=D, E=E, flags=flags, t=t)
 
 
