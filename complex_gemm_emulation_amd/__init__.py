@@ -29,7 +29,7 @@ EXPORTED_SYMBOLS = (
     "oz2_plan_info", "oz2_dgemm", "oz2_zgemm", "oz2_dgemm_strided_batched", "oz2_status_string",
     "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt", "oz2_operand_create",
     "oz2_operand_update", "oz2_operand_destroy", "oz2_gemm_prepared", "oz2_chain_plan_create",
-    "oz2_chain_plan_info", "oz2_chain_rescale_be", "oz2_chain_plan_destroy",
+    "oz2_chain_plan_info", "oz2_chain_rescale_be", "oz2_chain_plan_destroy", "oz2_dgemm_noalloc",
 )
 
 _lib = None
@@ -63,6 +63,7 @@ def _raw():
             "oz2_moduli_for_bits": [I64, I, I],
             "oz2_plan_info": [I, I64, I, P, P, P, P],
             "oz2_dgemm": [P, C, C, I64, I64, I64, D, P, I64, P, I64, D, P, I64, I],
+            "oz2_dgemm_noalloc": [P, C, C, I64, I64, I64, D, P, I64, P, I64, D, P, I64, I],
             "oz2_zgemm": [P, C, C, I64, I64, I64, P, P, I64, P, I64, P, P, I64, I],
             "oz2_dgemm_strided_batched": [P, C, C, I64, I64, I64, D, P, I64, I64, P, I64, I64, D,
                                           P, I64, I64, I64, I],
@@ -260,6 +261,20 @@ class Handle:
         _check("oz2_dgemm", _raw().oz2_dgemm(self._h, transa.encode(), transb.encode(), m, n, k,
                                              float(alpha), pa, lda, pb, ldb, float(beta), pc,
                                              ldc, s))
+
+    def dgemm_noalloc(self, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s):
+        """oz2_dgemm_noalloc: the same product with the library's fixed device
+        scratch as workspace (no device allocation during the call)."""
+        ra, ca = self._stored(transa, m, k)
+        rb, cb = self._stored(transb, k, n)
+        need_ab = m > 0 and n > 0 and k > 0 and alpha != 0.0
+        pa = _dev_ptr(A, "f64", _extent(ra, ca, lda), "A") if need_ab else None
+        pb = _dev_ptr(B, "f64", _extent(rb, cb, ldb), "B") if need_ab else None
+        pc = _dev_ptr(C, "f64", _extent(m, n, ldc), "C") if m > 0 and n > 0 else None
+        self._bind_stream()
+        _check("oz2_dgemm_noalloc", _raw().oz2_dgemm_noalloc(self._h, transa.encode(), transb.encode(), m, n,
+                                                             k, float(alpha), pa, lda, pb, ldb, float(beta),
+                                                             pc, ldc, s))
 
     def zgemm(self, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s):
         ra, ca = self._stored(transa, m, k)

@@ -53,6 +53,11 @@ struct oz2_context {
     hipEvent_t ev[5] = {};
     hipEvent_t order_ev = nullptr;  // orders a stream switch after the old stream's work
     Layout last;
+    void* last_ws = nullptr;        // the workspace `last` refers to
+    // the fixed device scratch (oz2_dgemm_noalloc), its address on this
+    // handle's device; noalloc is set for the duration of such a call
+    void* scratch = nullptr;
+    bool noalloc = false;
 };
 
 // a scanned and encoded operand kept on the device between products
@@ -82,7 +87,12 @@ bool valid_op(char c) {
 bool is_trans(char c) { return !(c == 'N' || c == 'n'); }
 bool is_conj(char c) { return c == 'C' || c == 'c'; }
 
+// the workspace of the call in progress: the handle's own, or the fixed
+// scratch during oz2_dgemm_noalloc
+char* workspace(const oz2_context* h) { return (char*)(h->noalloc ? h->scratch : h->ws); }
+
 int ensure_workspace(oz2_context* h, size_t bytes) {
+    if (h->noalloc) return bytes <= kScratchBytes ? OZ2_STATUS_SUCCESS : OZ2_STATUS_WORKSPACE_LIMIT;
     if (bytes <= h->ws_size) return OZ2_STATUS_SUCCESS;
     size_t cap = h->mem_limit;
     if (cap == 0) {
@@ -211,6 +221,10 @@ Layout plan_layout(const oz2_context* h, bool cplx, int s, const ModuliPlan& pla
 // is set, else within the free device memory (plus the current workspace);
 // *cap receives the bound
 bool fits(oz2_context* h, size_t bytes, size_t* cap) {
+    if (h->noalloc) {
+        *cap = kScratchBytes;
+        return bytes <= kScratchBytes;
+    }
     if (h->mem_limit) {
         *cap = h->mem_limit;
         return bytes <= h->mem_limit;
@@ -272,7 +286,7 @@ int product(oz2_context* h, bool cplx, const Layout& L, const int8_t* pa, const 
             const ModuliPlan* pl, bool record) {
     const bool beta_zero = beta[0] == 0.0 && beta[1] == 0.0;
     const int s = L.s;
-    char* ws = (char*)h->ws;
+    char* ws = workspace(h);
     uint8_t* res = (uint8_t*)(ws + L.off_res);
     uint32_t* chat = h->debug ? (uint32_t*)(ws + L.off_chat) : nullptr;
     hipStream_t stm = h->stream;
@@ -329,7 +343,7 @@ int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t
     Layout L = plan_layout(h, cplx, s, *pl, t, m, n, k);
     int st = ensure_workspace(h, L.total);
     if (st) return st;
-    char* ws = (char*)h->ws;
+    char* ws = workspace(h);
     uint64_t* amaxA = (uint64_t*)(ws + L.off_amaxA);
     uint64_t* amaxB = (uint64_t*)(ws + L.off_amaxB);
     int8_t* pa = (int8_t*)(ws + L.off_pa);
@@ -347,6 +361,7 @@ int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t
     if (st) return st;
     L.valid = true;
     h->last = L;
+    h->last_ws = ws;
     return OZ2_STATUS_SUCCESS;
 }
 
@@ -448,6 +463,9 @@ int oz2_create(oz2_handle_t* out) {
         delete h;
         return OZ2_STATUS_HIP_ERROR;
     }
+    // the fixed scratch's address on this device, taken once per device here
+    // at set-up; without it only oz2_dgemm_noalloc fails (HIP_ERROR)
+    if (scratch_address(h->device, &h->scratch) != OZ2_STATUS_SUCCESS) h->scratch = nullptr;
     *out = h;
     return OZ2_STATUS_SUCCESS;
 }
@@ -538,6 +556,25 @@ int oz2_dgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, in
     return gemm_impl(h, false, transa, transb, m, n, k, al, A, lda, B, ldb, be, C, ldc, num_moduli);
 }
 
+int oz2_dgemm_noalloc(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
+                      double alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
+                      double beta, double* C, int64_t ldc, int num_moduli) {
+    if (!h) return -1;
+    if (!h->scratch) return OZ2_STATUS_HIP_ERROR;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != h->device) return OZ2_STATUS_HIP_ERROR;
+    // the same path as oz2_dgemm with the fixed scratch as its workspace; a
+    // product larger than the scratch runs in blocks of C that fit it
+    struct Scope {
+        oz2_context* h;
+        explicit Scope(oz2_context* c) : h(c) { h->noalloc = true; }
+        ~Scope() { h->noalloc = false; }
+    } scope(h);
+    const double al[2] = {alpha, 0.0}, be[2] = {beta, 0.0};
+    const int st = gemm_impl(h, false, transa, transb, m, n, k, al, A, lda, B, ldb, be, C, ldc, num_moduli);
+    return st == OZ2_STATUS_WORKSPACE_LIMIT ? OZ2_STATUS_SCRATCH_LIMIT : st;
+}
+
 int oz2_zgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
               const double* alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
               const double* beta, double* C, int64_t ldc, int num_moduli) {
@@ -600,6 +637,8 @@ const char* oz2_status_string(int status) {
         case OZ2_STATUS_RANGE: return "no scaling width t >= 1 for this number of moduli and k";
         case OZ2_STATUS_WORKSPACE_LIMIT: return "workspace would exceed the memory limit";
         case OZ2_STATUS_NOT_SUPPORTED: return "not supported on this device";
+        case OZ2_STATUS_SCRATCH_LIMIT:
+            return "oz2_dgemm_noalloc: one 256 x 256 block of C with all of k does not fit the fixed 128 MiB scratch";
         case OZ2_STATUS_INTERNAL: return "internal error";
         default: return status < 0 ? "invalid argument" : "unknown status";
     }
@@ -713,6 +752,7 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
     if (st) return st;
     L.valid = true;
     h->last = L;
+    h->last_ws = workspace(h);
     return OZ2_STATUS_SUCCESS;
 }
 
@@ -845,7 +885,7 @@ int oz2_debug_copy(oz2_handle_t h, int which, void* dst, size_t capacity, size_t
     if (!dst) return OZ2_STATUS_SUCCESS;
     if (capacity < nbytes) return -4;
     if (hipStreamSynchronize(h->stream) != hipSuccess) return OZ2_STATUS_HIP_ERROR;
-    if (nbytes && hipMemcpy(dst, (char*)h->ws + off, nbytes, hipMemcpyDeviceToHost) != hipSuccess)
+    if (nbytes && hipMemcpy(dst, (char*)h->last_ws + off, nbytes, hipMemcpyDeviceToHost) != hipSuccess)
         return OZ2_STATUS_HIP_ERROR;
     return OZ2_STATUS_SUCCESS;
 }

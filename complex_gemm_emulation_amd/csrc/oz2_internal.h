@@ -170,6 +170,12 @@ struct CrtTestParams {
     uint32_t M16[kMaxLimb16];
 };
 
+// The fixed device scratch of oz2_dgemm_noalloc (oz2_scratch.hip): one array
+// of kScratchBytes per GPU.  scratch_address gives its device address on
+// `device`, which must be the current device; 0 or an OZ2_STATUS_* code.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+int scratch_address(int device, void** out);
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_fill_u64(uint64_t* p, int64_t n, uint64_t value, hipStream_t st);
 hipError_t launch_scan(const ScanParams& P, bool contiguous, bool cplx, hipStream_t st);

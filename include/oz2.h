@@ -63,7 +63,8 @@ enum {
     OZ2_STATUS_RANGE = 3,            /* no scaling width t >= 1 for this (s, k) */
     OZ2_STATUS_WORKSPACE_LIMIT = 4,  /* workspace would exceed the memory limit */
     OZ2_STATUS_NOT_SUPPORTED = 5,    /* e.g. no gfx950 device */
-    OZ2_STATUS_INTERNAL = 6
+    OZ2_STATUS_INTERNAL = 6,
+    OZ2_STATUS_SCRATCH_LIMIT = 7     /* oz2_dgemm_noalloc: too large for the fixed scratch */
 };
 
 /* Create a handle bound to the current HIP device; its stream is the null
@@ -130,6 +131,26 @@ int oz2_plan_info(int num_moduli, int64_t k, int is_complex, int32_t* moduli_out
 int oz2_dgemm(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
               double alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
               double beta, double* C, int64_t ldc, int num_moduli);
+
+/* For callers that cannot allocate device memory during a call (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * oz2_dgemm with the same arguments, results and status codes, that calls
+ * no hipMalloc, hipFree or other allocating routine.  Its workspace is a
+ * fixed 128 MiB device array per GPU, held from the library's load on that
+ * GPU until the process ends; oz2_create takes its address for the handle's
+ * device.  A product whose workspace exceeds 128 MiB runs in blocks of C
+ * that fit it, bitwise equal to the untiled result (as under
+ * oz2_set_memory_limit); OZ2_STATUS_SCRATCH_LIMIT when not even one
+ * 256 x 256 block with all of k fits (about k > 16000 at s = 16), with
+ * nothing enqueued.  Every call on one GPU, from any handle, shares that
+ * GPU's array and finds the previous call's contents in it (nothing here
+ * needs it cleared): calls that overlap on one GPU race, so issue them on
+ * one stream or order them.  OZ2_STATUS_HIP_ERROR if the current device is
+ * not the handle's or the array's address could not be taken.  The
+ * handle's own workspace is not used or grown. */
+int oz2_dgemm_noalloc(oz2_handle_t h, char transa, char transb, int64_t m, int64_t n, int64_t k,
+                      double alpha, const double* A, int64_t lda, const double* B, int64_t ldb,
+                      double beta, double* C, int64_t ldc, int num_moduli);
 
 /* Complex version (Arc page Sec. 5): A, B, C are interleaved complex128;
  * alpha[2] and beta[2] are HOST arrays (re, im); 'C' conjugates.  Uses one
