@@ -26,9 +26,12 @@ Other workloads (--workload), each printing the same kind of JSON line:
              s = 8 and 16; one step = the 16 calls, all inputs resident
 
 Printed: ONE JSON line with the metric, per-call phase times (HIP events
-recorded on the stream the kernels run on), the roofline of the dominant
-kernel and the oracle's rate on a bounded sample on the host cores
-(cpu_baseline).
+recorded on the stream the kernels run on), the median and best step, the
+memory phases against HBM ceilings measured on the same GPU with this
+library's own stream kernels, the roofline of the dominant kernel, the
+oracle's rate on a bounded sample on the host cores and on one core
+(cpu_baseline), and how many of that sample's entries differ from one GPU
+call at the same s (parity_sample).
 
 Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload dgemm8192]
        python bench.py --copy-calibration ...   (also runs a plain device copy of
@@ -121,6 +124,62 @@ def copy_calibration(torch):
     del src, dst
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+STREAM_LIB = os.path.join(ROOT, "complex_gemm_emulation_amd", "liboz2_stream.so")
+
+
+def hbm_ceilings(torch, nbytes=1 << 30, reps=3):
+    """Measured HBM ceilings on this GPU: the best rate over launch shapes of
+    this library's own read-only, write-only and copy stream kernels
+    (liboz2_stream.so) on `nbytes` buffers, each shape timed `reps` times
+    with events on the current stream after one untimed run.  Copy counts
+    the bytes read plus the bytes written."""
+    import ctypes
+    lib = ctypes.CDLL(STREAM_LIB)
+    lib.oz2_stream_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.oz2_stream_run.restype = ctypes.c_int
+    src = torch.empty(nbytes // 8, dtype=torch.float64, device="cuda").uniform_(-1, 1)
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream()
+    best = {}
+    for kind, name in ((0, "read"), (1, "write"), (2, "copy")):
+        moved = nbytes * (2 if kind == 2 else 1)
+        for blocks in (1024, 2048, 4096, 8192):
+            for unroll in (2, 4, 8):
+                for nt in (0, 1):
+                    args = (kind, ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes,
+                            blocks, unroll, nt, ctypes.c_void_p(st.cuda_stream))
+                    if lib.oz2_stream_run(*args) != 0:
+                        raise RuntimeError("oz2_stream_run failed")
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(reps):
+                        lib.oz2_stream_run(*args)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    gbs = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                    if gbs > best.get(name, (0.0,))[0]:
+                        best[name] = (gbs, f"{blocks}x256 threads, {unroll} x 16 B per trip"
+                                           + (", nontemporal" if nt else ""))
+    del src, dst
+    out = {f"{k}_gbs": round(v[0], 1) for k, v in best.items()}
+    out["shapes"] = {k: v[1] for k, v in best.items()}
+    out["how"] = (f"best over 24 launch shapes of this library's stream kernels on {nbytes >> 20} MiB, "
+                  "events on the stream; copy counts read + write bytes")
+    return out
+
+
 def sample_entries(m, n, side, seed):
     rng = np.random.default_rng(seed)
     rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, min(side, m), replace=False)]))[:side]
@@ -129,22 +188,41 @@ def sample_entries(m, n, side, seed):
     return ii.reshape(-1), jj.reshape(-1), rows.size, cols.size
 
 
-def cpu_baseline_gemm(spec, ops_a, A, B, C, s, side, label):
+def cpu_baseline_gemm(spec, ops_a, A, B, C, s, side, label, got=None, single_side=64):
     """The oracle (as it stands) on a seeded side x side sample of output
-    entries of the same workload, on all host cores."""
+    entries of the same workload, on all host cores, then on a smaller
+    single_side^2 sample on one core.  got: the GPU's output of one call at
+    this s (column-major, flat); the sample's entries are compared with it
+    bit for bit and the count that differ is returned with the rates."""
     import oracle
     m, n, k = spec["m"], spec["n"], spec["k"]
     ii, jj, nr, nc = sample_entries(m, n, side, 12345)
     nt = oracle.max_threads()
     lda, ldb = ops_a
     t0 = time.perf_counter()
-    oracle.gemm_entries(spec["cplx"], spec["transa"], spec["transb"], m, n, k, spec["alpha"], A, lda,
-                        B, ldb, spec["beta"], C, m, s, rows=ii, cols=jj, nthreads=nt)
+    r = oracle.gemm_entries(spec["cplx"], spec["transa"], spec["transb"], m, n, k, spec["alpha"], A, lda,
+                            B, ldb, spec["beta"], C, m, s, rows=ii, cols=jj, nthreads=nt, chat_ints=False)
     dt = time.perf_counter() - t0
     flops_per_entry = (8.0 if spec["cplx"] else 2.0) * k
-    return dict(value=flops_per_entry * ii.size / dt / 1e12, unit="TFLOP/s", cores=nt, kind="oracle",
-                sample=f"{nr}x{nc} sampled output entries of the {label} s={s} workload "
-                       f"(exact wide-integer products), {dt:.1f} s")
+    i1, j1, _, _ = sample_entries(m, n, single_side, 54321)
+    t1 = time.perf_counter()
+    oracle.gemm_entries(spec["cplx"], spec["transa"], spec["transb"], m, n, k, spec["alpha"], A, lda,
+                        B, ldb, spec["beta"], C, m, s, rows=i1, cols=j1, nthreads=1, chat_ints=False)
+    dt1 = time.perf_counter() - t1
+    out = dict(value=flops_per_entry * ii.size / dt / 1e12, unit="TFLOP/s", cores=nt, kind="oracle",
+               sample=f"{nr}x{nc} sampled output entries of the {label} s={s} workload "
+                      f"(exact wide-integer products), {dt:.1f} s",
+               cpu_model=cpu_model(),
+               single_thread=dict(value=flops_per_entry * i1.size / dt1 / 1e12, unit="TFLOP/s",
+                                  sample=f"{i1.size} sampled entries, {dt1:.1f} s"))
+    parity = None
+    if got is not None:
+        w = np.ascontiguousarray(r["out"])
+        g = np.ascontiguousarray(got[ii + jj * m])
+        wb, gb = w.view(np.uint64).reshape(w.size, -1), g.view(np.uint64).reshape(g.size, -1)
+        parity = dict(s=s, entries=int(ii.size), not_bit_identical=int(np.count_nonzero(np.any(wb != gb, axis=1))),
+                      how="one GPU call at this s on a fresh C, against the oracle at the sampled entries")
+    return out, parity
 
 
 GEMM_SPECS = {
@@ -363,11 +441,15 @@ def run_gemm(args, name):
     phases = {s: [] for s in s_list}
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    ev[0].record()
+    for q in range(args.steps):
         step(phases)
+        ev[q + 1].record()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    step_ms = [ev[q].elapsed_time(ev[q + 1]) for q in range(args.steps)]
     ms_per_step = dt / args.steps * 1e3
     fl = (8.0 if cplx else 2.0) * m * n * k
     value = fl * len(s_list) / (dt / args.steps) / 1e12
@@ -400,12 +482,37 @@ def run_gemm(args, name):
                     ops_per_launch=gemm_ops / len(s_list),
                     launch_ms=round(gemm_ms / len(s_list), 4))
 
-    cpu = None
+    ceil = None
+    if not args.no_ceiling:
+        log("[bench] HBM ceilings: this library's read, write and copy stream kernels")
+        ceil = hbm_ceilings(torch)
+        for s in s_list:
+            rec = per_s[str(s)]
+            rec["scan_frac_of_read_ceiling"] = round(rec["scan_gbs"] / ceil["read_gbs"], 4)
+            rec["encode_frac_of_copy_ceiling"] = round(rec["encode_gbs"] / ceil["copy_gbs"], 4)
+            rec["reconstruct_frac_of_copy_ceiling"] = round(rec["reconstruct_gbs"] / ceil["copy_gbs"], 4)
+            for ph in ("scan", "encode", "reconstruct"):
+                rec[f"{ph}_frac_of_peak"] = round(rec[f"{ph}_gbs"] / PEAK_HBM_GBS, 4)
+
+    cpu = parity = None
     if not args.no_cpu_baseline:
         s_cpu = s_list[-1]
         side = args.cpu_side or spec["cpu_side"]
+        got = None
+        if not prepared:
+            log(f"[bench] one s={s_cpu} call on a fresh C for the sample's parity")
+            dC2 = (torch.from_numpy(C.copy()).cuda() if C is not None else
+                   torch.zeros(m * n, dtype=torch.complex128 if cplx else torch.float64, device="cuda"))
+            h = handles[s_cpu]
+            if cplx:
+                h.zgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC2, m, s_cpu)
+            else:
+                h.dgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC2, m, s_cpu)
+            torch.cuda.synchronize()
+            got = dC2.cpu().numpy()
+            del dC2
         log(f"[bench] oracle cpu baseline on a {side}^2 entry sample, s={s_cpu}")
-        cpu = cpu_baseline_gemm(spec, (ra, rb), A, B, C, s_cpu, side, f"{m}x{n}x{k}")
+        cpu, parity = cpu_baseline_gemm(spec, (ra, rb), A, B, C, s_cpu, side, f"{m}x{n}x{k}", got)
 
     accuracy = None
     if not cplx and spec["beta"] == 0:
@@ -419,10 +526,6 @@ def run_gemm(args, name):
             err, how = general_accuracy(handles[s], spec, A, B, C, s)
             accuracy[str(s)] = err
         accuracy["sample"] = how
-
-    native = None
-    if not args.no_native:
-        native = native_fp64_rate(torch, dA, dB, m, n, k, ta, tb, cplx)
 
     for pa, pb in prepared.values():
         pa.close()
@@ -442,41 +545,15 @@ def run_gemm(args, name):
                                + ("_prepared_a" if prepared else ""),
                    "m": m, "n": n, "k": k, "s": s_list, "ops": f"{ta}/{tb}",
                    "alpha": str(spec["alpha"]), "beta": str(spec["beta"])},
+        "step_ms": dict(median=round(float(np.median(step_ms)), 3), best=round(float(np.min(step_ms)), 3),
+                        how="HIP events on the stream around each timed step"),
         "per_s": per_s,
+        "hbm_ceiling": ceil,
         "accuracy": accuracy,
+        "parity_sample": parity,
         "roofline": roofline,
-        "native_fp64": native,
         "cpu_baseline": cpu,
     }
-
-
-def native_fp64_rate(torch, dA, dB, m, n, k, ta, tb, cplx, reps=5):
-    """Context, not a target: the same product in native FP64 (complex128)
-    with torch.matmul on the same GPU, which the pages use as the
-    denominator of their speed-ups.  Median of `reps` timed calls."""
-    def op(X, rows, cols, t):
-        Xm = X.reshape(cols, rows).T          # column-major rows x cols
-        if t == "N":
-            return Xm
-        return Xm.T.conj() if t == "C" else Xm.T
-    A = op(dA, m if ta == "N" else k, k if ta == "N" else m, ta).contiguous()
-    B = op(dB, k if tb == "N" else n, n if tb == "N" else k, tb).contiguous()
-    for _ in range(2):
-        C = A @ B
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        C = A @ B
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    del C, A, B
-    ms = float(np.median(times))
-    fl = (8.0 if cplx else 2.0) * m * n * k
-    return {"tflops": round(fl / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 3),
-            "how": f"torch.matmul in {'complex128' if cplx else 'float64'}, median of {reps}"}
 
 
 def run_nonsquare(args):
@@ -552,7 +629,7 @@ def run_nonsquare(args):
         spec = dict(m=m, n=n, k=k, cplx=False, transa="N", transb="N", alpha=1.0, beta=0.0)
         side = args.cpu_side or 1024
         log(f"[bench] oracle cpu baseline on a {side}^2 entry sample of {m}x{k}x{n}, s=16")
-        cpu = cpu_baseline_gemm(spec, (m, k), A, B, None, 16, side, f"{m}x{k}x{n}")
+        cpu, _ = cpu_baseline_gemm(spec, (m, k), A, B, None, 16, side, f"{m}x{k}x{n}")
     for h in handles.values():
         h.close()
     return {
@@ -646,7 +723,7 @@ def run_chain_rbe(args):
             oracle.rescale_be.chain_tensor(X[t * n3:(t + 1) * n3], rplan)
         cdt = time.perf_counter() - t0
         cpu = dict(value=n3 * nt / cdt / 1e9, unit="GDoF/s", cores=1, kind="oracle",
-                   sample=f"first {nt} of the {batch} tensors, whole chain, {cdt:.1f} s")
+                   sample=f"first {nt} of the {batch} tensors, whole chain, {cdt:.1f} s", cpu_model=cpu_model())
     log("[bench] accuracy against the exact chain")
     err, how = chain_accuracy(dY.cpu().numpy(), X, ops, n, args.chain_acc_tensors)
     accuracy = {"normwise_rel_err": err, "sample": how}
@@ -743,7 +820,7 @@ def run_chain(args):
         oracle_chain(X, ops[0], ops[1], ops[2], n, nt, s)
         cdt = time.perf_counter() - t0
         cpu = dict(value=n3 * nt / cdt / 1e9, unit="GDoF/s", cores=oracle.max_threads(), kind="oracle",
-                   sample=f"first {nt} of the {batch} tensors, all three modes, {cdt:.1f} s")
+                   sample=f"first {nt} of the {batch} tensors, all three modes, {cdt:.1f} s", cpu_model=cpu_model())
     log("[bench] accuracy against the exact chain")
     err, how = chain_accuracy(dY.cpu().numpy(), X, ops, n, args.chain_acc_tensors)
     accuracy = {"normwise_rel_err": err, "sample": how}
@@ -778,7 +855,7 @@ def main():
     ap.add_argument("--chain-acc-tensors", type=int, default=8)
     ap.add_argument("--chain-depth", type=int, default=3, help="chain_rbe: operators (3 = one pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-native", action="store_true", help="skip timing the native FP64 product (context)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip timing the HBM stream ceilings")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -802,7 +879,8 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
             "data": "synthetic", "config": out["config"]}
-    for key in ("per_s", "per_shape", "accuracy", "roofline", "native_fp64", "cpu_baseline"):
+    for key in ("step_ms", "per_s", "per_shape", "hbm_ceiling", "accuracy", "parity_sample", "roofline",
+                "cpu_baseline"):
         if key in out:
             line[key] = out[key]
     print(json.dumps(line))
