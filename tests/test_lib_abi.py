@@ -1,4 +1,4 @@
-"""The C-ABI library loads, exports every symbol include/oz2.h declares, and
+"""The C-ABI libraries load and export every symbol include/*.h declares, and
 its host planner agrees with the independently written oracle (no GPU)."""
 import os
 import re
@@ -19,6 +19,27 @@ def _declared_symbols():
 
 def test_header_symbols_match_binding_list():
     assert _declared_symbols() == sorted(oz2.EXPORTED_SYMBOLS)
+
+
+def test_stream_library_exports_its_header():
+    # include/oz2_stream.h: the stream kernels the bench times as HBM ceilings
+    import ctypes
+    text = open(os.path.join(ROOT, "include", "oz2_stream.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(oz2_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["oz2_stream_run"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "complex_gemm_emulation_amd", "liboz2_stream.so"))
+    for name in names:
+        assert hasattr(lib, name), name
+    # argument checks return before any launch (no GPU needed)
+    fn = lib.oz2_stream_run
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    assert fn(7, None, None, 16, 1, 2, 0, None) == -1
+    assert fn(1, None, None, 16, 1, 2, 0, None) == -3
+    assert fn(1, None, ctypes.c_void_p(16), 17, 1, 2, 0, None) == -4
+    assert fn(1, None, ctypes.c_void_p(16), 16, 1, 3, 0, None) == -6
 
 
 def test_library_exports_every_declared_symbol():
