@@ -24,6 +24,9 @@ Other workloads (--workload), each printing the same kind of JSON line:
   nonsquare  the eight m x k x n shapes of the Arc page's Table 10 (k from
              256 to 65536, m or n from 1024 to 65536), N/N, U(-1,1) entries,
              s = 8 and 16; one step = the 16 calls, all inputs resident
+  tiled8192  the headline product under a 1 GiB workspace cap: memory-aware
+             tiling in blocks of C; reports each s's blocking and the
+             slowdown against the same calls untiled
 
 Printed: ONE JSON line with the metric, per-call phase times (HIP events
 recorded on the stream the kernels run on), the median and best step, the
@@ -238,6 +241,10 @@ GEMM_SPECS = {
     # (oz2_operand_update) and runs oz2_gemm_prepared
     "reuse8192": dict(cplx=False, m=8192, n=8192, k=8192, s=[8, 12, 16], transa="N", transb="N",
                       alpha=1.0, beta=0.0, phi=0.5, seedw=2, cpu_side=1024, prepared_a=True),
+    # the headline product under a 1 GiB workspace cap (memory-aware tiling):
+    # the untiled workspace is 1.5 / 2.25 / 3 GiB at s = 8 / 12 / 16
+    "tiled8192": dict(cplx=False, m=8192, n=8192, k=8192, s=[8, 12, 16], transa="N", transb="N",
+                      alpha=1.0, beta=0.0, phi=0.5, seedw=2, cpu_side=1024, mem_limit=1 << 30),
 }
 
 
@@ -412,6 +419,8 @@ def run_gemm(args, name):
     handles = {s: oz2.Handle(stream) for s in s_list}
     for h in handles.values():
         h.set_timing(True)
+        if spec.get("mem_limit"):
+            h.set_memory_limit(spec["mem_limit"])
 
     prepared = {}
     if spec.get("prepared_a"):
@@ -461,6 +470,10 @@ def run_gemm(args, name):
         ph = np.mean(np.array(phases[s]), axis=0)  # ms: scan, encode, gemm, reconstruct
         wk = algorithmic(m, n, k, s, cplx, beta_nz)
         call_ms = float(np.sum(ph))
+        if spec.get("mem_limit"):
+            # a tiled call times only its whole duration
+            per_s[str(s)] = dict(tflops=fl / (call_ms * 1e-3) / 1e12, ms=dict(call=round(call_ms, 4)))
+            continue
         per_s[str(s)] = dict(
             tflops=fl / (call_ms * 1e-3) / 1e12,
             ms=dict(scan=round(float(ph[0]), 4), encode=round(float(ph[1]), 4),
@@ -473,14 +486,44 @@ def run_gemm(args, name):
         )
         gemm_ops += wk["int8_ops"]
         gemm_ms += float(ph[2])
+    tiling = None
+    if spec.get("mem_limit"):
+        # the same calls untiled, for the slowdown (own handles, no cap)
+        plans = {str(s): handles[s].tile_plan() for s in s_list}
+        free = {s: oz2.Handle(stream) for s in s_list}
+        for _ in range(2):
+            for s in s_list:
+                free[s].dgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for s in s_list:
+                free[s].dgemm(ta, tb, m, n, k, spec["alpha"], dA, ra, dB, rb, spec["beta"], dC, m, s)
+        e1.record()
+        torch.cuda.synchronize()
+        untiled_ms = e0.elapsed_time(e1) / reps
+        for h2 in free.values():
+            h2.close()
+        tiling = dict(mem_limit=spec["mem_limit"], plans=plans,
+                      workspace_bytes={str(s): handles[s].workspace_size() for s in s_list},
+                      untiled_ms_per_step=round(untiled_ms, 3),
+                      slowdown=round(float(np.median(step_ms)) / untiled_ms, 4),
+                      how="median tiled step over the untiled step of the same calls without a cap")
+
     # residue GEMM: one launch per call; the mean launch of a step does the
     # mean of the calls' INT8 ops, timed by HIP events on its stream
-    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else 0.0
     roofline = dict(kernel="residue_gemm_kernel (INT8 MFMA, fused mod m)", bound="mfma",
                     achieved=round(achieved, 2), peak=PEAK_INT8_TOPS, unit="TOP/s",
                     frac=round(achieved / PEAK_INT8_TOPS, 4), traffic=measured_traffic(name),
                     ops_per_launch=gemm_ops / len(s_list),
                     launch_ms=round(gemm_ms / len(s_list), 4))
+    if tiling:
+        # a tiled call records only its whole duration (reported as the GEMM
+        # phase), so the GEMM's own rate is not separable here
+        roofline = None
 
     ceil = None
     if not args.no_ceiling:
@@ -488,6 +531,8 @@ def run_gemm(args, name):
         ceil = hbm_ceilings(torch)
         for s in s_list:
             rec = per_s[str(s)]
+            if "scan_gbs" not in rec:
+                continue
             rec["scan_frac_of_read_ceiling"] = round(rec["scan_gbs"] / ceil["read_gbs"], 4)
             rec["encode_frac_of_copy_ceiling"] = round(rec["encode_gbs"] / ceil["copy_gbs"], 4)
             rec["reconstruct_frac_of_copy_ceiling"] = round(rec["reconstruct_gbs"] / ceil["copy_gbs"], 4)
@@ -542,13 +587,14 @@ def run_gemm(args, name):
         "ms_per_step": round(ms_per_step, 3),
         "dtype": "i8",
         "config": {"workload": f"{kind}_{m}_{ta}{tb}_phi{spec['phi']}_s{'_'.join(map(str, s_list))}"
-                               + ("_prepared_a" if prepared else ""),
+                               + ("_prepared_a" if prepared else "") + ("_cap1GiB" if spec.get("mem_limit") else ""),
                    "m": m, "n": n, "k": k, "s": s_list, "ops": f"{ta}/{tb}",
                    "alpha": str(spec["alpha"]), "beta": str(spec["beta"])},
         "step_ms": dict(median=round(float(np.median(step_ms)), 3), best=round(float(np.min(step_ms)), 3),
                         how="HIP events on the stream around each timed step"),
         "per_s": per_s,
         "hbm_ceiling": ceil,
+        "tiling": tiling,
         "accuracy": accuracy,
         "parity_sample": parity,
         "roofline": roofline,
@@ -846,7 +892,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
                     choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "nonsquare",
-                             "reuse8192"])
+                             "reuse8192", "tiled8192"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)
@@ -879,8 +925,8 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
             "data": "synthetic", "config": out["config"]}
-    for key in ("step_ms", "per_s", "per_shape", "hbm_ceiling", "accuracy", "parity_sample", "roofline",
-                "cpu_baseline"):
+    for key in ("step_ms", "per_s", "per_shape", "hbm_ceiling", "tiling", "accuracy", "parity_sample",
+                "roofline", "cpu_baseline"):
         if key in out:
             line[key] = out[key]
     print(json.dumps(line))

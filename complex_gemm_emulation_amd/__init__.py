@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt", "oz2_operand_create",
     "oz2_operand_update", "oz2_operand_destroy", "oz2_gemm_prepared", "oz2_chain_plan_create",
     "oz2_chain_plan_info", "oz2_chain_rescale_be", "oz2_chain_plan_destroy", "oz2_dgemm_noalloc",
+    "oz2_get_tile_plan",
 )
 
 _lib = None
@@ -64,6 +65,7 @@ def _raw():
             "oz2_plan_info": [I, I64, I, P, P, P, P],
             "oz2_dgemm": [P, C, C, I64, I64, I64, D, P, I64, P, I64, D, P, I64, I],
             "oz2_dgemm_noalloc": [P, C, C, I64, I64, I64, D, P, I64, P, I64, D, P, I64, I],
+            "oz2_get_tile_plan": [P, P, P, P],
             "oz2_zgemm": [P, C, C, I64, I64, I64, P, P, I64, P, I64, P, P, I64, I],
             "oz2_dgemm_strided_batched": [P, C, C, I64, I64, I64, D, P, I64, I64, P, I64, I64, D,
                                           P, I64, I64, I64, I],
@@ -241,6 +243,14 @@ class Handle:
         arr = (ctypes.c_float * 4)()
         _check("oz2_get_phase_times", _raw().oz2_get_phase_times(self._h, arr))
         return list(arr)
+
+    def tile_plan(self) -> dict:
+        """Blocking of the last product (oz2_get_tile_plan): block sides and
+        which operand's encoded block was kept ('untiled', 'A', 'B', 'prepared')."""
+        mb, nb, held = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+        _check("oz2_get_tile_plan", _raw().oz2_get_tile_plan(self._h, ctypes.byref(mb), ctypes.byref(nb),
+                                                             ctypes.byref(held)))
+        return dict(mb=mb.value, nb=nb.value, held=("untiled", "A", "B", "prepared")[held.value])
 
     def set_debug(self, enable: bool) -> None:
         _check("oz2_set_debug", _raw().oz2_set_debug(self._h, int(enable)))

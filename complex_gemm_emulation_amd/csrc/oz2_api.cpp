@@ -58,6 +58,10 @@ struct oz2_context {
     // handle's device; noalloc is set for the duration of such a call
     void* scratch = nullptr;
     bool noalloc = false;
+    // blocking of the last product: block rows and columns of C, and which
+    // operand's encoded block was kept across the other's blocks
+    int64_t tile_mb = 0, tile_nb = 0;
+    int tile_held = OZ2_TILE_UNTILED;
 };
 
 // a scanned and encoded operand kept on the device between products
@@ -281,9 +285,9 @@ int encode_operand(oz2_context* h, bool cplx, bool is_a, char trans, int64_t row
 // per k run of at most kMaxRunK positions), then CRT, rounding, scale back
 // and alpha/beta.  L gives the padded sizes and the workspace offsets of the
 // product residues (and c_hat).
-int product(oz2_context* h, bool cplx, const Layout& L, const int8_t* pa, const uint64_t* amaxA, const int8_t* pb,
-            const uint64_t* amaxB, const double alpha[2], const double beta[2], double* C, int64_t ldc,
-            const ModuliPlan* pl, bool record) {
+int product(oz2_context* h, bool cplx, const Layout& L, const int8_t* pa, int64_t a_rows, const uint64_t* amaxA,
+            const int8_t* pb, int64_t b_rows, const uint64_t* amaxB, const double alpha[2], const double beta[2],
+            double* C, int64_t ldc, const ModuliPlan* pl, bool record) {
     const bool beta_zero = beta[0] == 0.0 && beta[1] == 0.0;
     const int s = L.s;
     char* ws = workspace(h);
@@ -295,8 +299,9 @@ int product(oz2_context* h, bool cplx, const Layout& L, const int8_t* pa, const 
         GemmParams G{};
         G.A = pa; G.B = pb;
         G.mp = L.mp; G.np = L.np; G.kp = L.kp; G.n = L.n;
-        G.a_set_stride = (int64_t)s * L.mp * L.kp;
-        G.b_set_stride = (int64_t)s * L.np * L.kp;
+        G.a_rows = a_rows; G.b_rows = b_rows;
+        G.a_set_stride = (int64_t)s * a_rows * L.kp;
+        G.b_set_stride = (int64_t)s * b_rows * L.kp;
         G.c_set_stride = (int64_t)s * L.n * L.mp;
         G.s = s;
         for (int q = 0; q < s; ++q) {
@@ -357,11 +362,178 @@ int core(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t
     if ((st = encode_operand(h, cplx, false, transb, n, k, B, ldb, s, pl, t, ext, amaxB, pb, L.np, L.kp)))
         return st;
     if (record) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
-    st = product(h, cplx, L, pa, amaxA, pb, amaxB, alpha, beta, C, ldc, pl, record);
+    st = product(h, cplx, L, pa, L.mp, amaxA, pb, L.np, amaxB, alpha, beta, C, ldc, pl, record);
     if (st) return st;
     L.valid = true;
     h->last = L;
     h->last_ws = ws;
+    return OZ2_STATUS_SUCCESS;
+}
+
+// ------------------------------------------------------------------------
+// Memory-aware tiling (Arc page Sec. 6, memory-aware tiling, and Table 16's
+// power-of-two tiles; Sec. 9.2 for the shape of the cost model).  When the
+// workspace of the whole product exceeds the cap, C is computed in blocks of
+// mb x nb entries, each with all of k, so that every block has the full row
+// and column exponents and the result is bitwise that of the untiled call.
+// One operand's encoded block is kept while the other's blocks go by, so
+// that operand is scanned and encoded once in total.
+// ------------------------------------------------------------------------
+struct TilePlan {
+    int64_t mb = 0, nb = 0;
+    bool hold_a = true;  // block rows outer (op(A) block kept); else block columns outer
+    double cost_us = 0;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Time of one block's residue products (us): the per-block model measured on
+// this GPU, about 11 us fixed plus 0.76 us per 64-position k step for a
+// 256 x 256 tile with one block per CU, over waves of 256 CUs; the 128 x 128
+// tile (small grids or short k) runs four blocks per CU at about 1.22 times
+// the time per step.  Complex products run three k-loops per block.
+double gemm_block_us(int64_t mb, int64_t nb, int64_t kp, int s, bool cplx) {
+    const double steps = (double)kp / kGemmStepK;
+    const int64_t mp = round_up(mb, kPadM), np = round_up(nb, kPadM);
+    const double passes = cplx ? 3.0 : 1.0;
+    const int64_t big = (mp / 256) * (np / 256) * s;
+    if (big >= 512 && kp > 512) return (double)ceil_div(big, 256) * (11.0 + 0.76 * steps * passes);
+    const int64_t small = (mp / 128) * (np / 128) * s;
+    return (double)ceil_div(small, 1024) * (11.0 + 0.93 * steps * passes);
+}
+
+// Modelled time of the whole product under a blocking (us): residue products
+// of every block, the scans and encodes (each operand block read once and
+// its planes written once, at about 4.5 TB/s), the reconstructions (the same
+// for every blocking) and about 4 us per kernel launch.
+double tile_cost_us(bool cplx, int s, int64_t m, int64_t n, int64_t k, int64_t mb, int64_t nb, bool hold_a,
+                    bool prepared) {
+    const int64_t kp = round_up(k, kPadK);
+    const int64_t br = ceil_div(m, mb), bc = ceil_div(n, nb);
+    const int64_t mlast = m - (br - 1) * mb, nlast = n - (bc - 1) * nb;
+    double gemm = 0;
+    gemm += (double)(br - 1) * (bc - 1) * gemm_block_us(mb, nb, kp, s, cplx);
+    gemm += (double)(br - 1) * gemm_block_us(mb, nlast, kp, s, cplx);
+    gemm += (double)(bc - 1) * gemm_block_us(mlast, nb, kp, s, cplx);
+    gemm += gemm_block_us(mlast, nlast, kp, s, cplx);
+    const double w = cplx ? 2.0 : 1.0, sets = cplx ? 3.0 : 1.0, outs = cplx ? 2.0 : 1.0;
+    const double per_elem = 16.0 * w + sets * s;  // scan reads 8w, encode reads 8w and writes sets * s
+    double enc_bytes = 0;
+    int64_t launches = br * bc * (kp > 130816 ? 3 : 2);
+    if (!prepared) {
+        const double a_times = hold_a ? 1.0 : (double)bc, b_times = hold_a ? (double)br : 1.0;
+        enc_bytes = per_elem * ((double)m * k * a_times + (double)n * k * b_times);
+        launches += 4 * (hold_a ? br + br * bc : bc + br * bc);
+    }
+    const double crt_bytes = (outs * s + 8.0 * w) * (double)m * n;
+    return gemm + enc_bytes / 4.5e6 + crt_bytes / 4.0e6 + 4.0 * (double)launches;
+}
+
+// Cheapest blocking whose workspace fits `cap`: block sides are the whole
+// dimension or a power-of-two multiple of 256 below it, non-square allowed,
+// with either operand held.  Returns false when no 256 x 256 block fits.
+bool choose_tiles(const oz2_context* h, bool cplx, int s, const ModuliPlan& pl, int t, int64_t m, int64_t n,
+                  int64_t k, size_t cap, bool prepared, TilePlan* best) {
+    int64_t cm[40], cn[40];
+    int nm = 0, nn = 0;
+    for (int64_t T = kPadM; T < m && nm < 39; T *= 2) cm[nm++] = T;
+    cm[nm++] = m;
+    for (int64_t T = kPadM; T < n && nn < 39; T *= 2) cn[nn++] = T;
+    cn[nn++] = n;
+    bool found = false;
+    for (int a = 0; a < nm; ++a) {
+        for (int b = 0; b < nn; ++b) {
+            const int64_t mb = cm[a], nb = cn[b];
+            if (plan_layout(h, cplx, s, pl, t, mb, nb, k, !prepared).total > cap) continue;
+            for (int held = 0; held < (prepared ? 1 : 2); ++held) {
+                const double c = tile_cost_us(cplx, s, m, n, k, mb, nb, held == 0, prepared);
+                // ties go to the larger block (fewer launches)
+                if (!found || c < best->cost_us || (c == best->cost_us && mb * nb > best->mb * best->nb)) {
+                    best->mb = mb; best->nb = nb; best->hold_a = held == 0; best->cost_us = c;
+                    found = true;
+                }
+            }
+        }
+    }
+    return found;
+}
+
+// the four phases over the blocks of a plan; the workspace is laid out for
+// the largest block, and each block's planes use its own padded sizes
+int tiled_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, int64_t n, int64_t k,
+               const double alpha[2], const double* A, int64_t lda, const double* B, int64_t ldb,
+               const double beta[2], double* C, int64_t ldc, int s, const ModuliPlan* pl, int t, bool ext,
+               const TilePlan& tp) {
+    const int64_t mb = tp.mb < m ? tp.mb : m, nb = tp.nb < n ? tp.nb : n;
+    const Layout Lmax = plan_layout(h, cplx, s, *pl, t, mb, nb, k);
+    int st = ensure_workspace(h, Lmax.total);
+    if (st) return st;
+    char* ws = workspace(h);
+    uint64_t* amaxA = (uint64_t*)(ws + Lmax.off_amaxA);
+    uint64_t* amaxB = (uint64_t*)(ws + Lmax.off_amaxB);
+    int8_t* pa = (int8_t*)(ws + Lmax.off_pa);
+    int8_t* pb = (int8_t*)(ws + Lmax.off_pb);
+    const int64_t w = cplx ? 2 : 1;  // doubles per element
+    hipStream_t stm = h->stream;
+    const bool rec = h->timing != 0;
+    if (rec)
+        for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+    auto encode_a = [&](int64_t i0, int64_t rows) -> int {
+        const double* Ab = A + w * (is_trans(transa) ? i0 * lda : i0);
+        const int64_t rp = round_up(rows, kPadM);
+        int r = scan_operand(h, cplx, true, transa, rows, k, Ab, lda, amaxA, rp);
+        if (!r) r = encode_operand(h, cplx, true, transa, rows, k, Ab, lda, s, pl, t, ext, amaxA, pa, rp, Lmax.kp);
+        return r;
+    };
+    auto encode_b = [&](int64_t j0, int64_t cols) -> int {
+        const double* Bb = B + w * (is_trans(transb) ? j0 : j0 * ldb);
+        const int64_t cp = round_up(cols, kPadM);
+        int r = scan_operand(h, cplx, false, transb, cols, k, Bb, ldb, amaxB, cp);
+        if (!r) r = encode_operand(h, cplx, false, transb, cols, k, Bb, ldb, s, pl, t, ext, amaxB, pb, cp, Lmax.kp);
+        return r;
+    };
+    auto block = [&](int64_t i0, int64_t rows, int64_t j0, int64_t cols) -> int {
+        Layout Lb = plan_layout(h, cplx, s, *pl, t, rows, cols, k);
+        Lb.off_amaxA = Lmax.off_amaxA; Lb.off_amaxB = Lmax.off_amaxB;
+        Lb.off_pa = Lmax.off_pa; Lb.off_pb = Lmax.off_pb;
+        Lb.off_res = Lmax.off_res; Lb.off_chat = Lmax.off_chat;
+        double* Cb = C + w * (i0 + j0 * ldc);
+        const int r = product(h, cplx, Lb, pa, Lb.mp, amaxA, pb, Lb.np, amaxB, alpha, beta, Cb, ldc, pl, false);
+        if (!r) {
+            Lb.valid = true;
+            h->last = Lb;
+            h->last_ws = ws;
+        }
+        return r;
+    };
+    if (tp.hold_a) {
+        for (int64_t i0 = 0; i0 < m; i0 += mb) {
+            const int64_t rows = m - i0 < mb ? m - i0 : mb;
+            if ((st = encode_a(i0, rows))) return st;
+            for (int64_t j0 = 0; j0 < n; j0 += nb) {
+                const int64_t cols = n - j0 < nb ? n - j0 : nb;
+                if ((st = encode_b(j0, cols))) return st;
+                if ((st = block(i0, rows, j0, cols))) return st;
+            }
+        }
+    } else {
+        for (int64_t j0 = 0; j0 < n; j0 += nb) {
+            const int64_t cols = n - j0 < nb ? n - j0 : nb;
+            if ((st = encode_b(j0, cols))) return st;
+            for (int64_t i0 = 0; i0 < m; i0 += mb) {
+                const int64_t rows = m - i0 < mb ? m - i0 : mb;
+                if ((st = encode_a(i0, rows))) return st;
+                if ((st = block(i0, rows, j0, cols))) return st;
+            }
+        }
+    }
+    if (rec) {
+        for (int e = 3; e < 5; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+        h->timed = true;
+    }
+    h->tile_mb = mb;
+    h->tile_nb = nb;
+    h->tile_held = tp.hold_a ? OZ2_TILE_HOLD_A : OZ2_TILE_HOLD_B;
     return OZ2_STATUS_SUCCESS;
 }
 
@@ -396,46 +568,26 @@ int gemm_impl(oz2_context* h, bool cplx, char transa, char transb, int64_t m, in
     const int t = scaling_width(*pl, k, cplx);
     if (t < 1) return OZ2_STATUS_RANGE;
     const bool ext = t > kMaxStdT;
-    if (!cplx && small_path(h, m, n, k))
+    if (!cplx && small_path(h, m, n, k)) {
+        h->tile_mb = m;
+        h->tile_nb = n;
+        h->tile_held = OZ2_TILE_UNTILED;
         return small_impl(h, *pl, t, transa, transb, m, n, k, alpha[0], A, lda, 0, B, ldb, 0, beta[0], C,
                           ldc, 0, 1, s);
+    }
 
-    // memory-aware tiling (Arc page Sec. 6, memory-aware tiling): blocks of C
-    // with all of k each, so every block's row and column exponents are the
-    // full ones and the result is bitwise that of the untiled product
+    // memory-aware tiling when the whole product's workspace exceeds the cap
     const Layout full = plan_layout(h, cplx, s, *pl, t, m, n, k);
     size_t cap = 0;
     if (!fits(h, full.total, &cap)) {
-        int64_t T = kPadM;
-        while (T < (m > n ? m : n)) T *= 2;
-        for (; T >= kPadM; T /= 2) {
-            const int64_t mt = m < T ? m : T, nt = n < T ? n : T;
-            if (plan_layout(h, cplx, s, *pl, t, mt, nt, k).total <= cap) break;
-        }
-        if (T < kPadM) return OZ2_STATUS_WORKSPACE_LIMIT;
-        const int64_t mt = m < T ? m : T, nt = n < T ? n : T;
-        const int64_t w = cplx ? 2 : 1;  // doubles per element
-        hipStream_t stm = h->stream;
-        const bool rec = h->timing != 0;
-        if (rec)
-            for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
-        for (int64_t j0 = 0; j0 < n; j0 += nt) {
-            for (int64_t i0 = 0; i0 < m; i0 += mt) {
-                const int64_t mb = m - i0 < mt ? m - i0 : mt, nb = n - j0 < nt ? n - j0 : nt;
-                const double* Ab = A + w * (is_trans(transa) ? i0 * lda : i0);
-                const double* Bb = B + w * (is_trans(transb) ? j0 : j0 * ldb);
-                double* Cb = C + w * (i0 + j0 * ldc);
-                const int st = core(h, cplx, transa, transb, mb, nb, k, alpha, Ab, lda, Bb, ldb, beta, Cb, ldc, s,
-                                    pl, t, ext, false);
-                if (st) return st;
-            }
-        }
-        if (rec) {
-            for (int e = 3; e < 5; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
-            h->timed = true;
-        }
-        return OZ2_STATUS_SUCCESS;
+        TilePlan tp;
+        if (!choose_tiles(h, cplx, s, *pl, t, m, n, k, cap, false, &tp)) return OZ2_STATUS_WORKSPACE_LIMIT;
+        return tiled_impl(h, cplx, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, pl, t, ext,
+                          tp);
     }
+    h->tile_mb = m;
+    h->tile_nb = n;
+    h->tile_held = OZ2_TILE_UNTILED;
     return core(h, cplx, transa, transb, m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, s, pl, t, ext,
                 h->timing != 0);
 }
@@ -525,6 +677,14 @@ int oz2_get_phase_times(oz2_handle_t h, float ms[4]) {
     for (int i = 0; i < 4; ++i)
         if (hipEventElapsedTime(&ms[i], h->ev[i], h->ev[i + 1]) != hipSuccess)
             return OZ2_STATUS_HIP_ERROR;
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_get_tile_plan(oz2_handle_t h, int64_t* mb, int64_t* nb, int* held) {
+    if (!h) return -1;
+    if (mb) *mb = h->tile_mb;
+    if (nb) *nb = h->tile_nb;
+    if (held) *held = h->tile_held;
     return OZ2_STATUS_SUCCESS;
 }
 
@@ -740,19 +900,50 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
     }
     const ModuliPlan* pl = moduli_plan(pa->s);
     if (!pl) return OZ2_STATUS_INTERNAL;
-    Layout L = plan_layout(h, cplx, pa->s, *pl, pa->t, m, n, k, false);
+    const int sm = pa->s;
+    Layout L = plan_layout(h, cplx, sm, *pl, pa->t, m, n, k, false);
     size_t cap = 0;
-    if (!fits(h, L.total, &cap)) return OZ2_STATUS_WORKSPACE_LIMIT;
+    TilePlan tp;
+    tp.mb = m;
+    tp.nb = n;
+    if (!fits(h, L.total, &cap)) {
+        // blocks of C over sub-blocks of the prepared planes: a block's rows
+        // start at a multiple of 256, so they are a run of whole GEMM tiles
+        // inside every k-panel of the operand
+        if (!choose_tiles(h, cplx, sm, *pl, pa->t, m, n, k, cap, true, &tp)) return OZ2_STATUS_WORKSPACE_LIMIT;
+        L = plan_layout(h, cplx, sm, *pl, pa->t, tp.mb < m ? tp.mb : m, tp.nb < n ? tp.nb : n, k, false);
+    }
     int st = ensure_workspace(h, L.total);
     if (st) return st;
+    const int64_t mb = tp.mb < m ? tp.mb : m, nb = tp.nb < n ? tp.nb : n;
+    const int64_t w = cplx ? 2 : 1;
     const bool rec = h->timing != 0;
     if (rec)
         for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], h->stream));
-    st = product(h, cplx, L, pa->planes, pa->amax, pb->planes, pb->amax, al, be, C, ldc, pl, rec);
-    if (st) return st;
-    L.valid = true;
-    h->last = L;
-    h->last_ws = workspace(h);
+    const bool tiled = mb < m || nb < n;
+    for (int64_t j0 = 0; j0 < n; j0 += nb) {
+        const int64_t cols = n - j0 < nb ? n - j0 : nb;
+        for (int64_t i0 = 0; i0 < m; i0 += mb) {
+            const int64_t rows = m - i0 < mb ? m - i0 : mb;
+            Layout Lb = plan_layout(h, cplx, sm, *pl, pa->t, rows, cols, k, false);
+            Lb.off_res = L.off_res;
+            Lb.off_chat = L.off_chat;
+            st = product(h, cplx, Lb, pa->planes + i0 * kPanelK, pa->rows_pad, pa->amax + i0,
+                         pb->planes + j0 * kPanelK, pb->rows_pad, pb->amax + j0, al, be, C + w * (i0 + j0 * ldc), ldc,
+                         pl, rec && !tiled);
+            if (st) return st;
+            Lb.valid = true;
+            h->last = Lb;
+            h->last_ws = workspace(h);
+        }
+    }
+    if (rec && tiled) {
+        for (int e = 3; e < 5; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], h->stream));
+        h->timed = true;
+    }
+    h->tile_mb = mb;
+    h->tile_nb = nb;
+    h->tile_held = tiled ? OZ2_TILE_PREPARED : OZ2_TILE_UNTILED;
     return OZ2_STATUS_SUCCESS;
 }
 

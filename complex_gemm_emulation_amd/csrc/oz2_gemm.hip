@@ -184,7 +184,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     const int boff = BM * kBK + (wn * WTN + fr) * kBK;
     const int row_out0 = tm * BM + wm * WTM + 4 * (lane >> 5);
     const int col_out0 = tn * BN + wn * WTN + fr;
-    const int64_t panelA = P.mp * kBK, panelB = P.np * kBK;  // bytes per k step
+    const int64_t panelA = P.a_rows * kBK, panelB = P.b_rows * kBK;  // bytes per k step
 
     v16i acc[FM][FN];
     v4i fa[2][FM], fb[2][FN];
@@ -194,9 +194,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
 
 #pragma unroll 1
     for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
-        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.mp * kp + (P.k_begin / kBK) * panelA +
+        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.a_rows * kp + (P.k_begin / kBK) * panelA +
                            (int64_t)tm * BM * kBK;
-        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.np * kp + (P.k_begin / kBK) * panelB +
+        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.b_rows * kp + (P.k_begin / kBK) * panelB +
                            (int64_t)tn * BN * kBK;
         auto issue = [&](int kt, int st) {
             const int8_t* Ak = Ag + (int64_t)kt * panelA;
@@ -355,6 +355,7 @@ hipError_t gemm_go(GemmParams P, bool cplx, hipStream_t st) {
 hipError_t launch_residue_gemm(const GemmParams& P, bool cplx, hipStream_t st) {
     if (P.mp % kPadM || P.np % kPadM || P.kp % kPadK || P.k_begin % (kBK * kMaxStages))
         return hipErrorInvalidValue;
+    if (P.a_rows < P.mp || P.b_rows < P.np || P.a_rows % kPadM || P.b_rows % kPadM) return hipErrorInvalidValue;
     if (P.k_steps <= 0 || P.k_steps % kMaxStages || P.k_begin + (int64_t)P.k_steps * kBK > P.kp)
         return hipErrorInvalidValue;
     // 256 x 256 tiles on 8 wavefronts with four stages unless the grid is

@@ -52,10 +52,11 @@ struct EncodeParams {
 };
 
 struct GemmParams {
-    const int8_t* A;   // planes of op(A): [sets][s][mp][kp]
-    const int8_t* B;   // planes of op(B): [sets][s][np][kp]
+    const int8_t* A;   // planes of op(A): [sets][s][kp/64][a_rows][64], from row 0 of this product
+    const int8_t* B;   // planes of op(B): [sets][s][kp/64][b_rows][64], from column 0 of this product
     uint8_t* C;        // [outs][s][n][mp]
-    int64_t mp, np, kp, n;
+    int64_t mp, np, kp, n;     // this product's padded rows, columns and k; n columns of C
+    int64_t a_rows, b_rows;    // rows per k-panel of the planes (>= mp, np; larger for a block of bigger planes)
     int64_t a_set_stride, b_set_stride, c_set_stride;  // bytes
     int s;
     int tiles_m, tiles_n;

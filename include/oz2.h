@@ -85,13 +85,21 @@ int oz2_set_stream(oz2_handle_t h, void* stream);
 
 /* Cap on the workspace in bytes; 0 (the default) means the free device
  * memory reported by hipMemGetInfo at the call.  A product whose workspace
- * would exceed the cap is computed in blocks of C (square, a power-of-two
- * multiple of 256 on a side, each with all of k) one after another: every
+ * would exceed the cap is computed in blocks of C, each with all of k: every
  * block has the full row and column exponents, so the result is bitwise
  * that of the untiled call (the resident-memory hint and memory-aware tiling
- * of Arc page Sec. 6).  OZ2_STATUS_WORKSPACE_LIMIT is returned only when
- * not even a 256 x 256 block fits.  A tiled call reports its whole duration
- * in ms[2] of oz2_get_phase_times, and oz2_debug_copy sees its last block. */
+ * of Arc page Sec. 6).  The blocking is the cheapest one that fits under a
+ * cost model (the shape of Arc page Sec. 9.2): block sides are the whole
+ * dimension or a power-of-two multiple of 256 below it (Table 16's 2^j
+ * tiles), rows and columns chosen separately; the model sums the residue
+ * products of every block (a per-block time measured on this GPU, over
+ * waves of 256 CUs), the scans and encodes, the reconstruction and the
+ * launches.  One operand's encoded block is kept while the other's blocks
+ * go by, so that operand is encoded once in total; the model picks which.
+ * OZ2_STATUS_WORKSPACE_LIMIT is returned only when not even a 256 x 256 block
+ * fits.  A tiled call reports its whole duration in ms[2] of
+ * oz2_get_phase_times, oz2_get_tile_plan reports its blocking, and
+ * oz2_debug_copy sees its last block. */
 int oz2_set_memory_limit(oz2_handle_t h, size_t bytes);
 
 /* Current workspace size in bytes (0 before the first call). */
@@ -106,6 +114,18 @@ int oz2_set_timing(oz2_handle_t h, int enable);
  * path (see oz2_dgemm) reports its single kernel in ms[2] and 0 elsewhere.
  * Synchronizes with the last call. */
 int oz2_get_phase_times(oz2_handle_t h, float ms[4]);
+
+/* Blocking of the last product on this handle (oz2_set_memory_limit):
+ * *mb x *nb entries of C per block (the whole m x n when untiled) and
+ * *held, one of OZ2_TILE_*: which operand's encoded block stayed in the
+ * workspace across the other's blocks.  Any output pointer may be NULL. */
+enum {
+    OZ2_TILE_UNTILED = 0,   /* one block: the whole product */
+    OZ2_TILE_HOLD_A = 1,    /* block rows outer: each op(A) block encoded once */
+    OZ2_TILE_HOLD_B = 2,    /* block columns outer: each op(B) block encoded once */
+    OZ2_TILE_PREPARED = 3   /* oz2_gemm_prepared in blocks of the prepared planes */
+};
+int oz2_get_tile_plan(oz2_handle_t h, int64_t* mb, int64_t* nb, int* held);
 
 /* Default precision policy (Arc page Sec. 9.1): the smallest s in [2, 24]
  * whose scaling width t(s, k) reaches `bits`; 24 when none does. */
@@ -221,9 +241,13 @@ int oz2_operand_destroy(oz2_operand_t op);
  * residue GEMM and reconstruct phases only.  m = rows of pa, n = rows of pb.
  * alpha[2], beta[2]: HOST arrays (re, im); the imaginary parts are ignored
  * for real operands.  C is a DEVICE pointer, ldc >= m.  The workspace holds
- * only the product residues; when it exceeds the memory limit the call
- * returns OZ2_STATUS_WORKSPACE_LIMIT (no tiling on this path).  Phase times:
- * ms[0] = ms[1] = 0.  Argument numbers of the -i codes: h 1, pa 2, pb 3
+ * only the product residues; when they exceed the memory limit, C is
+ * computed in blocks whose residues fit (sides a power-of-two multiple of
+ * 256 or the whole dimension, chosen by the cost model of oz2_set_memory_limit),
+ * each reading its rows and columns of the prepared planes in place: bitwise
+ * the untiled result.  OZ2_STATUS_WORKSPACE_LIMIT only when not even a
+ * 256 x 256 block fits.  Phase times: ms[0] = ms[1] = 0 (a tiled call reports
+ * its whole duration in ms[2]).  Argument numbers of the -i codes: h 1, pa 2, pb 3
  * (also when it does not match pa), alpha 4, beta 5, C 6, ldc 7.
  * oz2_debug_copy of buffers 0-3 after such a call returns
  * OZ2_STATUS_NOT_SUPPORTED (they live in the operand objects). */
