@@ -32,10 +32,19 @@
 // 128 x 128 tile, which instead runs four blocks per CU.  The loads are issued from inline assembly: the
 // compiler cannot tell the stages of an LDS-DMA pipeline apart and would
 // otherwise wait for every load in flight before each LDS read; here the
-// kernel's own vmcnt wait before each step's barrier orders them.  Operand
-// fragments are double buffered in registers and the MFMAs are interleaved
-// one-to-one with the LDS fragment reads of the next 32-wide k sub-step
-// (sched_group_barrier).  LDS rows are 64 bytes of four 16-byte chunks whose
+// kernel's own vmcnt wait before each barrier orders them.
+//
+// The 256 x 256 tile runs a ping-pong schedule.  Its 8 wavefronts form two
+// groups of four, waves 0-3 and 4-7, one wave of each group per SIMD.  Every
+// wave alternates a memory phase (read one k step's fragments from LDS into
+// registers, issue its share of the loads three steps ahead) and a compute
+// phase (that step's 16 MFMAs from registers), with a block barrier between
+// phases; the second group starts one phase late.  So on every SIMD one wave
+// issues MFMAs while the other reads LDS, and no MFMA waits for an LDS read
+// (measured: GEMM 1.3% faster at 8192^3, the 3M ZGEMM at 4096^3 2.5%).  The
+// 128 x 128 tile keeps one schedule for all waves: fragments double buffered
+// in registers, MFMAs interleaved one-to-one with the LDS reads of the next
+// 32-wide k sub-step (sched_group_barrier).  LDS rows are 64 bytes of four 16-byte chunks whose
 // position is XOR-ed with (row/4) mod 4: the LDS serves a 16-byte-per-lane
 // read 16 lanes per clock over 64 banks, and 16 consecutive rows then hit
 // distinct bank groups.  The 256 x 256 tile uses 8 wavefronts (two per SIMD)
@@ -269,6 +278,48 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+        if constexpr (NST == 4) {
+            // ping-pong: waves 0-3 and 4-7 (one of each per SIMD) alternate
+            // every half step between reading a step's fragments (and
+            // issuing the loads three steps ahead) and running that step's
+            // MFMAs from registers; a block barrier separates the phases
+            const int grp = wave_u >> 2;
+            constexpr int kWaitPP = waitcnt_vm(2 * kLoadsPerStep, true);
+            auto mem = [&](int st, int kdma, int st_dma) {
+                rd(st, 0, fa[0], fb[0]);
+                rd(st, 1, fa[1], fb[1]);
+                issue(kdma, st_dma);
+            };
+            auto comp = [&]() {
+                __builtin_amdgcn_s_setprio(1);
+                mm(fa[0], fb[0]);
+                mm(fa[1], fb[1]);
+                __builtin_amdgcn_s_setprio(0);
+            };
+            auto sync = [&]() {
+                __builtin_amdgcn_s_waitcnt(kWaitPP);
+                __syncthreads();
+            };
+#pragma unroll
+            for (int j = 0; j < 3; ++j) issue(j, j);
+            sync();
+            // the second group starts one phase late: it reads step k while
+            // the first runs step k's MFMAs, and runs them while the first
+            // reads step k + 1.  Every wave passes the same number of
+            // barriers: the first group takes its extra one at the end.
+            if (grp == 1) sync();
+#pragma unroll 1
+            for (int kt = 0; kt < nk; kt += 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    mem(j, min(kt + j + 3, nk - 1), (j + 3) & 3);
+                    sync();
+                    comp();
+                    sync();
+                }
+            }
+            if (grp == 0) sync();
+        } else {
 #pragma unroll
         for (int j = 0; j < kStages; ++j) issue(j, j);
         __builtin_amdgcn_s_waitcnt(kWaitFirst);
@@ -280,6 +331,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
             // per step keeps the vmcnt arithmetic exact)
 #pragma unroll
             for (int j = 0; j < kStages; ++j) kstep(j, min(kt + j + kStages, nk - 1));
+        }
         }
         // no LDS DMA may be in flight when the stages are reused or released
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, false));

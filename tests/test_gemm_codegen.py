@@ -68,16 +68,39 @@ def test_main_loop_keeps_loads_in_flight(gemm_asm):
     for name, lines in kernels.items():
         bm, bn, wm, wn, nst = _template_args(name)
         loads = (bm + bn) * 4 // (64 * wm * wn)  # 1 KiB loads per wave and step
-        # the wait before every barrier: the prologue's NST steps of loads
-        # less the first step, then in each of the NST unrolled k steps of the
-        # main loop the loads of NST - 2 later steps still in flight, then one
-        # full drain before the epilogue
         before_barrier = [lines[i - 1] for i, l in enumerate(lines) if l == "s_barrier"]
         counts = [int(m.group(1)) for w in before_barrier for m in [re.search(r"vmcnt\((\d+)\)", w)] if m]
-        loop = (nst - 2) * loads
-        first = (nst - 1) * loads
-        assert counts.count(first) == 1, (name, counts)
-        if loop:
-            assert counts.count(loop) == nst and counts.count(0) == 1, (name, counts)
+        assert len(counts) == len(before_barrier), (name, before_barrier)
+        if nst == 4:
+            # ping-pong: loads are issued three steps ahead, so every barrier
+            # (prologue, the staggering ones, 2 per unrolled step) waits with
+            # the loads of two later steps in flight; one drain before the epilogue
+            assert counts.count(0) == 1 and counts.count(2 * loads) == len(counts) - 1, (name, counts)
+            assert len(counts) == 1 + 2 + 2 * 4 + 1, (name, counts)
         else:
+            # the prologue's NST steps of loads less the first step, then in
+            # each of the NST unrolled k steps the loads of NST - 2 later
+            # steps in flight (none for two stages), then one full drain
+            first = (nst - 1) * loads
+            assert counts.count(first) == 1, (name, counts)
             assert counts.count(0) == nst + 1, (name, counts)
+
+
+def test_ping_pong_phases(gemm_asm):
+    # in the main loop of the 256 x 256 tile, consecutive barriers enclose
+    # either a memory phase (LDS fragment reads and loads, no MFMA) or a
+    # compute phase (the step's 16 MFMAs, no LDS read)
+    for name, lines in _kernels(gemm_asm).items():
+        if _template_args(name)[4] != 4:
+            continue
+        bars = [i for i, l in enumerate(lines) if l == "s_barrier"]
+        phases = []
+        for a, b in zip(bars, bars[1:]):
+            seg = lines[a + 1:b]
+            mf = sum(l.startswith("v_mfma") for l in seg)
+            rd = sum(l.startswith("ds_read") for l in seg)
+            if mf or rd:
+                phases.append((mf, rd))
+        loop = [p for p in phases if p in ((16, 0), (0, 12))]
+        assert len(loop) >= 8, (name, phases)
+        assert all(p in ((16, 0), (0, 12)) for p in phases if p[0] == 16 or p[1] == 12), (name, phases)
