@@ -27,6 +27,8 @@ Other workloads (--workload), each printing the same kind of JSON line:
   tiled8192  the headline product under a 1 GiB workspace cap: memory-aware
              tiling in blocks of C; reports each s's blocking and the
              slowdown against the same calls untiled
+  datapower  the headline product at s = 16 on zero, constant, random-integer
+             and headline operands: the residue GEMM's rate by operand data
 
 Printed: ONE JSON line with the metric, per-call phase times (HIP events
 recorded on the stream the kernels run on), the median and best step, the
@@ -885,6 +887,55 @@ def run_chain(args):
     }
 
 
+def run_datapower(args):
+    """The headline product at s = 16 on four operand data sets with the
+    same shapes and hence the same kernels, loads and instruction streams:
+    all zeros, one constant, random integers and the headline's data.  The
+    residue bytes are then all zero, constant per modulus, or random; the
+    GEMM phase times (HIP events on the stream) show how much of the
+    residue GEMM's rate depends on its operand data."""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+    n, s = 8192, 16
+    h = oz2.Handle(torch.cuda.current_stream())
+    h.set_timing(True)
+    dC = torch.zeros(n * n, dtype=torch.float64, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(workloads.seed(2, 7))
+    cases = [("zeros", torch.zeros(n * n, dtype=torch.float64, device="cuda")),
+             ("constant 0.75", torch.full((n * n,), 0.75, dtype=torch.float64, device="cuda")),
+             ("integers in [-2^15, 2^15)",
+              torch.randint(-2 ** 15, 2 ** 15, (n * n,), device="cuda", generator=gen).double()),
+             ("headline (u - 1/2) exp(0.5 g)",
+              torch.from_numpy(workloads.real_matrix(n, n, workloads.seed(2, 0), "phi", 0.5)).cuda())]
+    out = {}
+    t_all = time.perf_counter()
+    for name, X in cases:
+        log(f"[bench] datapower: {name}")
+        for _ in range(args.warmup):
+            h.dgemm("N", "N", n, n, n, 1.0, X, n, X, n, 0.0, dC, n, s)
+        torch.cuda.synchronize()
+        g = []
+        for _ in range(args.steps):
+            h.dgemm("N", "N", n, n, n, 1.0, X, n, X, n, 0.0, dC, n, s)
+            g.append(h.phase_times()[2])
+        ms = float(np.median(g))
+        out[name] = dict(gemm_ms=round(ms, 4), int8_tops=round(2.0 * n ** 3 * s / (ms * 1e-3) / 1e12, 1),
+                         frac_of_peak=round(2.0 * n ** 3 * s / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4))
+    dt = time.perf_counter() - t_all
+    h.close()
+    head = out[cases[-1][0]]
+    return {
+        "metric": "residue GEMM INT8 TOP/s on the headline product at s = 16, by operand data",
+        "value": head["int8_tops"],
+        "unit": "TOP/s",
+        "ms_per_step": round(dt / (len(cases) * (args.steps + args.warmup)) * 1e3, 3),
+        "dtype": "i8",
+        "config": {"workload": "dgemm_8192_NN_s16_operand_data", "m": n, "n": n, "k": n, "s": s},
+        "per_data": out,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -892,7 +943,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
                     choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "nonsquare",
-                             "reuse8192", "tiled8192"])
+                             "reuse8192", "tiled8192", "datapower"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)
@@ -919,13 +970,15 @@ def main():
         out = run_chain_rbe(args)
     elif args.workload == "nonsquare":
         out = run_nonsquare(args)
+    elif args.workload == "datapower":
+        out = run_datapower(args)
     else:
         out = run_gemm(args, args.workload)
     line = {"metric": out["metric"], "value": out["value"], "unit": out["unit"], "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": out["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": out["dtype"],
             "data": "synthetic", "config": out["config"]}
-    for key in ("step_ms", "per_s", "per_shape", "hbm_ceiling", "tiling", "accuracy", "parity_sample",
+    for key in ("step_ms", "per_s", "per_shape", "per_data", "hbm_ceiling", "tiling", "accuracy", "parity_sample",
                 "roofline", "cpu_baseline"):
         if key in out:
             line[key] = out[key]
