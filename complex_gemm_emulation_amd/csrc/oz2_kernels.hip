@@ -38,8 +38,20 @@ __global__ void fill_u64_kernel(uint64_t* p, int64_t n, uint64_t v) {
 }
 
 // ------------------------------------------------------------------ scan
-// One wavefront per vector whose elements are contiguous.
-template <bool CPLX>
+// |x| as the bit pattern of a double (monotone in |x|, Inf < NaN) of both
+// halves of a 16-byte pair
+__device__ __forceinline__ uint64_t abs_bits2(double2 v) { return max(abs_bits(v.x), abs_bits(v.y)); }
+
+typedef double nd2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ double2 load_stream(const double2* p) {
+    const nd2 v = __builtin_nontemporal_load((const nd2*)p);
+    return double2(v.x, v.y);
+}
+
+// One wavefront per vector whose elements are contiguous.  VEC: the vector
+// starts 16-byte aligned (wave-uniform: the host checks the base and the
+// leading dimension), so lanes read 16-byte pairs, four in flight each.
+template <bool CPLX, bool VEC>
 __global__ __launch_bounds__(256) void scan_contig_kernel(ScanParams P) {
     const int lane = threadIdx.x & 63;
     const int64_t v = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -48,14 +60,30 @@ __global__ __launch_bounds__(256) void scan_contig_kernel(ScanParams P) {
     const int64_t len = P.k * W;
     const double* x = P.X + v * P.ld * W;
     uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
-    int64_t p = lane;
-    for (; p + 192 < len; p += 256) {
-        m0 = max(m0, abs_bits(x[p]));
-        m1 = max(m1, abs_bits(x[p + 64]));
-        m2 = max(m2, abs_bits(x[p + 128]));
-        m3 = max(m3, abs_bits(x[p + 192]));
+    if (VEC) {
+        const double2* x2 = (const double2*)x;
+        const int64_t len2 = len >> 1;
+        int64_t p = lane;
+        for (; p + 192 < len2; p += 256) {
+            const double2 a = load_stream(x2 + p), b = load_stream(x2 + p + 64);
+            const double2 c = load_stream(x2 + p + 128), d = load_stream(x2 + p + 192);
+            m0 = max(m0, abs_bits2(a));
+            m1 = max(m1, abs_bits2(b));
+            m2 = max(m2, abs_bits2(c));
+            m3 = max(m3, abs_bits2(d));
+        }
+        for (; p < len2; p += 64) m0 = max(m0, abs_bits2(load_stream(x2 + p)));
+        if ((len & 1) && lane == 0) m1 = max(m1, abs_bits(x[len - 1]));
+    } else {
+        int64_t p = lane;
+        for (; p + 192 < len; p += 256) {
+            m0 = max(m0, abs_bits(x[p]));
+            m1 = max(m1, abs_bits(x[p + 64]));
+            m2 = max(m2, abs_bits(x[p + 128]));
+            m3 = max(m3, abs_bits(x[p + 192]));
+        }
+        for (; p < len; p += 64) m0 = max(m0, abs_bits(x[p]));
     }
-    for (; p < len; p += 64) m0 = max(m0, abs_bits(x[p]));
     unsigned long long mx = max(max(m0, m1), max(m2, m3));
     for (int off = 32; off >= 1; off >>= 1) {
         unsigned long long o = __shfl_xor(mx, off);
@@ -64,25 +92,61 @@ __global__ __launch_bounds__(256) void scan_contig_kernel(ScanParams P) {
     if (lane == 0) P.amax[v] = mx;
 }
 
-// One thread per vector whose elements are strided (a wavefront reads 64
-// consecutive vectors at one p, coalesced); the p range is split across
-// blocks and combined with an atomic max on the zero-filled output.
-template <bool CPLX>
+// Vectors whose elements are strided: a wavefront reads consecutive vectors
+// at one position p, coalesced.  Real data with an even leading dimension
+// and a 16-byte aligned base (VEC) gives each thread two neighbouring
+// vectors as one 16-byte pair; otherwise one vector (complex: one 16-byte
+// element).  The p range is split across blocks and combined with an atomic
+// max on the zero-filled output; four positions are loaded per trip.
+template <bool CPLX, bool VEC>
 __global__ __launch_bounds__(256) void scan_strided_kernel(ScanParams P) {
-    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    constexpr int VPT = (VEC && !CPLX) ? 2 : 1;  // vectors per thread
+    const int64_t v = ((int64_t)blockIdx.x * 256 + threadIdx.x) * VPT;
     if (v >= P.nvec) return;
     const int64_t p0 = (int64_t)blockIdx.y * P.pchunk;
     const int64_t p1 = min(P.k, p0 + P.pchunk);
-    uint64_t mx = 0;
-    for (int64_t p = p0; p < p1; ++p) {
-        if (CPLX) {
+    uint64_t mx = 0, my = 0;
+    if (CPLX && VEC) {
+        // one complex element per load: 16 bytes, aligned with the base
+        const double2* z = (const double2*)P.X + v;
+        int64_t p = p0;
+        for (; p + 3 < p1; p += 4) {
+            const double2 a = z[p * P.ld], b = z[(p + 1) * P.ld], c = z[(p + 2) * P.ld], d = z[(p + 3) * P.ld];
+            mx = max(mx, max(max(abs_bits2(a), abs_bits2(b)), max(abs_bits2(c), abs_bits2(d))));
+        }
+        for (; p < p1; ++p) mx = max(mx, abs_bits2(z[p * P.ld]));
+    } else if (CPLX) {
+        for (int64_t p = p0; p < p1; ++p) {
             const double* z = P.X + 2 * (v + p * P.ld);
             mx = max(mx, max(abs_bits(z[0]), abs_bits(z[1])));
-        } else {
-            mx = max(mx, abs_bits(P.X[v + p * P.ld]));
         }
+    } else if (VEC) {
+        // v is even, ld even and the base 16-byte aligned: X + v + p ld is too
+        const double* x = P.X + v;
+        int64_t p = p0;
+        for (; p + 3 < p1; p += 4) {
+            const double2 a = load_stream((const double2*)(x + p * P.ld));
+            const double2 b = load_stream((const double2*)(x + (p + 1) * P.ld));
+            const double2 c = load_stream((const double2*)(x + (p + 2) * P.ld));
+            const double2 d = load_stream((const double2*)(x + (p + 3) * P.ld));
+            mx = max(mx, max(max(abs_bits(a.x), abs_bits(b.x)), max(abs_bits(c.x), abs_bits(d.x))));
+            my = max(my, max(max(abs_bits(a.y), abs_bits(b.y)), max(abs_bits(c.y), abs_bits(d.y))));
+        }
+        for (; p < p1; ++p) {
+            const double2 a = load_stream((const double2*)(x + p * P.ld));
+            mx = max(mx, abs_bits(a.x));
+            my = max(my, abs_bits(a.y));
+        }
+    } else {
+        const double* x = P.X + v;
+        int64_t p = p0;
+        for (; p + 3 < p1; p += 4)
+            mx = max(mx, max(max(abs_bits(x[p * P.ld]), abs_bits(x[(p + 1) * P.ld])),
+                             max(abs_bits(x[(p + 2) * P.ld]), abs_bits(x[(p + 3) * P.ld]))));
+        for (; p < p1; ++p) mx = max(mx, abs_bits(x[p * P.ld]));
     }
     if (mx) atomicMax((unsigned long long*)&P.amax[v], (unsigned long long)mx);
+    if (VEC && !CPLX && my && v + 1 < P.nvec) atomicMax((unsigned long long*)&P.amax[v + 1], (unsigned long long)my);
 }
 
 // ---------------------------------------------------------------- encode
@@ -431,18 +495,31 @@ hipError_t launch_fill_u64(uint64_t* p, int64_t n, uint64_t value, hipStream_t s
 
 hipError_t launch_scan(const ScanParams& P, bool contiguous, bool cplx, hipStream_t st) {
     if (P.nvec <= 0 || P.k <= 0) return hipSuccess;
+    const bool aligned = ((uintptr_t)P.X & 15) == 0;
     if (contiguous) {
+        // 16-byte pairs when every vector starts 16-byte aligned
+        const bool vec = aligned && (cplx || (P.ld & 1) == 0);
         dim3 grid((unsigned)blocks_for(P.nvec, 4));
-        if (cplx)
-            hipLaunchKernelGGL(scan_contig_kernel<true>, grid, dim3(256), 0, st, P);
+        if (cplx && vec)
+            hipLaunchKernelGGL((scan_contig_kernel<true, true>), grid, dim3(256), 0, st, P);
+        else if (cplx)
+            hipLaunchKernelGGL((scan_contig_kernel<true, false>), grid, dim3(256), 0, st, P);
+        else if (vec)
+            hipLaunchKernelGGL((scan_contig_kernel<false, true>), grid, dim3(256), 0, st, P);
         else
-            hipLaunchKernelGGL(scan_contig_kernel<false>, grid, dim3(256), 0, st, P);
+            hipLaunchKernelGGL((scan_contig_kernel<false, false>), grid, dim3(256), 0, st, P);
     } else {
-        dim3 grid((unsigned)blocks_for(P.nvec, 256), (unsigned)blocks_for(P.k, P.pchunk));
-        if (cplx)
-            hipLaunchKernelGGL(scan_strided_kernel<true>, grid, dim3(256), 0, st, P);
+        const bool vec = aligned && (cplx || (P.ld & 1) == 0);
+        const int64_t per_block = (vec && !cplx) ? 512 : 256;
+        dim3 grid((unsigned)blocks_for(P.nvec, per_block), (unsigned)blocks_for(P.k, P.pchunk));
+        if (cplx && vec)
+            hipLaunchKernelGGL((scan_strided_kernel<true, true>), grid, dim3(256), 0, st, P);
+        else if (cplx)
+            hipLaunchKernelGGL((scan_strided_kernel<true, false>), grid, dim3(256), 0, st, P);
+        else if (vec)
+            hipLaunchKernelGGL((scan_strided_kernel<false, true>), grid, dim3(256), 0, st, P);
         else
-            hipLaunchKernelGGL(scan_strided_kernel<false>, grid, dim3(256), 0, st, P);
+            hipLaunchKernelGGL((scan_strided_kernel<false, false>), grid, dim3(256), 0, st, P);
     }
     return hipGetLastError();
 }

@@ -229,3 +229,51 @@ def test_c_base_only_8_byte_aligned(handle, m, n, k, ldc):
     want = oracle.gemm_entries(False, "N", "N", m, n, k, -0.5, A, m, B, k, 1.25, C, ldc, 12)["out"]
     check_float_parity(full[:, :m].T, want.reshape(n, m).T, f"C+8 {m}x{n}x{k} ldc={ldc}")
     assert np.array_equal(full[:, m:], C.reshape(n, ldc)[:, m:])
+
+
+@pytest.mark.parametrize("cplx", [False, True])
+@pytest.mark.parametrize("ta,tb", [("N", "N"), ("T", "T")])
+def test_operands_only_8_byte_aligned(handle, cplx, ta, tb):
+    # A and B starting one double into their allocations (and even leading
+    # dimensions): the scan's 16-byte-pair paths must not be taken, and the
+    # results must match the oracle
+    import torch
+    m, n, k, s = 300, 260, 200, 16
+    ra, ca = workloads.stored_shape(ta, m, k)
+    rb, cb = workloads.stored_shape(tb, k, n)
+    rng = np.random.default_rng(9 + 2 * int(cplx) + (ta == "T"))
+    sd = [int(x) for x in rng.integers(1 << 30, size=4)]
+    if cplx:
+        A = workloads.complex_matrix(ra, ca, sd[0], sd[1], "phi", 1.0)
+        B = workloads.complex_matrix(rb, cb, sd[2], sd[3], "phi", 1.0)
+    else:
+        A = workloads.real_matrix(ra, ca, sd[0], "phi", 1.0)
+        B = workloads.real_matrix(rb, cb, sd[2], "phi", 1.0)
+    _say(f"[dgemm] operands +8 bytes cplx={cplx} {ta}{tb}")
+    if cplx:
+        # complex operands from the raw C ABI with 8-byte-offset pointers
+        import ctypes
+        import complex_gemm_emulation_amd as oz2
+        bufA = to_dev(np.concatenate([[0.0], A.view(np.float64)]))
+        bufB = to_dev(np.concatenate([[0.0], B.view(np.float64)]))
+        dC = torch.zeros(m * n, dtype=torch.complex128, device="cuda")
+        al = (ctypes.c_double * 2)(1.0, 0.0)
+        be = (ctypes.c_double * 2)(0.0, 0.0)
+        handle._bind_stream()
+        st = oz2.lib().oz2_zgemm(handle._h, ta.encode(), tb.encode(), m, n, k, al,
+                                 ctypes.c_void_p(bufA.data_ptr() + 8), ra, ctypes.c_void_p(bufB.data_ptr() + 8), rb,
+                                 be, ctypes.c_void_p(dC.data_ptr()), m, s)
+        assert st == 0
+        torch.cuda.synchronize()
+        got = from_dev(dC)
+    else:
+        bufA = to_dev(np.concatenate([[0.0], A]))
+        bufB = to_dev(np.concatenate([[0.0], B]))
+        dC = to_dev(np.zeros(m * n))
+        dA, dB = bufA[1:], bufB[1:]
+        assert dA.data_ptr() % 16 == 8 and dB.data_ptr() % 16 == 8
+        handle.dgemm(ta, tb, m, n, k, 1.0, dA, ra, dB, rb, 0.0, dC, m, s)
+        torch.cuda.synchronize()
+        got = from_dev(dC)
+    want = oracle.gemm_entries(cplx, ta, tb, m, n, k, 1.0, A, ra, B, rb, 0.0, None, m, s, chat_ints=False)["out"]
+    assert check_float_parity(got, want, "operands +8 bytes") == 0
