@@ -29,6 +29,11 @@ Other workloads (--workload), each printing the same kind of JSON line:
              slowdown against the same calls untiled
   datapower  the headline product at s = 16 on zero, constant, random-integer
              and headline operands: the residue GEMM's rate by operand data
+  accuracy   the Arc page's accuracy protocol (Tables 6 and 8): 512 x 512 x
+             4096 products of U(-1,1), phi = 2, sin/cos, spike, cancellation
+             and 1 - 2^-53 data at s = 16, 20, 24; max ulp, correctly rounded
+             share, componentwise and normwise error on 256 sampled entries
+             against the exact products
 
 Printed: ONE JSON line with the metric, per-call phase times (HIP events
 recorded on the stream the kernels run on), the median and best step, the
@@ -285,6 +290,108 @@ def exact_dot_fraction(a, b):
     for x, y, z in zip(qa.tolist(), qb.tolist(), (e - e0).tolist()):
         tot += (x * y) << z
     return Fraction(tot) * (Fraction(2) ** e0)
+
+
+def entry_accuracy(got, Am, Bm, rows, cols):
+    """Accuracy of computed entries against the exact products (Arc page
+    Sec. 7: maximum error in ulps of the exact result, the share of correctly
+    rounded entries, the componentwise error |c~ - c| / (|A||B|)_ij and the
+    normwise relative error).  Am[i] is row i of op(A), Bm[j] column j of
+    op(B) (real); got[q] the computed entry (rows[q], cols[q])."""
+    from fractions import Fraction
+    max_ulp = comp = 0.0
+    cr = 0
+    num = den = Fraction(0)
+    for q, (i, j) in enumerate(zip(rows, cols)):
+        a, b = Am[i], Bm[j]
+        ex = exact_dot_fraction(a, b)
+        g = float(got[q])
+        rn = float(ex) if ex != 0 else 0.0   # CPython rounds a Fraction once, to nearest even
+        cr += int(g == rn)
+        err = abs(Fraction(g) - ex)
+        if rn != 0.0:
+            ulp = Fraction(2) ** (int(np.frexp(rn)[1]) - 53)
+            max_ulp = max(max_ulp, float(err / ulp))
+        elif err != 0:
+            max_ulp = float("inf")
+        aabb = float(np.dot(np.abs(a), np.abs(b)))
+        if aabb > 0:
+            comp = max(comp, float(err) / aabb)
+        num += err * err
+        den += ex * ex
+    normwise = float((num / den) ** 0.5) if den != 0 else 0.0
+    return dict(max_ulp=max_ulp, cr_pct=100.0 * cr / len(rows), componentwise=comp, normwise=normwise)
+
+
+ACCURACY_DATA = ("uniform", "phi2", "sincos", "spike", "cancel", "one_minus_ulp")
+
+
+def accuracy_operands(data, m, n, k, seed_base):
+    """op(A) (m x k) and op(B) (k x n), N/N column-major, of one data family
+    of the Arc page's Sec. 7 and Sec. 8.3"""
+    import workloads
+    if data == "uniform":
+        return workloads.real_matrix(m, k, seed_base), workloads.real_matrix(k, n, seed_base + 1)
+    if data == "phi2":
+        return (workloads.real_matrix(m, k, seed_base, "phi", 2.0),
+                workloads.real_matrix(k, n, seed_base + 1, "phi", 2.0))
+    if data == "sincos":
+        return workloads.sincos_matrix(m, k, seed_base), workloads.sincos_matrix(k, n, seed_base + 1)
+    if data == "spike":
+        # one element per row of A 2^40 times larger than the rest
+        return workloads.spike_matrix(m, k, seed_base), workloads.real_matrix(k, n, seed_base + 1)
+    if data == "cancel":
+        return workloads.cancel_pair(m, n, k, seed_base)
+    if data == "one_minus_ulp":
+        return np.full(m * k, 1.0 - 2.0 ** -53), np.full(k * n, 1.0 - 2.0 ** -53)
+    raise ValueError(data)
+
+
+def run_accuracy(args):
+    """The accuracy protocol of the Arc page (Sec. 7, Sec. 8.2-8.3, Tables 6
+    and 8) on this GPU: 512 x 512 x 4096 DGEMM (N/N) for each data family at
+    s = 16, 20, 24, the entries of a seeded 16 x 16 sample of rows and
+    columns (256 entries, first and last included) compared with the exact
+    products."""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+    m = n = 512
+    k = 4096
+    side = 16
+    rng = np.random.default_rng(777)
+    ri = np.unique(np.concatenate([[0, m - 1], rng.choice(m, side, replace=False)]))[:side]
+    cj = np.unique(np.concatenate([[0, n - 1], rng.choice(n, side, replace=False)]))[:side]
+    rows, cols = (x.reshape(-1) for x in np.meshgrid(ri, cj, indexing="ij"))
+    h = oz2.Handle(torch.cuda.current_stream())
+    table = {}
+    t0 = time.perf_counter()
+    for q, data in enumerate(ACCURACY_DATA):
+        A, B = accuracy_operands(data, m, n, k, workloads.seed(8, 10 * q))
+        dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+        dC = torch.zeros(m * n, dtype=torch.float64, device="cuda")
+        Am, Bm = A.reshape(k, m).T, B.reshape(n, k)
+        for s in (16, 20, 24):
+            log(f"[bench] accuracy: {data}, s = {s}")
+            h.dgemm("N", "N", m, n, k, 1.0, dA, m, dB, k, 0.0, dC, m, s)
+            torch.cuda.synchronize()
+            got = dC.cpu().numpy()[rows + cols * m]
+            st = entry_accuracy(got, Am, Bm, rows, cols)
+            st["t"] = oz2.plan_info(s, k)["t"]
+            table[f"{data} s={s}"] = {key: (round(v, 4) if key == "cr_pct" else (float(f"{v:.3g}") if isinstance(v, float) else v))
+                                      for key, v in st.items()}
+    h.close()
+    dt = time.perf_counter() - t0
+    return {
+        "metric": "accuracy of emulated DGEMM against exact products (512 x 512 x 4096, 256 sampled entries)",
+        "value": table["uniform s=16"]["cr_pct"],
+        "unit": "% correctly rounded (U(-1,1), s = 16)",
+        "ms_per_step": round(dt * 1e3, 1),
+        "dtype": "i8",
+        "config": {"workload": "dgemm_512_512_4096_accuracy", "m": m, "n": n, "k": k, "s": [16, 20, 24],
+                   "data": list(ACCURACY_DATA), "sample": f"{side} x {side} rows x columns"},
+        "per_data": table,
+    }
 
 
 def general_accuracy(h, spec, A, B, C, s, count=32, seed=4242):
@@ -943,7 +1050,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
                     choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "nonsquare",
-                             "reuse8192", "tiled8192", "datapower"])
+                             "reuse8192", "tiled8192", "datapower", "accuracy"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)
@@ -972,6 +1079,8 @@ def main():
         out = run_nonsquare(args)
     elif args.workload == "datapower":
         out = run_datapower(args)
+    elif args.workload == "accuracy":
+        out = run_accuracy(args)
     else:
         out = run_gemm(args, args.workload)
     line = {"metric": out["metric"], "value": out["value"], "unit": out["unit"], "n_gpus": 1,

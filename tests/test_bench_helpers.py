@@ -102,3 +102,42 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_entry_accuracy_statistics():
+    # correctly rounded entries give 100% and at most half an ulp; an entry
+    # moved by one ulp counts as not correctly rounded with an error near 1 ulp
+    rng = np.random.default_rng(71)
+    k, m, n = 40, 3, 4
+    Am = rng.uniform(-1, 1, (m, k))
+    Bm = rng.uniform(-1, 1, (n, k))
+    rows = np.array([0, 1, 2, 0])
+    cols = np.array([0, 1, 2, 3])
+    exact = [bench.exact_dot_fraction(Am[i], Bm[j]) for i, j in zip(rows, cols)]
+    good = np.array([float(x) for x in exact])
+    st = bench.entry_accuracy(good, Am, Bm, rows, cols)
+    assert st["cr_pct"] == 100.0 and st["max_ulp"] <= 0.5
+    assert st["normwise"] < 2.0 ** -52
+    bad = good.copy()
+    bad[2] = np.nextafter(bad[2], np.inf)
+    st2 = bench.entry_accuracy(bad, Am, Bm, rows, cols)
+    assert st2["cr_pct"] == 75.0 and 0.5 < st2["max_ulp"] <= 1.5
+    aabb = float(np.abs(Am[2]) @ np.abs(Bm[2]))
+    assert st2["componentwise"] == pytest.approx(float(abs(Fraction(bad[2]) - exact[2])) / aabb)
+
+
+def test_accuracy_operands_shapes_and_structure():
+    m, n, k = 8, 6, 10
+    for data in bench.ACCURACY_DATA:
+        A, B = bench.accuracy_operands(data, m, n, k, 123)
+        assert A.size == m * k and B.size == k * n, data
+    A, _ = bench.accuracy_operands("spike", m, n, k, 5)
+    Am = A.reshape(k, m).T
+    for i in range(m):  # one element per row of A is 2^40 times the scale of the others
+        big = np.abs(Am[i]) > 2.0 ** 20
+        assert big.sum() == 1
+    A, B = bench.accuracy_operands("cancel", m, n, k, 6)
+    Am, Bm = A.reshape(k, m).T, B.reshape(n, k).T
+    assert np.array_equal(Am[:, : k // 2], Am[:, k // 2:])
+    C = Am @ Bm
+    assert np.max(np.abs(C)) < 2.0 ** -25 * np.max(np.abs(Am) @ np.abs(Bm))

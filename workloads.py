@@ -115,6 +115,20 @@ def spike_matrix(rows: int, cols: int, seed_value: int, factor_log2: int = 40) -
     return np.ascontiguousarray(a.reshape(-1))
 
 
+def cancel_pair(m: int, n: int, k: int, seed_value: int) -> tuple[np.ndarray, np.ndarray]:
+    """A = [X X] (m x k) and B = [Y; -Y + 2^-30 Z] (k x n), X, Y, Z from
+    U(-1, 1), k even: C = X (2^-30 Z) is about 2^-30 |A||B| (Arc page
+    Sec. 8.3, cancellation).  Column-major flat arrays."""
+    rng = np.random.default_rng(seed_value)
+    h = k // 2
+    X = rng.uniform(-1.0, 1.0, (m, h))
+    Y = rng.uniform(-1.0, 1.0, (h, n))
+    Z = rng.uniform(-1.0, 1.0, (h, n))
+    A = np.concatenate([X, X], axis=1)
+    B = np.concatenate([Y, -Y + 2.0 ** -30 * Z], axis=0)
+    return A.reshape(-1, order="F"), B.reshape(-1, order="F")
+
+
 def tensor_batch(n: int, batch: int, seed_value: int) -> np.ndarray:
     """batch independent n x n x n tensors, column-major X[i + n j + n^2 k + n^3 b]."""
     rng = np.random.default_rng(seed_value)
