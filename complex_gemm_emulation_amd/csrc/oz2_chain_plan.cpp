@@ -11,9 +11,12 @@
 //    exponents then replace them (operator i acts on direction i mod 3);
 //  - Sec. 4.3 Eq. (21): rho_i = maximal absolute row sum of the integer
 //    operator;
-//  - Algorithm 2 (DropPlan) with restoration, Algorithm 3 (Planner): the
-//    largest b <= 53 whose greedy schedule passes every range check, with
-//    exact wide-integer bounds;
+//  - Sec. 4.3 Eq. (22)-(23), the drop schedule and the choice of b: the
+//    bound B starts at 2^b and is multiplied by rho_i per product under
+//    2 B < P; after a non-final product the smallest moduli leave while
+//    floor(B/q) keeps b bits, each leaving floor(B/q) + 1 under
+//    2 B' < P_L / q; b is the largest value <= 53 whose schedule passes
+//    (exact wide-integer bounds throughout);
 //  - Sec. 2.3 Eq. (11): centred residues, [v]_p in [-floor(p/2), ceil(p/2) - 1];
 //  - Sec. 4.4 Eq. (24)-(26): mixed-radix weights omega_{i,p} = [prod_{l<i} m_l]_p.
 // The basis is the max-product modulus set of the DGEMM emulation for s,
@@ -99,35 +102,45 @@ uint64_t row_sum_bound(const int64_t* Abar, int n) {
     return rho;
 }
 
-// DropPlan with restoration (tau = 1) over d products; false on a failed
-// range check
-bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* g) {
-    UBig PL = UBig::from_u64(1);
-    for (int i = 0; i < s; ++i) PL.mul_small((uint32_t)basis[i]);
-    const UBig P = PL;
+// The rescaling after a non-final product (the chain page, Sec. 4.3 around
+// Eq. 23).  B bounds the product's entries; the moduli leave smallest first
+// (the basis is descending, so from its end) while floor(B/q) keeps b bits
+// and more than one modulus would remain, each leaving floor(B/q) + 1 (one
+// unit for the rounding of the division), which must stay recoverable on
+// the moduli left, 2 B' < P_L / q.  Sets *removed and B; false when a
+// removal breaks that condition.
+bool greedy_rescale(UBig& B, int b, const int* basis, int s, const UBig& P, int* removed) {
     const UBig two_b = pow2(b);
-    UBig B = two_b;
-    int nL = s;
+    UBig P_left = P;
+    int left = s;
+    *removed = 0;
+    while (left > 1) {
+        const uint32_t q = (uint32_t)basis[left - 1];
+        const UBig quot = B.div_small(q);
+        if (quot.cmp(two_b) < 0) break;
+        B = add(quot, UBig::from_u64(1));
+        P_left = P_left.div_small(q);
+        if (B.shl(1).cmp(P_left) >= 0) return false;
+        --left;
+        ++*removed;
+    }
+    return true;
+}
+
+// Drop counts of a chain with row-sum bounds rho (Sec. 4.3, Eq. 21-23): the
+// bound starts at 2^b and each product multiplies it by its rho (Eq. 22),
+// keeping 2 B < P; after every product but the last, greedy_rescale, then
+// base extension restores the whole basis for the next product (the
+// proposed method's restoration).  The last product is decoded directly.
+bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* g) {
+    UBig P = UBig::from_u64(1);
+    for (int i = 0; i < s; ++i) P.mul_small((uint32_t)basis[i]);
+    UBig B = pow2(b);
     for (int i = 0; i < d; ++i) {
         B = mul_u64(B, rho[i]);
-        if (B.shl(1).cmp(PL) >= 0) return false;
+        if (B.shl(1).cmp(P) >= 0) return false;
         g[i] = 0;
-        if (i < d - 1) {
-            while (nL > 1) {
-                const uint32_t q = (uint32_t)basis[nL - 1];  // smallest available modulus
-                const UBig Bq0 = B.div_small(q);
-                if (Bq0.cmp(two_b) < 0) break;
-                const UBig Bq = add(Bq0, UBig::from_u64(1));
-                const UBig PLq = PL.div_small(q);
-                if (Bq.shl(1).cmp(PLq) >= 0) return false;
-                PL = PLq;
-                B = Bq;
-                --nL;
-                ++g[i];
-            }
-            PL = P;
-            nL = s;
-        }
+        if (i < d - 1 && !greedy_rescale(B, b, basis, s, P, &g[i])) return false;
     }
     return true;
 }
@@ -147,19 +160,22 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
     int64_t Abar[kChainMaxD][kChainN * kChainN];
     int f[kChainMaxD][kChainN];
     int pend[3][kChainN];
-    int b = 53, g[kChainMaxD] = {};
-    for (; b >= 1; --b) {
+    int g[kChainMaxD] = {};
+    // the effective integer operators at b (the pending scales of a direction
+    // folded into the next operator on it) and whether their schedule passes;
+    // encoding depends on b, so the bounds are taken afresh for every b
+    auto passes = [&](int b) {
         uint64_t rho[kChainMaxD];
         std::memset(pend, 0, sizeof(pend));
-        bool ok = true;
-        for (int i = 0; i < d && ok; ++i) {
-            // the effective operator: pending scales of its direction folded in
-            ok = encode_rows(ops[i], pend[modes[i]], n, b, Abar[i], f[i]);
+        for (int i = 0; i < d; ++i) {
+            if (!encode_rows(ops[i], pend[modes[i]], n, b, Abar[i], f[i])) return false;
             rho[i] = row_sum_bound(Abar[i], n);
             std::memcpy(pend[modes[i]], f[i], sizeof(int) * n);
         }
-        if (ok && drop_plan(b, d, rho, pl->mod, s, g)) break;
-    }
+        return drop_plan(b, d, rho, pl->mod, s, g);
+    };
+    int b = 53;
+    while (b >= 1 && !passes(b)) --b;
     if (b < 1) return OZ2_STATUS_RANGE;
     P->n = n;
     P->s = s;

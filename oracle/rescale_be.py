@@ -188,32 +188,59 @@ def row_sum_bound(Mbar: np.ndarray) -> int:
     return max(sum(abs(int(x)) for x in row) for row in Mbar)
 
 
-def drop_plan(b: int, rhos: Sequence[int], basis: Sequence[int], tau: int = 1):
-    """DropPlan: drop counts (g_1 .. g_d) or None (the page's failure)."""
-    B = 1 << b
-    L = list(basis)
-    PL = moduli_product(L)
-    d = len(rhos)
-    g = []
-    for i in range(d):
-        B = B * rhos[i]
-        if 2 * B >= PL:
+def greedy_rescale(B: int, b: int, available: Sequence[int]):
+    """The rescaling after a non-final product (Sec. 4.3, around Eq. 23).
+
+    A product leaves entries bounded by B.  Moduli are removed smallest
+    first for as long as the quotient bound floor(B/q) still has b bits
+    and more than one modulus would remain.  Removing q leaves the bound
+    floor(B/q) + 1 (the extra unit covers the rounding of the division) on
+    the basis without q, where it must stay recoverable: 2 B' < P_L / q.
+    Returns (number removed, the bound left, the moduli left), or None when
+    a removal would break that range condition."""
+    left = sorted(available)
+    P_left = moduli_product(left)
+    removed = 0
+    while len(left) > 1:
+        q = left[0]
+        if B // q < (1 << b):
+            break
+        B, P_left = B // q + 1, P_left // q
+        if not 2 * B < P_left:
             return None
-        gi = 0
-        if i < d - 1:
-            while len(L) > 1 and B // min(L) >= (1 << b):
-                q = min(L)
-                Bq = B // q + 1
-                if 2 * Bq >= PL // q:
-                    return None
-                L.remove(q)
-                PL //= q
-                B = Bq
-                gi += 1
-            if tau == 1:
-                L = list(basis)
-                PL = moduli_product(L)
-        g.append(gi)
+        left = left[1:]
+        removed += 1
+    return removed, B, left
+
+
+def drop_plan(b: int, rhos: Sequence[int], basis: Sequence[int], tau: int = 1):
+    """Drop counts (g_1 .. g_d) of a chain whose products have the operator
+    row-sum bounds rhos (Sec. 4.3, Eq. 21-23; the schedule the page calls
+    DropPlan), or None.
+
+    The bound starts at 2^b (every encoded entry) and follows the chain:
+    each product multiplies it by its rho (Eq. 22) and must keep it
+    recoverable on the moduli then available, 2 B < P_L; each non-final
+    product is followed by greedy_rescale.  With restoration (tau = 1, the
+    proposed method) base extension brings back the whole basis before the
+    next product; without it (tau = 0) the next product sees only the
+    moduli left.  The last product is decoded directly (g_d = 0)."""
+    B = 1 << b
+    available = list(basis)
+    g = []
+    for i, rho in enumerate(rhos):
+        B *= rho
+        if not 2 * B < moduli_product(available):
+            return None
+        if i == len(rhos) - 1:
+            g.append(0)
+            break
+        step = greedy_rescale(B, b, available)
+        if step is None:
+            return None
+        removed, B, left = step
+        g.append(removed)
+        available = list(basis) if tau == 1 else left
     return g
 
 
@@ -252,15 +279,14 @@ def effective_operators(ops: Sequence[np.ndarray], b: int, modes: Sequence[int] 
 
 
 def planner(ops: Sequence[np.ndarray], basis: Sequence[int], modes: Sequence[int] | None = None):
-    """Planner: the largest b <= 53 whose drop plan (with restoration) passes,
-    with rho_i(b) from the effective operators encoded at b.  Returns
-    (b, g) or None."""
-    for b in range(MAX_BITS, 0, -1):
-        rhos = [row_sum_bound(A) for A in effective_operators(ops, b, modes)[0]]
-        g = drop_plan(b, rhos, basis, 1)
-        if g is not None:
-            return b, g
-    return None
+    """The significand bits b and drop counts of a chain (Sec. 4.3; the page's
+    Planner): the largest b <= 53 whose schedule with restoration passes,
+    the row-sum bounds rho_i(b) taken from the effective operators encoded
+    at that b (encoding changes with b).  Returns (b, g) or None when no
+    b >= 1 passes."""
+    def schedule(b):
+        return drop_plan(b, [row_sum_bound(A) for A in effective_operators(ops, b, modes)[0]], basis, 1)
+    return next(((b, g) for b in range(MAX_BITS, 0, -1) for g in [schedule(b)] if g is not None), None)
 
 
 # ----------------------------------------------------------------------------

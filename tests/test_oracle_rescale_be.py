@@ -155,6 +155,20 @@ def test_horner_is_exact_below_2_53_and_close_above():
                 assert abs(Fraction(V[x]) - v) <= abs(v) * Fraction(16, 1 << 53)
 
 
+def test_greedy_rescale_hand_example():
+    # Sec. 4.3 around Eq. (23), basis (7, 5, 3), b = 2: after a product bounded
+    # by 12, floor(12/3) = 4 >= 2^2 drops 3 and leaves 4 + 1 = 5 with
+    # 2 * 5 < 35; floor(5/5) = 1 < 4 stops.
+    assert rb.greedy_rescale(12, 2, [7, 5, 3]) == (1, 5, [5, 7])
+    # a bound too small for any drop leaves everything
+    assert rb.greedy_rescale(11, 2, [7, 5, 3]) == (0, 11, [3, 5, 7])
+    # floor(200/3) + 1 = 67 but 2 * 67 >= 35: the quotient is not recoverable
+    assert rb.greedy_rescale(200, 2, [7, 5, 3]) is None
+    # b = 1, bound 40: 3 leaves (13 + 1 = 14, 2 * 14 < 35), then 5
+    # (2 + 1 = 3, 2 * 3 < 7); one modulus always remains
+    assert rb.greedy_rescale(40, 1, [7, 5, 3]) == (2, 3, [7])
+
+
 def test_drop_plan_hand_example():
     # basis (7, 5, 3), P = 105, b = 2, rho = (3, 3), restoration on:
     #   B = 4; i = 1: B = 12, 2B = 24 < 105; floor(12/3) = 4 >= 2^2 -> drop 3:
