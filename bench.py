@@ -29,6 +29,9 @@ Other workloads (--workload), each printing the same kind of JSON line:
              slowdown against the same calls untiled
   datapower  the headline product at s = 16 on zero, constant, random-integer
              and headline operands: the residue GEMM's rate by operand data
+  perfmodel  the performance model (the Arc page's Sec. 9.2 form: GEMM
+             blocks + memory bytes + launches) fitted to square DGEMMs and
+             checked on the non-square shapes of Table 10
   accuracy   the Arc page's accuracy protocol (Tables 6 and 8): 512 x 512 x
              4096 products of U(-1,1), phi = 2, sin/cos, spike, cancellation
              and 1 - 2^-53 data at s = 16, 20, 24; max ulp, correctly rounded
@@ -1043,6 +1046,122 @@ def run_datapower(args):
     }
 
 
+def gemm_block_terms(m, n, k, s, cplx=False):
+    """The residue GEMM's time terms under the per-block model, for the tile
+    the library launches: (waves, waves x k steps x passes) of the 256 x 256
+    tile and of the 128 x 128 tile (one of the two pairs is zero).  A wave is
+    one block per CU on 256 CUs (256 x 256), or four per CU (128 x 128);
+    k runs of at most 130816 positions are separate launches."""
+    pad = lambda x, q: (x + q - 1) // q * q
+    mp, np_, kp = pad(m, 256), pad(n, 256), pad(k, 256)
+    passes = 3 if cplx else 1
+    big = [0.0, 0.0]
+    small = [0.0, 0.0]
+    for k0 in range(0, kp, 130816):
+        steps = (min(kp, k0 + 130816) - k0) // 64
+        nb256 = (mp // 256) * (np_ // 256) * s
+        if nb256 >= 512 and steps * 64 > 512:
+            w = -(-nb256 // 256)
+            big[0] += w
+            big[1] += w * steps * passes
+        else:
+            w = -(-((mp // 128) * (np_ // 128) * s) // 1024)
+            small[0] += w
+            small[1] += w * steps * passes
+    return big + small
+
+
+def model_terms(m, n, k, s):
+    """Regressors of the performance model of one real N/N call (the Arc
+    page's Sec. 9.2 model, re-derived for this design): the four GEMM block
+    terms; the memory bytes, scan and encode (8 + 8 + s)(mk + kn) and
+    reconstruct (s + 8) mn, the GEMM's own s mn written counted in its block
+    time; and the launches (two fills, two scans, two encodes, one GEMM per
+    k run, one reconstruct)."""
+    runs = -(-((k + 255) // 256 * 256) // 130816)
+    mem = (16.0 + s) * (m * k + k * n) + (s + 8.0) * m * n
+    return gemm_block_terms(m, n, k, s) + [mem, 7.0 + runs]
+
+
+def run_perfmodel(args):
+    """Fit T = waves x (c0 + c1 k steps) [per tile kind] + bytes / beta + launches x tau
+    to measured call times of square DGEMMs (N = 1024 .. 8192, s = 8, 16, 24:
+    the grid of the Arc page's Table 17 and the headline's size) and check it
+    on the held-out non-square shapes of Table 10 (s = 8, 16)."""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import workloads
+    h = oz2.Handle(torch.cuda.current_stream())
+    h.set_timing(True)
+
+    def measure(m, n, k, s, A, B):
+        dC = torch.zeros(m * n, dtype=torch.float64, device="cuda")
+        for _ in range(2):
+            h.dgemm("N", "N", m, n, k, 1.0, A, m, B, k, 0.0, dC, m, s)
+        torch.cuda.synchronize()
+        tot, ph = [], []
+        for _ in range(max(3, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            h.dgemm("N", "N", m, n, k, 1.0, A, m, B, k, 0.0, dC, m, s)
+            e1.record()
+            torch.cuda.synchronize()
+            tot.append(e0.elapsed_time(e1))
+            ph.append(h.phase_times())
+        return float(np.median(tot)), [float(x) for x in np.median(np.array(ph), axis=0)]
+
+    fit_pts, test_pts = [], []
+    for N in (1024, 2048, 3072, 4096, 8192):
+        A = torch.from_numpy(workloads.real_matrix(N, N, workloads.seed(10, 0), "phi", 0.5)).cuda()
+        B = torch.from_numpy(workloads.real_matrix(N, N, workloads.seed(10, 1), "phi", 0.5)).cuda()
+        for s_ in (8, 16, 24):
+            log(f"[bench] perfmodel: {N}^3, s = {s_}")
+            t, ph = measure(N, N, N, s_, A, B)
+            fit_pts.append(((N, N, N, s_), t, ph))
+        del A, B
+    W = workloads.NONSQUARE
+    for q, (m, k, n) in enumerate(W["shapes"]):
+        A = torch.from_numpy(workloads.real_matrix(m, k, workloads.nonsquare_seed(q, 0), W["dist"])).cuda()
+        B = torch.from_numpy(workloads.real_matrix(k, n, workloads.nonsquare_seed(q, 1), W["dist"])).cuda()
+        for s_ in W["s"]:
+            log(f"[bench] perfmodel: {m} x {k} x {n}, s = {s_}")
+            t, ph = measure(m, n, k, s_, A, B)
+            test_pts.append(((m, n, k, s_), t, ph))
+        del A, B
+    h.close()
+    X = np.array([model_terms(*p[0]) for p in fit_pts])
+    y = np.array([p[1] for p in fit_pts])
+    used = [j for j in range(X.shape[1]) if np.any(X[:, j])]
+    coef = np.zeros(X.shape[1])
+    coef[used] = np.linalg.lstsq(X[:, used] / y[:, None], np.ones(len(y)), rcond=None)[0]  # relative errors
+    params = dict(c0_256_us=coef[0] * 1e3, c1_256_us=coef[1] * 1e3, c0_128_us=coef[2] * 1e3,
+                  c1_128_us=coef[3] * 1e3, beta_mem_GBs=(1e-6 / coef[4]) if coef[4] > 0 else None,
+                  tau_us=coef[5] * 1e3)
+
+    def rows(pts):
+        out = []
+        for (m, n, k, s_), t, ph in pts:
+            pred = float(np.dot(model_terms(m, n, k, s_), coef))
+            out.append(dict(shape=f"{m}x{k}x{n}", s=s_, measured_ms=round(t, 4), model_ms=round(pred, 4),
+                            deviation=round(pred / t - 1.0, 4),
+                            phases_ms=dict(scan=round(ph[0], 4), encode=round(ph[1], 4), gemm=round(ph[2], 4),
+                                           reconstruct=round(ph[3], 4))))
+        return out
+    fit_rows, test_rows = rows(fit_pts), rows(test_pts)
+    worst = max(abs(r["deviation"]) for r in test_rows)
+    return {
+        "metric": "performance model: largest |model / measured - 1| on the held-out non-square shapes",
+        "value": round(worst, 4),
+        "unit": "relative deviation",
+        "ms_per_step": None,
+        "dtype": "i8",
+        "config": {"workload": "dgemm_perf_model", "fit": "square N = 1024..8192, s = 8, 16, 24",
+                   "check": "Table 10 non-square shapes, s = 8, 16"},
+        "per_shape": {"params": {k_: (round(v, 4) if v is not None else None) for k_, v in params.items()},
+                      "fit": fit_rows, "check": test_rows},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1050,7 +1169,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
                     choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "nonsquare",
-                             "reuse8192", "tiled8192", "datapower", "accuracy"])
+                             "reuse8192", "tiled8192", "datapower", "accuracy", "perfmodel"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
     ap.add_argument("--cpu-side", type=int, default=0)
@@ -1081,6 +1200,8 @@ def main():
         out = run_datapower(args)
     elif args.workload == "accuracy":
         out = run_accuracy(args)
+    elif args.workload == "perfmodel":
+        out = run_perfmodel(args)
     else:
         out = run_gemm(args, args.workload)
     line = {"metric": out["metric"], "value": out["value"], "unit": out["unit"], "n_gpus": 1,

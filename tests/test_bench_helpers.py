@@ -141,3 +141,18 @@ def test_accuracy_operands_shapes_and_structure():
     assert np.array_equal(Am[:, : k // 2], Am[:, k // 2:])
     C = Am @ Bm
     assert np.max(np.abs(C)) < 2.0 ** -25 * np.max(np.abs(Am) @ np.abs(Bm))
+
+
+def test_gemm_block_terms_follow_the_tile_choice():
+    # 256 x 256 tile when >= 512 such blocks over all moduli and k > 512;
+    # 8192^3 at s = 16: 32 x 32 x 16 blocks = 64 waves of 256 CUs, 128 steps
+    assert bench.gemm_block_terms(8192, 8192, 8192, 16) == [64, 64 * 128, 0, 0]
+    # short k takes the 128 x 128 tile, four blocks per CU
+    assert bench.gemm_block_terms(8192, 8192, 256, 8) == [0, 0, 32, 32 * 4]
+    # few blocks: 1024^2 at s = 8 is 128 blocks of 256 x 256
+    assert bench.gemm_block_terms(1024, 1024, 1024, 8)[:2] == [0, 0]
+    # k beyond one exact run: two launches
+    t = bench.gemm_block_terms(2048, 2048, 131330, 8)
+    assert t[0] == 2 * 2 and t[1] == 2 * (2044 + 12)
+    # the complex 3M kernel runs three k-loops per block
+    assert bench.gemm_block_terms(4096, 4096, 4096, 16, cplx=True)[1] == 16 * 64 * 3
