@@ -1,6 +1,6 @@
 // oz2_gemm.hip -- the s exact INT8 residue products of Ozaki scheme II on the
-// gfx950 INT8 matrix cores (v_mfma_i32_32x32x32_i8), with the reduction
-// mod m_t fused into the epilogue.
+// gfx950 INT8 matrix cores (v_mfma_i32_16x16x64_i8 and _32x32x32_i8), with
+// the reduction mod m_t fused into the epilogue.
 //
 // "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
 // Ozaki Scheme II on the Xe2 Architecture", Sec. 2.3 step 3: each product
@@ -23,34 +23,40 @@
 // contiguous run of memory.  The output plane of modulus t is uint8
 // [n][m_pad] (column-major like C) holding C^(t) mod m_t in [0, m_t).
 //
-// Kernel shape (CDNA4): a BM x BN tile of one modulus per block, WM x WN
-// wavefronts, each owning (BM/WM) x (BN/WN) INT32 accumulators in 32 x 32
-// MFMA tiles.  k advances one 64-byte panel per step through NST LDS stages
-// filled by direct global->LDS loads (global_load_lds_dwordx4: no VGPR
-// staging, no ds_write) issued NST - 1 steps ahead: four stages for the
-// 256 x 256 tile, so a load has three steps of MFMAs to arrive; two for the
-// 128 x 128 tile, which instead runs four blocks per CU.  The loads are issued from inline assembly: the
-// compiler cannot tell the stages of an LDS-DMA pipeline apart and would
-// otherwise wait for every load in flight before each LDS read; here the
-// kernel's own vmcnt wait before each barrier orders them.
+// Kernel shapes (CDNA4).  Large products: a 256 x 256 tile of one modulus
+// per block on 8 wavefronts of 128 x 64, on v_mfma_i32_16x16x64_i8 (one
+// MFMA per 16 x 16 block and 64-byte k step).  k advances one 64-byte panel
+// per step through four LDS stages filled by direct global->LDS loads
+// (global_load_lds_dwordx4: no VGPR staging, no ds_write) issued three steps
+// ahead.  The waves form two groups of four, waves 0-3 and 4-7, one of each
+// per SIMD, that alternate every half step between a memory phase (read one
+// k step's fragments from LDS into registers, issue their share of the
+// loads) and a compute phase (that step's 32 MFMAs from registers), with a
+// block barrier between phases and the second group one phase behind: on
+// every SIMD one wave issues MFMAs while the other reads LDS (a ping-pong
+// schedule, measured 1.3% faster than interleaving both in every wave).
+// The 16 x 16 x 64 form does the same work as 32 x 32 x 32 with the same
+// LDS traffic and accumulator count, but reads and writes half the
+// accumulator bytes per multiply-add; since the GEMM on residue data is
+// limited by power, not by issue (it runs at 72% of the INT8 peak on
+// operands whose bits do not toggle, 49% on residues), that made it 11%
+// faster at 8192^3.
 //
-// The 256 x 256 tile runs a ping-pong schedule.  Its 8 wavefronts form two
-// groups of four, waves 0-3 and 4-7, one wave of each group per SIMD.  Every
-// wave alternates a memory phase (read one k step's fragments from LDS into
-// registers, issue its share of the loads three steps ahead) and a compute
-// phase (that step's 16 MFMAs from registers), with a block barrier between
-// phases; the second group starts one phase late.  So on every SIMD one wave
-// issues MFMAs while the other reads LDS, and no MFMA waits for an LDS read
-// (measured: GEMM 1.3% faster at 8192^3, the 3M ZGEMM at 4096^3 2.5%).  The
-// 128 x 128 tile keeps one schedule for all waves: fragments double buffered
-// in registers, MFMAs interleaved one-to-one with the LDS reads of the next
-// 32-wide k sub-step (sched_group_barrier).  LDS rows are 64 bytes of four 16-byte chunks whose
-// position is XOR-ed with (row/4) mod 4: the LDS serves a 16-byte-per-lane
-// read 16 lanes per clock over 64 banks, and 16 consecutive rows then hit
-// distinct bank groups.  The 256 x 256 tile uses 8 wavefronts (two per SIMD)
-// so that one wave's MFMAs cover the other's waits.  Blocks are remapped so
-// that each of the 8 XCDs (which receive blocks round-robin) works on a
-// contiguous range of tiles, grouped 8 tiles tall for L2 reuse.
+// Small grids and short k: a 128 x 128 tile on 4 wavefronts with two LDS
+// stages (four blocks per CU, whose epilogues overlap the others' MFMAs) on
+// v_mfma_i32_32x32x32_i8, fragments double buffered in registers and the
+// MFMAs interleaved one-to-one with the LDS reads of the next 32-wide k
+// sub-step (sched_group_barrier).
+//
+// The loads are issued from inline assembly: the compiler cannot tell the
+// stages of an LDS-DMA pipeline apart and would otherwise wait for every
+// load in flight before each LDS read; the kernel's own vmcnt wait before
+// each barrier orders them.  LDS rows are 64 bytes of four 16-byte chunks
+// whose position is XOR-ed with (row/4) mod 4: the LDS serves a
+// 16-byte-per-lane read 16 lanes per clock over 64 banks, and 16 consecutive
+// rows then hit distinct bank groups.  Blocks are remapped so that each of
+// the 8 XCDs (which receive blocks round-robin) works on a contiguous range
+// of tiles, grouped 8 tiles tall for L2 reuse.
 #include "oz2_internal.h"
 
 namespace oz2 {
@@ -278,48 +284,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-        if constexpr (NST == 4) {
-            // ping-pong: waves 0-3 and 4-7 (one of each per SIMD) alternate
-            // every half step between reading a step's fragments (and
-            // issuing the loads three steps ahead) and running that step's
-            // MFMAs from registers; a block barrier separates the phases
-            const int grp = wave_u >> 2;
-            constexpr int kWaitPP = waitcnt_vm(2 * kLoadsPerStep, true);
-            auto mem = [&](int st, int kdma, int st_dma) {
-                rd(st, 0, fa[0], fb[0]);
-                rd(st, 1, fa[1], fb[1]);
-                issue(kdma, st_dma);
-            };
-            auto comp = [&]() {
-                __builtin_amdgcn_s_setprio(1);
-                mm(fa[0], fb[0]);
-                mm(fa[1], fb[1]);
-                __builtin_amdgcn_s_setprio(0);
-            };
-            auto sync = [&]() {
-                __builtin_amdgcn_s_waitcnt(kWaitPP);
-                __syncthreads();
-            };
-#pragma unroll
-            for (int j = 0; j < 3; ++j) issue(j, j);
-            sync();
-            // the second group starts one phase late: it reads step k while
-            // the first runs step k's MFMAs, and runs them while the first
-            // reads step k + 1.  Every wave passes the same number of
-            // barriers: the first group takes its extra one at the end.
-            if (grp == 1) sync();
-#pragma unroll 1
-            for (int kt = 0; kt < nk; kt += 4) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    mem(j, min(kt + j + 3, nk - 1), (j + 3) & 3);
-                    sync();
-                    comp();
-                    sync();
-                }
-            }
-            if (grp == 0) sync();
-        } else {
 #pragma unroll
         for (int j = 0; j < kStages; ++j) issue(j, j);
         __builtin_amdgcn_s_waitcnt(kWaitFirst);
@@ -331,7 +295,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
             // per step keeps the vmcnt arithmetic exact)
 #pragma unroll
             for (int j = 0; j < kStages; ++j) kstep(j, min(kt + j + kStages, nk - 1));
-        }
         }
         // no LDS DMA may be in flight when the stages are reused or released
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, false));
@@ -389,16 +352,186 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParam
     }
 }
 
+// The 256 x 256 tile on v_mfma_i32_16x16x64_i8: one MFMA covers a 16 x 16
+// block and a whole 64-byte k step.  8 wavefronts of 128 x 64 (8 x 4 blocks,
+// 32 accumulators of 4 registers each), four LDS stages, loads three steps
+// ahead and the ping-pong schedule described at the top.  A fragment is 16 rows x 64 bytes:
+// lane l reads row l mod 16, chunk l / 16.  Output: lane l holds column
+// l mod 16, rows 4 (l / 16) + {0..3} of a block: four consecutive bytes of
+// the output plane.
+template <bool CPLX>
+__global__ __launch_bounds__(512, 1) void residue_gemm16_kernel(GemmParams P) {
+    constexpr int BM = 256, BN = 256, WM = 2, WN = 4, NW = 8, kStages = 4;
+    constexpr int WTM = BM / WM, WTN = BN / WN, GM = WTM / 16, GN = WTN / 16;
+    constexpr int LOADS_A = BM * kChunks / 64 / NW, LOADS_B = BN * kChunks / 64 / NW;
+    constexpr int STAGE = (BM + BN) * kBK;
+    __shared__ __attribute__((aligned(1024))) int8_t sS0[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS1[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS2[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS3[STAGE];
+    auto stage = [&](int st) -> int8_t* { return st == 0 ? sS0 : st == 1 ? sS1 : st == 2 ? sS2 : sS3; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave % WM, wn = wave / WM;
+    int t, tm, tn;
+    block_tile(blockIdx.x, gridDim.x, P.tiles_m, P.tiles_n, t, tm, tn);
+    const uint32_t m = P.mod[t];
+    const double dm = (double)m, rcp = P.rcp[t], half_rcp = 0.5 * rcp;
+    const int64_t kp = P.kp;
+    const int nk = P.k_steps;
+
+    uint32_t goffA[LOADS_A], goffB[LOADS_B];
+#pragma unroll
+    for (int q = 0; q < LOADS_A; ++q) {
+        const int piece = (wave * LOADS_A + q) * 64 + lane;
+        const int row = piece / kChunks, pos = piece % kChunks;
+        goffA[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
+    }
+#pragma unroll
+    for (int q = 0; q < LOADS_B; ++q) {
+        const int piece = (wave * LOADS_B + q) * 64 + lane;
+        const int row = piece / kChunks, pos = piece % kChunks;
+        goffB[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
+    }
+    const int r16 = lane & 15, c16 = lane >> 4;
+    const int sw = (c16 ^ ((r16 >> 2) & 3)) << 4;  // swizzled chunk of this lane's row
+    const int aoff = (wm * WTM + r16) * kBK + sw;
+    const int boff = BM * kBK + (wn * WTN + r16) * kBK + sw;
+    const int64_t row_out0 = (int64_t)tm * BM + wm * WTM + 4 * c16;
+    const int64_t col_out0 = (int64_t)tn * BN + wn * WTN + r16;
+    const int64_t panelA = P.a_rows * kBK, panelB = P.b_rows * kBK;
+
+    v4i acc[GM][GN];
+    v4i fa[GM], fb[GN];
+    uint32_t park[CPLX ? GM : 1][CPLX ? GN : 1];
+
+#pragma unroll 1
+    for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
+        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.a_rows * kp + (P.k_begin / kBK) * panelA +
+                           (int64_t)tm * BM * kBK;
+        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.b_rows * kp + (P.k_begin / kBK) * panelB +
+                           (int64_t)tn * BN * kBK;
+        auto issue = [&](int kt, int st) {
+            const int8_t* Ak = Ag + (int64_t)kt * panelA;
+            const int8_t* Bk = Bg + (int64_t)kt * panelB;
+            const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)stage(st);
+#pragma unroll
+            for (int q = 0; q < LOADS_A; ++q) dma_1k(Ak, goffA[q], lds + (wave_u * LOADS_A + q) * 1024);
+#pragma unroll
+            for (int q = 0; q < LOADS_B; ++q) dma_1k(Bk, goffB[q], lds + BM * kBK + (wave_u * LOADS_B + q) * 1024);
+        };
+        constexpr int kLoadsPerStep = LOADS_A + LOADS_B;
+        constexpr int kWaitPP = waitcnt_vm(2 * kLoadsPerStep, true);
+        auto mem = [&](int st, int kdma, int st_dma) {
+            const int8_t* S = stage(st);
+#pragma unroll
+            for (int i = 0; i < GM; ++i) fa[i] = *(const v4i*)(S + aoff + i * 16 * kBK);
+#pragma unroll
+            for (int j = 0; j < GN; ++j) fb[j] = *(const v4i*)(S + boff + j * 16 * kBK);
+            issue(kdma, st_dma);
+        };
+        auto comp = [&]() {
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int i = 0; i < GM; ++i)
+#pragma unroll
+                for (int j = 0; j < GN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
+        };
+        auto sync = [&]() {
+            __builtin_amdgcn_s_waitcnt(kWaitPP);
+            __syncthreads();
+        };
+#pragma unroll
+        for (int i = 0; i < GM; ++i)
+#pragma unroll
+            for (int j = 0; j < GN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        const int grp = wave_u >> 2;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) issue(j, j);
+        sync();
+        if (grp == 1) sync();
+#pragma unroll 1
+        for (int kt = 0; kt < nk; kt += 4) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                mem(j, min(kt + j + 3, nk - 1), (j + 3) & 3);
+                sync();
+                comp();
+                sync();
+            }
+        }
+        if (grp == 0) sync();
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, false));
+        __syncthreads();
+
+#pragma unroll
+        for (int i = 0; i < GM; ++i) {
+#pragma unroll
+            for (int j = 0; j < GN; ++j) {
+                const int64_t col = col_out0 + j * 16;
+                const int64_t row = row_out0 + i * 16;
+                uint32_t r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][e], dm, rcp, half_rcp);
+                uint8_t* re_dst = P.C + (int64_t)t * P.n * P.mp + col * P.mp + row;
+                if (!CPLX) {
+                    if (col < P.n) *(uint32_t*)re_dst = pack4(r);
+                } else if (pass == 0) {
+                    park[i][j] = pack4(r);
+                } else if (pass == 1) {
+                    const uint32_t t1w = park[i][j];
+                    uint32_t re[4], smv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t r1 = (t1w >> (8 * e)) & 0xffu;
+                        const uint32_t x = r1 + m - r[e];
+                        const uint32_t x1 = x - m;
+                        re[e] = x < x1 ? x : x1;
+                        const uint32_t y = r1 + r[e];
+                        const uint32_t y1 = y - m;
+                        smv[e] = y < y1 ? y : y1;
+                    }
+                    park[i][j] = pack4(smv);
+                    if (col < P.n) *(uint32_t*)re_dst = pack4(re);
+                } else {
+                    const uint32_t swd = park[i][j];
+                    uint32_t im[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t x = r[e] + m - ((swd >> (8 * e)) & 0xffu);
+                        const uint32_t x1 = x - m;
+                        im[e] = x < x1 ? x : x1;
+                    }
+                    if (col < P.n) *(uint32_t*)(re_dst + P.c_set_stride) = pack4(im);
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WM, int WN, int NST>
 hipError_t gemm_go(GemmParams P, bool cplx, hipStream_t st) {
     P.tiles_m = (int)(P.mp / BM);
     P.tiles_n = (int)(P.np / BN);
     const int64_t nb = (int64_t)P.tiles_m * P.tiles_n * P.s;
     const dim3 block(64 * WM * WN);
-    if (cplx)
-        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, true>), dim3((unsigned)nb), block, 0, st, P);
-    else
-        hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, false>), dim3((unsigned)nb), block, 0, st, P);
+    static_assert(NST == 2 || (BM == 256 && BN == 256 && WM == 2 && WN == 4), "the four-stage tile is 256 x 256");
+    if constexpr (NST == 4) {
+        if (cplx)
+            hipLaunchKernelGGL((residue_gemm16_kernel<true>), dim3((unsigned)nb), block, 0, st, P);
+        else
+            hipLaunchKernelGGL((residue_gemm16_kernel<false>), dim3((unsigned)nb), block, 0, st, P);
+    } else {
+        if (cplx)
+            hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, true>), dim3((unsigned)nb), block, 0, st, P);
+        else
+            hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, false>), dim3((unsigned)nb), block, 0, st, P);
+    }
     return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ def gemm_asm(tmp_path_factory):
 
 def _kernels(asm):
     bodies = {}
-    for m in re.finditer(r"^(_Z\w*residue_gemm_kernel\w*):", asm, re.M):
+    for m in re.finditer(r"^(_Z\w*residue_gemm(?:16)?_kernel\w*):", asm, re.M):
         end = asm.index(".Lfunc_end", m.end())
         lines = [l.split(";")[0].strip() for l in asm[m.end():end].split("\n")]
         bodies[m.group(1)] = [l for l in lines if l and not l.startswith(".")]
@@ -56,7 +56,10 @@ def test_m0_written_only_by_the_load_sequence(gemm_asm):
 
 
 def _template_args(name):
-    # residue_gemm_kernel<BM, BN, WM, WN, NST, CPLX>
+    # residue_gemm_kernel<BM, BN, WM, WN, NST, CPLX>; residue_gemm16_kernel<CPLX>
+    # is the 256 x 256, 8-wave, four-stage tile
+    if "residue_gemm16_kernel" in name:
+        return 256, 256, 2, 4, 4
     ints = [int(x) for x in re.findall(r"Li(\d+)E", name)]
     bm, bn, wm, wn, nst = ints[:5]
     return bm, bn, wm, wn, nst
@@ -88,8 +91,8 @@ def test_main_loop_keeps_loads_in_flight(gemm_asm):
 
 def test_ping_pong_phases(gemm_asm):
     # in the main loop of the 256 x 256 tile, consecutive barriers enclose
-    # either a memory phase (LDS fragment reads and loads, no MFMA) or a
-    # compute phase (the step's 16 MFMAs, no LDS read)
+    # either a memory phase (a k step's 12 LDS fragment reads and its loads,
+    # no MFMA) or a compute phase (the step's 32 16x16x64 MFMAs, no LDS read)
     for name, lines in _kernels(gemm_asm).items():
         if _template_args(name)[4] != 4:
             continue
@@ -101,6 +104,8 @@ def test_ping_pong_phases(gemm_asm):
             rd = sum(l.startswith("ds_read") for l in seg)
             if mf or rd:
                 phases.append((mf, rd))
-        loop = [p for p in phases if p in ((16, 0), (0, 12))]
+        assert "residue_gemm16_kernel" in name
+        loop = [p for p in phases if p in ((32, 0), (0, 12))]
         assert len(loop) >= 8, (name, phases)
-        assert all(p in ((16, 0), (0, 12)) for p in phases if p[0] == 16 or p[1] == 12), (name, phases)
+        assert all(p in ((32, 0), (0, 12)) for p in phases), (name, phases)
+        assert all(l.startswith("v_mfma_i32_16x16x64_i8") for l in lines if l.startswith("v_mfma")), name
