@@ -1,6 +1,6 @@
 // oz2_gemm.hip -- the s exact INT8 residue products of Ozaki scheme II on the
-// gfx950 INT8 matrix cores (v_mfma_i32_16x16x64_i8 and _32x32x32_i8), with
-// the reduction mod m_t fused into the epilogue.
+// gfx950 INT8 matrix cores (v_mfma_i32_16x16x64_i8), with the reduction
+// mod m_t fused into the epilogue.
 //
 // "Emulating DGEMM and ZGEMM with INT8 Matrix Engines on Intel Arc GPUs:
 // Ozaki Scheme II on the Xe2 Architecture", Sec. 2.3 step 3: each product
@@ -42,11 +42,11 @@
 // operands whose bits do not toggle, 49% on residues), that made it 11%
 // faster at 8192^3.
 //
-// Small grids and short k: a 128 x 128 tile on 4 wavefronts with two LDS
-// stages (four blocks per CU, whose epilogues overlap the others' MFMAs) on
-// v_mfma_i32_32x32x32_i8, fragments double buffered in registers and the
-// MFMAs interleaved one-to-one with the LDS reads of the next 32-wide k
-// sub-step (sched_group_barrier).
+// Small grids and short k: a 128 x 128 tile on 4 wavefronts of 64 x 64, also
+// on v_mfma_i32_16x16x64_i8, with two LDS stages (the loads of step k + 1
+// issued at the start of step k); several blocks per CU cover each other's
+// waits and epilogues (16x16x64 made the k = 256 products' GEMM 13% faster
+// than the 32x32x32 form it replaced).
 //
 // The loads are issued from inline assembly: the compiler cannot tell the
 // stages of an LDS-DMA pipeline apart and would otherwise wait for every
@@ -63,7 +63,6 @@ namespace oz2 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* global_ptr_t;
 
@@ -72,9 +71,6 @@ constexpr int kChunks = kBK / 16;
 constexpr int kMaxStages = 4;  // LDS stages of the 256 x 256 tile; 128 x 128 tiles use 2
 static_assert(kBK == kPanelK, "one k step is one panel");
 static_assert(kPadK % (kBK * kMaxStages) == 0, "padded k holds whole stage rounds");
-
-// instruction classes for __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 
 // INT32 accumulator -> [0, m): r = acc - m floor((acc + 1/2) / m) in FP64.
 // (acc + 1/2) / m lies at least 1 / (2m) from an integer, and
@@ -145,211 +141,6 @@ __device__ __forceinline__ void block_tile(int bid, int nb, int tiles_m, int til
     const int in = rem % per_group;
     tm = first_m + in % gsz;
     tn = in / gsz;
-}
-
-template <int BM, int BN, int WM, int WN, int NST, bool CPLX>
-__global__ __launch_bounds__(64 * WM * WN, 1) void residue_gemm_kernel(GemmParams P) {
-    constexpr int kStages = NST;
-    static_assert(NST == 2 || NST == 4, "two or four stages");
-    constexpr int NW = WM * WN;
-    constexpr int WTM = BM / WM, WTN = BN / WN, FM = WTM / 32, FN = WTN / 32;
-    constexpr int LOADS_A = BM * kChunks / 64 / NW;  // wave-wide 1 KiB loads per wave and stage
-    constexpr int LOADS_B = BN * kChunks / 64 / NW;
-    static_assert(LOADS_A * 64 * NW == BM * kChunks && LOADS_B * 64 * NW == BN * kChunks, "tile/wave mismatch");
-    constexpr int STAGE = (BM + BN) * kBK;  // A rows then B rows
-    // one object per stage
-    __shared__ __attribute__((aligned(1024))) int8_t sS0[STAGE];
-    __shared__ __attribute__((aligned(1024))) int8_t sS1[STAGE];
-    __shared__ __attribute__((aligned(1024))) int8_t sS2[NST > 2 ? STAGE : 1];
-    __shared__ __attribute__((aligned(1024))) int8_t sS3[NST > 2 ? STAGE : 1];
-    auto stage = [&](int st) -> int8_t* { return st == 0 ? sS0 : st == 1 ? sS1 : st == 2 ? sS2 : sS3; };
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const int wm = wave % WM, wn = wave / WM;
-
-    // block -> (modulus, tile row, tile column)
-    int t, tm, tn;
-    block_tile(blockIdx.x, gridDim.x, P.tiles_m, P.tiles_n, t, tm, tn);
-
-    const uint32_t m = P.mod[t];
-    const double dm = (double)m, rcp = P.rcp[t], half_rcp = 0.5 * rcp;
-    const int64_t kp = P.kp;
-    const int nk = P.k_steps;  // multiple of 4; this launch covers k in [k_begin, k_begin + 64 nk)
-
-    // per-lane source offsets of the direct loads: piece = 16 bytes landing at
-    // LDS byte 16 * piece, i.e. row piece / 4, stored chunk position piece % 4
-    uint32_t goffA[LOADS_A], goffB[LOADS_B];
-#pragma unroll
-    for (int q = 0; q < LOADS_A; ++q) {
-        const int piece = (wave * LOADS_A + q) * 64 + lane;
-        const int row = piece / kChunks, pos = piece % kChunks;
-        goffA[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
-    }
-#pragma unroll
-    for (int q = 0; q < LOADS_B; ++q) {
-        const int piece = (wave * LOADS_B + q) * 64 + lane;
-        const int row = piece / kChunks, pos = piece % kChunks;
-        goffB[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
-    }
-    const int fr = lane & 31;
-    const int aoff = (wm * WTM + fr) * kBK;
-    const int boff = BM * kBK + (wn * WTN + fr) * kBK;
-    const int row_out0 = tm * BM + wm * WTM + 4 * (lane >> 5);
-    const int col_out0 = tn * BN + wn * WTN + fr;
-    const int64_t panelA = P.a_rows * kBK, panelB = P.b_rows * kBK;  // bytes per k step
-
-    v16i acc[FM][FN];
-    v4i fa[2][FM], fb[2][FN];
-    // complex: T1 mod m, then (T1 + T2) mod m, four bytes per word, kept in
-    // registers across the k-loops of the three products
-    uint32_t park[CPLX ? FM : 1][CPLX ? FN : 1][4];
-
-#pragma unroll 1
-    for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
-        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.a_rows * kp + (P.k_begin / kBK) * panelA +
-                           (int64_t)tm * BM * kBK;
-        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.b_rows * kp + (P.k_begin / kBK) * panelB +
-                           (int64_t)tn * BN * kBK;
-        auto issue = [&](int kt, int st) {
-            const int8_t* Ak = Ag + (int64_t)kt * panelA;
-            const int8_t* Bk = Bg + (int64_t)kt * panelB;
-            const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)stage(st);
-#pragma unroll
-            for (int q = 0; q < LOADS_A; ++q) dma_1k(Ak, goffA[q], lds + (wave_u * LOADS_A + q) * 1024);
-#pragma unroll
-            for (int q = 0; q < LOADS_B; ++q) dma_1k(Bk, goffB[q], lds + BM * kBK + (wave_u * LOADS_B + q) * 1024);
-        };
-        // fragments of sub-step ks: lane l holds row (l mod 32), chunk 2 ks + l / 32
-        auto rd = [&](int st, int ks, v4i (&a)[FM], v4i (&b)[FN]) {
-            const int8_t* S = stage(st);
-            const int c = ks * 2 + (lane >> 5);
-            const int sw = (c ^ ((fr >> 2) & 3)) << 4;
-#pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = *(const v4i*)(S + aoff + i * 32 * kBK + sw);
-#pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = *(const v4i*)(S + boff + j * 32 * kBK + sw);
-        };
-        auto mm = [&](v4i (&a)[FM], v4i (&b)[FN]) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-        };
-        constexpr int NMF = FM * FN, NDS = FM + FN;
-        auto sched = [&]() {
-#pragma unroll
-            for (int q = 0; q < NDS; ++q) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, NMF - NDS, 0);
-        };
-        // this wave's loads of the next step have landed when at most the
-        // loads of the two steps after it are in flight
-        constexpr int kLoadsPerStep = LOADS_A + LOADS_B;
-        constexpr int kWaitStep = waitcnt_vm((kStages - 2) * kLoadsPerStep, true);
-        constexpr int kWaitFirst = waitcnt_vm((kStages - 1) * kLoadsPerStep, false);
-        static_assert((kStages - 1) * kLoadsPerStep < 64, "vmcnt range");
-        // one k step on stage st; after the barrier the next stage's first
-        // fragments are read and the loads of step kdma refill stage st.
-        // Each half runs at raised wave priority and drops it before the
-        // barrier, so that the other wave on the SIMD, which is still in
-        // its half, gets its MFMAs issued first (measured: 1.6% faster).
-        auto kstep = [&](int st, int kdma) {
-            __builtin_amdgcn_s_setprio(1);
-            rd(st, 1, fa[1], fb[1]);
-            mm(fa[0], fb[0]);
-            sched();
-            __builtin_amdgcn_s_setprio(0);
-            // every read of this stage has returned and the next stage has
-            // landed for this wave; after the barrier both hold block-wide
-            __builtin_amdgcn_s_waitcnt(kWaitStep);
-            __syncthreads();
-            // past the last step these read data that is not used
-            __builtin_amdgcn_s_setprio(1);
-            rd((st + 1) % kStages, 0, fa[0], fb[0]);
-            issue(kdma, st);
-            mm(fa[1], fb[1]);
-            sched();
-            __builtin_amdgcn_s_setprio(0);
-        };
-
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-#pragma unroll
-        for (int j = 0; j < kStages; ++j) issue(j, j);
-        __builtin_amdgcn_s_waitcnt(kWaitFirst);
-        __syncthreads();
-        rd(0, 0, fa[0], fb[0]);
-#pragma unroll 1
-        for (int kt = 0; kt < nk; kt += kStages) {
-            // steps past the end reload the last step (same count of loads
-            // per step keeps the vmcnt arithmetic exact)
-#pragma unroll
-            for (int j = 0; j < kStages; ++j) kstep(j, min(kt + j + kStages, nk - 1));
-        }
-        // no LDS DMA may be in flight when the stages are reused or released
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, false));
-        __syncthreads();
-
-        // epilogue: lane holds rows 8g + 4(lane/32) + {0..3} of column lane%32
-        // of every 32x32 tile, i.e. four consecutive bytes of the output plane
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int64_t col = col_out0 + j * 32;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    uint32_t r[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][4 * g + e], dm, rcp, half_rcp);
-                    const int64_t row = row_out0 + i * 32 + 8 * g;
-                    uint8_t* re_dst = P.C + (int64_t)t * P.n * P.mp + col * P.mp + row;
-                    if (!CPLX) {
-                        if (col < P.n) *(uint32_t*)re_dst = pack4(r);
-                    } else if (pass == 0) {
-                        park[i][j][g] = pack4(r);  // T1 mod m
-                    } else if (pass == 1) {
-                        // Re = T1 - T2 leaves; T1 + T2 stays parked
-                        const uint32_t t1w = park[i][j][g];
-                        uint32_t re[4], sm[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t r1 = (t1w >> (8 * e)) & 0xffu;
-                            const uint32_t x = r1 + m - r[e];
-                            const uint32_t x1 = x - m;
-                            re[e] = x < x1 ? x : x1;
-                            const uint32_t y = r1 + r[e];
-                            const uint32_t y1 = y - m;
-                            sm[e] = y < y1 ? y : y1;
-                        }
-                        park[i][j][g] = pack4(sm);
-                        if (col < P.n) *(uint32_t*)re_dst = pack4(re);
-                    } else {
-                        // Im = T3 - (T1 + T2)
-                        const uint32_t sw = park[i][j][g];
-                        uint32_t im[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t x = r[e] + m - ((sw >> (8 * e)) & 0xffu);
-                            const uint32_t x1 = x - m;
-                            im[e] = x < x1 ? x : x1;
-                        }
-                        if (col < P.n) *(uint32_t*)(re_dst + P.c_set_stride) = pack4(im);
-                    }
-                }
-            }
-        }
-    }
 }
 
 // The 256 x 256 tile on v_mfma_i32_16x16x64_i8: one MFMA covers a 16 x 16
@@ -514,24 +305,162 @@ __global__ __launch_bounds__(512, 1) void residue_gemm16_kernel(GemmParams P) {
     }
 }
 
-template <int BM, int BN, int WM, int WN, int NST>
-hipError_t gemm_go(GemmParams P, bool cplx, hipStream_t st) {
-    P.tiles_m = (int)(P.mp / BM);
-    P.tiles_n = (int)(P.np / BN);
-    const int64_t nb = (int64_t)P.tiles_m * P.tiles_n * P.s;
-    const dim3 block(64 * WM * WN);
-    static_assert(NST == 2 || (BM == 256 && BN == 256 && WM == 2 && WN == 4), "the four-stage tile is 256 x 256");
-    if constexpr (NST == 4) {
-        if (cplx)
-            hipLaunchKernelGGL((residue_gemm16_kernel<true>), dim3((unsigned)nb), block, 0, st, P);
-        else
-            hipLaunchKernelGGL((residue_gemm16_kernel<false>), dim3((unsigned)nb), block, 0, st, P);
-    } else {
-        if (cplx)
-            hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, true>), dim3((unsigned)nb), block, 0, st, P);
-        else
-            hipLaunchKernelGGL((residue_gemm_kernel<BM, BN, WM, WN, NST, false>), dim3((unsigned)nb), block, 0, st, P);
+// The 128 x 128 tile on v_mfma_i32_16x16x64_i8: 4 wavefronts of 64 x 64
+// (4 x 4 blocks), two LDS stages, the loads of step k + 1 issued after the
+// barrier that opens step k; several blocks per CU cover each other's waits.
+template <bool CPLX>
+__global__ __launch_bounds__(256, 2) void residue_gemm16s_kernel(GemmParams P) {
+    constexpr int BM = 128, BN = 128, WM = 2, WN = 2, NW = 4;
+    constexpr int WTM = BM / WM, WTN = BN / WN, GM = WTM / 16, GN = WTN / 16;
+    constexpr int LOADS_A = BM * kChunks / 64 / NW, LOADS_B = BN * kChunks / 64 / NW;
+    constexpr int STAGE = (BM + BN) * kBK;
+    __shared__ __attribute__((aligned(1024))) int8_t sS0[STAGE];
+    __shared__ __attribute__((aligned(1024))) int8_t sS1[STAGE];
+    auto stage = [&](int st) -> int8_t* { return st == 0 ? sS0 : sS1; };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wm = wave % WM, wn = wave / WM;
+    int t, tm, tn;
+    block_tile(blockIdx.x, gridDim.x, P.tiles_m, P.tiles_n, t, tm, tn);
+    const uint32_t m = P.mod[t];
+    const double dm = (double)m, rcp = P.rcp[t], half_rcp = 0.5 * rcp;
+    const int64_t kp = P.kp;
+    const int nk = P.k_steps;
+
+    uint32_t goffA[LOADS_A], goffB[LOADS_B];
+#pragma unroll
+    for (int q = 0; q < LOADS_A; ++q) {
+        const int piece = (wave * LOADS_A + q) * 64 + lane;
+        const int row = piece / kChunks, pos = piece % kChunks;
+        goffA[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
     }
+#pragma unroll
+    for (int q = 0; q < LOADS_B; ++q) {
+        const int piece = (wave * LOADS_B + q) * 64 + lane;
+        const int row = piece / kChunks, pos = piece % kChunks;
+        goffB[q] = (uint32_t)(row * kBK + ((pos ^ ((row >> 2) & 3)) << 4));
+    }
+    const int r16 = lane & 15, c16 = lane >> 4;
+    const int sw = (c16 ^ ((r16 >> 2) & 3)) << 4;
+    const int aoff = (wm * WTM + r16) * kBK + sw;
+    const int boff = BM * kBK + (wn * WTN + r16) * kBK + sw;
+    const int64_t row_out0 = (int64_t)tm * BM + wm * WTM + 4 * c16;
+    const int64_t col_out0 = (int64_t)tn * BN + wn * WTN + r16;
+    const int64_t panelA = P.a_rows * kBK, panelB = P.b_rows * kBK;
+
+    v4i acc[GM][GN];
+    v4i fa[GM], fb[GN];
+    uint32_t park[CPLX ? GM : 1][CPLX ? GN : 1];
+
+#pragma unroll 1
+    for (int pass = 0; pass < (CPLX ? 3 : 1); ++pass) {
+        const int8_t* Ag = P.A + pass * P.a_set_stride + (int64_t)t * P.a_rows * kp + (P.k_begin / kBK) * panelA +
+                           (int64_t)tm * BM * kBK;
+        const int8_t* Bg = P.B + pass * P.b_set_stride + (int64_t)t * P.b_rows * kp + (P.k_begin / kBK) * panelB +
+                           (int64_t)tn * BN * kBK;
+        auto issue = [&](int kt, int st) {
+            const int8_t* Ak = Ag + (int64_t)kt * panelA;
+            const int8_t* Bk = Bg + (int64_t)kt * panelB;
+            const uint32_t lds = (uint32_t)(uintptr_t)(lds_ptr_t)stage(st);
+#pragma unroll
+            for (int q = 0; q < LOADS_A; ++q) dma_1k(Ak, goffA[q], lds + (wave_u * LOADS_A + q) * 1024);
+#pragma unroll
+            for (int q = 0; q < LOADS_B; ++q) dma_1k(Bk, goffB[q], lds + BM * kBK + (wave_u * LOADS_B + q) * 1024);
+        };
+#pragma unroll
+        for (int i = 0; i < GM; ++i)
+#pragma unroll
+            for (int j = 0; j < GN; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        issue(0, 0);
+        auto step = [&](int st, int kdma) {
+            // this step's loads have landed and every wave is done with the
+            // other stage; refill it with the next step, then read and multiply
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, true));
+            __syncthreads();
+            issue(kdma, st ^ 1);
+            const int8_t* S = stage(st);
+#pragma unroll
+            for (int i = 0; i < GM; ++i) fa[i] = *(const v4i*)(S + aoff + i * 16 * kBK);
+#pragma unroll
+            for (int j = 0; j < GN; ++j) fb[j] = *(const v4i*)(S + boff + j * 16 * kBK);
+#pragma unroll
+            for (int i = 0; i < GM; ++i)
+#pragma unroll
+                for (int j = 0; j < GN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        };
+#pragma unroll 1
+        for (int kt = 0; kt < nk; kt += 2) {
+            // past the last step the loads repeat the last step (the count per step stays the same)
+            step(0, min(kt + 1, nk - 1));
+            step(1, min(kt + 2, nk - 1));
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, false));
+        __syncthreads();
+
+#pragma unroll
+        for (int i = 0; i < GM; ++i) {
+#pragma unroll
+            for (int j = 0; j < GN; ++j) {
+                const int64_t col = col_out0 + j * 16;
+                const int64_t row = row_out0 + i * 16;
+                uint32_t r[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = acc_mod(acc[i][j][e], dm, rcp, half_rcp);
+                uint8_t* re_dst = P.C + (int64_t)t * P.n * P.mp + col * P.mp + row;
+                if (!CPLX) {
+                    if (col < P.n) *(uint32_t*)re_dst = pack4(r);
+                } else if (pass == 0) {
+                    park[i][j] = pack4(r);
+                } else if (pass == 1) {
+                    const uint32_t t1w = park[i][j];
+                    uint32_t re[4], smv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t r1 = (t1w >> (8 * e)) & 0xffu;
+                        const uint32_t x = r1 + m - r[e];
+                        const uint32_t x1 = x - m;
+                        re[e] = x < x1 ? x : x1;
+                        const uint32_t y = r1 + r[e];
+                        const uint32_t y1 = y - m;
+                        smv[e] = y < y1 ? y : y1;
+                    }
+                    park[i][j] = pack4(smv);
+                    if (col < P.n) *(uint32_t*)re_dst = pack4(re);
+                } else {
+                    const uint32_t swd = park[i][j];
+                    uint32_t im[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t x = r[e] + m - ((swd >> (8 * e)) & 0xffu);
+                        const uint32_t x1 = x - m;
+                        im[e] = x < x1 ? x : x1;
+                    }
+                    if (col < P.n) *(uint32_t*)(re_dst + P.c_set_stride) = pack4(im);
+                }
+            }
+        }
+    }
+}
+
+// big: the 256 x 256 tile on 8 wavefronts; otherwise the 128 x 128 tile on 4
+hipError_t gemm_go(GemmParams P, bool big, bool cplx, hipStream_t st) {
+    const int T = big ? 256 : 128;
+    P.tiles_m = (int)(P.mp / T);
+    P.tiles_n = (int)(P.np / T);
+    const int64_t nb = (int64_t)P.tiles_m * P.tiles_n * P.s;
+    const dim3 grid((unsigned)nb), block(big ? 512 : 256);
+    if (big && cplx)
+        hipLaunchKernelGGL((residue_gemm16_kernel<true>), grid, block, 0, st, P);
+    else if (big)
+        hipLaunchKernelGGL((residue_gemm16_kernel<false>), grid, block, 0, st, P);
+    else if (cplx)
+        hipLaunchKernelGGL((residue_gemm16s_kernel<true>), grid, block, 0, st, P);
+    else
+        hipLaunchKernelGGL((residue_gemm16s_kernel<false>), grid, block, 0, st, P);
     return hipGetLastError();
 }
 
@@ -545,13 +474,12 @@ hipError_t launch_residue_gemm(const GemmParams& P, bool cplx, hipStream_t st) {
         return hipErrorInvalidValue;
     // 256 x 256 tiles on 8 wavefronts with four stages unless the grid is
     // small or the k-loop very short.  Otherwise 128 x 128 tiles on 4
-    // wavefronts with two stages (32 KiB): four blocks per CU, whose epilogues
-    // overlap the others' MFMAs.  Measured at 8192 x k x 8192, s = 8: 9%
-    // faster at k = 256, even at k = 1024, and 22% slower at
+    // wavefronts with two stages (32 KiB of LDS, several blocks per CU, whose
+    // epilogues overlap the others' MFMAs).  Measured at 8192 x k x 8192,
+    // s = 8: faster at k = 256, even at k = 1024, and slower at
     // 16384 x 2048 x 16384 (twice the L2->LDS bytes per MAC).
     const int64_t big_blocks = (P.mp / 256) * (P.np / 256) * P.s;
-    if (big_blocks >= 512 && (int64_t)P.k_steps * kBK > 512) return gemm_go<256, 256, 2, 4, 4>(P, cplx, st);
-    return gemm_go<128, 128, 2, 2, 2>(P, cplx, st);
+    return gemm_go(P, big_blocks >= 512 && (int64_t)P.k_steps * kBK > 512, cplx, st);
 }
 
 }  // namespace oz2

@@ -33,7 +33,7 @@ def gemm_asm(tmp_path_factory):
 
 def _kernels(asm):
     bodies = {}
-    for m in re.finditer(r"^(_Z\w*residue_gemm(?:16)?_kernel\w*):", asm, re.M):
+    for m in re.finditer(r"^(_Z\w*residue_gemm16s?_kernel\w*):", asm, re.M):
         end = asm.index(".Lfunc_end", m.end())
         lines = [l.split(";")[0].strip() for l in asm[m.end():end].split("\n")]
         bodies[m.group(1)] = [l for l in lines if l and not l.startswith(".")]
@@ -55,22 +55,18 @@ def test_m0_written_only_by_the_load_sequence(gemm_asm):
         assert loads and len(loads) == len(writes), name
 
 
-def _template_args(name):
-    # residue_gemm_kernel<BM, BN, WM, WN, NST, CPLX>; residue_gemm16_kernel<CPLX>
-    # is the 256 x 256, 8-wave, four-stage tile
-    if "residue_gemm16_kernel" in name:
-        return 256, 256, 2, 4, 4
-    ints = [int(x) for x in re.findall(r"Li(\d+)E", name)]
-    bm, bn, wm, wn, nst = ints[:5]
-    return bm, bn, wm, wn, nst
+def _shape(name):
+    # residue_gemm16_kernel<CPLX>: the 256 x 256 tile, 8 waves, four stages;
+    # residue_gemm16s_kernel<CPLX>: the 128 x 128 tile, 4 waves, two stages
+    return (256, 256, 8, 4) if "residue_gemm16_kernel" in name else (128, 128, 4, 2)
 
 
 def test_main_loop_keeps_loads_in_flight(gemm_asm):
     kernels = _kernels(gemm_asm)
-    assert {_template_args(n)[4] for n in kernels} == {2, 4}
+    assert {_shape(n)[3] for n in kernels} == {2, 4}
     for name, lines in kernels.items():
-        bm, bn, wm, wn, nst = _template_args(name)
-        loads = (bm + bn) * 4 // (64 * wm * wn)  # 1 KiB loads per wave and step
+        bm, bn, nw, nst = _shape(name)
+        loads = (bm + bn) * 4 // (64 * nw)  # 1 KiB loads per wave and step
         before_barrier = [lines[i - 1] for i, l in enumerate(lines) if l == "s_barrier"]
         counts = [int(m.group(1)) for w in before_barrier for m in [re.search(r"vmcnt\((\d+)\)", w)] if m]
         assert len(counts) == len(before_barrier), (name, before_barrier)
@@ -81,12 +77,11 @@ def test_main_loop_keeps_loads_in_flight(gemm_asm):
             assert counts.count(0) == 1 and counts.count(2 * loads) == len(counts) - 1, (name, counts)
             assert len(counts) == 1 + 2 + 2 * 4 + 1, (name, counts)
         else:
-            # the prologue's NST steps of loads less the first step, then in
-            # each of the NST unrolled k steps the loads of NST - 2 later
-            # steps in flight (none for two stages), then one full drain
-            first = (nst - 1) * loads
-            assert counts.count(first) == 1, (name, counts)
-            assert counts.count(0) == nst + 1, (name, counts)
+            # two stages: the loads of step k + 1 are issued after the barrier
+            # that opens step k, so each barrier waits for all loads (vmcnt(0)):
+            # two per unrolled loop trip and the drain
+            assert counts == [0] * len(counts) and len(counts) == 3, (name, counts)
+        assert all(l.startswith("v_mfma_i32_16x16x64_i8") for l in lines if l.startswith("v_mfma")), name
 
 
 def test_ping_pong_phases(gemm_asm):
@@ -94,7 +89,7 @@ def test_ping_pong_phases(gemm_asm):
     # either a memory phase (a k step's 12 LDS fragment reads and its loads,
     # no MFMA) or a compute phase (the step's 32 16x16x64 MFMAs, no LDS read)
     for name, lines in _kernels(gemm_asm).items():
-        if _template_args(name)[4] != 4:
+        if _shape(name)[3] != 4:
             continue
         bars = [i for i, l in enumerate(lines) if l == "s_barrier"]
         phases = []
@@ -104,8 +99,6 @@ def test_ping_pong_phases(gemm_asm):
             rd = sum(l.startswith("ds_read") for l in seg)
             if mf or rd:
                 phases.append((mf, rd))
-        assert "residue_gemm16_kernel" in name
         loop = [p for p in phases if p in ((32, 0), (0, 12))]
         assert len(loop) >= 8, (name, phases)
         assert all(p in ((32, 0), (0, 12)) for p in phases), (name, phases)
-        assert all(l.startswith("v_mfma_i32_16x16x64_i8") for l in lines if l.startswith("v_mfma")), name
