@@ -387,25 +387,26 @@ struct TilePlan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Time of one block's residue products (us): the per-block model measured on
-// this GPU, about 11 us fixed plus 0.76 us per 64-position k step for a
-// 256 x 256 tile with one block per CU, over waves of 256 CUs; the 128 x 128
-// tile (small grids or short k) runs four blocks per CU at about 1.22 times
-// the time per step.  Complex products run three k-loops per block.
+// Time of one block's residue products (us): the per-block model fitted to
+// measured DGEMMs on this GPU (N = 1024 .. 8192, s = 8, 16, 24), about 19 us
+// fixed plus 0.62 us per 64-position k step for a 256 x 256 tile with one
+// block per CU, over waves of 256 CUs; for the 128 x 128 tile (small grids
+// or short k) about 2.5 us per step per wave of 1024 blocks.  Complex
+// products run three k-loops per block.
 double gemm_block_us(int64_t mb, int64_t nb, int64_t kp, int s, bool cplx) {
     const double steps = (double)kp / kGemmStepK;
     const int64_t mp = round_up(mb, kPadM), np = round_up(nb, kPadM);
     const double passes = cplx ? 3.0 : 1.0;
     const int64_t big = (mp / 256) * (np / 256) * s;
-    if (big >= 512 && kp > 512) return (double)ceil_div(big, 256) * (11.0 + 0.76 * steps * passes);
+    if (big >= 512 && kp > 512) return (double)ceil_div(big, 256) * (19.0 + 0.62 * steps * passes);
     const int64_t small = (mp / 128) * (np / 128) * s;
-    return (double)ceil_div(small, 1024) * (11.0 + 0.93 * steps * passes);
+    return (double)ceil_div(small, 1024) * (0.16 + 2.53 * steps * passes);
 }
 
 // Modelled time of the whole product under a blocking (us): residue products
 // of every block, the scans and encodes (each operand block read once and
-// its planes written once, at about 4.5 TB/s), the reconstructions (the same
-// for every blocking) and about 4 us per kernel launch.
+// its planes written once) and the reconstructions (the same for every
+// blocking) at the fitted 4.6 TB/s, and about 7 us per kernel launch.
 double tile_cost_us(bool cplx, int s, int64_t m, int64_t n, int64_t k, int64_t mb, int64_t nb, bool hold_a,
                     bool prepared) {
     const int64_t kp = round_up(k, kPadK);
@@ -426,7 +427,7 @@ double tile_cost_us(bool cplx, int s, int64_t m, int64_t n, int64_t k, int64_t m
         launches += 4 * (hold_a ? br + br * bc : bc + br * bc);
     }
     const double crt_bytes = (outs * s + 8.0 * w) * (double)m * n;
-    return gemm + enc_bytes / 4.5e6 + crt_bytes / 4.0e6 + 4.0 * (double)launches;
+    return gemm + enc_bytes / 4.6e6 + crt_bytes / 4.6e6 + 7.0 * (double)launches;
 }
 
 // Cheapest blocking whose workspace fits `cap`: block sides are the whole
