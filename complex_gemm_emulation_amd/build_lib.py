@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liboz2.so")
 SOURCES = ["oz2_api.cpp", "oz2_plan.cpp", "oz2_chain_plan.cpp", "oz2_kernels.hip", "oz2_gemm.hip",
-           "oz2_small.hip", "oz2_chain.hip", "oz2_scratch.hip"]
+           "oz2_small.hip", "oz2_chain.hip", "oz2_chain_hbm.hip", "oz2_scratch.hip"]
 # HBM stream kernels that the bench times as bandwidth ceilings (not the method)
 STREAM_LIB = os.path.join(HERE, "liboz2_stream.so")
 STREAM_SOURCES = ["oz2_stream.hip"]

@@ -13,6 +13,8 @@
 
 #include <cstdio>
 #include <cstring>
+#include <new>
+#include <vector>
 
 #include "oz2.h"
 #include "oz2_internal.h"
@@ -62,6 +64,8 @@ struct oz2_context {
     // operand's encoded block was kept across the other's blocks
     int64_t tile_mb = 0, tile_nb = 0;
     int tile_held = OZ2_TILE_UNTILED;
+    // which kernels run a persistent chain (OZ2_CHAIN_KERNEL_*)
+    int chain_kernel = OZ2_CHAIN_KERNEL_AUTO;
 };
 
 // a scanned and encoded operand kept on the device between products
@@ -76,11 +80,15 @@ struct oz2_operand {
     int8_t* planes = nullptr;  // [sets][s][kp/64][rows_pad][64]
 };
 
-// a planned persistent tensor-mode chain: the kernel's tables and the
-// operator residues on the device
+// a planned persistent tensor-mode chain: the kernels' tables and the
+// operator residues on the device, in the layouts of both chain kernels
+// (the LDS kernel's only for n <= 16)
 struct oz2_chain_plan {
     ChainParams params;        // b, g, Qd and device pointers; X, Y, batch per call
-    void* mem = nullptr;       // device: ChainTables, then the operator residues
+    void* mem = nullptr;       // device: ChainTables, LDS-kernel residues, fexp, HBM-kernel residues
+    int np = 0, ap = 0;        // n rounded up to 8 (plane padding) and to 16 (operator rows)
+    const int* fexp = nullptr;     // device [3][np] row exponents left pending on each direction
+    const int8_t* hops = nullptr;  // device [d][s][ap][np] operator residues of the HBM kernels
 };
 
 namespace {
@@ -951,7 +959,7 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
 int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* const* ops, const int* modes,
                           int num_moduli, oz2_chain_plan_t* out) {
     if (!h) return -1;
-    if (n < 1 || n > kChainN) return -2;
+    if (n < 1 || n > kChainMaxN) return -2;
     if (depth < 1 || depth > kChainMaxD) return -3;
     if (!ops) return -4;
     for (int i = 0; i < depth; ++i)
@@ -964,37 +972,66 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     if (num_moduli < kMinS || num_moduli > kChainMaxS) return -6;
     if (!out) return -7;
     *out = nullptr;
+    const int nn = (int)n, s = num_moduli;
     oz2_chain_plan* plan = new (std::nothrow) oz2_chain_plan();
     if (!plan) return OZ2_STATUS_ALLOC_FAILED;
-    const size_t ops_bytes = (size_t)depth * kChainMaxS * kChainN * kChainN;
-    const size_t off_ops = align_up(sizeof(ChainTables));
-    struct Host {
-        ChainTables tab;
-        int8_t ops[kChainMaxD * kChainMaxS * kChainN * kChainN];
-    };
-    Host* host = new (std::nothrow) Host();
-    if (!host) {
-        delete plan;
-        return OZ2_STATUS_ALLOC_FAILED;
+    plan->np = (nn + 7) & ~7;
+    plan->ap = (plan->np + 15) & ~15;
+    const int np = plan->np, ap = plan->ap;
+    const bool lds = nn <= kChainN;
+    const size_t lds_bytes = lds ? (size_t)depth * kChainMaxS * kChainN * kChainN : 0;
+    const size_t hops_bytes = (size_t)depth * s * ap * np;
+    const size_t off_lds = align_up(sizeof(ChainTables));
+    const size_t off_fexp = align_up(off_lds + lds_bytes);
+    const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
+    const size_t total = off_hops + hops_bytes;
+    std::vector<char> host;
+    std::vector<int8_t> res;
+    std::vector<int> fexp;
+    int st = OZ2_STATUS_SUCCESS;
+    try {
+        host.assign(total, 0);
+        res.resize((size_t)depth * s * nn * nn);
+        fexp.resize((size_t)3 * nn);
+    } catch (...) {
+        st = OZ2_STATUS_ALLOC_FAILED;
     }
-    int st = chain_plan(num_moduli, (int)n, depth, ops, dirs, &plan->params, &host->tab, host->ops);
-    if (st < 0) st = -4;  // a non-finite operator entry
-    if (!st && hipMalloc(&plan->mem, off_ops + ops_bytes) != hipSuccess) {
+    if (!st) {
+        ChainTables* tab = (ChainTables*)host.data();
+        st = chain_plan(s, nn, depth, ops, dirs, &plan->params, tab, res.data(), fexp.data());
+        if (st < 0) st = -4;  // a non-finite operator entry
+    }
+    if (!st) {
+        // the LDS kernel: [d][kChainMaxS][16][16] by modulus index, zero padded
+        int8_t* lo = (int8_t*)(host.data() + off_lds);
+        int* fe = (int*)(host.data() + off_fexp);
+        int8_t* ho = (int8_t*)(host.data() + off_hops);
+        for (int i = 0; i < depth; ++i)
+            for (int q = 0; q < s; ++q)
+                for (int a = 0; a < nn; ++a)
+                    for (int k = 0; k < nn; ++k) {
+                        const int8_t v = res[(((size_t)i * s + q) * nn + a) * nn + k];
+                        if (lds) lo[(((size_t)i * kChainMaxS + q) * kChainN + a) * kChainN + k] = v;
+                        ho[(((size_t)i * s + q) * ap + a) * np + k] = v;  // [d][s][ap][np], zero padded
+                    }
+        for (int m = 0; m < 3; ++m)
+            for (int a = 0; a < nn; ++a) fe[m * np + a] = fexp[(size_t)m * nn + a];
+    }
+    if (!st && hipMalloc(&plan->mem, total) != hipSuccess) {
         (void)hipGetLastError();
         plan->mem = nullptr;
         st = OZ2_STATUS_ALLOC_FAILED;
     }
-    if (!st && (hipMemcpy(plan->mem, &host->tab, sizeof(ChainTables), hipMemcpyHostToDevice) != hipSuccess ||
-                hipMemcpy((char*)plan->mem + off_ops, host->ops, ops_bytes, hipMemcpyHostToDevice) != hipSuccess))
-        st = OZ2_STATUS_HIP_ERROR;
-    delete host;
+    if (!st && hipMemcpy(plan->mem, host.data(), total, hipMemcpyHostToDevice) != hipSuccess) st = OZ2_STATUS_HIP_ERROR;
     if (st) {
         if (plan->mem) (void)hipFree(plan->mem);
         delete plan;
         return st;
     }
     plan->params.tab = (const float*)plan->mem;
-    plan->params.ops = (const int8_t*)((char*)plan->mem + off_ops);
+    plan->params.ops = lds ? (const int8_t*)((char*)plan->mem + off_lds) : nullptr;
+    plan->fexp = (const int*)((char*)plan->mem + off_fexp);
+    plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
     *out = plan;
     return OZ2_STATUS_SUCCESS;
 }
@@ -1008,6 +1045,84 @@ int oz2_chain_plan_info(oz2_chain_plan_t plan, int* depth, int* b, int* g) {
     return OZ2_STATUS_SUCCESS;
 }
 
+namespace {
+
+// The chain on HBM-resident residue planes (oz2_chain_hbm.hip): per batch
+// of tensors that fits the workspace, a scan, the encode, one kernel per
+// product.  Phase times: scan, encode, the rescaling products, the last
+// product with the reconstruction (with several batches: all in the third).
+int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, double* Y, int64_t batch) {
+    const ChainParams& C = plan->params;
+    const int n = C.n, np = plan->np, s = C.s;
+    const int64_t np3 = (int64_t)np * np * np, n3 = (int64_t)n * n * n;
+    const size_t per_tensor = 2 * (size_t)s * np3 + sizeof(unsigned long long);
+    const size_t fixed = 3 * 256;  // alignment of the three parts
+    int64_t chunk = batch;
+    size_t cap = 0;
+    if (!fits(h, fixed + per_tensor * (size_t)batch, &cap)) {
+        chunk = cap > fixed ? (int64_t)((cap - fixed) / per_tensor) : 0;
+        if (chunk < 1) return OZ2_STATUS_WORKSPACE_LIMIT;
+        // equal batches
+        const int64_t parts = (batch + chunk - 1) / chunk;
+        chunk = (batch + parts - 1) / parts;
+    }
+    const size_t off_b0 = align_up(sizeof(unsigned long long) * (size_t)chunk);
+    const size_t off_b1 = align_up(off_b0 + (size_t)s * chunk * np3);
+    const size_t bytes = off_b1 + (size_t)s * chunk * np3;
+    int st = ensure_workspace(h, bytes);
+    if (st) return st;
+    char* ws = workspace(h);
+    hipStream_t stm = h->stream;
+    const bool timed = h->timing && chunk == batch;
+    if (h->timing && !timed)
+        for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
+    for (int64_t t0 = 0; t0 < batch; t0 += chunk) {
+        const int64_t nb = batch - t0 < chunk ? batch - t0 : chunk;
+        ChainHbmParams P{};
+        P.X = X + t0 * n3;
+        P.Y = Y + t0 * n3;
+        P.batch = nb;
+        P.n = n;
+        P.np = np;
+        P.s = s;
+        P.b = C.b;
+        P.m0 = C.m0;
+        for (int j = 0; j < 3; ++j) P.fin[j] = C.fin[j];
+        P.Qd = C.Qd;
+        P.tab = C.tab;
+        P.fexp = plan->fexp;
+        P.smax = (unsigned long long*)ws;
+        P.pstride = nb * np3;
+        int8_t* buf[2] = {(int8_t*)(ws + off_b0), (int8_t*)(ws + off_b1)};
+        if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[0], stm));
+        OZ2_LAUNCH(launch_fill_u64((uint64_t*)P.smax, nb, 0, stm));
+        OZ2_LAUNCH(launch_chain_scan(P, stm));
+        if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
+        P.out = buf[0];
+        OZ2_LAUNCH(launch_chain_encode(P, stm));
+        if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
+        for (int i = 0; i < C.d; ++i) {
+            const bool last = i == C.d - 1;
+            if (last && timed) OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
+            P.in = buf[i & 1];
+            P.out = last ? nullptr : buf[(i + 1) & 1];
+            P.g = C.g[i];
+            P.kind = C.kind[i];
+            P.ops = plan->hops + (size_t)i * s * plan->ap * np;
+            OZ2_LAUNCH(launch_chain_step(P, last, stm));
+        }
+        if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
+    }
+    if (h->timing && !timed) {
+        OZ2_LAUNCH(hipEventRecord(h->ev[3], stm));
+        OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
+    }
+    h->timed = h->timing != 0;
+    return OZ2_STATUS_SUCCESS;
+}
+
+}  // namespace
+
 int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X, double* Y, int64_t batch) {
     if (!h) return -1;
     if (!plan) return -2;
@@ -1016,12 +1131,16 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
     if (batch == 0) return OZ2_STATUS_SUCCESS;
     if (!X) return -3;
     if (!Y) return -4;
+    const bool lds = h->chain_kernel == OZ2_CHAIN_KERNEL_LDS ||
+                     (h->chain_kernel == OZ2_CHAIN_KERNEL_AUTO && plan->params.n <= kChainN);
+    if (lds && plan->params.n > kChainN) return OZ2_STATUS_NOT_SUPPORTED;
+    h->last.valid = false;
+    if (!lds) return chain_hbm(h, plan, X, Y, batch);
     ChainParams P = plan->params;
     P.X = X;
     P.Y = Y;
     P.batch = batch;
     hipStream_t stm = h->stream;
-    h->last.valid = false;
     if (h->timing)
         for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
     OZ2_LAUNCH(launch_chain(P, stm));
@@ -1030,6 +1149,13 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
         OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
         h->timed = true;
     }
+    return OZ2_STATUS_SUCCESS;
+}
+
+int oz2_set_chain_kernel(oz2_handle_t h, int kernel) {
+    if (!h) return -1;
+    if (kernel < OZ2_CHAIN_KERNEL_AUTO || kernel > OZ2_CHAIN_KERNEL_HBM) return -2;
+    h->chain_kernel = kernel;
     return OZ2_STATUS_SUCCESS;
 }
 

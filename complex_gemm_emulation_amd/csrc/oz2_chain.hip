@@ -34,125 +34,19 @@
 // chain visiting the directions in turn needs; the final store undoes the
 // rotation.  The operators' residues cycle through three LDS slots.
 //
-// Moduli sit right-aligned in 16 slots, descending, so that the smallest
-// (the ones dropped) are always slots 15, 14, ... at compile time; unused
-// leading slots carry the modulus 1, which leaves every mixed-radix step,
-// weight and Horner step unchanged.  All modular arithmetic is on exact
-// small integers held as floats: [x]_m = x - m floor(x / m + 1/2), with
-// fl32(x * fl32(1/m)) close enough to x/m that the floor is exact for odd m
-// (|x| < 2^19 here), and exact outright for m = 256.
-#include "oz2_internal.h"
+// The per-entry residue arithmetic (drops, mixed-radix digits, base
+// extension, Horner) is shared with the HBM-resident kernels for larger
+// tensors (oz2_chain_device.h).
+#include "oz2_chain_device.h"
 
 namespace oz2 {
 namespace {
 
+using namespace chain;
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int kSlots = kChainMaxS;  // 16
 constexpr int kPlane = kChainN * kChainN * kChainN;  // 4096 entries per residue plane
-
-__device__ __forceinline__ float cmod(float x, float m, float rm) {
-    return fmaf(-m, floorf(fmaf(x, rm, 0.5f)), x);
-}
-
-// the same reduction of x - 128, offset by 128: [x - 128]_m + 128 in
-// [0, 255] for m <= 256 (oh = fl32(1/2 - 128 fl32(1/m)); the floor argument
-// is within 2^-5 / m + 2^-12 of (x - 128) / m + 1/2, and exact for m = 256
-// and m = 1), the offset-binary byte that v_cvt_pk_u8_f32 packs
-__device__ __forceinline__ float cmod128(float x, float m, float rm, float oh) {
-    return fmaf(-m, floorf(fmaf(x, rm, oh)), x);
-}
-
-// centred residue of an integer-valued double |v| <= 2^53 modulo an odd m
-// (the quotient estimate can be one off; two corrections bring r into range)
-__device__ __forceinline__ float dmod_odd(double v, double m, double rm) {
-    const double q = rint(v * rm);
-    double r = fma(-m, q, v);  // exact: |r| < 2m
-    const double h = 0.5 * (m - 1.0);
-    r = r > h ? r - m : r;
-    r = r < -h ? r + m : r;
-    return (float)r;
-}
-
-// byte `e` of a word of four offset-binary residues, as a float: the
-// residue plus 128 (v_cvt_f32_ubyte)
-__device__ __forceinline__ float unpack128(uint32_t w, int e) {
-    return (float)((w >> (8 * e)) & 0xffu);
-}
-
-// four centred residues (exact integers held as floats) as one word
-__device__ __forceinline__ uint32_t pack4(float r0, float r1, float r2, float r3) {
-    return ((uint32_t)(int)r0 & 0xffu) | (((uint32_t)(int)r1 & 0xffu) << 8) |
-           (((uint32_t)(int)r2 & 0xffu) << 16) | (((uint32_t)(int)r3 & 0xffu) << 24);
-}
-
-// After a non-final mode, for the four entries of a lane: RnsDrop g times
-// (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), store
-// the kept slots, MrcDigits on them and BaseExtend to the dropped slots
-// (Algorithm 4, Eq. 26), storing those too.  Every slot loop is unrolled;
-// with G >= 0 the drop count is a compile-time constant and the guards
-// fold away, with G < 0 it is g_rt and the guards are uniform branches.
-// Unused leading slots (modulus 1) hold zeros after every step; they are
-// stored like the others, and their zero operators make them inert.
-// at: this lane's word of slot 0 in the plane buffer.
-// the four entries of a lane into one plane: contiguous (step 0, one 32-bit
-// store) or step bytes apart (byte stores; only with ANY layouts)
-template <bool ANY>
-__device__ __forceinline__ void store4(int8_t* p, int step, float r0, float r1, float r2, float r3) {
-    if (!ANY || step == 0) {
-        *(uint32_t*)p = pack4(r0, r1, r2, r3);
-    } else {
-        p[0] = (int8_t)(int)r0;
-        p[step] = (int8_t)(int)r1;
-        p[2 * step] = (int8_t)(int)r2;
-        p[3 * step] = (int8_t)(int)r3;
-    }
-}
-
-template <int G, bool ANY>
-__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, int8_t* at,
-                                               int step) {
-    const int g = G >= 0 ? G : g_rt;
-    const int keep = kSlots - 1 - g;  // last slot of the reduced basis
-#pragma unroll
-    for (int qs = kSlots - 1; qs > 0; --qs)
-        if (qs > keep) {
-#pragma unroll
-            for (int p = 0; p < qs; ++p) {
-                const float iv = T->inv[qs][p], m = T->mod[p], rm = T->rmod[p];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
-            }
-        }
-#pragma unroll
-    for (int u = 0; u < kSlots; ++u)
-        if (u <= keep) store4<ANY>(at + u * kPlane, step, r[0][u], r[1][u], r[2][u], r[3][u]);
-    // mixed-radix digits of the kept residues, in place
-#pragma unroll
-    for (int i = 0; i < kSlots - 1; ++i)
-#pragma unroll
-        for (int j = i + 1; j < kSlots; ++j)
-            if (j <= keep) {
-                const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e][j] = cmod((r[e][j] - r[e][i]) * iv, m, rm);
-            }
-#pragma unroll
-    for (int p = 1; p < kSlots; ++p)
-        if (p > keep) {
-            float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int i = 0; i < kSlots - 1; ++i)
-                if (i <= keep) {
-                    const float w = T->omega[i][p];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
-                }
-            const float m = T->mod[p], rm = T->rmod[p];
-            store4<ANY>(at + p * kPlane, step, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm),
-                        cmod(ts[3], m, rm));
-        }
-}
 
 // residue products of one 16-fibre tile for every slot, reduced modulo the
 // slot's modulus and packed: pk[u] holds the four entries of this lane
@@ -175,12 +69,8 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int u = u0 + v;
-            const float m = T->mod[u], rm = T->rmod[u], oh = T->ohalf[u];
-            uint32_t w = 0u;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) w = __builtin_amdgcn_cvt_pk_u8_f32(cmod128((float)acc[v][q], m, rm, oh), q, w);
-            pk[u] = w;
+            const int a4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
+            pk[u0 + v] = pack_products(a4, T, u0 + v);
         }
     }
 }
@@ -192,24 +82,26 @@ __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint3
     // offset by 128; the first drop's differences remove the offset from
     // every kept slot, and without drops it is subtracted here
     float r[4][kSlots];
-#pragma unroll
-    for (int u = 0; u < kSlots; ++u)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) r[q][u] = unpack128(pk[u], q);
+    unpack_tile(pk, r);
     if (G0 < 0 && g[mode] == 0) {
 #pragma unroll
         for (int u = 0; u < kSlots; ++u)
 #pragma unroll
             for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
     }
+    // unused leading slots (modulus 1) hold zeros after every step; they are
+    // stored like the others, and their zero operators make them inert
+    const auto put = [&](int u, float r0, float r1, float r2, float r3) {
+        store4<ANY>(at + u * kPlane, step, r0, r1, r2, r3);
+    };
     if (G0 >= 0 && G0 == G1)
-        rescale_extend<G0, ANY>(0, r, T, at, step);
+        rescale_extend<G0>(0, r, T, put);
     else if (G0 >= 0 && mode == 0)
-        rescale_extend<G0, ANY>(0, r, T, at, step);
+        rescale_extend<G0>(0, r, T, put);
     else if (G0 >= 0)
-        rescale_extend<G1, ANY>(0, r, T, at, step);
+        rescale_extend<G1>(0, r, T, put);
     else
-        rescale_extend<-1, ANY>(g[mode], r, T, at, step);
+        rescale_extend<-1>(g[mode], r, T, put);
 }
 
 // G0, G1: the drop counts after products 1 and 2 when fixed at compile time
@@ -360,32 +252,8 @@ void chain_kernel(ChainParams P) {
         const int t = wave + 8 * tt;
         uint32_t pk[kSlots];
         tile_products(buf, ops[(d - 1) % 3], T, t, a, kq, pk);
-        // offset by 128: the first digit step's differences remove it from
-        // slots 1..; slot 0, the first digit itself, loses it after the steps
-        float dg[4][kSlots];
-#pragma unroll
-        for (int u = 0; u < kSlots; ++u)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][u] = unpack128(pk[u], q);
-#pragma unroll
-        for (int i = 0; i < kSlots - 1; ++i)
-#pragma unroll
-            for (int j = i + 1; j < kSlots; ++j) {
-                const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
-            }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
         double V[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) V[q] = (double)dg[q][kSlots - 1];
-#pragma unroll
-        for (int j = kSlots - 2; j >= 0; --j) {
-            const double m = (double)T->mod[j];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)dg[q][j]);
-        }
+        mrc_horner(pk, T, V);
         // the values are complete here (the compiler would otherwise sink
         // each entry's whole digit computation into its guarded store)
 #pragma unroll

@@ -1,0 +1,181 @@
+// oz2_chain_device.h -- per-entry residue arithmetic of the persistent
+// tensor-mode chain (OzII-RescaleBE), shared by its two kernels: the
+// one-block-per-tensor kernel with residues in LDS (oz2_chain.hip, n <= 16)
+// and the HBM-resident kernels for larger tensors (oz2_chain_hbm.hip).
+//
+// "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products":
+//  - Sec. 2.3 Eq. (11): centred residues, [v]_m in [-floor(m/2), ceil(m/2) - 1];
+//  - Sec. 2.3.1 Eq. (15), Algorithm 1 (RnsDrop): dropping the modulus q maps
+//    the residue r_p of every other modulus p to [(r_p - r_q) q^{-1}]_p;
+//  - Sec. 4.4 Eq. (24)-(26), Algorithm 4 (MrcDigits, BaseExtend): centred
+//    mixed-radix digits by successive elimination and the residues on the
+//    dropped moduli from the weights omega_{i,p} = [prod_{l<i} m_l]_p;
+//  - Algorithm 5 (ReconstructFP64): FP64 Horner over the digits.
+//
+// Moduli sit right-aligned in kChainMaxS slots, descending, so the smallest
+// (the ones dropped) are always the last slots; unused leading slots carry
+// the modulus 1, which leaves every mixed-radix step, weight and Horner step
+// unchanged.  A lane works on four entries at once, so one read of a table
+// entry serves four modular steps.  All modular arithmetic is on exact small
+// integers held as floats: [x]_m = x - m floor(x fl32(1/m) + 1/2), exact for
+// odd m while |x| < 2^19 and for m = 256 outright.
+#pragma once
+
+#include "oz2_internal.h"
+
+namespace oz2 {
+namespace chain {
+
+constexpr int kSlots = kChainMaxS;  // 16
+
+__device__ __forceinline__ float cmod(float x, float m, float rm) {
+    return fmaf(-m, floorf(fmaf(x, rm, 0.5f)), x);
+}
+
+// the same reduction of x - 128, offset by 128: [x - 128]_m + 128 in
+// [0, 255] for m <= 256 (oh = fl32(1/2 - 128 fl32(1/m)); the floor argument
+// is within 2^-5 / m + 2^-12 of (x - 128) / m + 1/2, and exact for m = 256
+// and m = 1), the offset-binary byte that v_cvt_pk_u8_f32 packs
+__device__ __forceinline__ float cmod128(float x, float m, float rm, float oh) {
+    return fmaf(-m, floorf(fmaf(x, rm, oh)), x);
+}
+
+// centred residue of an integer-valued double |v| <= 2^53 modulo an odd m
+// (the quotient estimate can be one off; two corrections bring r into range)
+__device__ __forceinline__ float dmod_odd(double v, double m, double rm) {
+    const double q = rint(v * rm);
+    double r = fma(-m, q, v);  // exact: |r| < 2m
+    const double h = 0.5 * (m - 1.0);
+    r = r > h ? r - m : r;
+    r = r < -h ? r + m : r;
+    return (float)r;
+}
+
+// byte `e` of a word of four offset-binary residues, as a float: the
+// residue plus 128 (v_cvt_f32_ubyte)
+__device__ __forceinline__ float unpack128(uint32_t w, int e) {
+    return (float)((w >> (8 * e)) & 0xffu);
+}
+
+// four centred residues (exact integers held as floats) as one word
+__device__ __forceinline__ uint32_t pack4(float r0, float r1, float r2, float r3) {
+    return ((uint32_t)(int)r0 & 0xffu) | (((uint32_t)(int)r1 & 0xffu) << 8) |
+           (((uint32_t)(int)r2 & 0xffu) << 16) | (((uint32_t)(int)r3 & 0xffu) << 24);
+}
+
+// the four entries of a lane into one plane: contiguous (step 0, one 32-bit
+// store) or step bytes apart (byte stores; only when ANY)
+template <bool ANY, class I>
+__device__ __forceinline__ void store4(int8_t* p, I step, float r0, float r1, float r2, float r3) {
+    if (!ANY || step == 0) {
+        *(uint32_t*)p = pack4(r0, r1, r2, r3);
+    } else {
+        p[0] = (int8_t)(int)r0;
+        p[step] = (int8_t)(int)r1;
+        p[2 * step] = (int8_t)(int)r2;
+        p[3 * step] = (int8_t)(int)r3;
+    }
+}
+
+// the four accumulators of a 16 x 16 MFMA tile of slot u (each offset by the
+// accumulator input 128), reduced modulo the slot's modulus and packed as
+// offset-binary bytes
+__device__ __forceinline__ uint32_t pack_products(const int (&acc)[4], const ChainTables* T, int u) {
+    const float m = T->mod[u], rm = T->rmod[u], oh = T->ohalf[u];
+    uint32_t w = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w = __builtin_amdgcn_cvt_pk_u8_f32(cmod128((float)acc[q], m, rm, oh), q, w);
+    return w;
+}
+
+// the four entries of every slot as floats, still offset by 128
+__device__ __forceinline__ void unpack_tile(const uint32_t (&pk)[kSlots], float (&r)[4][kSlots]) {
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q][u] = unpack128(pk[u], q);
+}
+
+// After a non-final product, for the four entries of a lane: RnsDrop g times
+// (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), store
+// the kept slots, MrcDigits on them and BaseExtend to the dropped slots
+// (Algorithm 4, Eq. 26), storing those too.  Every slot loop is unrolled;
+// with G >= 0 the drop count is a compile-time constant and the guards fold
+// away, with G < 0 it is g_rt and the guards are uniform branches.  The
+// residues come in offset by 128: the first drop's differences remove the
+// offset from every kept slot (with no drop the caller removes it).
+// put(u, r0, r1, r2, r3) stores slot u's four entries.
+template <int G, class Put>
+__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, const Put& put) {
+    const int g = G >= 0 ? G : g_rt;
+    const int keep = kSlots - 1 - g;  // last slot of the reduced basis
+#pragma unroll
+    for (int qs = kSlots - 1; qs > 0; --qs)
+        if (qs > keep) {
+#pragma unroll
+            for (int p = 0; p < qs; ++p) {
+                const float iv = T->inv[qs][p], m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
+            }
+        }
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u)
+        if (u <= keep) put(u, r[0][u], r[1][u], r[2][u], r[3][u]);
+    // mixed-radix digits of the kept residues, in place
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+#pragma unroll
+        for (int j = i + 1; j < kSlots; ++j)
+            if (j <= keep) {
+                const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e][j] = cmod((r[e][j] - r[e][i]) * iv, m, rm);
+            }
+#pragma unroll
+    for (int p = 1; p < kSlots; ++p)
+        if (p > keep) {
+            float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < kSlots - 1; ++i)
+                if (i <= keep) {
+                    const float w = T->omega[i][p];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
+                }
+            const float m = T->mod[p], rm = T->rmod[p];
+            put(p, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm), cmod(ts[3], m, rm));
+        }
+}
+
+// ReconstructFP64's integer part (Algorithm 5) for the four entries of a
+// lane: centred mixed-radix digits of the residues of every slot (offset by
+// 128 on entry: the first digit step's differences remove it from slots
+// 1 ..; slot 0, the first digit itself, loses it after the steps), then the
+// FP64 Horner sum V = d_0 + m_0 (d_1 + m_1 (...)), each step one rounding of
+// the exact value.
+__device__ __forceinline__ void mrc_horner(const uint32_t (&pk)[kSlots], const ChainTables* T, double (&V)[4]) {
+    float dg[4][kSlots];
+    unpack_tile(pk, dg);
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+#pragma unroll
+        for (int j = i + 1; j < kSlots; ++j) {
+            const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
+        }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) V[q] = (double)dg[q][kSlots - 1];
+#pragma unroll
+    for (int j = kSlots - 2; j >= 0; --j) {
+        const double m = (double)T->mod[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)dg[q][j]);
+    }
+}
+
+}  // namespace chain
+}  // namespace oz2

@@ -1,0 +1,320 @@
+// oz2_chain_hbm.hip -- persistent Ozaki scheme II for chained tensor mode
+// products (OzII-RescaleBE) on tensors too large for one block's LDS
+// (n > 16): the residue planes stay in HBM between the products, one kernel
+// per product.
+//
+// "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products":
+//  - Sec. 5.2 and Algorithm 7: the tensor is encoded once with one exponent,
+//    multiplied mode after mode on its residue planes, rescaled by g_i moduli
+//    (Algorithm 1, Eq. 15) and base-extended (Algorithm 4, Eq. 26) after each
+//    non-final product, and reconstructed once;
+//  - Algorithm 5: Encode (the exponent from the tensor's largest magnitude,
+//    rounding to nearest, ties to even), ToRns and ReconstructFP64 (centred
+//    mixed-radix digits, FP64 Horner, scaling by alpha * Gamma, Eq. 28);
+//  - Sec. 2.3 Eq. (11): centred residues.
+// The chain page runs its method as batched GEMMs and elementwise kernels
+// over HBM-resident residues (Sec. 5.2); here each product and its
+// rescaling are one kernel.
+//
+// Launches for a chain of depth d: a scan (the largest |x| of each tensor),
+// the encode (all s residue planes of every tensor), d - 1 rescaling
+// products (planes in, planes out: two buffers in turn) and the last
+// product with the reconstruction (planes in, FP64 out).
+//
+// Plane layout: every direction is padded to np = n rounded up to 8, and a
+// tensor occupies np^3 bytes of each plane, position (p0, p1, p2) at
+// p0 + np p1 + np^2 p2 with p0 the direction the next product contracts.
+// Fibre f = p1 + np p2 (np^2 per tensor) is then the row of np bytes at
+// f np, and a product is, per modulus, Y^T = R^T Abar^T on
+// v_mfma_i32_16x16x32_i8: a wavefront takes 16 fibres (the MFMA's rows;
+// each lane loads 8 bytes of one row) against 16 operator rows (the MFMA's
+// columns) and loops over the operator's rows in tiles of 16, so a fibre
+// tile is read from HBM once and from cache for the other row tiles.  Each
+// lane then holds four consecutive fibres of one output row for every
+// modulus, and reduces, rescales and base-extends them in registers with the
+// arithmetic of the LDS kernel (oz2_chain_device.h).  The output layout puts
+// the next product's direction at p0: with the directions in turn that is
+// the fibres' p1, so the lane's four entries are four consecutive bytes of
+// every output plane.
+//
+// Padding never reaches a result: the encode writes residues of zero there,
+// the operators' columns k >= n are zero (whatever a padded position holds
+// is multiplied by zero), outputs of padded fibres go to padded positions,
+// operator rows beyond np are not stored, and the reconstruction stores only
+// positions < n.
+#include "oz2_chain_device.h"
+
+namespace oz2 {
+namespace {
+
+using namespace chain;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kScanChunk = 4096;      // entries of one tensor per scan block
+constexpr int kStepBlocksMax = 2048;  // blocks of the product kernels (8 per CU), each looping over tiles
+
+constexpr unsigned long long kInfBits = 0x7ff0000000000000ull;
+
+// exponent e = b - E of a tensor whose largest |x| has the bit pattern M
+// (2^(E-1) <= max|x| < 2^E), 0 for an all-zero tensor
+__device__ __forceinline__ int tensor_exponent(unsigned long long M, int b) {
+    if (!M) return 0;
+    int E = 0;
+    (void)frexp(__longlong_as_double((long long)M), &E);
+    return b - E;
+}
+
+// ---------------------------------------------------------------- scan
+// the largest |x| bit pattern of each tensor (positive doubles order as
+// their bit patterns; non-finite entries give a pattern >= kInfBits)
+__global__ __launch_bounds__(256) void chain_scan_kernel(const double* __restrict__ X, int64_t n3, int64_t chunks,
+                                                         unsigned long long* smax) {
+    __shared__ unsigned long long bm;
+    const int64_t t = blockIdx.x / chunks, c = blockIdx.x % chunks;
+    if (threadIdx.x == 0) bm = 0;
+    __syncthreads();
+    const double* x = X + t * n3;
+    unsigned long long mx = 0;
+#pragma unroll
+    for (int j = 0; j < kScanChunk / 256; ++j) {
+        const int64_t i = c * kScanChunk + j * 256 + threadIdx.x;
+        if (i < n3) {
+            const unsigned long long v = (unsigned long long)__double_as_longlong(x[i]) & 0x7fffffffffffffffull;
+            mx = v > mx ? v : mx;
+        }
+    }
+    atomicMax(&bm, mx);
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(&smax[t], bm);
+}
+
+// -------------------------------------------------------------- encode
+// four consecutive positions p0 .. p0 + 3 of one tensor per thread, every
+// modulus: x (zero at padding and for a tensor with a non-finite entry,
+// whose result the reconstruction sets to NaN), xbar = rint(2^e x), its
+// centred residues packed into one 32-bit word per plane
+__global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, int64_t bpt) {
+    const int n = P.n, np = P.np;
+    const int64_t np3 = (int64_t)np * np * np;
+    const int64_t t = blockIdx.x / bpt;
+    const int64_t i4 = ((blockIdx.x % bpt) * 256 + threadIdx.x) * 4;
+    if (i4 >= np3) return;
+    const int p0 = (int)(i4 % np);
+    const int64_t rest = i4 / np;
+    const int p1 = (int)(rest % np), p2 = (int)(rest / np);
+    const unsigned long long M = P.smax[t];
+    const bool finite = M < kInfBits;
+    const int e = finite ? tensor_exponent(M, P.b) : 0;
+    const int d0 = P.m0, d1 = (P.m0 + 1) % 3, d2 = (P.m0 + 2) % 3;
+    const int64_t nn = (int64_t)n * n;
+    const int64_t sd0 = d0 == 0 ? 1 : d0 == 1 ? n : nn;
+    const int64_t sd1 = d1 == 0 ? 1 : d1 == 1 ? n : nn;
+    const int64_t sd2 = d2 == 0 ? 1 : d2 == 1 ? n : nn;
+    const double* x = P.X + t * n * nn + p1 * sd1 + p2 * sd2;
+    double xb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const bool in = finite && p0 + q < n && p1 < n && p2 < n;
+        xb[q] = in ? rint(ldexp(x[(p0 + q) * sd0], e)) : 0.0;  // |xb| <= 2^b
+    }
+    const ChainTables* T = (const ChainTables*)P.tab;
+    const int first = kSlots - P.s;
+    int8_t* out = P.out + t * np3 + i4;
+    // modulus 256 (index 0): the low byte of the two's-complement integer
+    uint32_t w = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w |= ((uint32_t)(int64_t)xb[q] & 0xffu) << (8 * q);
+    *(uint32_t*)out = w;
+#pragma unroll 1
+    for (int qm = 1; qm < P.s; ++qm) {
+        const double m = (double)T->mod[first + qm], rm = 1.0 / m;
+        w = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w |= ((uint32_t)(int)dmod_odd(xb[q], m, rm) & 0xffu) << (8 * q);
+        *(uint32_t*)(out + qm * P.pstride) = w;
+    }
+}
+
+// ------------------------------------------------------ product kernels
+// One wavefront per tile of 16 fibres of one tensor, in a grid-stride loop;
+// for every tile of 16 operator rows: the residue products of every modulus
+// (offset by the MFMA's accumulator input 128, reduced and packed), then
+// either (LAST) the reconstruction of the four entries of each lane, or the
+// rescaling with G drops (G < 0: P.g at run time) and the stores into the
+// next layout (CONTIG: P.kind == 0, four consecutive bytes per plane).
+template <int G, bool CONTIG, bool LAST>
+__global__ __launch_bounds__(256) void chain_step_kernel(ChainHbmParams P) {
+    __shared__ ChainTables KT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    static_assert(sizeof(ChainTables) % 4 == 0, "words");
+    for (int x = tid; x < (int)(sizeof(ChainTables) / 4); x += 256)
+        ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
+    __syncthreads();
+    const ChainTables* T = &KT;
+
+    const int n = P.n, np = P.np;
+    const int first = kSlots - P.s;  // first active slot; slot u holds modulus index u - first
+    const int64_t np2 = (int64_t)np * np, np3 = np2 * np;
+    const int64_t nft = np2 / 16;  // fibre tiles per tensor (np^2 is a multiple of 64)
+    const int ap = (np + 15) & ~15;
+    const int nc = (np + 31) / 32;  // k chunks of the MFMA
+    const int64_t opstride = (int64_t)ap * np;
+    const int r16 = lane & 15;  // MFMA row of the fibres' operand / column of the operator's and the output
+    const int kq = lane >> 4;   // k group of the operands (8 bytes each), output row group
+    const int64_t tiles = P.batch * nft;
+    const int64_t n3 = (int64_t)n * n * n;
+    const int* F0 = P.fexp + P.fin[0] * np;
+    const int* F1 = P.fexp + P.fin[1] * np;
+    const int* F2 = P.fexp + P.fin[2] * np;
+    const int64_t st0 = P.fin[0] == 0 ? 1 : P.fin[0] == 1 ? n : (int64_t)n * n;
+    const int64_t st1 = P.fin[1] == 0 ? 1 : P.fin[1] == 1 ? n : (int64_t)n * n;
+    const int64_t st2 = P.fin[2] == 0 ? 1 : P.fin[2] == 1 ? n : (int64_t)n * n;
+
+#pragma unroll 1
+    for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < tiles; w += (int64_t)gridDim.x * 4) {
+        const int64_t t = w / nft;
+        const int64_t f0 = (w % nft) * 16;
+        const int8_t* xin = P.in + t * np3 + (f0 + r16) * np + 8 * kq;
+        const int64_t fa = f0 + 4 * kq;  // the lane's first fibre
+        const int p1 = (int)(fa % np), p2 = (int)(fa / np);
+        const unsigned long long M = LAST ? P.smax[t] : 0ull;
+        const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
+#pragma unroll 1
+        for (int a0 = 0; a0 < np; a0 += 16) {
+            asm volatile("" ::: "memory");
+            const int a = a0 + r16;
+            const int8_t* opl = P.ops + (int64_t)a * np + 8 * kq;
+            uint32_t pk[kSlots];
+#pragma unroll
+            for (int u0 = 0; u0 < kSlots; u0 += 4) {
+                v4i acc[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] = v4i{128, 128, 128, 128};
+#pragma unroll 1
+                for (int c = 0; c < nc; ++c) {
+                    const bool ok = 32 * c + 8 * kq < np;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int u = u0 + v;
+                        if (u >= first) {
+                            const int64_t qm = u - first;
+                            const long a8 = ok ? *(const long*)(xin + qm * P.pstride + 32 * c) : 0l;
+                            const long b8 = ok ? *(const long*)(opl + qm * opstride + 32 * c) : 0l;
+                            acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8, b8, acc[v], 0, 0, 0);
+                        }
+                    }
+                }
+                // unused slots keep the accumulator input: the byte of a zero residue
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int a4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
+                    pk[u0 + v] = pack_products(a4, T, u0 + v);
+                }
+            }
+            if (LAST) {
+                double V[4];
+                mrc_horner(pk, T, V);
+                if (p2 < n && a < n) {
+                    const int f12 = F1[p2] + F2[a];
+                    double* y = P.Y + t * n3 + p2 * st1 + a * st2;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (p1 + q < n)
+                            y[(p1 + q) * st0] =
+                                M < kInfBits ? ldexp(alpha, -(F0[p1 + q] + f12)) * V[q] : __builtin_nan("");
+                }
+            } else {
+                float r[4][kSlots];
+                unpack_tile(pk, r);
+                if (G == 0 || (G < 0 && P.g == 0)) {
+#pragma unroll
+                    for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
+                }
+                // the next layout: (p1, p2, a) with the four entries
+                // contiguous, (p2, p1, a) or (a, p1, p2) with them np apart
+                int8_t* base = P.out + t * np3;
+                int64_t step = 0;
+                if (CONTIG) {
+                    base += fa + np2 * a;
+                } else if (P.kind == 1) {
+                    base += p2 + (int64_t)np * p1 + np2 * a;
+                    step = np;
+                } else {
+                    base += a + (int64_t)np * fa;
+                    step = np;
+                }
+                const bool ok = a < np;
+                const auto put = [&](int u, float r0, float r1, float r2, float r3) {
+                    if (u >= first && ok) store4<!CONTIG>(base + (int64_t)(u - first) * P.pstride, step, r0, r1, r2, r3);
+                };
+                rescale_extend<G>(P.g, r, T, put);
+            }
+        }
+    }
+}
+
+template <int G, bool CONTIG>
+void go_step(const ChainHbmParams& P, unsigned blocks, hipStream_t st) {
+    hipLaunchKernelGGL((chain_step_kernel<G, CONTIG, false>), dim3(blocks), dim3(256), 0, st, P);
+}
+
+}  // namespace
+
+hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st) {
+    if (P.n < 1 || P.n > kChainMaxN || P.batch < 1) return hipErrorInvalidValue;
+    const int64_t n3 = (int64_t)P.n * P.n * P.n;
+    const int64_t chunks = (n3 + kScanChunk - 1) / kScanChunk;
+    if (P.batch * chunks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)(P.batch * chunks)), dim3(256), 0, st, P.X, n3, chunks,
+                       P.smax);
+    return hipGetLastError();
+}
+
+hipError_t launch_chain_encode(const ChainHbmParams& P, hipStream_t st) {
+    if (P.n < 1 || P.n > kChainMaxN || P.np != ((P.n + 7) & ~7) || P.batch < 1 || P.s < kMinS || P.s > kChainMaxS ||
+        P.m0 < 0 || P.m0 > 2)
+        return hipErrorInvalidValue;
+    const int64_t np3 = (int64_t)P.np * P.np * P.np;
+    const int64_t bpt = (np3 / 4 + 255) / 256;
+    if (P.batch * bpt > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(chain_encode_kernel, dim3((unsigned)(P.batch * bpt)), dim3(256), 0, st, P, bpt);
+    return hipGetLastError();
+}
+
+hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st) {
+    if (P.n < 1 || P.n > kChainMaxN || P.np != ((P.n + 7) & ~7) || P.batch < 1 || P.s < kMinS || P.s > kChainMaxS)
+        return hipErrorInvalidValue;
+    if (!last && (P.g < 0 || P.g >= P.s || P.kind < 0 || P.kind > 2)) return hipErrorInvalidValue;
+    for (int j = 0; j < 3; ++j)
+        if (P.fin[j] < 0 || P.fin[j] > 2) return hipErrorInvalidValue;
+    const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
+    const int64_t want = (tiles + 3) / 4;
+    const unsigned blocks = (unsigned)(want < kStepBlocksMax ? want : kStepBlocksMax);
+    if (last) {
+        hipLaunchKernelGGL((chain_step_kernel<0, true, true>), dim3(blocks), dim3(256), 0, st, P);
+    } else if (P.kind == 0) {
+        // compile-time drop counts for the usual plans (7 or 8 with 15 or 16
+        // moduli, 6 with 12, 4 with 8); any other count takes the run-time
+        // instance
+        if (P.g == 7)
+            go_step<7, true>(P, blocks, st);
+        else if (P.g == 8)
+            go_step<8, true>(P, blocks, st);
+        else if (P.g == 6)
+            go_step<6, true>(P, blocks, st);
+        else if (P.g == 4)
+            go_step<4, true>(P, blocks, st);
+        else
+            go_step<-1, true>(P, blocks, st);
+    } else {
+        go_step<-1, false>(P, blocks, st);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace oz2

@@ -23,6 +23,7 @@
 // descending, so 256 (its only even modulus) comes first.
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "oz2.h"
 #include "oz2_internal.h"
@@ -148,29 +149,29 @@ bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* 
 }  // namespace
 
 int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, ChainParams* P,
-               ChainTables* T, int8_t* ops_residues) {
+               ChainTables* T, int8_t* ops_res, int* fexp) {
     const ModuliPlan* pl = moduli_plan(s);
-    if (!pl || s > kChainMaxS || n < 1 || n > kChainN || d < 1 || d > kChainMaxD) return OZ2_STATUS_INTERNAL;
+    if (!pl || s > kChainMaxS || n < 1 || n > kChainMaxN || d < 1 || d > kChainMaxD) return OZ2_STATUS_INTERNAL;
     if (pl->mod[0] != 256) return OZ2_STATUS_INTERNAL;
     for (int i = 1; i < s; ++i)
         if (pl->mod[i] % 2 == 0) return OZ2_STATUS_INTERNAL;
     for (int i = 0; i < d; ++i)
         for (int x = 0; x < n * n; ++x)
             if (!std::isfinite(ops[i][x])) return -(i + 1);
-    int64_t Abar[kChainMaxD][kChainN * kChainN];
-    int f[kChainMaxD][kChainN];
-    int pend[3][kChainN];
+    std::vector<int64_t> Abar((size_t)d * n * n);
+    std::vector<int> f((size_t)d * n), pend((size_t)3 * n);
     int g[kChainMaxD] = {};
     // the effective integer operators at b (the pending scales of a direction
     // folded into the next operator on it) and whether their schedule passes;
     // encoding depends on b, so the bounds are taken afresh for every b
     auto passes = [&](int b) {
         uint64_t rho[kChainMaxD];
-        std::memset(pend, 0, sizeof(pend));
+        std::fill(pend.begin(), pend.end(), 0);
         for (int i = 0; i < d; ++i) {
-            if (!encode_rows(ops[i], pend[modes[i]], n, b, Abar[i], f[i])) return false;
-            rho[i] = row_sum_bound(Abar[i], n);
-            std::memcpy(pend[modes[i]], f[i], sizeof(int) * n);
+            int* pm = &pend[(size_t)modes[i] * n];
+            if (!encode_rows(ops[i], pm, n, b, &Abar[(size_t)i * n * n], &f[(size_t)i * n])) return false;
+            rho[i] = row_sum_bound(&Abar[(size_t)i * n * n], n);
+            std::memcpy(pm, &f[(size_t)i * n], sizeof(int) * n);
         }
         return drop_plan(b, d, rho, pl->mod, s, g);
     };
@@ -216,15 +217,16 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < g[i]; ++j) Qd = Qd * (double)pl->mod[s - 1 - j];
     P->Qd = Qd;
-    std::memset(ops_residues, 0, (size_t)d * kChainMaxS * kChainN * kChainN);
-    for (int m = 0; m < 3; ++m)
-        for (int a = 0; a < kChainN; ++a) T->fexp[m][a] = a < n ? pend[m][a] : 0;
+    for (int m = 0; m < 3; ++m) {
+        for (int a = 0; a < n; ++a) fexp[m * n + a] = pend[(size_t)m * n + a];
+        for (int a = 0; a < kChainN; ++a) T->fexp[m][a] = a < n ? pend[(size_t)m * n + a] : 0;
+    }
     for (int i = 0; i < d; ++i)
         for (int q = 0; q < s; ++q)
             for (int a = 0; a < n; ++a)
                 for (int k = 0; k < n; ++k)
-                    ops_residues[((i * kChainMaxS + q) * kChainN + a) * kChainN + k] =
-                        (int8_t)centered(Abar[i][a * n + k], pl->mod[q]);
+                    ops_res[(((size_t)i * s + q) * n + a) * n + k] =
+                        (int8_t)centered(Abar[((size_t)i * n + a) * n + k], pl->mod[q]);
     // kernel tables in slot order: the s moduli right-aligned in kChainMaxS
     // slots (descending), the unused leading slots with the modulus 1
     const int first = kChainMaxS - s;

@@ -115,9 +115,12 @@ struct SmallParams {
 // Persistent tensor-mode chain, OzII-RescaleBE ("You Only Convert Twice:
 // Ozaki Scheme II for Chained Tensor Mode Products", Sec. 5.2 and
 // Algorithm 7): Y = X x_{m1} A1 x_{m2} A2 ... for a batch of n x n x n
-// tensors, d operators, by default along the directions in turn, one block
-// per tensor, residues in LDS for the whole chain (oz2_chain.hip).
-constexpr int kChainN = 16;      // tensor side of the kernel's tiles (n <= 16 is zero padded)
+// tensors, d operators, by default along the directions in turn.  For
+// n <= kChainN one block per tensor keeps the residues in LDS for the whole
+// chain (oz2_chain.hip); larger tensors keep them in HBM between one kernel
+// per product (oz2_chain_hbm.hip).
+constexpr int kChainN = 16;      // tensor side of the LDS kernel's tiles (n <= 16 is zero padded)
+constexpr int kChainMaxN = 256;  // tensor side of the HBM-resident kernels
 constexpr int kChainMaxS = 16;   // moduli: one LDS buffer of 16 residue planes (64 KiB)
 constexpr int kChainMaxD = 8;    // chain depth: operators
 struct ChainParams {
@@ -136,7 +139,7 @@ struct ChainParams {
     int kind[kChainMaxD];
     int fin[3];
     double Qd;                   // fl64 product of the dropped moduli, in drop order
-    const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators
+    const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators, by modulus index
     const float* tab;            // device ChainTables (below)
 };
 
@@ -156,10 +159,40 @@ struct ChainTables {
 // it, Sec. 5.2): the significand bits b, the drop counts g, the effective
 // integer operators' residues and the residue layout of every product.
 // ops: d HOST n x n column-major operators; modes: d directions in
-// {0, 1, 2}.  Returns 0, -(i + 1) for a non-finite entry in operator i, or
-// OZ2_STATUS_RANGE when no b in [1, 53] passes.
+// {0, 1, 2}; 1 <= n <= kChainMaxN.  Writes P (all but the device pointers
+// and the per-call fields), T (T->fexp only for n <= kChainN), ops_res
+// [d][s][n][n] (operator i, modulus index q, row a, column k: the centred
+// residue of the integer operator) and fexp [3][n] (the row exponents left
+// pending on each direction).  Returns 0, -(i + 1) for a non-finite entry in
+// operator i, or OZ2_STATUS_RANGE when no b in [1, 53] passes.
 int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, ChainParams* P,
-               ChainTables* T, int8_t* ops_residues);
+               ChainTables* T, int8_t* ops_res, int* fexp);
+
+// One launch of the HBM-resident chain (oz2_chain_hbm.hip).  Every residue
+// plane holds each tensor as np^3 bytes, np = n rounded up to a multiple of
+// 8 in every direction: position (p0, p1, p2) at p0 + np p1 + np^2 p2, p0 the
+// direction the next product contracts; fibre f = p1 + np p2 is the row of
+// np bytes at f np.  Padding positions hold residues too (of zero, or of
+// products of padding) and never reach a result: the operators' columns
+// k >= n are zero, and rows, fibres and outputs beyond n are not stored.
+struct ChainHbmParams {
+    const double* X;             // [batch][n^3] column-major tensors
+    double* Y;
+    int64_t batch;
+    int n, np, s, b;
+    int m0;                      // direction at position 0 of the encoded planes
+    int g;                       // moduli dropped after this product
+    int kind;                    // this product's output layout (as ChainParams::kind)
+    int fin[3];                  // the last product's entry, fibre and output directions
+    double Qd;                   // as ChainParams::Qd
+    const int8_t* ops;           // [s][ap][np] this product's operator residues, ap = np rounded up to 16
+    const float* tab;            // ChainTables
+    const int* fexp;             // [3][np] row exponents left pending on each direction
+    unsigned long long* smax;    // [batch] max |x| bit pattern of each tensor (0 before the scan)
+    const int8_t* in;            // planes [s][batch][np^3] read by this product
+    int8_t* out;                 // planes written by the encode or a non-final product
+    int64_t pstride;             // bytes between planes: batch np^3
+};
 
 struct CrtTestParams {
     const uint8_t* R;  // [s][count]
@@ -190,5 +223,8 @@ hipError_t launch_scale_c(double* C, int64_t m, int64_t n, int64_t ldc, const do
 hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st);
 hipError_t launch_small_gemm(SmallParams P, int NL, bool beta_nonzero, hipStream_t st);
 hipError_t launch_chain(const ChainParams& P, hipStream_t st);
+hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st);
+hipError_t launch_chain_encode(const ChainHbmParams& P, hipStream_t st);
+hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st);
 
 }  // namespace oz2

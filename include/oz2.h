@@ -274,9 +274,13 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
  * residue basis is the max-product modulus set for num_moduli, descending.
  * Limits of this implementation: 1 <= n <= OZ2_CHAIN_MAX_N,
  * 1 <= depth <= OZ2_CHAIN_MAX_DEPTH, 2 <= num_moduli <= OZ2_CHAIN_MAX_MODULI.
- * Results are deterministic; parity with the CPU oracle is bitwise.
+ * Two kernels run it, with identical results: for n <= 16 one kernel per
+ * batch keeps each tensor's residues in LDS; for larger n (or when
+ * oz2_set_chain_kernel asks for it) the residues stay in HBM, in the handle's
+ * workspace, between one kernel per product.  Results are deterministic;
+ * parity with the CPU oracle is bitwise.
  * ------------------------------------------------------------------- */
-#define OZ2_CHAIN_MAX_N 16
+#define OZ2_CHAIN_MAX_N 256
 #define OZ2_CHAIN_MAX_DEPTH 8
 #define OZ2_CHAIN_MAX_MODULI 16
 typedef struct oz2_chain_plan* oz2_chain_plan_t;
@@ -285,7 +289,8 @@ typedef struct oz2_chain_plan* oz2_chain_plan_t;
  * greedy drop schedule passes every range check for the effective
  * operators, the drop counts g, and the effective operators' residues and
  * the row exponents left pending on each direction, which are copied to
- * DEVICE memory owned by the plan (2.3 KiB + depth * 4 KiB).  ops: HOST
+ * DEVICE memory owned by the plan (about 2.5 KiB + 12 np + depth * s * np *
+ * (np rounded up to 16) bytes, plus depth * 4 KiB for n <= 16).  ops: HOST
  * array of depth pointers to HOST n x n column-major operators (finite).
  * modes: HOST array of depth directions in {1, 2, 3}, or NULL for the
  * directions in turn.  Argument numbers: h 1, n 2, depth 3, ops 4 (also a
@@ -300,12 +305,28 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
 int oz2_chain_plan_info(oz2_chain_plan_t plan, int* depth, int* b, int* g);
 
 /* Run the planned chain on `batch` tensors: X and Y are DEVICE arrays of
- * batch * n^3 doubles that must not overlap.  One kernel on h's stream
- * (phase times: the whole chain in ms[2]).  A tensor with a non-finite entry
- * gives an all-NaN result tensor.  Argument numbers: h 1, plan 2, X 3, Y 4,
- * batch 5. */
+ * batch * n^3 doubles that must not overlap.  Asynchronous on h's stream.
+ * The LDS kernel is one launch (phase times: the whole chain in ms[2]).  The
+ * HBM kernels use 2 s np^3 + 8 bytes of workspace per tensor (np = n rounded
+ * up to a multiple of 8), under the memory limit in as many equal batches as
+ * needed, OZ2_STATUS_WORKSPACE_LIMIT when not even one tensor fits; phase
+ * times: scan ms[0], encode ms[1], the rescaling products ms[2], the last
+ * product and the reconstruction ms[3] (everything in ms[2] when the call
+ * ran in several batches).  A tensor with a non-finite entry gives an
+ * all-NaN result tensor.  Argument numbers: h 1, plan 2, X 3, Y 4, batch 5.
+ * OZ2_STATUS_NOT_SUPPORTED when the LDS kernel is asked for and n > 16. */
 int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X, double* Y,
                          int64_t batch);
+
+/* Which kernels oz2_chain_rescale_be uses on this handle: AUTO (the
+ * default: LDS for n <= 16, else HBM), LDS, or HBM (any n).  Argument
+ * numbers: h 1, kernel 2. */
+enum {
+    OZ2_CHAIN_KERNEL_AUTO = 0,
+    OZ2_CHAIN_KERNEL_LDS = 1,
+    OZ2_CHAIN_KERNEL_HBM = 2
+};
+int oz2_set_chain_kernel(oz2_handle_t h, int kernel);
 
 /* Free a plan and its device memory. */
 int oz2_chain_plan_destroy(oz2_chain_plan_t plan);

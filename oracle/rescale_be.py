@@ -315,6 +315,26 @@ def mode_product(T: np.ndarray, M: np.ndarray, mode: int) -> np.ndarray:
     return np.einsum("ak,ijk->ija", M, T)
 
 
+def residue_mode_product(R: np.ndarray, Ares: np.ndarray, mode: int) -> np.ndarray:
+    """One residue product of Algorithm 7 (one modulus, one mode) before its
+    reduction, exactly.  Every entry is a sum of n products of centred
+    residues of moduli <= 256 (each |r| <= 128), so every partial sum is an
+    integer below n 2^14 < 2^53 and float64 arithmetic forms it without
+    rounding, in any order: the contraction is a BLAS product on the
+    residues as doubles."""
+    n = Ares.shape[0]
+    if n * 128 * 128 >= 2 ** 53:
+        raise ValueError("residue product not exact in float64")
+    T, M = np.asarray(R, dtype=np.float64), np.asarray(Ares, dtype=np.float64)
+    if mode == 0:
+        out = np.tensordot(M, T, axes=([1], [0]))                  # (a, j, l)
+    elif mode == 1:
+        out = np.moveaxis(np.tensordot(M, T, axes=([1], [1])), 0, 1)  # (i, a, l)
+    else:
+        out = np.tensordot(T, M, axes=([2], [1]))                  # (i, j, a)
+    return out.astype(np.int64)
+
+
 def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int, modes: Sequence[int] | None = None):
     """Plan and prepare the operators of a chain of depth d = len(ops_flat)
     (Algorithm 7 lines 2-9): returns a dict with basis, b, g, the effective
@@ -360,7 +380,7 @@ def chain_tensor(x_flat: np.ndarray, plan: dict, keep: dict | None = None) -> np
         keep["encoded"] = (Xbar, e)
         keep["stages"] = []
     for i in range(len(plan["g"])):
-        R = {p: centered_array(mode_product(R[p], plan["Ares"][i][p], plan["modes"][i]), p) for p in basis}
+        R = {p: centered_array(residue_mode_product(R[p], plan["Ares"][i][p], plan["modes"][i]), p) for p in basis}
         if keep is not None:
             keep["stages"].append(("product", i, dict(R)))
         if plan["g"][i] > 0:

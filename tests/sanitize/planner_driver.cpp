@@ -42,9 +42,10 @@ int main() {
         (void)pl->M.log2();
         for (int l = 0; l < kMaxLimb16; ++l) (void)pl->M.limb16(l);
     }
-    std::vector<int8_t> residues((size_t)kChainMaxD * kChainMaxS * 16 * 16);
     for (int rep = 0; rep < 40; ++rep) {
-        const int n = 1 + (int)(next_u64() % 16), d = 1 + (int)(next_u64() % 8);
+        // sides of the LDS kernel and, every fifth plan, of the HBM kernels
+        const int n = rep % 5 == 4 ? 17 + (int)(next_u64() % 80) : 1 + (int)(next_u64() % 16);
+        const int d = 1 + (int)(next_u64() % 8);
         const int s = 6 + 2 * (int)(next_u64() % 6);
         std::vector<std::vector<double>> ops(d, std::vector<double>((size_t)n * n));
         std::vector<const double*> ptr(d);
@@ -57,7 +58,9 @@ int main() {
         if (rep % 7 == 3) ops[d - 1][0] = NAN;
         ChainParams P{};
         ChainTables T{};
-        const int st = chain_plan(s, n, d, ptr.data(), modes.data(), &P, &T, residues.data());
+        std::vector<int8_t> residues((size_t)d * s * n * n);
+        std::vector<int> fexp((size_t)3 * n);
+        const int st = chain_plan(s, n, d, ptr.data(), modes.data(), &P, &T, residues.data(), fexp.data());
         if (rep % 7 == 3) bad += st != -d;
     }
     std::printf("planner driver: %d unexpected results\n", bad);

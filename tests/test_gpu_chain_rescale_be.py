@@ -197,7 +197,7 @@ def test_chain_argument_errors(handle):
     three = (ctypes.c_void_p * 3)(p, p, p)
     out = ctypes.c_void_p()
     assert lib.oz2_chain_plan_create(handle._h, 0, 3, three, None, 8, ctypes.byref(out)) == -2
-    assert lib.oz2_chain_plan_create(handle._h, 17, 3, three, None, 8, ctypes.byref(out)) == -2
+    assert lib.oz2_chain_plan_create(handle._h, 257, 3, three, None, 8, ctypes.byref(out)) == -2
     assert lib.oz2_chain_plan_create(handle._h, 4, 0, three, None, 8, ctypes.byref(out)) == -3
     assert lib.oz2_chain_plan_create(handle._h, 4, 9, three, None, 8, ctypes.byref(out)) == -3
     assert lib.oz2_chain_plan_create(handle._h, 4, 3, None, None, 8, ctypes.byref(out)) == -4
