@@ -21,6 +21,9 @@ Other workloads (--workload), each printing the same kind of JSON line:
   chain_rbe  the same chain by OzII-RescaleBE ("You Only Convert Twice",
              Algorithm 7): one kernel per chain, residues persist across the
              modes (rescaling + base extension), reconstruction once
+  chain_sizes  OzII-RescaleBE over tensor sides n = 8 .. 256 at about 2^24
+             entries per chain, s = 15 (the chain page's Sec. 6 throughput
+             test): LDS kernel for n <= 16, HBM-resident kernels above
   nonsquare  the eight m x k x n shapes of the Arc page's Table 10 (k from
              256 to 65536, m or n from 1024 to 65536), N/N, U(-1,1) entries,
              s = 8 and 16; one step = the 16 calls, all inputs resident
@@ -906,6 +909,100 @@ def run_chain_rbe(args):
     }
 
 
+CHAIN_SIZES = (8, 12, 16, 32, 64, 128, 256)
+CHAIN_SIZES_DOF = 1 << 24
+
+
+def run_chain_sizes(args):
+    """OzII-RescaleBE over tensor sides (the chain page's Sec. 6 throughput
+    test, Fig. 7): depth 3, the directions in turn, U(-1, 1) tensors and
+    operators, s = 15 unless --s, batch floor(2^24 / n^3) so that every chain
+    processes about 2^24 entries.  n <= 16 runs the LDS kernel (and n = 16
+    the HBM kernels as well, for comparison), larger n the HBM kernels.  Per
+    side: GDoF/s over whole chains (encode to reconstruction), the phase
+    times, the algorithmic vector-ALU rate (rbe_valu_ops_per_entry per real
+    entry); for n <= 64 one tensor bit for bit against the oracle, for
+    n <= 32 the normwise error of one tensor against the exact chain.  The
+    line's value is all sides' entries over all sides' chain times."""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    import oracle
+    import workloads
+
+    s = int(args.s) if args.s else 15
+    sizes = [(n, "auto") for n in CHAIN_SIZES] + [(n, "hbm") for n in CHAIN_SIZES if n <= 16]
+    h = oz2.Handle(torch.cuda.current_stream())
+    h.set_timing(True)
+    rows, tot_dof, tot_ms, parity_bad, parity_n = {}, 0, 0.0, 0, 0
+    roofline = None
+    for n, kern in sizes:
+        batch = CHAIN_SIZES_DOF // n ** 3
+        n3 = n ** 3
+        log(f"[bench] chain_sizes: n={n} batch={batch} kernel={kern}")
+        X = workloads.tensor_batch(n, batch, workloads.seed(8, n))
+        ops = [workloads.real_matrix(n, n, workloads.seed(8, 1000 + 10 * n + q)) for q in range(3)]
+        dX = torch.from_numpy(X).cuda()
+        dY = torch.empty_like(dX)
+        h.set_chain_kernel(kern)
+        plan = h.chain_plan(ops, n, s)
+        for _ in range(args.warmup):
+            h.chain_rescale_be(plan, dX, dY, batch)
+        torch.cuda.synchronize()
+        ph, t0 = [], time.perf_counter()
+        for _ in range(args.steps):
+            h.chain_rescale_be(plan, dX, dY, batch)
+            ph.append(h.phase_times())
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        phm = [float(x) for x in np.mean(np.array(ph), axis=0)]
+        dof = n3 * batch
+        lds = n <= 16 and kern == "auto"
+        valu = float(rbe_valu_ops_per_entry(s, plan.g)) * dof / (sum(phm) * 1e-3) / 1e12
+        row = dict(batch=batch, kernel="lds" if lds else "hbm", gdofs=round(dof / (ms * 1e-3) / 1e9, 3),
+                   ms=round(ms, 4), b=plan.b, g=list(plan.g),
+                   phases_ms=(dict(chain=round(phm[2], 4)) if lds else
+                              dict(scan=round(phm[0], 4), encode=round(phm[1], 4), rescaling_products=round(phm[2], 4),
+                                   last_product=round(phm[3], 4))),
+                   valu_tops=round(valu, 2))
+        if n <= 64:
+            Y = dY[:n3].cpu().numpy()
+            rplan = oracle.rescale_be.prepare_chain(ops, n, s)
+            want = oracle.rescale_be.chain_tensor(X[:n3], rplan)
+            bad = int(np.count_nonzero(Y.view(np.int64) != want.view(np.int64)))
+            row["parity_first_tensor_not_bit_identical"] = bad
+            parity_bad += bad
+            parity_n += n3
+        if n <= 32:
+            row["normwise_rel_err"] = chain_accuracy(dY[:n3].cpu().numpy(), X, ops, n, 1)[0]
+        rows[f"{n}" if kern == "auto" else f"{n}_{kern}"] = row
+        if kern == "auto":
+            tot_dof += dof
+            tot_ms += ms
+        if n == max(CHAIN_SIZES):
+            roofline = dict(kernel="chain_step_kernel (OzII-RescaleBE product + rescaling, HBM residues), n = 256",
+                            bound="alu", achieved=round(valu, 2), peak=round(PEAK_VALU_TOPS, 2), unit="TOP/s",
+                            frac=round(valu / PEAK_VALU_TOPS, 4), traffic=None,
+                            launch_ms=round(sum(phm), 4))
+        plan.close()
+        del dX, dY
+    h.set_chain_kernel("auto")
+    h.close()
+    value = tot_dof / (tot_ms * 1e-3) / 1e9
+    return {
+        "metric": "OzII-RescaleBE tensor-mode chain GDoF/s over tensor sides n = 8 .. 256 (about 2^24 entries per chain)",
+        "value": round(value, 3),
+        "unit": "GDoF/s",
+        "ms_per_step": round(tot_ms, 3),
+        "dtype": "i8",
+        "config": {"workload": f"tensor_chain_rescale_be_sizes_dof2^24_s{s}_d3", "sizes": list(CHAIN_SIZES),
+                   "dof_per_chain": CHAIN_SIZES_DOF, "s": s, "depth": 3, "dist": "uniform"},
+        "per_shape": rows,
+        "parity_sample": dict(entries=parity_n, not_bit_identical=parity_bad,
+                              how="the first tensor of each side n <= 64 against the oracle"),
+        "roofline": roofline,
+    }
+
+
 def oracle_chain(X, Aop, Bop, Cop, n, nt, s):
     """The three emulated modes of nt tensors with the oracle, as the library
     decomposes them (mode 1 over all nt tensors at once)."""
@@ -1168,7 +1265,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="dgemm8192",
-                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "nonsquare",
+                    choices=["dgemm8192", "wide4096", "zgemm4096", "chain", "chain_rbe", "chain_sizes", "nonsquare",
                              "reuse8192", "tiled8192", "datapower", "accuracy", "perfmodel"])
     ap.add_argument("--s", type=str, default="")
     ap.add_argument("--n", type=int, default=0)
@@ -1194,6 +1291,8 @@ def main():
         out = run_chain(args)
     elif args.workload == "chain_rbe":
         out = run_chain_rbe(args)
+    elif args.workload == "chain_sizes":
+        out = run_chain_sizes(args)
     elif args.workload == "nonsquare":
         out = run_nonsquare(args)
     elif args.workload == "datapower":

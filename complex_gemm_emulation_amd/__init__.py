@@ -379,7 +379,7 @@ class Handle:
 
     def set_chain_kernel(self, kernel: str) -> None:
         """Which kernels run persistent chains (oz2_set_chain_kernel): 'auto'
-        (LDS for n <= 16, else HBM), 'lds' or 'hbm'."""
+        (LDS for 8 < n <= 16, else HBM), 'lds' or 'hbm'."""
         _check("oz2_set_chain_kernel", _raw().oz2_set_chain_kernel(self._h, self.CHAIN_KERNELS.index(kernel)))
 
     def chain_rescale_be(self, plan: ChainPlan, X, Y, batch) -> None:

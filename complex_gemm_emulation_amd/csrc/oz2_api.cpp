@@ -1131,8 +1131,11 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
     if (batch == 0) return OZ2_STATUS_SUCCESS;
     if (!X) return -3;
     if (!Y) return -4;
+    // automatic choice: the LDS kernel pads every tensor to 16^3, so it
+    // serves 8 < n <= 16; smaller tensors (padded to 8^3) and larger ones
+    // run on the HBM kernels
     const bool lds = h->chain_kernel == OZ2_CHAIN_KERNEL_LDS ||
-                     (h->chain_kernel == OZ2_CHAIN_KERNEL_AUTO && plan->params.n <= kChainN);
+                     (h->chain_kernel == OZ2_CHAIN_KERNEL_AUTO && plan->params.n > 8 && plan->params.n <= kChainN);
     if (lds && plan->params.n > kChainN) return OZ2_STATUS_NOT_SUPPORTED;
     h->last.valid = false;
     if (!lds) return chain_hbm(h, plan, X, Y, batch);

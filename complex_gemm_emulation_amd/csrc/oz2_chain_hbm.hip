@@ -141,10 +141,16 @@ __global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, int
 // for every tile of 16 operator rows: the residue products of every modulus
 // (offset by the MFMA's accumulator input 128, reduced and packed), then
 // either (LAST) the reconstruction of the four entries of each lane, or the
-// rescaling with G drops (G < 0: P.g at run time) and the stores into the
-// next layout (CONTIG: P.kind == 0, four consecutive bytes per plane).
-template <int G, bool CONTIG, bool LAST>
-__global__ __launch_bounds__(256) void chain_step_kernel(ChainHbmParams P) {
+// rescaling with P.g drops and the stores into the next layout (CONTIG:
+// P.kind == 0, four consecutive bytes per plane).
+// The drop count is a run-time value: with it fixed at compile time the
+// fully unrolled slot loops keep more table values live and need about 200
+// registers, and at 4 wavefronts per SIMD (128 registers) they spill
+// hundreds of bytes; the run-time form spills 48.  The reconstruction needs
+// about 250 registers and runs at 2 wavefronts per SIMD.
+template <bool CONTIG, bool LAST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
+void chain_step_kernel(ChainHbmParams P) {
     __shared__ ChainTables KT;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(256) void chain_step_kernel(ChainHbmParams P) {
             } else {
                 float r[4][kSlots];
                 unpack_tile(pk, r);
-                if (G == 0 || (G < 0 && P.g == 0)) {
+                if (P.g == 0) {
 #pragma unroll
                     for (int u = 0; u < kSlots; ++u)
 #pragma unroll
@@ -252,15 +258,10 @@ __global__ __launch_bounds__(256) void chain_step_kernel(ChainHbmParams P) {
                 const auto put = [&](int u, float r0, float r1, float r2, float r3) {
                     if (u >= first && ok) store4<!CONTIG>(base + (int64_t)(u - first) * P.pstride, step, r0, r1, r2, r3);
                 };
-                rescale_extend<G>(P.g, r, T, put);
+                rescale_extend<-1>(P.g, r, T, put);
             }
         }
     }
-}
-
-template <int G, bool CONTIG>
-void go_step(const ChainHbmParams& P, unsigned blocks, hipStream_t st) {
-    hipLaunchKernelGGL((chain_step_kernel<G, CONTIG, false>), dim3(blocks), dim3(256), 0, st, P);
 }
 
 }  // namespace
@@ -295,25 +296,13 @@ hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st)
     const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
     const int64_t want = (tiles + 3) / 4;
     const unsigned blocks = (unsigned)(want < kStepBlocksMax ? want : kStepBlocksMax);
-    if (last) {
-        hipLaunchKernelGGL((chain_step_kernel<0, true, true>), dim3(blocks), dim3(256), 0, st, P);
-    } else if (P.kind == 0) {
-        // compile-time drop counts for the usual plans (7 or 8 with 15 or 16
-        // moduli, 6 with 12, 4 with 8); any other count takes the run-time
-        // instance
-        if (P.g == 7)
-            go_step<7, true>(P, blocks, st);
-        else if (P.g == 8)
-            go_step<8, true>(P, blocks, st);
-        else if (P.g == 6)
-            go_step<6, true>(P, blocks, st);
-        else if (P.g == 4)
-            go_step<4, true>(P, blocks, st);
-        else
-            go_step<-1, true>(P, blocks, st);
-    } else {
-        go_step<-1, false>(P, blocks, st);
-    }
+    const dim3 grid(blocks), block(256);
+    if (last)
+        hipLaunchKernelGGL((chain_step_kernel<true, true>), grid, block, 0, st, P);
+    else if (P.kind == 0)
+        hipLaunchKernelGGL((chain_step_kernel<true, false>), grid, block, 0, st, P);
+    else
+        hipLaunchKernelGGL((chain_step_kernel<false, false>), grid, block, 0, st, P);
     return hipGetLastError();
 }
 

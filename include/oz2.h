@@ -274,10 +274,11 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
  * residue basis is the max-product modulus set for num_moduli, descending.
  * Limits of this implementation: 1 <= n <= OZ2_CHAIN_MAX_N,
  * 1 <= depth <= OZ2_CHAIN_MAX_DEPTH, 2 <= num_moduli <= OZ2_CHAIN_MAX_MODULI.
- * Two kernels run it, with identical results: for n <= 16 one kernel per
- * batch keeps each tensor's residues in LDS; for larger n (or when
- * oz2_set_chain_kernel asks for it) the residues stay in HBM, in the handle's
- * workspace, between one kernel per product.  Results are deterministic;
+ * Two kernels run it, with identical results: for 8 < n <= 16 one kernel
+ * per batch keeps each tensor's residues (padded to 16^3) in LDS; for other
+ * n (or when oz2_set_chain_kernel asks for it) the residues (padded to a
+ * multiple of 8 in each direction) stay in HBM, in the handle's workspace,
+ * between one kernel per product.  Results are deterministic;
  * parity with the CPU oracle is bitwise.
  * ------------------------------------------------------------------- */
 #define OZ2_CHAIN_MAX_N 256
@@ -319,7 +320,7 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
                          int64_t batch);
 
 /* Which kernels oz2_chain_rescale_be uses on this handle: AUTO (the
- * default: LDS for n <= 16, else HBM), LDS, or HBM (any n).  Argument
+ * default: LDS for 8 < n <= 16, else HBM), LDS (n <= 16), or HBM (any n).  Argument
  * numbers: h 1, kernel 2. */
 enum {
     OZ2_CHAIN_KERNEL_AUTO = 0,

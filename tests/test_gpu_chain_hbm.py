@@ -187,6 +187,22 @@ def test_chain_hbm_lds_kernel_refuses_large_n(handle):
         handle.set_chain_kernel("auto")
 
 
+def test_chain_kernel_choice():
+    """the automatic choice: the HBM kernels (which take the handle's
+    workspace for the residue planes) for n <= 8 and n > 16, the LDS kernel
+    (no workspace) for 8 < n <= 16"""
+    import torch
+    import complex_gemm_emulation_amd as oz2
+    for n, lds in ((8, False), (9, True), (16, True), (17, False)):
+        ops = _ops(n, 9650 + n)
+        X = workloads.tensor_batch(n, 2, 9660 + n)
+        with oz2.Handle() as h, h.chain_plan(ops, n, 12) as cp:
+            dY = torch.empty(2 * n ** 3, dtype=torch.float64, device="cuda")
+            h.chain_rescale_be(cp, to_dev(X), dY, 2)
+            torch.cuda.synchronize()
+            assert (h.workspace_size() == 0) == lds, (n, h.workspace_size())
+
+
 def _golden_cases():
     path = os.path.join(GOLDEN, "chain_hbm_samples.json")
     with open(path) as f:

@@ -1,7 +1,10 @@
 """GPU parity of the persistent tensor-mode chain (oz2_chain_plan_create /
 oz2_chain_rescale_be, OzII-RescaleBE of "You Only Convert Twice: Ozaki
 Scheme II for Chained Tensor Mode Products", Algorithm 7, chains of depth
-1 to 8) against the CPU oracle (oracle/rescale_be.py), through the C ABI.
+1 to 8) against the CPU oracle (oracle/rescale_be.py), through the C ABI,
+on the kernel that keeps each tensor's residues in LDS (oz2_chain.hip; the
+handle asks for it, since n <= 8 would otherwise run on the HBM kernels of
+tests/test_gpu_chain_hbm.py).
 
 Bar: the plan (b, g) equals the oracle planner's, and every output entry is
 bit-identical to the oracle's: every step is exact integer arithmetic except
@@ -28,6 +31,7 @@ def handle():
         pytest.skip("no GPU")
     import complex_gemm_emulation_amd as oz2
     h = oz2.Handle()
+    h.set_chain_kernel("lds")   # n <= 8 would otherwise run on the HBM kernels
     yield h
     h.close()
 
