@@ -917,8 +917,8 @@ def run_chain_sizes(args):
     """OzII-RescaleBE over tensor sides (the chain page's Sec. 6 throughput
     test, Fig. 7): depth 3, the directions in turn, U(-1, 1) tensors and
     operators, s = 15 unless --s, batch floor(2^24 / n^3) so that every chain
-    processes about 2^24 entries.  n <= 16 runs the LDS kernel (and n = 16
-    the HBM kernels as well, for comparison), larger n the HBM kernels.  Per
+    processes about 2^24 entries.  8 < n <= 16 runs the LDS kernel (and the
+    HBM kernels as well, for comparison), other n the HBM kernels.  Per
     side: GDoF/s over whole chains (encode to reconstruction), the phase
     times, the algorithmic vector-ALU rate (rbe_valu_ops_per_entry per real
     entry); for n <= 64 one tensor bit for bit against the oracle, for
@@ -930,7 +930,10 @@ def run_chain_sizes(args):
     import workloads
 
     s = int(args.s) if args.s else 15
-    sizes = [(n, "auto") for n in CHAIN_SIZES] + [(n, "hbm") for n in CHAIN_SIZES if n <= 16]
+    only = [int(x) for x in args.chain_sizes.split(",")] if args.chain_sizes else None
+    sizes = [(n, "auto") for n in CHAIN_SIZES] + [(n, "hbm") for n in CHAIN_SIZES if 8 < n <= 16]
+    if only:
+        sizes = [(n, "auto") for n in only]
     h = oz2.Handle(torch.cuda.current_stream())
     h.set_timing(True)
     rows, tot_dof, tot_ms, parity_bad, parity_n = {}, 0, 0.0, 0, 0
@@ -956,7 +959,7 @@ def run_chain_sizes(args):
         ms = (time.perf_counter() - t0) / args.steps * 1e3
         phm = [float(x) for x in np.mean(np.array(ph), axis=0)]
         dof = n3 * batch
-        lds = n <= 16 and kern == "auto"
+        lds = 8 < n <= 16 and kern == "auto"
         valu = float(rbe_valu_ops_per_entry(s, plan.g)) * dof / (sum(phm) * 1e-3) / 1e12
         row = dict(batch=batch, kernel="lds" if lds else "hbm", gdofs=round(dof / (ms * 1e-3) / 1e9, 3),
                    ms=round(ms, 4), b=plan.b, g=list(plan.g),
@@ -1274,6 +1277,7 @@ def main():
     ap.add_argument("--chain-rbe-cpu-tensors", type=int, default=384)
     ap.add_argument("--chain-acc-tensors", type=int, default=8)
     ap.add_argument("--chain-depth", type=int, default=3, help="chain_rbe: operators (3 = one pass)")
+    ap.add_argument("--chain-sizes", type=str, default="", help="chain_sizes: only these sides (comma list)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip timing the HBM stream ceilings")
     ap.add_argument("--copy-calibration", action="store_true")

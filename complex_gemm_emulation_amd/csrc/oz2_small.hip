@@ -57,9 +57,11 @@ __device__ __forceinline__ void load8(const double* X, int64_t ld, bool contig, 
 // addresses where used, so they neither occupy SGPRs nor spill into VGPR lanes.
 // Past the last modulus every field is zero.
 struct ModConst {
-    float fm, frcp, fhalf, foffb;   // m, fl32(1 / m), fl32(1 / m) / 2, residue_word's offset
+    float fm, frcp, foffb;          // m, fl32(1 / m), residue_word's offset
     uint32_t K128;                  // K_m + 128 (residue_word)
     uint32_t c4[kExtWords];
+    int32_t mu;                     // ceil(2^29 / m) (acc_mod)
+    int32_t negm;                   // -m
 };
 constexpr int kTableWords = (kMaxS / 2) * kMaxLimb16 + kMaxLimb16 + kMaxS / 2;
 struct SmallConsts {
@@ -102,17 +104,27 @@ __device__ __forceinline__ void encode8(const double x[8], const SmallParams& P,
     }
 }
 
-// INT32 accumulator -> [0, m): r = acc - m floor((acc + 1/2) / m) in FP32.
-// With k <= 32 and residues of magnitude <= 128, |acc| <= 2^19, so acc is
-// exact in FP32; (acc + 1/2) / m lies at least 1 / (2m) from an integer, and
-// fma(acc, fl32(1/m), fl32(1/m) / 2) is within 2^-5 / m + 2^-11 of it for
-// m >= 64 (every modulus here is >= 157), so the floor and r are exact.
-// Past the last modulus (all constants 0) it returns acc, which is 0 there.
-// The result is an integer-valued float; v_cvt_pk_u8_f32 converts it
-// straight into its byte of the packed word of a modulus pair.
-__device__ __forceinline__ float acc_mod(int32_t acc, const ModConst& C) {
-    const float a = (float)acc;
-    return fmaf(-C.fm, floorf(fmaf(a, C.frcp, C.fhalf)), a);
+// A residue of a product acc (|acc| <= 2^19: k <= 32 terms of magnitude
+// <= 2^14) modulo m <= 255, as r = acc - q m with q = floor(8 acc mu / 2^32),
+// mu = ceil(2^29 / m) < 2^22: v_mul_hi_i32_i24 of 8 acc (|8 acc| <= 2^22
+// fits its signed 24-bit operand) and one v_mad_i32_i24, three full-rate
+// integer instructions.  acc mu / 2^29 = acc / m + acc d / 2^29 with
+// 0 <= d < 1, an error below 2^-10 in magnitude, while acc / m lies at least
+// 1/m > 2^-10 from the next integer above it, and from the one below it
+// unless it is an integer itself: so q = floor(acc / m), except that a
+// negative multiple of m gives q one less and r = m.  Hence r in [0, m], r
+// congruent to acc: the CRT sums below take any representative <= 255 (a
+// residue m adds m W_t, a multiple of M, to the sum and exactly y_t to the
+// quotient estimate, whose error bound holds for every r <= 255), so c_hat
+// is unchanged.  The first modulus, 256, is the low byte of acc instead.
+// Past the last modulus (all constants 0) acc = 0 and r = 0.
+// (Written as instructions: the compiler would otherwise pick the
+// quarter-rate 32-bit v_mul_hi_i32 and v_mad_u64_u32.)
+__device__ __forceinline__ uint32_t acc_mod(int32_t acc, const ModConst& C) {
+    int32_t q, r;
+    asm("v_mul_hi_i32_i24 %0, %1, %2" : "=v"(q) : "v"(acc << 3), "v"(C.mu));
+    asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(r) : "v"(q), "v"(C.negm), "v"(acc));
+    return (uint32_t)r;
 }
 
 // PAIR (k <= 16): the instruction's k of 32 holds two tiles.  Lanes 0-31
@@ -120,8 +132,11 @@ __device__ __forceinline__ float acc_mod(int32_t acc, const ModConst& C) {
 // lane encodes useful values; the product of tile n + h takes the lanes of
 // half h of op(A) and zeros in the other half, which removes the other
 // tile's terms from the sum.
+// Occupancy: 3 wavefronts per SIMD up to 16 moduli (at most 168 registers;
+// with 16 moduli the compiler spills about 50 bytes per lane, and the chain's
+// modes still run 4% faster than at 2), 2 up to 20, 1 beyond.
 template <int NL, bool BETA, bool PAIR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1 : 2))) void small_gemm_kernel(SmallParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1 : NL >= 5 ? 2 : 3))) void small_gemm_kernel(SmallParams P) {
     constexpr int SMAX = 4 * NL;     // N_L words hold products of up to 4 N_L moduli <= 256
     constexpr bool EXT = NL >= 5;    // t > 61 is only reachable with more than 16 moduli
     constexpr int STEP = PAIR ? 2 : 1;
@@ -143,8 +158,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
             if (i < P.s) {
                 c.fm = (float)P.mod[i];
                 c.frcp = P.frcp[i];
-                c.fhalf = 0.5f * P.frcp[i];
                 c.foffb = P.foffb[i];
+                c.mu = (int32_t)((536870912u + P.mod[i] - 1) / P.mod[i]);
+                c.negm = -(int32_t)P.mod[i];
                 c.K128 = P.K[i] + 128u;
 #pragma unroll
                 for (int l = 0; l < kExtWords; ++l) c.c4[l] = P.c[i][l];
@@ -236,18 +252,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NL >= 6 ? 1
             for (int t = 0; t < SMAX; t += 2) {
                 if (t < P.s) {
                     // past the last modulus: zero fragments, constants and limbs
-                    const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t] & amask, fb[t], zero, 0, 0, 0);
-                    const v4i cb = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero, 0, 0, 0);
                     const ModConst& C0 = Q.q[t];
                     const ModConst& C1 = Q.q[t + 1];
+                    const v4i ca = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t] & amask, fb[t], zero, 0, 0, 0);
+                    const v4i cb = __builtin_amdgcn_mfma_i32_16x16x32_i8(fa[t + 1] & amask, fb[t + 1], zero, 0, 0, 0);
                     // residues of moduli t, t + 1 as the 16-bit halves of one
                     // word; modulus 256 (always the first) is the low byte of the sum
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = t == 0 ? ((uint32_t)ca[e] & 0xffu)
-                                                   : __builtin_amdgcn_cvt_pk_u8_f32(acc_mod(ca[e], C0), 0, 0u);
-                        acc[e].add2(__builtin_amdgcn_cvt_pk_u8_f32(acc_mod(cb[e], C1), 2, lo), Q.Y2[t >> 1],
-                                    Q.W2[t >> 1]);
+                        const uint32_t lo = t == 0 ? ((uint32_t)ca[e] & 0xffu) : acc_mod(ca[e], C0);
+                        acc[e].add2((acc_mod(cb[e], C1) << 16) | lo, Q.Y2[t >> 1], Q.W2[t >> 1]);
                     }
                 }
             }
