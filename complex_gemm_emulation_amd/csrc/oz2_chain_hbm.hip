@@ -53,6 +53,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kScanChunk = 4096;      // entries of one tensor per scan block
 constexpr int kStepBlocksMax = 2048;  // blocks of the product kernels (8 per CU), each looping over tiles
+constexpr int kStagedNp = 128;        // padded sides from which the fibre tiles are staged in LDS
+constexpr size_t kStepLdsMax = 65536; // staged fibre tiles of one block: 16 moduli x 16 rows x 256 bytes
 
 constexpr unsigned long long kInfBits = 0x7ff0000000000000ull;
 
@@ -137,129 +139,216 @@ __global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, int
 }
 
 // ------------------------------------------------------ product kernels
-// One wavefront per tile of 16 fibres of one tensor, in a grid-stride loop;
-// for every tile of 16 operator rows: the residue products of every modulus
-// (offset by the MFMA's accumulator input 128, reduced and packed), then
-// either (LAST) the reconstruction of the four entries of each lane, or the
-// rescaling with P.g drops and the stores into the next layout (CONTIG:
-// P.kind == 0, four consecutive bytes per plane).
-// The drop count is a run-time value: with it fixed at compile time the
-// fully unrolled slot loops keep more table values live and need about 200
-// registers, and at 4 wavefronts per SIMD (128 registers) they spill
-// hundreds of bytes; the run-time form spills 48.  The reconstruction needs
-// about 250 registers and runs at 2 wavefronts per SIMD.
+// Per-launch constants of the product kernels.
+struct StepConsts {
+    int n, np, first, ap, nc;
+    int64_t np2, np3, n3, opstride;
+    const int *F0, *F1, *F2;
+    int64_t st0, st1, st2;
+    __device__ explicit StepConsts(const ChainHbmParams& P) {
+        n = P.n;
+        np = P.np;
+        first = kSlots - P.s;  // first active slot; slot u holds modulus index u - first
+        ap = (np + 15) & ~15;
+        nc = (np + 31) / 32;   // k chunks of the MFMA
+        np2 = (int64_t)np * np;
+        np3 = np2 * np;
+        n3 = (int64_t)n * n * n;
+        opstride = (int64_t)ap * np;
+        F0 = P.fexp + P.fin[0] * np;
+        F1 = P.fexp + P.fin[1] * np;
+        F2 = P.fexp + P.fin[2] * np;
+        st0 = P.fin[0] == 0 ? 1 : P.fin[0] == 1 ? n : (int64_t)n * n;
+        st1 = P.fin[1] == 0 ? 1 : P.fin[1] == 1 ? n : (int64_t)n * n;
+        st2 = P.fin[2] == 0 ? 1 : P.fin[2] == 1 ? n : (int64_t)n * n;
+    }
+};
+
+// One tile: 16 fibres f0 .. f0 + 15 of tensor t against operator rows
+// a0 .. a0 + 15.  The residue products of every modulus (offset by the
+// MFMA's accumulator input 128, reduced and packed; xload(qm, c) gives this
+// lane's 8 bytes of the fibres' operand for modulus index qm and k chunk c,
+// called only where 32 c + 8 kq < np), then either (LAST) the
+// reconstruction of the four entries of each lane, or the rescaling with
+// P.g drops and the stores into the next layout (CONTIG: P.kind == 0, four
+// consecutive bytes per plane).
+// fa = f0 + 4 kq is the lane's first fibre within the tensor (< np^2 <=
+// 2^16), at positions p1 = fa mod np, p2 = fa / np (the caller's, once per
+// fibre tile).
+template <bool CONTIG, bool LAST, class XLoad>
+__device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepConsts& K, const ChainTables* T,
+                                          int64_t t, int fa, int p1, int p2, int a0, int lane, const XLoad& xload,
+                                          unsigned long long M, double alpha) {
+    const int r16 = lane & 15;  // MFMA row of the fibres' operand / column of the operator's and the output
+    const int kq = lane >> 4;   // k group of the operands (8 bytes each), output row group
+    const int a = a0 + r16;
+    const int8_t* opl = P.ops + (int64_t)a * K.np + 8 * kq;
+    uint32_t pk[kSlots];
+#pragma unroll
+    for (int u0 = 0; u0 < kSlots; u0 += 4) {
+        v4i acc[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = v4i{128, 128, 128, 128};
+#pragma unroll 1
+        for (int c = 0; c < K.nc; ++c) {
+            const bool ok = 32 * c + 8 * kq < K.np;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int u = u0 + v;
+                if (u >= K.first) {
+                    const int qm = u - K.first;
+                    const long a8 = ok ? xload(qm, c) : 0l;
+                    const long b8 = ok ? *(const long*)(opl + qm * K.opstride + 32 * c) : 0l;
+                    acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8, b8, acc[v], 0, 0, 0);
+                }
+            }
+        }
+        // unused slots keep the accumulator input: the byte of a zero residue
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int a4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
+            pk[u0 + v] = pack_products(a4, T, u0 + v);
+        }
+    }
+    if (LAST) {
+        double V[4];
+        mrc_horner(pk, T, V);
+        if (p2 < K.n && a < K.n) {
+            const int f12 = K.F1[p2] + K.F2[a];
+            double* y = P.Y + t * K.n3 + p2 * K.st1 + a * K.st2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (p1 + q < K.n)
+                    y[(p1 + q) * K.st0] = M < kInfBits ? ldexp(alpha, -(K.F0[p1 + q] + f12)) * V[q] : __builtin_nan("");
+        }
+    } else {
+        float r[4][kSlots];
+        unpack_tile(pk, r);
+        if (P.g == 0) {
+#pragma unroll
+            for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
+        }
+        // the next layout: (p1, p2, a) with the four entries contiguous,
+        // (p2, p1, a) or (a, p1, p2) with them np apart
+        int8_t* base = P.out + t * K.np3;
+        int64_t step = 0;
+        if (CONTIG) {
+            base += fa + K.np2 * a;
+        } else if (P.kind == 1) {
+            base += p2 + (int64_t)K.np * p1 + K.np2 * a;
+            step = K.np;
+        } else {
+            base += a + (int64_t)K.np * fa;
+            step = K.np;
+        }
+        const bool ok = a < K.np;
+        const int first = K.first;
+        const int64_t pstride = P.pstride;
+        const auto put = [=](int u, float r0, float r1, float r2, float r3) {
+            if (u >= first && ok) store4<!CONTIG>(base + (int64_t)(u - first) * pstride, step, r0, r1, r2, r3);
+        };
+        rescale_extend<-1>(P.g, r, T, put);
+    }
+}
+
+// the constant tables into LDS (read per use; hoisted into registers they
+// would not fit)
+__device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTables& KT) {
+    static_assert(sizeof(ChainTables) % 4 == 0, "words");
+    for (int x = threadIdx.x; x < (int)(sizeof(ChainTables) / 4); x += blockDim.x)
+        ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
+    __syncthreads();
+}
+
+// Occupancy of both forms: the drop count is a run-time value (with it
+// fixed at compile time the unrolled slot loops keep more table values live,
+// about 200 registers, and spill hundreds of bytes at 128; the run-time form
+// spills about 40) at 4 wavefronts per SIMD; the reconstruction needs about
+// 250 registers and runs at 2.
+//
+// Direct form (np < 128): one wavefront per tile of 16 fibres, in a
+// grid-stride loop, walking the operator's rows in tiles of 16 and reading
+// the fibres' operand from memory (the tile stays in cache between row
+// tiles when there are few of them).
 template <bool CONTIG, bool LAST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_kernel(ChainHbmParams P) {
     __shared__ ChainTables KT;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    static_assert(sizeof(ChainTables) % 4 == 0, "words");
-    for (int x = tid; x < (int)(sizeof(ChainTables) / 4); x += 256)
-        ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
-    __syncthreads();
-    const ChainTables* T = &KT;
-
-    const int n = P.n, np = P.np;
-    const int first = kSlots - P.s;  // first active slot; slot u holds modulus index u - first
-    const int64_t np2 = (int64_t)np * np, np3 = np2 * np;
-    const int64_t nft = np2 / 16;  // fibre tiles per tensor (np^2 is a multiple of 64)
-    const int ap = (np + 15) & ~15;
-    const int nc = (np + 31) / 32;  // k chunks of the MFMA
-    const int64_t opstride = (int64_t)ap * np;
-    const int r16 = lane & 15;  // MFMA row of the fibres' operand / column of the operator's and the output
-    const int kq = lane >> 4;   // k group of the operands (8 bytes each), output row group
+    stage_tables(P, KT);
+    const StepConsts K(P);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int64_t nft = K.np2 / 16;  // fibre tiles per tensor (np^2 is a multiple of 64)
     const int64_t tiles = P.batch * nft;
-    const int64_t n3 = (int64_t)n * n * n;
-    const int* F0 = P.fexp + P.fin[0] * np;
-    const int* F1 = P.fexp + P.fin[1] * np;
-    const int* F2 = P.fexp + P.fin[2] * np;
-    const int64_t st0 = P.fin[0] == 0 ? 1 : P.fin[0] == 1 ? n : (int64_t)n * n;
-    const int64_t st1 = P.fin[1] == 0 ? 1 : P.fin[1] == 1 ? n : (int64_t)n * n;
-    const int64_t st2 = P.fin[2] == 0 ? 1 : P.fin[2] == 1 ? n : (int64_t)n * n;
-
 #pragma unroll 1
     for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < tiles; w += (int64_t)gridDim.x * 4) {
         const int64_t t = w / nft;
-        const int64_t f0 = (w % nft) * 16;
-        const int8_t* xin = P.in + t * np3 + (f0 + r16) * np + 8 * kq;
-        const int64_t fa = f0 + 4 * kq;  // the lane's first fibre
-        const int p1 = (int)(fa % np), p2 = (int)(fa / np);
+        const int f0 = (int)(w % nft) * 16;
+        const int8_t* xin = P.in + t * K.np3 + (int64_t)(f0 + r16) * K.np + 8 * kq;
+        // captured by value: a reference into the kernel's parameters keeps
+        // them in memory and costs about 100 bytes of spills per lane
+        const int64_t pstride = P.pstride;
+        const auto xload = [=](int qm, int c) { return *(const long*)(xin + (int64_t)qm * pstride + 32 * c); };
+        const int fa = f0 + 4 * kq;
+        const int p1 = fa % K.np, p2 = fa / K.np;
         const unsigned long long M = LAST ? P.smax[t] : 0ull;
         const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
 #pragma unroll 1
-        for (int a0 = 0; a0 < np; a0 += 16) {
+        for (int a0 = 0; a0 < K.np; a0 += 16) {
             asm volatile("" ::: "memory");
-            const int a = a0 + r16;
-            const int8_t* opl = P.ops + (int64_t)a * np + 8 * kq;
-            uint32_t pk[kSlots];
-#pragma unroll
-            for (int u0 = 0; u0 < kSlots; u0 += 4) {
-                v4i acc[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[v] = v4i{128, 128, 128, 128};
+            step_tile<CONTIG, LAST>(P, K, &KT, t, fa, p1, p2, a0, lane, xload, M, alpha);
+        }
+    }
+}
+
+// Staged form (np >= 128): a block takes F fibre tiles of one tensor at a
+// time (F = 1 there), stages their rows of every plane in LDS in MFMA
+// fragment order (the word at row r, k bytes 8 w .. 8 w + 7 of fibre tile f
+// and modulus index q goes to lane r + 16 (w mod 4) of chunk w / 4, so every
+// fragment read is 512 contiguous bytes), and its 4 wavefronts take the
+// (fibre tile, operator-row tile) pairs in turn.  The fibres are read from
+// HBM once; in the direct form a fibre tile's 16 row tiles re-fetched it
+// after the tiles in flight on an XCD (about 4 MB at n = 256) had evicted it
+// from L2, 36 times the planes per launch at n = 256.
+template <bool CONTIG, bool LAST>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
+void chain_step_staged_kernel(ChainHbmParams P, int F) {
+    __shared__ ChainTables KT;
+    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][nc][64 lanes][8 bytes]
+    stage_tables(P, KT);
+    const StepConsts K(P);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int na = K.ap / 16;                   // operator-row tiles
+    const int64_t nft = K.np2 / 16;
+    const int words_row = K.np / 8;             // 8-byte words per fibre row
+    const int words = P.s * F * 16 * words_row; // words staged per block tile
+    const int64_t btiles = P.batch * (nft / F);
 #pragma unroll 1
-                for (int c = 0; c < nc; ++c) {
-                    const bool ok = 32 * c + 8 * kq < np;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int u = u0 + v;
-                        if (u >= first) {
-                            const int64_t qm = u - first;
-                            const long a8 = ok ? *(const long*)(xin + qm * P.pstride + 32 * c) : 0l;
-                            const long b8 = ok ? *(const long*)(opl + qm * opstride + 32 * c) : 0l;
-                            acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8, b8, acc[v], 0, 0, 0);
-                        }
-                    }
-                }
-                // unused slots keep the accumulator input: the byte of a zero residue
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int a4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
-                    pk[u0 + v] = pack_products(a4, T, u0 + v);
-                }
-            }
-            if (LAST) {
-                double V[4];
-                mrc_horner(pk, T, V);
-                if (p2 < n && a < n) {
-                    const int f12 = F1[p2] + F2[a];
-                    double* y = P.Y + t * n3 + p2 * st1 + a * st2;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (p1 + q < n)
-                            y[(p1 + q) * st0] =
-                                M < kInfBits ? ldexp(alpha, -(F0[p1 + q] + f12)) * V[q] : __builtin_nan("");
-                }
-            } else {
-                float r[4][kSlots];
-                unpack_tile(pk, r);
-                if (P.g == 0) {
-#pragma unroll
-                    for (int u = 0; u < kSlots; ++u)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
-                }
-                // the next layout: (p1, p2, a) with the four entries
-                // contiguous, (p2, p1, a) or (a, p1, p2) with them np apart
-                int8_t* base = P.out + t * np3;
-                int64_t step = 0;
-                if (CONTIG) {
-                    base += fa + np2 * a;
-                } else if (P.kind == 1) {
-                    base += p2 + (int64_t)np * p1 + np2 * a;
-                    step = np;
-                } else {
-                    base += a + (int64_t)np * fa;
-                    step = np;
-                }
-                const bool ok = a < np;
-                const auto put = [&](int u, float r0, float r1, float r2, float r3) {
-                    if (u >= first && ok) store4<!CONTIG>(base + (int64_t)(u - first) * P.pstride, step, r0, r1, r2, r3);
-                };
-                rescale_extend<-1>(P.g, r, T, put);
-            }
+    for (int64_t bt = blockIdx.x; bt < btiles; bt += gridDim.x) {
+        const int64_t t = bt / (nft / F);
+        const int fb0 = (int)(bt % (nft / F)) * F * 16;  // first fibre of the block tile
+        __syncthreads();  // the previous tile's fragments are read
+        for (int x = tid; x < words; x += 256) {
+            const int w = x % words_row;
+            const int rest = x / words_row;
+            const int row = rest % (16 * F), q = rest / (16 * F);
+            const long v = *(const long*)(P.in + q * P.pstride + t * K.np3 + (int64_t)(fb0 + row) * K.np + 8 * w);
+            *(long*)(xs + ((((int64_t)q * F + (row >> 4)) * K.nc + (w >> 2)) * 64 + (row & 15) + 16 * (w & 3)) * 8) = v;
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int pr = wave; pr < F * na; pr += 4) {
+            asm volatile("" ::: "memory");
+            const int f = pr / na;
+            const int8_t* xl = xs + ((int64_t)f * K.nc * 64 + lane) * 8;
+            const int64_t qstride = (int64_t)F * K.nc * 512;
+            const auto xload = [=](int qm, int c) { return *(const long*)(xl + qm * qstride + c * 512); };
+            const int fa = fb0 + 16 * f + 4 * (lane >> 4);
+            const unsigned long long M = LAST ? P.smax[t] : 0ull;
+            const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
+            step_tile<CONTIG, LAST>(P, K, &KT, t, fa, fa % K.np, fa / K.np, (pr % na) * 16, lane, xload, M, alpha);
         }
     }
 }
@@ -293,16 +382,33 @@ hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st)
     if (!last && (P.g < 0 || P.g >= P.s || P.kind < 0 || P.kind > 2)) return hipErrorInvalidValue;
     for (int j = 0; j < 3; ++j)
         if (P.fin[j] < 0 || P.fin[j] > 2) return hipErrorInvalidValue;
-    const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
-    const int64_t want = (tiles + 3) / 4;
-    const unsigned blocks = (unsigned)(want < kStepBlocksMax ? want : kStepBlocksMax);
-    const dim3 grid(blocks), block(256);
-    if (last)
-        hipLaunchKernelGGL((chain_step_kernel<true, true>), grid, block, 0, st, P);
-    else if (P.kind == 0)
-        hipLaunchKernelGGL((chain_step_kernel<true, false>), grid, block, 0, st, P);
-    else
-        hipLaunchKernelGGL((chain_step_kernel<false, false>), grid, block, 0, st, P);
+    const dim3 block(256);
+    if (P.np >= kStagedNp) {
+        // F fibre tiles per block so that its 4 wavefronts have at least 4
+        // (fibre tile, operator-row tile) pairs
+        const int na = ((P.np + 15) & ~15) / 16;
+        const int F = na >= 4 ? 1 : na >= 2 ? 2 : 4;
+        const size_t lds = (size_t)P.s * F * ((P.np + 31) / 32) * 512;
+        if (lds > kStepLdsMax) return hipErrorInvalidValue;
+        const int64_t btiles = P.batch * ((int64_t)P.np * P.np / 16 / F);
+        const dim3 grid((unsigned)(btiles < kStepBlocksMax ? btiles : kStepBlocksMax));
+        if (last)
+            hipLaunchKernelGGL((chain_step_staged_kernel<true, true>), grid, block, lds, st, P, F);
+        else if (P.kind == 0)
+            hipLaunchKernelGGL((chain_step_staged_kernel<true, false>), grid, block, lds, st, P, F);
+        else
+            hipLaunchKernelGGL((chain_step_staged_kernel<false, false>), grid, block, lds, st, P, F);
+    } else {
+        const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
+        const int64_t want = (tiles + 3) / 4;
+        const dim3 grid((unsigned)(want < kStepBlocksMax ? want : kStepBlocksMax));
+        if (last)
+            hipLaunchKernelGGL((chain_step_kernel<true, true>), grid, block, 0, st, P);
+        else if (P.kind == 0)
+            hipLaunchKernelGGL((chain_step_kernel<true, false>), grid, block, 0, st, P);
+        else
+            hipLaunchKernelGGL((chain_step_kernel<false, false>), grid, block, 0, st, P);
+    }
     return hipGetLastError();
 }
 
