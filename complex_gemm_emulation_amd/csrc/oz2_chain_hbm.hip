@@ -311,9 +311,12 @@ void chain_step_kernel(ChainHbmParams P) {
 // (fibre tile, operator-row tile) pairs in turn.  The fibres are read from
 // HBM once; in the direct form a fibre tile's 16 row tiles re-fetched it
 // after the tiles in flight on an XCD (about 4 MB at n = 256) had evicted it
-// from L2, 36 times the planes per launch at n = 256.
-template <bool CONTIG, bool LAST>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
+// from L2, 36 times the planes per launch at n = 256.  NW wavefronts per
+// block: 8 when a block stages more than 32 KiB (then LDS admits only two
+// blocks per compute unit, and 4 wavefronts each would leave 2 per SIMD to
+// interleave the dependent modular steps: 12% slower at n = 256), else 4.
+template <bool CONTIG, bool LAST, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_staged_kernel(ChainHbmParams P, int F) {
     __shared__ ChainTables KT;
     extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][nc][64 lanes][8 bytes]
@@ -330,7 +333,7 @@ void chain_step_staged_kernel(ChainHbmParams P, int F) {
         const int64_t t = bt / (nft / F);
         const int fb0 = (int)(bt % (nft / F)) * F * 16;  // first fibre of the block tile
         __syncthreads();  // the previous tile's fragments are read
-        for (int x = tid; x < words; x += 256) {
+        for (int x = tid; x < words; x += 64 * NW) {
             const int w = x % words_row;
             const int rest = x / words_row;
             const int row = rest % (16 * F), q = rest / (16 * F);
@@ -339,7 +342,7 @@ void chain_step_staged_kernel(ChainHbmParams P, int F) {
         }
         __syncthreads();
 #pragma unroll 1
-        for (int pr = wave; pr < F * na; pr += 4) {
+        for (int pr = wave; pr < F * na; pr += NW) {
             asm volatile("" ::: "memory");
             const int f = pr / na;
             const int8_t* xl = xs + ((int64_t)f * K.nc * 64 + lane) * 8;
@@ -392,12 +395,22 @@ hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st)
         if (lds > kStepLdsMax) return hipErrorInvalidValue;
         const int64_t btiles = P.batch * ((int64_t)P.np * P.np / 16 / F);
         const dim3 grid((unsigned)(btiles < kStepBlocksMax ? btiles : kStepBlocksMax));
-        if (last)
-            hipLaunchKernelGGL((chain_step_staged_kernel<true, true>), grid, block, lds, st, P, F);
-        else if (P.kind == 0)
-            hipLaunchKernelGGL((chain_step_staged_kernel<true, false>), grid, block, lds, st, P, F);
-        else
-            hipLaunchKernelGGL((chain_step_staged_kernel<false, false>), grid, block, lds, st, P, F);
+        if (lds > 32768) {
+            const dim3 block8(512);
+            if (last)
+                hipLaunchKernelGGL((chain_step_staged_kernel<true, true, 8>), grid, block8, lds, st, P, F);
+            else if (P.kind == 0)
+                hipLaunchKernelGGL((chain_step_staged_kernel<true, false, 8>), grid, block8, lds, st, P, F);
+            else
+                hipLaunchKernelGGL((chain_step_staged_kernel<false, false, 8>), grid, block8, lds, st, P, F);
+        } else {
+            if (last)
+                hipLaunchKernelGGL((chain_step_staged_kernel<true, true, 4>), grid, block, lds, st, P, F);
+            else if (P.kind == 0)
+                hipLaunchKernelGGL((chain_step_staged_kernel<true, false, 4>), grid, block, lds, st, P, F);
+            else
+                hipLaunchKernelGGL((chain_step_staged_kernel<false, false, 4>), grid, block, lds, st, P, F);
+        }
     } else {
         const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
         const int64_t want = (tiles + 3) / 4;
