@@ -1,7 +1,7 @@
 // oz2_chain_hbm.hip -- persistent Ozaki scheme II for chained tensor mode
-// products (OzII-RescaleBE) on tensors too large for one block's LDS
-// (n > 16): the residue planes stay in HBM between the products, one kernel
-// per product.
+// products (OzII-RescaleBE) with the residue planes in HBM between the
+// products, one kernel per product: tensors too large for one block's LDS
+// (n > 16), and small ones (n <= 8) that the LDS kernel would pad to 16^3.
 //
 // "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products":
 //  - Sec. 5.2 and Algorithm 7: the tensor is encoded once with one exponent,
@@ -26,10 +26,12 @@
 // p0 + np p1 + np^2 p2 with p0 the direction the next product contracts.
 // Fibre f = p1 + np p2 (np^2 per tensor) is then the row of np bytes at
 // f np, and a product is, per modulus, Y^T = R^T Abar^T on
-// v_mfma_i32_16x16x32_i8: a wavefront takes 16 fibres (the MFMA's rows;
-// each lane loads 8 bytes of one row) against 16 operator rows (the MFMA's
-// columns) and loops over the operator's rows in tiles of 16, so a fibre
-// tile is read from HBM once and from cache for the other row tiles.  Each
+// v_mfma_i32_16x16x32_i8: a tile is 16 fibres (the MFMA's rows; each lane
+// loads 8 bytes of one row) against 16 operator rows (the MFMA's columns).
+// For padded sides below 128 a wavefront walks the operator's row tiles of
+// one fibre tile, reading the fibres from memory (they stay in cache between
+// the few row tiles); from 128 on a block stages its fibre tile in LDS once
+// and its wavefronts share it across the row tiles.  Each
 // lane then holds four consecutive fibres of one output row for every
 // modulus, and reduces, rescales and base-extends them in registers with the
 // arithmetic of the LDS kernel (oz2_chain_device.h).  The output layout puts
