@@ -87,8 +87,9 @@ struct oz2_chain_plan {
     ChainParams params;        // b, g, Qd and device pointers; X, Y, batch per call
     void* mem = nullptr;       // device: ChainTables, LDS-kernel residues, fexp, HBM-kernel residues
     int np = 0, ap = 0;        // n rounded up to 8 (plane padding) and to 16 (operator rows)
+    int ncp = 0;               // pairs of 32-byte MFMA k chunks covering np
     const int* fexp = nullptr;     // device [3][np] row exponents left pending on each direction
-    const int8_t* hops = nullptr;  // device [d][s][ap][np] operator residues of the HBM kernels
+    const int8_t* hops = nullptr;  // device [d][s][ap / 16][ncp][64][16] operator residues of the HBM kernels
 };
 
 namespace {
@@ -977,10 +978,11 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     if (!plan) return OZ2_STATUS_ALLOC_FAILED;
     plan->np = (nn + 7) & ~7;
     plan->ap = (plan->np + 15) & ~15;
-    const int np = plan->np, ap = plan->ap;
+    plan->ncp = (plan->np + 63) / 64;
+    const int np = plan->np, ap = plan->ap, ncp = plan->ncp;
     const bool lds = nn <= kChainN;
     const size_t lds_bytes = lds ? (size_t)depth * kChainMaxS * kChainN * kChainN : 0;
-    const size_t hops_bytes = (size_t)depth * s * ap * np;
+    const size_t hops_bytes = (size_t)depth * s * ap * ncp * 64;
     const size_t off_lds = align_up(sizeof(ChainTables));
     const size_t off_fexp = align_up(off_lds + lds_bytes);
     const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
@@ -1012,7 +1014,11 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
                     for (int k = 0; k < nn; ++k) {
                         const int8_t v = res[(((size_t)i * s + q) * nn + a) * nn + k];
                         if (lds) lo[(((size_t)i * kChainMaxS + q) * kChainN + a) * kChainN + k] = v;
-                        ho[(((size_t)i * s + q) * ap + a) * np + k] = v;  // [d][s][ap][np], zero padded
+                        // fragment order, zero padded: row a = 16 at + r, byte k = 64 cp + 16 j + e at
+                        // [i][q][at][cp][r + 16 j][e], the 16 bytes lane r + 16 j of a wavefront loads for
+                        // the two MFMA k chunks of pair cp
+                        const int at = a >> 4, r = a & 15, cp = k >> 6, j = (k >> 4) & 3, e = k & 15;
+                        ho[((((((size_t)i * s + q) * (ap / 16) + at) * ncp + cp) * 64) + r + 16 * j) * 16 + e] = v;
                     }
         for (int m = 0; m < 3; ++m)
             for (int a = 0; a < nn; ++a) fe[m * np + a] = fexp[(size_t)m * nn + a];
@@ -1108,7 +1114,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
             P.out = last ? nullptr : buf[(i + 1) & 1];
             P.g = C.g[i];
             P.kind = C.kind[i];
-            P.ops = plan->hops + (size_t)i * s * plan->ap * np;
+            P.ops = plan->hops + (size_t)i * s * plan->ap * plan->ncp * 64;
             OZ2_LAUNCH(launch_chain_step(P, last, stm));
         }
         if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));

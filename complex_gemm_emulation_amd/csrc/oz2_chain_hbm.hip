@@ -52,6 +52,7 @@ namespace {
 using namespace chain;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef long v2l __attribute__((ext_vector_type(2)));
 
 constexpr int kScanChunk = 4096;      // entries of one tensor per scan block
 constexpr int kStepBlocksMax = 2048;  // blocks of the product kernels (8 per CU), each looping over tiles
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, int
 // ------------------------------------------------------ product kernels
 // Per-launch constants of the product kernels.
 struct StepConsts {
-    int n, np, first, ap, nc;
-    int64_t np2, np3, n3, opstride;
+    int n, np, first, ap;
+    int64_t np2, np3, n3, opq;
     const int *F0, *F1, *F2;
     int64_t st0, st1, st2;
     __device__ explicit StepConsts(const ChainHbmParams& P) {
@@ -152,11 +153,10 @@ struct StepConsts {
         np = P.np;
         first = kSlots - P.s;  // first active slot; slot u holds modulus index u - first
         ap = (np + 15) & ~15;
-        nc = (np + 31) / 32;   // k chunks of the MFMA
         np2 = (int64_t)np * np;
         np3 = np2 * np;
         n3 = (int64_t)n * n * n;
-        opstride = (int64_t)ap * np;
+        opq = (int64_t)ap * ((np + 63) / 64) * 64;  // operator bytes per modulus
         F0 = P.fexp + P.fin[0] * np;
         F1 = P.fexp + P.fin[1] * np;
         F2 = P.fexp + P.fin[2] * np;
@@ -168,48 +168,68 @@ struct StepConsts {
 
 // One tile: 16 fibres f0 .. f0 + 15 of tensor t against operator rows
 // a0 .. a0 + 15.  The residue products of every modulus (offset by the
-// MFMA's accumulator input 128, reduced and packed; xload(qm, c) gives this
-// lane's 8 bytes of the fibres' operand for modulus index qm and k chunk c,
-// called only where 32 c + 8 kq < np), then either (LAST) the
+// MFMA's accumulator input 128, reduced and packed), then either (LAST) the
 // reconstruction of the four entries of each lane, or the rescaling with
 // P.g drops and the stores into the next layout (CONTIG: P.kind == 0, four
 // consecutive bytes per plane).
+// The contraction runs over NCP pairs of 32-byte k chunks: lane r + 16 j
+// holds bytes 64 cp + 16 j .. 64 cp + 16 j + 15 of its row (fibre r of the
+// tile, operator row a0 + r) for pair cp, the first 8 for one MFMA and the
+// last 8 for the other.  Both operands take the same k for the same lane
+// and half, so the two MFMAs of every pair sum the same products as two
+// chunks of 32 consecutive k would.  xload(qm, cp) gives the fibres' 16
+// bytes (zero at k >= np); the operator's come in fragment order (zero
+// padded), 1 KiB per wavefront per pair, all four moduli of a slot group
+// loaded before its MFMAs.
 // fa = f0 + 4 kq is the lane's first fibre within the tensor (< np^2 <=
 // 2^16), at positions p1 = fa mod np, p2 = fa / np (the caller's, once per
 // fibre tile).
-template <bool CONTIG, bool LAST, class XLoad>
+template <bool CONTIG, bool LAST, int NCP, class XLoad>
 __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepConsts& K, const ChainTables* T,
                                           int64_t t, int fa, int p1, int p2, int a0, int lane, const XLoad& xload,
                                           unsigned long long M, double alpha) {
-    const int r16 = lane & 15;  // MFMA row of the fibres' operand / column of the operator's and the output
-    const int kq = lane >> 4;   // k group of the operands (8 bytes each), output row group
-    const int a = a0 + r16;
-    const int8_t* opl = P.ops + (int64_t)a * K.np + 8 * kq;
+    const int a = a0 + (lane & 15);  // column of the output (operator row)
+    const int8_t* opf = P.ops + ((int64_t)(a0 >> 4) * NCP * 64 + lane) * 16;
     uint32_t pk[kSlots];
 #pragma unroll
     for (int u0 = 0; u0 < kSlots; u0 += 4) {
+        // one slot group's operands in registers at a time: without the
+        // barrier the scheduler hoists every group's loads and spills
+        __builtin_amdgcn_sched_barrier(0);
+        if (u0 + 3 < K.first) {  // no modulus in the group: residues of zero
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pk[u0 + v] = 0x80808080u;
+            continue;
+        }
+        // A slot below K.first (modulus 1) takes modulus index 0's operands:
+        // its reduction modulo 1 gives the byte of a zero residue whatever
+        // the products, so the group needs no branch.
+        int qm[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) qm[v] = u0 + v >= K.first ? u0 + v - K.first : 0;
+        v2l ob[4][NCP];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int cp = 0; cp < NCP; ++cp) ob[v][cp] = *(const v2l*)(opf + (int64_t)qm[v] * K.opq + cp * 1024);
         v4i acc[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = v4i{128, 128, 128, 128};
-#pragma unroll 1
-        for (int c = 0; c < K.nc; ++c) {
-            const bool ok = 32 * c + 8 * kq < K.np;
+        for (int v = 0; v < 4; ++v) {
+            acc[v] = v4i{128, 128, 128, 128};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int u = u0 + v;
-                if (u >= K.first) {
-                    const int qm = u - K.first;
-                    const long a8 = ok ? xload(qm, c) : 0l;
-                    const long b8 = ok ? *(const long*)(opl + qm * K.opstride + 32 * c) : 0l;
-                    acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a8, b8, acc[v], 0, 0, 0);
-                }
+            for (int cp = 0; cp < NCP; ++cp) {
+                const v2l x = xload(qm[v], cp);
+                acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(x[0], ob[v][cp][0], acc[v], 0, 0, 0);
+                acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(x[1], ob[v][cp][1], acc[v], 0, 0, 0);
             }
         }
-        // unused slots keep the accumulator input: the byte of a zero residue
+        // each word is pinned here, or the reductions sink below the later
+        // groups and their accumulators spill
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int a4[4] = {acc[v][0], acc[v][1], acc[v][2], acc[v][3]};
             pk[u0 + v] = pack_products(a4, T, u0 + v);
+            asm volatile("" : "+v"(pk[u0 + v]));
         }
     }
     if (LAST) {
@@ -268,13 +288,15 @@ __device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTable
 // fixed at compile time the unrolled slot loops keep more table values live,
 // about 200 registers, and spill hundreds of bytes at 128; the run-time form
 // spills about 40) at 4 wavefronts per SIMD; the reconstruction needs about
-// 250 registers and runs at 2.
+// 250 registers and runs at 2.  NCP (pairs of k chunks, np / 64 rounded up)
+// is a compile-time constant so that every operator fragment of a slot group
+// is loaded before its first MFMA.
 //
 // Direct form (np < 128): one wavefront per tile of 16 fibres, in a
 // grid-stride loop, walking the operator's rows in tiles of 16 and reading
 // the fibres' operand from memory (the tile stays in cache between row
 // tiles when there are few of them).
-template <bool CONTIG, bool LAST>
+template <bool CONTIG, bool LAST, int NCP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_kernel(ChainHbmParams P) {
     __shared__ ChainTables KT;
@@ -288,11 +310,11 @@ void chain_step_kernel(ChainHbmParams P) {
     for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < tiles; w += (int64_t)gridDim.x * 4) {
         const int64_t t = w / nft;
         const int f0 = (int)(w % nft) * 16;
-        const int8_t* xin = P.in + t * K.np3 + (int64_t)(f0 + r16) * K.np + 8 * kq;
+        const int8_t* xt = P.in + t * K.np3;  // the tensor in plane 0
         // captured by value: a reference into the kernel's parameters keeps
         // them in memory and costs about 100 bytes of spills per lane
         const int64_t pstride = P.pstride;
-        const auto xload = [=](int qm, int c) { return *(const long*)(xin + (int64_t)qm * pstride + 32 * c); };
+        const int np = K.np, k0 = 16 * kq;
         const int fa = f0 + 4 * kq;
         const int p1 = fa % K.np, p2 = fa / K.np;
         const unsigned long long M = LAST ? P.smax[t] : 0ull;
@@ -300,62 +322,103 @@ void chain_step_kernel(ChainHbmParams P) {
 #pragma unroll 1
         for (int a0 = 0; a0 < K.np; a0 += 16) {
             asm volatile("" ::: "memory");
-            step_tile<CONTIG, LAST>(P, K, &KT, t, fa, p1, p2, a0, lane, xload, M, alpha);
+            // the lane's fibre row (< np^3 <= 2^24), opaque in each row tile:
+            // hoisted out of this loop, the 16 NCP fibre addresses would hold
+            // registers across the rescaling and spill
+            int xrow = (f0 + r16) * np;
+            asm volatile("" : "+v"(xrow));
+            // bytes at k >= np (the row ends at np, a multiple of 8) are zero;
+            // their loads read the row's first bytes instead, so that no load
+            // is conditional
+            const auto xload = [=](int qm, int cp) {
+                const int8_t* x = xt + (int64_t)qm * pstride + xrow;
+                const int k = k0 + 64 * cp;
+                const long lo = *(const long*)(x + (k < np ? k : 0));
+                const long hi = *(const long*)(x + (k + 8 < np ? k + 8 : 0));
+                return v2l{k < np ? lo : 0l, k + 8 < np ? hi : 0l};
+            };
+            step_tile<CONTIG, LAST, NCP>(P, K, &KT, t, fa, p1, p2, a0, lane, xload, M, alpha);
         }
     }
 }
 
 // Staged form (np >= 128): a block takes F fibre tiles of one tensor at a
-// time (F = 1 there), stages their rows of every plane in LDS in MFMA
-// fragment order (the word at row r, k bytes 8 w .. 8 w + 7 of fibre tile f
-// and modulus index q goes to lane r + 16 (w mod 4) of chunk w / 4, so every
-// fragment read is 512 contiguous bytes), and its 4 wavefronts take the
-// (fibre tile, operator-row tile) pairs in turn.  The fibres are read from
-// HBM once; in the direct form a fibre tile's 16 row tiles re-fetched it
-// after the tiles in flight on an XCD (about 4 MB at n = 256) had evicted it
-// from L2, 36 times the planes per launch at n = 256.  NW wavefronts per
-// block: 8 when a block stages more than 32 KiB (then LDS admits only two
-// blocks per compute unit, and 4 wavefronts each would leave 2 per SIMD to
-// interleave the dependent modular steps: 12% slower at n = 256), else 4.
-template <bool CONTIG, bool LAST, int NW>
+// time (F = 1 there) and stages their rows of every plane in LDS in the
+// operand order of the MFMAs, [q][F][NCP][64 lanes][16 bytes] (lane r + 16 j
+// of pair cp: bytes 64 cp + 16 j .. + 15 of fibre row r, zero at k >= np),
+// so that both the staging copy and every operand read are contiguous; its
+// NW wavefronts take the (fibre tile, operator-row tile) pairs in turn.  The
+// fibres are read from HBM once; in the direct form a fibre tile's 16 row
+// tiles re-fetched it after the tiles in flight on an XCD (about 4 MB at
+// n = 256) had evicted it from L2, 36 times the planes per launch at
+// n = 256.  NW is 8 when a block stages more than 32 KiB and the row tiles
+// divide evenly (then LDS admits only two blocks per compute unit, and 4
+// wavefronts each would leave 2 per SIMD to interleave the dependent
+// modular steps), else 4.
+template <bool CONTIG, bool LAST, int NCP, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_staged_kernel(ChainHbmParams P, int F) {
     __shared__ ChainTables KT;
-    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][nc][64 lanes][8 bytes]
+    extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][NCP][64 lanes][16 bytes]
     stage_tables(P, KT);
     const StepConsts K(P);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int na = K.ap / 16;                   // operator-row tiles
+    const int na = K.ap / 16;                // operator-row tiles
     const int64_t nft = K.np2 / 16;
-    const int words_row = K.np / 8;             // 8-byte words per fibre row
-    const int words = P.s * F * 16 * words_row; // words staged per block tile
+    const int items = P.s * F * NCP * 64;    // 16-byte items staged per block tile
     const int64_t btiles = P.batch * (nft / F);
 #pragma unroll 1
     for (int64_t bt = blockIdx.x; bt < btiles; bt += gridDim.x) {
         const int64_t t = bt / (nft / F);
         const int fb0 = (int)(bt % (nft / F)) * F * 16;  // first fibre of the block tile
-        __syncthreads();  // the previous tile's fragments are read
-        for (int x = tid; x < words; x += 64 * NW) {
-            const int w = x % words_row;
-            const int rest = x / words_row;
-            const int row = rest % (16 * F), q = rest / (16 * F);
-            const long v = *(const long*)(P.in + q * P.pstride + t * K.np3 + (int64_t)(fb0 + row) * K.np + 8 * w);
-            *(long*)(xs + ((((int64_t)q * F + (row >> 4)) * K.nc + (w >> 2)) * 64 + (row & 15) + 16 * (w & 3)) * 8) = v;
+        __syncthreads();  // the previous tile's operands are read
+        for (int x = tid; x < items; x += 64 * NW) {
+            const int L = x & 63, rest = x >> 6;
+            const int cp = rest % NCP, rest2 = rest / NCP;
+            const int f = rest2 % F, q = rest2 / F;
+            const int k = 64 * cp + 16 * (L >> 4);
+            const int8_t* row = P.in + q * P.pstride + t * K.np3 + (int64_t)(fb0 + 16 * f + (L & 15)) * K.np;
+            // zero at k >= np; those loads read the row's first bytes
+            const long lo = *(const long*)(row + (k < K.np ? k : 0));
+            const long hi = *(const long*)(row + (k + 8 < K.np ? k + 8 : 0));
+            *(v2l*)(xs + (int64_t)x * 16) = v2l{k < K.np ? lo : 0l, k + 8 < K.np ? hi : 0l};
         }
         __syncthreads();
 #pragma unroll 1
         for (int pr = wave; pr < F * na; pr += NW) {
             asm volatile("" ::: "memory");
             const int f = pr / na;
-            const int8_t* xl = xs + ((int64_t)f * K.nc * 64 + lane) * 8;
-            const int64_t qstride = (int64_t)F * K.nc * 512;
-            const auto xload = [=](int qm, int c) { return *(const long*)(xl + qm * qstride + c * 512); };
+            const int8_t* xl = xs + ((int64_t)f * NCP * 64 + lane) * 16;
+            const int64_t qstride = (int64_t)F * NCP * 1024;
+            const auto xload = [=](int qm, int cp) { return *(const v2l*)(xl + qm * qstride + cp * 1024); };
             const int fa = fb0 + 16 * f + 4 * (lane >> 4);
             const unsigned long long M = LAST ? P.smax[t] : 0ull;
             const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
-            step_tile<CONTIG, LAST>(P, K, &KT, t, fa, fa % K.np, fa / K.np, (pr % na) * 16, lane, xload, M, alpha);
+            step_tile<CONTIG, LAST, NCP>(P, K, &KT, t, fa, fa % K.np, fa / K.np, (pr % na) * 16, lane, xload,
+                                         M, alpha);
         }
     }
+}
+
+template <int NCP>
+void launch_direct(const ChainHbmParams& P, bool last, dim3 grid, hipStream_t st) {
+    if (last)
+        hipLaunchKernelGGL((chain_step_kernel<true, true, NCP>), grid, dim3(256), 0, st, P);
+    else if (P.kind == 0)
+        hipLaunchKernelGGL((chain_step_kernel<true, false, NCP>), grid, dim3(256), 0, st, P);
+    else
+        hipLaunchKernelGGL((chain_step_kernel<false, false, NCP>), grid, dim3(256), 0, st, P);
+}
+
+template <int NCP, int NW>
+void launch_staged(const ChainHbmParams& P, bool last, dim3 grid, size_t lds, int F, hipStream_t st) {
+    const dim3 block(64 * NW);
+    if (last)
+        hipLaunchKernelGGL((chain_step_staged_kernel<true, true, NCP, NW>), grid, block, lds, st, P, F);
+    else if (P.kind == 0)
+        hipLaunchKernelGGL((chain_step_staged_kernel<true, false, NCP, NW>), grid, block, lds, st, P, F);
+    else
+        hipLaunchKernelGGL((chain_step_staged_kernel<false, false, NCP, NW>), grid, block, lds, st, P, F);
 }
 
 }  // namespace
@@ -387,42 +450,34 @@ hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st)
     if (!last && (P.g < 0 || P.g >= P.s || P.kind < 0 || P.kind > 2)) return hipErrorInvalidValue;
     for (int j = 0; j < 3; ++j)
         if (P.fin[j] < 0 || P.fin[j] > 2) return hipErrorInvalidValue;
-    const dim3 block(256);
+    const int ncp = (P.np + 63) / 64;
     if (P.np >= kStagedNp) {
-        // F fibre tiles per block so that its 4 wavefronts have at least 4
+        // F fibre tiles per block so that its wavefronts have at least 4
         // (fibre tile, operator-row tile) pairs
         const int na = ((P.np + 15) & ~15) / 16;
         const int F = na >= 4 ? 1 : na >= 2 ? 2 : 4;
-        const size_t lds = (size_t)P.s * F * ((P.np + 31) / 32) * 512;
+        const size_t lds = (size_t)P.s * F * ncp * 1024;
         if (lds > kStepLdsMax) return hipErrorInvalidValue;
         const int64_t btiles = P.batch * ((int64_t)P.np * P.np / 16 / F);
         const dim3 grid((unsigned)(btiles < kStepBlocksMax ? btiles : kStepBlocksMax));
-        if (lds > 32768) {
-            const dim3 block8(512);
-            if (last)
-                hipLaunchKernelGGL((chain_step_staged_kernel<true, true, 8>), grid, block8, lds, st, P, F);
-            else if (P.kind == 0)
-                hipLaunchKernelGGL((chain_step_staged_kernel<true, false, 8>), grid, block8, lds, st, P, F);
-            else
-                hipLaunchKernelGGL((chain_step_staged_kernel<false, false, 8>), grid, block8, lds, st, P, F);
-        } else {
-            if (last)
-                hipLaunchKernelGGL((chain_step_staged_kernel<true, true, 4>), grid, block, lds, st, P, F);
-            else if (P.kind == 0)
-                hipLaunchKernelGGL((chain_step_staged_kernel<true, false, 4>), grid, block, lds, st, P, F);
-            else
-                hipLaunchKernelGGL((chain_step_staged_kernel<false, false, 4>), grid, block, lds, st, P, F);
+        const bool nw8 = lds > 32768 && (F * na) % 8 == 0;
+        switch (ncp * 2 + (nw8 ? 1 : 0)) {
+            case 4: launch_staged<2, 4>(P, last, grid, lds, F, st); break;
+            case 5: launch_staged<2, 8>(P, last, grid, lds, F, st); break;
+            case 6: launch_staged<3, 4>(P, last, grid, lds, F, st); break;
+            case 7: launch_staged<3, 8>(P, last, grid, lds, F, st); break;
+            case 8: launch_staged<4, 4>(P, last, grid, lds, F, st); break;
+            case 9: launch_staged<4, 8>(P, last, grid, lds, F, st); break;
+            default: return hipErrorInvalidValue;
         }
     } else {
         const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
         const int64_t want = (tiles + 3) / 4;
         const dim3 grid((unsigned)(want < kStepBlocksMax ? want : kStepBlocksMax));
-        if (last)
-            hipLaunchKernelGGL((chain_step_kernel<true, true>), grid, block, 0, st, P);
-        else if (P.kind == 0)
-            hipLaunchKernelGGL((chain_step_kernel<true, false>), grid, block, 0, st, P);
+        if (ncp == 1)
+            launch_direct<1>(P, last, grid, st);
         else
-            hipLaunchKernelGGL((chain_step_kernel<false, false>), grid, block, 0, st, P);
+            launch_direct<2>(P, last, grid, st);
     }
     return hipGetLastError();
 }

@@ -185,7 +185,8 @@ struct ChainHbmParams {
     int kind;                    // this product's output layout (as ChainParams::kind)
     int fin[3];                  // the last product's entry, fibre and output directions
     double Qd;                   // as ChainParams::Qd
-    const int8_t* ops;           // [s][ap][np] this product's operator residues, ap = np rounded up to 16
+    const int8_t* ops;           // [s][ap / 16][ncp][64][16] this product's operator residues in MFMA fragment
+                                 // order (ap = np rounded up to 16, ncp = np / 64 rounded up)
     const float* tab;            // ChainTables
     const int* fexp;             // [3][np] row exponents left pending on each direction
     unsigned long long* smax;    // [batch] max |x| bit pattern of each tensor (0 before the scan)
