@@ -26,11 +26,13 @@
 // p0 + np p1 + np^2 p2 with p0 the direction the next product contracts.
 // Fibre f = p1 + np p2 (np^2 per tensor) is then the row of np bytes at
 // f np, and a product is, per modulus, Y^T = R^T Abar^T on
-// v_mfma_i32_16x16x32_i8: a tile is 16 fibres (the MFMA's rows; each lane
-// loads 8 bytes of one row) against 16 operator rows (the MFMA's columns).
-// For padded sides below 128 a wavefront walks the operator's row tiles of
-// one fibre tile, reading the fibres from memory (they stay in cache between
-// the few row tiles); from 128 on a block stages its fibre tile in LDS once
+// v_mfma_i32_16x16x32_i8: a tile is 16 fibres (the MFMA's rows) against 16
+// operator rows (the MFMA's columns), k in pairs of 32-byte chunks of which
+// each lane holds 16 consecutive bytes of its row.  The operator's residues
+// are stored in that fragment order (1 KiB per wavefront and pair).  For
+// padded sides below 96 a wavefront walks the operator's row tiles of one
+// fibre tile, reading the fibres from memory (they stay in cache between
+// the few row tiles); from 96 on a block stages its fibre tile in LDS once
 // and its wavefronts share it across the row tiles.  Each
 // lane then holds four consecutive fibres of one output row for every
 // modulus, and reduces, rescales and base-extends them in registers with the
@@ -56,7 +58,7 @@ typedef long v2l __attribute__((ext_vector_type(2)));
 
 constexpr int kScanChunk = 4096;      // entries of one tensor per scan block
 constexpr int kStepBlocksMax = 2048;  // blocks of the product kernels (8 per CU), each looping over tiles
-constexpr int kStagedNp = 128;        // padded sides from which the fibre tiles are staged in LDS
+constexpr int kStagedNp = 96;         // padded sides from which the fibre tiles are staged in LDS
 constexpr size_t kStepLdsMax = 65536; // staged fibre tiles of one block: 16 moduli x 16 rows x 256 bytes
 
 constexpr unsigned long long kInfBits = 0x7ff0000000000000ull;
@@ -292,7 +294,7 @@ __device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTable
 // is a compile-time constant so that every operator fragment of a slot group
 // is loaded before its first MFMA.
 //
-// Direct form (np < 128): one wavefront per tile of 16 fibres, in a
+// Direct form (np < 96): one wavefront per tile of 16 fibres, in a
 // grid-stride loop, walking the operator's rows in tiles of 16 and reading
 // the fibres' operand from memory (the tile stays in cache between row
 // tiles when there are few of them).
@@ -342,16 +344,16 @@ void chain_step_kernel(ChainHbmParams P) {
     }
 }
 
-// Staged form (np >= 128): a block takes F fibre tiles of one tensor at a
+// Staged form (np >= 96): a block takes F fibre tiles of one tensor at a
 // time (F = 1 there) and stages their rows of every plane in LDS in the
 // operand order of the MFMAs, [q][F][NCP][64 lanes][16 bytes] (lane r + 16 j
 // of pair cp: bytes 64 cp + 16 j .. + 15 of fibre row r, zero at k >= np),
 // so that both the staging copy and every operand read are contiguous; its
 // NW wavefronts take the (fibre tile, operator-row tile) pairs in turn.  The
-// fibres are read from HBM once; in the direct form a fibre tile's 16 row
-// tiles re-fetched it after the tiles in flight on an XCD (about 4 MB at
-// n = 256) had evicted it from L2, 36 times the planes per launch at
-// n = 256.  NW is 8 when a block stages more than 32 KiB and the row tiles
+// fibres are read from HBM once; in the direct form a fibre tile's row
+// tiles re-fetch it once the tiles in flight on an XCD (about 4 MB at
+// n = 256) have evicted it from L2, 36 times the planes per launch at
+// n = 256, and from 96 on the staged form is faster.  NW is 8 when a block stages more than 32 KiB and the row tiles
 // divide evenly (then LDS admits only two blocks per compute unit, and 4
 // wavefronts each would leave 2 per SIMD to interleave the dependent
 // modular steps), else 4.
@@ -460,14 +462,19 @@ hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st)
         if (lds > kStepLdsMax) return hipErrorInvalidValue;
         const int64_t btiles = P.batch * ((int64_t)P.np * P.np / 16 / F);
         const dim3 grid((unsigned)(btiles < kStepBlocksMax ? btiles : kStepBlocksMax));
+        // 8 wavefronts only where the row tiles divide evenly among them:
+        // with more than 32 KiB staged that is np > 240 (16 row tiles),
+        // four chunk pairs
         const bool nw8 = lds > 32768 && (F * na) % 8 == 0;
-        switch (ncp * 2 + (nw8 ? 1 : 0)) {
-            case 4: launch_staged<2, 4>(P, last, grid, lds, F, st); break;
-            case 5: launch_staged<2, 8>(P, last, grid, lds, F, st); break;
-            case 6: launch_staged<3, 4>(P, last, grid, lds, F, st); break;
-            case 7: launch_staged<3, 8>(P, last, grid, lds, F, st); break;
-            case 8: launch_staged<4, 4>(P, last, grid, lds, F, st); break;
-            case 9: launch_staged<4, 8>(P, last, grid, lds, F, st); break;
+        switch (ncp) {
+            case 2: launch_staged<2, 4>(P, last, grid, lds, F, st); break;
+            case 3: launch_staged<3, 4>(P, last, grid, lds, F, st); break;
+            case 4:
+                if (nw8)
+                    launch_staged<4, 8>(P, last, grid, lds, F, st);
+                else
+                    launch_staged<4, 4>(P, last, grid, lds, F, st);
+                break;
             default: return hipErrorInvalidValue;
         }
     } else {

@@ -337,10 +337,10 @@ def residue_mode_product(R: np.ndarray, Ares: np.ndarray, mode: int) -> np.ndarr
 
 def prepare_chain(ops_flat: Sequence[np.ndarray], n: int, s: int, modes: Sequence[int] | None = None):
     """Plan and prepare the operators of a chain of depth d = len(ops_flat)
-    (Algorithm 7 lines 2-9): returns a dict with basis, b, g, the effective
-    integer operators and their row exponents, the exponents left pending on
-    each direction, the operator residues per modulus, and the dropped moduli
-    per mode.  modes[i]: the direction (0-based) of operator i, the
+    (Algorithm 7, the steps before the tensor is encoded): returns a dict
+    with basis, b, g, the effective integer operators and their row
+    exponents, the exponents left pending on each direction, the operator
+    residues per modulus, and the dropped moduli per mode.  modes[i]: the direction (0-based) of operator i, the
     directions in turn if None (Algorithm 7 takes any sequence)."""
     basis = list(max_product_moduli(s))           # descending: 256 first
     ops = [matrix_from_flat(a, n) for a in ops_flat]

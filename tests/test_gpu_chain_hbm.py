@@ -12,8 +12,8 @@ equal the LDS kernel bit for bit.  The sides cover padding (n not a multiple
 of 8, operator rows beyond a multiple of 16), the drop counts of the
 compile-time instances and the run-time one, every residue layout kind, the
 sub-batches under a memory limit, and the edge tensors.  Larger sides
-(128, 256) are checked against stored oracle samples in
-test_chain_hbm_golden_samples.
+(100, 128, 136, 200, 256: the staged form of the product kernels) are
+checked against stored oracle samples in test_chain_hbm_golden_samples.
 """
 import json
 import os
@@ -209,18 +209,27 @@ def _golden_cases():
         return json.load(f)["cases"]
 
 
-@pytest.mark.parametrize("case", range(2), ids=["n128", "n256"])
+def _golden_id(c):
+    return f"n{c['n']}" + ("" if c.get("modes") is None else "m" + "".join(map(str, c["modes"])))
+
+
+GOLDEN_CASES = _golden_cases()
+
+
+@pytest.mark.parametrize("case", range(len(GOLDEN_CASES)), ids=[_golden_id(c) for c in GOLDEN_CASES])
 def test_chain_hbm_golden_samples(handle, case):
-    """n = 128 (batch 2) and 256 (batch 1) at s = 16, depth 3: seeded entries
-    of each tensor against values the oracle computed once
-    (tests/golden/make_chain_hbm_samples.py)"""
-    c = _golden_cases()[case]
-    n, s, batch = c["n"], c["s"], c["batch"]
-    _say(f"[chain hbm golden] n={n} s={s} batch={batch}")
-    ops = _ops(n, c["ops_seed"], 3)
+    """the staged product kernels with 2, 3 and 4 pairs of k chunks (n = 100,
+    128, 136, 200, 256; 8 wavefronts per block at 256), in turn and in other
+    mode orders (store kinds 1 and 2): seeded entries of each tensor against
+    values the oracle computed once (tests/golden/make_chain_hbm_samples.py)"""
+    c = GOLDEN_CASES[case]
+    n, s, batch, modes = c["n"], c["s"], c["batch"], c.get("modes")
+    d = 3 if modes is None else len(modes)
+    _say(f"[chain hbm golden] n={n} s={s} batch={batch} modes={modes}")
+    ops = _ops(n, c["ops_seed"], d)
     X = workloads.tensor_batch(n, batch, c["x_seed"])
-    got, info = _run(handle, ops, n, s, X, batch)
-    assert info == (3, c["b"], c["g"]), info
+    got, info = _run(handle, ops, n, s, X, batch, modes)
+    assert info == (d, c["b"], c["g"]), info
     idx = np.array(c["index"], dtype=np.int64)
     want = np.array([float.fromhex(v) for v in c["value"]])
-    _check_bitwise(got[idx], want, f"golden n={n}")
+    _check_bitwise(got[idx], want, f"golden n={n} modes={modes}")
