@@ -827,6 +827,14 @@ def rbe_valu_ops_per_entry(s, g):
     return ops
 
 
+def rbe_product_ops_per_entry(s, gi):
+    """The part of rbe_valu_ops_per_entry that one non-final product takes:
+    the reduction of the s products of an entry, gi drops, the digits of the
+    k = s - gi kept moduli and the base extension to the gi dropped ones."""
+    k = s - gi
+    return 3 * s + 5 * sum(s - 1 - j for j in range(gi)) + 5 * k * (k - 1) // 2 + gi * (k + 3)
+
+
 def run_chain_rbe(args):
     """The 32768 x 16^3 chain by OzII-RescaleBE: one kernel per chain, the
     tensor in residue form from encode to reconstruction."""
@@ -981,11 +989,18 @@ def run_chain_sizes(args):
         if kern == "auto":
             tot_dof += dof
             tot_ms += ms
-        if n == max(CHAIN_SIZES):
-            roofline = dict(kernel="chain_step_kernel (OzII-RescaleBE product + rescaling, HBM residues), n = 256",
-                            bound="alu", achieved=round(valu, 2), peak=round(PEAK_VALU_TOPS, 2), unit="TOP/s",
-                            frac=round(valu / PEAK_VALU_TOPS, 4), traffic=None,
-                            launch_ms=round(sum(phm), 4))
+        if n == max(CHAIN_SIZES) and not lds:
+            # the dominant kernel: the rescaling products (d - 1 launches,
+            # timed together by the phase events on the library's stream)
+            gr = list(plan.g)[:-1]
+            per_launch = phm[2] / len(gr)
+            ops_launch = np.mean([rbe_product_ops_per_entry(s, gi) for gi in gr]) * dof
+            ach = ops_launch / (per_launch * 1e-3) / 1e12
+            roofline = dict(kernel=f"chain_step_staged_kernel (OzII-RescaleBE product and rescaling, residues "
+                                   f"in HBM), n = {n}",
+                            bound="alu", achieved=round(ach, 2), peak=round(PEAK_VALU_TOPS, 2), unit="TOP/s",
+                            frac=round(ach / PEAK_VALU_TOPS, 4), traffic=None, launch_ms=round(per_launch, 4),
+                            ops_per_launch=float(ops_launch))
         plan.close()
         del dX, dY
     h.set_chain_kernel("auto")

@@ -78,6 +78,13 @@ def test_algorithmic_counts_complex_and_beta():
 def test_rescale_be_operation_count_at_the_workload():
     # s = 16, drops g = 7 after the first two products of a depth-3 chain
     assert bench.rbe_valu_ops_per_entry(16, [7, 7, 0]) == 2144
+    # one rescaling product: 16 reductions (3 each), drops over 15 .. 9
+    # remaining moduli (84 steps of 5), 36 digit steps of 5 among the 9 kept,
+    # 7 extensions of 9 products and a reduction
+    assert bench.rbe_product_ops_per_entry(16, 7) == 48 + 420 + 180 + 84
+    # the chain is two such products, the last product's 16 reductions and
+    # the reconstruction (120 digit steps, 15 fp64 Horner FMAs, one scaling)
+    assert bench.rbe_valu_ops_per_entry(16, [7, 7, 0]) == 2 * 732 + 48 + 600 + 30 + 2
 
 
 def test_traffic_records_are_keyed_on_workload_and_sources(tmp_path):
