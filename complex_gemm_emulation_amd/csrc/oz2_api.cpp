@@ -89,6 +89,7 @@ struct oz2_chain_plan {
     int np = 0, ap = 0;        // n rounded up to 8 (plane padding) and to 16 (operator rows)
     int ncp = 0;               // pairs of 32-byte MFMA k chunks covering np
     const int* fexp = nullptr;     // device [3][np] row exponents left pending on each direction
+    const ChainDropTable* drop = nullptr;  // device [d] drop weights of each product (HBM kernels)
     const int8_t* hops = nullptr;  // device [d][s][ap / 16][ncp][64][16] operator residues of the HBM kernels
 };
 
@@ -986,7 +987,8 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     const size_t off_lds = align_up(sizeof(ChainTables));
     const size_t off_fexp = align_up(off_lds + lds_bytes);
     const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
-    const size_t total = off_hops + hops_bytes;
+    const size_t off_drop = align_up(off_hops + hops_bytes);
+    const size_t total = off_drop + sizeof(ChainDropTable) * depth;
     std::vector<char> host;
     std::vector<int8_t> res;
     std::vector<int> fexp;
@@ -1016,12 +1018,21 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
                         if (lds) lo[(((size_t)i * kChainMaxS + q) * kChainN + a) * kChainN + k] = v;
                         // fragment order, zero padded: row a = 16 at + r, byte k = 64 cp + 16 j + e at
                         // [i][q][at][cp][r + 16 j][e], the 16 bytes lane r + 16 j of a wavefront loads for
-                        // the two MFMA k chunks of pair cp
-                        const int at = a >> 4, r = a & 15, cp = k >> 6, j = (k >> 4) & 3, e = k & 15;
-                        ho[((((((size_t)i * s + q) * (ap / 16) + at) * ncp + cp) * 64) + r + 16 * j) * 16 + e] = v;
+                        // the two MFMA k chunks of pair cp.  np = 8 (8 rows, 32 fibres per tile): row a
+                        // at lanes a (k group 0) and a + 8 + 16 (k group 1), only the first chunk used
+                        const size_t mq = (((size_t)i * s + q) * (ap / 16)) * ncp * 64;
+                        if (np == 8) {
+                            ho[(mq + a) * 16 + k] = v;
+                            ho[(mq + a + 8 + 16) * 16 + k] = v;
+                        } else {
+                            const int at = a >> 4, r = a & 15, cp = k >> 6, j = (k >> 4) & 3, e = k & 15;
+                            ho[(mq + ((size_t)at * ncp + cp) * 64 + r + 16 * j) * 16 + e] = v;
+                        }
                     }
         for (int m = 0; m < 3; ++m)
             for (int a = 0; a < nn; ++a) fe[m * np + a] = fexp[(size_t)m * nn + a];
+        ChainDropTable* dt = (ChainDropTable*)(host.data() + off_drop);
+        for (int i = 0; i < depth; ++i) chain_drop_table(*(const ChainTables*)host.data(), plan->params.g[i], dt + i);
     }
     if (!st && hipMalloc(&plan->mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -1038,6 +1049,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->params.ops = lds ? (const int8_t*)((char*)plan->mem + off_lds) : nullptr;
     plan->fexp = (const int*)((char*)plan->mem + off_fexp);
     plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
+    plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
     *out = plan;
     return OZ2_STATUS_SUCCESS;
 }
@@ -1115,6 +1127,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
             P.g = C.g[i];
             P.kind = C.kind[i];
             P.ops = plan->hops + (size_t)i * s * plan->ap * plan->ncp * 64;
+            P.drop = plan->drop + i;
             OZ2_LAUNCH(launch_chain_step(P, last, stm));
         }
         if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));

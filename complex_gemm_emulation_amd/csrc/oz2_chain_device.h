@@ -96,32 +96,19 @@ __device__ __forceinline__ void unpack_tile(const uint32_t (&pk)[kSlots], float 
         for (int q = 0; q < 4; ++q) r[q][u] = unpack128(pk[u], q);
 }
 
-// After a non-final product, for the four entries of a lane: RnsDrop g times
-// (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), store
-// the kept slots, MrcDigits on them and BaseExtend to the dropped slots
-// (Algorithm 4, Eq. 26), storing those too.  Every slot loop is unrolled;
-// with G >= 0 the drop count is a compile-time constant and the guards fold
-// away, with G < 0 it is g_rt and the guards are uniform branches.  The
-// residues come in offset by 128: the first drop's differences remove the
-// offset from every kept slot (with no drop the caller removes it).
+// After RnsDrop: store the kept slots (0 .. 15 - g), MrcDigits on them and
+// BaseExtend to the dropped slots (Algorithm 4, Eq. 26), storing those too.
+// With G >= 0 the drop count is a compile-time constant and the guards fold
+// away, with G < 0 it is g_rt and the guards are uniform branches.
 // put(u, r0, r1, r2, r3) stores slot u's four entries.
 template <int G, class Put>
-__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, const Put& put) {
+__device__ __forceinline__ void extend_dropped(int g_rt, float (&r)[4][kSlots], const ChainTables* T, const Put& put) {
     const int g = G >= 0 ? G : g_rt;
     const int keep = kSlots - 1 - g;  // last slot of the reduced basis
 #pragma unroll
-    for (int qs = kSlots - 1; qs > 0; --qs)
-        if (qs > keep) {
-#pragma unroll
-            for (int p = 0; p < qs; ++p) {
-                const float iv = T->inv[qs][p], m = T->mod[p], rm = T->rmod[p];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
-            }
-        }
-#pragma unroll
     for (int u = 0; u < kSlots; ++u)
         if (u <= keep) put(u, r[0][u], r[1][u], r[2][u], r[3][u]);
+    if (g == 0) return;  // nothing to extend to
     // mixed-radix digits of the kept residues, in place
 #pragma unroll
     for (int i = 0; i < kSlots - 1; ++i)
@@ -146,6 +133,93 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
             const float m = T->mod[p], rm = T->rmod[p];
             put(p, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm), cmod(ts[3], m, rm));
         }
+}
+
+
+// After a non-final product, for the four entries of a lane: RnsDrop g times
+// (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), each
+// drop updating every remaining slot, then extend_dropped.  Every slot loop
+// is unrolled (G as in extend_dropped).  The residues come in offset by 128:
+// the first drop's differences remove the offset from every kept slot (with
+// no drop the caller removes it).
+template <int G, class Put>
+__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, const Put& put) {
+    const int g = G >= 0 ? G : g_rt;
+    const int keep = kSlots - 1 - g;
+#pragma unroll
+    for (int qs = kSlots - 1; qs > 0; --qs)
+        if (qs > keep) {
+#pragma unroll
+            for (int p = 0; p < qs; ++p) {
+                const float iv = T->inv[qs][p], m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
+            }
+        }
+    extend_dropped<G>(g_rt, r, T, put);
+}
+
+// The same result with the g drops taken at once (g >= 1, a run-time value):
+// g successive RnsDrops by the moduli q_0, q_1, .. (slots 15, 14, ..) turn
+// the entry X into X_g = (X - D) / Q, Q = prod_j q_j and
+// D = sum_j d_j prod_{l<j} q_l, with d_j the centred mixed-radix digits of X
+// over q_0, q_1, .. (Algorithm 1 applied g times; Eq. 24 for the digits).
+// So the digits come from successive elimination among the dropped slots
+// alone (g (g - 1) / 2 steps, each slot's steps in the order the repeated
+// drop takes them), and every kept slot p gets
+// [X_g]_p = [r_p qinv_p + sum_j d_j nw_{j,p}]_{m_p} with the per-product
+// table D (qinv_p = [Q^-1]_p, nw_{j,p} = -[prod_{l<j} q_l Q^-1]_p, centred,
+// zero for j >= g): one exact integer sum (|sum| < 2^19) and one reduction
+// instead of g modular steps.  The residues and digits are integers, so the
+// result is bitwise that of rescale_extend.  d_0 and the r_p come in offset
+// by 128; nw_{0,p} = -qinv_p cancels it.  The sum runs over j < 8 without
+// guards (zero weights) and over 8 <= j < 15 only when g > 8.
+template <class Put>
+__device__ __forceinline__ void drop_extend(int g, float (&r)[4][kSlots], const ChainTables* T,
+                                            const ChainDropTable* D, const Put& put) {
+    const int keep = kSlots - 1 - g;
+    // digits over the dropped slots: slot 15 - jp takes its steps with the
+    // earlier dropped slots 15, 14, .. 15 - jp + 1 in that order
+#pragma unroll
+    for (int jp = 1; jp < kSlots - 1; ++jp)
+        if (jp < g) {
+            const int p = kSlots - 1 - jp;
+            const float m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+            for (int j = 0; j < jp; ++j) {
+                const int qs = kSlots - 1 - j;
+                const float iv = T->inv[qs][p];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
+            }
+        }
+    // the kept slots, in place (a zero weight may meet an updated slot)
+#pragma unroll
+    for (int p = 0; p < kSlots - 1; ++p)
+        if (p <= keep) {
+            const float qi = D->qinv[p];
+            float acc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = r[e][p] * qi;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float w = D->nw[j][p];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = fmaf(r[e][kSlots - 1 - j], w, acc[e]);
+            }
+            if (g > 8) {
+#pragma unroll
+                for (int j = 8; j < kSlots - 1; ++j) {
+                    const float w = D->nw[j][p];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(r[e][kSlots - 1 - j], w, acc[e]);
+                }
+            }
+            const float m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[e][p] = cmod(acc[e], m, rm);
+        }
+    extend_dropped<-1>(g, r, T, put);
 }
 
 // ReconstructFP64's integer part (Algorithm 5) for the four entries of a

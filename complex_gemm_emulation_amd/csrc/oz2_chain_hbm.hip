@@ -96,6 +96,27 @@ __global__ __launch_bounds__(256) void chain_scan_kernel(const double* __restric
     if (threadIdx.x == 0) atomicMax(&smax[t], bm);
 }
 
+// the same for tensors of at most kScanChunk entries: one wavefront per
+// tensor, reduced across the wavefront, one store (no atomics)
+__global__ __launch_bounds__(256) void chain_scan_small_kernel(const double* __restrict__ X, int64_t n3,
+                                                               int64_t batch, unsigned long long* smax) {
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (t >= batch) return;
+    const double* x = X + t * n3;
+    unsigned long long mx = 0;
+    for (int64_t i = lane; i < n3; i += 64) {
+        const unsigned long long v = (unsigned long long)__double_as_longlong(x[i]) & 0x7fffffffffffffffull;
+        mx = v > mx ? v : mx;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long v = __shfl_xor(mx, o, 64);
+        mx = v > mx ? v : mx;
+    }
+    if (lane == 0) smax[t] = mx;
+}
+
 // -------------------------------------------------------------- encode
 // four consecutive positions p0 .. p0 + 3 of one tensor per thread, every
 // modulus: x (zero at padding and for a tensor with a non-finite entry,
@@ -186,11 +207,20 @@ struct StepConsts {
 // fa = f0 + 4 kq is the lane's first fibre within the tensor (< np^2 <=
 // 2^16), at positions p1 = fa mod np, p2 = fa / np (the caller's, once per
 // fibre tile).
-template <bool CONTIG, bool LAST, int NCP, class XLoad>
+// HALF (np = 8, one pair): the operator has 8 rows, so a tile is 32 fibres
+// against them: MFMA column c takes operator row c mod 8 in k group c / 8
+// (the operator's fragments hold each row twice, zero elsewhere) and row i
+// of the fibres' operand holds fibre f0 + i in k group 0 and fibre
+// f0 + 16 + i in k group 1, so column c of the output is fibre set c / 8
+// against operator row c mod 8, and every lane's entries are used: the lane
+// of column c holds fibres f0 + 16 (c / 8) + 4 kq + q (the caller's fa).
+// Only the pair's first MFMA carries data.
+template <bool CONTIG, bool LAST, int NCP, bool HALF, class XLoad>
 __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepConsts& K, const ChainTables* T,
-                                          int64_t t, int fa, int p1, int p2, int a0, int lane, const XLoad& xload,
-                                          unsigned long long M, double alpha) {
-    const int a = a0 + (lane & 15);  // column of the output (operator row)
+                                          const ChainDropTable* DT, int64_t t, int fa, int p1, int p2, int a0,
+                                          int lane, const XLoad& xload, unsigned long long M, double alpha) {
+    static_assert(!HALF || NCP == 1, "one pair of k chunks at np = 8");
+    const int a = HALF ? (lane & 7) : a0 + (lane & 15);  // column of the output (operator row)
     const int8_t* opf = P.ops + ((int64_t)(a0 >> 4) * NCP * 64 + lane) * 16;
     uint32_t pk[kSlots];
 #pragma unroll
@@ -222,7 +252,7 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
             for (int cp = 0; cp < NCP; ++cp) {
                 const v2l x = xload(qm[v], cp);
                 acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(x[0], ob[v][cp][0], acc[v], 0, 0, 0);
-                acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(x[1], ob[v][cp][1], acc[v], 0, 0, 0);
+                if (!HALF) acc[v] = __builtin_amdgcn_mfma_i32_16x16x32_i8(x[1], ob[v][cp][1], acc[v], 0, 0, 0);
             }
         }
         // each word is pinned here, or the reductions sink below the later
@@ -248,23 +278,21 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
     } else {
         float r[4][kSlots];
         unpack_tile(pk, r);
-        if (P.g == 0) {
-#pragma unroll
-            for (int u = 0; u < kSlots; ++u)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
-        }
         // the next layout: (p1, p2, a) with the four entries contiguous,
-        // (p2, p1, a) or (a, p1, p2) with them np apart
+        // (p2, p1, a) or (a, p1, p2) with them np apart.  The lane's column
+        // is made opaque here so that the 16 x 4 store addresses are formed
+        // after the products, not hoisted above them into spilled registers.
+        int ao = a;
+        asm volatile("" : "+v"(ao));
         int8_t* base = P.out + t * K.np3;
         int64_t step = 0;
         if (CONTIG) {
-            base += fa + K.np2 * a;
+            base += fa + K.np2 * ao;
         } else if (P.kind == 1) {
-            base += p2 + (int64_t)K.np * p1 + K.np2 * a;
+            base += p2 + (int64_t)K.np * p1 + K.np2 * ao;
             step = K.np;
         } else {
-            base += a + (int64_t)K.np * fa;
+            base += ao + (int64_t)K.np * fa;
             step = K.np;
         }
         const bool ok = a < K.np;
@@ -273,16 +301,29 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
         const auto put = [=](int u, float r0, float r1, float r2, float r3) {
             if (u >= first && ok) store4<!CONTIG>(base + (int64_t)(u - first) * pstride, step, r0, r1, r2, r3);
         };
-        rescale_extend<-1>(P.g, r, T, put);
+        if (P.g == 0) {
+            // no drop: the residues lose their offset here and are stored
+#pragma unroll
+            for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
+            extend_dropped<-1>(0, r, T, put);
+        } else {
+            drop_extend(P.g, r, T, DT, put);
+        }
     }
 }
 
 // the constant tables into LDS (read per use; hoisted into registers they
-// would not fit)
-__device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTables& KT) {
-    static_assert(sizeof(ChainTables) % 4 == 0, "words");
+// would not fit), with this product's drop weights unless it is the last
+template <bool LAST>
+__device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTables& KT, ChainDropTable& KD) {
+    static_assert(sizeof(ChainTables) % 4 == 0 && sizeof(ChainDropTable) % 4 == 0, "words");
     for (int x = threadIdx.x; x < (int)(sizeof(ChainTables) / 4); x += blockDim.x)
         ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
+    if (!LAST)
+        for (int x = threadIdx.x; x < (int)(sizeof(ChainDropTable) / 4); x += blockDim.x)
+            ((uint32_t*)&KD)[x] = ((const uint32_t*)P.drop)[x];
     __syncthreads();
 }
 
@@ -298,26 +339,28 @@ __device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTable
 // grid-stride loop, walking the operator's rows in tiles of 16 and reading
 // the fibres' operand from memory (the tile stays in cache between row
 // tiles when there are few of them).
-template <bool CONTIG, bool LAST, int NCP>
+template <bool CONTIG, bool LAST, int NCP, bool HALF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_kernel(ChainHbmParams P) {
     __shared__ ChainTables KT;
-    stage_tables(P, KT);
+    __shared__ ChainDropTable KD;
+    stage_tables<LAST>(P, KT, KD);
     const StepConsts K(P);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
-    const int64_t nft = K.np2 / 16;  // fibre tiles per tensor (np^2 is a multiple of 64)
+    constexpr int TF = HALF ? 32 : 16;  // fibres per tile
+    const int64_t nft = K.np2 / TF;     // fibre tiles per tensor (np^2 is a multiple of 64)
     const int64_t tiles = P.batch * nft;
 #pragma unroll 1
     for (int64_t w = (int64_t)blockIdx.x * 4 + wave; w < tiles; w += (int64_t)gridDim.x * 4) {
         const int64_t t = w / nft;
-        const int f0 = (int)(w % nft) * 16;
+        const int f0 = (int)(w % nft) * TF;
         const int8_t* xt = P.in + t * K.np3;  // the tensor in plane 0
         // captured by value: a reference into the kernel's parameters keeps
         // them in memory and costs about 100 bytes of spills per lane
         const int64_t pstride = P.pstride;
         const int np = K.np, k0 = 16 * kq;
-        const int fa = f0 + 4 * kq;
+        const int fa = f0 + (HALF ? 16 * (r16 >> 3) : 0) + 4 * kq;
         const int p1 = fa % K.np, p2 = fa / K.np;
         const unsigned long long M = LAST ? P.smax[t] : 0ull;
         const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
@@ -327,19 +370,21 @@ void chain_step_kernel(ChainHbmParams P) {
             // the lane's fibre row (< np^3 <= 2^24), opaque in each row tile:
             // hoisted out of this loop, the 16 NCP fibre addresses would hold
             // registers across the rescaling and spill
-            int xrow = (f0 + r16) * np;
+            int xrow = (f0 + r16 + (HALF ? 16 * (kq & 1) : 0)) * np;
             asm volatile("" : "+v"(xrow));
             // bytes at k >= np (the row ends at np, a multiple of 8) are zero;
             // their loads read the row's first bytes instead, so that no load
-            // is conditional
+            // is conditional.  HALF: k groups 0 and 1 hold bytes 0 .. 7 of
+            // fibres f0 + r16 and f0 + 16 + r16.
             const auto xload = [=](int qm, int cp) {
                 const int8_t* x = xt + (int64_t)qm * pstride + xrow;
+                if (HALF) return v2l{kq < 2 ? *(const long*)x : 0l, 0l};
                 const int k = k0 + 64 * cp;
                 const long lo = *(const long*)(x + (k < np ? k : 0));
                 const long hi = *(const long*)(x + (k + 8 < np ? k + 8 : 0));
                 return v2l{k < np ? lo : 0l, k + 8 < np ? hi : 0l};
             };
-            step_tile<CONTIG, LAST, NCP>(P, K, &KT, t, fa, p1, p2, a0, lane, xload, M, alpha);
+            step_tile<CONTIG, LAST, NCP, HALF>(P, K, &KT, &KD, t, fa, p1, p2, a0, lane, xload, M, alpha);
         }
     }
 }
@@ -361,8 +406,9 @@ template <bool CONTIG, bool LAST, int NCP, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_staged_kernel(ChainHbmParams P, int F) {
     __shared__ ChainTables KT;
+    __shared__ ChainDropTable KD;
     extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][NCP][64 lanes][16 bytes]
-    stage_tables(P, KT);
+    stage_tables<LAST>(P, KT, KD);
     const StepConsts K(P);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int na = K.ap / 16;                // operator-row tiles
@@ -396,20 +442,20 @@ void chain_step_staged_kernel(ChainHbmParams P, int F) {
             const int fa = fb0 + 16 * f + 4 * (lane >> 4);
             const unsigned long long M = LAST ? P.smax[t] : 0ull;
             const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
-            step_tile<CONTIG, LAST, NCP>(P, K, &KT, t, fa, fa % K.np, fa / K.np, (pr % na) * 16, lane, xload,
-                                         M, alpha);
+            step_tile<CONTIG, LAST, NCP, false>(P, K, &KT, &KD, t, fa, fa % K.np, fa / K.np, (pr % na) * 16,
+                                                lane, xload, M, alpha);
         }
     }
 }
 
-template <int NCP>
+template <int NCP, bool HALF>
 void launch_direct(const ChainHbmParams& P, bool last, dim3 grid, hipStream_t st) {
     if (last)
-        hipLaunchKernelGGL((chain_step_kernel<true, true, NCP>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((chain_step_kernel<true, true, NCP, HALF>), grid, dim3(256), 0, st, P);
     else if (P.kind == 0)
-        hipLaunchKernelGGL((chain_step_kernel<true, false, NCP>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((chain_step_kernel<true, false, NCP, HALF>), grid, dim3(256), 0, st, P);
     else
-        hipLaunchKernelGGL((chain_step_kernel<false, false, NCP>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((chain_step_kernel<false, false, NCP, HALF>), grid, dim3(256), 0, st, P);
 }
 
 template <int NCP, int NW>
@@ -430,8 +476,13 @@ hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st) {
     const int64_t n3 = (int64_t)P.n * P.n * P.n;
     const int64_t chunks = (n3 + kScanChunk - 1) / kScanChunk;
     if (P.batch * chunks > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)(P.batch * chunks)), dim3(256), 0, st, P.X, n3, chunks,
-                       P.smax);
+    if (chunks == 1) {
+        hipLaunchKernelGGL(chain_scan_small_kernel, dim3((unsigned)((P.batch + 3) / 4)), dim3(256), 0, st, P.X, n3,
+                           P.batch, P.smax);
+    } else {
+        hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)(P.batch * chunks)), dim3(256), 0, st, P.X, n3,
+                           chunks, P.smax);
+    }
     return hipGetLastError();
 }
 
@@ -478,13 +529,16 @@ hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st)
             default: return hipErrorInvalidValue;
         }
     } else {
-        const int64_t tiles = P.batch * ((int64_t)P.np * P.np / 16);
+        const bool half = P.np == 8;
+        const int64_t tiles = P.batch * ((int64_t)P.np * P.np / (half ? 32 : 16));
         const int64_t want = (tiles + 3) / 4;
         const dim3 grid((unsigned)(want < kStepBlocksMax ? want : kStepBlocksMax));
-        if (ncp == 1)
-            launch_direct<1>(P, last, grid, st);
+        if (half)
+            launch_direct<1, true>(P, last, grid, st);
+        else if (ncp == 1)
+            launch_direct<1, false>(P, last, grid, st);
         else
-            launch_direct<2>(P, last, grid, st);
+            launch_direct<2, false>(P, last, grid, st);
     }
     return hipGetLastError();
 }

@@ -250,4 +250,25 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
     return OZ2_STATUS_SUCCESS;
 }
 
+void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D) {
+    std::memset(D, 0, sizeof(*D));
+    if (g < 1 || g > kChainMaxS - 1) return;
+    int slot[kChainMaxS];
+    for (int u = 0; u < kChainMaxS; ++u) slot[u] = (int)T.mod[u];
+    const int keep = kChainMaxS - 1 - g;
+    for (int p = 0; p <= keep; ++p) {
+        const int m = slot[p];
+        if (m == 1) continue;  // residues modulo 1 are zero
+        int64_t Q = 1;  // prod_j q_j reduced mod m
+        for (int j = 0; j < g; ++j) Q = Q * slot[kChainMaxS - 1 - j] % m;
+        const int64_t qi = inverse_mod(Q, m);
+        D->qinv[p] = (float)centered(qi, m);
+        int64_t w = 1;  // prod_{l<j} q_l reduced mod m
+        for (int j = 0; j < g; ++j) {
+            D->nw[j][p] = (float)-centered(w * qi % m, m);
+            w = w * slot[kChainMaxS - 1 - j] % m;
+        }
+    }
+}
+
 }  // namespace oz2

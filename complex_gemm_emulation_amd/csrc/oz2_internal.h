@@ -154,6 +154,18 @@ struct ChainTables {
     int fexp[3][kChainN];                 // row exponents left pending on each direction (0 for padding)
 };
 
+// Per non-final product with g >= 1 drops (slots 15, 14, .. 15 - g + 1 in
+// that order, q_j = the modulus of slot 15 - j, Q = prod_{j<g} q_j): the
+// weights that take the kept residues of X to those of X_g = (X - D) / Q in
+// one sum (D from the mixed-radix digits d_j of X over q_0, q_1, ..):
+// [X_g]_p = [r_p qinv[p] + sum_{j<g} d_j nw[j][p]]_{m_p}.  Centred values,
+// zero for j >= g, for the dropped slots and for slots of modulus 1.
+struct ChainDropTable {
+    float qinv[kChainMaxS];                 // [Q^{-1}]_{m_p}
+    float nw[kChainMaxS - 1][kChainMaxS];   // -[prod_{l<j} q_l Q^{-1}]_{m_p}
+};
+void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D);
+
 // Host planning of the chain (Algorithms 2, 3 and 5 of the chain page, with
 // the pending row scales of a direction folded into the next operator on
 // it, Sec. 5.2): the significand bits b, the drop counts g, the effective
@@ -188,6 +200,7 @@ struct ChainHbmParams {
     const int8_t* ops;           // [s][ap / 16][ncp][64][16] this product's operator residues in MFMA fragment
                                  // order (ap = np rounded up to 16, ncp = np / 64 rounded up)
     const float* tab;            // ChainTables
+    const ChainDropTable* drop;  // this product's drop weights (g >= 1)
     const int* fexp;             // [3][np] row exponents left pending on each direction
     unsigned long long* smax;    // [batch] max |x| bit pattern of each tensor (0 before the scan)
     const int8_t* in;            // planes [s][batch][np^3] read by this product
