@@ -1032,7 +1032,9 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         for (int m = 0; m < 3; ++m)
             for (int a = 0; a < nn; ++a) fe[m * np + a] = fexp[(size_t)m * nn + a];
         ChainDropTable* dt = (ChainDropTable*)(host.data() + off_drop);
-        for (int i = 0; i < depth; ++i) chain_drop_table(*(const ChainTables*)host.data(), plan->params.g[i], dt + i);
+        const ChainTables& tabs = *(const ChainTables*)host.data();
+        for (int i = 0; i + 1 < depth; ++i) chain_drop_table(tabs, plan->params.g[i], dt + i);
+        chain_split_table(tabs, kChainSplit, dt + depth - 1);  // the last product's reconstruction
     }
     if (!st && hipMalloc(&plan->mem, total) != hipSuccess) {
         (void)hipGetLastError();

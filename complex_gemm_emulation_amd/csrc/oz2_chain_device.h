@@ -159,7 +159,8 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
     extend_dropped<G>(g_rt, r, T, put);
 }
 
-// The same result with the g drops taken at once (g >= 1, a run-time value):
+// The same result with the g drops taken at once (g >= 1; G >= 1 a
+// compile-time drop count, G < 0 the run-time g_rt):
 // g successive RnsDrops by the moduli q_0, q_1, .. (slots 15, 14, ..) turn
 // the entry X into X_g = (X - D) / Q, Q = prod_j q_j and
 // D = sum_j d_j prod_{l<j} q_l, with d_j the centred mixed-radix digits of X
@@ -174,9 +175,10 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
 // result is bitwise that of rescale_extend.  d_0 and the r_p come in offset
 // by 128; nw_{0,p} = -qinv_p cancels it.  The sum runs over j < 8 without
 // guards (zero weights) and over 8 <= j < 15 only when g > 8.
-template <class Put>
-__device__ __forceinline__ void drop_extend(int g, float (&r)[4][kSlots], const ChainTables* T,
+template <int G, class Put>
+__device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T,
                                             const ChainDropTable* D, const Put& put) {
+    const int g = G >= 0 ? G : g_rt;
     const int keep = kSlots - 1 - g;
     // digits over the dropped slots: slot 15 - jp takes its steps with the
     // earlier dropped slots 15, 14, .. 15 - jp + 1 in that order
@@ -219,7 +221,7 @@ __device__ __forceinline__ void drop_extend(int g, float (&r)[4][kSlots], const 
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e][p] = cmod(acc[e], m, rm);
         }
-    extend_dropped<-1>(g, r, T, put);
+    extend_dropped<G>(g_rt, r, T, put);
 }
 
 // ReconstructFP64's integer part (Algorithm 5) for the four entries of a
@@ -233,6 +235,67 @@ __device__ __forceinline__ void mrc_horner(const uint32_t (&pk)[kSlots], const C
     unpack_tile(pk, dg);
 #pragma unroll
     for (int i = 0; i < kSlots - 1; ++i)
+#pragma unroll
+        for (int j = i + 1; j < kSlots; ++j) {
+            const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
+        }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) V[q] = (double)dg[q][kSlots - 1];
+#pragma unroll
+    for (int j = kSlots - 2; j >= 0; --j) {
+        const double m = (double)T->mod[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)dg[q][j]);
+    }
+}
+
+// mrc_horner with the digits in two blocks of kSplit slots: the digits of
+// slots 0 .. kSplit - 1 by elimination among themselves; the residues of
+// X' = (X - A) / M1 at slots kSplit .. 15 (A = sum_{i<kSplit} d_i
+// prod_{l<i} m_l, M1 = prod_{l<kSplit} m_l) from one exact integer sum each,
+// [X']_p = [r_p qinv_p + sum_{i<kSplit} d_i nw_{i,p}]_{m_p} with the table D
+// (qinv_p = [M1^-1]_p, nw_{i,p} = -[prod_{l<i} m_l M1^-1]_p, centred); and
+// the digits of X' over slots kSplit .. 15, which are X's digits there (the
+// mixed-radix digits are unique).  So the digits, and the Horner sum over
+// them, are bitwise those of mrc_horner; 28 + 8 reductions + 28 steps
+// instead of 120.  d_0 and the r_p come in offset by 128; nw_{0,p} = -qinv_p
+// cancels it in the sums, and d_0 loses it after the steps (|sum| < 2^19).
+constexpr int kSplit = kChainSplit;
+
+__device__ __forceinline__ void mrc_horner_split(const uint32_t (&pk)[kSlots], const ChainTables* T,
+                                                 const ChainDropTable* D, double (&V)[4]) {
+    float dg[4][kSlots];
+    unpack_tile(pk, dg);
+#pragma unroll
+    for (int i = 0; i < kSplit - 1; ++i)
+#pragma unroll
+        for (int j = i + 1; j < kSplit; ++j) {
+            const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
+        }
+#pragma unroll
+    for (int p = kSplit; p < kSlots; ++p) {
+        const float qi = D->qinv[p];
+        float acc[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = dg[q][p] * qi;
+#pragma unroll
+        for (int i = 0; i < kSplit; ++i) {
+            const float w = D->nw[i][p];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = fmaf(dg[q][i], w, acc[q]);
+        }
+        const float m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dg[q][p] = cmod(acc[q], m, rm);
+    }
+#pragma unroll
+    for (int i = kSplit; i < kSlots - 1; ++i)
 #pragma unroll
         for (int j = i + 1; j < kSlots; ++j) {
             const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];

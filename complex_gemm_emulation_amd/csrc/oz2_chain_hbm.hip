@@ -266,7 +266,7 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
     }
     if (LAST) {
         double V[4];
-        mrc_horner(pk, T, V);
+        mrc_horner_split(pk, T, DT, V);
         if (p2 < K.n && a < K.n) {
             const int f12 = K.F1[p2] + K.F2[a];
             double* y = P.Y + t * K.n3 + p2 * K.st1 + a * K.st2;
@@ -309,21 +309,20 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
                 for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
             extend_dropped<-1>(0, r, T, put);
         } else {
-            drop_extend(P.g, r, T, DT, put);
+            drop_extend<-1>(P.g, r, T, DT, put);
         }
     }
 }
 
 // the constant tables into LDS (read per use; hoisted into registers they
-// would not fit), with this product's drop weights unless it is the last
-template <bool LAST>
+// would not fit), with this product's drop weights (the last product's:
+// those of the two-block reconstruction)
 __device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTables& KT, ChainDropTable& KD) {
     static_assert(sizeof(ChainTables) % 4 == 0 && sizeof(ChainDropTable) % 4 == 0, "words");
     for (int x = threadIdx.x; x < (int)(sizeof(ChainTables) / 4); x += blockDim.x)
         ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
-    if (!LAST)
-        for (int x = threadIdx.x; x < (int)(sizeof(ChainDropTable) / 4); x += blockDim.x)
-            ((uint32_t*)&KD)[x] = ((const uint32_t*)P.drop)[x];
+    for (int x = threadIdx.x; x < (int)(sizeof(ChainDropTable) / 4); x += blockDim.x)
+        ((uint32_t*)&KD)[x] = ((const uint32_t*)P.drop)[x];
     __syncthreads();
 }
 
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 
 void chain_step_kernel(ChainHbmParams P) {
     __shared__ ChainTables KT;
     __shared__ ChainDropTable KD;
-    stage_tables<LAST>(P, KT, KD);
+    stage_tables(P, KT, KD);
     const StepConsts K(P);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
@@ -408,7 +407,7 @@ void chain_step_staged_kernel(ChainHbmParams P, int F) {
     __shared__ ChainTables KT;
     __shared__ ChainDropTable KD;
     extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][NCP][64 lanes][16 bytes]
-    stage_tables<LAST>(P, KT, KD);
+    stage_tables(P, KT, KD);
     const StepConsts K(P);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int na = K.ap / 16;                // operator-row tiles

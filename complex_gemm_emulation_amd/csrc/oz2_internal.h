@@ -165,6 +165,12 @@ struct ChainDropTable {
     float nw[kChainMaxS - 1][kChainMaxS];   // -[prod_{l<j} q_l Q^{-1}]_{m_p}
 };
 void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D);
+// The last product's table for the two-block reconstruction: slots 0 ..
+// split - 1 play the dropped moduli (in that order, M1 their product) for
+// the slots split .. 15: qinv[p] = [M1^{-1}]_{m_p},
+// nw[i][p] = -[prod_{l<i} m_l M1^{-1}]_{m_p}, centred, zero elsewhere.
+void chain_split_table(const ChainTables& T, int split, ChainDropTable* D);
+constexpr int kChainSplit = 8;  // slots in the first block of the HBM kernels' reconstruction
 
 // Host planning of the chain (Algorithms 2, 3 and 5 of the chain page, with
 // the pending row scales of a direction folded into the next operator on
@@ -200,7 +206,7 @@ struct ChainHbmParams {
     const int8_t* ops;           // [s][ap / 16][ncp][64][16] this product's operator residues in MFMA fragment
                                  // order (ap = np rounded up to 16, ncp = np / 64 rounded up)
     const float* tab;            // ChainTables
-    const ChainDropTable* drop;  // this product's drop weights (g >= 1)
+    const ChainDropTable* drop;  // this product's drop weights (g >= 1; the last product: chain_split_table)
     const int* fexp;             // [3][np] row exponents left pending on each direction
     unsigned long long* smax;    // [batch] max |x| bit pattern of each tensor (0 before the scan)
     const int8_t* in;            // planes [s][batch][np^3] read by this product
