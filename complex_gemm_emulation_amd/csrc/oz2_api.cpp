@@ -1052,6 +1052,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->fexp = (const int*)((char*)plan->mem + off_fexp);
     plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
     plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
+    plan->params.split = plan->drop + depth - 1;
     *out = plan;
     return OZ2_STATUS_SUCCESS;
 }

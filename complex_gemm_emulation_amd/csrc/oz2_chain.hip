@@ -114,6 +114,7 @@ void chain_kernel(ChainParams P) {
     __shared__ __attribute__((aligned(16))) int8_t buf[kSlots * kPlane];
     __shared__ __attribute__((aligned(16))) int8_t ops[3][kSlots][kChainN * kChainN];  // operator i in i mod 3
     __shared__ ChainTables KT;
+    __shared__ ChainDropTable KS;  // the two-block reconstruction's weights
     __shared__ unsigned long long smax;
 
     const int tid = threadIdx.x;
@@ -129,6 +130,9 @@ void chain_kernel(ChainParams P) {
     static_assert(sizeof(ChainTables) % 4 == 0, "words");
     for (int x = tid; x < (int)(sizeof(ChainTables) / 4); x += 512)
         ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
+    static_assert(sizeof(ChainDropTable) % 4 == 0, "words");
+    for (int x = tid; x < (int)(sizeof(ChainDropTable) / 4); x += 512)
+        ((uint32_t*)&KS)[x] = ((const uint32_t*)P.split)[x];
     const ChainTables* T = &KT;
     // operator i's residues (slot order) into LDS buffer i mod 3: 512 words of 8 bytes
     auto stage_ops = [&](int i) {
@@ -253,7 +257,7 @@ void chain_kernel(ChainParams P) {
         uint32_t pk[kSlots];
         tile_products(buf, ops[(d - 1) % 3], T, t, a, kq, pk);
         double V[4];
-        mrc_horner(pk, T, V);
+        mrc_horner_split(pk, T, &KS, V);
         // the values are complete here (the compiler would otherwise sink
         // each entry's whole digit computation into its guarded store)
 #pragma unroll

@@ -123,6 +123,8 @@ constexpr int kChainN = 16;      // tensor side of the LDS kernel's tiles (n <= 
 constexpr int kChainMaxN = 256;  // tensor side of the HBM-resident kernels
 constexpr int kChainMaxS = 16;   // moduli: one LDS buffer of 16 residue planes (64 KiB)
 constexpr int kChainMaxD = 8;    // chain depth: operators
+struct ChainDropTable;
+
 struct ChainParams {
     const double* X;             // [batch][n^3] column-major tensors
     double* Y;
@@ -141,6 +143,7 @@ struct ChainParams {
     double Qd;                   // fl64 product of the dropped moduli, in drop order
     const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators, by modulus index
     const float* tab;            // device ChainTables (below)
+    const ChainDropTable* split; // device: the two-block reconstruction's table (chain_split_table)
 };
 
 // Constant tables of the chain kernel, in slot order (the s moduli
