@@ -1090,6 +1090,17 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
     const size_t off_b0 = align_up(sizeof(unsigned long long) * (size_t)chunk);
     const size_t off_b1 = align_up(off_b0 + (size_t)s * chunk * np3);
     const size_t bytes = off_b1 + (size_t)s * chunk * np3;
+    // the encode's residue constants of the chain's moduli (index q = slot - first)
+    const ModuliPlan* mpl = moduli_plan(s);
+    if (!mpl) return OZ2_STATUS_INTERNAL;
+    ChainEncodeConsts E{};
+    for (int q = 0; q < s; ++q) {
+        E.K128[q] = mpl->Kstd[q] + 128u;
+        for (int l = 0; l < kStdWords; ++l) E.c4[q][l] = mpl->c4[q][l];
+        E.mod[q] = (float)mpl->mod[q];
+        E.frcp[q] = mpl->frcp[q];
+        E.foffb[q] = mpl->foffb[q];
+    }
     int st = ensure_workspace(h, bytes);
     if (st) return st;
     char* ws = workspace(h);
@@ -1120,7 +1131,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
         OZ2_LAUNCH(launch_chain_scan(P, stm));
         if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[1], stm));
         P.out = buf[0];
-        OZ2_LAUNCH(launch_chain_encode(P, stm));
+        OZ2_LAUNCH(launch_chain_encode(P, E, stm));
         if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[2], stm));
         for (int i = 0; i < C.d; ++i) {
             const bool last = i == C.d - 1;

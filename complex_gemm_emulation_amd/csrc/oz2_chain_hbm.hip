@@ -47,6 +47,7 @@
 // operator rows beyond np are not stored, and the reconstruction stores only
 // positions < n.
 #include "oz2_chain_device.h"
+#include "oz2_device.h"
 
 namespace oz2 {
 namespace {
@@ -120,9 +121,12 @@ __global__ __launch_bounds__(256) void chain_scan_small_kernel(const double* __r
 // -------------------------------------------------------------- encode
 // four consecutive positions p0 .. p0 + 3 of one tensor per thread, every
 // modulus: x (zero at padding and for a tensor with a non-finite entry,
-// whose result the reconstruction sets to NaN), xbar = rint(2^e x), its
-// centred residues packed into one 32-bit word per plane
-__global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, int64_t bpt) {
+// whose result the reconstruction sets to NaN), xbar = rint(2^e x) split into
+// byte limbs exactly (|xbar| <= 2^53), and its centred residues packed into
+// one 32-bit word per plane: the low byte of xbar for m = 256, and for the
+// odd moduli the byte-limb identity of the GEMM path's encoder (two
+// v_dot4_u32_u8 per residue, an FP32 floor, one byte insert; exact)
+__global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, ChainEncodeConsts E, int64_t bpt) {
     const int n = P.n, np = P.np;
     const int64_t np3 = (int64_t)np * np * np;
     const int64_t t = blockIdx.x / bpt;
@@ -140,28 +144,18 @@ __global__ __launch_bounds__(256) void chain_encode_kernel(ChainHbmParams P, int
     const int64_t sd1 = d1 == 0 ? 1 : d1 == 1 ? n : nn;
     const int64_t sd2 = d2 == 0 ? 1 : d2 == 1 ? n : nn;
     const double* x = P.X + t * n * nn + p1 * sd1 + p2 * sd2;
-    double xb[4];
+    dev::Limbs<false> L[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const bool in = finite && p0 + q < n && p1 < n && p2 < n;
-        xb[q] = in ? rint(ldexp(x[(p0 + q) * sd0], e)) : 0.0;  // |xb| <= 2^b
+        L[q] = dev::make_limbs<false>(in ? x[(p0 + q) * sd0] : 0.0, e, !in);
     }
-    const ChainTables* T = (const ChainTables*)P.tab;
-    const int first = kSlots - P.s;
     int8_t* out = P.out + t * np3 + i4;
-    // modulus 256 (index 0): the low byte of the two's-complement integer
-    uint32_t w = 0u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w |= ((uint32_t)(int64_t)xb[q] & 0xffu) << (8 * q);
-    *(uint32_t*)out = w;
+    *(uint32_t*)out = dev::low_byte_word<false>(L);  // modulus 256 (index 0)
 #pragma unroll 1
-    for (int qm = 1; qm < P.s; ++qm) {
-        const double m = (double)T->mod[first + qm], rm = 1.0 / m;
-        w = 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w |= ((uint32_t)(int)dmod_odd(xb[q], m, rm) & 0xffu) << (8 * q);
-        *(uint32_t*)(out + qm * P.pstride) = w;
-    }
+    for (int qm = 1; qm < P.s; ++qm)
+        *(uint32_t*)(out + qm * P.pstride) =
+            dev::residue_word<false>(L, E.K128[qm], E.c4[qm], E.mod[qm], E.frcp[qm], E.foffb[qm]);
 }
 
 // ------------------------------------------------------ product kernels
@@ -485,14 +479,14 @@ hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_chain_encode(const ChainHbmParams& P, hipStream_t st) {
+hipError_t launch_chain_encode(const ChainHbmParams& P, const ChainEncodeConsts& E, hipStream_t st) {
     if (P.n < 1 || P.n > kChainMaxN || P.np != ((P.n + 7) & ~7) || P.batch < 1 || P.s < kMinS || P.s > kChainMaxS ||
         P.m0 < 0 || P.m0 > 2)
         return hipErrorInvalidValue;
     const int64_t np3 = (int64_t)P.np * P.np * P.np;
     const int64_t bpt = (np3 / 4 + 255) / 256;
     if (P.batch * bpt > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(chain_encode_kernel, dim3((unsigned)(P.batch * bpt)), dim3(256), 0, st, P, bpt);
+    hipLaunchKernelGGL(chain_encode_kernel, dim3((unsigned)(P.batch * bpt)), dim3(256), 0, st, P, E, bpt);
     return hipGetLastError();
 }
 

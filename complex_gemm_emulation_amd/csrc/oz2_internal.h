@@ -247,7 +247,15 @@ hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st);
 hipError_t launch_small_gemm(SmallParams P, int NL, bool beta_nonzero, hipStream_t st);
 hipError_t launch_chain(const ChainParams& P, hipStream_t st);
 hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st);
-hipError_t launch_chain_encode(const ChainHbmParams& P, hipStream_t st);
+// The residue constants of the chain's moduli (by modulus index) for the
+// HBM kernels' encode, from the GEMM path's moduli plan (oz2_plan.h): the
+// byte-limb identity of the encoder with the standard width.
+struct ChainEncodeConsts {
+    uint32_t K128[kChainMaxS];            // ((-2^62) mod m) + 128
+    uint32_t c4[kChainMaxS][kStdWords];   // byte j of word p: 2^(32p + 8j) mod m
+    float mod[kChainMaxS], frcp[kChainMaxS], foffb[kChainMaxS];
+};
+hipError_t launch_chain_encode(const ChainHbmParams& P, const ChainEncodeConsts& E, hipStream_t st);
 hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st);
 
 }  // namespace oz2
