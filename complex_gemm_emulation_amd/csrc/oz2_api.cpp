@@ -1053,6 +1053,18 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
     plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
     plan->params.split = plan->drop + depth - 1;
+    {
+        // the encode's residue constants of the chain's moduli (index q = slot - first)
+        const ModuliPlan* mpl = moduli_plan(s);
+        ChainEncodeConsts& E = plan->params.enc;
+        for (int q = 0; q < s; ++q) {
+            E.K128[q] = mpl->Kstd[q] + 128u;
+            for (int l = 0; l < kStdWords; ++l) E.c4[q][l] = mpl->c4[q][l];
+            E.mod[q] = (float)mpl->mod[q];
+            E.frcp[q] = mpl->frcp[q];
+            E.foffb[q] = mpl->foffb[q];
+        }
+    }
     *out = plan;
     return OZ2_STATUS_SUCCESS;
 }
@@ -1090,17 +1102,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
     const size_t off_b0 = align_up(sizeof(unsigned long long) * (size_t)chunk);
     const size_t off_b1 = align_up(off_b0 + (size_t)s * chunk * np3);
     const size_t bytes = off_b1 + (size_t)s * chunk * np3;
-    // the encode's residue constants of the chain's moduli (index q = slot - first)
-    const ModuliPlan* mpl = moduli_plan(s);
-    if (!mpl) return OZ2_STATUS_INTERNAL;
-    ChainEncodeConsts E{};
-    for (int q = 0; q < s; ++q) {
-        E.K128[q] = mpl->Kstd[q] + 128u;
-        for (int l = 0; l < kStdWords; ++l) E.c4[q][l] = mpl->c4[q][l];
-        E.mod[q] = (float)mpl->mod[q];
-        E.frcp[q] = mpl->frcp[q];
-        E.foffb[q] = mpl->foffb[q];
-    }
+    const ChainEncodeConsts& E = plan->params.enc;
     int st = ensure_workspace(h, bytes);
     if (st) return st;
     char* ws = workspace(h);

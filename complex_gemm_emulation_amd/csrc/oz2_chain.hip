@@ -38,6 +38,7 @@
 // extension, Horner) is shared with the HBM-resident kernels for larger
 // tensors (oz2_chain_device.h).
 #include "oz2_chain_device.h"
+#include "oz2_device.h"
 
 namespace oz2 {
 namespace {
@@ -177,21 +178,23 @@ void chain_kernel(ChainParams P) {
         (void)frexp(__longlong_as_double((long long)M), &E);
         e = P.b - E;
     }
-    double xb[8];
+    // xbar = rint(2^e x) (|xbar| <= 2^b) as exact byte limbs; its centred
+    // residues: the low byte for m = 256, the GEMM path's byte-limb identity
+    // (two v_dot4_u32_u8, an FP32 floor, a byte insert) for the odd moduli
+    dev::Limbs<false> L[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xb[j] = rint(ldexp(x[j], e));  // |xb| <= 2^b
+    for (int j = 0; j < 8; ++j) L[j] = dev::make_limbs<false>(x[j], e, false);
 #pragma unroll 1
     for (int u = first; u < kSlots; ++u) {
-        uint32_t w[2] = {0u, 0u};
+        uint32_t w[2];
         if (u == first) {
-            // m = 256: the low byte of the two's-complement integer
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w[j >> 2] |= ((uint32_t)(int64_t)xb[j] & 0xffu) << (8 * (j & 3));
+            w[0] = dev::low_byte_word<false>(L);
+            w[1] = dev::low_byte_word<false>(L + 4);
         } else {
-            const double m = (double)T->mod[u], rm = 1.0 / m;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                w[j >> 2] |= ((uint32_t)(int)dmod_odd(xb[j], m, rm) & 0xffu) << (8 * (j & 3));
+            const int q = u - first;
+            const ChainEncodeConsts& E = P.enc;
+            w[0] = dev::residue_word<false>(L, E.K128[q], E.c4[q], E.mod[q], E.frcp[q], E.foffb[q]);
+            w[1] = dev::residue_word<false>(L + 4, E.K128[q], E.c4[q], E.mod[q], E.frcp[q], E.foffb[q]);
         }
         if (D > 0 || m0 == 0) {
             *(uint2*)(buf + u * kPlane + idx0) = make_uint2(w[0], w[1]);

@@ -40,17 +40,6 @@ __device__ __forceinline__ float cmod128(float x, float m, float rm, float oh) {
     return fmaf(-m, floorf(fmaf(x, rm, oh)), x);
 }
 
-// centred residue of an integer-valued double |v| <= 2^53 modulo an odd m
-// (the quotient estimate can be one off; two corrections bring r into range)
-__device__ __forceinline__ float dmod_odd(double v, double m, double rm) {
-    const double q = rint(v * rm);
-    double r = fma(-m, q, v);  // exact: |r| < 2m
-    const double h = 0.5 * (m - 1.0);
-    r = r > h ? r - m : r;
-    r = r < -h ? r + m : r;
-    return (float)r;
-}
-
 // byte `e` of a word of four offset-binary residues, as a float: the
 // residue plus 128 (v_cvt_f32_ubyte)
 __device__ __forceinline__ float unpack128(uint32_t w, int e) {

@@ -123,6 +123,14 @@ constexpr int kChainN = 16;      // tensor side of the LDS kernel's tiles (n <= 
 constexpr int kChainMaxN = 256;  // tensor side of the HBM-resident kernels
 constexpr int kChainMaxS = 16;   // moduli: one LDS buffer of 16 residue planes (64 KiB)
 constexpr int kChainMaxD = 8;    // chain depth: operators
+// The residue constants of the chain's moduli (by modulus index) for the
+// chain kernels' encode, from the GEMM path's moduli plan (oz2_plan.h): the
+// byte-limb identity of the encoder with the standard width.
+struct ChainEncodeConsts {
+    uint32_t K128[kChainMaxS];            // ((-2^62) mod m) + 128
+    uint32_t c4[kChainMaxS][kStdWords];   // byte j of word p: 2^(32p + 8j) mod m
+    float mod[kChainMaxS], frcp[kChainMaxS], foffb[kChainMaxS];
+};
 struct ChainDropTable;
 
 struct ChainParams {
@@ -144,6 +152,7 @@ struct ChainParams {
     const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators, by modulus index
     const float* tab;            // device ChainTables (below)
     const ChainDropTable* split; // device: the two-block reconstruction's table (chain_split_table)
+    ChainEncodeConsts enc;       // the encode's residue constants
 };
 
 // Constant tables of the chain kernel, in slot order (the s moduli
@@ -247,14 +256,6 @@ hipError_t launch_crt_test(const CrtTestParams& P, int NL, hipStream_t st);
 hipError_t launch_small_gemm(SmallParams P, int NL, bool beta_nonzero, hipStream_t st);
 hipError_t launch_chain(const ChainParams& P, hipStream_t st);
 hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st);
-// The residue constants of the chain's moduli (by modulus index) for the
-// HBM kernels' encode, from the GEMM path's moduli plan (oz2_plan.h): the
-// byte-limb identity of the encoder with the standard width.
-struct ChainEncodeConsts {
-    uint32_t K128[kChainMaxS];            // ((-2^62) mod m) + 128
-    uint32_t c4[kChainMaxS][kStdWords];   // byte j of word p: 2^(32p + 8j) mod m
-    float mod[kChainMaxS], frcp[kChainMaxS], foffb[kChainMaxS];
-};
 hipError_t launch_chain_encode(const ChainHbmParams& P, const ChainEncodeConsts& E, hipStream_t st);
 hipError_t launch_chain_step(const ChainHbmParams& P, bool last, hipStream_t st);
 
