@@ -1,8 +1,12 @@
 // Host sanitizer driver for the library's host planners (oz2_plan.cpp: UBig,
 // the moduli plans and scaling widths; oz2_chain_plan.cpp: the persistent
-// chain's planner), built with -fsanitize=address,undefined by
+// chain's planner and the weight tables of its one-pass drops and two-block
+// reconstruction), built with -fsanitize=address,undefined by
 // tests/test_sanitizers.py.  Every s, a spread of k, and chain plans over
 // n, s, depth and mode orders, including non-finite and all-zero operators.
+// The weight tables are also checked against their definitions, in exact
+// integers on random residue vectors: the one-pass drop against g repeated
+// RnsDrops, the two-block digits against one elimination over all slots.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -21,6 +25,79 @@ static uint64_t next_u64() {
     return state;
 }
 static double uniform() { return (double)(next_u64() >> 11) * 0x1.0p-53 * 2.0 - 1.0; }
+
+static int centered_i(int64_t v, int m) {
+    int64_t r = v % m;
+    if (r < 0) r += m;
+    return (int)(r < (m + 1) / 2 ? r : r - m);
+}
+
+// a random centred residue vector over the table's slots (0 for modulus 1)
+static void random_residues(const int (&m)[kChainMaxS], int (&r)[kChainMaxS]) {
+    for (int u = 0; u < kChainMaxS; ++u) r[u] = m[u] == 1 ? 0 : centered_i((int64_t)(next_u64() % 65536), m[u]);
+}
+
+// one-pass drop (chain_drop_table's weights) against g repeated RnsDrops
+static int check_drop_table(const ChainTables& T, int g) {
+    ChainDropTable D;
+    chain_drop_table(T, g, &D);
+    int m[kChainMaxS], bad = 0;
+    for (int u = 0; u < kChainMaxS; ++u) m[u] = (int)T.mod[u];
+    const int keep = kChainMaxS - 1 - g;
+    for (int trial = 0; trial < 20; ++trial) {
+        int r[kChainMaxS], a[kChainMaxS], b[kChainMaxS];
+        random_residues(m, r);
+        for (int u = 0; u < kChainMaxS; ++u) a[u] = r[u], b[u] = r[u] + 128;
+        for (int qs = kChainMaxS - 1; qs > keep; --qs)
+            for (int p = 0; p < qs; ++p)
+                a[p] = m[p] == 1 ? 0 : centered_i((int64_t)(a[p] - a[qs]) * (int)T.inv[qs][p], m[p]);
+        for (int jp = 1; jp < g; ++jp)
+            for (int j = 0; j < jp; ++j) {
+                const int p = kChainMaxS - 1 - jp, qs = kChainMaxS - 1 - j;
+                b[p] = centered_i((int64_t)(b[p] - b[qs]) * (int)T.inv[qs][p], m[p]);
+            }
+        for (int p = 0; p <= keep; ++p) {
+            int64_t acc = (int64_t)b[p] * (int)D.qinv[p];
+            for (int j = 0; j < kChainMaxS - 1; ++j) acc += (int64_t)b[kChainMaxS - 1 - j] * (int)D.nw[j][p];
+            bad += acc >= (1 << 19) || acc <= -(1 << 19);
+            b[p] = m[p] == 1 ? 0 : centered_i(acc, m[p]);
+        }
+        for (int p = 0; p <= keep; ++p) bad += a[p] != b[p];
+    }
+    return bad;
+}
+
+// two-block mixed-radix digits (chain_split_table's weights) against one
+// elimination over all slots, entries offset by 128 as in the kernels
+static int check_split_table(const ChainTables& T) {
+    ChainDropTable D;
+    chain_split_table(T, kChainSplit, &D);
+    int m[kChainMaxS], bad = 0;
+    for (int u = 0; u < kChainMaxS; ++u) m[u] = (int)T.mod[u];
+    const auto step = [&](int (&x)[kChainMaxS], int i, int j) {
+        x[j] = m[j] == 1 ? 0 : centered_i((int64_t)(x[j] - x[i]) * (int)T.inv[i][j], m[j]);
+    };
+    for (int trial = 0; trial < 20; ++trial) {
+        int r[kChainMaxS], a[kChainMaxS], b[kChainMaxS];
+        random_residues(m, r);
+        for (int u = 0; u < kChainMaxS; ++u) a[u] = b[u] = r[u] + 128;
+        for (int i = 0; i < kChainMaxS - 1; ++i)
+            for (int j = i + 1; j < kChainMaxS; ++j) step(a, i, j);
+        for (int i = 0; i < kChainSplit - 1; ++i)
+            for (int j = i + 1; j < kChainSplit; ++j) step(b, i, j);
+        for (int p = kChainSplit; p < kChainMaxS; ++p) {
+            int64_t acc = (int64_t)b[p] * (int)D.qinv[p];
+            for (int i = 0; i < kChainSplit; ++i) acc += (int64_t)b[i] * (int)D.nw[i][p];
+            bad += acc >= (1 << 19) || acc <= -(1 << 19);
+            b[p] = m[p] == 1 ? 0 : centered_i(acc, m[p]);
+        }
+        for (int i = kChainSplit; i < kChainMaxS - 1; ++i)
+            for (int j = i + 1; j < kChainMaxS; ++j) step(b, i, j);
+        for (int u = 1; u < kChainMaxS; ++u) bad += a[u] != b[u];
+        bad += a[0] != b[0];  // both still offset by 128
+    }
+    return bad;
+}
 
 int main() {
     int bad = 0;
@@ -62,6 +139,29 @@ int main() {
         std::vector<int> fexp((size_t)3 * n);
         const int st = chain_plan(s, n, d, ptr.data(), modes.data(), &P, &T, residues.data(), fexp.data());
         if (rep % 7 == 3) bad += st != -d;
+        if (st == 0) {
+            for (int i = 0; i + 1 < d; ++i)
+                if (P.g[i] >= 1) bad += check_drop_table(T, P.g[i]);
+            bad += check_split_table(T);
+        }
+    }
+    // the tables at every drop count the kernels accept, for s = 2 .. 16
+    for (int s = kMinS; s <= kChainMaxS; ++s) {
+        const ModuliPlan* pl = moduli_plan(s);
+        ChainTables T{};
+        const int first = kChainMaxS - s;
+        for (int u = 0; u < kChainMaxS; ++u) T.mod[u] = (float)(u < first ? 1 : pl->mod[u - first]);
+        for (int i = 0; i < kChainMaxS; ++i)
+            for (int j = 0; j < kChainMaxS; ++j) {
+                const int mi = (int)T.mod[i], mj = (int)T.mod[j];
+                int iv = 0;
+                if (i != j && mj > 1)
+                    for (int x = 1; x < mj; ++x)
+                        if ((int64_t)mi * x % mj == 1) { iv = x; break; }
+                T.inv[i][j] = (float)iv;
+            }
+        for (int g = 1; g < s; ++g) bad += check_drop_table(T, g);
+        bad += check_split_table(T);
     }
     std::printf("planner driver: %d unexpected results\n", bad);
     return bad != 0;
