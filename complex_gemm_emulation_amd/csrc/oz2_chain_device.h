@@ -11,6 +11,10 @@
 //    mixed-radix digits by successive elimination and the residues on the
 //    dropped moduli from the weights omega_{i,p} = [prod_{l<i} m_l]_p;
 //  - Algorithm 5 (ReconstructFP64): FP64 Horner over the digits.
+// Besides the page's step order (rescale_extend, mrc_horner), the same
+// integers come out of two shortcuts built on the uniqueness of mixed-radix
+// digits: the g drops at once (drop_extend, HBM kernels) and the final
+// digits in two blocks (mrc_horner_split, both kernels).
 //
 // Moduli sit right-aligned in kChainMaxS slots, descending, so the smallest
 // (the ones dropped) are always the last slots; unused leading slots carry

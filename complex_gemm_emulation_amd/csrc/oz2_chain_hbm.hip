@@ -33,13 +33,16 @@
 // padded sides below 96 a wavefront walks the operator's row tiles of one
 // fibre tile, reading the fibres from memory (they stay in cache between
 // the few row tiles); from 96 on a block stages its fibre tile in LDS once
-// and its wavefronts share it across the row tiles.  Each
-// lane then holds four consecutive fibres of one output row for every
-// modulus, and reduces, rescales and base-extends them in registers with the
-// arithmetic of the LDS kernel (oz2_chain_device.h).  The output layout puts
-// the next product's direction at p0: with the directions in turn that is
-// the fibres' p1, so the lane's four entries are four consecutive bytes of
-// every output plane.
+// and its wavefronts share it across the row tiles; at np = 8 a tile stacks
+// two sets of 16 fibres against the operator's 8 rows.  Each lane then holds
+// four consecutive fibres of one output row for every modulus, and reduces,
+// rescales and base-extends them in registers (oz2_chain_device.h): the g
+// drops at once, by the mixed-radix digits over the dropped moduli and one
+// weighted sum per kept residue (drop_extend, bitwise the repeated RnsDrop),
+// and the reconstruction's digits in two blocks (mrc_horner_split).  The
+// output layout puts the next product's direction at p0: with the directions
+// in turn that is the fibres' p1, so the lane's four entries are four
+// consecutive bytes of every output plane.
 //
 // Padding never reaches a result: the encode writes residues of zero there,
 // the operators' columns k >= n are zero (whatever a padded position holds
