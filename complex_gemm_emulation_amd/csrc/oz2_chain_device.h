@@ -11,10 +11,10 @@
 //    mixed-radix digits by successive elimination and the residues on the
 //    dropped moduli from the weights omega_{i,p} = [prod_{l<i} m_l]_p;
 //  - Algorithm 5 (ReconstructFP64): FP64 Horner over the digits.
-// Besides the page's step order (rescale_extend, mrc_horner), the same
-// integers come out of two shortcuts built on the uniqueness of mixed-radix
-// digits: the g drops at once (drop_extend, HBM kernels) and the final
-// digits in two blocks (mrc_horner_split, both kernels).
+// Besides the page's step order (rescale_extend), the same integers come out
+// of two shortcuts built on the uniqueness of mixed-radix digits: the g
+// drops at once (drop_extend, HBM kernels) and the final digits in two
+// blocks (mrc_horner_split, both kernels).
 //
 // Moduli sit right-aligned in kChainMaxS slots, descending, so the smallest
 // (the ones dropped) are always the last slots; unused leading slots carry
@@ -218,45 +218,22 @@ __device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], con
 }
 
 // ReconstructFP64's integer part (Algorithm 5) for the four entries of a
-// lane: centred mixed-radix digits of the residues of every slot (offset by
-// 128 on entry: the first digit step's differences remove it from slots
-// 1 ..; slot 0, the first digit itself, loses it after the steps), then the
-// FP64 Horner sum V = d_0 + m_0 (d_1 + m_1 (...)), each step one rounding of
-// the exact value.
-__device__ __forceinline__ void mrc_horner(const uint32_t (&pk)[kSlots], const ChainTables* T, double (&V)[4]) {
-    float dg[4][kSlots];
-    unpack_tile(pk, dg);
-#pragma unroll
-    for (int i = 0; i < kSlots - 1; ++i)
-#pragma unroll
-        for (int j = i + 1; j < kSlots; ++j) {
-            const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
-        }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) V[q] = (double)dg[q][kSlots - 1];
-#pragma unroll
-    for (int j = kSlots - 2; j >= 0; --j) {
-        const double m = (double)T->mod[j];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) V[q] = fma(m, V[q], (double)dg[q][j]);
-    }
-}
-
-// mrc_horner with the digits in two blocks of kSplit slots: the digits of
-// slots 0 .. kSplit - 1 by elimination among themselves; the residues of
-// X' = (X - A) / M1 at slots kSplit .. 15 (A = sum_{i<kSplit} d_i
-// prod_{l<i} m_l, M1 = prod_{l<kSplit} m_l) from one exact integer sum each,
-// [X']_p = [r_p qinv_p + sum_{i<kSplit} d_i nw_{i,p}]_{m_p} with the table D
-// (qinv_p = [M1^-1]_p, nw_{i,p} = -[prod_{l<i} m_l M1^-1]_p, centred); and
-// the digits of X' over slots kSplit .. 15, which are X's digits there (the
-// mixed-radix digits are unique).  So the digits, and the Horner sum over
-// them, are bitwise those of mrc_horner; 28 + 8 reductions + 28 steps
-// instead of 120.  d_0 and the r_p come in offset by 128; nw_{0,p} = -qinv_p
-// cancels it in the sums, and d_0 loses it after the steps (|sum| < 2^19).
+// lane: the centred mixed-radix digits of the residues of every slot, then
+// the FP64 Horner sum V = d_0 + m_0 (d_1 + m_1 (...)), each step one rounding
+// of the exact value.  The page takes the digits by successive elimination
+// over all 16 slots (120 steps); here they come in two blocks of kSplit:
+//  - the digits of slots 0 .. kSplit - 1 by elimination among themselves;
+//  - the residues of X' = (X - A) / M1 at slots kSplit .. 15, with
+//    A = sum_{i<kSplit} d_i prod_{l<i} m_l and M1 = prod_{l<kSplit} m_l,
+//    from one exact integer sum each, [X']_p = [r_p qinv_p +
+//    sum_{i<kSplit} d_i nw_{i,p}]_{m_p}, with the table D (qinv_p =
+//    [M1^-1]_p, nw_{i,p} = -[prod_{l<i} m_l M1^-1]_p, centred);
+//  - the digits of X' over slots kSplit .. 15, which are X's digits there
+//    (mixed-radix digits are unique).
+// So the digits, and the Horner sum over them, are bitwise those of the
+// single elimination, in 28 + 8 reductions + 28 steps instead of 120.  d_0
+// and the r_p come in offset by 128: nw_{0,p} = -qinv_p cancels the offset
+// in the sums (|sum| < 2^19), and d_0 loses it after the steps.
 constexpr int kSplit = kChainSplit;
 
 __device__ __forceinline__ void mrc_horner_split(const uint32_t (&pk)[kSlots], const ChainTables* T,
