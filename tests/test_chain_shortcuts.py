@@ -1,0 +1,96 @@
+"""The two shortcuts the chain kernels take, pinned on the CPU against the
+oracle's own steps of "You Only Convert Twice: Ozaki Scheme II for Chained
+Tensor Mode Products" (oracle/rescale_be.py), in exact integers:
+
+- the g drops at once: g successive RnsDrops (Algorithm 1, Eq. 15) by the
+  smallest moduli take v to v_g = (v - D) / Q, with Q the product of the
+  dropped moduli and D the part of v that its mixed-radix digits over them
+  represent; so each kept residue is [r_p Q^-1 - sum_j d_j prod_{l<j} q_l
+  Q^-1]_p, from the digits over the dropped moduli alone;
+- the final digits in two blocks: the mixed-radix digits over all moduli
+  (Algorithm 4's MrcDigits, Eq. 24) are those over the first block followed
+  by those of (v - A) / M1 over the second block, whose residues come from
+  one such sum each.
+
+The kernels compute these sums in FP32 from tables the library builds on the
+host (checked against the same definitions by tests/sanitize); here the
+identities themselves are checked, with the oracle's rns_drop and
+mrc_digits as the reference, on random integers of every size the moduli
+allow, for every s and drop count.  The bounds the kernels rely on are
+checked too: every sum stays below 2^19 in magnitude."""
+import numpy as np
+import pytest
+
+import oracle
+
+rb = oracle.rescale_be
+
+
+def _rand_ints(P, count, seed):
+    """count random integers in the centred range of P (Python ints)."""
+    rng = np.random.default_rng(seed)
+    lim = P // 2 - 1
+    out = []
+    for _ in range(count):
+        words = [int(w) for w in rng.integers(0, 2 ** 32, size=(P.bit_length() + 31) // 32 + 1)]
+        v = sum(w << (32 * i) for i, w in enumerate(words)) % (2 * lim + 1)
+        out.append(v - lim)
+    return out
+
+
+def _residues(vals, basis):
+    return {p: np.array([rb.centered(v, p) for v in vals], dtype=np.int64) for p in basis}
+
+
+@pytest.mark.parametrize("s", [4, 8, 12, 15, 16])
+def test_drops_at_once_equal_repeated_rns_drop(s):
+    basis = list(rb.max_product_moduli(s))            # descending: 256 first
+    vals = _rand_ints(rb.moduli_product(basis), 64, 7000 + s)
+    R = _residues(vals, basis)
+    for g in range(1, s):
+        dropped = sorted(basis)[:g]                   # smallest first: q_0, q_1, ..
+        kept = [p for p in basis if p not in dropped]
+        # the oracle: g successive drops
+        Rs, L = dict(R), list(basis)
+        for q in dropped:
+            Rs, L = rb.rns_drop(Rs, L, q)
+        # at once: the digits over the dropped moduli, then one sum per kept modulus
+        digits = rb.mrc_digits(R, dropped)
+        Q = rb.moduli_product(dropped)
+        for p in kept:
+            qinv = pow(Q % p, -1, p)
+            acc = R[p] * rb.centered(qinv, p)
+            for j, d in enumerate(digits):
+                Wj = rb.moduli_product(dropped[:j])
+                acc = acc - d * rb.centered(Wj * qinv % p, p)
+            assert np.all(np.abs(acc) < 2 ** 19), (s, g, p)
+            assert np.array_equal(rb.centered_array(acc, p), Rs[p]), (s, g, p)
+
+
+@pytest.mark.parametrize("s", [4, 8, 12, 15, 16])
+@pytest.mark.parametrize("split", [4, 8])
+def test_digits_in_two_blocks_equal_one_elimination(s, split):
+    basis = list(rb.max_product_moduli(s))
+    if split >= s:
+        pytest.skip("one block")
+    vals = _rand_ints(rb.moduli_product(basis), 64, 7100 + s + split)
+    R = _residues(vals, basis)
+    want = rb.mrc_digits(R, basis)
+    first, second = basis[:split], basis[split:]
+    d1 = rb.mrc_digits(R, first)
+    M1 = rb.moduli_product(first)
+    R2 = {}
+    for p in second:
+        qinv = pow(M1 % p, -1, p)
+        acc = R[p] * rb.centered(qinv, p)
+        for i, d in enumerate(d1):
+            acc = acc - d * rb.centered(rb.moduli_product(first[:i]) * qinv % p, p)
+        assert np.all(np.abs(acc) < 2 ** 19), (s, split, p)
+        R2[p] = rb.centered_array(acc, p)
+    got = d1 + rb.mrc_digits(R2, second)
+    for i, (a, b) in enumerate(zip(got, want)):
+        assert np.array_equal(a, b), (s, split, i)
+    # and the digits rebuild the integers (Eq. 24)
+    W = rb.mixed_radix_weights(basis)
+    for k, v in enumerate(vals[:8]):
+        assert sum(int(d[k]) * w for d, w in zip(got, W)) == v
