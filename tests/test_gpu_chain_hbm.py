@@ -87,6 +87,8 @@ CASES = [
     (36, 10, [1, 3], 3),           # depth 2, store kind 1, np = 40
     (48, 16, [2], 2),              # depth 1: encode, then the last product
     (72, 16, None, 1),             # three k chunks, five operator-row tiles
+    (20, 12, [1, 2, 3, 1, 2, 3, 1, 2], 2),  # depth 8: seven rescaling products, buffers in turn
+    (100, 10, [3, 2, 1], 1),       # staged form (2 chunk pairs, ragged), stores np apart
 ]
 
 
