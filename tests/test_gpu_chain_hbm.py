@@ -10,8 +10,9 @@ the FP64 Horner evaluation and the final scaling, which both sides do in the
 same order with the same roundings).  For n <= 16 the HBM kernels must also
 equal the LDS kernel bit for bit.  The sides cover padding (n not a multiple
 of 8, operator rows beyond a multiple of 16), the drop counts of the
-compile-time instances and the run-time one, every residue layout kind, the
-sub-batches under a memory limit, and the edge tensors.  Larger sides
+compile-time instances and the run-time one, every residue layout kind,
+small s (2: a rescaling product with no drop; 4), the sub-batches under a
+memory limit, and the edge tensors.  Larger sides
 (100, 128, 136, 200, 256: the staged form of the product kernels) are
 checked against stored oracle samples in test_chain_hbm_golden_samples.
 """
@@ -89,6 +90,8 @@ CASES = [
     (72, 16, None, 1),             # three k chunks, five operator-row tiles
     (20, 12, [1, 2, 3, 1, 2, 3, 1, 2], 2),  # depth 8: seven rescaling products, buffers in turn
     (100, 10, [3, 2, 1], 1),       # staged form (2 chunk pairs, ragged), stores np apart
+    (24, 2, None, 2),              # g = 0, 1, 0: a rescaling product with no drop; 14 slots of modulus 1
+    (24, 4, None, 2),              # g = 1, 2; the reconstruction's first digit block holds only slots of modulus 1
 ]
 
 
