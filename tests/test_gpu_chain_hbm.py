@@ -1,8 +1,8 @@
 """GPU parity of the persistent tensor-mode chain on HBM-resident residues
 (OzII-RescaleBE of "You Only Convert Twice: Ozaki Scheme II for Chained
 Tensor Mode Products", Algorithm 7; the kernels of oz2_chain_hbm.hip, which
-run every chain with n > 16 and, on request, smaller ones) against the CPU
-oracle (oracle/rescale_be.py), through the C ABI.
+run every chain with n <= 8 or n > 16 and, on request, the others) against
+the CPU oracle (oracle/rescale_be.py), through the C ABI.
 
 Bar: the plan (b, g) equals the oracle planner's, and every output entry is
 bit-identical to the oracle's (every step is exact integer arithmetic except
