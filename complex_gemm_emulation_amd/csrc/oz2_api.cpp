@@ -1054,7 +1054,8 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
     plan->params.split = plan->drop + depth - 1;
     {
-        // the encode's residue constants of the chain's moduli (index q = slot - first)
+        // the encode's residue constants of the chain's moduli (index q = slot - first);
+        // moduli_plan(s) is non-null here: chain_plan above succeeded with this s
         const ModuliPlan* mpl = moduli_plan(s);
         ChainEncodeConsts& E = plan->params.enc;
         for (int q = 0; q < s; ++q) {
