@@ -375,11 +375,12 @@ class Handle:
                _raw().oz2_chain_plan_create(self._h, n, len(mats), ptrs, pm, s, ctypes.byref(out)))
         return ChainPlan(out, n, s)
 
-    CHAIN_KERNELS = ("auto", "lds", "hbm")
+    CHAIN_KERNELS = ("auto", "lds", "hbm", "hbm_mixed_radix")
 
     def set_chain_kernel(self, kernel: str) -> None:
         """Which kernels run persistent chains (oz2_set_chain_kernel): 'auto'
-        (LDS for 8 < n <= 16, else HBM), 'lds' or 'hbm'."""
+        (LDS for 8 < n <= 16, else HBM), 'lds', 'hbm', or 'hbm_mixed_radix'
+        (HBM with the mixed-radix base extension after every product)."""
         _check("oz2_set_chain_kernel", _raw().oz2_set_chain_kernel(self._h, self.CHAIN_KERNELS.index(kernel)))
 
     def chain_rescale_be(self, plan: ChainPlan, X, Y, batch) -> None:

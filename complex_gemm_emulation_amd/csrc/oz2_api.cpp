@@ -90,6 +90,7 @@ struct oz2_chain_plan {
     int ncp = 0;               // pairs of 32-byte MFMA k chunks covering np
     const int* fexp = nullptr;     // device [3][np] row exponents left pending on each direction
     const ChainDropTable* drop = nullptr;  // device [d] drop weights of each product (HBM kernels)
+    const ChainCrtTable* crt = nullptr;    // device [d] CRT base-extension tables (HBM kernels; used where params.crt)
     const int8_t* hops = nullptr;  // device [d][s][ap / 16][ncp][64][16] operator residues of the HBM kernels
 };
 
@@ -988,7 +989,8 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     const size_t off_fexp = align_up(off_lds + lds_bytes);
     const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
     const size_t off_drop = align_up(off_hops + hops_bytes);
-    const size_t total = off_drop + sizeof(ChainDropTable) * depth;
+    const size_t off_crt = align_up(off_drop + sizeof(ChainDropTable) * depth);
+    const size_t total = off_crt + sizeof(ChainCrtTable) * depth;
     std::vector<char> host;
     std::vector<int8_t> res;
     std::vector<int> fexp;
@@ -1035,6 +1037,8 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         const ChainTables& tabs = *(const ChainTables*)host.data();
         for (int i = 0; i + 1 < depth; ++i) chain_drop_table(tabs, plan->params.g[i], dt + i);
         chain_split_table(tabs, kChainSplit, dt + depth - 1);  // the last product's reconstruction
+        ChainCrtTable* ct = (ChainCrtTable*)(host.data() + off_crt);
+        for (int i = 0; i < depth; ++i) chain_crt_table(tabs, i + 1 < depth ? plan->params.g[i] : 0, ct + i);
     }
     if (!st && hipMalloc(&plan->mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -1052,6 +1056,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->fexp = (const int*)((char*)plan->mem + off_fexp);
     plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
     plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
+    plan->crt = (const ChainCrtTable*)((char*)plan->mem + off_crt);
     plan->params.split = plan->drop + depth - 1;
     {
         // the encode's residue constants of the chain's moduli (index q = slot - first);
@@ -1145,6 +1150,9 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
             P.kind = C.kind[i];
             P.ops = plan->hops + (size_t)i * s * plan->ap * plan->ncp * 64;
             P.drop = plan->drop + i;
+            // the CRT base extension where the plan's bound allows it
+            const bool crt = h->chain_kernel != OZ2_CHAIN_KERNEL_HBM_MIXED_RADIX && C.crt[i];
+            P.crt = !last && C.g[i] > 0 && crt ? plan->crt + i : nullptr;
             OZ2_LAUNCH(launch_chain_step(P, last, stm));
         }
         if (timed) OZ2_LAUNCH(hipEventRecord(h->ev[4], stm));
@@ -1193,7 +1201,7 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
 
 int oz2_set_chain_kernel(oz2_handle_t h, int kernel) {
     if (!h) return -1;
-    if (kernel < OZ2_CHAIN_KERNEL_AUTO || kernel > OZ2_CHAIN_KERNEL_HBM) return -2;
+    if (kernel < OZ2_CHAIN_KERNEL_AUTO || kernel > OZ2_CHAIN_KERNEL_HBM_MIXED_RADIX) return -2;
     h->chain_kernel = kernel;
     return OZ2_STATUS_SUCCESS;
 }

@@ -128,6 +128,60 @@ __device__ __forceinline__ void extend_dropped(int g_rt, float (&r)[4][kSlots], 
         }
 }
 
+// extend_dropped's residues by the Chinese remainder theorem (the table C,
+// see ChainCrtTable): the kept slots are stored, then turned in place into
+// xi_i = [r_i cinv_i]_{m_i}, and every dropped slot p gets
+// [sum_i xi_i cw[p][i] - alpha cM[p]]_{m_p} with alpha = floor(S + 1/2),
+// S = sum_i xi_i fl32(1/m_i).  Exactly, S = X_g / M + alpha with
+// |X_g| / M <= 1/2 - 2^-13 (the plan's condition for C).  In FP32, S + 1/2
+// is within 2^-16 of its exact value (at most 15 terms of magnitude <= 1/2,
+// each off by <= 2^-25 through fl32(1/m_i), 15 roundings of <= 2^-22 in
+// partial sums below 8, one of 2^-21 in adding 1/2), so the floor gives
+// alpha.  The other sums are of exact integers below 2^18.  Both forms give
+// the residues of the same integer X_g, so the results are bitwise equal,
+// with k + 1 products per dropped slot and k reductions in place of
+// extend_dropped's k (k - 1) / 2 digit steps (k kept slots).
+template <int G, class Put>
+__device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], const ChainTables* T,
+                                           const ChainCrtTable* C, const Put& put) {
+    const int g = G >= 0 ? G : g_rt;
+    const int keep = kSlots - 1 - g;
+#pragma unroll
+    for (int u = 0; u < kSlots; ++u)
+        if (u <= keep) put(u, r[0][u], r[1][u], r[2][u], r[3][u]);
+    if (g == 0) return;
+    float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kSlots - 1; ++i)
+        if (i <= keep) {
+            const float c = C->cinv[i], m = T->mod[i], rm = T->rmod[i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                r[e][i] = cmod(r[e][i] * c, m, rm);
+                S[e] = fmaf(r[e][i], rm, S[e]);
+            }
+        }
+    float al[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) al[e] = floorf(S[e] + 0.5f);
+#pragma unroll
+    for (int p = 1; p < kSlots; ++p)
+        if (p > keep) {
+            const float cm = C->cM[p];
+            float ts[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ts[e] = -al[e] * cm;
+#pragma unroll
+            for (int i = 0; i < kSlots - 1; ++i)
+                if (i <= keep) {
+                    const float w = C->cw[p][i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
+                }
+            const float m = T->mod[p], rm = T->rmod[p];
+            put(p, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm), cmod(ts[3], m, rm));
+        }
+}
 
 // After a non-final product, for the four entries of a lane: RnsDrop g times
 // (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), each
@@ -167,10 +221,13 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
 // instead of g modular steps.  The residues and digits are integers, so the
 // result is bitwise that of rescale_extend.  d_0 and the r_p come in offset
 // by 128; nw_{0,p} = -qinv_p cancels it.  The sum runs over j < 8 without
-// guards (zero weights) and over 8 <= j < 15 only when g > 8.
-template <int G, class Put>
+// guards (zero weights) and over 8 <= j < 15 only when g > 8.  The base
+// extension takes the CRT form with CRT (extend_crt, table C), else the
+// mixed-radix form (extend_dropped); a compile-time choice, since the
+// register allocation of a kernel holding both spills hundreds of bytes.
+template <int G, bool CRT, class Put>
 __device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T,
-                                            const ChainDropTable* D, const Put& put) {
+                                            const ChainDropTable* D, const ChainCrtTable* C, const Put& put) {
     const int g = G >= 0 ? G : g_rt;
     const int keep = kSlots - 1 - g;
     // digits over the dropped slots: slot 15 - jp takes its steps with the
@@ -214,7 +271,10 @@ __device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], con
 #pragma unroll
             for (int e = 0; e < 4; ++e) r[e][p] = cmod(acc[e], m, rm);
         }
-    extend_dropped<G>(g_rt, r, T, put);
+    if constexpr (CRT)
+        extend_crt<G>(g_rt, r, T, C, put);
+    else
+        extend_dropped<G>(g_rt, r, T, put);
 }
 
 // ReconstructFP64's integer part (Algorithm 5) for the four entries of a

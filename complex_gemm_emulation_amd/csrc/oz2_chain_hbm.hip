@@ -212,10 +212,11 @@ struct StepConsts {
 // against operator row c mod 8, and every lane's entries are used: the lane
 // of column c holds fibres f0 + 16 (c / 8) + 4 kq + q (the caller's fa).
 // Only the pair's first MFMA carries data.
-template <bool CONTIG, bool LAST, int NCP, bool HALF, class XLoad>
+template <bool CONTIG, bool LAST, int NCP, bool HALF, bool CRT, class XLoad>
 __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepConsts& K, const ChainTables* T,
-                                          const ChainDropTable* DT, int64_t t, int fa, int p1, int p2, int a0,
-                                          int lane, const XLoad& xload, unsigned long long M, double alpha) {
+                                          const ChainDropTable* DT, const ChainCrtTable* CT, int64_t t, int fa,
+                                          int p1, int p2, int a0, int lane, const XLoad& xload,
+                                          unsigned long long M, double alpha) {
     static_assert(!HALF || NCP == 1, "one pair of k chunks at np = 8");
     const int a = HALF ? (lane & 7) : a0 + (lane & 15);  // column of the output (operator row)
     const int8_t* opf = P.ops + ((int64_t)(a0 >> 4) * NCP * 64 + lane) * 16;
@@ -306,20 +307,26 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
                 for (int q = 0; q < 4; ++q) r[q][u] -= 128.0f;
             extend_dropped<-1>(0, r, T, put);
         } else {
-            drop_extend<-1>(P.g, r, T, DT, put);
+            drop_extend<-1, CRT>(P.g, r, T, DT, CT, put);
         }
     }
 }
 
 // the constant tables into LDS (read per use; hoisted into registers they
 // would not fit), with this product's drop weights (the last product's:
-// those of the two-block reconstruction)
-__device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTables& KT, ChainDropTable& KD) {
-    static_assert(sizeof(ChainTables) % 4 == 0 && sizeof(ChainDropTable) % 4 == 0, "words");
+// those of the two-block reconstruction) and its CRT table if it has one
+template <bool CRT>
+__device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTables& KT, ChainDropTable& KD,
+                                             ChainCrtTable& KC) {
+    static_assert(sizeof(ChainTables) % 4 == 0 && sizeof(ChainDropTable) % 4 == 0 &&
+                  sizeof(ChainCrtTable) % 4 == 0, "words");
     for (int x = threadIdx.x; x < (int)(sizeof(ChainTables) / 4); x += blockDim.x)
         ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
     for (int x = threadIdx.x; x < (int)(sizeof(ChainDropTable) / 4); x += blockDim.x)
         ((uint32_t*)&KD)[x] = ((const uint32_t*)P.drop)[x];
+    if (CRT)
+        for (int x = threadIdx.x; x < (int)(sizeof(ChainCrtTable) / 4); x += blockDim.x)
+            ((uint32_t*)&KC)[x] = ((const uint32_t*)P.crt)[x];
     __syncthreads();
 }
 
@@ -335,12 +342,14 @@ __device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTable
 // grid-stride loop, walking the operator's rows in tiles of 16 and reading
 // the fibres' operand from memory (the tile stays in cache between row
 // tiles when there are few of them).
-template <bool CONTIG, bool LAST, int NCP, bool HALF>
+template <bool CONTIG, bool LAST, int NCP, bool HALF, bool CRT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_kernel(ChainHbmParams P) {
+    static_assert(!(LAST && CRT), "the last product has no base extension");
     __shared__ ChainTables KT;
     __shared__ ChainDropTable KD;
-    stage_tables(P, KT, KD);
+    __shared__ ChainCrtTable KC;
+    stage_tables<CRT>(P, KT, KD, KC);
     const StepConsts K(P);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
@@ -380,7 +389,7 @@ void chain_step_kernel(ChainHbmParams P) {
                 const long hi = *(const long*)(x + (k + 8 < np ? k + 8 : 0));
                 return v2l{k < np ? lo : 0l, k + 8 < np ? hi : 0l};
             };
-            step_tile<CONTIG, LAST, NCP, HALF>(P, K, &KT, &KD, t, fa, p1, p2, a0, lane, xload, M, alpha);
+            step_tile<CONTIG, LAST, NCP, HALF, CRT>(P, K, &KT, &KD, &KC, t, fa, p1, p2, a0, lane, xload, M, alpha);
         }
     }
 }
@@ -398,13 +407,15 @@ void chain_step_kernel(ChainHbmParams P) {
 // divide evenly (then LDS admits only two blocks per compute unit, and 4
 // wavefronts each would leave 2 per SIMD to interleave the dependent
 // modular steps), else 4.
-template <bool CONTIG, bool LAST, int NCP, int NW>
+template <bool CONTIG, bool LAST, int NCP, int NW, bool CRT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(LAST ? 2 : 4, LAST ? 2 : 4)))
 void chain_step_staged_kernel(ChainHbmParams P, int F) {
+    static_assert(!(LAST && CRT), "the last product has no base extension");
     __shared__ ChainTables KT;
     __shared__ ChainDropTable KD;
+    __shared__ ChainCrtTable KC;
     extern __shared__ __attribute__((aligned(16))) int8_t xs[];  // [s][F][NCP][64 lanes][16 bytes]
-    stage_tables(P, KT, KD);
+    stage_tables<CRT>(P, KT, KD, KC);
     const StepConsts K(P);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int na = K.ap / 16;                // operator-row tiles
@@ -438,31 +449,41 @@ void chain_step_staged_kernel(ChainHbmParams P, int F) {
             const int fa = fb0 + 16 * f + 4 * (lane >> 4);
             const unsigned long long M = LAST ? P.smax[t] : 0ull;
             const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
-            step_tile<CONTIG, LAST, NCP, false>(P, K, &KT, &KD, t, fa, fa % K.np, fa / K.np, (pr % na) * 16,
-                                                lane, xload, M, alpha);
+            step_tile<CONTIG, LAST, NCP, false, CRT>(P, K, &KT, &KD, &KC, t, fa, fa % K.np, fa / K.np,
+                                                     (pr % na) * 16, lane, xload, M, alpha);
         }
     }
 }
 
 template <int NCP, bool HALF>
 void launch_direct(const ChainHbmParams& P, bool last, dim3 grid, hipStream_t st) {
+    const bool crt = P.crt != nullptr;
     if (last)
-        hipLaunchKernelGGL((chain_step_kernel<true, true, NCP, HALF>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((chain_step_kernel<true, true, NCP, HALF, false>), grid, dim3(256), 0, st, P);
+    else if (P.kind == 0 && crt)
+        hipLaunchKernelGGL((chain_step_kernel<true, false, NCP, HALF, true>), grid, dim3(256), 0, st, P);
     else if (P.kind == 0)
-        hipLaunchKernelGGL((chain_step_kernel<true, false, NCP, HALF>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((chain_step_kernel<true, false, NCP, HALF, false>), grid, dim3(256), 0, st, P);
+    else if (crt)
+        hipLaunchKernelGGL((chain_step_kernel<false, false, NCP, HALF, true>), grid, dim3(256), 0, st, P);
     else
-        hipLaunchKernelGGL((chain_step_kernel<false, false, NCP, HALF>), grid, dim3(256), 0, st, P);
+        hipLaunchKernelGGL((chain_step_kernel<false, false, NCP, HALF, false>), grid, dim3(256), 0, st, P);
 }
 
 template <int NCP, int NW>
 void launch_staged(const ChainHbmParams& P, bool last, dim3 grid, size_t lds, int F, hipStream_t st) {
     const dim3 block(64 * NW);
+    const bool crt = P.crt != nullptr;
     if (last)
-        hipLaunchKernelGGL((chain_step_staged_kernel<true, true, NCP, NW>), grid, block, lds, st, P, F);
+        hipLaunchKernelGGL((chain_step_staged_kernel<true, true, NCP, NW, false>), grid, block, lds, st, P, F);
+    else if (P.kind == 0 && crt)
+        hipLaunchKernelGGL((chain_step_staged_kernel<true, false, NCP, NW, true>), grid, block, lds, st, P, F);
     else if (P.kind == 0)
-        hipLaunchKernelGGL((chain_step_staged_kernel<true, false, NCP, NW>), grid, block, lds, st, P, F);
+        hipLaunchKernelGGL((chain_step_staged_kernel<true, false, NCP, NW, false>), grid, block, lds, st, P, F);
+    else if (crt)
+        hipLaunchKernelGGL((chain_step_staged_kernel<false, false, NCP, NW, true>), grid, block, lds, st, P, F);
     else
-        hipLaunchKernelGGL((chain_step_staged_kernel<false, false, NCP, NW>), grid, block, lds, st, P, F);
+        hipLaunchKernelGGL((chain_step_staged_kernel<false, false, NCP, NW, false>), grid, block, lds, st, P, F);
 }
 
 }  // namespace

@@ -108,9 +108,9 @@ uint64_t row_sum_bound(const int64_t* Abar, int n) {
 // (the basis is descending, so from its end) while floor(B/q) keeps b bits
 // and more than one modulus would remain, each leaving floor(B/q) + 1 (one
 // unit for the rounding of the division), which must stay recoverable on
-// the moduli left, 2 B' < P_L / q.  Sets *removed and B; false when a
-// removal breaks that condition.
-bool greedy_rescale(UBig& B, int b, const int* basis, int s, const UBig& P, int* removed) {
+// the moduli left, 2 B' < P_L / q.  Sets *removed, B and *kept (the product
+// of the moduli left); false when a removal breaks that condition.
+bool greedy_rescale(UBig& B, int b, const int* basis, int s, const UBig& P, int* removed, UBig* kept) {
     const UBig two_b = pow2(b);
     UBig P_left = P;
     int left = s;
@@ -125,6 +125,7 @@ bool greedy_rescale(UBig& B, int b, const int* basis, int s, const UBig& P, int*
         --left;
         ++*removed;
     }
+    *kept = P_left;
     return true;
 }
 
@@ -133,7 +134,10 @@ bool greedy_rescale(UBig& B, int b, const int* basis, int s, const UBig& P, int*
 // keeping 2 B < P; after every product but the last, greedy_rescale, then
 // base extension restores the whole basis for the next product (the
 // proposed method's restoration).  The last product is decoded directly.
-bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* g) {
+// crt[i]: the bound B' left after product i's drops keeps 2^-13 from half
+// the kept moduli's product, 2^13 B' <= (2^12 - 1) P_L (the condition of
+// ChainCrtTable: B' / P_L <= 1/2 - 2^-13).
+bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* g, int* crt) {
     UBig P = UBig::from_u64(1);
     for (int i = 0; i < s; ++i) P.mul_small((uint32_t)basis[i]);
     UBig B = pow2(b);
@@ -141,7 +145,14 @@ bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* 
         B = mul_u64(B, rho[i]);
         if (B.shl(1).cmp(P) >= 0) return false;
         g[i] = 0;
-        if (i < d - 1 && !greedy_rescale(B, b, basis, s, P, &g[i])) return false;
+        crt[i] = 0;
+        if (i < d - 1) {
+            UBig kept;
+            if (!greedy_rescale(B, b, basis, s, P, &g[i], &kept)) return false;
+            UBig lim = kept;
+            lim.mul_small(4095);
+            crt[i] = B.shl(13).cmp(lim) <= 0;
+        }
     }
     return true;
 }
@@ -160,7 +171,7 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
             if (!std::isfinite(ops[i][x])) return -(i + 1);
     std::vector<int64_t> Abar((size_t)d * n * n);
     std::vector<int> f((size_t)d * n), pend((size_t)3 * n);
-    int g[kChainMaxD] = {};
+    int g[kChainMaxD] = {}, crt[kChainMaxD] = {};
     // the effective integer operators at b (the pending scales of a direction
     // folded into the next operator on it) and whether their schedule passes;
     // encoding depends on b, so the bounds are taken afresh for every b
@@ -173,7 +184,7 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
             rho[i] = row_sum_bound(&Abar[(size_t)i * n * n], n);
             std::memcpy(pm, &f[(size_t)i * n], sizeof(int) * n);
         }
-        return drop_plan(b, d, rho, pl->mod, s, g);
+        return drop_plan(b, d, rho, pl->mod, s, g, crt);
     };
     int b = 53;
     while (b >= 1 && !passes(b)) --b;
@@ -182,7 +193,10 @@ int chain_plan(int s, int n, int d, const double* const* ops, const int* modes, 
     P->s = s;
     P->b = b;
     P->d = d;
-    for (int i = 0; i < kChainMaxD; ++i) P->g[i] = i < d ? g[i] : 0;
+    for (int i = 0; i < kChainMaxD; ++i) {
+        P->g[i] = i < d ? g[i] : 0;
+        P->crt[i] = i < d ? crt[i] : 0;
+    }
     // residue layout: a product contracts position 0 and leaves its lane's
     // entries (the old position 1), fibres (old position 2) and outputs (its
     // own direction); the next direction to contract goes to position 0
@@ -288,6 +302,32 @@ void chain_split_table(const ChainTables& T, int split, ChainDropTable* D) {
             D->nw[i][p] = (float)-centered(w * qi % m, m);
             w = w * slot[i] % m;
         }
+    }
+}
+
+void chain_crt_table(const ChainTables& T, int g, ChainCrtTable* C) {
+    std::memset(C, 0, sizeof(*C));
+    if (g < 1 || g > kChainMaxS - 1) return;
+    int slot[kChainMaxS];
+    for (int u = 0; u < kChainMaxS; ++u) slot[u] = (int)T.mod[u];
+    const int keep = kChainMaxS - 1 - g;
+    // M / m_i reduced mod m (the kept moduli but m_i; modulus-1 slots add nothing)
+    auto cofactor = [&](int i, int m) {
+        int64_t w = 1 % m;
+        for (int l = 0; l <= keep; ++l)
+            if (l != i) w = w * slot[l] % m;
+        return w;
+    };
+    for (int i = 0; i <= keep; ++i)
+        if (slot[i] > 1) C->cinv[i] = (float)centered(inverse_mod(cofactor(i, slot[i]), slot[i]), slot[i]);
+    for (int p = keep + 1; p < kChainMaxS; ++p) {
+        const int m = slot[p];
+        if (m == 1) continue;
+        int64_t M = 1;
+        for (int l = 0; l <= keep; ++l) M = M * slot[l] % m;
+        C->cM[p] = (float)centered(M, m);
+        for (int i = 0; i <= keep; ++i)
+            if (slot[i] > 1) C->cw[p][i] = (float)centered(cofactor(i, m), m);
     }
 }
 

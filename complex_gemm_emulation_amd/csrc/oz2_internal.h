@@ -139,6 +139,8 @@ struct ChainParams {
     int64_t batch;
     int n, s, b, d;
     int g[kChainMaxD];           // moduli dropped after product i (g[d - 1] = 0)
+    int crt[kChainMaxD];         // 1: after product i's drops |X_g| <= (1/2 - 2^-13) M (M: the kept moduli), so
+                                 // that its base extension may take the CRT form (ChainCrtTable)
     // residue layout: position 0 of a plane row is the contracted direction.
     // m0: direction at position 0 before the first product (positions hold
     // m0, m0 + 1, m0 + 2 mod 3); kind[i]: how product i's output is stored
@@ -177,6 +179,21 @@ struct ChainDropTable {
     float nw[kChainMaxS - 1][kChainMaxS];   // -[prod_{l<j} q_l Q^{-1}]_{m_p}
 };
 void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D);
+// Per non-final product with g >= 1 drops: the base extension of X_g from
+// its kept slots 0 .. 15 - g (M the product of their moduli) to the dropped
+// slots by the Chinese remainder theorem instead of mixed-radix digits.
+// With xi_i = [r_i cinv[i]]_{m_i}, sum_i xi_i M / m_i = X_g + alpha M for the
+// integer alpha = round(sum_i xi_i / m_i), so that
+// [X_g]_p = [sum_i xi_i cw[p][i] - alpha cM[p]]_{m_p}.  Centred values; zero
+// for slots of modulus 1, cinv for the dropped slots, cw and cM for the kept
+// ones.  Used only where the plan bounds |X_g| by (1/2 - 2^-13) M
+// (ChainParams::crt), which keeps the rounding of alpha away from a tie.
+struct ChainCrtTable {
+    float cinv[kChainMaxS];            // [(M / m_i)^{-1}]_{m_i}, kept i
+    float cM[kChainMaxS];              // [M]_{m_p}, dropped p
+    float cw[kChainMaxS][kChainMaxS];  // cw[p][i] = [M / m_i]_{m_p}, dropped p, kept i
+};
+void chain_crt_table(const ChainTables& T, int g, ChainCrtTable* C);
 // The last product's table for the two-block reconstruction: slots 0 ..
 // split - 1 play the dropped moduli (in that order, M1 their product) for
 // the slots split .. 15: qinv[p] = [M1^{-1}]_{m_p},
@@ -219,6 +236,7 @@ struct ChainHbmParams {
                                  // order (ap = np rounded up to 16, ncp = np / 64 rounded up)
     const float* tab;            // ChainTables
     const ChainDropTable* drop;  // this product's drop weights (g >= 1; the last product: chain_split_table)
+    const ChainCrtTable* crt;    // this product's CRT base extension, or null: the mixed-radix form
     const int* fexp;             // [3][np] row exponents left pending on each direction
     unsigned long long* smax;    // [batch] max |x| bit pattern of each tensor (0 before the scan)
     const int8_t* in;            // planes [s][batch][np^3] read by this product

@@ -6,7 +6,8 @@
 // n, s, depth and mode orders, including non-finite and all-zero operators.
 // The weight tables are also checked against their definitions, in exact
 // integers on random residue vectors: the one-pass drop against g repeated
-// RnsDrops, the two-block digits against one elimination over all slots.
+// RnsDrops, the two-block digits against one elimination over all slots,
+// the CRT base extension against the residues of the integer it extends.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -99,6 +100,45 @@ static int check_split_table(const ChainTables& T) {
     return bad;
 }
 
+// CRT base extension (chain_crt_table's weights and the kernels' FP32
+// rounding of alpha) against the residues of the integer itself: X drawn in
+// |X| <= (1/2 - 2^-13) M, the plan's condition, with both ends of that range
+static int check_crt_table(const ChainTables& T, int g) {
+    ChainCrtTable C;
+    chain_crt_table(T, g, &C);
+    int m[kChainMaxS], bad = 0;
+    for (int u = 0; u < kChainMaxS; ++u) m[u] = (int)T.mod[u];
+    const int keep = kChainMaxS - 1 - g;
+    __int128 M = 1;  // at most 15 moduli below 2^8: below 2^120
+    for (int i = 0; i <= keep; ++i) M *= m[i];
+    const __int128 lim = M / 2 - (M + 8191) / 8192;  // <= (1/2 - 2^-13) M
+    const auto res = [](__int128 x, int q) { return centered_i((int64_t)(x % q), q); };
+    for (int trial = 0; trial < 24; ++trial) {
+        const unsigned __int128 rnd = (unsigned __int128)next_u64() << 64 | next_u64();
+        __int128 X = (__int128)(rnd % (unsigned __int128)(lim + 1));
+        if (trial % 2) X = -X;
+        if (trial < 2) X = trial ? -lim : lim;
+        int xi[kChainMaxS] = {};
+        float S = 0.0f;
+        __int128 sum = 0;
+        for (int i = 0; i <= keep; ++i) {
+            if (m[i] == 1) continue;
+            xi[i] = centered_i((int64_t)res(X, m[i]) * (int)C.cinv[i], m[i]);
+            S = std::fmaf((float)xi[i], T.rmod[i], S);
+            sum += (__int128)xi[i] * (M / m[i]);
+        }
+        const int alpha = (int)std::floor(S + 0.5f);
+        bad += (sum - X) % M != 0 || (sum - X) / M != alpha;
+        for (int p = keep + 1; p < kChainMaxS; ++p) {
+            int64_t acc = -(int64_t)alpha * (int)C.cM[p];
+            for (int i = 0; i <= keep; ++i) acc += (int64_t)xi[i] * (int)C.cw[p][i];
+            bad += acc >= (1 << 18) || acc <= -(1 << 18);
+            bad += centered_i(acc, m[p]) != res(X, m[p]);
+        }
+    }
+    return bad;
+}
+
 int main() {
     int bad = 0;
     for (int s = -1; s <= 26; ++s) {
@@ -141,7 +181,7 @@ int main() {
         if (rep % 7 == 3) bad += st != -d;
         if (st == 0) {
             for (int i = 0; i + 1 < d; ++i)
-                if (P.g[i] >= 1) bad += check_drop_table(T, P.g[i]);
+                if (P.g[i] >= 1) bad += check_drop_table(T, P.g[i]) + check_crt_table(T, P.g[i]);
             bad += check_split_table(T);
         }
     }
@@ -160,7 +200,8 @@ int main() {
                         if ((int64_t)mi * x % mj == 1) { iv = x; break; }
                 T.inv[i][j] = (float)iv;
             }
-        for (int g = 1; g < s; ++g) bad += check_drop_table(T, g);
+        for (int u = 0; u < kChainMaxS; ++u) T.rmod[u] = 1.0f / T.mod[u];
+        for (int g = 1; g < s; ++g) bad += check_drop_table(T, g) + check_crt_table(T, g);
         bad += check_split_table(T);
     }
     std::printf("planner driver: %d unexpected results\n", bad);

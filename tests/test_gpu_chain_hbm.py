@@ -7,8 +7,9 @@ the CPU oracle (oracle/rescale_be.py), through the C ABI.
 Bar: the plan (b, g) equals the oracle planner's, and every output entry is
 bit-identical to the oracle's (every step is exact integer arithmetic except
 the FP64 Horner evaluation and the final scaling, which both sides do in the
-same order with the same roundings).  For n <= 16 the HBM kernels must also
-equal the LDS kernel bit for bit.  The sides cover padding (n not a multiple
+same order with the same roundings), with the base extension in the CRT form
+(where the plan allows it) and in the mixed-radix form.  For n <= 16 the HBM
+kernels must also equal the LDS kernel bit for bit.  The sides cover padding (n not a multiple
 of 8, operator rows beyond a multiple of 16), the drop counts of the
 compile-time instances and the run-time one, every residue layout kind,
 small s (2: a rescaling product with no drop; 4), the sub-batches under a
@@ -105,9 +106,12 @@ def test_chain_hbm_matches_oracle_bitwise(handle, n, s, modes, batch):
     X = workloads.tensor_batch(n, batch, 9100 + n + s)
     want, plan = rb.rescale_be_chain(X, ops, n, s, batch, None if modes is None else [m - 1 for m in modes])
     assert plan is not None
-    got, info = _run(handle, ops, n, s, X, batch, modes)
-    assert info == (d, plan["b"], plan["g"]), (info, plan["b"], plan["g"])
-    _check_bitwise(got, want, f"n={n} s={s} modes={modes}")
+    # auto: the CRT base extension where the plan's bound allows it;
+    # hbm_mixed_radix: the mixed-radix one after every product
+    for kernel in ("auto", "hbm_mixed_radix"):
+        got, info = _run(handle, ops, n, s, X, batch, modes, kernel)
+        assert info == (d, plan["b"], plan["g"]), (info, plan["b"], plan["g"])
+        _check_bitwise(got, want, f"n={n} s={s} modes={modes} {kernel}")
 
 
 SMALL_CASES = [
@@ -225,16 +229,18 @@ GOLDEN_CASES = _golden_cases()
 def test_chain_hbm_golden_samples(handle, case):
     """the staged product kernels with 2, 3 and 4 pairs of k chunks (n = 100,
     128, 136, 200, 256; 8 wavefronts per block at 256), in turn and in other
-    mode orders (store kinds 1 and 2): seeded entries of each tensor against
-    values the oracle computed once (tests/golden/make_chain_hbm_samples.py)"""
+    mode orders (store kinds 1 and 2), with both forms of the base extension:
+    seeded entries of each tensor against values the oracle computed once
+    (tests/golden/make_chain_hbm_samples.py)"""
     c = GOLDEN_CASES[case]
     n, s, batch, modes = c["n"], c["s"], c["batch"], c.get("modes")
     d = 3 if modes is None else len(modes)
     _say(f"[chain hbm golden] n={n} s={s} batch={batch} modes={modes}")
     ops = _ops(n, c["ops_seed"], d)
     X = workloads.tensor_batch(n, batch, c["x_seed"])
-    got, info = _run(handle, ops, n, s, X, batch, modes)
-    assert info == (d, c["b"], c["g"]), info
     idx = np.array(c["index"], dtype=np.int64)
     want = np.array([float.fromhex(v) for v in c["value"]])
-    _check_bitwise(got[idx], want, f"golden n={n} modes={modes}")
+    for kernel in ("auto", "hbm_mixed_radix"):
+        got, info = _run(handle, ops, n, s, X, batch, modes, kernel)
+        assert info == (d, c["b"], c["g"]), info
+        _check_bitwise(got[idx], want, f"golden n={n} modes={modes} {kernel}")
