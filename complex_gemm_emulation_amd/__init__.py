@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "oz2_set_debug", "oz2_debug_copy", "oz2_test_crt", "oz2_operand_create",
     "oz2_operand_update", "oz2_operand_destroy", "oz2_gemm_prepared", "oz2_chain_plan_create",
     "oz2_chain_plan_info", "oz2_chain_rescale_be", "oz2_chain_plan_destroy", "oz2_dgemm_noalloc",
-    "oz2_get_tile_plan", "oz2_set_chain_kernel",
+    "oz2_get_tile_plan", "oz2_set_chain_kernel", "oz2_set_chain_crt",
 )
 
 _lib = None
@@ -67,6 +67,7 @@ def _raw():
             "oz2_dgemm_noalloc": [P, C, C, I64, I64, I64, D, P, I64, P, I64, D, P, I64, I],
             "oz2_get_tile_plan": [P, P, P, P],
             "oz2_set_chain_kernel": [P, I],
+            "oz2_set_chain_crt": [P, I],
             "oz2_zgemm": [P, C, C, I64, I64, I64, P, P, I64, P, I64, P, P, I64, I],
             "oz2_dgemm_strided_batched": [P, C, C, I64, I64, I64, D, P, I64, I64, P, I64, I64, D,
                                           P, I64, I64, I64, I],
@@ -375,13 +376,18 @@ class Handle:
                _raw().oz2_chain_plan_create(self._h, n, len(mats), ptrs, pm, s, ctypes.byref(out)))
         return ChainPlan(out, n, s)
 
-    CHAIN_KERNELS = ("auto", "lds", "hbm", "hbm_mixed_radix")
+    CHAIN_KERNELS = ("auto", "lds", "hbm")
 
     def set_chain_kernel(self, kernel: str) -> None:
         """Which kernels run persistent chains (oz2_set_chain_kernel): 'auto'
-        (LDS for 8 < n <= 16, else HBM), 'lds', 'hbm', or 'hbm_mixed_radix'
-        (HBM with the mixed-radix base extension after every product)."""
+        (LDS for 8 < n <= 16, else HBM), 'lds' or 'hbm'."""
         _check("oz2_set_chain_kernel", _raw().oz2_set_chain_kernel(self._h, self.CHAIN_KERNELS.index(kernel)))
+
+    def set_chain_crt(self, enable: bool) -> None:
+        """Base extension of the chain kernels (oz2_set_chain_crt): the CRT
+        form where the plan allows it (True, the default) or the mixed-radix
+        form after every product (False)."""
+        _check("oz2_set_chain_crt", _raw().oz2_set_chain_crt(self._h, 1 if enable else 0))
 
     def chain_rescale_be(self, plan: ChainPlan, X, Y, batch) -> None:
         """Run a planned chain on `batch` tensors (oz2_chain_rescale_be)."""

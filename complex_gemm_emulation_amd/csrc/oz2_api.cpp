@@ -66,6 +66,7 @@ struct oz2_context {
     int tile_held = OZ2_TILE_UNTILED;
     // which kernels run a persistent chain (OZ2_CHAIN_KERNEL_*)
     int chain_kernel = OZ2_CHAIN_KERNEL_AUTO;
+    int chain_crt = 1;  // base extension in the CRT form where the plan allows it
 };
 
 // a scanned and encoded operand kept on the device between products
@@ -91,6 +92,7 @@ struct oz2_chain_plan {
     const int* fexp = nullptr;     // device [3][np] row exponents left pending on each direction
     const ChainDropTable* drop = nullptr;  // device [d] drop weights of each product (HBM kernels)
     const ChainCrtTable* crt = nullptr;    // device [d] CRT base-extension tables (HBM kernels; used where params.crt)
+    const float* tab_hbm = nullptr;        // device ChainTables of the HBM kernels (params.tab: the LDS kernel's)
     const int8_t* hops = nullptr;  // device [d][s][ap / 16][ncp][64][16] operator residues of the HBM kernels
 };
 
@@ -990,7 +992,10 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
     const size_t off_drop = align_up(off_hops + hops_bytes);
     const size_t off_crt = align_up(off_drop + sizeof(ChainDropTable) * depth);
-    const size_t total = off_crt + sizeof(ChainCrtTable) * depth;
+    // the LDS kernel's own copy of the tables, with the CRT table in place of
+    // the mixed-radix weights when every rescaling can take the CRT form
+    const size_t off_tlds = align_up(off_crt + sizeof(ChainCrtTable) * depth);
+    const size_t total = off_tlds + sizeof(ChainTables);
     std::vector<char> host;
     std::vector<int8_t> res;
     std::vector<int> fexp;
@@ -1039,6 +1044,15 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         chain_split_table(tabs, kChainSplit, dt + depth - 1);  // the last product's reconstruction
         ChainCrtTable* ct = (ChainCrtTable*)(host.data() + off_crt);
         for (int i = 0; i < depth; ++i) chain_crt_table(tabs, i + 1 < depth ? plan->params.g[i] : 0, ct + i);
+        // the LDS kernel holds one table in the mixed-radix weights' place:
+        // the CRT form when every rescaling drops the same count, with margin
+        bool lds_crt = depth >= 2;
+        for (int i = 0; i + 1 < depth; ++i)
+            lds_crt = lds_crt && plan->params.crt[i] && plan->params.g[i] == plan->params.g[0];
+        ChainTables* tl = (ChainTables*)(host.data() + off_tlds);
+        *tl = tabs;
+        if (lds_crt) tl->crt = ct[0];
+        plan->params.lds_crt = lds_crt;
     }
     if (!st && hipMalloc(&plan->mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -1051,7 +1065,8 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         delete plan;
         return st;
     }
-    plan->params.tab = (const float*)plan->mem;
+    plan->tab_hbm = (const float*)plan->mem;
+    plan->params.tab = (const float*)((char*)plan->mem + off_tlds);
     plan->params.ops = lds ? (const int8_t*)((char*)plan->mem + off_lds) : nullptr;
     plan->fexp = (const int*)((char*)plan->mem + off_fexp);
     plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
@@ -1129,7 +1144,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
         P.m0 = C.m0;
         for (int j = 0; j < 3; ++j) P.fin[j] = C.fin[j];
         P.Qd = C.Qd;
-        P.tab = C.tab;
+        P.tab = plan->tab_hbm;
         P.fexp = plan->fexp;
         P.smax = (unsigned long long*)ws;
         P.pstride = nb * np3;
@@ -1151,7 +1166,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
             P.ops = plan->hops + (size_t)i * s * plan->ap * plan->ncp * 64;
             P.drop = plan->drop + i;
             // the CRT base extension where the plan's bound allows it
-            const bool crt = h->chain_kernel != OZ2_CHAIN_KERNEL_HBM_MIXED_RADIX && C.crt[i];
+            const bool crt = h->chain_crt && C.crt[i];
             P.crt = !last && C.g[i] > 0 && crt ? plan->crt + i : nullptr;
             OZ2_LAUNCH(launch_chain_step(P, last, stm));
         }
@@ -1187,6 +1202,11 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
     P.X = X;
     P.Y = Y;
     P.batch = batch;
+    if (!h->chain_crt) {
+        // the tables with the mixed-radix weights
+        P.tab = plan->tab_hbm;
+        P.lds_crt = 0;
+    }
     hipStream_t stm = h->stream;
     if (h->timing)
         for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));
@@ -1199,9 +1219,16 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
     return OZ2_STATUS_SUCCESS;
 }
 
+int oz2_set_chain_crt(oz2_handle_t h, int enable) {
+    if (!h) return -1;
+    if (enable != 0 && enable != 1) return -2;
+    h->chain_crt = enable;
+    return OZ2_STATUS_SUCCESS;
+}
+
 int oz2_set_chain_kernel(oz2_handle_t h, int kernel) {
     if (!h) return -1;
-    if (kernel < OZ2_CHAIN_KERNEL_AUTO || kernel > OZ2_CHAIN_KERNEL_HBM_MIXED_RADIX) return -2;
+    if (kernel < OZ2_CHAIN_KERNEL_AUTO || kernel > OZ2_CHAIN_KERNEL_HBM) return -2;
     h->chain_kernel = kernel;
     return OZ2_STATUS_SUCCESS;
 }

@@ -76,8 +76,9 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
     }
 }
 
-// unpack the four entries of every slot of one tile and rescale them
-template <int G0, int G1, bool ANY>
+// unpack the four entries of every slot of one tile and rescale them (CRT:
+// the base extension in the CRT form, on the table T->crt)
+template <int G0, int G1, bool ANY, bool CRT>
 __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint32_t (&pk)[kSlots],
                                              const ChainTables* T, int8_t* at, int step) {
     // offset by 128; the first drop's differences remove the offset from
@@ -96,20 +97,22 @@ __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint3
         store4<ANY>(at + u * kPlane, step, r0, r1, r2, r3);
     };
     if (G0 >= 0 && G0 == G1)
-        rescale_extend<G0>(0, r, T, put);
+        rescale_extend<G0, CRT>(0, r, T, put);
     else if (G0 >= 0 && mode == 0)
-        rescale_extend<G0>(0, r, T, put);
+        rescale_extend<G0, CRT>(0, r, T, put);
     else if (G0 >= 0)
-        rescale_extend<G1>(0, r, T, put);
+        rescale_extend<G1, CRT>(0, r, T, put);
     else
-        rescale_extend<-1>(g[mode], r, T, put);
+        rescale_extend<-1, CRT>(g[mode], r, T, put);
 }
 
 // G0, G1: the drop counts after products 1 and 2 when fixed at compile time
 // (G0 = G1: after every product but the last), -1 to read them from P.g;
 // D: the depth when fixed at compile time with the modes 1, 2, 3 (every
-// residue store contiguous), 0 to read the depth, modes and layouts from P
-template <int G0, int G1, int D>
+// residue store contiguous), 0 to read the depth, modes and layouts from P;
+// CRT: every rescaling drops the same count and extends in the CRT form
+// (P.lds_crt: the table P.tab->crt in place of the mixed-radix weights)
+template <int G0, int G1, int D, bool CRT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 4)))
 void chain_kernel(ChainParams P) {
     __shared__ __attribute__((aligned(16))) int8_t buf[kSlots * kPlane];
@@ -230,9 +233,9 @@ void chain_kernel(ChainParams P) {
             return buf + (kind == 0 ? (t + 16 * a) * kChainN + 4 * kq
                                     : kind == 1 ? t + 64 * kq + 256 * a : a + 64 * kq + 256 * t);
         };
-        rescale_tile<G0, G1, D == 0>(mode, P.g, pk0, T, at(wave), step);
+        rescale_tile<G0, G1, D == 0, CRT>(mode, P.g, pk0, T, at(wave), step);
         asm volatile("" ::: "memory");  // one tile at a time
-        rescale_tile<G0, G1, D == 0>(mode, P.g, pk1, T, at(wave + 8), step);
+        rescale_tile<G0, G1, D == 0, CRT>(mode, P.g, pk1, T, at(wave + 8), step);
         asm volatile("" ::: "memory");
         // operator mode + 3 into the buffer this product read (before the
         // barrier above); it is next read three products later
@@ -295,22 +298,38 @@ hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
     bool same = P.d >= 2;
     for (int i = 1; i + 1 < P.d; ++i) same = same && P.g[i] == P.g[0];
     const int g0 = same ? P.g[0] : -1;
+    // the CRT form needs the common drop count's table in place of the
+    // mixed-radix weights
+    bool crt = P.lds_crt != 0 && same;
+    for (int i = 0; i + 1 < P.d; ++i) crt = crt && P.crt[i];
     const dim3 grid((unsigned)P.batch), block(512);
     if (P.d == 3 && P.cyclic) {
-        if (g0 == 7)
-            hipLaunchKernelGGL((chain_kernel<7, 7, 3>), grid, block, 0, st, P);
+        if (g0 == 7 && crt)
+            hipLaunchKernelGGL((chain_kernel<7, 7, 3, true>), grid, block, 0, st, P);
+        else if (g0 == 7)
+            hipLaunchKernelGGL((chain_kernel<7, 7, 3, false>), grid, block, 0, st, P);
+        else if (g0 == 6 && crt)
+            hipLaunchKernelGGL((chain_kernel<6, 6, 3, true>), grid, block, 0, st, P);
         else if (g0 == 6)
-            hipLaunchKernelGGL((chain_kernel<6, 6, 3>), grid, block, 0, st, P);
+            hipLaunchKernelGGL((chain_kernel<6, 6, 3, false>), grid, block, 0, st, P);
+        else if (g0 == 4 && crt)
+            hipLaunchKernelGGL((chain_kernel<4, 4, 3, true>), grid, block, 0, st, P);
         else if (g0 == 4)
-            hipLaunchKernelGGL((chain_kernel<4, 4, 3>), grid, block, 0, st, P);
+            hipLaunchKernelGGL((chain_kernel<4, 4, 3, false>), grid, block, 0, st, P);
         else if (P.g[0] == 4 && P.g[1] == 5)
-            hipLaunchKernelGGL((chain_kernel<4, 5, 3>), grid, block, 0, st, P);
+            hipLaunchKernelGGL((chain_kernel<4, 5, 3, false>), grid, block, 0, st, P);
+        else if (crt)
+            hipLaunchKernelGGL((chain_kernel<-1, -1, 3, true>), grid, block, 0, st, P);
         else
-            hipLaunchKernelGGL((chain_kernel<-1, -1, 3>), grid, block, 0, st, P);
+            hipLaunchKernelGGL((chain_kernel<-1, -1, 3, false>), grid, block, 0, st, P);
+    } else if (g0 == 7 && crt) {
+        hipLaunchKernelGGL((chain_kernel<7, 7, 0, true>), grid, block, 0, st, P);
     } else if (g0 == 7) {
-        hipLaunchKernelGGL((chain_kernel<7, 7, 0>), grid, block, 0, st, P);
+        hipLaunchKernelGGL((chain_kernel<7, 7, 0, false>), grid, block, 0, st, P);
+    } else if (crt) {
+        hipLaunchKernelGGL((chain_kernel<-1, -1, 0, true>), grid, block, 0, st, P);
     } else {
-        hipLaunchKernelGGL((chain_kernel<-1, -1, 0>), grid, block, 0, st, P);
+        hipLaunchKernelGGL((chain_kernel<-1, -1, 0, false>), grid, block, 0, st, P);
     }
     return hipGetLastError();
 }

@@ -129,10 +129,10 @@ __device__ __forceinline__ void extend_dropped(int g_rt, float (&r)[4][kSlots], 
 }
 
 // extend_dropped's residues by the Chinese remainder theorem (the table C,
-// see ChainCrtTable): the kept slots are stored, then turned in place into
-// xi_i = [r_i cinv_i]_{m_i}, and every dropped slot p gets
-// [sum_i xi_i cw[p][i] - alpha cM[p]]_{m_p} with alpha = floor(S + 1/2),
-// S = sum_i xi_i fl32(1/m_i).  Exactly, S = X_g / M + alpha with
+// see ChainCrtTable; 1 <= g <= 14): the kept slots are stored, then turned
+// in place into xi_i = [r_i cinv_i]_{m_i}, and every dropped slot p gets
+// [sum_i xi_i [M / m_i]_{m_p} - alpha [M]_{m_p}]_{m_p} with
+// alpha = floor(S + 1/2), S = sum_i xi_i fl32(1/m_i).  Exactly, S = X_g / M + alpha with
 // |X_g| / M <= 1/2 - 2^-13 (the plan's condition for C).  In FP32, S + 1/2
 // is within 2^-16 of its exact value (at most 15 terms of magnitude <= 1/2,
 // each off by <= 2^-25 through fl32(1/m_i), 15 roundings of <= 2^-22 in
@@ -154,7 +154,7 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
 #pragma unroll
     for (int i = 0; i < kSlots - 1; ++i)
         if (i <= keep) {
-            const float c = C->cinv[i], m = T->mod[i], rm = T->rmod[i];
+            const float c = C->w[0][i], m = T->mod[i], rm = T->rmod[i];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 r[e][i] = cmod(r[e][i] * c, m, rm);
@@ -167,14 +167,14 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
 #pragma unroll
     for (int p = 1; p < kSlots; ++p)
         if (p > keep) {
-            const float cm = C->cM[p];
+            const float cm = C->w[1][p];
             float ts[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ts[e] = -al[e] * cm;
 #pragma unroll
             for (int i = 0; i < kSlots - 1; ++i)
                 if (i <= keep) {
-                    const float w = C->cw[p][i];
+                    const float w = C->w[p][i];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
                 }
@@ -185,11 +185,12 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
 
 // After a non-final product, for the four entries of a lane: RnsDrop g times
 // (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), each
-// drop updating every remaining slot, then extend_dropped.  Every slot loop
-// is unrolled (G as in extend_dropped).  The residues come in offset by 128:
-// the first drop's differences remove the offset from every kept slot (with
-// no drop the caller removes it).
-template <int G, class Put>
+// drop updating every remaining slot, then extend_dropped, or with CRT
+// extend_crt on the table T->crt.  Every slot loop is unrolled (G as in
+// extend_dropped).  The residues come in offset by 128: the first drop's
+// differences remove the offset from every kept slot (with no drop the
+// caller removes it).
+template <int G, bool CRT, class Put>
 __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, const Put& put) {
     const int g = G >= 0 ? G : g_rt;
     const int keep = kSlots - 1 - g;
@@ -203,7 +204,10 @@ __device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], 
                 for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
             }
         }
-    extend_dropped<G>(g_rt, r, T, put);
+    if constexpr (CRT)
+        extend_crt<G>(g_rt, r, T, &T->crt, put);
+    else
+        extend_dropped<G>(g_rt, r, T, put);
 }
 
 // The same result with the g drops taken at once (g >= 1; G >= 1 a

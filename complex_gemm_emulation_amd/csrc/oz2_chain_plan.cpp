@@ -134,9 +134,10 @@ bool greedy_rescale(UBig& B, int b, const int* basis, int s, const UBig& P, int*
 // keeping 2 B < P; after every product but the last, greedy_rescale, then
 // base extension restores the whole basis for the next product (the
 // proposed method's restoration).  The last product is decoded directly.
-// crt[i]: the bound B' left after product i's drops keeps 2^-13 from half
-// the kept moduli's product, 2^13 B' <= (2^12 - 1) P_L (the condition of
-// ChainCrtTable: B' / P_L <= 1/2 - 2^-13).
+// crt[i]: 1 <= g[i] <= 14 (the packing of ChainCrtTable needs slots 0 and 1
+// kept) and the bound B' left after product i's drops keeps 2^-13 from half
+// the kept moduli's product, 2^13 B' <= (2^12 - 1) P_L
+// (B' / P_L <= 1/2 - 2^-13).
 bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* g, int* crt) {
     UBig P = UBig::from_u64(1);
     for (int i = 0; i < s; ++i) P.mul_small((uint32_t)basis[i]);
@@ -151,7 +152,7 @@ bool drop_plan(int b, int d, const uint64_t* rho, const int* basis, int s, int* 
             if (!greedy_rescale(B, b, basis, s, P, &g[i], &kept)) return false;
             UBig lim = kept;
             lim.mul_small(4095);
-            crt[i] = B.shl(13).cmp(lim) <= 0;
+            crt[i] = g[i] >= 1 && g[i] <= kChainMaxS - 2 && B.shl(13).cmp(lim) <= 0;
         }
     }
     return true;
@@ -307,7 +308,7 @@ void chain_split_table(const ChainTables& T, int split, ChainDropTable* D) {
 
 void chain_crt_table(const ChainTables& T, int g, ChainCrtTable* C) {
     std::memset(C, 0, sizeof(*C));
-    if (g < 1 || g > kChainMaxS - 1) return;
+    if (g < 1 || g > kChainMaxS - 2) return;
     int slot[kChainMaxS];
     for (int u = 0; u < kChainMaxS; ++u) slot[u] = (int)T.mod[u];
     const int keep = kChainMaxS - 1 - g;
@@ -319,15 +320,15 @@ void chain_crt_table(const ChainTables& T, int g, ChainCrtTable* C) {
         return w;
     };
     for (int i = 0; i <= keep; ++i)
-        if (slot[i] > 1) C->cinv[i] = (float)centered(inverse_mod(cofactor(i, slot[i]), slot[i]), slot[i]);
+        if (slot[i] > 1) C->w[0][i] = (float)centered(inverse_mod(cofactor(i, slot[i]), slot[i]), slot[i]);
     for (int p = keep + 1; p < kChainMaxS; ++p) {
         const int m = slot[p];
         if (m == 1) continue;
         int64_t M = 1;
         for (int l = 0; l <= keep; ++l) M = M * slot[l] % m;
-        C->cM[p] = (float)centered(M, m);
+        C->w[1][p] = (float)centered(M, m);
         for (int i = 0; i <= keep; ++i)
-            if (slot[i] > 1) C->cw[p][i] = (float)centered(cofactor(i, m), m);
+            if (slot[i] > 1) C->w[p][i] = (float)centered(cofactor(i, m), m);
     }
 }
 

@@ -139,8 +139,10 @@ struct ChainParams {
     int64_t batch;
     int n, s, b, d;
     int g[kChainMaxD];           // moduli dropped after product i (g[d - 1] = 0)
-    int crt[kChainMaxD];         // 1: after product i's drops |X_g| <= (1/2 - 2^-13) M (M: the kept moduli), so
-                                 // that its base extension may take the CRT form (ChainCrtTable)
+    int crt[kChainMaxD];         // 1: 1 <= g[i] <= 14 and after product i's drops |X_g| <= (1/2 - 2^-13) M
+                                 // (M: the kept moduli), so that its base extension may take the CRT form
+    int lds_crt;                 // 1: tab->crt holds the CRT table of the common drop count of every
+                                 // rescaling (the LDS kernel's CRT instances)
     // residue layout: position 0 of a plane row is the contracted direction.
     // m0: direction at position 0 before the first product (positions hold
     // m0, m0 + 1, m0 + 2 mod 3); kind[i]: how product i's output is stored
@@ -157,11 +159,31 @@ struct ChainParams {
     ChainEncodeConsts enc;       // the encode's residue constants
 };
 
+// Per non-final product with 1 <= g <= 14 drops: the base extension of X_g
+// from its kept slots 0 .. keep = 15 - g (M the product of their moduli) to
+// the dropped slots by the Chinese remainder theorem instead of mixed-radix
+// digits.  With xi_i = [r_i cinv_i]_{m_i}, cinv_i = [(M / m_i)^{-1}]_{m_i},
+// sum_i xi_i M / m_i = X_g + alpha M for the integer
+// alpha = round(sum_i xi_i / m_i), so that
+// [X_g]_p = [sum_i xi_i [M / m_i]_{m_p} - alpha [M]_{m_p}]_{m_p}.
+// Packed in one 16 x 16 block, centred values: w[0][i] = cinv_i (kept i),
+// w[1][p] = [M]_{m_p} (dropped p), w[p][i] = [M / m_i]_{m_p} (dropped p,
+// kept i); rows 0 and 1 are kept slots since keep >= 1.  Zero elsewhere and
+// for slots of modulus 1.  Used only where the plan bounds |X_g| by
+// (1/2 - 2^-13) M (ChainParams::crt), which keeps the rounding of alpha away
+// from a tie.
+struct ChainCrtTable {
+    float w[kChainMaxS][kChainMaxS];
+};
+
 // Constant tables of the chain kernel, in slot order (the s moduli
 // right-aligned in kChainMaxS slots, descending; unused slots hold 1)
 struct ChainTables {
     float inv[kChainMaxS][kChainMaxS];    // m_i^{-1} mod m_j (i != j), in [0, m_j)
-    float omega[kChainMaxS][kChainMaxS];  // [prod_{l<i} m_l]_{m_j}, centred
+    union {
+        float omega[kChainMaxS][kChainMaxS];  // [prod_{l<i} m_l]_{m_j}, centred
+        ChainCrtTable crt;  // in the LDS kernel's tables of a plan whose rescalings all take the CRT form
+    };
     float mod[kChainMaxS];                // m_u
     float rmod[kChainMaxS];               // fl32(1 / m_u)
     float ohalf[kChainMaxS];              // fl32(1/2 - 128 rmod[u]): reduction of an accumulator offset by 128
@@ -179,20 +201,6 @@ struct ChainDropTable {
     float nw[kChainMaxS - 1][kChainMaxS];   // -[prod_{l<j} q_l Q^{-1}]_{m_p}
 };
 void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D);
-// Per non-final product with g >= 1 drops: the base extension of X_g from
-// its kept slots 0 .. 15 - g (M the product of their moduli) to the dropped
-// slots by the Chinese remainder theorem instead of mixed-radix digits.
-// With xi_i = [r_i cinv[i]]_{m_i}, sum_i xi_i M / m_i = X_g + alpha M for the
-// integer alpha = round(sum_i xi_i / m_i), so that
-// [X_g]_p = [sum_i xi_i cw[p][i] - alpha cM[p]]_{m_p}.  Centred values; zero
-// for slots of modulus 1, cinv for the dropped slots, cw and cM for the kept
-// ones.  Used only where the plan bounds |X_g| by (1/2 - 2^-13) M
-// (ChainParams::crt), which keeps the rounding of alpha away from a tie.
-struct ChainCrtTable {
-    float cinv[kChainMaxS];            // [(M / m_i)^{-1}]_{m_i}, kept i
-    float cM[kChainMaxS];              // [M]_{m_p}, dropped p
-    float cw[kChainMaxS][kChainMaxS];  // cw[p][i] = [M / m_i]_{m_p}, dropped p, kept i
-};
 void chain_crt_table(const ChainTables& T, int g, ChainCrtTable* C);
 // The last product's table for the two-block reconstruction: slots 0 ..
 // split - 1 play the dropped moduli (in that order, M1 their product) for

@@ -320,20 +320,24 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
                          int64_t batch);
 
 /* Which kernels oz2_chain_rescale_be uses on this handle: AUTO (the
- * default: LDS for 8 < n <= 16, else HBM), LDS (n <= 16), or HBM (any n).
- * After a product's drops the HBM kernels extend the kept residues to the
- * dropped moduli by the Chinese remainder theorem where the plan's bound
- * leaves the kept moduli's product M a margin (|X| <= (1/2 - 2^-13) M), else
- * by mixed-radix digits (Algorithm 4); both give the same residues.
- * HBM_MIXED_RADIX takes the mixed-radix form everywhere (a test hook).
- * Argument numbers: h 1, kernel 2. */
+ * default: LDS for 8 < n <= 16, else HBM), LDS (n <= 16), or HBM (any n).  Argument
+ * numbers: h 1, kernel 2. */
 enum {
     OZ2_CHAIN_KERNEL_AUTO = 0,
     OZ2_CHAIN_KERNEL_LDS = 1,
-    OZ2_CHAIN_KERNEL_HBM = 2,
-    OZ2_CHAIN_KERNEL_HBM_MIXED_RADIX = 3
+    OZ2_CHAIN_KERNEL_HBM = 2
 };
 int oz2_set_chain_kernel(oz2_handle_t h, int kernel);
+
+/* After a product's drops the chain kernels extend the kept residues to the
+ * dropped moduli by the Chinese remainder theorem where the plan's bound
+ * leaves the kept moduli's product M a margin (|X| <= (1/2 - 2^-13) M; in
+ * the LDS kernel only when every rescaling drops the same count), else by
+ * mixed-radix digits (Algorithm 4, Eq. 26); both give the same residues.
+ * enable = 0 takes the mixed-radix form everywhere on this handle (a test
+ * hook), 1 (the default) the CRT form where allowed.  Argument numbers:
+ * h 1, enable 2. */
+int oz2_set_chain_crt(oz2_handle_t h, int enable);
 
 /* Free a plan and its device memory. */
 int oz2_chain_plan_destroy(oz2_chain_plan_t plan);

@@ -62,9 +62,10 @@ def _check_bitwise(got, want, label):
                            f"got {got[bad[:4]]} want {want[bad[:4]]}")
 
 
-def _run(handle, ops, n, s, X, batch, modes=None, kernel="auto"):
+def _run(handle, ops, n, s, X, batch, modes=None, kernel="auto", crt=True):
     import torch
     handle.set_chain_kernel(kernel)
+    handle.set_chain_crt(crt)
     try:
         with handle.chain_plan(ops, n, s, modes) as cp:
             dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
@@ -73,6 +74,7 @@ def _run(handle, ops, n, s, X, batch, modes=None, kernel="auto"):
             info = (cp.depth, cp.b, list(cp.g))
     finally:
         handle.set_chain_kernel("auto")
+        handle.set_chain_crt(True)
     return from_dev(dY), info
 
 
@@ -106,12 +108,12 @@ def test_chain_hbm_matches_oracle_bitwise(handle, n, s, modes, batch):
     X = workloads.tensor_batch(n, batch, 9100 + n + s)
     want, plan = rb.rescale_be_chain(X, ops, n, s, batch, None if modes is None else [m - 1 for m in modes])
     assert plan is not None
-    # auto: the CRT base extension where the plan's bound allows it;
-    # hbm_mixed_radix: the mixed-radix one after every product
-    for kernel in ("auto", "hbm_mixed_radix"):
-        got, info = _run(handle, ops, n, s, X, batch, modes, kernel)
+    # the CRT base extension where the plan's bound allows it, and the
+    # mixed-radix one after every product
+    for crt in (True, False):
+        got, info = _run(handle, ops, n, s, X, batch, modes, crt=crt)
         assert info == (d, plan["b"], plan["g"]), (info, plan["b"], plan["g"])
-        _check_bitwise(got, want, f"n={n} s={s} modes={modes} {kernel}")
+        _check_bitwise(got, want, f"n={n} s={s} modes={modes} crt={crt}")
 
 
 SMALL_CASES = [
@@ -240,7 +242,7 @@ def test_chain_hbm_golden_samples(handle, case):
     X = workloads.tensor_batch(n, batch, c["x_seed"])
     idx = np.array(c["index"], dtype=np.int64)
     want = np.array([float.fromhex(v) for v in c["value"]])
-    for kernel in ("auto", "hbm_mixed_radix"):
-        got, info = _run(handle, ops, n, s, X, batch, modes, kernel)
+    for crt in (True, False):
+        got, info = _run(handle, ops, n, s, X, batch, modes, crt=crt)
         assert info == (d, c["b"], c["g"]), info
-        _check_bitwise(got[idx], want, f"golden n={n} modes={modes} {kernel}")
+        _check_bitwise(got[idx], want, f"golden n={n} modes={modes} crt={crt}")

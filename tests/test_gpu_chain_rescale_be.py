@@ -9,7 +9,9 @@ tests/test_gpu_chain_hbm.py).
 Bar: the plan (b, g) equals the oracle planner's, and every output entry is
 bit-identical to the oracle's: every step is exact integer arithmetic except
 the FP64 Horner evaluation and the final scaling, which both sides perform in
-the same order with the same roundings.
+the same order with the same roundings.  The parity cases run the base
+extension in both forms (the CRT one where the plan allows it, and the
+mixed-radix one of the page's Algorithm 4).
 """
 import sys
 
@@ -54,6 +56,23 @@ def _check_bitwise(got, want, label):
                            f"got {got[bad[:4]]} want {want[bad[:4]]}")
 
 
+def _run_forms(handle, cp, X, n, batch):
+    """the chain with the base extension in the CRT form (where the plan
+    allows it) and in the mixed-radix form after every product"""
+    import torch
+    out = []
+    for crt in (True, False):
+        handle.set_chain_crt(crt)
+        try:
+            dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
+            handle.chain_rescale_be(cp, to_dev(X), dY, batch)
+            torch.cuda.synchronize()
+        finally:
+            handle.set_chain_crt(True)
+        out.append(("crt" if crt else "mixed radix", from_dev(dY)))
+    return out
+
+
 CASES = [
     # n, s, batch, tensor distribution
     (16, 16, 3, "uniform"),
@@ -78,10 +97,8 @@ def test_chain_matches_oracle_bitwise(handle, n, s, batch, dist):
     assert plan is not None
     with handle.chain_plan(ops, n, s) as cp:
         assert (cp.depth, cp.b, list(cp.g)) == (3, plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
-        dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
-        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
-        torch.cuda.synchronize()
-    _check_bitwise(from_dev(dY), want, f"n={n} s={s}")
+        for form, got in _run_forms(handle, cp, X, n, batch):
+            _check_bitwise(got, want, f"n={n} s={s} {form}")
 
 
 def test_chain_edge_tensors(handle):
@@ -155,10 +172,8 @@ def test_chain_depth_matches_oracle_bitwise(handle, n, s, d, batch):
     assert plan is not None
     with handle.chain_plan(ops, n, s) as cp:
         assert (cp.depth, cp.b, list(cp.g)) == (d, plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
-        dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
-        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
-        torch.cuda.synchronize()
-    _check_bitwise(from_dev(dY), want, f"n={n} s={s} d={d}")
+        for form, got in _run_forms(handle, cp, X, n, batch):
+            _check_bitwise(got, want, f"n={n} s={s} d={d} {form}")
 
 
 MODE_CASES = [
@@ -186,10 +201,8 @@ def test_chain_mode_sequences_match_oracle_bitwise(handle, n, s, modes, batch):
     assert plan is not None
     with handle.chain_plan(ops, n, s, modes) as cp:
         assert (cp.depth, cp.b, list(cp.g)) == (d, plan["b"], plan["g"]), (cp.b, cp.g, plan["b"], plan["g"])
-        dY = torch.full((n ** 3 * batch,), 7.0, dtype=torch.float64, device="cuda")
-        handle.chain_rescale_be(cp, to_dev(X), dY, batch)
-        torch.cuda.synchronize()
-    _check_bitwise(from_dev(dY), want, f"modes={modes}")
+        for form, got in _run_forms(handle, cp, X, n, batch):
+            _check_bitwise(got, want, f"modes={modes} {form}")
 
 
 def test_chain_argument_errors(handle):
