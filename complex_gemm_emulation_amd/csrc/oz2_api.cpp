@@ -91,8 +91,7 @@ struct oz2_chain_plan {
     int ncp = 0;               // pairs of 32-byte MFMA k chunks covering np
     const int* fexp = nullptr;     // device [3][np] row exponents left pending on each direction
     const ChainDropTable* drop = nullptr;  // device [d] drop weights of each product (HBM kernels)
-    const ChainCrtTable* crt = nullptr;    // device [d] CRT base-extension tables (HBM kernels; used where params.crt)
-    const float* tab_hbm = nullptr;        // device ChainTables of the HBM kernels (params.tab: the LDS kernel's)
+    const ChainCrtTable* crt = nullptr;    // device [d] CRT base-extension tables (used where params.crt)
     const int8_t* hops = nullptr;  // device [d][s][ap / 16][ncp][64][16] operator residues of the HBM kernels
 };
 
@@ -992,10 +991,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
     const size_t off_drop = align_up(off_hops + hops_bytes);
     const size_t off_crt = align_up(off_drop + sizeof(ChainDropTable) * depth);
-    // the LDS kernel's own copy of the tables, with the CRT table in place of
-    // the mixed-radix weights when every rescaling can take the CRT form
-    const size_t off_tlds = align_up(off_crt + sizeof(ChainCrtTable) * depth);
-    const size_t total = off_tlds + sizeof(ChainTables);
+    const size_t total = off_crt + sizeof(ChainCrtTable) * depth;
     std::vector<char> host;
     std::vector<int8_t> res;
     std::vector<int> fexp;
@@ -1044,15 +1040,6 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         chain_split_table(tabs, kChainSplit, dt + depth - 1);  // the last product's reconstruction
         ChainCrtTable* ct = (ChainCrtTable*)(host.data() + off_crt);
         for (int i = 0; i < depth; ++i) chain_crt_table(tabs, i + 1 < depth ? plan->params.g[i] : 0, ct + i);
-        // the LDS kernel holds one table in the mixed-radix weights' place:
-        // the CRT form when every rescaling drops the same count, with margin
-        bool lds_crt = depth >= 2;
-        for (int i = 0; i + 1 < depth; ++i)
-            lds_crt = lds_crt && plan->params.crt[i] && plan->params.g[i] == plan->params.g[0];
-        ChainTables* tl = (ChainTables*)(host.data() + off_tlds);
-        *tl = tabs;
-        if (lds_crt) tl->crt = ct[0];
-        plan->params.lds_crt = lds_crt;
     }
     if (!st && hipMalloc(&plan->mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -1065,13 +1052,13 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         delete plan;
         return st;
     }
-    plan->tab_hbm = (const float*)plan->mem;
-    plan->params.tab = (const float*)((char*)plan->mem + off_tlds);
+    plan->params.tab = (const float*)plan->mem;
     plan->params.ops = lds ? (const int8_t*)((char*)plan->mem + off_lds) : nullptr;
     plan->fexp = (const int*)((char*)plan->mem + off_fexp);
     plan->hops = (const int8_t*)((char*)plan->mem + off_hops);
     plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
     plan->crt = (const ChainCrtTable*)((char*)plan->mem + off_crt);
+    plan->params.crts = plan->crt;
     plan->params.split = plan->drop + depth - 1;
     {
         // the encode's residue constants of the chain's moduli (index q = slot - first);
@@ -1144,7 +1131,7 @@ int chain_hbm(oz2_context* h, const oz2_chain_plan* plan, const double* X, doubl
         P.m0 = C.m0;
         for (int j = 0; j < 3; ++j) P.fin[j] = C.fin[j];
         P.Qd = C.Qd;
-        P.tab = plan->tab_hbm;
+        P.tab = C.tab;
         P.fexp = plan->fexp;
         P.smax = (unsigned long long*)ws;
         P.pstride = nb * np3;
@@ -1202,11 +1189,7 @@ int oz2_chain_rescale_be(oz2_handle_t h, oz2_chain_plan_t plan, const double* X,
     P.X = X;
     P.Y = Y;
     P.batch = batch;
-    if (!h->chain_crt) {
-        // the tables with the mixed-radix weights
-        P.tab = plan->tab_hbm;
-        P.lds_crt = 0;
-    }
+    if (!h->chain_crt) P.crts = nullptr;  // the mixed-radix form everywhere
     hipStream_t stm = h->stream;
     if (h->timing)
         for (int e = 0; e < 3; ++e) OZ2_LAUNCH(hipEventRecord(h->ev[e], stm));

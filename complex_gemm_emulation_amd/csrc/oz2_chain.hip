@@ -110,8 +110,8 @@ __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint3
 // (G0 = G1: after every product but the last), -1 to read them from P.g;
 // D: the depth when fixed at compile time with the modes 1, 2, 3 (every
 // residue store contiguous), 0 to read the depth, modes and layouts from P;
-// CRT: every rescaling drops the same count and extends in the CRT form
-// (P.lds_crt: the table P.tab->crt in place of the mixed-radix weights)
+// CRT: every rescaling extends in the CRT form, each product's table
+// (P.crts) copied into the mixed-radix weights' place in LDS before it
 template <int G0, int G1, int D, bool CRT>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(4, 4)))
 void chain_kernel(ChainParams P) {
@@ -131,9 +131,16 @@ void chain_kernel(ChainParams P) {
     double* Y = P.Y + (int64_t)blockIdx.x * n3;
     // constant tables and operator residues (slot order) staged in LDS and
     // read per use (hoisted into registers they would not fit)
+    // With CRT and one drop count for every rescaling (G0 = G1), the CRT
+    // table is the same for every product and takes the mixed-radix weights'
+    // place here, once; otherwise each product copies its own (below).
+    constexpr bool kCrtOnce = CRT && G0 >= 0 && G0 == G1;
     static_assert(sizeof(ChainTables) % 4 == 0, "words");
+    constexpr int kCrtWord = (int)(offsetof(ChainTables, crt) / 4), kCrtWords = (int)(sizeof(ChainCrtTable) / 4);
     for (int x = tid; x < (int)(sizeof(ChainTables) / 4); x += 512)
-        ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
+        ((uint32_t*)&KT)[x] = kCrtOnce && x >= kCrtWord && x < kCrtWord + kCrtWords
+                                  ? ((const uint32_t*)P.crts)[x - kCrtWord]
+                                  : ((const uint32_t*)P.tab)[x];
     static_assert(sizeof(ChainDropTable) % 4 == 0, "words");
     for (int x = tid; x < (int)(sizeof(ChainDropTable) / 4); x += 512)
         ((uint32_t*)&KS)[x] = ((const uint32_t*)P.split)[x];
@@ -219,6 +226,13 @@ void chain_kernel(ChainParams P) {
 #pragma unroll 1
     for (int mode = 0; mode + 1 < d; ++mode) {
         asm volatile("" ::: "memory");  // keep the table reads inside the loop
+        if (CRT && !kCrtOnce) {
+            // this product's CRT table: read only after the barrier below,
+            // written after the previous product's last read of it (the
+            // barrier that closed that product)
+            static_assert(kCrtWords <= 512, "one word per thread");
+            if (tid < kCrtWords) ((uint32_t*)&KT.crt)[tid] = ((const uint32_t*)(P.crts + mode))[tid];
+        }
         uint32_t pk0[kSlots], pk1[kSlots];
         tile_products(buf, ops[mode % 3], T, wave, a, kq, pk0);
         tile_products(buf, ops[mode % 3], T, wave + 8, a, kq, pk1);
@@ -298,10 +312,9 @@ hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
     bool same = P.d >= 2;
     for (int i = 1; i + 1 < P.d; ++i) same = same && P.g[i] == P.g[0];
     const int g0 = same ? P.g[0] : -1;
-    // the CRT form needs the common drop count's table in place of the
-    // mixed-radix weights
-    bool crt = P.lds_crt != 0 && same;
-    for (int i = 0; i + 1 < P.d; ++i) crt = crt && P.crt[i];
+    // the CRT form where every product with drops has the plan's margin
+    bool crt = P.crts != nullptr;
+    for (int i = 0; i + 1 < P.d; ++i) crt = crt && (P.g[i] == 0 || P.crt[i]);
     const dim3 grid((unsigned)P.batch), block(512);
     if (P.d == 3 && P.cyclic) {
         if (g0 == 7 && crt)
@@ -316,6 +329,8 @@ hipError_t launch_chain(const ChainParams& P, hipStream_t st) {
             hipLaunchKernelGGL((chain_kernel<4, 4, 3, true>), grid, block, 0, st, P);
         else if (g0 == 4)
             hipLaunchKernelGGL((chain_kernel<4, 4, 3, false>), grid, block, 0, st, P);
+        else if (P.g[0] == 4 && P.g[1] == 5 && crt)
+            hipLaunchKernelGGL((chain_kernel<4, 5, 3, true>), grid, block, 0, st, P);
         else if (P.g[0] == 4 && P.g[1] == 5)
             hipLaunchKernelGGL((chain_kernel<4, 5, 3, false>), grid, block, 0, st, P);
         else if (crt)

@@ -132,6 +132,7 @@ struct ChainEncodeConsts {
     float mod[kChainMaxS], frcp[kChainMaxS], foffb[kChainMaxS];
 };
 struct ChainDropTable;
+struct ChainCrtTable;
 
 struct ChainParams {
     const double* X;             // [batch][n^3] column-major tensors
@@ -141,8 +142,8 @@ struct ChainParams {
     int g[kChainMaxD];           // moduli dropped after product i (g[d - 1] = 0)
     int crt[kChainMaxD];         // 1: 1 <= g[i] <= 14 and after product i's drops |X_g| <= (1/2 - 2^-13) M
                                  // (M: the kept moduli), so that its base extension may take the CRT form
-    int lds_crt;                 // 1: tab->crt holds the CRT table of the common drop count of every
-                                 // rescaling (the LDS kernel's CRT instances)
+    const ChainCrtTable* crts;   // device [d] per-product CRT tables (chain_crt_table), or null: the
+                                 // mixed-radix base extension everywhere
     // residue layout: position 0 of a plane row is the contracted direction.
     // m0: direction at position 0 before the first product (positions hold
     // m0, m0 + 1, m0 + 2 mod 3); kind[i]: how product i's output is stored
@@ -182,7 +183,7 @@ struct ChainTables {
     float inv[kChainMaxS][kChainMaxS];    // m_i^{-1} mod m_j (i != j), in [0, m_j)
     union {
         float omega[kChainMaxS][kChainMaxS];  // [prod_{l<i} m_l]_{m_j}, centred
-        ChainCrtTable crt;  // in the LDS kernel's tables of a plan whose rescalings all take the CRT form
+        ChainCrtTable crt;  // in the LDS kernel's CRT instances: the current product's CRT table
     };
     float mod[kChainMaxS];                // m_u
     float rmod[kChainMaxS];               // fl32(1 / m_u)

@@ -267,8 +267,9 @@ int oz2_gemm_prepared(oz2_handle_t h, oz2_operand_t pa, oz2_operand_t pb, const 
  * power-of-two exponent (b significand bits), stays in residue form through
  * all d mode products -- after every product but the last the g_i smallest
  * moduli are dropped by rounded division (Sec. 2.3.1 Eq. 15, Algorithm 1)
- * and restored by mixed-radix base extension (Sec. 4.4 Eq. 26,
- * Algorithm 4) -- and is reconstructed once (Algorithm 5).  Row scales still
+ * and restored by base extension (Sec. 4.4 Eq. 26, Algorithm 4; the
+ * kernels may take the CRT form of it, oz2_set_chain_crt, with the same
+ * residues) -- and is reconstructed once (Algorithm 5).  Row scales still
  * pending on a direction are folded into the columns of the next operator
  * on it before that operator is encoded (Sec. 5.2, after Eq. 28).  The
  * residue basis is the max-product modulus set for num_moduli, descending.
@@ -332,8 +333,8 @@ int oz2_set_chain_kernel(oz2_handle_t h, int kernel);
 /* After a product's drops the chain kernels extend the kept residues to the
  * dropped moduli by the Chinese remainder theorem where the plan's bound
  * leaves the kept moduli's product M a margin (|X| <= (1/2 - 2^-13) M; in
- * the LDS kernel only when every rescaling drops the same count), else by
- * mixed-radix digits (Algorithm 4, Eq. 26); both give the same residues.
+ * the LDS kernel when every product with drops has it), else by mixed-radix
+ * digits (Algorithm 4, Eq. 26); both give the same residues.
  * enable = 0 takes the mixed-radix form everywhere on this handle (a test
  * hook), 1 (the default) the CRT form where allowed.  Argument numbers:
  * h 1, enable 2. */

@@ -1,4 +1,4 @@
-"""The two shortcuts the chain kernels take, pinned on the CPU against the
+"""The three shortcuts the chain kernels take, pinned on the CPU against the
 oracle's own steps of "You Only Convert Twice: Ozaki Scheme II for Chained
 Tensor Mode Products" (oracle/rescale_be.py), in exact integers:
 
@@ -10,7 +10,13 @@ Tensor Mode Products" (oracle/rescale_be.py), in exact integers:
 - the final digits in two blocks: the mixed-radix digits over all moduli
   (Algorithm 4's MrcDigits, Eq. 24) are those over the first block followed
   by those of (v - A) / M1 over the second block, whose residues come from
-  one such sum each.
+  one such sum each;
+- the base extension by the CRT: the residues of v on the dropped moduli
+  from those on the kept ones (product M) as [sum_i xi_i [M/m_i]_p -
+  alpha [M]_p]_p, xi_i = [r_i (M/m_i)^-1]_{m_i}, alpha the rounding of
+  sum_i xi_i / m_i, equal Algorithm 4's BaseExtend for |v| <= (1/2 - 2^-13) M;
+  alpha is rounded here as the kernels round it (an FP32 fused multiply-add
+  chain, then floor(S + 1/2) in FP32), at both ends of that range.
 
 The kernels compute these sums in FP32 from tables the library builds on the
 host (checked against the same definitions by tests/sanitize); here the
@@ -94,3 +100,37 @@ def test_digits_in_two_blocks_equal_one_elimination(s, split):
     W = rb.mixed_radix_weights(basis)
     for k, v in enumerate(vals[:8]):
         assert sum(int(d[k]) * w for d, w in zip(got, W)) == v
+
+
+def _fma32(a, b, c):
+    """fl32(a b + c) for float32 a, b, c, with one rounding: the product of two
+    24-bit significands and the sum below are exact in float64 at these
+    magnitudes (at most 40 significant bits)"""
+    return np.float32(np.float64(a) * np.float64(b) + np.float64(c))
+
+
+@pytest.mark.parametrize("s", [4, 8, 12, 15, 16])
+def test_crt_base_extension_equals_mixed_radix(s):
+    basis = list(rb.max_product_moduli(s))            # descending: the kernels' slot order
+    for g in range(1, s):
+        dropped = sorted(basis)[:g]
+        kept = [p for p in basis if p not in dropped]
+        M = rb.moduli_product(kept)
+        lim = M // 2 - (M + 8191) // 8192              # (1/2 - 2^-13) M, rounded down
+        vals = [lim, -lim] + [v % (2 * lim + 1) - lim for v in _rand_ints(M, 48, 7200 + 16 * s + g)]
+        R = _residues(vals, kept)
+        want = rb.base_extend(R, kept, dropped)
+        xi = {p: rb.centered_array(R[p] * rb.centered(pow(M // p % p, -1, p), p), p) for p in kept}
+        S = np.zeros(len(vals), dtype=np.float32)
+        for p in kept:
+            S = np.array([_fma32(np.float32(x), np.float32(1.0) / np.float32(p), v) for x, v in zip(xi[p], S)],
+                         dtype=np.float32)
+        alpha = np.floor(S + np.float32(0.5)).astype(np.int64)
+        exact = [(sum(int(xi[p][k]) * (M // p) for p in kept) - v) // M for k, v in enumerate(vals)]
+        assert alpha.tolist() == exact, (s, g)
+        for q in dropped:
+            acc = -alpha * rb.centered(M % q, q)
+            for p in kept:
+                acc = acc + xi[p] * rb.centered(M // p % q, q)
+            assert np.all(np.abs(acc) < 2 ** 18), (s, g, q)
+            assert np.array_equal(rb.centered_array(acc, q), want[q]), (s, g, q)
