@@ -6,7 +6,8 @@
 // "You Only Convert Twice: Ozaki Scheme II for Chained Tensor Mode Products":
 //  - Sec. 5.2 and Algorithm 7: the tensor is encoded once with one exponent,
 //    multiplied mode after mode on its residue planes, rescaled by g_i
-//    moduli (Algorithm 1, Eq. 15) and base-extended (Algorithm 4, Eq. 26)
+//    moduli (Algorithm 1, Eq. 15) and base-extended (Algorithm 4, Eq. 26;
+//    here in the CRT form where the plan allows it, with the same residues)
 //    after each non-final mode, and reconstructed once; the pending row
 //    scales of a direction are folded into the next operator on it on the
 //    host, before encoding;

@@ -14,7 +14,9 @@
 // Besides the page's step order (rescale_extend), the same integers come out
 // of two shortcuts built on the uniqueness of mixed-radix digits: the g
 // drops at once (drop_extend, HBM kernels) and the final digits in two
-// blocks (mrc_horner_split, both kernels).
+// blocks (mrc_horner_split, both kernels); and of a third, the base
+// extension by the Chinese remainder theorem (extend_crt, both kernels,
+// where the plan's bound leaves the margin its FP32 rounding needs).
 //
 // Moduli sit right-aligned in kChainMaxS slots, descending, so the smallest
 // (the ones dropped) are always the last slots; unused leading slots carry

@@ -39,7 +39,9 @@
 // rescales and base-extends them in registers (oz2_chain_device.h): the g
 // drops at once, by the mixed-radix digits over the dropped moduli and one
 // weighted sum per kept residue (drop_extend, bitwise the repeated RnsDrop),
-// and the reconstruction's digits in two blocks (mrc_horner_split).  The
+// the base extension in the CRT form where the plan allows it (extend_crt;
+// the last template argument of the product kernels), and the
+// reconstruction's digits in two blocks (mrc_horner_split).  The
 // output layout puts the next product's direction at p0: with the directions
 // in turn that is the fibres' p1, so the lane's four entries are four
 // consecutive bytes of every output plane.
