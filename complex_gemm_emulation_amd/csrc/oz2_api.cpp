@@ -1060,6 +1060,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->crt = (const ChainCrtTable*)((char*)plan->mem + off_crt);
     plan->params.crts = plan->crt;
     plan->params.split = plan->drop + depth - 1;
+    plan->params.drops = plan->drop;
     {
         // the encode's residue constants of the chain's moduli (index q = slot - first);
         // moduli_plan(s) is non-null here: chain_plan above succeeded with this s

@@ -81,7 +81,7 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
 // the base extension in the CRT form, on the table T->crt)
 template <int G0, int G1, bool ANY, bool CRT>
 __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint32_t (&pk)[kSlots],
-                                             const ChainTables* T, int8_t* at, int step) {
+                                             const ChainTables* T, const ChainDropTable* D, int8_t* at, int step) {
     // offset by 128; the first drop's differences remove the offset from
     // every kept slot, and without drops it is subtracted here
     float r[4][kSlots];
@@ -98,13 +98,15 @@ __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint3
         store4<ANY>(at + u * kPlane, step, r0, r1, r2, r3);
     };
     if (G0 >= 0 && G0 == G1)
-        rescale_extend<G0, CRT>(0, r, T, put);
+        drop_extend<G0, CRT>(0, r, T, D, &T->crt, put);
     else if (G0 >= 0 && mode == 0)
-        rescale_extend<G0, CRT>(0, r, T, put);
+        drop_extend<G0, CRT>(0, r, T, D, &T->crt, put);
     else if (G0 >= 0)
-        rescale_extend<G1, CRT>(0, r, T, put);
+        drop_extend<G1, CRT>(0, r, T, D, &T->crt, put);
+    else if (g[mode] > 0)
+        drop_extend<-1, CRT>(g[mode], r, T, D, &T->crt, put);
     else
-        rescale_extend<-1, CRT>(g[mode], r, T, put);
+        extend_dropped<-1>(0, r, T, put);
 }
 
 // G0, G1: the drop counts after products 1 and 2 when fixed at compile time
@@ -234,6 +236,7 @@ void chain_kernel(ChainParams P) {
             static_assert(kCrtWords <= 512, "one word per thread");
             if (tid < kCrtWords) ((uint32_t*)&KT.crt)[tid] = ((const uint32_t*)(P.crts + mode))[tid];
         }
+        if (tid < (int)(sizeof(ChainDropTable) / 4)) ((uint32_t*)&KS)[tid] = ((const uint32_t*)(P.drops + mode))[tid];
         uint32_t pk0[kSlots], pk1[kSlots];
         tile_products(buf, ops[mode % 3], T, wave, a, kq, pk0);
         tile_products(buf, ops[mode % 3], T, wave + 8, a, kq, pk1);
@@ -248,13 +251,19 @@ void chain_kernel(ChainParams P) {
             return buf + (kind == 0 ? (t + 16 * a) * kChainN + 4 * kq
                                     : kind == 1 ? t + 64 * kq + 256 * a : a + 64 * kq + 256 * t);
         };
-        rescale_tile<G0, G1, D == 0, CRT>(mode, P.g, pk0, T, at(wave), step);
+        rescale_tile<G0, G1, D == 0, CRT>(mode, P.g, pk0, T, &KS, at(wave), step);
         asm volatile("" ::: "memory");  // one tile at a time
-        rescale_tile<G0, G1, D == 0, CRT>(mode, P.g, pk1, T, at(wave + 8), step);
+        rescale_tile<G0, G1, D == 0, CRT>(mode, P.g, pk1, T, &KS, at(wave + 8), step);
         asm volatile("" ::: "memory");
         // operator mode + 3 into the buffer this product read (before the
         // barrier above); it is next read three products later
         if (mode + 3 < d) stage_ops(mode + 3);
+        __syncthreads();
+    }
+    if (d >= 2) {
+        // the two-block reconstruction's weights back in place of the last
+        // rescaling's drop table (read after the barrier closing that product)
+        if (tid < (int)(sizeof(ChainDropTable) / 4)) ((uint32_t*)&KS)[tid] = ((const uint32_t*)P.split)[tid];
         __syncthreads();
     }
 

@@ -157,6 +157,7 @@ struct ChainParams {
     const int8_t* ops;           // device [d][kChainMaxS][16][16] centred residues of the integer operators, by modulus index
     const float* tab;            // device ChainTables (below)
     const ChainDropTable* split; // device: the two-block reconstruction's table (chain_split_table)
+    const ChainDropTable* drops; // device [d]: product i's drop table (chain_drop_table; the last: split)
     ChainEncodeConsts enc;       // the encode's residue constants
 };
 
