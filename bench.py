@@ -807,6 +807,11 @@ def run_nonsquare(args):
     }
 
 
+RBE_OPS_BASIS = ("the page's steps per entry (repeated RnsDrop, mixed-radix BaseExtend, one elimination for the "
+                 "final digits: rbe_valu_ops_per_entry); the kernels reach the same integers with fewer (drops at "
+                 "once, CRT base extension, final digits in two blocks), so this is an effective rate")
+
+
 def rbe_valu_ops_per_entry(s, g):
     """Vector-ALU operations per tensor entry that the modular steps of an
     OzII-RescaleBE chain of depth d = len(g) take, counting one per 32-bit
@@ -880,6 +885,7 @@ def run_chain_rbe(args):
                     achieved=round(achieved, 2), peak=round(PEAK_VALU_TOPS, 2), unit="TOP/s",
                     frac=round(achieved / PEAK_VALU_TOPS, 4), traffic=None,
                     ops_per_launch=ops_per_launch, launch_ms=round(lm, 4),
+                    ops_basis=RBE_OPS_BASIS,
                     hbm_GBs=round(bytes_per_launch / (lm * 1e-3) / 1e9, 1))
     cpu = None
     if not args.no_cpu_baseline:
@@ -1000,7 +1006,7 @@ def run_chain_sizes(args):
                                    f"in HBM), n = {n}",
                             bound="alu", achieved=round(ach, 2), peak=round(PEAK_VALU_TOPS, 2), unit="TOP/s",
                             frac=round(ach / PEAK_VALU_TOPS, 4), traffic=None, launch_ms=round(per_launch, 4),
-                            ops_per_launch=float(ops_launch))
+                            ops_per_launch=float(ops_launch), ops_basis=RBE_OPS_BASIS)
         plan.close()
         del dX, dY
     h.set_chain_kernel("auto")
