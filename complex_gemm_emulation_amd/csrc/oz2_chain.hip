@@ -77,8 +77,9 @@ __device__ __forceinline__ void tile_products(const int8_t* buf, const int8_t (*
     }
 }
 
-// unpack the four entries of every slot of one tile and rescale them (CRT:
-// the base extension in the CRT form, on the table T->crt)
+// unpack the four entries of every slot of one tile and rescale them: the g
+// drops at once with the product's drop table D, then the base extension
+// (CRT: in the CRT form, on the table T->crt)
 template <int G0, int G1, bool ANY, bool CRT>
 __device__ __forceinline__ void rescale_tile(int mode, const int* g, const uint32_t (&pk)[kSlots],
                                              const ChainTables* T, const ChainDropTable* D, int8_t* at, int step) {
@@ -121,7 +122,7 @@ void chain_kernel(ChainParams P) {
     __shared__ __attribute__((aligned(16))) int8_t buf[kSlots * kPlane];
     __shared__ __attribute__((aligned(16))) int8_t ops[3][kSlots][kChainN * kChainN];  // operator i in i mod 3
     __shared__ ChainTables KT;
-    __shared__ ChainDropTable KS;  // the two-block reconstruction's weights
+    __shared__ ChainDropTable KS;  // the current product's drop table; for the last, the reconstruction's
     __shared__ unsigned long long smax;
 
     const int tid = threadIdx.x;
