@@ -11,12 +11,12 @@
 //    mixed-radix digits by successive elimination and the residues on the
 //    dropped moduli from the weights omega_{i,p} = [prod_{l<i} m_l]_p;
 //  - Algorithm 5 (ReconstructFP64): FP64 Horner over the digits.
-// Besides the page's step order (rescale_extend), the same integers come out
-// of two shortcuts built on the uniqueness of mixed-radix digits: the g
-// drops at once (drop_extend, HBM kernels) and the final digits in two
-// blocks (mrc_horner_split, both kernels); and of a third, the base
-// extension by the Chinese remainder theorem (extend_crt, both kernels,
-// where the plan's bound leaves the margin its FP32 rounding needs).
+// The kernels reach the integers of the page's steps by two shortcuts built
+// on the uniqueness of mixed-radix digits, the g drops at once (drop_extend)
+// and the final digits in two blocks (mrc_horner_split), and by a third,
+// the base extension by the Chinese remainder theorem (extend_crt, where the
+// plan's bound leaves the margin its FP32 rounding needs; else the page's
+// mixed-radix form, extend_dropped).
 //
 // Moduli sit right-aligned in kChainMaxS slots, descending, so the smallest
 // (the ones dropped) are always the last slots; unused leading slots carry
@@ -24,7 +24,9 @@
 // unchanged.  A lane works on four entries at once, so one read of a table
 // entry serves four modular steps.  All modular arithmetic is on exact small
 // integers held as floats: [x]_m = x - m floor(x fl32(1/m) + 1/2), exact for
-// odd m while |x| < 2^19 and for m = 256 outright.
+// odd m while |x| < 2^19 and for m = 256 outright (cmod), or with the
+// quotient rounded to nearest by two adds where the modulus cannot be 256
+// with x outside [-128, 127] (cmod_odd).
 #pragma once
 
 #include "oz2_internal.h"
@@ -36,6 +38,21 @@ constexpr int kSlots = kChainMaxS;  // 16
 
 __device__ __forceinline__ float cmod(float x, float m, float rm) {
     return fmaf(-m, floorf(fmaf(x, rm, 0.5f)), x);
+}
+
+// the same reduction where m is odd or 1, or m = 256 with x in [-128, 127]:
+// q = x fl32(1/m) rounded to nearest by adding and subtracting 1.5 2^23
+// (exact while |x fl32(1/m)| < 2^22).  For odd m, x / m is never a
+// half-integer, and for |x| < 2^19 it lies within 2^-5 / m of x fl32(1/m),
+// less than its distance 1 / (2m) to one, so q = floor(x / m + 1/2) as in
+// cmod; for m = 256 and x in [-128, 127], x / 256 is in [-1/2, 1/2) and q = 0
+// in both (the tie at -1/2 goes to the even 0).  Two FP32 adds in place of
+// a floor, which issues at about half their rate.
+constexpr float kRound = 12582912.0f;  // 1.5 2^23: adding and subtracting it rounds |y| < 2^22 to nearest
+
+__device__ __forceinline__ float cmod_odd(float x, float m, float rm) {
+    const float q = fmaf(x, rm, kRound) - kRound;
+    return fmaf(-m, q, x);
 }
 
 // the same reduction of x - 128, offset by 128: [x - 128]_m + 128 in
@@ -112,7 +129,7 @@ __device__ __forceinline__ void extend_dropped(int g_rt, float (&r)[4][kSlots], 
             if (j <= keep) {
                 const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e][j] = cmod((r[e][j] - r[e][i]) * iv, m, rm);
+                for (int e = 0; e < 4; ++e) r[e][j] = cmod_odd((r[e][j] - r[e][i]) * iv, m, rm);
             }
 #pragma unroll
     for (int p = 1; p < kSlots; ++p)
@@ -126,20 +143,19 @@ __device__ __forceinline__ void extend_dropped(int g_rt, float (&r)[4][kSlots], 
                     for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
                 }
             const float m = T->mod[p], rm = T->rmod[p];
-            put(p, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm), cmod(ts[3], m, rm));
+            put(p, cmod_odd(ts[0], m, rm), cmod_odd(ts[1], m, rm), cmod_odd(ts[2], m, rm), cmod_odd(ts[3], m, rm));
         }
 }
 
 // extend_dropped's residues by the Chinese remainder theorem (the table C,
 // see ChainCrtTable; 1 <= g <= 14): the kept slots are stored, then turned
 // in place into xi_i = [r_i cinv_i]_{m_i}, and every dropped slot p gets
-// [sum_i xi_i [M / m_i]_{m_p} - alpha [M]_{m_p}]_{m_p} with
-// alpha = floor(S + 1/2), S = sum_i xi_i fl32(1/m_i).  Exactly, S = X_g / M + alpha with
-// |X_g| / M <= 1/2 - 2^-13 (the plan's condition for C).  In FP32, S + 1/2
-// is within 2^-16 of its exact value (at most 15 terms of magnitude <= 1/2,
-// each off by <= 2^-25 through fl32(1/m_i), 15 roundings of <= 2^-22 in
-// partial sums below 8, one of 2^-21 in adding 1/2), so the floor gives
-// alpha.  The other sums are of exact integers below 2^18.  Both forms give
+// [sum_i xi_i [M / m_i]_{m_p} - alpha [M]_{m_p}]_{m_p} with alpha the
+// integer nearest S = sum_i xi_i fl32(1/m_i).  Exactly, S = X_g / M + alpha
+// with |X_g| / M <= 1/2 - 2^-13 (the plan's condition for C).  In FP32, S is
+// within 2^-17 of its exact value (at most 15 terms of magnitude <= 1/2, each
+// off by <= 2^-25 through fl32(1/m_i), 15 roundings of <= 2^-22 in partial
+// sums below 8), so rounding it to nearest gives alpha.  The other sums are of exact integers below 2^18.  Both forms give
 // the residues of the same integer X_g, so the results are bitwise equal,
 // with k + 1 products per dropped slot and k reductions in place of
 // extend_dropped's k (k - 1) / 2 digit steps (k kept slots).
@@ -165,7 +181,7 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
         }
     float al[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) al[e] = floorf(S[e] + 0.5f);
+    for (int e = 0; e < 4; ++e) al[e] = (S[e] + kRound) - kRound;
 #pragma unroll
     for (int p = 1; p < kSlots; ++p)
         if (p > keep) {
@@ -181,39 +197,14 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
                     for (int e = 0; e < 4; ++e) ts[e] = fmaf(r[e][i], w, ts[e]);
                 }
             const float m = T->mod[p], rm = T->rmod[p];
-            put(p, cmod(ts[0], m, rm), cmod(ts[1], m, rm), cmod(ts[2], m, rm), cmod(ts[3], m, rm));
+            put(p, cmod_odd(ts[0], m, rm), cmod_odd(ts[1], m, rm), cmod_odd(ts[2], m, rm), cmod_odd(ts[3], m, rm));
         }
 }
 
-// After a non-final product, for the four entries of a lane: RnsDrop g times
-// (Algorithm 1, Eq. 15: slot 15 - j holds the smallest modulus left), each
-// drop updating every remaining slot, then extend_dropped, or with CRT
-// extend_crt on the table T->crt.  Every slot loop is unrolled (G as in
-// extend_dropped).  The residues come in offset by 128: the first drop's
-// differences remove the offset from every kept slot (with no drop the
-// caller removes it).
-template <int G, bool CRT, class Put>
-__device__ __forceinline__ void rescale_extend(int g_rt, float (&r)[4][kSlots], const ChainTables* T, const Put& put) {
-    const int g = G >= 0 ? G : g_rt;
-    const int keep = kSlots - 1 - g;
-#pragma unroll
-    for (int qs = kSlots - 1; qs > 0; --qs)
-        if (qs > keep) {
-#pragma unroll
-            for (int p = 0; p < qs; ++p) {
-                const float iv = T->inv[qs][p], m = T->mod[p], rm = T->rmod[p];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
-            }
-        }
-    if constexpr (CRT)
-        extend_crt<G>(g_rt, r, T, &T->crt, put);
-    else
-        extend_dropped<G>(g_rt, r, T, put);
-}
-
-// The same result with the g drops taken at once (g >= 1; G >= 1 a
-// compile-time drop count, G < 0 the run-time g_rt):
+// After a non-final product, for the four entries of a lane, the page's g
+// successive RnsDrops (Algorithm 1, Eq. 15: slot 15 - j holds the smallest
+// modulus left) taken at once (g >= 1; G >= 1 a compile-time drop count,
+// G < 0 the run-time g_rt):
 // g successive RnsDrops by the moduli q_0, q_1, .. (slots 15, 14, ..) turn
 // the entry X into X_g = (X - D) / Q, Q = prod_j q_j and
 // D = sum_j d_j prod_{l<j} q_l, with d_j the centred mixed-radix digits of X
@@ -248,7 +239,7 @@ __device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], con
                 const int qs = kSlots - 1 - j;
                 const float iv = T->inv[qs][p];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[e][p] = cmod((r[e][p] - r[e][qs]) * iv, m, rm);
+                for (int e = 0; e < 4; ++e) r[e][p] = cmod_odd((r[e][p] - r[e][qs]) * iv, m, rm);
             }
         }
     // the kept slots, in place (a zero weight may meet an updated slot)
@@ -312,7 +303,7 @@ __device__ __forceinline__ void mrc_horner_split(const uint32_t (&pk)[kSlots], c
         for (int j = i + 1; j < kSplit; ++j) {
             const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
+            for (int q = 0; q < 4; ++q) dg[q][j] = cmod_odd((dg[q][j] - dg[q][i]) * iv, m, rm);
         }
 #pragma unroll
     for (int p = kSplit; p < kSlots; ++p) {
@@ -336,7 +327,7 @@ __device__ __forceinline__ void mrc_horner_split(const uint32_t (&pk)[kSlots], c
         for (int j = i + 1; j < kSlots; ++j) {
             const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][j] = cmod((dg[q][j] - dg[q][i]) * iv, m, rm);
+            for (int q = 0; q < 4; ++q) dg[q][j] = cmod_odd((dg[q][j] - dg[q][i]) * iv, m, rm);
         }
 #pragma unroll
     for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
