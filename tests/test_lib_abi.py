@@ -92,3 +92,11 @@ def test_prepared_operand_entry_points_reject_null_handles():
     assert lib.oz2_operand_update(None, None, None, 1) == -1
     assert lib.oz2_operand_destroy(None) == -1
     assert lib.oz2_gemm_prepared(None, None, None, None, None, None, 1) == -1
+
+
+def test_chain_controls_reject_null_handles():
+    # no GPU needed: argument checks run before any HIP call
+    lib = oz2.lib()
+    assert lib.oz2_set_chain_kernel(None, 0) == -1
+    assert lib.oz2_set_chain_crt(None, 1) == -1
+    assert lib.oz2_chain_plan_info(None, None, None, None) == -1
