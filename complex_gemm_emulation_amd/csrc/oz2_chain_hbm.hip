@@ -322,13 +322,30 @@ __device__ __forceinline__ void stage_tables(const ChainHbmParams& P, ChainTable
                                              ChainCrtTable& KC) {
     static_assert(sizeof(ChainTables) % 4 == 0 && sizeof(ChainDropTable) % 4 == 0 &&
                   sizeof(ChainCrtTable) % 4 == 0, "words");
-    for (int x = threadIdx.x; x < (int)(sizeof(ChainTables) / 4); x += blockDim.x)
-        ((uint32_t*)&KT)[x] = ((const uint32_t*)P.tab)[x];
-    for (int x = threadIdx.x; x < (int)(sizeof(ChainDropTable) / 4); x += blockDim.x)
-        ((uint32_t*)&KD)[x] = ((const uint32_t*)P.drop)[x];
-    if (CRT)
-        for (int x = threadIdx.x; x < (int)(sizeof(ChainCrtTable) / 4); x += blockDim.x)
-            ((uint32_t*)&KC)[x] = ((const uint32_t*)P.crt)[x];
+    // the words of the two or three tables in one sequence, a thread's loads
+    // all in flight before its stores (blocks have 256 or 512 threads); a word
+    // past the end loads word 0 instead and stores nothing
+    constexpr int nT = (int)(sizeof(ChainTables) / 4), nD = (int)(sizeof(ChainDropTable) / 4);
+    constexpr int nW = nT + nD + (CRT ? (int)(sizeof(ChainCrtTable) / 4) : 0);
+    constexpr int kPer = (nW + 255) / 256;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int x = threadIdx.x + i * blockDim.x < nW ? threadIdx.x + i * blockDim.x : 0;
+        v[i] = x < nT ? ((const uint32_t*)P.tab)[x]
+                      : x < nT + nD ? ((const uint32_t*)P.drop)[x - nT] : ((const uint32_t*)P.crt)[x - nT - nD];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int x = threadIdx.x + i * blockDim.x;
+        if (x < nT)
+            ((uint32_t*)&KT)[x] = v[i];
+        else if (x < nT + nD)
+            ((uint32_t*)&KD)[x - nT] = v[i];
+        else if (x < nW)
+            ((uint32_t*)&KC)[x - nT - nD] = v[i];
+    }
     __syncthreads();
 }
 
