@@ -81,25 +81,42 @@ __device__ __forceinline__ int tensor_exponent(unsigned long long M, int b) {
 // ---------------------------------------------------------------- scan
 // the largest |x| bit pattern of each tensor (positive doubles order as
 // their bit patterns; non-finite entries give a pattern >= kInfBits)
+// (a block takes R consecutive chunks of one tensor, so that at most 256
+// blocks meet at one tensor's atomic; reduced across each wavefront by
+// shuffles, then across the four wavefronts in LDS, then one atomic per
+// block.  An entry past the tensor's end loads the chunk's first entry
+// instead, so that every load of a chunk is unconditional and in flight
+// together.)
 __global__ __launch_bounds__(256) void chain_scan_kernel(const double* __restrict__ X, int64_t n3, int64_t chunks,
-                                                         unsigned long long* smax) {
-    __shared__ unsigned long long bm;
-    const int64_t t = blockIdx.x / chunks, c = blockIdx.x % chunks;
-    if (threadIdx.x == 0) bm = 0;
-    __syncthreads();
+                                                         int R, unsigned long long* smax) {
+    __shared__ unsigned long long wm[4];
+    const int64_t bpt = (chunks + R - 1) / R;  // blocks per tensor
+    const int64_t t = blockIdx.x / bpt, c0 = (blockIdx.x % bpt) * R;
     const double* x = X + t * n3;
     unsigned long long mx = 0;
+#pragma unroll 1
+    for (int64_t c = c0; c < c0 + R && c < chunks; ++c) {
 #pragma unroll
-    for (int j = 0; j < kScanChunk / 256; ++j) {
-        const int64_t i = c * kScanChunk + j * 256 + threadIdx.x;
-        if (i < n3) {
-            const unsigned long long v = (unsigned long long)__double_as_longlong(x[i]) & 0x7fffffffffffffffull;
+        for (int j = 0; j < kScanChunk / 256; ++j) {
+            const int64_t i = c * kScanChunk + j * 256 + threadIdx.x;
+            const unsigned long long v =
+                (unsigned long long)__double_as_longlong(x[i < n3 ? i : c * kScanChunk]) & 0x7fffffffffffffffull;
             mx = v > mx ? v : mx;
         }
     }
-    atomicMax(&bm, mx);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long v = __shfl_xor(mx, o, 64);
+        mx = v > mx ? v : mx;
+    }
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
     __syncthreads();
-    if (threadIdx.x == 0) atomicMax(&smax[t], bm);
+    if (threadIdx.x == 0) {
+        unsigned long long b = wm[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) b = wm[w] > b ? wm[w] : b;
+        atomicMax(&smax[t], b);
+    }
 }
 
 // the same for tensors of at most kScanChunk entries: one wavefront per
@@ -532,8 +549,10 @@ hipError_t launch_chain_scan(const ChainHbmParams& P, hipStream_t st) {
         hipLaunchKernelGGL(chain_scan_small_kernel, dim3((unsigned)((P.batch + 3) / 4)), dim3(256), 0, st, P.X, n3,
                            P.batch, P.smax);
     } else {
-        hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)(P.batch * chunks)), dim3(256), 0, st, P.X, n3,
-                           chunks, P.smax);
+        const int R = (int)((chunks + 255) / 256);
+        const int64_t bpt = (chunks + R - 1) / R;
+        hipLaunchKernelGGL(chain_scan_kernel, dim3((unsigned)(P.batch * bpt)), dim3(256), 0, st, P.X, n3, chunks, R,
+                           P.smax);
     }
     return hipGetLastError();
 }
