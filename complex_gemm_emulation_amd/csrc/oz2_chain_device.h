@@ -155,10 +155,11 @@ __device__ __forceinline__ void extend_dropped(int g_rt, float (&r)[4][kSlots], 
 // with |X_g| / M <= 1/2 - 2^-13 (the plan's condition for C).  In FP32, S is
 // within 2^-17 of its exact value (at most 15 terms of magnitude <= 1/2, each
 // off by <= 2^-25 through fl32(1/m_i), 15 roundings of <= 2^-22 in partial
-// sums below 8), so rounding it to nearest gives alpha.  The other sums are of exact integers below 2^18.  Both forms give
-// the residues of the same integer X_g, so the results are bitwise equal,
-// with k + 1 products per dropped slot and k reductions in place of
-// extend_dropped's k (k - 1) / 2 digit steps (k kept slots).
+// sums below 8), so rounding it to nearest gives alpha.  The other sums are
+// of exact integers below 2^18.  Both forms give the residues of the same
+// integer X_g, so the results are bitwise equal, with k + 1 products per
+// dropped slot and k reductions in place of extend_dropped's k (k - 1) / 2
+// digit steps (k kept slots).
 template <int G, class Put>
 __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], const ChainTables* T,
                                            const ChainCrtTable* C, const Put& put) {
