@@ -217,7 +217,7 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
 // table D (qinv_p = [Q^-1]_p, nw_{j,p} = -[prod_{l<j} q_l Q^-1]_p, centred,
 // zero for j >= g): one exact integer sum (|sum| < 2^19) and one reduction
 // instead of g modular steps.  The residues and digits are integers, so the
-// result is bitwise that of rescale_extend.  d_0 and the r_p come in offset
+// result is bitwise that of the g repeated drops.  d_0 and the r_p come in offset
 // by 128; nw_{0,p} = -qinv_p cancels it.  The sum runs over j < 8 without
 // guards (zero weights) and over 8 <= j < 15 only when g > 8.  The base
 // extension takes the CRT form with CRT (extend_crt, table C), else the
