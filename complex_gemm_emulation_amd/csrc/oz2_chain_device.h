@@ -217,9 +217,10 @@ __device__ __forceinline__ void extend_crt(int g_rt, float (&r)[4][kSlots], cons
 // table D (qinv_p = [Q^-1]_p, nw_{j,p} = -[prod_{l<j} q_l Q^-1]_p, centred,
 // zero for j >= g): one exact integer sum (|sum| < 2^19) and one reduction
 // instead of g modular steps.  The residues and digits are integers, so the
-// result is bitwise that of the g repeated drops.  d_0 and the r_p come in offset
-// by 128; nw_{0,p} = -qinv_p cancels it.  The sum runs over j < 8 without
-// guards (zero weights) and over 8 <= j < 15 only when g > 8.  The base
+// result is bitwise that of the g repeated drops.  d_0 and the r_p come in
+// offset by 128; nw_{0,p} = -qinv_p cancels it.  With a run-time g the sum
+// runs over j < 8 without guards (zero weights) and over 8 <= j < 15 only
+// when g > 8; a compile-time G takes its terms alone.  The base
 // extension takes the CRT form with CRT (extend_crt, table C), else the
 // mixed-radix form (extend_dropped); a compile-time choice, since the
 // register allocation of a kernel holding both spills hundreds of bytes.
@@ -251,8 +252,10 @@ __device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], con
             float acc[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = r[e][p] * qi;
+            // a compile-time G takes exactly its G terms (up to 8 here)
+            constexpr int J8 = G >= 0 && G < 8 ? G : 8;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < J8; ++j) {
                 const float w = D->nw[j][p];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[e] = fmaf(r[e][kSlots - 1 - j], w, acc[e]);
