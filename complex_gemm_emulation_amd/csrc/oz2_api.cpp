@@ -991,7 +991,8 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     const size_t off_hops = align_up(off_fexp + sizeof(int) * 3 * np);
     const size_t off_drop = align_up(off_hops + hops_bytes);
     const size_t off_crt = align_up(off_drop + sizeof(ChainDropTable) * depth);
-    const size_t total = off_crt + sizeof(ChainCrtTable) * depth;
+    const size_t off_split = align_up(off_crt + sizeof(ChainCrtTable) * depth);  // the LDS kernel's reconstruction
+    const size_t total = off_split + sizeof(ChainDropTable);
     std::vector<char> host;
     std::vector<int8_t> res;
     std::vector<int> fexp;
@@ -1037,7 +1038,10 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
         ChainDropTable* dt = (ChainDropTable*)(host.data() + off_drop);
         const ChainTables& tabs = *(const ChainTables*)host.data();
         for (int i = 0; i + 1 < depth; ++i) chain_drop_table(tabs, plan->params.g[i], dt + i);
-        chain_split_table(tabs, kChainSplit, dt + depth - 1);  // the last product's reconstruction
+        // the last product's reconstruction: on the HBM kernels in blocks of
+        // 4 slots when staged, 8 when direct; on the LDS kernel in blocks of 4
+        chain_split_table(tabs, np >= kChainStagedNp ? kChainSplit : kChainSplitWide, dt + depth - 1);
+        chain_split_table(tabs, kChainSplit, (ChainDropTable*)(host.data() + off_split));
         ChainCrtTable* ct = (ChainCrtTable*)(host.data() + off_crt);
         for (int i = 0; i < depth; ++i) chain_crt_table(tabs, i + 1 < depth ? plan->params.g[i] : 0, ct + i);
     }
@@ -1059,7 +1063,7 @@ int oz2_chain_plan_create(oz2_handle_t h, int64_t n, int depth, const double* co
     plan->drop = (const ChainDropTable*)((char*)plan->mem + off_drop);
     plan->crt = (const ChainCrtTable*)((char*)plan->mem + off_crt);
     plan->params.crts = plan->crt;
-    plan->params.split = plan->drop + depth - 1;
+    plan->params.split = (const ChainDropTable*)((char*)plan->mem + off_split);
     plan->params.drops = plan->drop;
     {
         // the encode's residue constants of the chain's moduli (index q = slot - first);

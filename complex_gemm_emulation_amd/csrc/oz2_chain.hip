@@ -288,7 +288,7 @@ void chain_kernel(ChainParams P) {
         uint32_t pk[kSlots];
         tile_products(buf, ops[(d - 1) % 3], T, t, a, kq, pk);
         double V[4];
-        mrc_horner_split(pk, T, &KS, V);
+        mrc_horner_split<kChainSplit>(pk, T, &KS, V);
         // the values are complete here (the compiler would otherwise sink
         // each entry's whole digit computation into its guarded store)
 #pragma unroll

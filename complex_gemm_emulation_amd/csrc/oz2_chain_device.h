@@ -295,44 +295,47 @@ __device__ __forceinline__ void drop_extend(int g_rt, float (&r)[4][kSlots], con
 // single elimination, in 28 + 8 reductions + 28 steps instead of 120.  d_0
 // and the r_p come in offset by 128: nw_{0,p} = -qinv_p cancels the offset
 // in the sums (|sum| < 2^19), and d_0 loses it after the steps.
-constexpr int kSplit = kChainSplit;
-
+template <int kSplit>
 __device__ __forceinline__ void mrc_horner_split(const uint32_t (&pk)[kSlots], const ChainTables* T,
                                                  const ChainDropTable* D, double (&V)[4]) {
+    static_assert(kSlots % kSplit == 0 && (kSlots / kSplit - 1) * (kSplit + 1) <= kSlots, "table rows");
     float dg[4][kSlots];
     unpack_tile(pk, dg);
+    // row r of the table: qinv for r = 0, nw[r - 1] after
+    const auto row = [D](int r) -> const float* { return r == 0 ? D->qinv : D->nw[r - 1]; };
 #pragma unroll
-    for (int i = 0; i < kSplit - 1; ++i)
+    for (int b = 0; b < kSlots / kSplit; ++b) {
+        const int lo = b * kSplit, hi = lo + kSplit;
+        // the block's digits, by elimination among its slots
 #pragma unroll
-        for (int j = i + 1; j < kSplit; ++j) {
-            const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+        for (int i = lo; i < hi - 1; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][j] = cmod_odd((dg[q][j] - dg[q][i]) * iv, m, rm);
+            for (int j = i + 1; j < hi; ++j) {
+                const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dg[q][j] = cmod_odd((dg[q][j] - dg[q][i]) * iv, m, rm);
+            }
+        if (hi < kSlots) {
+            // the later slots: the residues of (X_b - A_b) / M_b
+            const float* qr = row(b * (kSplit + 1));
+#pragma unroll
+            for (int p = hi; p < kSlots; ++p) {
+                const float qi = qr[p];
+                float acc[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = dg[q][p] * qi;
+#pragma unroll
+                for (int i = 0; i < kSplit; ++i) {
+                    const float w = row(b * (kSplit + 1) + 1 + i)[p];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[q] = fmaf(dg[q][lo + i], w, acc[q]);
+                }
+                const float m = T->mod[p], rm = T->rmod[p];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) dg[q][p] = cmod(acc[q], m, rm);
+            }
         }
-#pragma unroll
-    for (int p = kSplit; p < kSlots; ++p) {
-        const float qi = D->qinv[p];
-        float acc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = dg[q][p] * qi;
-#pragma unroll
-        for (int i = 0; i < kSplit; ++i) {
-            const float w = D->nw[i][p];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] = fmaf(dg[q][i], w, acc[q]);
-        }
-        const float m = T->mod[p], rm = T->rmod[p];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dg[q][p] = cmod(acc[q], m, rm);
     }
-#pragma unroll
-    for (int i = kSplit; i < kSlots - 1; ++i)
-#pragma unroll
-        for (int j = i + 1; j < kSlots; ++j) {
-            const float iv = T->inv[i][j], m = T->mod[j], rm = T->rmod[j];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) dg[q][j] = cmod_odd((dg[q][j] - dg[q][i]) * iv, m, rm);
-        }
 #pragma unroll
     for (int q = 0; q < 4; ++q) dg[q][0] -= 128.0f;
 #pragma unroll

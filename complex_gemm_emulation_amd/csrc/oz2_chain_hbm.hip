@@ -64,7 +64,7 @@ typedef long v2l __attribute__((ext_vector_type(2)));
 
 constexpr int kScanChunk = 4096;      // entries of one tensor per scan block
 constexpr int kStepBlocksMax = 2048;  // blocks of the product kernels (8 per CU), each looping over tiles
-constexpr int kStagedNp = 96;         // padded sides from which the fibre tiles are staged in LDS
+constexpr int kStagedNp = kChainStagedNp;  // padded sides from which the fibre tiles are staged in LDS
 constexpr size_t kStepLdsMax = 65536; // staged fibre tiles of one block: 16 moduli x 16 rows x 256 bytes
 
 constexpr unsigned long long kInfBits = 0x7ff0000000000000ull;
@@ -231,7 +231,7 @@ struct StepConsts {
 // against operator row c mod 8, and every lane's entries are used: the lane
 // of column c holds fibres f0 + 16 (c / 8) + 4 kq + q (the caller's fa).
 // Only the pair's first MFMA carries data.
-template <bool CONTIG, bool LAST, int NCP, bool HALF, bool CRT, class XLoad>
+template <bool CONTIG, bool LAST, int NCP, bool HALF, bool CRT, int SPLIT, class XLoad>
 __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepConsts& K, const ChainTables* T,
                                           const ChainDropTable* DT, const ChainCrtTable* CT, int64_t t, int fa,
                                           int p1, int p2, int a0, int lane, const XLoad& xload,
@@ -283,7 +283,7 @@ __device__ __forceinline__ void step_tile(const ChainHbmParams& P, const StepCon
     }
     if (LAST) {
         double V[4];
-        mrc_horner_split(pk, T, DT, V);
+        mrc_horner_split<SPLIT>(pk, T, DT, V);
         if (p2 < K.n && a < K.n) {
             const int f12 = K.F1[p2] + K.F2[a];
             double* y = P.Y + t * K.n3 + p2 * K.st1 + a * K.st2;
@@ -425,7 +425,8 @@ void chain_step_kernel(ChainHbmParams P) {
                 const long hi = *(const long*)(x + (k + 8 < np ? k + 8 : 0));
                 return v2l{k < np ? lo : 0l, k + 8 < np ? hi : 0l};
             };
-            step_tile<CONTIG, LAST, NCP, HALF, CRT>(P, K, &KT, &KD, &KC, t, fa, p1, p2, a0, lane, xload, M, alpha);
+            step_tile<CONTIG, LAST, NCP, HALF, CRT, kChainSplitWide>(P, K, &KT, &KD, &KC, t, fa, p1, p2, a0, lane,
+                                                                     xload, M, alpha);
         }
     }
 }
@@ -501,8 +502,8 @@ void chain_step_staged_kernel(ChainHbmParams P, int F) {
             const int fa = fb0 + 16 * f + 4 * (lane >> 4);
             const unsigned long long M = LAST ? P.smax[t] : 0ull;
             const double alpha = LAST ? ldexp(P.Qd, -tensor_exponent(M < kInfBits ? M : 0ull, P.b)) : 0.0;
-            step_tile<CONTIG, LAST, NCP, false, CRT>(P, K, &KT, &KD, &KC, t, fa, fa % K.np, fa / K.np,
-                                                     (pr % na) * 16, lane, xload, M, alpha);
+            step_tile<CONTIG, LAST, NCP, false, CRT, kChainSplit>(P, K, &KT, &KD, &KC, t, fa, fa % K.np, fa / K.np,
+                                                                  (pr % na) * 16, lane, xload, M, alpha);
         }
     }
 }

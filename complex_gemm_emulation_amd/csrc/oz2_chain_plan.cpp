@@ -288,20 +288,25 @@ void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D) {
 
 void chain_split_table(const ChainTables& T, int split, ChainDropTable* D) {
     std::memset(D, 0, sizeof(*D));
-    if (split < 1 || split > kChainMaxS - 1) return;
+    if (split < 1 || kChainMaxS % split != 0 || (kChainMaxS / split - 1) * (split + 1) > kChainMaxS) return;
     int slot[kChainMaxS];
     for (int u = 0; u < kChainMaxS; ++u) slot[u] = (int)T.mod[u];
-    for (int p = split; p < kChainMaxS; ++p) {
-        const int m = slot[p];
-        if (m == 1) continue;
-        int64_t M1 = 1;
-        for (int l = 0; l < split; ++l) M1 = M1 * slot[l] % m;
-        const int64_t qi = inverse_mod(M1, m);
-        D->qinv[p] = (float)centered(qi, m);
-        int64_t w = 1;  // prod_{l<i} m_l reduced mod m
-        for (int i = 0; i < split; ++i) {
-            D->nw[i][p] = (float)-centered(w * qi % m, m);
-            w = w * slot[i] % m;
+    // row r of the table: qinv for r = 0, nw[r - 1] after
+    auto row = [D](int r) -> float* { return r == 0 ? D->qinv : D->nw[r - 1]; };
+    for (int b = 0; b + 1 < kChainMaxS / split; ++b) {
+        const int lo = b * split, hi = lo + split;
+        for (int p = hi; p < kChainMaxS; ++p) {
+            const int m = slot[p];
+            if (m == 1) continue;
+            int64_t Mb = 1;  // the block's modulus product reduced mod m
+            for (int l = lo; l < hi; ++l) Mb = Mb * slot[l] % m;
+            const int64_t qi = inverse_mod(Mb, m);
+            row(b * (split + 1))[p] = (float)centered(qi, m);
+            int64_t w = 1;  // prod_{lo <= l < lo + i} m_l reduced mod m
+            for (int i = 0; i < split; ++i) {
+                row(b * (split + 1) + 1 + i)[p] = (float)-centered(w * qi % m, m);
+                w = w * slot[lo + i] % m;
+            }
         }
     }
 }

@@ -204,12 +204,18 @@ struct ChainDropTable {
 };
 void chain_drop_table(const ChainTables& T, int g, ChainDropTable* D);
 void chain_crt_table(const ChainTables& T, int g, ChainCrtTable* C);
-// The last product's table for the two-block reconstruction: slots 0 ..
-// split - 1 play the dropped moduli (in that order, M1 their product) for
-// the slots split .. 15: qinv[p] = [M1^{-1}]_{m_p},
-// nw[i][p] = -[prod_{l<i} m_l M1^{-1}]_{m_p}, centred, zero elsewhere.
+// The last product's table for the reconstruction's digits in blocks of
+// `split` slots (16 / split blocks): after block b (slots lo .. lo + split
+// - 1, M_b their moduli's product) the later slots p get the residues of
+// (X_b - A_b) / M_b, with the weights in rows b (split + 1) .. b (split + 1)
+// + split of the table (row 0 is qinv, row r > 0 is nw[r - 1]): first
+// [M_b^{-1}]_{m_p}, then -[prod_{lo <= l < lo + i} m_l M_b^{-1}]_{m_p} for
+// i = 0 .. split - 1; centred, zero elsewhere and for slots of modulus 1.
+// Needs (16 / split - 1)(split + 1) <= 16 rows: split = 4 or 8.
 void chain_split_table(const ChainTables& T, int split, ChainDropTable* D);
-constexpr int kChainSplit = 8;  // slots in the first block of the HBM kernels' reconstruction
+constexpr int kChainSplit = 4;      // slots per block of the reconstruction: the LDS kernel, the staged HBM one
+constexpr int kChainSplitWide = 8;  // the direct HBM kernel (fewer registers; 4 spills there)
+constexpr int kChainStagedNp = 96;  // padded sides from which the HBM product kernels stage their fibre tiles
 
 // Host planning of the chain (Algorithms 2, 3 and 5 of the chain page, with
 // the pending row scales of a direction folded into the next operator on

@@ -291,8 +291,8 @@ typedef struct oz2_chain_plan* oz2_chain_plan_t;
  * greedy drop schedule passes every range check for the effective
  * operators, the drop counts g, and the effective operators' residues and
  * the row exponents left pending on each direction, which are copied to
- * DEVICE memory owned by the plan (about 2.5 KiB + 12 np + depth * s * np *
- * (np rounded up to 16) bytes, plus depth * 4 KiB for n <= 16).  ops: HOST
+ * DEVICE memory owned by the plan (about 3.5 KiB + 12 np + depth * (2 KiB +
+ * s * np * (np rounded up to 16)) bytes, plus depth * 4 KiB for n <= 16).  ops: HOST
  * array of depth pointers to HOST n x n column-major operators (finite).
  * modes: HOST array of depth directions in {1, 2, 3}, or NULL for the
  * directions in turn.  Argument numbers: h 1, n 2, depth 3, ops 4 (also a

@@ -6,7 +6,7 @@
 // n, s, depth and mode orders, including non-finite and all-zero operators.
 // The weight tables are also checked against their definitions, in exact
 // integers on random residue vectors: the one-pass drop against g repeated
-// RnsDrops, the two-block digits against one elimination over all slots,
+// RnsDrops, the digits in blocks against one elimination over all slots,
 // the CRT base extension against the residues of the integer it extends.
 #include <cmath>
 #include <cstdint>
@@ -68,11 +68,13 @@ static int check_drop_table(const ChainTables& T, int g) {
     return bad;
 }
 
-// two-block mixed-radix digits (chain_split_table's weights) against one
-// elimination over all slots, entries offset by 128 as in the kernels
-static int check_split_table(const ChainTables& T) {
+// the mixed-radix digits in blocks of `split` slots (chain_split_table's
+// weights) against one elimination over all slots, entries offset by 128 as
+// in the kernels
+static int check_split_table(const ChainTables& T, int split) {
     ChainDropTable D;
-    chain_split_table(T, kChainSplit, &D);
+    chain_split_table(T, split, &D);
+    const auto row = [&D](int r) -> const float* { return r == 0 ? D.qinv : D.nw[r - 1]; };
     int m[kChainMaxS], bad = 0;
     for (int u = 0; u < kChainMaxS; ++u) m[u] = (int)T.mod[u];
     const auto step = [&](int (&x)[kChainMaxS], int i, int j) {
@@ -84,16 +86,19 @@ static int check_split_table(const ChainTables& T) {
         for (int u = 0; u < kChainMaxS; ++u) a[u] = b[u] = r[u] + 128;
         for (int i = 0; i < kChainMaxS - 1; ++i)
             for (int j = i + 1; j < kChainMaxS; ++j) step(a, i, j);
-        for (int i = 0; i < kChainSplit - 1; ++i)
-            for (int j = i + 1; j < kChainSplit; ++j) step(b, i, j);
-        for (int p = kChainSplit; p < kChainMaxS; ++p) {
-            int64_t acc = (int64_t)b[p] * (int)D.qinv[p];
-            for (int i = 0; i < kChainSplit; ++i) acc += (int64_t)b[i] * (int)D.nw[i][p];
-            bad += acc >= (1 << 19) || acc <= -(1 << 19);
-            b[p] = m[p] == 1 ? 0 : centered_i(acc, m[p]);
+        for (int lo = 0; lo < kChainMaxS; lo += split) {
+            const int hi = lo + split;
+            for (int i = lo; i < hi - 1; ++i)
+                for (int j = i + 1; j < hi; ++j) step(b, i, j);
+            if (hi == kChainMaxS) break;
+            const int rb = (lo / split) * (split + 1);
+            for (int p = hi; p < kChainMaxS; ++p) {
+                int64_t acc = (int64_t)b[p] * (int)row(rb)[p];
+                for (int i = 0; i < split; ++i) acc += (int64_t)b[lo + i] * (int)row(rb + 1 + i)[p];
+                bad += acc >= (1 << 19) || acc <= -(1 << 19);
+                b[p] = m[p] == 1 ? 0 : centered_i(acc, m[p]);
+            }
         }
-        for (int i = kChainSplit; i < kChainMaxS - 1; ++i)
-            for (int j = i + 1; j < kChainMaxS; ++j) step(b, i, j);
         for (int u = 1; u < kChainMaxS; ++u) bad += a[u] != b[u];
         bad += a[0] != b[0];  // both still offset by 128
     }
@@ -183,7 +188,7 @@ int main() {
         if (st == 0) {
             for (int i = 0; i + 1 < d; ++i)
                 if (P.g[i] >= 1) bad += check_drop_table(T, P.g[i]) + (P.g[i] <= 14 ? check_crt_table(T, P.g[i]) : 0);
-            bad += check_split_table(T);
+            bad += check_split_table(T, kChainSplit) + check_split_table(T, 8);
         }
     }
     // the tables at every drop count the kernels accept, for s = 2 .. 16
@@ -203,7 +208,7 @@ int main() {
             }
         for (int u = 0; u < kChainMaxS; ++u) T.rmod[u] = 1.0f / T.mod[u];
         for (int g = 1; g < s; ++g) bad += check_drop_table(T, g) + (g <= 14 ? check_crt_table(T, g) : 0);
-        bad += check_split_table(T);
+        bad += check_split_table(T, kChainSplit) + check_split_table(T, 8);
     }
     std::printf("planner driver: %d unexpected results\n", bad);
     return bad != 0;

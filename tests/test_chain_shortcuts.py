@@ -7,10 +7,10 @@ Tensor Mode Products" (oracle/rescale_be.py), in exact integers:
   dropped moduli and D the part of v that its mixed-radix digits over them
   represent; so each kept residue is [r_p Q^-1 - sum_j d_j prod_{l<j} q_l
   Q^-1]_p, from the digits over the dropped moduli alone;
-- the final digits in two blocks: the mixed-radix digits over all moduli
+- the final digits in blocks: the mixed-radix digits over all moduli
   (Algorithm 4's MrcDigits, Eq. 24) are those over the first block followed
-  by those of (v - A) / M1 over the second block, whose residues come from
-  one such sum each;
+  by those of (v - A) / M1 over the rest, block by block, whose residues
+  come from one such sum each;
 - the base extension by the CRT: the residues of v on the dropped moduli
   from those on the kept ones (product M) as [sum_i xi_i [M/m_i]_p -
   alpha [M]_p]_p, xi_i = [r_i (M/m_i)^-1]_{m_i}, alpha the rounding of
@@ -75,25 +75,30 @@ def test_drops_at_once_equal_repeated_rns_drop(s):
 
 @pytest.mark.parametrize("s", [4, 8, 12, 15, 16])
 @pytest.mark.parametrize("split", [4, 8])
-def test_digits_in_two_blocks_equal_one_elimination(s, split):
+def test_digits_in_blocks_equal_one_elimination(s, split):
+    """the digits block by block: each block's by elimination among its
+    moduli, then the later moduli's residues of (v - A) / M_b by one sum each"""
     basis = list(rb.max_product_moduli(s))
     if split >= s:
         pytest.skip("one block")
     vals = _rand_ints(rb.moduli_product(basis), 64, 7100 + s + split)
     R = _residues(vals, basis)
     want = rb.mrc_digits(R, basis)
-    first, second = basis[:split], basis[split:]
-    d1 = rb.mrc_digits(R, first)
-    M1 = rb.moduli_product(first)
-    R2 = {}
-    for p in second:
-        qinv = pow(M1 % p, -1, p)
-        acc = R[p] * rb.centered(qinv, p)
-        for i, d in enumerate(d1):
-            acc = acc - d * rb.centered(rb.moduli_product(first[:i]) * qinv % p, p)
-        assert np.all(np.abs(acc) < 2 ** 19), (s, split, p)
-        R2[p] = rb.centered_array(acc, p)
-    got = d1 + rb.mrc_digits(R2, second)
+    got, rest, Rb = [], list(basis), dict(R)
+    while rest:
+        block, rest = rest[:split], rest[split:]
+        d = rb.mrc_digits(Rb, block)
+        got += d
+        Mb = rb.moduli_product(block)
+        nxt = {}
+        for p in rest:
+            qinv = pow(Mb % p, -1, p)
+            acc = Rb[p] * rb.centered(qinv, p)
+            for i, di in enumerate(d):
+                acc = acc - di * rb.centered(rb.moduli_product(block[:i]) * qinv % p, p)
+            assert np.all(np.abs(acc) < 2 ** 19), (s, split, p)
+            nxt[p] = rb.centered_array(acc, p)
+        Rb = nxt
     for i, (a, b) in enumerate(zip(got, want)):
         assert np.array_equal(a, b), (s, split, i)
     # and the digits rebuild the integers (Eq. 24)
